@@ -1,0 +1,209 @@
+"""Base-weight formats: NF4 code book, pack and dequant (oracle only).
+
+The base weight W is fp32 [N, K] (row n = output feature, K = input features,
+the nn.Linear convention).  Blocks run along K.  Packing decisions are taken
+in IEEE fp32 (numpy float32 arithmetic is correctly rounded), ties to even.
+
+4-bit code layout (Q4_0-style and NF4): each row's codes are cut into groups
+of 32 consecutive elements; a group occupies 16 bytes, and byte j of the group
+holds element j in its low nibble and element j + 16 in its high nibble.
+Codes are u8 [N, K/2]; scales are a separate array (structure of arrays).
+
+Formats (the legacy-GGUF 4-bit type that the GGUF-recipe page names, the
+bitsandbytes NF4 base named on the Surogate pages and the Soup page, and the
+FP8 E4M3 base of the Surogate FP8 recipe):
+
+* Q4_0-style: block of 32, fp16 scale d = fp16(absmax / 7), code
+  q = clamp(rint(w / d) + 8, 0, 15), value (q - 8) * d.  A zero block stores
+  code 8 everywhere.
+* NF4: block of 64, fp32 scale a = absmax, code = index of the nearest entry
+  of the 16-level code book (ties go to the lower code), value c[q] * a.  A
+  zero block stores code 7 (the exact zero of the book).  No double
+  quantization.
+* FP8: per-tensor fp32 scale s = absmax / 448, code = E4M3(w / s) with
+  saturation; value E4M3(q) * s.  A zero tensor has s = 0 and codes 0.
+"""
+
+import statistics
+
+import numpy as np
+
+from . import codecs
+
+FMT_Q4_0, FMT_NF4, FMT_FP8 = 1, 2, 3
+BLOCK = {FMT_Q4_0: 32, FMT_NF4: 64}
+
+
+# ----------------------------------------------------------------------------- NF4 book
+
+def nf4_codebook_f64(inv_cdf=None):
+    """The 16 NF4 levels in fp64 (QLoRA paper, section "4-bit NormalFloat").
+
+    The levels are quantiles of N(0, 1): 8 for the positive half and 7 for the
+    negative half, taken at equally spaced probabilities from an offset delta
+    down to 1/2 (the 1/2 endpoint, i.e. zero, is dropped from each half and a
+    single exact zero is added), then normalised so the largest magnitude is 1.
+    delta is the mean of 1 - 1/(2*15) and 1 - 1/(2*16), the two outermost
+    quantile positions for 15 and 16 levels.
+    """
+    if inv_cdf is None:
+        inv_cdf = statistics.NormalDist().inv_cdf
+    delta = 0.5 * ((1.0 - 1.0 / 30.0) + (1.0 - 1.0 / 32.0))
+    pos = [inv_cdf(delta - i * (delta - 0.5) / 8.0) for i in range(8)]
+    neg = [-inv_cdf(delta - i * (delta - 0.5) / 7.0) for i in range(7)]
+    levels = sorted(pos + neg + [0.0])
+    top = max(abs(v) for v in levels)
+    return np.array([v / top for v in levels], dtype=np.float64)
+
+
+def nf4_codebook(inv_cdf=None):
+    """NF4 levels rounded once to fp32."""
+    return nf4_codebook_f64(inv_cdf).astype(np.float32)
+
+
+def nf4_thresholds(book=None):
+    """Decision thresholds m_i = fl32(fl32(c_i + c_{i+1}) * 0.5), i = 0..14."""
+    c = nf4_codebook() if book is None else np.asarray(book, np.float32)
+    return ((c[:-1] + c[1:]) * np.float32(0.5)).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------- nibbles
+
+def nibbles_to_bytes(q):
+    """Codes u8 [N, K] (values 0..15) -> packed bytes u8 [N, K/2], split-half groups of 32."""
+    q = np.asarray(q, dtype=np.uint8)
+    n, k = q.shape
+    assert k % 32 == 0
+    g = q.reshape(n, k // 32, 32)
+    lo, hi = g[:, :, :16], g[:, :, 16:]
+    return (lo | (hi << 4)).astype(np.uint8).reshape(n, k // 2)
+
+
+def bytes_to_nibbles(b):
+    """Packed bytes u8 [N, K/2] -> codes u8 [N, K]."""
+    b = np.asarray(b, dtype=np.uint8)
+    n, kh = b.shape
+    g = b.reshape(n, kh // 16, 16)
+    q = np.concatenate([g & 0x0F, g >> 4], axis=2)
+    return q.reshape(n, kh * 2).astype(np.uint8)
+
+
+def _check_w(w):
+    w = np.asarray(w)
+    if w.dtype != np.float32:
+        raise TypeError("base weight must be fp32")
+    if not np.all(np.isfinite(w)):
+        raise ValueError("non-finite base weight")
+    return w
+
+
+# ----------------------------------------------------------------------------- Q4_0-style
+
+def pack_q4_0(w):
+    """fp32 W [N, K] -> (codes u8 [N, K/2], scales fp16 bits u16 [N, K/32])."""
+    w = _check_w(w)
+    n, k = w.shape
+    if k % 32:
+        raise ValueError("K must be a multiple of 32")
+    blk = w.reshape(n, k // 32, 32)
+    amax = np.max(np.abs(blk), axis=2)                      # exact
+    d32 = (amax / np.float32(7.0)).astype(np.float32)       # IEEE fp32 divide
+    d_bits, over = codecs.fp16_encode(d32)
+    if np.any(over):
+        raise OverflowError("Q4_0 scale overflows fp16")
+    d = codecs.fp16_decode(d_bits)                          # the stored scale, as fp32
+    q = np.full(blk.shape, 8, dtype=np.int64)
+    nz = d != 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = (blk / d[:, :, None]).astype(np.float32)    # IEEE fp32 divide
+    ratio = np.where(nz[:, :, None], ratio, np.float32(0.0))
+    qq = np.clip(np.rint(ratio).astype(np.int64) + 8, 0, 15)
+    q = np.where(nz[:, :, None], qq, q)
+    codes = nibbles_to_bytes(q.reshape(n, k).astype(np.uint8))
+    return codes, d_bits
+
+
+def dequant_q4_0(codes, scales_fp16_bits):
+    """(codes, fp16 scale bits) -> fp32 W [N, K]: (q - 8) * d, exact in fp32."""
+    q = bytes_to_nibbles(codes).astype(np.float32)
+    n, k = q.shape
+    d = codecs.fp16_decode(scales_fp16_bits).astype(np.float32)
+    w = (q.reshape(n, k // 32, 32) - np.float32(8.0)) * d[:, :, None]
+    return w.reshape(n, k).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------- NF4
+
+def pack_nf4(w, book=None):
+    """fp32 W [N, K] -> (codes u8 [N, K/2], absmax scales fp32 [N, K/64])."""
+    w = _check_w(w)
+    n, k = w.shape
+    if k % 64:
+        raise ValueError("K must be a multiple of 64")
+    mids = nf4_thresholds(book)
+    blk = w.reshape(n, k // 64, 64)
+    amax = np.max(np.abs(blk), axis=2).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        v = (blk / amax[:, :, None]).astype(np.float32)     # IEEE fp32 divide
+    v = np.where((amax == 0)[:, :, None], np.float32(0.0), v)
+    q = np.zeros(blk.shape, dtype=np.int64)
+    for m in mids:                                          # q = #{i : v > m_i}
+        q += (v > m)
+    q = np.where((amax == 0)[:, :, None], 7, q)
+    codes = nibbles_to_bytes(q.reshape(n, k).astype(np.uint8))
+    return codes, amax
+
+
+def dequant_nf4(codes, absmax, book=None):
+    """(codes, fp32 absmax) -> fp32 W [N, K]: fl32(c[q] * a)."""
+    c = nf4_codebook() if book is None else np.asarray(book, np.float32)
+    q = bytes_to_nibbles(codes)
+    n, k = q.shape
+    vals = c[q].reshape(n, k // 64, 64)
+    w = vals * np.asarray(absmax, np.float32)[:, :, None]   # one fp32 rounding
+    return w.reshape(n, k).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------- FP8
+
+def pack_fp8(w):
+    """fp32 W [N, K] -> (E4M3 codes u8 [N, K], per-tensor fp32 scale)."""
+    w = _check_w(w)
+    amax = np.float32(np.max(np.abs(w))) if w.size else np.float32(0.0)
+    s = np.float32(amax / np.float32(448.0))
+    if s == 0:
+        return np.zeros(w.shape, dtype=np.uint8), s
+    ratio = (w / s).astype(np.float32)
+    return codecs.e4m3_encode(ratio), s
+
+
+def dequant_fp8(codes, scale):
+    """(E4M3 codes, fp32 scale) -> fp32 W: fl32(E4M3(q) * s)."""
+    return (codecs.e4m3_decode(codes) * np.float32(scale)).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------- dispatch
+
+def pack(fmt, w):
+    if fmt == FMT_Q4_0:
+        return pack_q4_0(w)
+    if fmt == FMT_NF4:
+        return pack_nf4(w)
+    if fmt == FMT_FP8:
+        return pack_fp8(w)
+    raise ValueError(f"unknown format {fmt}")
+
+
+def dequant(fmt, codes, scales):
+    if fmt == FMT_Q4_0:
+        return dequant_q4_0(codes, scales)
+    if fmt == FMT_NF4:
+        return dequant_nf4(codes, scales)
+    if fmt == FMT_FP8:
+        return dequant_fp8(codes, scales)
+    raise ValueError(f"unknown format {fmt}")
+
+
+def bf16_tile_values(w_f32):
+    """The bf16 operand values a GEMM feeds to the matrix cores: one RNE rounding."""
+    return codecs.bf16_round(w_f32)

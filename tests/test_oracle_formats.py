@@ -1,0 +1,243 @@
+"""Pins for the oracle's NF4 code book, pack rules and dequant.  CPU only."""
+
+import os
+import statistics
+
+import numpy as np
+import pytest
+import scipy.stats
+
+from oracle import codecs, formats
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------- NF4 code book
+
+def test_nf4_book_two_independent_inverse_cdfs_agree():
+    a = formats.nf4_codebook(statistics.NormalDist().inv_cdf)
+    b = formats.nf4_codebook(lambda p: float(scipy.stats.norm.ppf(p)))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_nf4_book_invariants():
+    c = formats.nf4_codebook().astype(np.float64)
+    assert c.shape == (16,)
+    assert np.all(np.diff(c) > 0)
+    assert c[0] == -1.0 and c[7] == 0.0 and c[15] == 1.0
+    assert (c < 0).sum() == 7 and (c > 0).sum() == 8
+    gaps = np.diff(c)
+    assert abs(gaps.min() - 0.0796) < 5e-4 and abs(gaps.max() - 0.3038) < 5e-4
+    # smallest positive level: Phi^-1(1/2 + (delta - 1/2)/8) / Phi^-1(delta)
+    delta = 0.5 * ((1 - 1 / 30) + (1 - 1 / 32))
+    ppf = scipy.stats.norm.ppf
+    assert abs(c[8] - ppf(0.5 + (delta - 0.5) / 8) / ppf(delta)) < 1e-7
+    assert abs(c[6] + ppf(0.5 + (delta - 0.5) / 7) / ppf(delta)) < 1e-7
+
+
+def test_nf4_book_bits_from_exact_rational_offset():
+    """Every level, bit for bit, from an independent route: delta as the exact
+    rational (29/30 + 31/32) / 2, probabilities built upward from 1/2, scipy's
+    inverse CDF.  A rounded delta (e.g. 0.9677083) moves levels by 1-2 ulps."""
+    from fractions import Fraction
+    delta = (Fraction(29, 30) + Fraction(31, 32)) / 2
+    ppf = scipy.stats.norm.ppf
+    top = ppf(float(delta))
+    pos = [ppf(float(Fraction(1, 2) + (delta - Fraction(1, 2)) * j / 8)) / top for j in range(1, 9)]
+    neg = [-ppf(float(Fraction(1, 2) + (delta - Fraction(1, 2)) * j / 7)) / top for j in range(7, 0, -1)]
+    want = np.array(neg + [0.0] + pos, dtype=np.float64).astype(np.float32)
+    assert np.array_equal(formats.nf4_codebook().view(np.uint32), want.view(np.uint32))
+
+
+def test_nf4_thresholds_between_levels():
+    c = formats.nf4_codebook()
+    m = formats.nf4_thresholds()
+    assert np.all(c[:-1] < m) and np.all(m < c[1:])
+
+
+# ----------------------------------------------------------------------------- nibbles
+
+def test_nibble_layout_round_trip_and_positions():
+    g = np.random.default_rng(0)
+    q = g.integers(0, 16, size=(3, 96), dtype=np.uint8)
+    b = formats.nibbles_to_bytes(q)
+    assert b.shape == (3, 48)
+    assert np.array_equal(formats.bytes_to_nibbles(b), q)
+    # byte j of group t: element 32t + j low, element 32t + j + 16 high
+    for t in range(3):
+        for j in range(16):
+            assert b[1, 16 * t + j] == q[1, 32 * t + j] | (q[1, 32 * t + j + 16] << 4)
+
+
+# ----------------------------------------------------------------------------- Q4_0-style
+
+def _read_q40_golden():
+    vals, codes, scale, byts = [], [], None, None
+    with open(os.path.join(GOLDEN, "q4_0_block.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            if line.startswith("scale_fp16_bits"):
+                scale = int(line.split()[1], 16)
+            elif line.startswith("bytes"):
+                byts = [int(t, 16) for t in line.split()[1:]]
+            else:
+                _, v, c = line.split()
+                vals.append(np.float32(v))
+                codes.append(int(c))
+    return np.array(vals, np.float32), np.array(codes), scale, np.array(byts, np.uint8)
+
+
+def test_q40_golden_block():
+    w, codes, scale, byts = _read_q40_golden()
+    c, s = formats.pack_q4_0(w.reshape(1, 32))
+    assert int(s[0, 0]) == scale
+    assert np.array_equal(formats.bytes_to_nibbles(c)[0], codes)
+    assert np.array_equal(c[0], byts)
+    deq = formats.dequant_q4_0(c, s)[0]
+    d = np.float64(np.uint16(scale).view(np.float16))
+    assert np.array_equal(deq.astype(np.float64), (codes - 8) * d)
+
+
+def test_q40_dequant_exhaustive_codes_times_all_fp16_scales():
+    d_bits = np.arange(0, 0x7C00, dtype=np.uint32).astype(np.uint16)    # every finite d >= +0
+    d = d_bits.view(np.float16).astype(np.float64)
+    for q in range(16):
+        codes = formats.nibbles_to_bytes(np.full((d_bits.size, 32), q, np.uint8))
+        w = formats.dequant_q4_0(codes, d_bits[:, None])
+        assert np.array_equal(w.astype(np.float64), np.repeat(((q - 8) * d)[:, None], 32, 1))
+
+
+def test_q40_pack_error_bound_and_code_range():
+    g = np.random.default_rng(5)
+    w = (g.standard_normal((64, 256)) * 0.02).astype(np.float32)
+    c, s = formats.pack_q4_0(w)
+    q = formats.bytes_to_nibbles(c)
+    assert q.min() >= 1 and q.max() <= 15                               # |w/d| < 7.5 never clamps
+    d = np.repeat(codecs.fp16_decode(s).astype(np.float64), 32, axis=1)
+    err = np.abs(formats.dequant_q4_0(c, s).astype(np.float64) - w)
+    assert np.all(err <= d * (0.5 + 1e-6))
+
+
+def test_q40_zero_and_tiny_blocks():
+    w = np.zeros((2, 64), np.float32)
+    w[1, 32:] = 1e-12                                                   # absmax/7 underflows fp16
+    c, s = formats.pack_q4_0(w)
+    assert np.all(formats.bytes_to_nibbles(c) == 8)
+    assert np.all(s == 0)
+    assert np.all(formats.dequant_q4_0(c, s) == 0)
+
+
+def test_q40_overflow_rejected_and_nonfinite_rejected():
+    with pytest.raises(OverflowError):
+        formats.pack_q4_0(np.full((1, 32), 1e6, np.float32))
+    w = np.zeros((1, 32), np.float32)
+    w[0, 3] = np.nan
+    with pytest.raises(ValueError):
+        formats.pack_q4_0(w)
+
+
+# ----------------------------------------------------------------------------- NF4
+
+def test_nf4_pack_matches_brute_force_nearest_code():
+    """The threshold rule equals 'nearest level, ties to the lower code' except
+    inside the fp32 rounding sliver of a midpoint, where the rounded threshold
+    decides.  Checked against a brute-force nearest-level search."""
+    g = np.random.default_rng(7)
+    book = formats.nf4_codebook().astype(np.float64)
+    mids = formats.nf4_thresholds().astype(np.float64)
+    w = (g.standard_normal((32, 640)) * 0.02).astype(np.float32)
+    w[0, :15] = mids.astype(np.float32)                                 # exact threshold values
+    w[0, 63] = 1.0
+    c, a = formats.pack_nf4(w)
+    q = formats.bytes_to_nibbles(c).reshape(32, 10, 64)
+    v = (w.reshape(32, 10, 64) / a[:, :, None]).astype(np.float32).astype(np.float64)
+    dist = np.abs(v[..., None] - book)                                   # exact in fp64
+    brute = np.argmin(dist, axis=-1)                                     # first minimum = lower code
+    diff = brute != q
+    if diff.any():
+        vv = v[diff]
+        true_mid = (book[q[diff]] + book[brute[diff]]) / 2
+        assert np.all(np.abs(vv - true_mid) <= 2 ** -24)
+    # a value equal to a rounded threshold goes to the lower code
+    assert np.array_equal(q[0, 0, :15], np.arange(15))
+
+
+def test_nf4_levels_times_scale_recover_codes():
+    book = formats.nf4_codebook()
+    w = np.tile(book, 4).reshape(1, 64) * np.float32(0.0371)
+    c, a = formats.pack_nf4(w.astype(np.float32))
+    assert a[0, 0] == np.float32(0.0371) * np.float32(1.0)
+    assert np.array_equal(formats.bytes_to_nibbles(c)[0], np.tile(np.arange(16), 4))
+
+
+def test_nf4_dequant_product_rounded_once():
+    book = formats.nf4_codebook().astype(np.float64)
+    g = np.random.default_rng(11)
+    scales = np.concatenate([2.0 ** np.arange(-20, 5), g.uniform(1e-4, 0.2, 200),
+                             [1.1754944e-38, 3e-38]]).astype(np.float32)
+    q = np.tile(np.arange(16, dtype=np.uint8), 4)
+    codes = formats.nibbles_to_bytes(np.tile(q, (scales.size, 1)))
+    w = formats.dequant_nf4(codes, scales[:, None])
+    ref = (book[q][None, :] * scales.astype(np.float64)[:, None]).astype(np.float32)
+    assert np.array_equal(w, ref)
+    p2 = scales[:25].astype(np.float64)
+    assert np.array_equal(w[:25].astype(np.float64), book.astype(np.float32)[q][None, :] * p2[:, None])
+
+
+def test_nf4_zero_block_and_error_bound():
+    g = np.random.default_rng(9)
+    w = (g.standard_normal((16, 128)) * 0.02).astype(np.float32)
+    w[3, 64:] = 0
+    c, a = formats.pack_nf4(w)
+    q = formats.bytes_to_nibbles(c)
+    assert np.all(q[3, 64:] == 7) and a[3, 1] == 0
+    book = formats.nf4_codebook().astype(np.float64)
+    maxgap = np.max(np.diff(book))
+    err = np.abs(formats.dequant_nf4(c, a).astype(np.float64) - w)
+    assert np.all(err <= np.repeat(a.astype(np.float64), 64, 1) * (maxgap / 2 + 1e-6))
+
+
+# ----------------------------------------------------------------------------- FP8
+
+def test_fp8_dequant_all_codes_times_scales():
+    import torch
+    c = np.arange(256, dtype=np.uint8)
+    ok = (c != 0x7F) & (c != 0xFF)
+    dec = torch.from_numpy(c).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    for s in np.float32([1.0, 0.02 / 448, 3.3e-5, 7.77e-3]):
+        w = formats.dequant_fp8(c[ok].reshape(1, -1), s)[0]
+        assert np.array_equal(w, (dec[ok] * np.float64(s)).astype(np.float32))
+
+
+def test_fp8_pack_properties():
+    g = np.random.default_rng(13)
+    w = (g.standard_normal((32, 256)) * 0.02).astype(np.float32)
+    c, s = formats.pack_fp8(w)
+    assert s == np.float32(np.max(np.abs(w)) / np.float32(448.0))
+    dq = formats.dequant_fp8(c, s).astype(np.float64)
+    rel = np.abs(dq - w) / np.maximum(np.abs(w), 2.0 ** -6 * s)
+    assert rel.max() <= 2 ** -4 + 1e-6                                   # 3 mantissa bits
+    c0, s0 = formats.pack_fp8(np.zeros((2, 32), np.float32))
+    assert s0 == 0 and not c0.any()
+
+
+# ----------------------------------------------------------------------------- re-pack
+
+@pytest.mark.parametrize("fmt", [formats.FMT_Q4_0, formats.FMT_NF4])
+def test_repack_is_idempotent_4bit(fmt):
+    g = np.random.default_rng(17 + fmt)
+    w = (g.standard_normal((40, 512)) * 0.02).astype(np.float32)
+    c1, s1 = formats.pack(fmt, w)
+    c2, s2 = formats.pack(fmt, formats.dequant(fmt, c1, s1))
+    assert np.array_equal(c1, c2) and np.array_equal(np.asarray(s1), np.asarray(s2))
+
+
+def test_repack_fp8_codes_identical():
+    g = np.random.default_rng(19)
+    w = (g.standard_normal((40, 512)) * 0.02).astype(np.float32)
+    c1, s1 = formats.pack_fp8(w)
+    c2, s2 = formats.pack_fp8(formats.dequant_fp8(c1, s1))
+    assert np.array_equal(c1, c2)
+    assert abs(float(s2) - float(s1)) <= float(np.spacing(s1))

@@ -1,0 +1,178 @@
+"""Pins for the oracle's forward / backward: special cases, finite differences,
+integer-exact data, the merged-weight route and brute force.  CPU only."""
+
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import codecs, formats, lora
+
+
+def _tiny(fmt, seed, m=3, k=64, n=5, r=2):
+    g = np.random.default_rng(seed)
+    w = (g.standard_normal((n, k)) * 0.02).astype(np.float32)
+    c, s = formats.pack(fmt, w)
+    wd = formats.dequant(fmt, c, s).astype(np.float64)
+    x = codecs.bf16_round(g.standard_normal((m, k)).astype(np.float32)).astype(np.float64)
+    a = codecs.bf16_round((g.standard_normal((r, k)) / np.sqrt(k)).astype(np.float32)).astype(np.float64)
+    b = codecs.bf16_round((g.standard_normal((n, r)) * 0.3).astype(np.float32)).astype(np.float64)
+    dy = g.standard_normal((m, n))
+    return x, wd, a, b, dy
+
+
+@pytest.mark.parametrize("fmt", [formats.FMT_Q4_0, formats.FMT_NF4])
+def test_b_zero_gives_base_exactly(fmt):
+    x, wd, a, b, dy = _tiny(fmt, 1)
+    b0 = np.zeros_like(b)
+    y, _ = lora.forward(x, wd, a, b0, 4.0)
+    assert np.array_equal(y, lora.forward_base(x, wd))
+    dx, da, db = lora.backward(x, dy, wd, a, b0, 4.0)
+    assert np.array_equal(dx, dy @ wd)
+    assert not np.any(da)
+    y32, _ = lora.forward(x, wd, a, b0, 4.0, dtype=np.float32)
+    assert np.array_equal(y32, lora.forward_base(x, wd, dtype=np.float32))
+
+
+def test_a_zero_gives_base_and_zero_db():
+    x, wd, a, b, dy = _tiny(formats.FMT_NF4, 2)
+    a0 = np.zeros_like(a)
+    y, u = lora.forward(x, wd, a0, b, 4.0)
+    assert np.array_equal(y, lora.forward_base(x, wd)) and not np.any(u)
+    _, _, db = lora.backward(x, dy, wd, a0, b, 4.0)
+    assert not np.any(db)
+
+
+@pytest.mark.parametrize("fmt", [formats.FMT_Q4_0, formats.FMT_NF4])
+def test_finite_differences_match_analytic_gradients(fmt):
+    """L = sum(G * y); y is linear in each of x, A, B separately, so a central
+    difference is exact up to rounding for any step."""
+    x, wd, a, b, g = _tiny(fmt, 3)
+    alpha = 4.0
+    dx, da, db = lora.backward(x, g, wd, a, b, alpha)
+
+    def loss(xx, aa, bb):
+        return float(np.sum(g * lora.forward(xx, wd, aa, bb, alpha)[0]))
+
+    h = 0.5
+    for name, t, grad in (("x", x, dx), ("A", a, da), ("B", b, db)):
+        num = np.zeros_like(t)
+        for idx in np.ndindex(t.shape):
+            tp, tm = t.copy(), t.copy()
+            tp[idx] += h
+            tm[idx] -= h
+            args = {"x": (x, a, b), "A": (x, a, b), "B": (x, a, b)}[name]
+            if name == "x":
+                num[idx] = (loss(tp, a, b) - loss(tm, a, b)) / (2 * h)
+            elif name == "A":
+                num[idx] = (loss(x, tp, b) - loss(x, tm, b)) / (2 * h)
+            else:
+                num[idx] = (loss(x, a, tp) - loss(x, a, tm)) / (2 * h)
+            del args
+        assert np.max(np.abs(num - grad)) <= 1e-10 * max(1.0, np.max(np.abs(grad))), name
+
+
+def test_integer_data_is_exact():
+    """Integer weights (Q4_0 with d = 1), ternary x, small integer adapters:
+    every product and sum is a small integer, so the result is exact in any
+    order.  Compared against an explicit triple loop."""
+    g = np.random.default_rng(4)
+    m, k, n, r, alpha = 4, 64, 6, 2, 4.0          # s = 2
+    q = g.integers(1, 16, size=(n, k)).astype(np.uint8)
+    codes = formats.nibbles_to_bytes(q)
+    d_bits = np.full((n, k // 32), 0x3C00, np.uint16)  # fp16 1.0
+    wd = formats.dequant_q4_0(codes, d_bits)
+    assert np.array_equal(wd, q.astype(np.float32) - 8)
+    x = g.integers(-1, 2, size=(m, k)).astype(np.float32)
+    a = g.integers(-2, 3, size=(r, k)).astype(np.float32)
+    b = g.integers(-2, 3, size=(n, r)).astype(np.float32)
+    dy = g.integers(-1, 2, size=(m, n)).astype(np.float32)
+    y, _ = lora.forward(x, wd, a, b, alpha)
+    dx, da, db = lora.backward(x, dy, wd, a, b, alpha)
+    s = 2
+    for i, j in itertools.product(range(m), range(n)):
+        base = sum(int(x[i, t]) * int(wd[j, t]) for t in range(k))
+        u = [sum(int(x[i, t]) * int(a[p, t]) for t in range(k)) for p in range(r)]
+        assert y[i, j] == base + s * sum(u[p] * int(b[j, p]) for p in range(r))
+    for i, t in itertools.product(range(m), range(k)):
+        v = [sum(int(dy[i, j]) * int(b[j, p]) for j in range(n)) for p in range(r)]
+        ref = sum(int(dy[i, j]) * int(wd[j, t]) for j in range(n)) + s * sum(v[p] * int(a[p, t]) for p in range(r))
+        assert dx[i, t] == ref
+    v = dy.astype(np.int64) @ b.astype(np.int64)
+    u = x.astype(np.int64) @ a.astype(np.int64).T
+    for p, t in itertools.product(range(r), range(k)):
+        assert da[p, t] == s * sum(v[i, p] * int(x[i, t]) for i in range(m))
+    for j, p in itertools.product(range(n), range(r)):
+        assert db[j, p] == s * sum(int(dy[i, j]) * u[i, p] for i in range(m))
+
+
+@pytest.mark.parametrize("fmt", [formats.FMT_Q4_0, formats.FMT_NF4, formats.FMT_FP8])
+def test_merged_weight_route_agrees(fmt):
+    g = np.random.default_rng(6)
+    w = (g.standard_normal((24, 128)) * 0.02).astype(np.float32)
+    c, s = formats.pack(fmt, w)
+    wd = formats.dequant(fmt, c, s)
+    x = codecs.bf16_round(g.standard_normal((10, 128)).astype(np.float32))
+    a = codecs.bf16_round((g.standard_normal((8, 128)) / 11.3).astype(np.float32))
+    b = codecs.bf16_round((g.standard_normal((24, 8)) * 0.01).astype(np.float32))
+    y, _ = lora.forward(x, wd, a, b, 16.0)
+    ym = lora.forward_merged(x, wd, a, b, 16.0)
+    assert np.max(np.abs(y - ym)) <= 1e-13 * np.max(np.abs(y))
+
+
+def test_brute_force_loops_tiny():
+    x, wd, a, b, dy = _tiny(formats.FMT_NF4, 8, m=2, k=64, n=3, r=2)
+    alpha, r = 3.0, 2
+    s = alpha / r
+    y, u = lora.forward(x, wd, a, b, alpha)
+    dx, da, db = lora.backward(x, dy, wd, a, b, alpha)
+    m, k = x.shape
+    n = wd.shape[0]
+    U = [[sum(x[i, t] * a[p, t] for t in range(k)) for p in range(r)] for i in range(m)]
+    V = [[sum(dy[i, j] * b[j, p] for j in range(n)) for p in range(r)] for i in range(m)]
+    for i in range(m):
+        for j in range(n):
+            ref = sum(x[i, t] * wd[j, t] for t in range(k)) + s * sum(U[i][p] * b[j, p] for p in range(r))
+            assert abs(y[i, j] - ref) <= 1e-13
+        for t in range(k):
+            ref = sum(dy[i, j] * wd[j, t] for j in range(n)) + s * sum(V[i][p] * a[p, t] for p in range(r))
+            assert abs(dx[i, t] - ref) <= 1e-13
+    for p in range(r):
+        for t in range(k):
+            assert abs(da[p, t] - s * sum(V[i][p] * x[i, t] for i in range(m))) <= 1e-13
+    for j in range(n):
+        for p in range(r):
+            assert abs(db[j, p] - s * sum(dy[i, j] * U[i][p] for i in range(m))) <= 1e-13
+
+
+def test_rel_err_conventions():
+    assert lora.rel_err(np.zeros(3), np.zeros(3)) == 0.0
+    assert lora.rel_err(np.ones(3), np.zeros(3)) == float("inf")
+    assert lora.rel_err([1.0, 2.5], [1.0, 2.0]) == 0.25
+
+
+# ----------------------------------------------------------------------------- FP8 activations
+
+def test_act_split_error_bound():
+    """|x - s(hi + lo/16)| <= 2^-8 |x| + s 2^-13: hi carries 3 mantissa bits,
+    the 16x finer lo term 3 more, subnormal lo quantum 2^-9."""
+    g = np.random.default_rng(21)
+    x = codecs.bf16_round(g.standard_normal((64, 512)).astype(np.float32))
+    x[3] = 0
+    x[5, 7] = 1e-30
+    hi, lo, s = lora.act_split_e4m3(x)
+    assert s[3] == 0 and not hi[3].any() and not lo[3].any()
+    xr = lora.act_join_e4m3(hi, lo, s)
+    bound = 2.0 ** -8 * np.abs(x) + s[:, None].astype(np.float64) * 2.0 ** -13
+    assert np.all(np.abs(xr - x) <= bound)
+    assert lora.rel_err(xr, x) < 4e-3
+
+
+def test_act_split_exact_on_e4m3_grid():
+    """Values that are E4M3 codes times the row scale reproduce with lo = 0."""
+    c = np.arange(0, 0x7F, dtype=np.uint8)
+    vals = codecs.e4m3_decode(c)                     # includes 448, so s = 1
+    x = np.concatenate([vals, -vals]).reshape(1, -1).astype(np.float32)
+    hi, lo, s = lora.act_split_e4m3(x)
+    assert s[0] == 1.0
+    assert np.array_equal(codecs.e4m3_decode(hi)[0], x[0]) and not np.any(lo & 0x7F)
