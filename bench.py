@@ -1,0 +1,233 @@
+"""Benchmark: QLoRA linear layer forward + backward on one MI355X.
+
+One step = forward of every projection of a decoder layer (7 LoRA linears over
+a frozen quantized base), then backward of every projection (dX, dA, dB), on
+synthetic seeded inputs resident in HBM.  Reported value: tokens/s per layer.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--m M]
+
+Prints ONE JSON line.  Besides the headline value it carries the roofline of
+the dominant kernel (its launches bracketed by HIP events on the stream they
+run on) and the CPU oracle timed on this host on a bounded sample.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QLoRA-linear fwd+bwd tokens/s per layer; % bf16 MFMA peak, % HBM BW"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+FMT_NAME = {1: "q4_0", 2: "nf4", 3: "fp8_e4m3"}
+BPW = {1: 18 / 32, 2: 0.5 + 4 / 64, 3: 1.0}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3_0.6b_nf4")
+    ap.add_argument("--m", type=int, default=None, help="tokens (default: the workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="tokens in the CPU oracle sample (0: all)")
+    ap.add_argument("--copies", type=int, default=0, help="packed weight copies rotated per step (0: auto)")
+    return ap.parse_args()
+
+
+def layer_flops(wl, m):
+    return sum(m * (4 * p.n * p.k + 6 * wl.r * (p.k + p.n)) for p in wl.projs)
+
+
+def layer_bytes(wl, m):
+    bpw = BPW[wl.fmt]
+    sk = sum(p.k for p in wl.projs)
+    sn = sum(p.n for p in wl.projs)
+    snk = sum(p.n * p.k for p in wl.projs)
+    return 2 * bpw * snk + 8 * wl.r * (sk + sn) + m * (6 * sk + 4 * sn) + 12 * m * wl.r * len(wl.projs)
+
+
+def fwd_kernel_flops(wl, p, m):
+    return m * (2 * p.n * p.k + 2 * wl.r * (p.k + p.n))
+
+
+def source_hash():
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "quantized_base_lora_amd", "csrc", "kernels_gemm.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload, m):
+    """HBM bytes per dominant-kernel launch from committed rocprofv3 counters,
+    if they were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "qgemm_fwd_counters.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha") != source_hash():
+        return None
+    e = d.get("workloads", {}).get(f"{workload}@{m}")
+    return None if e is None else e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, tokens, min_seconds=10.0):
+    """The oracle (numpy, fp64 products) on `tokens` tokens of the same layer:
+    W dequantized once beforehand, then forward + backward of every
+    projection, repeated until at least min_seconds of wall time."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import formats as ofmt, lora as olora
+    from quantized_base_lora_amd import synth
+    f32 = synth.bf16_bits_to_f32
+    prep = []
+    for pi, _ in enumerate(wl.projs):
+        c = synth.layer_tensors(wl, pi, m=tokens)
+        codes, scales = ofmt.pack(wl.fmt, c["W"])
+        wd = ofmt.dequant(wl.fmt, codes, scales)
+        prep.append((f32(c["x"]), f32(c["dY"]), wd, f32(c["A"]), f32(c["B"])))
+    passes, dt = 0, 0.0
+    while dt < min_seconds and passes < 50:
+        t0 = time.perf_counter()
+        for x, dy, wd, a, b in prep:
+            olora.forward(x, wd, a, b, wl.alpha)
+            olora.backward(x, dy, wd, a, b, wl.alpha)
+        dt += time.perf_counter() - t0
+        passes += 1
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": tokens * passes / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{tokens} tokens of the same layer (all {len(wl.projs)} projections, fwd+bwd, "
+                      f"fp64 products, W dequantized beforehand), {passes} passes in {dt:.2f} s wall; "
+                      f"BLAS threads {threads}, host cpus visible {len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from quantized_base_lora_amd import binding as B, synth
+
+    B.load()
+    wl = synth.WORKLOADS[args.workload]
+    m = args.m or wl.m
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def t(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # inputs, packed bases and preallocated outputs / workspaces
+    projs = []
+    packed_bytes = 0
+    for pi, p in enumerate(wl.projs):
+        c = synth.layer_tensors(wl, pi, m=m)
+        qw = B.quant_pack(wl.fmt, torch.from_numpy(c["W"]).to(dev))
+        packed_bytes += qw.nbytes()
+        d = {"p": p, "qws": [qw], "x": t(c["x"]), "dy": t(c["dY"]), "a": t(c["A"]), "b": t(c["B"]),
+             "y": torch.empty((m, p.n), dtype=torch.bfloat16, device=dev),
+             "u": torch.empty((m, wl.r), dtype=torch.float32, device=dev),
+             "dx": torch.empty((m, p.k), dtype=torch.bfloat16, device=dev),
+             "da": torch.empty((wl.r, p.k), dtype=torch.float32, device=dev),
+             "db": torch.empty((p.n, wl.r), dtype=torch.float32, device=dev),
+             "ws": torch.empty(max(256, B.workspace_bytes(B.OP_BWD, wl.fmt, p.n, p.k, m, wl.r)),
+                               dtype=torch.uint8, device=dev)}
+        projs.append(d)
+    # rotate packed copies so weight reads come from HBM, not the 256 MB MALL
+    copies = args.copies or max(1, min(8, int(np.ceil(512e6 / packed_bytes))))
+    for d in projs:
+        base = d["qws"][0]
+        for _ in range(copies - 1):
+            q2 = B.QWeight(base.fmt, base.n, base.k, base.codes.clone(), base.scales.clone())
+            d["qws"].append(q2)
+    torch.cuda.synchronize()
+
+    ev_pairs = []
+
+    def step(i, timed):
+        for d in projs:
+            qw = d["qws"][i % copies]
+            if timed:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            B.linear_fwd(qw, d["x"], d["a"], d["b"], wl.alpha, y=d["y"], u=d["u"], stream=stream)
+            if timed:
+                e1.record(stream)
+                ev_pairs.append((d["p"], e0, e1))
+        for d in reversed(projs):
+            qw = d["qws"][i % copies]
+            B.linear_bwd(qw, d["x"], d["dy"], d["u"], d["a"], d["b"], wl.alpha, dx=d["dx"], da=d["da"],
+                         db=d["db"], ws=d["ws"], stream=stream)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, True)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+
+    fwd_ms = sum(e0.elapsed_time(e1) for _, e0, e1 in ev_pairs)
+    fwd_flops = sum(fwd_kernel_flops(wl, p, m) for p, _, _ in ev_pairs)
+    n_launch = len(ev_pairs)
+    avg_launch_ms = fwd_ms / n_launch
+    achieved = fwd_flops / (fwd_ms / 1e3) / 1e12
+    traffic = traffic_from_profile(args.workload, m)
+
+    flops = layer_flops(wl, m)
+    nbytes = layer_bytes(wl, m)
+    out = {
+        "metric": METRIC,
+        "value": m / (ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.notes, "name": wl.name, "tokens": m, "base_format": FMT_NAME[wl.fmt],
+                   "rank": wl.r, "alpha": wl.alpha, "projections": [f"{p.name}:{p.k}->{p.n}" for p in wl.projs],
+                   "packed_copies_rotated": copies},
+        "layer": {"tflops": flops / (ms / 1e3) / 1e12, "frac_bf16_peak": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+                  "algorithmic_bytes": nbytes, "hbm_gbs": nbytes / (ms / 1e3) / 1e9,
+                  "frac_hbm_peak": nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS},
+        "roofline": {"kernel": "qgemm_kernel (forward: dequant GEMM + fused LoRA)", "bound": "mfma",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "avg_launch_us": avg_launch_ms * 1e3, "launches_timed": n_launch,
+                     "flops_per_launch_avg": fwd_flops / n_launch},
+    }
+    if m <= 64:
+        fwd_bytes = sum(BPW[wl.fmt] * p.n * p.k + m * 2 * (p.k + p.n) for p, _, _ in ev_pairs) / n_launch
+        gbs = fwd_bytes / (avg_launch_ms / 1e3) / 1e9
+        out["roofline"].update({"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": gbs / PEAK_HBM_GBS, "bytes_per_launch_avg": fwd_bytes})
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, min(args.cpu_tokens, m) if args.cpu_tokens else m)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,214 @@
+/*
+ * qlora.h -- C ABI of libqlora.so: the LoRA linear layer over a frozen,
+ * block-quantized base weight, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (Surogate README page, "LoRA & QLoRA" capability row:
+ * adapters over an FP8 / NF4 quantized base; Soup page, opening paragraph:
+ * the frozen base is read and never written; GGUF-recipe page, "How it
+ * works": the base stays compressed during computation and LoRA uses fast
+ * backward formulas):
+ *
+ *   forward   y  = x . deq(W)^T + s . (x . A^T) . B^T,     s = alpha / r
+ *   backward  dX = dY . deq(W) + s . (dY . B) . A
+ *             dA = s . (dY . B)^T . x
+ *             dB = s . dY^T . (x . A^T)
+ *
+ * Conventions for every call below.
+ *   - Shapes follow nn.Linear: W [N, K] (N = out_features, K = in_features),
+ *     x [M, K], y and dY [M, N], A [r, K], B [N, r], U = x.A^T [M, r].
+ *     All matrices are row-major and dense (row stride = number of columns).
+ *   - bf16 tensors are passed as uint16_t bit patterns; fp32 as float.
+ *   - "dev" pointers are device (HBM) pointers on the current HIP device;
+ *     "host" pointers are ordinary host memory.  The caller owns every
+ *     buffer; the library never allocates inside quant_pack, qlora_linear_fwd
+ *     or qlora_linear_bwd (scratch comes in through ws / ws_bytes).
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *     enqueue work and return; buffers must stay alive until the stream has
+ *     passed the work.  Argument errors are reported synchronously and
+ *     nothing is enqueued.  A device fault surfaces at the caller's next
+ *     synchronize and as QL_EHIP from the next library call.
+ *   - Device pointers must be 16-byte aligned; M, N, K >= 1 (M may be 0:
+ *     then nothing is launched), K and N multiples of the format's block
+ *     (64 for NF4, 32 otherwise), r in {8, 16, 32}.
+ *   - The quantized base is const: no call writes codes or scales.
+ *   - Results do not depend on pointer values, only on shapes and data
+ *     (fixed launch configuration and fixed reduction order per shape), so
+ *     two calls on equal inputs give bitwise equal outputs.
+ *   - Return value: QL_OK (0) or a negative QL_E* code; ql_last_error()
+ *     gives a message for the calling thread.
+ */
+#ifndef QLORA_H
+#define QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+#define QL_OK 0
+#define QL_EINVAL (-1)        /* bad argument: null, misaligned, shape      */
+#define QL_EUNSUPPORTED (-2)  /* valid but not implemented (format, rank)   */
+#define QL_EWORKSPACE (-3)    /* ws_bytes below qlora_workspace_bytes()     */
+#define QL_EHIP (-4)          /* a HIP runtime call failed                  */
+#define QL_ENONFINITE (-5)    /* quant_pack saw NaN or Inf in W             */
+#define QL_ESTATE (-6)        /* stream-pool misuse                         */
+#define QL_EOVERFLOW (-7)     /* quant_pack: a Q4_0 scale overflows fp16    */
+
+/* ---------------------------------------------------------------- formats
+ * 4-bit code layout (Q4_0 and NF4): codes are u8 [N, K/2]; each row is cut
+ * into groups of 32 consecutive elements stored in 16 bytes, byte j of a
+ * group holding element j in its low nibble and element j + 16 in its high
+ * nibble.  Scales are a separate array.
+ *
+ * QL_FMT_Q4_0      legacy-GGUF-style 4-bit blocks of 32 along K (the GGUF
+ *                  page's base format): scales fp16 [N, K/32],
+ *                  d = fp16(absmax / 7), code q = clamp(rint(w/d) + 8, 0, 15)
+ *                  (ties to even), value (q - 8) * d; a zero block stores 8.
+ * QL_FMT_NF4       NormalFloat-4 (QLoRA paper, "4-bit NormalFloat"; the NF4
+ *                  base named on the Surogate and Soup pages): blocks of 64
+ *                  along K, scales fp32 [N, K/64] = block absmax, code =
+ *                  nearest of 16 normal-quantile levels (a value equal to a
+ *                  decision threshold takes the lower code), value c[q] * a;
+ *                  a zero block stores 7.  No double quantization.
+ * QL_FMT_FP8_E4M3  OCP E4M3FN codes u8 [N, K] (the Surogate FP8 recipe's base
+ *                  format) with one fp32 scale s = absmax / 448; code =
+ *                  E4M3(w / s) nearest even, saturating; value E4M3(q) * s.
+ */
+#define QL_FMT_Q4_0 1
+#define QL_FMT_NF4 2
+#define QL_FMT_FP8_E4M3 3
+
+/* workspace query operations */
+#define QL_OP_PACK 0
+#define QL_OP_FWD 1
+#define QL_OP_BWD 2
+
+/* A packed, frozen base weight (all pointers dev, read-only). */
+typedef struct ql_qweight {
+  int32_t format;        /* QL_FMT_*                                        */
+  int32_t reserved;      /* must be 0                                       */
+  int64_t n_out;         /* N                                               */
+  int64_t k_in;          /* K                                               */
+  const uint8_t* codes;  /* Q4_0 / NF4: u8 [N, K/2]; FP8: u8 [N, K]         */
+  const void* scales;    /* Q4_0: fp16 [N, K/32]; NF4: fp32 [N, K/64];
+                            FP8: fp32 [1]                                    */
+} ql_qweight;
+
+/* ---------------------------------------------------------------- misc */
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* ql_last_error(void);
+
+/* Library ABI version (increments on any signature change). */
+int32_t ql_version(void);
+
+/* The library's NF4 levels (16 fp32, ascending, c[0] = -1, c[7] = 0,
+ * c[15] = 1), built on the host at load time from the normal-quantile
+ * construction.  out: host, 16 floats.  Needs no GPU. */
+int ql_nf4_levels(float* out);
+
+/* Bytes of scratch that op needs for these shapes (format, N, K, M, r).
+ * op = QL_OP_PACK ignores m and r.  Needs no GPU. */
+size_t qlora_workspace_bytes(int32_t op, int32_t format, int64_t n_out,
+                             int64_t k_in, int64_t m, int32_t r);
+
+/* ---------------------------------------------------------------- a0: pack
+ * Quantize fp32 W (dev [N, K]) into codes and scales (dev, layouts above).
+ * Once per weight, not per step.  Blocks until the packed data is written
+ * (so that non-finite input can be reported): returns QL_ENONFINITE if W
+ * holds NaN or Inf (codes and scales are then unspecified), QL_EOVERFLOW if
+ * a Q4_0 scale would exceed the fp16 range.  ws: dev scratch of at least
+ * qlora_workspace_bytes(QL_OP_PACK, ...) bytes. */
+int quant_pack(int32_t format, const float* w, int64_t n_out, int64_t k_in,
+               uint8_t* codes, void* scales, void* ws, size_t ws_bytes,
+               void* stream);
+
+/* Dequantize (for verification): out_f32 dev [N, K] gets the exact fp32
+ * values, out_bf16 dev [N, K] the one-rounding bf16 values the GEMMs feed to
+ * the matrix cores.  Either output may be NULL. */
+int qlora_dequant(const ql_qweight* w, float* out_f32, uint16_t* out_bf16,
+                  void* stream);
+
+/* ---------------------------------------------------------------- a1: FP8 activations
+ * Per-row two-term E4M3 split used by the FP8 base:
+ *   s_m = fl32(max|x_m| / 448), t = fl32(x / s_m), hi = E4M3(t),
+ *   lo = E4M3(fl32(fl32(t - hi) * 16)),  x ~= s_m (hi + lo / 16).
+ * x: dev bf16 [M, K]; hi, lo: dev u8 [M, K]; scale: dev fp32 [M]. */
+int ql_act_quant_e4m3(const uint16_t* x, int64_t m, int64_t k, uint8_t* hi,
+                      uint8_t* lo, float* scale, void* stream);
+
+/* ---------------------------------------------------------------- a2-a4: forward
+ * y (dev bf16 [M, N]) = x . deq(W)^T + s . U . B^T,  U = x . A^T saved to
+ * u_save (dev fp32 [M, r], required).  x: dev bf16 [M, K]; lora_a: dev bf16
+ * [r, K]; lora_b: dev bf16 [N, r]; s = alpha / r.  Accumulation is fp32.
+ * ws: dev scratch, at least qlora_workspace_bytes(QL_OP_FWD, ...) bytes. */
+int qlora_linear_fwd(const ql_qweight* w, const uint16_t* x, int64_t m,
+                     const uint16_t* lora_a, const uint16_t* lora_b, int32_t r,
+                     float alpha, uint16_t* y, float* u_save, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- a5-a9: backward
+ * Given dY (dev bf16 [M, N]), x and the forward's u_save:
+ *   dx  (dev bf16 [M, K], may be NULL to skip) = dY . deq(W) + s . V . A,
+ *   d_a (dev fp32 [r, K]) = s . V^T . x,   d_b (dev fp32 [N, r]) = s . dY^T . U,
+ * with V = dY . B.  accumulate = 0 overwrites d_a / d_b, 1 adds into them.
+ * The reductions over M use a fixed split and a fixed summation order.
+ * ws: dev scratch, at least qlora_workspace_bytes(QL_OP_BWD, ...) bytes. */
+int qlora_linear_bwd(const ql_qweight* w, const uint16_t* x, const uint16_t* dy,
+                     const float* u_save, int64_t m, const uint16_t* lora_a,
+                     const uint16_t* lora_b, int32_t r, float alpha,
+                     uint16_t* dx, float* d_a, float* d_b, int32_t accumulate,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- a10: layer stream
+ * Soup page, opening paragraph: the frozen base lives in host RAM and
+ * streams into a small pool of pre-allocated VRAM buffers one decoder layer
+ * at a time, prefetched one layer ahead on a dedicated stream.
+ *
+ * The caller allocates n_slots device buffers of slot_bytes each (slot_dev,
+ * 256-byte aligned) and n_layers pinned host images (layer_host, page-locked,
+ * layer_bytes[l] <= slot_bytes).  The pool owns only HIP events and
+ * bookkeeping; it never allocates device or host memory.  One pool serves
+ * one host thread.
+ *
+ * layer_stream_prefetch: make layer l resident in some slot.  A hit (l
+ *   already resident or in flight) enqueues nothing.  A miss picks an empty
+ *   slot, else the least recently released one, makes copy_stream wait until
+ *   the compute stream has released that slot, then enqueues the
+ *   host-to-device copy on copy_stream and records the slot's ready event.
+ *   QL_ESTATE if every slot holds a layer that is prefetched or acquired but
+ *   not yet released.
+ * ql_pool_acquire: compute_stream waits for layer l's ready event; *slot_dev
+ *   receives the slot's device address.  QL_ESTATE if l was not prefetched
+ *   or is already acquired.
+ * ql_pool_release: records on compute_stream that the slot's readers are
+ *   enqueued, so a later copy into it waits for them.  QL_ESTATE if l is not
+ *   acquired. */
+typedef struct ql_pool ql_pool;
+
+int ql_pool_create(ql_pool** pool, int32_t n_slots, void* const* slot_dev,
+                   size_t slot_bytes, int32_t n_layers,
+                   const void* const* layer_host, const size_t* layer_bytes);
+int layer_stream_prefetch(ql_pool* pool, int32_t layer, void* copy_stream);
+int ql_pool_acquire(ql_pool* pool, int32_t layer, void* compute_stream,
+                    void** slot_dev);
+int ql_pool_release(ql_pool* pool, int32_t layer, void* compute_stream);
+/* counters: out[0] prefetch hits, out[1] copies issued, out[2] bytes copied */
+int ql_pool_stats(const ql_pool* pool, int64_t* out3);
+/* Test hooks, host-forced conditions only: delay_us > 0 makes each copy wait
+ * that long on the copy stream before it starts (a host function on the
+ * stream); poison != 0 fills a slot with 0xFF bytes before each copy (every
+ * bf16/fp32 read of it is NaN); skip_wait != 0 makes acquire skip the
+ * compute-stream wait (a deliberate race, for a negative control only). */
+int ql_pool_debug(ql_pool* pool, int32_t delay_us, int32_t poison,
+                  int32_t skip_wait);
+int ql_pool_destroy(ql_pool* pool);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H */

@@ -60,16 +60,24 @@ def forward_merged(x, w, a, b, alpha, dtype=np.float64):
     return _f(x, dtype) @ (wf + s * (bf @ af)).T
 
 
+def adapter_grads(x, dy, a, b, alpha, dtype=np.float64):
+    """(dA, dB): dA = s.(dY.B)^T.x and dB = s.dY^T.(x.A^T); W does not enter."""
+    r = np.asarray(a).shape[0]
+    s = lora_scale(alpha, r)
+    xf, dyf, af, bf = (_f(t, dtype) for t in (x, dy, a, b))
+    u = xf @ af.T
+    v = dyf @ bf
+    return s * (v.T @ xf), s * (dyf.T @ u)
+
+
 def backward(x, dy, w, a, b, alpha, dtype=np.float64):
     """Returns (dX, dA, dB) for upstream gradient dY."""
     r = np.asarray(a).shape[0]
     s = lora_scale(alpha, r)
-    xf, dyf, wf, af, bf = (_f(t, dtype) for t in (x, dy, w, a, b))
-    u = xf @ af.T
+    dyf, wf, af, bf = (_f(t, dtype) for t in (dy, w, a, b))
     v = dyf @ bf
     dx = dyf @ wf + s * (v @ af)
-    da = s * (v.T @ xf)
-    db = s * (dyf.T @ u)
+    da, db = adapter_grads(x, dy, a, b, alpha, dtype)
     return dx, da, db
 
 

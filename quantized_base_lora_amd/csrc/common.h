@@ -1,0 +1,87 @@
+// Internal declarations shared by the library's translation units.
+// gfx950 (CDNA4) only: wave64, bf16 and fp8 MFMA, LDS transpose reads.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/qlora.h"
+
+namespace ql {
+
+// ----------------------------------------------------------------- vector types
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ----------------------------------------------------------------- NF4 levels
+// The 16 levels (fp32, ascending) and the 15 decision thresholds
+// m_i = fl32(fl32(c_i + c_{i+1}) * 0.5), built once on the host.
+struct Nf4Table {
+  float level[16];
+  float mid[15];
+};
+const Nf4Table& nf4_table();
+
+// ----------------------------------------------------------------- errors
+int set_error(int code, const char* fmt, ...);
+int hip_error(hipError_t e, const char* what);
+#define QL_HIP(call)                                   \
+  do {                                                 \
+    hipError_t e_ = (call);                            \
+    if (e_ != hipSuccess) return ::ql::hip_error(e_, #call); \
+  } while (0)
+
+// ----------------------------------------------------------------- launchers
+// All take already-validated arguments and enqueue on `stream`.
+
+// pack / dequant / activation split (kernels_pack.hip)
+hipError_t launch_pack_4bit(int fmt, const float* w, int64_t n, int64_t k,
+                            uint8_t* codes, void* scales, uint32_t* status,
+                            hipStream_t s);
+hipError_t launch_pack_fp8(const float* w, int64_t n, int64_t k, uint8_t* codes,
+                           float* scale, uint32_t* ws, hipStream_t s);
+hipError_t launch_dequant(const ql_qweight& w, float* out_f32, uint16_t* out_bf16,
+                          hipStream_t s);
+hipError_t launch_act_quant(const uint16_t* x, int64_t m, int64_t k, uint8_t* hi,
+                            uint8_t* lo, float* scale, hipStream_t s);
+hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t s);
+
+// fused base GEMM + LoRA (kernels_gemm.hip)
+struct GemmCall {
+  const ql_qweight* w;
+  bool trans;              // false: y = act . W^T (contract K); true: dX = act . W (contract N)
+  const uint16_t* act;     // [M, C] bf16, C = contraction length
+  int64_t m;
+  const uint16_t* down;    // [r, C] bf16: A (forward) or B^T (backward)
+  const uint16_t* up;      // forward: B [N, r]; backward: A [r, K]
+  int32_t r;
+  float s;                 // alpha / r
+  uint16_t* out;           // [M, O] bf16, O = output columns
+  float* save;             // [M, r] fp32 rank-r projection (U or V), may be null
+};
+hipError_t launch_qgemm(const GemmCall& c, hipStream_t s);
+
+// LoRA-side kernels (kernels_lora.hip)
+// bt[j][n] = b[n][j]
+hipError_t launch_transpose_rn(const uint16_t* b, int64_t n, int32_t r, uint16_t* bt,
+                               hipStream_t s);
+// out[m][j] = sum_c x[m][c] * p[j][c]     (fp32)
+hipError_t launch_down_proj(const uint16_t* x, int64_t m, int64_t c, const uint16_t* p,
+                            int32_t r, float* out, hipStream_t s);
+// part[q][p][j] = sum_{m in chunk q} x[m][p] * v[m][j]
+hipError_t launch_grad_partial(const uint16_t* x, int64_t m, int64_t pdim, const float* v,
+                               int32_t r, float* part, int32_t nparts, hipStream_t s);
+// final reduction of the partials, scaled by s, optional accumulate;
+// transpose_out: out[j][p] (dA) instead of out[p][j] (dB)
+hipError_t launch_grad_reduce(const float* part, int32_t nparts, int64_t pdim, int32_t r,
+                              float s, float* out, bool transpose_out, bool accumulate,
+                              hipStream_t st);
+int32_t grad_parts(int64_t m);
+
+}  // namespace ql

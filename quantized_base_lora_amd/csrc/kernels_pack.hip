@@ -1,0 +1,383 @@
+// a0 quant_pack, verification dequant, and a1 activation split for the FP8 base.
+//
+// Formats (see include/qlora.h): Q4_0-style blocks of 32 with an fp16 scale
+// absmax/7 and value (q-8)*d; NF4 blocks of 64 with an fp32 absmax and the
+// normal-quantile book (QLoRA paper, "4-bit NormalFloat"); per-tensor FP8
+// E4M3 with scale absmax/448 (the Surogate FP8 recipe's format).  Every
+// quantization decision is taken in IEEE fp32 with correctly rounded
+// division and ties-to-even rounding, so codes are reproducible bit for bit.
+//
+// Codecs are written out here from the format definitions (integer bit
+// manipulation): the hardware fp8 conversion does not saturate, and the fp16
+// one depends on the rounding mode register, so neither is used for packing.
+#include <algorithm>
+
+#include "common.h"
+
+namespace ql {
+namespace {
+
+constexpr int kThreads = 256;
+
+struct Mids { float m[15]; };
+struct Levels { float c[16]; };
+
+__device__ __forceinline__ float fdiv_rn(float a, float b) { return __fdiv_rn(a, b); }
+
+// fp32 -> IEEE binary16, nearest even; sets *ovf if the result is not finite.
+__device__ __forceinline__ uint16_t f32_to_f16(float f, bool* ovf) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t sign = (u >> 16) & 0x8000u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a >= 0x477FF000u) {            // >= 65520: rounds past 65504 (or Inf/NaN)
+    *ovf = true;
+    return (uint16_t)(sign | 0x7C00u);
+  }
+  if (a < 0x38800000u) {             // below 2^-14: subnormal grid of 2^-24
+    float m = rintf(__uint_as_float(a) * 16777216.0f);   // exact scaling, RNE
+    return (uint16_t)(sign | (uint32_t)m);               // 1024 encodes 2^-14 exactly
+  }
+  int e = (int)(a >> 23) - 127;                          // -14..15
+  uint32_t mant = (a & 0x7FFFFFu) | 0x800000u;           // 24 bits
+  uint32_t r = mant >> 13, rem = mant & 0x1FFFu;
+  if (rem > 0x1000u || (rem == 0x1000u && (r & 1u))) ++r;
+  if (r == 0x800u) { r = 0x400u; ++e; }
+  if (e > 15) { *ovf = true; return (uint16_t)(sign | 0x7C00u); }
+  return (uint16_t)(sign | ((uint32_t)(e + 15) << 10) | (r & 0x3FFu));
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  uint32_t e = (h >> 10) & 0x1F, m = h & 0x3FF;
+  float v = (e == 0) ? (float)m * 5.9604644775390625e-08f              // m * 2^-24
+                     : __uint_as_float(((e + 112u) << 23) | (m << 13)); // rebias 15 -> 127
+  return (h & 0x8000) ? -v : v;
+}
+
+// fp32 -> OCP E4M3FN, nearest even, saturating to +-448; NaN -> 0x7F; keeps sign of zero.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return 0x7Fu;
+  float af = __uint_as_float(a);
+  if (af >= 448.0f) return sign | 0x7Eu;
+  if (af < 0.015625f) {                                   // below 2^-6: grid of 2^-9
+    float m = rintf(af * 512.0f);                          // 0..8; 8 is the smallest normal
+    return sign | (uint32_t)m;
+  }
+  int e = (int)(a >> 23) - 127;                            // -6..8
+  uint32_t mant = (a & 0x7FFFFFu) | 0x800000u;
+  uint32_t r = mant >> 20, rem = mant & 0xFFFFFu;
+  if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
+  if (r == 16u) { r = 8u; ++e; }
+  return sign | ((uint32_t)(e + 7) << 3) | (r & 7u);
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t e = (c >> 3) & 0xF, m = c & 7;
+  float v = (e == 0) ? (float)m * 0.001953125f                           // m/8 * 2^-6
+                     : __uint_as_float(((e + 120u) << 23) | (m << 20));  // rebias 7 -> 127
+  if (e == 15 && m == 7) v = __uint_as_float(0x7FC00000u);
+  return (c & 0x80) ? -v : v;
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float v) {
+  __bf16 h = (__bf16)v;                                    // v_cvt_pk_bf16_f32, nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// ------------------------------------------------------------------ 4-bit pack
+// One thread per 32-element group of a row (16 output bytes).  For NF4 two
+// neighbouring threads share a 64-element block and exchange their maxima.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void pack4_kernel(const float* __restrict__ w, int64_t groups,
+                                                         uint8_t* __restrict__ codes,
+                                                         void* __restrict__ scales,
+                                                         uint32_t* __restrict__ status, Mids mids) {
+  int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  bool valid = gid < groups;
+  float v[32];
+  float amax = 0.0f;
+  bool bad = false;
+  if (valid) {
+    const float4* src = reinterpret_cast<const float4*>(w + gid * 32);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float4 t = src[i];
+      v[4 * i + 0] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      bad |= !isfinite(v[i]);
+      amax = fmaxf(amax, fabsf(v[i]));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+  }
+  if (FMT == QL_FMT_NF4) amax = fmaxf(amax, __shfl_xor(amax, 1));
+  uint32_t q[32];
+  bool ovf = false;
+  if (FMT == QL_FMT_Q4_0) {
+    uint16_t d16 = f32_to_f16(fdiv_rn(amax, 7.0f), &ovf);
+    float d = f16_to_f32(d16);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float t = (d == 0.0f) ? 0.0f : rintf(fdiv_rn(v[i], d));
+      t = fminf(fmaxf(t + 8.0f, 0.0f), 15.0f);
+      q[i] = (uint32_t)t;
+    }
+    if (valid) reinterpret_cast<uint16_t*>(scales)[gid] = d16;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      uint32_t c = 7;
+      if (amax != 0.0f) {
+        float t = fdiv_rn(v[i], amax);
+        c = 0;
+#pragma unroll
+        for (int j = 0; j < 15; ++j) c += (t > mids.m[j]) ? 1u : 0u;
+      }
+      q[i] = c;
+    }
+    if (valid && (gid & 1) == 0) reinterpret_cast<float*>(scales)[gid >> 1] = amax;
+  }
+  if (valid) {
+    uint32_t word[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      word[i] = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        int j = 4 * i + b;
+        word[i] |= (q[j] | (q[j + 16] << 4)) << (8 * b);
+      }
+    }
+    *reinterpret_cast<uint4*>(codes + gid * 16) = make_uint4(word[0], word[1], word[2], word[3]);
+    if (bad) atomicOr(status, 1u);
+    if (ovf) atomicOr(status, 2u);
+  }
+}
+
+// ------------------------------------------------------------------ FP8 pack
+__global__ __launch_bounds__(kThreads) void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t value) {
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) p[i] = value;
+}
+
+// ws[0] = bits of max|w| (non-negative floats order like their bits), ws[1] |= 1 on non-finite.
+__global__ __launch_bounds__(kThreads) void absmax_kernel(const float* __restrict__ w, int64_t n4,
+                                                          uint32_t* __restrict__ ws) {
+  float amax = 0.0f;
+  bool bad = false;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * kThreads) {
+    float4 t = reinterpret_cast<const float4*>(w)[i];
+    bad |= !(isfinite(t.x) && isfinite(t.y) && isfinite(t.z) && isfinite(t.w));
+    amax = fmaxf(fmaxf(amax, fabsf(t.x)), fmaxf(fabsf(t.y), fmaxf(fabsf(t.z), fabsf(t.w))));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  bad = __any(bad);
+  if ((threadIdx.x & 63) == 0) {
+    atomicMax(&ws[0], __float_as_uint(amax));
+    if (bad) atomicOr(&ws[1], 1u);
+  }
+}
+
+// 16 elements per thread -> 16 code bytes.
+__global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const float* __restrict__ w, int64_t n16,
+                                                             const uint32_t* __restrict__ ws,
+                                                             uint8_t* __restrict__ codes,
+                                                             float* __restrict__ scale) {
+  float s = fdiv_rn(__uint_as_float(ws[0]), 448.0f);
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i == 0) scale[0] = s;
+  if (i >= n16) return;
+  const float4* src = reinterpret_cast<const float4*>(w) + i * 4;
+  uint32_t word[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float4 t = src[j];
+    float e[4] = {t.x, t.y, t.z, t.w};
+    uint32_t wd = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      uint32_t c = (s == 0.0f) ? 0u : f32_to_e4m3(fdiv_rn(e[b], s));
+      wd |= c << (8 * b);
+    }
+    word[j] = wd;
+  }
+  reinterpret_cast<uint4*>(codes)[i] = make_uint4(word[0], word[1], word[2], word[3]);
+}
+
+// ------------------------------------------------------------------ dequant (verification)
+// One thread per 32 consecutive elements of a row.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __restrict__ codes,
+                                                           const void* __restrict__ scales,
+                                                           int64_t groups, int64_t k,
+                                                           float* __restrict__ out_f32,
+                                                           uint16_t* __restrict__ out_bf16,
+                                                           Levels lv) {
+  int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (gid >= groups) return;
+  float v[32];
+  if (FMT == QL_FMT_FP8_E4M3) {
+    float s = reinterpret_cast<const float*>(scales)[0];
+    const uint4* src = reinterpret_cast<const uint4*>(codes + gid * 32);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint4 t = src[h];
+      uint32_t wd[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[16 * h + i] = e4m3_to_f32((wd[i / 4] >> (8 * (i % 4))) & 0xFF) * s;
+    }
+  } else {
+    uint4 t = *reinterpret_cast<const uint4*>(codes + gid * 16);
+    uint32_t wd[4] = {t.x, t.y, t.z, t.w};
+    float d;
+    if (FMT == QL_FMT_Q4_0) d = f16_to_f32(reinterpret_cast<const uint16_t*>(scales)[gid]);
+    else d = reinterpret_cast<const float*>(scales)[gid >> 1];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      int j = e & 15, hi = e >> 4;
+      uint32_t q = (wd[j / 4] >> (8 * (j % 4) + 4 * hi)) & 0xF;
+      v[e] = (FMT == QL_FMT_Q4_0) ? ((float)q - 8.0f) * d : lv.c[q] * d;
+    }
+  }
+  (void)k;
+  if (out_f32) {
+    float4* dst = reinterpret_cast<float4*>(out_f32 + gid * 32);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+  }
+  if (out_bf16) {
+    uint32_t p[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = (uint32_t)bf16_bits(v[2 * i]) | ((uint32_t)bf16_bits(v[2 * i + 1]) << 16);
+    uint4* dst = reinterpret_cast<uint4*>(out_bf16 + gid * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = make_uint4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
+  }
+}
+
+// ------------------------------------------------------------------ a1: activation split
+// One workgroup per row: s = max|x| / 448, t = x / s, hi = E4M3(t),
+// lo = E4M3((t - hi) * 16).
+__global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t* __restrict__ x, int64_t k,
+                                                             uint8_t* __restrict__ hi,
+                                                             uint8_t* __restrict__ lo,
+                                                             float* __restrict__ scale) {
+  __shared__ float red[kThreads / 64];
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * k;
+  float amax = 0.0f;
+  for (int64_t c = (int64_t)threadIdx.x * 8; c < k; c += kThreads * 8) {
+    uint4 t = *reinterpret_cast<const uint4*>(xr + c);
+    uint32_t wd[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      amax = fmaxf(amax, fabsf(__uint_as_float(wd[i] << 16)));
+      amax = fmaxf(amax, fabsf(__uint_as_float(wd[i] & 0xFFFF0000u)));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = fdiv_rn(amax, 448.0f);
+  if (threadIdx.x == 0) scale[row] = s;
+  for (int64_t c = (int64_t)threadIdx.x * 8; c < k; c += kThreads * 8) {
+    uint4 t = *reinterpret_cast<const uint4*>(xr + c);
+    uint32_t wd[4] = {t.x, t.y, t.z, t.w};
+    uint32_t h2[2] = {0, 0}, l2[2] = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t bits = (i & 1) ? (wd[i / 2] & 0xFFFF0000u) : (wd[i / 2] << 16);
+      uint32_t ch = 0, cl = 0;
+      if (s != 0.0f) {
+        float tv = fdiv_rn(__uint_as_float(bits), s);
+        ch = f32_to_e4m3(tv);
+        float res = tv - e4m3_to_f32(ch);
+        cl = f32_to_e4m3(res * 16.0f);
+      }
+      h2[i / 4] |= ch << (8 * (i % 4));
+      l2[i / 4] |= cl << (8 * (i % 4));
+    }
+    *reinterpret_cast<uint2*>(hi + row * k + c) = make_uint2(h2[0], h2[1]);
+    *reinterpret_cast<uint2*>(lo + row * k + c) = make_uint2(l2[0], l2[1]);
+  }
+}
+
+inline unsigned grid_for(int64_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
+
+}  // namespace
+
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(n)), dim3(kThreads), 0, s, p, n, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s) { return launch_fill_u32(p, n, 0u, s); }
+
+hipError_t launch_pack_4bit(int fmt, const float* w, int64_t n, int64_t k, uint8_t* codes,
+                            void* scales, uint32_t* status, hipStream_t s) {
+  int64_t groups = n * (k / 32);
+  Mids mids{};
+  const Nf4Table& t = nf4_table();
+  for (int i = 0; i < 15; ++i) mids.m[i] = t.mid[i];
+  if (fmt == QL_FMT_Q4_0)
+    hipLaunchKernelGGL(pack4_kernel<QL_FMT_Q4_0>, dim3(grid_for(groups)), dim3(kThreads), 0, s, w,
+                       groups, codes, scales, status, mids);
+  else
+    hipLaunchKernelGGL(pack4_kernel<QL_FMT_NF4>, dim3(grid_for(groups)), dim3(kThreads), 0, s, w,
+                       groups, codes, scales, status, mids);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_fp8(const float* w, int64_t n, int64_t k, uint8_t* codes, float* scale,
+                           uint32_t* ws, hipStream_t s) {
+  int64_t total = n * k;   // multiple of 16 (validated)
+  hipError_t e = launch_zero_u32(ws, 2, s);
+  if (e != hipSuccess) return e;
+  int64_t n4 = total / 4;
+  unsigned blocks = (unsigned)std::min<int64_t>(grid_for(n4), 4096);
+  hipLaunchKernelGGL(absmax_kernel, dim3(blocks), dim3(kThreads), 0, s, w, n4, ws);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  int64_t n16 = total / 16;
+  hipLaunchKernelGGL(quant_fp8_kernel, dim3(grid_for(n16)), dim3(kThreads), 0, s, w, n16, ws, codes,
+                     scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const ql_qweight& w, float* out_f32, uint16_t* out_bf16, hipStream_t s) {
+  int64_t groups = w.n_out * (w.k_in / 32);
+  Levels lv{};
+  const Nf4Table& t = nf4_table();
+  for (int i = 0; i < 16; ++i) lv.c[i] = t.level[i];
+  switch (w.format) {
+    case QL_FMT_Q4_0:
+      hipLaunchKernelGGL(dequant_kernel<QL_FMT_Q4_0>, dim3(grid_for(groups)), dim3(kThreads), 0, s,
+                         w.codes, w.scales, groups, w.k_in, out_f32, out_bf16, lv);
+      break;
+    case QL_FMT_NF4:
+      hipLaunchKernelGGL(dequant_kernel<QL_FMT_NF4>, dim3(grid_for(groups)), dim3(kThreads), 0, s,
+                         w.codes, w.scales, groups, w.k_in, out_f32, out_bf16, lv);
+      break;
+    default:
+      hipLaunchKernelGGL(dequant_kernel<QL_FMT_FP8_E4M3>, dim3(grid_for(groups)), dim3(kThreads), 0,
+                         s, w.codes, w.scales, groups, w.k_in, out_f32, out_bf16, lv);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_act_quant(const uint16_t* x, int64_t m, int64_t k, uint8_t* hi, uint8_t* lo,
+                            float* scale, hipStream_t s) {
+  hipLaunchKernelGGL(act_quant_kernel, dim3((unsigned)m), dim3(kThreads), 0, s, x, k, hi, lo, scale);
+  return hipGetLastError();
+}
+
+}  // namespace ql

@@ -1,0 +1,117 @@
+"""A stack of decoder layers whose frozen bases are either resident in VRAM or
+streamed from pinned host memory through the library's slot pool, one layer
+ahead on a side stream (Soup page, opening paragraph).
+
+Host orchestration only: every byte moves through the library (the pool's
+copies) and every arithmetic step runs in its kernels.  Each layer's packed
+projections are laid out in one contiguous image (codes then scales per
+projection, each at a 256-byte aligned offset), so a layer moves with one
+copy and the kernels see the same layout wherever the image lives.
+"""
+
+import torch
+
+from . import binding as B
+
+ALIGN = 256
+
+
+def _up(v):
+    return (v + ALIGN - 1) // ALIGN * ALIGN
+
+
+def _sizes(fmt, n, k):
+    if fmt == B.FMT_FP8:
+        return n * k, 4
+    if fmt == B.FMT_Q4_0:
+        return n * k // 2, n * (k // 32) * 2
+    return n * k // 2, n * (k // 64) * 4
+
+
+class LayerLayout:
+    """Offsets of each projection's codes and scales inside a layer image."""
+
+    def __init__(self, fmt, projs):
+        self.fmt = fmt
+        self.projs = [(int(p.n), int(p.k)) for p in projs]
+        self.offsets = []
+        off = 0
+        for n, k in self.projs:
+            cb, sb = _sizes(fmt, n, k)
+            co = off
+            off = _up(off + cb)
+            so = off
+            off = _up(off + sb)
+            self.offsets.append((co, cb, so, sb))
+        self.nbytes = off
+
+    def weights_at(self, base_ptr, keepalive=None):
+        """QWeight views of every projection for an image at device address base_ptr."""
+        return [B.QWeight.view(self.fmt, n, k, base_ptr + co, base_ptr + so, keepalive)
+                for (n, k), (co, _, so, _) in zip(self.projs, self.offsets)]
+
+    def image_from(self, qweights, device="cuda"):
+        """Device image holding the given packed weights at this layout's offsets."""
+        img = torch.zeros(self.nbytes, dtype=torch.uint8, device=device)
+        for qw, (co, cb, so, sb) in zip(qweights, self.offsets):
+            img[co:co + cb].copy_(qw.codes.reshape(-1).view(torch.uint8))
+            img[so:so + sb].copy_(qw.scales.reshape(-1).view(torch.uint8))
+        return img
+
+
+class Stack:
+    """fwd over layers 0..L-1 then bwd over L-1..0, every layer's 7 (or fewer)
+    projections with their own activations and adapters."""
+
+    def __init__(self, layout, r, alpha, images_dev=None, images_host=None, n_slots=2):
+        self.layout, self.r, self.alpha = layout, r, alpha
+        self.resident = images_dev is not None
+        if self.resident:
+            self.images = images_dev
+            self.n_layers = len(images_dev)
+            self.views = [layout.weights_at(img.data_ptr(), img) for img in images_dev]
+        else:
+            self.images = images_host
+            self.n_layers = len(images_host)
+            self.slots = [torch.empty(layout.nbytes, dtype=torch.uint8, device="cuda") for _ in range(n_slots)]
+            self.pool = B.Pool(self.slots, images_host)
+            self.copy_stream = torch.cuda.Stream()
+
+    def _weights(self, layer):
+        if self.resident:
+            return self.views[layer]
+        ptr = self.pool.acquire(layer)
+        return self.layout.weights_at(ptr, self.slots)
+
+    def _done(self, layer):
+        if not self.resident:
+            self.pool.release(layer)
+
+    def _ahead(self, layer):
+        if not self.resident and 0 <= layer < self.n_layers:
+            self.pool.prefetch(layer, self.copy_stream)
+
+    def run(self, acts, outs):
+        """acts[l][p] = dict(x, dy, a, b) device tensors; outs[l][p] = dict of
+        preallocated y, u, dx, da, db and ws tensors, written in place."""
+        L = self.n_layers
+        self._ahead(0)
+        for l in range(L):
+            self._ahead(l + 1)
+            ws = self._weights(l)
+            for p, qw in enumerate(ws):
+                a, o = acts[l][p], outs[l][p]
+                B.linear_fwd(qw, a["x"], a["a"], a["b"], self.alpha, y=o["y"], u=o["u"])
+            self._done(l)
+        for l in reversed(range(L)):
+            self._ahead(l - 1)
+            ws = self._weights(l)
+            for p, qw in enumerate(ws):
+                a, o = acts[l][p], outs[l][p]
+                B.linear_bwd(qw, a["x"], a["dy"], o["u"], a["a"], a["b"], self.alpha,
+                             dx=o["dx"], da=o["da"], db=o["db"], ws=o["ws"])
+            self._done(l)
+
+    def close(self):
+        if not self.resident:
+            self.pool.close()

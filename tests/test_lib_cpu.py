@@ -1,0 +1,114 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, agrees with the oracle on the NF4 levels, and rejects bad arguments
+synchronously with the documented codes (nothing is launched)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import formats as ofmt
+from quantized_base_lora_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load()
+
+
+def test_header_lists_the_four_named_calls():
+    names = declared_functions()
+    for n in ("quant_pack", "qlora_linear_fwd", "qlora_linear_bwd", "layer_stream_prefetch"):
+        assert n in names
+    assert len(names) >= 16
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(binding.EXPORTS) <= set(declared_functions())
+
+
+def test_version(lib):
+    assert binding.version() == 1
+
+
+def test_nf4_levels_equal_oracle_bitwise():
+    ours = np.array(binding.nf4_levels(), dtype=np.float32)
+    assert np.array_equal(ours.view(np.uint32), ofmt.nf4_codebook().view(np.uint32))
+
+
+def test_workspace_query(lib):
+    assert binding.workspace_bytes(binding.OP_PACK, binding.FMT_NF4, 64, 64) >= 8
+    a = binding.workspace_bytes(binding.OP_BWD, binding.FMT_NF4, 1024, 2048, 1000, 16)
+    b = binding.workspace_bytes(binding.OP_BWD, binding.FMT_NF4, 1024, 2048, 8192, 16)
+    assert b > a >= 16 * 1024 * 2 + 1000 * 16 * 4
+    assert a % 256 == 0 and b % 256 == 0
+
+
+FAKE = ctypes.c_void_p(0x10000)       # aligned, never dereferenced: calls fail before any launch
+
+
+def _qw(fmt=binding.FMT_NF4, n=64, k=128, reserved=0, codes=FAKE.value, scales=FAKE.value):
+    return binding.QWeightC(fmt, reserved, n, k, codes, scales)
+
+
+def _err(lib):
+    return lib.ql_last_error().decode()
+
+
+def test_pack_argument_errors(lib):
+    P = FAKE
+    assert lib.quant_pack(9, P, 64, 128, P, P, P, 256, None) == binding.QL_EUNSUPPORTED
+    assert lib.quant_pack(binding.FMT_NF4, P, 64, 96, P, P, P, 256, None) == binding.QL_EINVAL
+    assert "multiple of 64" in _err(lib)
+    assert lib.quant_pack(binding.FMT_Q4_0, P, 48, 64, P, P, P, 256, None) == binding.QL_EINVAL
+    assert lib.quant_pack(binding.FMT_Q4_0, None, 64, 64, P, P, P, 256, None) == binding.QL_EINVAL
+    assert lib.quant_pack(binding.FMT_Q4_0, ctypes.c_void_p(0x10004), 64, 64, P, P, P, 256, None) == binding.QL_EINVAL
+    assert lib.quant_pack(binding.FMT_FP8, P, 64, 64, P, P, P, 8, None) == binding.QL_EWORKSPACE
+
+
+def test_layer_argument_errors(lib):
+    P = FAKE
+    qw = _qw()
+    fwd = lib.qlora_linear_fwd
+    assert fwd(ctypes.byref(qw), P, 16, P, P, 12, 16.0, P, P, None, 0, None) == binding.QL_EUNSUPPORTED
+    assert fwd(ctypes.byref(qw), None, 16, P, P, 16, 16.0, P, P, None, 0, None) == binding.QL_EINVAL
+    assert fwd(ctypes.byref(qw), P, -1, P, P, 16, 16.0, P, P, None, 0, None) == binding.QL_EINVAL
+    assert fwd(ctypes.byref(qw), P, 0, P, P, 16, 16.0, P, P, None, 0, None) == binding.QL_OK
+    bad = _qw(reserved=1)
+    assert fwd(ctypes.byref(bad), P, 16, P, P, 16, 16.0, P, P, None, 0, None) == binding.QL_EINVAL
+    bad = _qw(codes=0x10008)
+    assert fwd(ctypes.byref(bad), P, 16, P, P, 16, 16.0, P, P, None, 0, None) == binding.QL_EINVAL
+    bwd = lib.qlora_linear_bwd
+    assert bwd(ctypes.byref(qw), P, P, P, 1024, P, P, 16, 16.0, P, P, P, 0, P, 0, None) == binding.QL_EWORKSPACE
+    assert bwd(ctypes.byref(qw), P, P, None, 1024, P, P, 16, 16.0, P, P, P, 0, P, 1 << 30, None) == binding.QL_EINVAL
+    assert lib.qlora_dequant(None, P, P, None) == binding.QL_EINVAL
+    assert lib.ql_act_quant_e4m3(P, 4, 24, P, P, P, None) == binding.QL_EINVAL
+
+
+def test_pool_argument_errors(lib):
+    h = ctypes.c_void_p()
+    slots = (ctypes.c_void_p * 2)(0x10000, 0x10100)
+    hosts = (ctypes.c_void_p * 3)(0x20000, 0x30000, 0x40000)
+    sizes = (ctypes.c_size_t * 3)(100, 100, 5000)
+    assert lib.ql_pool_create(ctypes.byref(h), 0, slots, 4096, 3, hosts, sizes) == binding.QL_EINVAL
+    assert lib.ql_pool_create(ctypes.byref(h), 2, slots, 4096, 3, hosts, sizes) == binding.QL_EINVAL
+    assert "exceeds slot size" in _err(lib)
+    odd = (ctypes.c_void_p * 2)(0x10000, 0x10010)
+    sizes_ok = (ctypes.c_size_t * 3)(100, 100, 100)
+    assert lib.ql_pool_create(ctypes.byref(h), 2, odd, 4096, 3, hosts, sizes_ok) == binding.QL_EINVAL
+    assert lib.layer_stream_prefetch(None, 0, None) == binding.QL_EINVAL
+    assert lib.ql_pool_destroy(None) == binding.QL_OK
