@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="tokens in the CPU oracle sample (0: all)")
     ap.add_argument("--copies", type=int, default=0, help="packed weight copies rotated per step (0: auto)")
+    ap.add_argument("--proj", default=None, help="run only this projection (profiling)")
+    ap.add_argument("--phase", default="both", choices=["both", "fwd", "bwd"], help="profiling: one pass only")
     return ap.parse_args()
 
 
@@ -134,6 +136,8 @@ def main():
     projs = []
     packed_bytes = 0
     for pi, p in enumerate(wl.projs):
+        if args.proj and p.name != args.proj:
+            continue
         c = synth.layer_tensors(wl, pi, m=m)
         qw = B.quant_pack(wl.fmt, torch.from_numpy(c["W"]).to(dev))
         packed_bytes += qw.nbytes()
@@ -158,7 +162,7 @@ def main():
     ev_pairs = []
 
     def step(i, timed):
-        for d in projs:
+        for d in (projs if args.phase != "bwd" else []):
             qw = d["qws"][i % copies]
             if timed:
                 e0 = torch.cuda.Event(enable_timing=True)
@@ -168,7 +172,7 @@ def main():
             if timed:
                 e1.record(stream)
                 ev_pairs.append((d["p"], e0, e1))
-        for d in reversed(projs):
+        for d in (reversed(projs) if args.phase != "fwd" else []):
             qw = d["qws"][i % copies]
             B.linear_bwd(qw, d["x"], d["dy"], d["u"], d["a"], d["b"], wl.alpha, dx=d["dx"], da=d["da"],
                          db=d["db"], ws=d["ws"], stream=stream)
@@ -187,7 +191,8 @@ def main():
 
     fwd_ms = sum(e0.elapsed_time(e1) for _, e0, e1 in ev_pairs)
     fwd_flops = sum(fwd_kernel_flops(wl, p, m) for p, _, _ in ev_pairs)
-    n_launch = len(ev_pairs)
+    n_launch = max(1, len(ev_pairs))
+    fwd_ms = fwd_ms or float("nan")
     avg_launch_ms = fwd_ms / n_launch
     achieved = fwd_flops / (fwd_ms / 1e3) / 1e12
     traffic = traffic_from_profile(args.workload, m)

@@ -63,17 +63,16 @@ int check_rank(int32_t r) {
   return QL_OK;
 }
 
-// backward workspace: B^T [r, N] bf16 | V [M, r] fp32 | partials for dA [P, K, r] | dB [P, N, r]
+// backward workspace: V [M, r] fp32 | partials for dA [P, K, r] | for dB [P, N, r]
 struct BwdLayout {
-  size_t bt, v, pa, pb, total;
+  size_t v, pa, pb, total;
   int32_t parts;
 };
 
 BwdLayout bwd_layout(int64_t n, int64_t k, int64_t m, int32_t r) {
   BwdLayout l{};
   l.parts = grad_parts(m);
-  l.bt = 0;
-  l.v = l.bt + up((size_t)r * n * 2);
+  l.v = 0;
   l.pa = l.v + up((size_t)m * r * 4);
   l.pb = l.pa + up((size_t)l.parts * k * r * 4);
   l.total = l.pb + up((size_t)l.parts * n * r * 4);
@@ -198,7 +197,8 @@ int qlora_linear_bwd(const ql_qweight* w, const uint16_t* x, const uint16_t* dy,
   int rc;
   if ((rc = check_weight(w)) || (rc = check_rank(r))) return rc;
   if (m < 0) return set_error(QL_EINVAL, "m < 0");
-  if (!x || !dy || !u_save || !lora_a || !lora_b || !d_a || !d_b || !ws)
+  // with m == 0 the token-dimension buffers may be empty (null); dA and dB are still written
+  if ((m > 0 && (!x || !dy || !u_save)) || !lora_a || !lora_b || !d_a || !d_b || !ws)
     return set_error(QL_EINVAL, "null pointer");
   if (!aligned16(x) || !aligned16(dy) || !aligned16(u_save) || !aligned16(lora_a) || !aligned16(lora_b) ||
       (dx && !aligned16(dx)) || !aligned16(d_a) || !aligned16(d_b) || !aligned16(ws))
@@ -209,35 +209,46 @@ int qlora_linear_bwd(const ql_qweight* w, const uint16_t* x, const uint16_t* dy,
   if ((rc = check_sticky())) return rc;
   hipStream_t s = as_stream(stream);
   char* base = reinterpret_cast<char*>(ws);
-  uint16_t* bt = reinterpret_cast<uint16_t*>(base + L.bt);
   float* v = reinterpret_cast<float*>(base + L.v);
   float* pa = reinterpret_cast<float*>(base + L.pa);
   float* pb = reinterpret_cast<float*>(base + L.pb);
   const float sc = alpha / (float)r;
-  hipError_t e = launch_transpose_rn(lora_b, n, r, bt, s);
-  if (e == hipSuccess && m > 0) {
-    if (dx) {
-      GemmCall c{};
-      c.w = w;
-      c.trans = true;
-      c.act = dy;
-      c.m = m;
-      c.down = bt;
-      c.up = lora_a;
-      c.r = r;
-      c.s = sc;
-      c.out = dx;
-      c.save = v;
-      e = launch_qgemm(c, s);
-    } else {
-      e = launch_down_proj(dy, m, n, bt, r, v, s);
-    }
+  hipError_t e = hipSuccess;
+  if (m > 0 && dx) {
+    GemmCall c{};
+    c.w = w;
+    c.trans = true;
+    c.act = dy;
+    c.m = m;
+    c.down = lora_b;
+    c.up = lora_a;
+    c.r = r;
+    c.s = sc;
+    c.out = dx;
+    c.save = v;
+    e = launch_qgemm(c, s);
+  } else if (m > 0) {
+    e = launch_down_proj(dy, m, n, lora_b, r, v, s);
   }
-  const int32_t parts = m > 0 ? L.parts : 0;
-  if (e == hipSuccess && parts > 0) e = launch_grad_partial(x, m, k, v, r, pa, parts, s);
-  if (e == hipSuccess && parts > 0) e = launch_grad_partial(dy, m, n, u_save, r, pb, parts, s);
-  if (e == hipSuccess) e = launch_grad_reduce(pa, parts, k, r, sc, d_a, true, accumulate != 0, s);
-  if (e == hipSuccess) e = launch_grad_reduce(pb, parts, n, r, sc, d_b, false, accumulate != 0, s);
+  if (e == hipSuccess) {
+    GradLaunch g{};
+    g.x = x;
+    g.dy = dy;
+    g.v = v;
+    g.u = u_save;
+    g.d_a = d_a;
+    g.d_b = d_b;
+    g.part_a = pa;
+    g.part_b = pb;
+    g.m = m;
+    g.k = k;
+    g.n = n;
+    g.r = r;
+    g.nparts = L.parts;
+    g.s = sc;
+    g.accumulate = accumulate != 0;
+    e = launch_grads(g, s);
+  }
   if (e != hipSuccess) return hip_error(e, "backward launch");
   return QL_OK;
 }

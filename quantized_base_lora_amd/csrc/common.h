@@ -18,6 +18,18 @@ typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+// ----------------------------------------------------------------- barriers
+// Workgroup barrier for LDS hand-offs only.  __syncthreads() is a release /
+// acquire fence at workgroup scope, which on gfx9 waits for every outstanding
+// vector-memory operation, loads included (vmcnt covers both), and so would
+// drain the prefetches of later tiles at every step.  Here only this wave's
+// LDS operations are completed before the barrier; global loads stay in
+// flight.  The memory clobber keeps the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ----------------------------------------------------------------- NF4 levels
 // The 16 levels (fp32, ascending) and the 15 decision thresholds
 // m_i = fl32(fl32(c_i + c_{i+1}) * 0.5), built once on the host.
@@ -58,30 +70,38 @@ struct GemmCall {
   bool trans;              // false: y = act . W^T (contract K); true: dX = act . W (contract N)
   const uint16_t* act;     // [M, C] bf16, C = contraction length
   int64_t m;
-  const uint16_t* down;    // [r, C] bf16: A (forward) or B^T (backward)
+  const uint16_t* down;    // forward: A [r, K]; backward: B [N, r]
   const uint16_t* up;      // forward: B [N, r]; backward: A [r, K]
   int32_t r;
   float s;                 // alpha / r
   uint16_t* out;           // [M, O] bf16, O = output columns
   float* save;             // [M, r] fp32 rank-r projection (U or V), may be null
+  uint32_t* zero_ptr;      // optional: words zeroed by the kernel (counters of a later launch)
+  int32_t zero_n;
 };
 hipError_t launch_qgemm(const GemmCall& c, hipStream_t s);
 
 // LoRA-side kernels (kernels_lora.hip)
-// bt[j][n] = b[n][j]
-hipError_t launch_transpose_rn(const uint16_t* b, int64_t n, int32_t r, uint16_t* bt,
-                               hipStream_t s);
-// out[m][j] = sum_c x[m][c] * p[j][c]     (fp32)
-hipError_t launch_down_proj(const uint16_t* x, int64_t m, int64_t c, const uint16_t* p,
+// out[m][j] = sum_c x[m][c] * b[c][j]     (fp32), b is [C, r]
+hipError_t launch_down_proj(const uint16_t* x, int64_t m, int64_t c, const uint16_t* b,
                             int32_t r, float* out, hipStream_t s);
-// part[q][p][j] = sum_{m in chunk q} x[m][p] * v[m][j]
-hipError_t launch_grad_partial(const uint16_t* x, int64_t m, int64_t pdim, const float* v,
-                               int32_t r, float* part, int32_t nparts, hipStream_t s);
-// final reduction of the partials, scaled by s, optional accumulate;
-// transpose_out: out[j][p] (dA) instead of out[p][j] (dB)
-hipError_t launch_grad_reduce(const float* part, int32_t nparts, int64_t pdim, int32_t r,
-                              float s, float* out, bool transpose_out, bool accumulate,
-                              hipStream_t st);
+// dA = s V^T x and dB = s dY^T U: one launch for both partial sums, one to reduce them in fixed order
+struct GradLaunch {
+  const uint16_t* x;       // [M, K]
+  const uint16_t* dy;      // [M, N]
+  const float* v;          // [M, r]
+  const float* u;          // [M, r]
+  float* d_a;              // [r, K]
+  float* d_b;              // [N, r]
+  float* part_a;           // [P, K, r]
+  float* part_b;           // [P, N, r]
+  int64_t m, k, n;
+  int32_t r, nparts;
+  float s;
+  int32_t accumulate;
+};
+hipError_t launch_grads(const GradLaunch& g, hipStream_t s);
 int32_t grad_parts(int64_t m);
+int64_t grad_tiles(int64_t pdim);
 
 }  // namespace ql

@@ -3,37 +3,182 @@
 //   dA = s . V^T . x   [r, K]      dB = s . dY^T . U   [N, r]
 //
 // Both have the form out[p][j] = s . sum_m X[m][p] . Q[m][j] with X a bf16
-// activation ([M, K] or [M, N]) and Q an fp32 rank-r projection ([M, r]).
-// grad_partial computes per-partition sums on 16x16x32 bf16 MFMAs: X tiles
-// sit in LDS as [m][p] and reach the MFMA A operand through LDS transpose
-// reads; Q is split into a high and a low bf16 term (about 16 bits kept) and
-// read the same way.  The M range is cut into a fixed number of partitions
-// and grad_reduce adds the partials in partition order, so the result does
-// not depend on scheduling (no float atomics).
+// activation ([M, K] or [M, N]) and Q an fp32 rank-r projection ([M, r]);
+// one launch serves both (blockIdx.z).  A workgroup owns 64 columns p and one
+// of P fixed partitions of M; it streams its rows through LDS in steps of
+// 64 (loads running three steps ahead) and accumulates on 16x16x32 bf16
+// MFMAs, with X reaching the A operand through LDS transpose reads and Q
+// split into a high and a low bf16 term (about 16 bits kept).  Each
+// workgroup writes its partial sums; a second launch adds the P partials in
+// partition order, so the sum order is fixed per shape and the result
+// bitwise reproducible (no float atomics).  The hand-off between the two is
+// a kernel boundary: an in-kernel "last workgroup reduces" scheme would need
+// an agent-scope fence per workgroup, which on a multi-XCD part writes back
+// and invalidates the XCD's L2 each time.
 #include "common.h"
 
 namespace ql {
 namespace {
 
 constexpr int NT = 256;
-constexpr int TP = 128;         // p columns per workgroup
+constexpr int TP = 64;          // p columns per workgroup (16 per wave)
 constexpr int TMC = 64;         // m rows per step
-constexpr int SX = TP + 32;     // X tile stride (bf16)
+constexpr int SX = TP + 32;     // X tile stride (bf16): 192 B rows
 constexpr int SQ = 32 + 16;     // Q tile stride (bf16), up to 32 columns
+constexpr int CHUNK = 512;      // rows per partition
 
-__global__ __launch_bounds__(NT) void transpose_rn_kernel(const uint16_t* __restrict__ b, int64_t n,
-                                                          int r, uint16_t* __restrict__ bt) {
-  int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
-  if (i >= n * r) return;
-  int64_t row = i / r;
-  int j = (int)(i % r);
-  bt[(int64_t)j * n + row] = b[i];
+struct GradProb {
+  const uint16_t* x;
+  const float* q;
+  float* out;
+  float* part;
+  int64_t pdim;
+  int32_t transpose_out;
+};
+
+struct GradArgs {
+  GradProb prob[2];
+  int64_t m;
+  int64_t chunk;
+  int32_t nparts;
+  float s;
+  int32_t accumulate;
+  int32_t r;
+};
+
+template <int R>
+__global__ __launch_bounds__(NT) void grad_kernel(GradArgs a) {
+  constexpr int RB = (R + 15) / 16;
+  constexpr int QPT = R / 4;                         // Q floats per thread per step
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[TMC * SX];
+  __shared__ __attribute__((aligned(16))) uint16_t Qh[TMC * SQ];
+  __shared__ __attribute__((aligned(16))) uint16_t Ql[TMC * SQ];
+
+  const GradProb& pr = a.prob[blockIdx.z];
+  const int64_t p0 = (int64_t)blockIdx.x * TP;
+  if (p0 >= pr.pdim) return;                         // whole workgroup: this problem is narrower
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t mq0 = (int64_t)blockIdx.y * a.chunk;
+  const int64_t mq1 = mq0 + a.chunk < a.m ? mq0 + a.chunk : a.m;
+
+  for (int i = tid; i < TMC * SQ; i += NT) { Qh[i] = 0; Ql[i] = 0; }
+
+  f32x4 acc[RB];
+#pragma unroll
+  for (int jb = 0; jb < RB; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int xr = tid >> 3, xc = (tid & 7) * 8;       // X: rows xr, xr + 32; 8 columns
+  const int qr = tid >> 2, qc = (tid & 3) * QPT;
+
+  // loads run DEPTH - 1 steps ahead of the LDS stores (a ring of register sets)
+  constexpr int DEPTH = 4;
+  uint4 xv[DEPTH][2];
+  float qv[DEPTH][QPT];
+  auto load = [&](int slot, int64_t mc) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int64_t row = mc + xr + 32 * i, col = p0 + xc;
+      const bool ok = row < mq1 && col < pr.pdim;
+      row = row < mq1 ? row : mq1 - 1;
+      col = col < pr.pdim ? col : pr.pdim - 8;
+      const uint4 v = *reinterpret_cast<const uint4*>(pr.x + row * pr.pdim + col);
+      xv[slot][i] = ok ? v : make_uint4(0, 0, 0, 0);
+    }
+    int64_t row = mc + qr;
+    const bool ok = row < mq1;
+    row = row < mq1 ? row : mq1 - 1;
+    const float* qs = pr.q + row * R + qc;
+#pragma unroll
+    for (int t = 0; t < QPT; ++t) qv[slot][t] = ok ? qs[t] : 0.0f;
+  };
+
+#pragma unroll
+  for (int u = 0; u < DEPTH - 1; ++u)
+    if (mq0 + u * TMC < mq1) load(u, mq0 + u * TMC);
+  for (int64_t base = mq0; base < mq1; base += DEPTH * TMC) {
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u) {
+      const int64_t mc = base + u * TMC;
+      if (mc >= mq1) break;
+      const int64_t ahead = mc + (DEPTH - 1) * TMC;
+      if (ahead < mq1) load((u + DEPTH - 1) % DEPTH, ahead);
+      lds_barrier();                                  // previous step's readers are done
+#pragma unroll
+      for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(Xs + (xr + 32 * i) * SX + xc) = xv[u][i];
+#pragma unroll
+      for (int t = 0; t < QPT; ++t) {
+        const __bf16 h = (__bf16)qv[u][t];
+        const __bf16 l = (__bf16)(qv[u][t] - (float)h);
+        Qh[qr * SQ + qc + t] = __builtin_bit_cast(uint16_t, h);
+        Ql[qr * SQ + qc + t] = __builtin_bit_cast(uint16_t, l);
+      }
+      lds_barrier();
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp) {
+        const int b = lane >> 4, sl = lane & 15;
+        const int rbase = 32 * kp + 8 * b + (sl >> 2);
+        typedef short s16x8 __attribute__((ext_vector_type(8)));
+        const int xcol = 16 * wave + 4 * (sl & 3);
+        s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Xs + rbase * SX + xcol));
+        s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Xs + (rbase + 4) * SX + xcol));
+        s16x8 tx = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        const bf16x8 af = __builtin_bit_cast(bf16x8, tx);
+#pragma unroll
+        for (int jb = 0; jb < RB; ++jb) {
+          const int col = 16 * jb + 4 * (sl & 3);
+          s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Qh + rbase * SQ + col));
+          s16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Qh + (rbase + 4) * SQ + col));
+          s16x4 l0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Ql + rbase * SQ + col));
+          s16x4 l1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Ql + (rbase + 4) * SQ + col));
+          s16x8 th = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+          s16x8 tl = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+          acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8, th), acc[jb], 0, 0, 0);
+          acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8, tl), acc[jb], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // partial[q][p][j]: lane holds column j = 16 jb + lane%16, rows 4 (lane/16) + e
+  float* dst = pr.part + (int64_t)blockIdx.y * pr.pdim * R;
+#pragma unroll
+  for (int jb = 0; jb < RB; ++jb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t prow = p0 + 16 * wave + 4 * (lane >> 4) + e;
+      const int j = 16 * jb + (lane & 15);
+      if (prow < pr.pdim && j < R) dst[prow * R + j] = acc[jb][e];
+    }
 }
 
-// out[m][j] = sum_c x[m][c] * p[j][c]; one workgroup per row.
+// out[p][j] (or out[j][p]) = s * sum_q part[q][p][j], q in partition order; one
+// thread per output element, the partials read 8 at a time.
+__global__ __launch_bounds__(NT) void grad_reduce_kernel(GradArgs a) {
+  const GradProb& pr = a.prob[blockIdx.y];
+  const int64_t total = pr.pdim * a.r;
+  const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (i >= total) return;
+  const float* src = pr.part + i;
+  float sum = 0.0f;
+  int q = 0;
+  for (; q + 8 <= a.nparts; q += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(q + u) * total];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += v[u];
+  }
+  for (; q < a.nparts; ++q) sum += src[(int64_t)q * total];
+  const int64_t pi = i / a.r;
+  const int j = (int)(i % a.r);
+  const int64_t o = pr.transpose_out ? (int64_t)j * pr.pdim + pi : i;
+  const float v = a.s * sum;
+  pr.out[o] = a.accumulate ? pr.out[o] + v : v;
+}
+
+// out[m][j] = sum_c x[m][c] * b[c][j]; one workgroup per row (used when dX is not wanted).
 template <int R>
 __global__ __launch_bounds__(NT) void down_proj_kernel(const uint16_t* __restrict__ x, int64_t c,
-                                                       const uint16_t* __restrict__ pm,
+                                                       const uint16_t* __restrict__ b,
                                                        float* __restrict__ out) {
   __shared__ float red[NT / 64][R];
   const int64_t row = blockIdx.x;
@@ -41,9 +186,9 @@ __global__ __launch_bounds__(NT) void down_proj_kernel(const uint16_t* __restric
 #pragma unroll
   for (int j = 0; j < R; ++j) acc[j] = 0.0f;
   for (int64_t k = threadIdx.x; k < c; k += NT) {
-    float xv = __uint_as_float((uint32_t)x[row * c + k] << 16);
+    const float xv = __uint_as_float((uint32_t)x[row * c + k] << 16);
 #pragma unroll
-    for (int j = 0; j < R; ++j) acc[j] = fmaf(xv, __uint_as_float((uint32_t)pm[(int64_t)j * c + k] << 16), acc[j]);
+    for (int j = 0; j < R; ++j) acc[j] = fmaf(xv, __uint_as_float((uint32_t)b[k * R + j] << 16), acc[j]);
   }
 #pragma unroll
   for (int j = 0; j < R; ++j)
@@ -59,165 +204,54 @@ __global__ __launch_bounds__(NT) void down_proj_kernel(const uint16_t* __restric
   }
 }
 
-template <int R>
-__global__ __launch_bounds__(NT) void grad_partial_kernel(const uint16_t* __restrict__ x, int64_t m,
-                                                          int64_t pdim, const float* __restrict__ q,
-                                                          int64_t chunk, float* __restrict__ part) {
-  constexpr int RB = (R + 15) / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[TMC * SX];
-  __shared__ __attribute__((aligned(16))) uint16_t Qh[TMC * SQ];
-  __shared__ __attribute__((aligned(16))) uint16_t Ql[TMC * SQ];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t p0 = (int64_t)blockIdx.x * TP;
-  const int64_t mq0 = (int64_t)blockIdx.y * chunk;
-  const int64_t mq1 = mq0 + chunk < m ? mq0 + chunk : m;
-
-  // columns R..16*RB-1 of the Q tiles stay zero
-  for (int i = tid; i < TMC * SQ; i += NT) { Qh[i] = 0; Ql[i] = 0; }
-
-  f32x4 acc[2][RB];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int jb = 0; jb < RB; ++jb) acc[a][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int xr = tid >> 4, xc = (tid & 15) * 8;      // X: rows xr + 16 i, 8 columns
-  constexpr int QPT = R / 4;                         // Q floats per thread
-  const int qr = tid >> 2, qc = (tid & 3) * QPT;
-
-  for (int64_t mc = mq0; mc < mq1; mc += TMC) {
-    uint4 xv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t row = mc + xr + 16 * i, col = p0 + xc;
-      xv[i] = (row < mq1 && col < pdim) ? *reinterpret_cast<const uint4*>(x + row * pdim + col)
-                                        : make_uint4(0, 0, 0, 0);
-    }
-    float qv[QPT];
-    {
-      const int64_t row = mc + qr;
-#pragma unroll
-      for (int t = 0; t < QPT; ++t) qv[t] = (row < mq1) ? q[row * R + qc + t] : 0.0f;
-    }
-    __syncthreads();   // previous step's readers are done
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(Xs + (xr + 16 * i) * SX + xc) = xv[i];
-#pragma unroll
-    for (int t = 0; t < QPT; ++t) {
-      const __bf16 h = (__bf16)qv[t];
-      const __bf16 l = (__bf16)(qv[t] - (float)h);
-      Qh[qr * SQ + qc + t] = __builtin_bit_cast(uint16_t, h);
-      Ql[qr * SQ + qc + t] = __builtin_bit_cast(uint16_t, l);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
-      const int b = lane >> 4, sl = lane & 15;
-      const int rbase = 32 * kp + 8 * b + (sl >> 2);
-      bf16x8 bh[RB], bl[RB];
-#pragma unroll
-      for (int jb = 0; jb < RB; ++jb) {
-        const int col = 16 * jb + 4 * (sl & 3);
-        s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Qh + rbase * SQ + col));
-        s16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Qh + (rbase + 4) * SQ + col));
-        s16x4 l0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Ql + rbase * SQ + col));
-        s16x4 l1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Ql + (rbase + 4) * SQ + col));
-        typedef short s16x8 __attribute__((ext_vector_type(8)));
-        s16x8 th = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-        s16x8 tl = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-        bh[jb] = __builtin_bit_cast(bf16x8, th);
-        bl[jb] = __builtin_bit_cast(bf16x8, tl);
-      }
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int col = 16 * (2 * wave + a) + 4 * (sl & 3);
-        s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Xs + rbase * SX + col));
-        s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Xs + (rbase + 4) * SX + col));
-        typedef short s16x8 __attribute__((ext_vector_type(8)));
-        s16x8 tx = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        bf16x8 af = __builtin_bit_cast(bf16x8, tx);
-#pragma unroll
-        for (int jb = 0; jb < RB; ++jb) {
-          acc[a][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh[jb], acc[a][jb], 0, 0, 0);
-          acc[a][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl[jb], acc[a][jb], 0, 0, 0);
-        }
-      }
-    }
-  }
-  // partial[q][p][j]: lane holds column j = 16 jb + lane%16, rows 4 (lane/16) + e
-  float* dst = part + (int64_t)blockIdx.y * pdim * R;
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int jb = 0; jb < RB; ++jb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t prow = p0 + 16 * (2 * wave + a) + 4 * (lane >> 4) + e;
-        const int j = 16 * jb + (lane & 15);
-        if (prow < pdim && j < R) dst[prow * R + j] = acc[a][jb][e];
-      }
-}
-
-__global__ __launch_bounds__(NT) void grad_reduce_kernel(const float* __restrict__ part, int nparts,
-                                                         int64_t pdim, int r, float s,
-                                                         float* __restrict__ out, int transpose_out,
-                                                         int accumulate) {
-  int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
-  if (i >= pdim * r) return;
-  float sum = 0.0f;
-  for (int q = 0; q < nparts; ++q) sum += part[(int64_t)q * pdim * r + i];
-  const int64_t pi = i / r;
-  const int j = (int)(i % r);
-  const int64_t o = transpose_out ? (int64_t)j * pdim + pi : i;
-  const float v = s * sum;
-  out[o] = accumulate ? out[o] + v : v;
-}
-
-inline unsigned blocks(int64_t n) { return (unsigned)((n + NT - 1) / NT); }
-
 }  // namespace
 
 int32_t grad_parts(int64_t m) {
-  int64_t p = (m + 255) / 256;
+  int64_t p = (m + CHUNK - 1) / CHUNK;
   if (p < 1) p = 1;
   if (p > 64) p = 64;
   return (int32_t)p;
 }
 
-hipError_t launch_transpose_rn(const uint16_t* b, int64_t n, int32_t r, uint16_t* bt, hipStream_t s) {
-  hipLaunchKernelGGL(transpose_rn_kernel, dim3(blocks(n * r)), dim3(NT), 0, s, b, n, r, bt);
-  return hipGetLastError();
-}
+int64_t grad_tiles(int64_t pdim) { return (pdim + TP - 1) / TP; }
 
-hipError_t launch_down_proj(const uint16_t* x, int64_t m, int64_t c, const uint16_t* p, int32_t r,
+hipError_t launch_down_proj(const uint16_t* x, int64_t m, int64_t c, const uint16_t* b, int32_t r,
                             float* out, hipStream_t s) {
   if (m == 0) return hipSuccess;
   switch (r) {
-    case 8: hipLaunchKernelGGL(down_proj_kernel<8>, dim3((unsigned)m), dim3(NT), 0, s, x, c, p, out); break;
-    case 16: hipLaunchKernelGGL(down_proj_kernel<16>, dim3((unsigned)m), dim3(NT), 0, s, x, c, p, out); break;
-    default: hipLaunchKernelGGL(down_proj_kernel<32>, dim3((unsigned)m), dim3(NT), 0, s, x, c, p, out); break;
+    case 8: hipLaunchKernelGGL(down_proj_kernel<8>, dim3((unsigned)m), dim3(NT), 0, s, x, c, b, out); break;
+    case 16: hipLaunchKernelGGL(down_proj_kernel<16>, dim3((unsigned)m), dim3(NT), 0, s, x, c, b, out); break;
+    default: hipLaunchKernelGGL(down_proj_kernel<32>, dim3((unsigned)m), dim3(NT), 0, s, x, c, b, out); break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_grad_partial(const uint16_t* x, int64_t m, int64_t pdim, const float* v, int32_t r,
-                               float* part, int32_t nparts, hipStream_t s) {
-  int64_t chunk = (m + nparts - 1) / nparts;
-  chunk = (chunk + TMC - 1) / TMC * TMC;
-  dim3 grid((unsigned)((pdim + TP - 1) / TP), (unsigned)nparts);
-  switch (r) {
-    case 8: hipLaunchKernelGGL(grad_partial_kernel<8>, grid, dim3(NT), 0, s, x, m, pdim, v, chunk, part); break;
-    case 16: hipLaunchKernelGGL(grad_partial_kernel<16>, grid, dim3(NT), 0, s, x, m, pdim, v, chunk, part); break;
-    default: hipLaunchKernelGGL(grad_partial_kernel<32>, grid, dim3(NT), 0, s, x, m, pdim, v, chunk, part); break;
+hipError_t launch_grads(const GradLaunch& g, hipStream_t s) {
+  GradArgs a{};
+  a.prob[0] = GradProb{g.x, g.v, g.d_a, g.part_a, g.k, 1};
+  a.prob[1] = GradProb{g.dy, g.u, g.d_b, g.part_b, g.n, 0};
+  a.r = g.r;
+  a.m = g.m;
+  a.nparts = g.nparts;
+  int64_t chunk = (g.m + g.nparts - 1) / g.nparts;
+  a.chunk = (chunk + TMC - 1) / TMC * TMC;
+  a.s = g.s;
+  a.accumulate = g.accumulate;
+  const int64_t tiles = grad_tiles(g.k > g.n ? g.k : g.n);
+  dim3 grid((unsigned)tiles, (unsigned)g.nparts, 2);
+  if (g.m > 0) {
+    switch (g.r) {
+      case 8: hipLaunchKernelGGL(grad_kernel<8>, grid, dim3(NT), 0, s, a); break;
+      case 16: hipLaunchKernelGGL(grad_kernel<16>, grid, dim3(NT), 0, s, a); break;
+      default: hipLaunchKernelGGL(grad_kernel<32>, grid, dim3(NT), 0, s, a); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else {
+    a.nparts = 0;                                     // no tokens: dA = dB = 0 (or unchanged)
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_grad_reduce(const float* part, int32_t nparts, int64_t pdim, int32_t r, float s,
-                              float* out, bool transpose_out, bool accumulate, hipStream_t st) {
-  hipLaunchKernelGGL(grad_reduce_kernel, dim3(blocks(pdim * r)), dim3(NT), 0, st, part, nparts, pdim, r,
-                     s, out, transpose_out ? 1 : 0, accumulate ? 1 : 0);
+  const int64_t big = (g.k > g.n ? g.k : g.n) * g.r;
+  hipLaunchKernelGGL(grad_reduce_kernel, dim3((unsigned)((big + NT - 1) / NT), 2), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
