@@ -76,8 +76,6 @@ struct GemmCall {
   float s;                 // alpha / r
   uint16_t* out;           // [M, O] bf16, O = output columns
   float* save;             // [M, r] fp32 rank-r projection (U or V), may be null
-  uint32_t* zero_ptr;      // optional: words zeroed by the kernel (counters of a later launch)
-  int32_t zero_n;
 };
 hipError_t launch_qgemm(const GemmCall& c, hipStream_t s);
 
