@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="packed weight copies rotated per step (0: auto)")
     ap.add_argument("--proj", default=None, help="run only this projection (profiling)")
     ap.add_argument("--phase", default="both", choices=["both", "fwd", "bwd"], help="profiling: one pass only")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device (a plain copy kernel of known size, "
+                         "to calibrate HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -120,6 +123,15 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20)
+        a = torch.ones(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
+        return
 
     from quantized_base_lora_amd import binding as B, synth
 
