@@ -160,7 +160,9 @@ def main():
              "da": torch.empty((wl.r, p.k), dtype=torch.float32, device=dev),
              "db": torch.empty((p.n, wl.r), dtype=torch.float32, device=dev),
              "ws": torch.empty(max(256, B.workspace_bytes(B.OP_BWD, wl.fmt, p.n, p.k, m, wl.r)),
-                               dtype=torch.uint8, device=dev)}
+                               dtype=torch.uint8, device=dev),
+             "wsf": torch.empty(max(256, B.workspace_bytes(B.OP_FWD, wl.fmt, p.n, p.k, m, wl.r)),
+                                dtype=torch.uint8, device=dev)}
         projs.append(d)
     # rotate packed copies so weight reads come from HBM, not the 256 MB MALL
     copies = args.copies or max(1, min(8, int(np.ceil(512e6 / packed_bytes))))
@@ -180,7 +182,7 @@ def main():
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-            B.linear_fwd(qw, d["x"], d["a"], d["b"], wl.alpha, y=d["y"], u=d["u"], stream=stream)
+            B.linear_fwd(qw, d["x"], d["a"], d["b"], wl.alpha, y=d["y"], u=d["u"], ws=d["wsf"], stream=stream)
             if timed:
                 e1.record(stream)
                 ev_pairs.append((d["p"], e0, e1))

@@ -144,7 +144,10 @@ int ql_act_quant_e4m3(const uint16_t* x, int64_t m, int64_t k, uint8_t* hi,
  * y (dev bf16 [M, N]) = x . deq(W)^T + s . U . B^T,  U = x . A^T saved to
  * u_save (dev fp32 [M, r], required).  x: dev bf16 [M, K]; lora_a: dev bf16
  * [r, K]; lora_b: dev bf16 [N, r]; s = alpha / r.  Accumulation is fp32.
- * ws: dev scratch, at least qlora_workspace_bytes(QL_OP_FWD, ...) bytes. */
+ * ws: dev scratch (16-byte aligned), at least qlora_workspace_bytes(
+ * QL_OP_FWD, ...) bytes: zero for M > 64; for M <= 64 the contraction is
+ * split across workgroups and the fp32 partial sums live there (they are
+ * added in a fixed order, so results do not depend on scheduling). */
 int qlora_linear_fwd(const ql_qweight* w, const uint16_t* x, int64_t m,
                      const uint16_t* lora_a, const uint16_t* lora_b, int32_t r,
                      float alpha, uint16_t* y, float* u_save, void* ws,

@@ -63,9 +63,10 @@ int check_rank(int32_t r) {
   return QL_OK;
 }
 
-// backward workspace: V [M, r] fp32 | partials for dA [P, K, r] | for dB [P, N, r]
+// backward workspace: V [M, r] fp32 | partials for dA [P, K, r] | for dB [P, N, r] |
+// the dX GEMM's own scratch (split-contraction partials, small M only)
 struct BwdLayout {
-  size_t v, pa, pb, total;
+  size_t v, pa, pb, g, total;
   int32_t parts;
 };
 
@@ -75,7 +76,8 @@ BwdLayout bwd_layout(int64_t n, int64_t k, int64_t m, int32_t r) {
   l.v = 0;
   l.pa = l.v + up((size_t)m * r * 4);
   l.pb = l.pa + up((size_t)l.parts * k * r * 4);
-  l.total = l.pb + up((size_t)l.parts * n * r * 4);
+  l.g = l.pb + up((size_t)l.parts * n * r * 4);
+  l.total = l.g + up(qgemm_workspace_bytes(true, m, n, k, r));
   return l;
 }
 
@@ -101,7 +103,7 @@ size_t qlora_workspace_bytes(int32_t op, int32_t format, int64_t n_out, int64_t 
   (void)format;
   switch (op) {
     case QL_OP_PACK: return 256;
-    case QL_OP_FWD: return 0;
+    case QL_OP_FWD: return qgemm_workspace_bytes(false, m < 0 ? 0 : m, n_out, k_in, r);
     case QL_OP_BWD: return bwd_layout(n_out, k_in, m < 0 ? 0 : m, r).total;
     default: return 0;
   }
@@ -172,7 +174,7 @@ int qlora_linear_fwd(const ql_qweight* w, const uint16_t* x, int64_t m, const ui
     return set_error(QL_EINVAL, "misaligned pointer");
   size_t need = qlora_workspace_bytes(QL_OP_FWD, w->format, w->n_out, w->k_in, m, r);
   if (ws_bytes < need) return set_error(QL_EWORKSPACE, "forward needs %zu workspace bytes", need);
-  (void)ws;
+  if (need && (!ws || !aligned16(ws))) return set_error(QL_EINVAL, "null or misaligned workspace");
   if ((rc = check_sticky())) return rc;
   GemmCall c{};
   c.w = w;
@@ -185,6 +187,7 @@ int qlora_linear_fwd(const ql_qweight* w, const uint16_t* x, int64_t m, const ui
   c.s = alpha / (float)r;
   c.out = y;
   c.save = u_save;
+  c.ws = ws;
   hipError_t e = launch_qgemm(c, as_stream(stream));
   if (e != hipSuccess) return hip_error(e, "forward launch");
   return QL_OK;
@@ -226,6 +229,7 @@ int qlora_linear_bwd(const ql_qweight* w, const uint16_t* x, const uint16_t* dy,
     c.s = sc;
     c.out = dx;
     c.save = v;
+    c.ws = base + L.g;
     e = launch_qgemm(c, s);
   } else if (m > 0) {
     e = launch_down_proj(dy, m, n, lora_b, r, v, s);

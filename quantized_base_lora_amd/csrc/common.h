@@ -76,8 +76,11 @@ struct GemmCall {
   float s;                 // alpha / r
   uint16_t* out;           // [M, O] bf16, O = output columns
   float* save;             // [M, r] fp32 rank-r projection (U or V), may be null
+  void* ws;                // scratch of qgemm_workspace_bytes(trans, m, n, k, r) bytes (small-M path)
 };
 hipError_t launch_qgemm(const GemmCall& c, hipStream_t s);
+// scratch the GEMM needs: split-contraction partials when m is small, else 0
+size_t qgemm_workspace_bytes(bool trans, int64_t m, int64_t n, int64_t k, int32_t r);
 
 // LoRA-side kernels (kernels_lora.hip)
 // out[m][j] = sum_c x[m][c] * b[c][j]     (fp32), b is [C, r]
