@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="packed weight copies rotated per step (0: auto)")
     ap.add_argument("--proj", default=None, help="run only this projection (profiling)")
     ap.add_argument("--phase", default="both", choices=["both", "fwd", "bwd"], help="profiling: one pass only")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="stack mode: this many layers, resident vs streamed from pinned host")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device (a plain copy kernel of known size, "
                          "to calibrate HBM byte counters) and exit")
@@ -116,6 +118,124 @@ def cpu_baseline(wl, tokens, min_seconds=10.0):
                       f"BLAS threads {threads}, host cpus visible {len(os.sched_getaffinity(0))}"}
 
 
+def bench_stack(args, wl, m):
+    """The layer stack: L Llama-shaped layers, forward 0..L-1 then backward
+    L-1..0, with the packed bases resident in VRAM or streamed from pinned
+    host memory through two device slots (one layer ahead on a side stream).
+    Bases are random normal W packed on the GPU; activations and adapters are
+    seeded normals generated on the GPU (their values do not affect timing)."""
+    import torch
+
+    from quantized_base_lora_amd import binding as B, stack
+
+    dev = torch.device("cuda:0")
+    L = args.layers
+    layout = stack.LayerLayout(wl.fmt, wl.projs)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    host = []
+    t0 = time.time()
+    for layer in range(L):
+        qws = []
+        for p in wl.projs:
+            w = torch.randn((p.n, p.k), generator=gen, device=dev, dtype=torch.float32) * 0.02
+            qws.append(B.quant_pack(wl.fmt, w))
+            del w
+        img = layout.image_from(qws)
+        h = torch.empty(layout.nbytes, dtype=torch.uint8, pin_memory=True)
+        h.copy_(img)
+        host.append(h)
+        del img, qws
+    torch.cuda.synchronize()
+    prep_s = time.time() - t0
+
+    def bf16(shape, std):
+        return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * std).to(torch.bfloat16)
+
+    acts, outs = [], []
+    for layer in range(L):
+        al, ol = [], []
+        for p in wl.projs:
+            al.append({"x": bf16((m, p.k), 1.0), "dy": bf16((m, p.n), 1.0),
+                       "a": bf16((wl.r, p.k), p.k ** -0.5), "b": bf16((p.n, wl.r), 0.01)})
+            ol.append({"y": torch.empty((m, p.n), dtype=torch.bfloat16, device=dev),
+                       "u": torch.empty((m, wl.r), dtype=torch.float32, device=dev),
+                       "dx": torch.empty((m, p.k), dtype=torch.bfloat16, device=dev),
+                       "da": torch.empty((wl.r, p.k), dtype=torch.float32, device=dev),
+                       "db": torch.empty((p.n, wl.r), dtype=torch.float32, device=dev),
+                       "ws": torch.empty(max(256, B.workspace_bytes(B.OP_BWD, wl.fmt, p.n, p.k, m, wl.r)),
+                                         dtype=torch.uint8, device=dev),
+                       "wsf": torch.empty(max(256, B.workspace_bytes(B.OP_FWD, wl.fmt, p.n, p.k, m, wl.r)),
+                                          dtype=torch.uint8, device=dev)})
+        acts.append(al)
+        outs.append(ol)
+    stream = torch.cuda.current_stream()
+
+    def timed(st, steps, warmup):
+        for _ in range(warmup):
+            st.run(acts, outs)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            st.run(acts, outs)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    # pinned host -> device bandwidth, 1 GiB, in the same process
+    hb = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    db = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    db.copy_(hb, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(3):
+        db.copy_(hb, non_blocking=True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    h2d_gbs = 3 * (1 << 30) / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del hb, db
+
+    dev_imgs = [h.to(dev) for h in host]
+    res = stack.Stack(layout, wl.r, wl.alpha, images_dev=dev_imgs)
+    ms_res = timed(res, args.steps, args.warmup)
+    del res, dev_imgs
+    torch.cuda.empty_cache()
+    st = stack.Stack(layout, wl.r, wl.alpha, images_host=host, n_slots=2)
+    ms_st = timed(st, args.steps, args.warmup)
+    stats = st.pool.stats()
+    st.close()
+    copies_per_step = 2 * L - 2
+    copy_ms = copies_per_step * layout.nbytes / (h2d_gbs * 1e9) * 1e3
+    out = {
+        "metric": "QLoRA stack fwd+bwd tokens/s, base streamed from pinned host",
+        "value": m / (ms_st / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_st,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.notes, "name": wl.name, "tokens": m, "layers": L,
+                   "base_format": FMT_NAME[wl.fmt], "rank": wl.r, "alpha": wl.alpha,
+                   "layer_image_bytes": layout.nbytes, "slots": 2},
+        "stack": {"resident_ms_per_step": ms_res, "resident_tokens_per_s": m / (ms_res / 1e3),
+                  "streamed_over_resident": ms_st / ms_res,
+                  "copies_per_step": copies_per_step,
+                  "streamed_bytes_per_step": copies_per_step * layout.nbytes,
+                  "pinned_h2d_gbs": h2d_gbs,
+                  "copy_ms_at_measured_h2d": copy_ms,
+                  "overlap_efficiency": max(copy_ms, ms_res) / ms_st,
+                  "pool_stats_total": stats, "host_prep_s": prep_s},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -138,6 +258,8 @@ def main():
     B.load()
     wl = synth.WORKLOADS[args.workload]
     m = args.m or wl.m
+    if args.layers:
+        return bench_stack(args, wl, m)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
 

@@ -93,7 +93,8 @@ class Stack:
 
     def run(self, acts, outs):
         """acts[l][p] = dict(x, dy, a, b) device tensors; outs[l][p] = dict of
-        preallocated y, u, dx, da, db and ws tensors, written in place."""
+        preallocated y, u, dx, da, db and ws (backward workspace) tensors,
+        written in place, and optionally wsf (forward workspace)."""
         L = self.n_layers
         self._ahead(0)
         for l in range(L):
@@ -101,7 +102,7 @@ class Stack:
             ws = self._weights(l)
             for p, qw in enumerate(ws):
                 a, o = acts[l][p], outs[l][p]
-                B.linear_fwd(qw, a["x"], a["a"], a["b"], self.alpha, y=o["y"], u=o["u"])
+                B.linear_fwd(qw, a["x"], a["a"], a["b"], self.alpha, y=o["y"], u=o["u"], ws=o.get("wsf"))
             self._done(l)
         for l in reversed(range(L)):
             self._ahead(l - 1)
