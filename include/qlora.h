@@ -133,9 +133,12 @@ int qlora_dequant(const ql_qweight* w, float* out_f32, uint16_t* out_bf16,
                   void* stream);
 
 /* ---------------------------------------------------------------- a1: FP8 activations
- * Per-row two-term E4M3 split used by the FP8 base:
- *   s_m = fl32(max|x_m| / 448), t = fl32(x / s_m), hi = E4M3(t),
- *   lo = E4M3(fl32(fl32(t - hi) * 16)),  x ~= s_m (hi + lo / 16).
+ * Per-row two-term E4M3 split used by the FP8 base (the pages quantize
+ * activations for their FP8 recipe without saying how; this is the reading):
+ *   s_m = 2^e, e the smallest integer with 448 * 2^e >= max|x_m|,
+ *   t = x / s_m (exact), hi = E4M3(t), lo = E4M3((t - hi) * 16) (the
+ *   difference and the factor are exact),  x ~= s_m (hi + lo / 16);
+ *   E4M3 = OCP E4M3FN, nearest even.  A zero row gives s_m = 0, codes 0.
  * x: dev bf16 [M, K]; hi, lo: dev u8 [M, K]; scale: dev fp32 [M]. */
 int ql_act_quant_e4m3(const uint16_t* x, int64_t m, int64_t k, uint8_t* hi,
                       uint8_t* lo, float* scale, void* stream);

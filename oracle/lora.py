@@ -97,28 +97,48 @@ def rel_err(got, ref):
 LO_SHIFT = 16.0   # the low term is stored 16x finer than the high term
 
 
+def act_row_exponent(amax):
+    """Smallest integer e with 448 * 2^e >= amax (amax > 0), by exact
+    comparisons (448 * 2^e is exact in fp64 over the whole fp32 range)."""
+    a = float(amax)
+    e = int(np.floor(np.log2(a))) - 8
+    while 448.0 * 2.0 ** e < a:
+        e += 1
+    while 448.0 * 2.0 ** (e - 1) >= a:
+        e -= 1
+    return e
+
+
 def act_split_e4m3(x):
     """Per-token two-term E4M3 split of activations for the FP8-base GEMM.
 
-    For each row m: s_m = fl32(max|x_m| / 448); t = fl32(x / s_m);
-    hi = E4M3(t); lo = E4M3(fl32(fl32(t - E4M3(hi)) * 16)), so that
-    x ~= s_m * (hi + lo / 16).  A zero row has s_m = 0 and zero codes.
+    For each row m with a = max|x_m| > 0 the scale is the power of two
+    s_m = 2^e, e the smallest integer with 448 * 2^e >= a, so t = x / s_m is
+    exact in fp32 and |t| <= 448; then hi = E4M3(t) and
+    lo = E4M3(fl32(t - E4M3(hi)) * 16) (the difference and the factor 16 are
+    exact too), so that x ~= s_m * (hi + lo / 16) with the two E4M3
+    roundings as the only ones.  A zero row has s_m = 0 and zero codes.
     Returns (hi u8 [M, K], lo u8 [M, K], s fp32 [M]).
 
-    This is an approximation the pages do not define (they quantize
-    activations for their FP8 recipe without stating how); it is checked by
-    tolerance only.
+    The pages quantize activations for their FP8 recipe without saying how:
+    the per-token scale, its power-of-two form (the form of the matrix cores'
+    E8M0 block-scale operand) and the second term are this implementation's
+    reading.  It is an approximation, checked by its error bound.
     """
     xf = np.asarray(x, dtype=np.float32)
-    amax = np.max(np.abs(xf), axis=1) if xf.shape[1] else np.zeros(xf.shape[0], np.float32)
-    s = (amax / np.float32(448.0)).astype(np.float32)
-    nz = s != 0
-    with np.errstate(divide="ignore", invalid="ignore"):
-        t = (xf / s[:, None]).astype(np.float32)
-    t = np.where(nz[:, None], t, np.float32(0.0))
+    m = xf.shape[0]
+    amax = np.max(np.abs(xf), axis=1) if xf.shape[1] else np.zeros(m, np.float32)
+    s = np.zeros(m, np.float32)
+    t = np.zeros_like(xf)
+    for i in range(m):
+        if amax[i] > 0:
+            e = act_row_exponent(amax[i])
+            s[i] = np.float32(np.ldexp(1.0, e))
+            t[i] = np.ldexp(xf[i].astype(np.float64), -e).astype(np.float32)   # exact
     hi = codecs.e4m3_encode(t)
     res = (t - codecs.e4m3_decode(hi)).astype(np.float32)
     lo = codecs.e4m3_encode((res * np.float32(LO_SHIFT)).astype(np.float32))
+    nz = amax > 0
     hi = np.where(nz[:, None], hi, np.uint8(0)).astype(np.uint8)
     lo = np.where(nz[:, None], lo, np.uint8(0)).astype(np.uint8)
     return hi, lo, s

@@ -70,14 +70,14 @@ struct BwdLayout {
   int32_t parts;
 };
 
-BwdLayout bwd_layout(int64_t n, int64_t k, int64_t m, int32_t r) {
+BwdLayout bwd_layout(int32_t fmt, int64_t n, int64_t k, int64_t m, int32_t r) {
   BwdLayout l{};
   l.parts = grad_parts(m);
   l.v = 0;
   l.pa = l.v + up((size_t)m * r * 4);
   l.pb = l.pa + up((size_t)l.parts * k * r * 4);
   l.g = l.pb + up((size_t)l.parts * n * r * 4);
-  l.total = l.g + up(qgemm_workspace_bytes(true, m, n, k, r));
+  l.total = l.g + up(qgemm_workspace_bytes(fmt, true, m, n, k, r));
   return l;
 }
 
@@ -100,11 +100,10 @@ int ql_nf4_levels(float* out) {
 
 size_t qlora_workspace_bytes(int32_t op, int32_t format, int64_t n_out, int64_t k_in, int64_t m,
                              int32_t r) {
-  (void)format;
   switch (op) {
     case QL_OP_PACK: return 256;
-    case QL_OP_FWD: return qgemm_workspace_bytes(false, m < 0 ? 0 : m, n_out, k_in, r);
-    case QL_OP_BWD: return bwd_layout(n_out, k_in, m < 0 ? 0 : m, r).total;
+    case QL_OP_FWD: return qgemm_workspace_bytes(format, false, m < 0 ? 0 : m, n_out, k_in, r);
+    case QL_OP_BWD: return bwd_layout(format, n_out, k_in, m < 0 ? 0 : m, r).total;
     default: return 0;
   }
 }
@@ -207,7 +206,7 @@ int qlora_linear_bwd(const ql_qweight* w, const uint16_t* x, const uint16_t* dy,
       (dx && !aligned16(dx)) || !aligned16(d_a) || !aligned16(d_b) || !aligned16(ws))
     return set_error(QL_EINVAL, "misaligned pointer");
   const int64_t n = w->n_out, k = w->k_in;
-  BwdLayout L = bwd_layout(n, k, m, r);
+  BwdLayout L = bwd_layout(w->format, n, k, m, r);
   if (ws_bytes < L.total) return set_error(QL_EWORKSPACE, "backward needs %zu workspace bytes", L.total);
   if ((rc = check_sticky())) return rc;
   hipStream_t s = as_stream(stream);

@@ -79,8 +79,29 @@ struct GemmCall {
   void* ws;                // scratch of qgemm_workspace_bytes(trans, m, n, k, r) bytes (small-M path)
 };
 hipError_t launch_qgemm(const GemmCall& c, hipStream_t s);
-// scratch the GEMM needs: split-contraction partials when m is small, else 0
-size_t qgemm_workspace_bytes(bool trans, int64_t m, int64_t n, int64_t k, int32_t r);
+// scratch the GEMM needs: split-contraction partials when m is small; for the
+// FP8 base with more tokens, the activation split (hi, lo planes and row scales)
+size_t qgemm_workspace_bytes(int32_t fmt, bool trans, int64_t m, int64_t n, int64_t k, int32_t r);
+
+// FP8 base on fp8 matrix cores (kernels_fp8.hip): the activation arrives split
+// (a1), the rank-r projection precomputed
+struct Gemm8Call {
+  const ql_qweight* w;
+  bool trans;
+  const uint8_t* hi;       // [M, C] E4M3
+  const uint8_t* lo;       // [M, C] E4M3
+  const float* rs;         // [M] row scales
+  int64_t m;
+  const float* u;          // [M, r] U (forward) or V (dX)
+  const uint16_t* up;      // forward: B [N, r]; dX: A [r, K]
+  int32_t r;
+  float s;
+  uint16_t* out;           // [M, O] bf16
+};
+hipError_t launch_qgemm8(const Gemm8Call& c, hipStream_t s);
+// out [m, r] fp32 = act [m, c] . D, D = A^T (a_layout, A [r, c]) or B ([c, r])
+hipError_t launch_rproj(const uint16_t* act, int64_t m, int64_t c, const uint16_t* d, bool a_layout, int32_t r,
+                        float* out, hipStream_t s);
 
 // LoRA-side kernels (kernels_lora.hip)
 // out[m][j] = sum_c x[m][c] * b[c][j]     (fp32), b is [C, r]

@@ -1,0 +1,387 @@
+// a3 / a6 for the FP8 E4M3 base on the fp8 matrix cores (more than 64
+// tokens), and the rank-r projection that these GEMMs take precomputed.
+//
+// The activation (x forward, dY for dX) arrives split per row into two E4M3
+// terms, act ~= s_m (hi + lo / 16), s_m a power of two (a1); W's codes are
+// used raw.  Each 64-deep contraction step issues, per 32 x 32 output block,
+// one scaled 32x32x64 f8f6f4 MFMA on hi (unit scales) and one on lo (E8M0
+// scale 2^-4 on that operand), into one fp32 accumulator.  The epilogue
+// multiplies by s_w s_m (tensor scale times row scale), adds s . U . up^T on
+// bf16 MFMAs (s . U split into a high and a low bf16 term, as in the bf16
+// GEMM) and rounds once to bf16.
+//
+// dX reads W through the same [row of W][column] LDS tile with 8-bit
+// transpose reads (ds_read_b64_tr_b8), so no transposed copy of the base is
+// made.  Tiling follows the bf16 GEMM: 512 threads, two waves per SIMD, a
+// 256 x TN output tile per workgroup, double-buffered LDS, loads of step
+// kt+2 issued as step kt+1 is stored.
+#include "common.h"
+#include "device.h"
+
+namespace ql {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+constexpr int TM = 256, TK = 64, NT = 512;
+constexpr int SB = 80;                 // act planes and forward W tile: row stride in bytes
+
+template <int TN, bool TRANS> struct Shape8 {
+  static constexpr int WAVES_N = TN == 256 ? 4 : 2;
+  static constexpr int WAVES_M = 8 / WAVES_N;
+  static constexpr int WM = TM / WAVES_M, WN = TN / WAVES_N;
+  static constexpr int MB = WM / 32, NB = WN / 32;
+  static constexpr int SBT = TN + 16;              // dX W tile [TK][TN]: row stride in bytes
+  static constexpr int A_BYTES = TM * SB;          // one activation plane
+  static constexpr int W_BYTES = TRANS ? TK * SBT : TN * SB;
+  static constexpr int STAGE = 2 * A_BYTES + W_BYTES;
+  static constexpr int WCH = TN * TK / 16 / NT;    // 16-byte W pieces per thread: 2 or 1
+  static constexpr int CPR = TN / 16;              // dX: pieces per W-tile row
+};
+
+struct P8 {
+  const uint8_t* hi;       // [M, C] E4M3
+  const uint8_t* lo;       // [M, C] E4M3, 16x finer
+  const float* rs;         // [M] row scales (powers of two)
+  const uint8_t* codes;    // W [N, K] E4M3
+  const float* wscale;     // [1] tensor scale of W
+  const float* u;          // [M, R] rank-r projection (U forward, V for dX)
+  const uint16_t* up;      // forward: B [N, R]; dX: A [R, K]
+  uint16_t* out;           // [M, O] bf16
+  int64_t M, N, K, C, O;
+  float s;
+};
+
+__device__ __forceinline__ v8i frag_b128x2(const uint8_t* p) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint4 b = *reinterpret_cast<const uint4*>(p + 16);
+  v8i r = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+  return r;
+}
+
+__device__ __forceinline__ v2i tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)p);
+}
+
+template <bool TRANS, int R, int TN>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void qgemm8_kernel(P8 p) {
+  using S = Shape8<TN, TRANS>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t sm8[];
+  constexpr int MB = S::MB, NB = S::NB, WCH = S::WCH;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / S::WAVES_N, wn = wave % S::WAVES_N;
+
+  const int nt = (int)((p.O + TN - 1) / TN);
+  const int mt = (int)((p.M + TM - 1) / TM);
+  const int tiles = nt * mt;
+  int t = blockIdx.x;
+  if ((tiles & 7) == 0) t = (t & 7) * (tiles >> 3) + (t >> 3);
+  const int64_t o0 = (int64_t)(t % nt) * TN;
+  const int64_t m0 = (int64_t)(t / nt) * TM;
+  const int KT = (int)((p.C + TK - 1) / TK);
+
+  const __amdgpu_buffer_rsrc_t rhi = rsrc(p.hi + m0 * p.C, (p.M - m0) * p.C);
+  const __amdgpu_buffer_rsrc_t rlo = rsrc(p.lo + m0 * p.C, (p.M - m0) * p.C);
+  const __amdgpu_buffer_rsrc_t rcode =
+      TRANS ? rsrc(p.codes + o0, p.N * p.K - o0) : rsrc(p.codes + o0 * p.K, (p.N - o0) * p.K);
+
+  // piece coordinates: activation planes 256 x 64 bytes (2 pieces a thread each), W tile
+  int arow[2], acol[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = tid + NT * i;
+    arow[i] = q >> 2;
+    acol[i] = (q & 3) * 16;
+  }
+  int wrow[WCH], wcol[WCH];
+#pragma unroll
+  for (int i = 0; i < WCH; ++i) {
+    const int q = tid + NT * i;
+    wrow[i] = TRANS ? q / S::CPR : q >> 2;
+    wcol[i] = TRANS ? (q % S::CPR) * 16 : (q & 3) * 16;
+  }
+  uint4 rh[2], rl[2], rw[WCH];
+
+  auto load = [&](int kt) {
+    const int64_t c0 = (int64_t)kt * TK;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const bool ok = c0 + acol[i] < p.C;
+      const uint32_t off = (uint32_t)(arow[i] * p.C + c0 + acol[i]);
+      rh[i] = bload16(rhi, ok ? off : OOB);
+      rl[i] = bload16(rlo, ok ? off : OOB);
+    }
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) {
+      uint32_t off;
+      bool ok;
+      if constexpr (TRANS) {          // W rows c0 + wrow (past N: outside the resource), columns o0 + wcol
+        off = (uint32_t)((c0 + wrow[i]) * p.K + wcol[i]);
+        ok = o0 + wcol[i] < p.K;
+      } else {                        // W rows o0 + wrow (past N: outside), columns c0 + wcol
+        off = (uint32_t)(wrow[i] * p.K + c0 + wcol[i]);
+        ok = c0 + wcol[i] < p.K;
+      }
+      rw[i] = bload16(rcode, ok ? off : OOB);
+    }
+  };
+  auto store = [&](uint8_t* st) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      *reinterpret_cast<uint4*>(st + arow[i] * SB + acol[i]) = rh[i];
+      *reinterpret_cast<uint4*>(st + S::A_BYTES + arow[i] * SB + acol[i]) = rl[i];
+    }
+#pragma unroll
+    for (int i = 0; i < WCH; ++i)
+      *reinterpret_cast<uint4*>(st + 2 * S::A_BYTES + wrow[i] * (TRANS ? S::SBT : SB) + wcol[i]) = rw[i];
+  };
+
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  auto compute = [&](const uint8_t* st) {
+    const uint8_t* Hs = st;
+    const uint8_t* Ls = st + S::A_BYTES;
+    const uint8_t* Ws = st + 2 * S::A_BYTES;
+    v8i wf[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if constexpr (TRANS) {
+        // lane: output column (row of the A operand) within the block, 32 contraction rows
+        const int b = lane >> 4, s = lane & 15;
+        const int col = S::WN * wn + 32 * j + 16 * (b & 1) + 8 * (s & 1);
+        const int row = 32 * (b >> 1) + (s >> 1);
+        const v2i t0 = tr8(Ws + (row + 0) * S::SBT + col);
+        const v2i t1 = tr8(Ws + (row + 8) * S::SBT + col);
+        const v2i t2 = tr8(Ws + (row + 16) * S::SBT + col);
+        const v2i t3 = tr8(Ws + (row + 24) * S::SBT + col);
+        v8i r = {t0.x, t0.y, t1.x, t1.y, t2.x, t2.y, t3.x, t3.y};
+        wf[j] = r;
+      } else {
+        wf[j] = frag_b128x2(Ws + (S::WN * wn + 32 * j + (lane & 31)) * SB + 32 * (lane >> 5));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int off = (S::WM * wm + 32 * i + (lane & 31)) * SB + 32 * (lane >> 5);
+      const v8i hf = frag_b128x2(Hs + off);
+      const v8i lf = frag_b128x2(Ls + off);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[j], hf, acc[i][j], 0, 0, 0, 127, 0, 127);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[j], lf, acc[i][j], 0, 0, 0, 127, 0, 123);
+      }
+    }
+  };
+
+  // ---- main loop: stage kt+1 stored and kt+2 loaded while stage kt computes
+  load(0);
+  store(sm8);
+  load(KT > 1 ? 1 : 0);
+  lds_barrier();
+  for (int kt = 0; kt + 1 < KT; ++kt) {
+    store(sm8 + ((kt + 1) & 1) * S::STAGE);
+    load(kt + 2 < KT ? kt + 2 : KT - 1);
+    compute(sm8 + (kt & 1) * S::STAGE);
+    lds_barrier();
+  }
+  compute(sm8 + ((KT - 1) & 1) * S::STAGE);
+  lds_barrier();
+
+  // ---- epilogue: scales, then s . U . up^T on bf16 MFMAs, one rounding to bf16
+  const float sw = *p.wscale;
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int64_t row = m0 + S::WM * wm + 32 * i + (lane & 31);
+    const float sc = row < p.M ? sw * p.rs[row] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] *= sc;
+  }
+  constexpr int SX = 2 * R + 8;
+  uint16_t* Ax = reinterpret_cast<uint16_t*>(sm8);
+  uint16_t* Bx = Ax + TM * SX;
+  for (int idx = tid; idx < TM * R; idx += NT) {
+    const int row = idx / R, j = idx % R;
+    const float su = m0 + row < p.M ? p.s * p.u[(m0 + row) * R + j] : 0.0f;
+    const __bf16 h = (__bf16)su;
+    const __bf16 l = (__bf16)(su - (float)h);
+    Ax[row * SX + j] = __builtin_bit_cast(uint16_t, h);
+    Ax[row * SX + R + j] = __builtin_bit_cast(uint16_t, l);
+  }
+  for (int idx = tid; idx < TN * R; idx += NT) {
+    const int col = idx / R, j = idx % R;
+    uint16_t v = 0;
+    if (o0 + col < p.O) v = TRANS ? p.up[(int64_t)j * p.K + o0 + col] : p.up[(o0 + col) * R + j];
+    Bx[col * SX + j] = v;
+    Bx[col * SX + R + j] = v;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int ks = 0; ks < (2 * R) / 16; ++ks) {
+    bf16x8 af[MB], bfr[NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+      af[i] = *reinterpret_cast<const bf16x8*>(Ax + (S::WM * wm + 32 * i + (lane & 31)) * SX + ks * 16 + 8 * (lane >> 5));
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      bfr[j] = *reinterpret_cast<const bf16x8*>(Bx + (S::WN * wn + 32 * j + (lane & 31)) * SX + ks * 16 + 8 * (lane >> 5));
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int64_t row = m0 + S::WM * wm + 32 * i + (lane & 31);
+    if (row < p.M) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const int64_t col = o0 + S::WN * wn + 32 * j + 8 * k4 + 4 * (lane >> 5);
+          if (col < p.O) {
+            const uint32_t lo = pack_bf16x2(acc[i][j][4 * k4 + 0], acc[i][j][4 * k4 + 1]);
+            const uint32_t hi = pack_bf16x2(acc[i][j][4 * k4 + 2], acc[i][j][4 * k4 + 3]);
+            *reinterpret_cast<uint2*>(p.out + row * p.O + col) = make_uint2(lo, hi);
+          }
+        }
+    }
+  }
+}
+
+template <bool TRANS, int R, int TN>
+hipError_t launch8_t(const P8& p, hipStream_t s) {
+  using S = Shape8<TN, TRANS>;
+  constexpr size_t smem = 2 * (size_t)S::STAGE;
+  static_assert(smem <= 160 * 1024, "LDS budget");
+  static_assert((size_t)(TM + TN) * (2 * R + 8) * 2 <= smem, "epilogue LDS");
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)qgemm8_kernel<TRANS, R, TN>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t tiles = ((p.O + TN - 1) / TN) * ((p.M + TM - 1) / TM);
+  hipLaunchKernelGGL((qgemm8_kernel<TRANS, R, TN>), dim3((unsigned)tiles), dim3(NT), smem, s, p);
+  return hipGetLastError();
+}
+
+template <bool TRANS, int R>
+hipError_t launch8_w(const P8& p, hipStream_t s) {
+  const int64_t tiles256 = ((p.O + 255) / 256) * ((p.M + TM - 1) / TM);
+  if (tiles256 >= 256) return launch8_t<TRANS, R, 256>(p, s);
+  return launch8_t<TRANS, R, 128>(p, s);
+}
+
+// ------------------------------------------------------------------ rank-r projection
+// out[m][j] = sum_c act[m][c] D(c, j), D(c, j) = A[j][c] (A layout, [R, C]) or
+// B[c][j] (B layout, [C, R]), fp32 accumulation on 32x32x16 bf16 MFMAs.  A
+// workgroup owns 32 rows; its four waves take the 64-wide contraction chunks
+// round robin and their partial sums are added in wave order (fixed).  The
+// activation fragments come straight from global memory; a B-layout chunk
+// goes through the wave's own LDS tile and transposing reads.
+template <int R, bool ALAYOUT>
+__global__ __launch_bounds__(256) void rproj_kernel(const uint16_t* __restrict__ act, int64_t M, int64_t C,
+                                                    const uint16_t* __restrict__ d, float* __restrict__ out) {
+  constexpr int SLD = 48;
+  __shared__ __attribute__((aligned(16))) uint16_t dl[4][64 * SLD];
+  __shared__ float red[4][32][33];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t m0 = (int64_t)blockIdx.x * 32;
+  const __amdgpu_buffer_rsrc_t ract = rsrc(act + m0 * C, (M - m0) * C * 2);
+  const __amdgpu_buffer_rsrc_t rd = rsrc(d, (int64_t)R * C * 2);
+  if constexpr (!ALAYOUT)
+    for (int i = lane; i < 64 * SLD; i += 64) dl[wave][i] = 0;   // columns past r stay zero
+  f32x16 acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+  for (int64_t c0 = (int64_t)wave * 64; c0 < C; c0 += 256) {
+    if constexpr (!ALAYOUT) {
+#pragma unroll
+      for (int t = 0; t < R / 8; ++t) {
+        const int q = lane + 64 * t;
+        const int row = q / (R / 8), col = (q % (R / 8)) * 8;
+        const uint4 v = bload16(rd, (uint32_t)(((c0 + row) * R + col) * 2));
+        *reinterpret_cast<uint4*>(&dl[wave][row * SLD + col]) = v;
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int64_t k = c0 + 16 * ks + 8 * (lane >> 5);
+      const bf16x8 af = __builtin_bit_cast(bf16x8, bload16(ract, k < C ? (uint32_t)(((lane & 31) * C + k) * 2) : OOB));
+      bf16x8 df;
+      if constexpr (ALAYOUT) {
+        const int j = lane & 31;
+        df = __builtin_bit_cast(bf16x8, bload16(rd, (j < R && k < C) ? (uint32_t)((j * C + k) * 2) : OOB));
+      } else {
+        const int b = lane >> 4, sl = lane & 15;
+        const int col = 16 * (b & 1) + 4 * (sl & 3);
+        const int row = 16 * ks + 8 * (b >> 1) + (sl >> 2);
+        df = tr16x8(&dl[wave][row * SLD + col], &dl[wave][(row + 4) * SLD + col]);
+      }
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, df, acc, 0, 0, 0);
+    }
+  }
+  // lane: column j = lane & 31, rows 8 (e / 4) + 4 (lane / 32) + e % 4
+#pragma unroll
+  for (int e = 0; e < 16; ++e) red[wave][8 * (e / 4) + 4 * (lane >> 5) + (e % 4)][lane & 31] = acc[e];
+  __syncthreads();
+  for (int i = tid; i < 32 * R; i += 256) {
+    const int m = i / R, j = i % R;
+    if (m0 + m < M) out[(m0 + m) * R + j] = ((red[0][m][j] + red[1][m][j]) + red[2][m][j]) + red[3][m][j];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rproj(const uint16_t* act, int64_t m, int64_t c, const uint16_t* d, bool a_layout, int32_t r,
+                        float* out, hipStream_t s) {
+  if (m == 0) return hipSuccess;
+  const dim3 grid((unsigned)((m + 31) / 32));
+#define QL_RPROJ(RR)                                                                                  \
+  if (a_layout) hipLaunchKernelGGL((rproj_kernel<RR, true>), grid, dim3(256), 0, s, act, m, c, d, out); \
+  else hipLaunchKernelGGL((rproj_kernel<RR, false>), grid, dim3(256), 0, s, act, m, c, d, out);
+  switch (r) {
+    case 8: QL_RPROJ(8) break;
+    case 16: QL_RPROJ(16) break;
+    default: QL_RPROJ(32) break;
+  }
+#undef QL_RPROJ
+  return hipGetLastError();
+}
+
+hipError_t launch_qgemm8(const Gemm8Call& c, hipStream_t s) {
+  P8 p{};
+  p.hi = c.hi;
+  p.lo = c.lo;
+  p.rs = c.rs;
+  p.codes = c.w->codes;
+  p.wscale = reinterpret_cast<const float*>(c.w->scales);
+  p.u = c.u;
+  p.up = c.up;
+  p.out = c.out;
+  p.M = c.m;
+  p.N = c.w->n_out;
+  p.K = c.w->k_in;
+  p.C = c.trans ? p.N : p.K;
+  p.O = c.trans ? p.K : p.N;
+  p.s = c.s;
+  switch (c.r) {
+    case 8: return c.trans ? launch8_w<true, 8>(p, s) : launch8_w<false, 8>(p, s);
+    case 16: return c.trans ? launch8_w<true, 16>(p, s) : launch8_w<false, 16>(p, s);
+    default: return c.trans ? launch8_w<true, 32>(p, s) : launch8_w<false, 32>(p, s);
+  }
+}
+
+}  // namespace ql

@@ -41,6 +41,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "device.h"
 
 namespace ql {
 namespace {
@@ -78,36 +79,6 @@ template <int TM_, int TN, int NTH> struct Shape {
 
 struct Book { float c[16]; };
 
-typedef float f2 __attribute__((ext_vector_type(2)));
-typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  f2 v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
-}
-
-__device__ __forceinline__ bf16x8 tr16x8(const uint16_t* p0, const uint16_t* p1) {
-  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p0);
-  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p1);
-  s16x8 t = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, t);
-}
-
-// Buffer resource over [p, p + bytes): reads past the end return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t bytes) {
-  if (bytes < 0) bytes = 0;
-  if (bytes > 0x7FFFFFFF) bytes = 0x7FFFFFFF;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
-}
-
 // ------------------------------------------------------------------ dequantization
 // One 32-element group of one row of W: codes plus its raw scale word.
 // Loads only fill these registers: every use of a loaded value (scale
@@ -119,8 +90,6 @@ struct WGroup {
   uint32_t ssh;      // Q4_0: bit offset of the fp16 scale in sraw (0 or 16)
 };
 
-// Buffer offset that reads as zero (beyond every resource's size).
-constexpr uint32_t OOB = 0x80000000u;
 
 __device__ __forceinline__ float decode_scale_q40(uint32_t h) {
   h &= 0xFFFF;
@@ -1027,7 +996,24 @@ hipError_t launch_f(const Params& p, bool trans, int r, int splits, hipStream_t 
 
 }  // namespace
 
-size_t qgemm_workspace_bytes(bool trans, int64_t m, int64_t n, int64_t k, int32_t r) {
+// FP8 base, more than SMALL_M tokens: hi [M, C] | lo [M, C] | row scales [M]
+struct Fp8Plan {
+  size_t lo_off = 0, rs_off = 0, total = 0;
+};
+Fp8Plan fp8_plan(bool trans, int64_t m, int64_t n, int64_t k) {
+  Fp8Plan pl;
+  const int64_t C = trans ? n : k;
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  pl.lo_off = al((size_t)m * C);
+  pl.rs_off = pl.lo_off + al((size_t)m * C);
+  pl.total = pl.rs_off + al((size_t)m * 4);
+  return pl;
+}
+
+bool use_fp8_mfma(int32_t fmt, int64_t m) { return fmt == QL_FMT_FP8_E4M3 && m > SMALL_M; }
+
+size_t qgemm_workspace_bytes(int32_t fmt, bool trans, int64_t m, int64_t n, int64_t k, int32_t r) {
+  if (use_fp8_mfma(fmt, m)) return fp8_plan(trans, m, n, k).total;
   return split_plan(trans, m, n, k, r).total;
 }
 
@@ -1046,6 +1032,30 @@ hipError_t launch_qgemm(const GemmCall& c, hipStream_t s) {
   p.C = c.trans ? p.N : p.K;
   p.O = c.trans ? p.K : p.N;
   p.s = c.s;
+  if (use_fp8_mfma(c.w->format, c.m)) {
+    // a1 split of the activation, the rank-r projection (U or V, written to save), fp8 GEMM
+    const Fp8Plan fp = fp8_plan(c.trans, c.m, p.N, p.K);
+    uint8_t* base = reinterpret_cast<uint8_t*>(c.ws);
+    uint8_t* hi = base;
+    uint8_t* lo = base + fp.lo_off;
+    float* rs = reinterpret_cast<float*>(base + fp.rs_off);
+    hipError_t e = launch_act_quant(c.act, c.m, p.C, hi, lo, rs, s);
+    if (e == hipSuccess) e = launch_rproj(c.act, c.m, p.C, c.down, !c.trans, c.r, c.save, s);
+    if (e != hipSuccess) return e;
+    Gemm8Call g{};
+    g.w = c.w;
+    g.trans = c.trans;
+    g.hi = hi;
+    g.lo = lo;
+    g.rs = rs;
+    g.m = c.m;
+    g.u = c.save;
+    g.up = c.up;
+    g.r = c.r;
+    g.s = c.s;
+    g.out = c.out;
+    return launch_qgemm8(g, s);
+  }
   const Nf4Table& t = nf4_table();
   for (int i = 0; i < 16; ++i) p.book.c[i] = t.level[i];
   const SplitPlan pl = split_plan(c.trans, c.m, p.N, p.K, c.r);

@@ -265,6 +265,18 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
 // ------------------------------------------------------------------ a1: activation split
 // One workgroup per row: s = max|x| / 448, t = x / s, hi = E4M3(t),
 // lo = E4M3((t - hi) * 16).
+// a1: per-token two-term E4M3 split.  Row scale s = 2^e, e the smallest
+// integer with 448 * 2^e >= max|x|; t = x * 2^-e is exact (|t| <= 448), and so
+// are t - hi and the factor 16, leaving the two E4M3 roundings (the hardware
+// conversion, nearest even; it is never asked to saturate: |t| <= 448 and
+// |16 (t - hi)| <= 256).  One workgroup per row; the second pass re-reads
+// the row from cache.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+  return (uint32_t)v;
+}
+
 __global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t* __restrict__ x, int64_t k,
                                                              uint8_t* __restrict__ hi,
                                                              uint8_t* __restrict__ lo,
@@ -287,27 +299,37 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t* __r
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = fdiv_rn(amax, 448.0f);
-  if (threadIdx.x == 0) scale[row] = s;
+  int e = 0;
+  if (amax > 0.0f) {
+    const int E = ilogbf(amax);                        // amax = m 2^E, m in [1, 2)
+    e = ldexpf(amax, -E) <= 1.75f ? E - 8 : E - 7;     // 448 2^(E-8) = 1.75 2^E
+  }
+  if (threadIdx.x == 0) scale[row] = amax > 0.0f ? ldexpf(1.0f, e) : 0.0f;
   for (int64_t c = (int64_t)threadIdx.x * 8; c < k; c += kThreads * 8) {
     uint4 t = *reinterpret_cast<const uint4*>(xr + c);
     uint32_t wd[4] = {t.x, t.y, t.z, t.w};
-    uint32_t h2[2] = {0, 0}, l2[2] = {0, 0};
+    float v[8], r[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t bits = (i & 1) ? (wd[i / 2] & 0xFFFF0000u) : (wd[i / 2] << 16);
-      uint32_t ch = 0, cl = 0;
-      if (s != 0.0f) {
-        float tv = fdiv_rn(__uint_as_float(bits), s);
-        ch = f32_to_e4m3(tv);
-        float res = tv - e4m3_to_f32(ch);
-        cl = f32_to_e4m3(res * 16.0f);
-      }
-      h2[i / 4] |= ch << (8 * (i % 4));
-      l2[i / 4] |= cl << (8 * (i % 4));
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = ldexpf(__uint_as_float(wd[i] << 16), -e);
+      v[2 * i + 1] = ldexpf(__uint_as_float(wd[i] & 0xFFFF0000u), -e);
     }
-    *reinterpret_cast<uint2*>(hi + row * k + c) = make_uint2(h2[0], h2[1]);
-    *reinterpret_cast<uint2*>(lo + row * k + c) = make_uint2(l2[0], l2[1]);
+    uint32_t h[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      h[q] = e4m3x4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      typedef float f2v __attribute__((ext_vector_type(2)));
+      const f2v d0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h[q], false);
+      const f2v d1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h[q], true);
+      r[4 * q] = (v[4 * q] - d0.x) * 16.0f;
+      r[4 * q + 1] = (v[4 * q + 1] - d0.y) * 16.0f;
+      r[4 * q + 2] = (v[4 * q + 2] - d1.x) * 16.0f;
+      r[4 * q + 3] = (v[4 * q + 3] - d1.y) * 16.0f;
+    }
+    const uint32_t l0 = e4m3x4(r[0], r[1], r[2], r[3]), l1 = e4m3x4(r[4], r[5], r[6], r[7]);
+    if (amax == 0.0f) h[0] = h[1] = 0u;
+    *reinterpret_cast<uint2*>(hi + row * k + c) = make_uint2(h[0], h[1]);
+    *reinterpret_cast<uint2*>(lo + row * k + c) = make_uint2(amax == 0.0f ? 0u : l0, amax == 0.0f ? 0u : l1);
   }
 }
 

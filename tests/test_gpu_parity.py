@@ -186,6 +186,9 @@ CASES = [
     ("nf4_r8", ofmt.FMT_NF4, 64, 128, 64, 8, 16.0),
     ("nf4_m1", ofmt.FMT_NF4, 1, 128, 32, 16, 16.0),
     ("nf4_tiles_multi", ofmt.FMT_NF4, 512, 1024, 384, 16, 32.0),
+    # FP8 base with more than 64 tokens: two-term E4M3 activations on fp8 matrix cores
+    ("fp8_mfma_ragged", ofmt.FMT_FP8, 300, 160, 224, 16, 32.0),
+    ("fp8_mfma_r8", ofmt.FMT_FP8, 520, 512, 384, 8, 16.0),
     # at most 64 tokens: contraction split across workgroups, fixed-order reduction
     ("small_q40_ragged_k", ofmt.FMT_Q4_0, 17, 1056, 224, 32, 64.0),
     ("small_nf4_splits", ofmt.FMT_NF4, 16, 2048, 320, 16, 32.0),

@@ -168,6 +168,28 @@ def test_act_split_error_bound():
     assert lora.rel_err(xr, x) < 4e-3
 
 
+def test_act_split_scale_is_minimal_power_of_two():
+    """s = 2^e with 448 s >= max|x| > 224 s, the exponent found by scanning
+    the integers directly; and the split of t = x / s is exact in fp32
+    (t - hi needs no rounding), so x is recovered to the bound above."""
+    g = np.random.default_rng(22)
+    x = (g.standard_normal((32, 64)) * np.exp(g.uniform(-60, 60, (32, 1)))).astype(np.float32)
+    x[0, :] = 448.0                                     # boundary: e = 0
+    x[1, :] = 448.0 * 1.0000001                        # just above: e = 1
+    x[2, :] = 224.0                                     # exactly 448 / 2: e = -1
+    hi, lo, s = lora.act_split_e4m3(x)
+    for i in range(x.shape[0]):
+        a = float(np.max(np.abs(x[i])))
+        e = next(k for k in range(-200, 200) if 448.0 * 2.0 ** k >= a)
+        assert s[i] == np.float32(2.0 ** e), (i, s[i], e)
+        assert 448.0 * float(s[i]) >= a > 224.0 * float(s[i])
+    assert s[0] == 1.0 and s[1] == 2.0 and s[2] == 0.5
+    t = x.astype(np.float64) / s[:, None]
+    assert np.all(np.abs(t) <= 448.0)
+    res = t - codecs.e4m3_decode(hi).astype(np.float64)
+    assert np.all(res.astype(np.float32).astype(np.float64) == res)
+
+
 def test_act_split_exact_on_e4m3_grid():
     """Values that are E4M3 codes times the row scale reproduce with lo = 0."""
     c = np.arange(0, 0x7F, dtype=np.uint8)
