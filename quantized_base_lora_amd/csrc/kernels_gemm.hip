@@ -64,7 +64,7 @@ template <int TM_, int TN, int NTH> struct Shape {
   static constexpr int SBT = TN + 32;                 // dX W tile [TK][TN] stride (576 / 320 B rows)
   static constexpr int BF_ELEMS = TN * SA;
   static constexpr int BT_ELEMS = TK * SBT;
-  static constexpr int WAVES_N = TM == 64 ? NW : ((NW == 8 && TN == 256) ? 4 : 2);
+  static constexpr int WAVES_N = TM == 64 ? NW : ((NW == 8 && TN == 256) ? 4 : 2);   // TN = 192: 64 x 96 blocks
   static constexpr int WAVES_M = NW / WAVES_N;
   static constexpr int WM = TM / WAVES_M, WN = TN / WAVES_N;
   static constexpr int MB = WM / 32, NB = WN / 32;    // 32x32 MFMA blocks per wave
@@ -962,6 +962,27 @@ SplitPlan split_plan(bool trans, int64_t m, int64_t n, int64_t k, int r) {
   return pl;
 }
 
+// Output tile width for 256-row tiles: the one with the least time in rounds
+// of 256 workgroups (one per CU) times work per tile, the narrower tiles
+// weighted for their lower MFMA efficiency (more LDS traffic per MFMA);
+// ties go to the wider tile.
+int pick_tn(int64_t m, int64_t o) {
+  const int64_t mt = (m + 255) / 256;
+  const int tns[3] = {256, 192, 128};
+  const double eff[3] = {1.0, 0.95, 0.85};
+  int best = 256;
+  double best_cost = 1e300;
+  for (int i = 0; i < 3; ++i) {
+    const int64_t tiles = mt * ((o + tns[i] - 1) / tns[i]);
+    const double cost = (double)((tiles + 255) / 256) * tns[i] / eff[i];
+    if (cost < best_cost * (1 - 1e-9)) {
+      best_cost = cost;
+      best = tns[i];
+    }
+  }
+  return best;
+}
+
 template <int FMT, bool TRANS, int R>
 hipError_t launch_w(const Params& p, int splits, hipStream_t s) {
   if (splits > 0) {
@@ -972,12 +993,14 @@ hipError_t launch_w(const Params& p, int splits, hipStream_t s) {
                        p.save);
     return hipGetLastError();
   }
-  const int64_t tiles256 = ((p.O + 255) / 256) * ((p.M + 255) / 256);
 #ifndef QL_GEMM_THREADS
 #define QL_GEMM_THREADS 512
 #endif
-  if (tiles256 >= 256) return launch_t<FMT, TRANS, R, 256, 256, QL_GEMM_THREADS, false>(p, 1, s);
-  return launch_t<FMT, TRANS, R, 256, 128, QL_GEMM_THREADS, false>(p, 1, s);
+  switch (pick_tn(p.M, p.O)) {
+    case 256: return launch_t<FMT, TRANS, R, 256, 256, QL_GEMM_THREADS, false>(p, 1, s);
+    case 192: return launch_t<FMT, TRANS, R, 256, 192, QL_GEMM_THREADS, false>(p, 1, s);
+    default: return launch_t<FMT, TRANS, R, 256, 128, QL_GEMM_THREADS, false>(p, 1, s);
+  }
 }
 
 template <int FMT, bool TRANS>
