@@ -42,6 +42,11 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="packed weight copies rotated per step (0: auto)")
     ap.add_argument("--proj", default=None, help="run only this projection (profiling)")
     ap.add_argument("--phase", default="both", choices=["both", "fwd", "bwd"], help="profiling: one pass only")
+    ap.add_argument("--graph", action="store_true",
+                    help="time HIP-graph replays of the step instead of eager launches")
+    ap.add_argument("--streams", action="store_true",
+                    help="run projections that are independent in a decoder layer (q|k|v, gate|up) "
+                         "on parallel streams")
     ap.add_argument("--layers", type=int, default=0,
                     help="stack mode: this many layers, resident vs streamed from pinned host")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -261,7 +266,8 @@ def main():
     if args.layers:
         return bench_stack(args, wl, m)
     dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream()
+    stream = torch.cuda.Stream()             # default priority; capturable (not the legacy stream)
+    torch.cuda.set_stream(stream)
 
     def t(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -297,30 +303,93 @@ def main():
 
     ev_pairs = []
 
-    def step(i, timed):
+    def fwd(d, i, st):
+        B.linear_fwd(d["qws"][i % copies], d["x"], d["a"], d["b"], wl.alpha, y=d["y"], u=d["u"], ws=d["wsf"],
+                     stream=st)
+
+    def bwd(d, i, st):
+        B.linear_bwd(d["qws"][i % copies], d["x"], d["dy"], d["u"], d["a"], d["b"], wl.alpha, dx=d["dx"],
+                     da=d["da"], db=d["db"], ws=d["ws"], stream=st)
+
+    def eager_step(i, timed):
+        """One stream; each forward launch bracketed by events (the roofline's kernel timing)."""
         for d in (projs if args.phase != "bwd" else []):
-            qw = d["qws"][i % copies]
             if timed:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-            B.linear_fwd(qw, d["x"], d["a"], d["b"], wl.alpha, y=d["y"], u=d["u"], ws=d["wsf"], stream=stream)
+            fwd(d, i, stream)
             if timed:
                 e1.record(stream)
                 ev_pairs.append((d["p"], e0, e1))
         for d in (reversed(projs) if args.phase != "fwd" else []):
-            qw = d["qws"][i % copies]
-            B.linear_bwd(qw, d["x"], d["dy"], d["u"], d["a"], d["b"], wl.alpha, dx=d["dx"], da=d["da"],
-                         db=d["db"], ws=d["ws"], stream=stream)
+            bwd(d, i, stream)
+
+    # groups of projections with no data dependence in a decoder layer
+    by_name = {d["p"].name: d for d in projs}
+    order = [g for g in (["q", "k", "v"], ["o"], ["gate", "up"], ["down"])]
+    groups = [[by_name[n] for n in g if n in by_name] for g in order]
+    groups = [g for g in groups if g] or [[d] for d in projs]
+    side = [torch.cuda.Stream() for _ in range(max(len(g) for g in groups))]
+
+    def layer_step(i):
+        """fwd groups in order, then bwd groups in reverse; a group's members on parallel streams."""
+        phases = []
+        if args.phase != "bwd":
+            phases.append((groups, fwd))
+        if args.phase != "fwd":
+            phases.append((list(reversed(groups)), bwd))
+        for gs, fn in phases:
+            for g in gs:
+                if len(g) == 1 or not args.streams:
+                    for d in g:
+                        fn(d, i, stream)
+                    continue
+                fork = torch.cuda.Event()
+                fork.record(stream)
+                for d, st in zip(g, side):
+                    st.wait_event(fork)
+                    fn(d, i, st)
+                for st in side[:len(g)]:
+                    join = torch.cuda.Event()
+                    join.record(st)
+                    stream.wait_event(join)
+
+    # the roofline's kernel timing: eager launches on one stream
+    for i in range(args.warmup):
+        eager_step(i, False)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        eager_step(i, True)
+    torch.cuda.synchronize()
+
+    # the step itself: HIP-graph replays (one graph per rotated weight copy) or eager launches
+    graphs = []
+    if args.graph:
+        for i in range(copies):
+            layer_step(i)                      # warm the side streams outside capture
+        torch.cuda.synchronize()
+        for i in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                layer_step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i):
+        if graphs:
+            graphs[i % copies].replay()
+        else:
+            layer_step(i)
 
     for i in range(args.warmup):
-        step(i, False)
+        run(i)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(args.steps):
-        step(i, True)
+        run(i)
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
@@ -350,7 +419,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.notes, "name": wl.name, "tokens": m, "base_format": FMT_NAME[wl.fmt],
                    "rank": wl.r, "alpha": wl.alpha, "projections": [f"{p.name}:{p.k}->{p.n}" for p in wl.projs],
-                   "packed_copies_rotated": copies},
+                   "packed_copies_rotated": copies,
+                   "step_mode": ("HIP graph replay" if args.graph else "eager launches") + (
+                       ", q|k|v and gate|up on parallel streams" if args.streams else ", one stream")},
         "layer": {"tflops": flops / (ms / 1e3) / 1e12, "frac_bf16_peak": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
                   "algorithmic_bytes": nbytes, "hbm_gbs": nbytes / (ms / 1e3) / 1e9,
                   "frac_hbm_peak": nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS},

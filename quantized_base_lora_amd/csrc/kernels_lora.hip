@@ -16,6 +16,7 @@
 // an agent-scope fence per workgroup, which on a multi-XCD part writes back
 // and invalidates the XCD's L2 each time.
 #include "common.h"
+#include "device.h"
 
 namespace ql {
 namespace {
@@ -70,72 +71,81 @@ __global__ __launch_bounds__(NT) void grad_kernel(GradArgs a) {
   const int xr = tid >> 3, xc = (tid & 7) * 8;       // X: rows xr, xr + 32; 8 columns
   const int qr = tid >> 2, qc = (tid & 3) * QPT;
 
-  // loads run DEPTH - 1 steps ahead of the LDS stores (a ring of register sets)
+  // loads run DEPTH - 1 steps ahead of the LDS stores (a ring of register sets).
+  // Reads past the partition or past the last column go to an out-of-range
+  // buffer offset and return zero, so no loaded value is inspected at issue.
   constexpr int DEPTH = 4;
+  const __amdgpu_buffer_rsrc_t rx = rsrc(pr.x + mq0 * pr.pdim, (mq1 - mq0) * pr.pdim * 2);
+  const __amdgpu_buffer_rsrc_t rq = rsrc(pr.q + mq0 * R, (mq1 - mq0) * R * 4);
+  const int NS = (int)((mq1 - mq0 + TMC - 1) / TMC);
   uint4 xv[DEPTH][2];
-  float qv[DEPTH][QPT];
-  auto load = [&](int slot, int64_t mc) {
+  uint32_t qv[DEPTH][QPT];
+  auto load = [&](int slot, int step) {
+    const int64_t r0 = (int64_t)step * TMC;            // first row of the step, partition-relative
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      int64_t row = mc + xr + 32 * i, col = p0 + xc;
-      const bool ok = row < mq1 && col < pr.pdim;
-      row = row < mq1 ? row : mq1 - 1;
-      col = col < pr.pdim ? col : pr.pdim - 8;
-      const uint4 v = *reinterpret_cast<const uint4*>(pr.x + row * pr.pdim + col);
-      xv[slot][i] = ok ? v : make_uint4(0, 0, 0, 0);
+      const int64_t row = r0 + xr + 32 * i, col = p0 + xc;
+      xv[slot][i] = bload16(rx, col < pr.pdim ? (uint32_t)((row * pr.pdim + col) * 2) : OOB);
     }
-    int64_t row = mc + qr;
-    const bool ok = row < mq1;
-    row = row < mq1 ? row : mq1 - 1;
-    const float* qs = pr.q + row * R + qc;
+    const uint32_t qoff = (uint32_t)(((r0 + qr) * R + qc) * 4);
 #pragma unroll
-    for (int t = 0; t < QPT; ++t) qv[slot][t] = ok ? qs[t] : 0.0f;
+    for (int t = 0; t < QPT; t += 4) {
+      if constexpr (QPT >= 4) {
+        const uint4 v = bload16(rq, qoff + 4 * t);
+        qv[slot][t] = v.x; qv[slot][t + 1] = v.y; qv[slot][t + 2] = v.z; qv[slot][t + 3] = v.w;
+      }
+    }
+    if constexpr (QPT < 4) {
+#pragma unroll
+      for (int t = 0; t < QPT; ++t) qv[slot][t] = bload4(rq, qoff + 4 * t);
+    }
+  };
+  auto step = [&](int u) {
+    lds_barrier();                                    // previous step's readers are done
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(Xs + (xr + 32 * i) * SX + xc) = xv[u][i];
+#pragma unroll
+    for (int t = 0; t < QPT; ++t) {
+      const float q = __uint_as_float(qv[u][t]);
+      const __bf16 h = (__bf16)q;
+      const __bf16 l = (__bf16)(q - (float)h);
+      Qh[qr * SQ + qc + t] = __builtin_bit_cast(uint16_t, h);
+      Ql[qr * SQ + qc + t] = __builtin_bit_cast(uint16_t, l);
+    }
+    lds_barrier();
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      const int b = lane >> 4, sl = lane & 15;
+      const int rbase = 32 * kp + 8 * b + (sl >> 2);
+      const int xcol = 16 * wave + 4 * (sl & 3);
+      const bf16x8 af = tr16x8(Xs + rbase * SX + xcol, Xs + (rbase + 4) * SX + xcol);
+#pragma unroll
+      for (int jb = 0; jb < RB; ++jb) {
+        const int col = 16 * jb + 4 * (sl & 3);
+        const bf16x8 th = tr16x8(Qh + rbase * SQ + col, Qh + (rbase + 4) * SQ + col);
+        const bf16x8 tl = tr16x8(Ql + rbase * SQ + col, Ql + (rbase + 4) * SQ + col);
+        acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, th, acc[jb], 0, 0, 0);
+        acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, tl, acc[jb], 0, 0, 0);
+      }
+    }
   };
 
 #pragma unroll
-  for (int u = 0; u < DEPTH - 1; ++u)
-    if (mq0 + u * TMC < mq1) load(u, mq0 + u * TMC);
-  for (int64_t base = mq0; base < mq1; base += DEPTH * TMC) {
+  for (int u = 0; u < DEPTH - 1; ++u) load(u, u);
+  // whole chunks of DEPTH steps run branch-free with static ring slots
+  int st = 0;
+  for (; st + DEPTH <= NS; st += DEPTH) {
 #pragma unroll
     for (int u = 0; u < DEPTH; ++u) {
-      const int64_t mc = base + u * TMC;
-      if (mc >= mq1) break;
-      const int64_t ahead = mc + (DEPTH - 1) * TMC;
-      if (ahead < mq1) load((u + DEPTH - 1) % DEPTH, ahead);
-      lds_barrier();                                  // previous step's readers are done
+      load((u + DEPTH - 1) % DEPTH, st + u + DEPTH - 1);
+      step(u);
+    }
+  }
 #pragma unroll
-      for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(Xs + (xr + 32 * i) * SX + xc) = xv[u][i];
-#pragma unroll
-      for (int t = 0; t < QPT; ++t) {
-        const __bf16 h = (__bf16)qv[u][t];
-        const __bf16 l = (__bf16)(qv[u][t] - (float)h);
-        Qh[qr * SQ + qc + t] = __builtin_bit_cast(uint16_t, h);
-        Ql[qr * SQ + qc + t] = __builtin_bit_cast(uint16_t, l);
-      }
-      lds_barrier();
-#pragma unroll
-      for (int kp = 0; kp < 2; ++kp) {
-        const int b = lane >> 4, sl = lane & 15;
-        const int rbase = 32 * kp + 8 * b + (sl >> 2);
-        typedef short s16x8 __attribute__((ext_vector_type(8)));
-        const int xcol = 16 * wave + 4 * (sl & 3);
-        s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Xs + rbase * SX + xcol));
-        s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Xs + (rbase + 4) * SX + xcol));
-        s16x8 tx = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        const bf16x8 af = __builtin_bit_cast(bf16x8, tx);
-#pragma unroll
-        for (int jb = 0; jb < RB; ++jb) {
-          const int col = 16 * jb + 4 * (sl & 3);
-          s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Qh + rbase * SQ + col));
-          s16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Qh + (rbase + 4) * SQ + col));
-          s16x4 l0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Ql + rbase * SQ + col));
-          s16x4 l1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(Ql + (rbase + 4) * SQ + col));
-          s16x8 th = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-          s16x8 tl = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-          acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8, th), acc[jb], 0, 0, 0);
-          acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8, tl), acc[jb], 0, 0, 0);
-        }
-      }
+  for (int u = 0; u < DEPTH; ++u) {
+    if (st + u < NS) {
+      load((u + DEPTH - 1) % DEPTH, st + u + DEPTH - 1);
+      step(u);
     }
   }
   // partial[q][p][j]: lane holds column j = 16 jb + lane%16, rows 4 (lane/16) + e
