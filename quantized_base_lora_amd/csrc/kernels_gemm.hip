@@ -638,9 +638,17 @@ void qsplit_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t o0 = (int64_t)blockIdx.x * TN;
+  // units (column tile, split) are handed to the 8 XCDs (round robin over the
+  // linear workgroup id) in contiguous runs, so adjacent column tiles of one
+  // split share their XCD's L2: a dX step reads 64 of the 128 bytes of each
+  // W-row line, and the neighbouring tile reads the other half
+  const int nunits = (int)(gridDim.x * gridDim.y);
+  int unit = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+  if ((nunits & 7) == 0) unit = (unit & 7) * (nunits >> 3) + (unit >> 3);
+  const int ntile = unit % (int)gridDim.x, split = unit / (int)gridDim.x;
+  const int64_t o0 = (int64_t)ntile * TN;
   const int KT = (int)((p.C + TK - 1) / TK);
-  const int kbeg = (int)blockIdx.y * p.sps;
+  const int kbeg = split * p.sps;
   const int kend = min(KT, kbeg + p.sps);
   const int NKT = kend - kbeg;
 
@@ -808,7 +816,7 @@ void qsplit_kernel(Params p) {
   }
 
   // fp32 partials: lane holds row (lane & 31) of block i and 4 consecutive columns per 8
-  float* pp = p.part + (int64_t)blockIdx.y * p.M * p.O;
+  float* pp = p.part + (int64_t)split * p.M * p.O;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int64_t row = 32 * i + (lane & 31);
@@ -822,8 +830,8 @@ void qsplit_kernel(Params p) {
       }
     }
   }
-  if (blockIdx.x == 0) {
-    float* up = p.upart + (int64_t)blockIdx.y * p.M * R;
+  if (ntile == 0) {
+    float* up = p.upart + (int64_t)split * p.M * R;
 #pragma unroll
     for (int jb = 0; jb < RB; ++jb)
 #pragma unroll
