@@ -1,0 +1,384 @@
+// a3 / a6 for at most 64 tokens: the split-contraction path.
+//
+// With so few tokens the base GEMM is bound by streaming and dequantizing W;
+// the contraction is split across workgroups (fp32 partials in the caller's
+// workspace) and a second kernel adds the partials in split order, fuses the
+// LoRA term and rounds once to bf16, so results do not depend on scheduling.
+#include <algorithm>
+
+#include "dequant.h"
+
+namespace ql {
+namespace {
+
+// At most 64 tokens the base GEMM is bound by streaming W, and each
+// workgroup sees only a few contraction steps, so every step's loads must be
+// in flight long before they are needed: a ring of D register stages keeps
+// the loads of steps it+1 .. it+D outstanding while step it computes.  Tile:
+// 64 rows (all tokens) x 128 output columns, four waves side by side (64 x 32
+// each), the contraction split over blockIdx.y; fp32 partial sums out.
+template <int FMT, bool TRANS, int R>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void qsplit_kernel(Params p) {
+  constexpr int TM = 64, TN = 128, NT = 256, D = 4;
+  static_assert(D % 2 == 0, "buffer parity of a step is its position in the chunk");
+  constexpr int SBT = TN + 32;
+  constexpr int A_EL = TM * SA;
+  constexpr int B_EL = TRANS ? TK * SBT : TN * SA;
+  constexpr int D_EL = TRANS ? BL_ELEMS : AD_ELEMS;
+  constexpr int STAGE = A_EL + B_EL + D_EL;
+  constexpr int RB = (R + 15) / 16;
+  constexpr int GPR = TRANS ? TN / 32 : TK / 32;
+  constexpr bool FP8 = FMT == QL_FMT_FP8_E4M3;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // units (column tile, split) are handed to the 8 XCDs (round robin over the
+  // linear workgroup id) in contiguous runs, so adjacent column tiles of one
+  // split share their XCD's L2: a dX step reads 64 of the 128 bytes of each
+  // W-row line, and the neighbouring tile reads the other half
+  const int nunits = (int)(gridDim.x * gridDim.y);
+  int unit = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+  if ((nunits & 7) == 0) unit = (unit & 7) * (nunits >> 3) + (unit >> 3);
+  const int ntile = unit % (int)gridDim.x, split = unit / (int)gridDim.x;
+  const int64_t o0 = (int64_t)ntile * TN;
+  const int KT = (int)((p.C + TK - 1) / TK);
+  const int kbeg = split * p.sps;
+  const int kend = min(KT, kbeg + p.sps);
+  const int NKT = kend - kbeg;
+
+  const __amdgpu_buffer_rsrc_t ract = rsrc(p.act, p.M * p.C * 2);
+  const int64_t crow = FP8 ? p.K : p.K / 2;
+  const int64_t wrow0 = TRANS ? 0 : o0;
+  const int64_t wcol0 = TRANS ? (FP8 ? o0 : o0 / 2) : 0;
+  const __amdgpu_buffer_rsrc_t rcode = rsrc(p.codes + wrow0 * crow + wcol0, (p.N - wrow0) * crow - wcol0);
+  const int64_t srow = FMT == QL_FMT_Q4_0 ? p.K / 32 : p.K / 64;
+  const int64_t ssz = FMT == QL_FMT_Q4_0 ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t rscale =
+      rsrc((const char*)p.scales + wrow0 * srow * ssz, (p.N - wrow0) * srow * ssz);
+  const __amdgpu_buffer_rsrc_t rdown = rsrc(p.down, (int64_t)R * p.C * 2);
+  float tscale = 0.0f;
+  if constexpr (FP8) tscale = reinterpret_cast<const float*>(p.scales)[0];
+
+  const int arow = tid >> 3, acol = (tid & 7) * 8;   // act rows arow, arow + 32
+  const int wr = tid / GPR, wg = tid % GPR;          // one W group per thread per step
+  const bool wg_in = !TRANS || (o0 + 32 * (wg + 1) <= p.K);
+  constexpr int DPR = TRANS ? R / 8 : TK / 8;
+  const bool dload = tid < 8 * R;
+  const int drow = tid / DPR, dcol = (tid % DPR) * 8;
+
+  struct Slot {
+    uint4 a0, a1, d;
+    WGroup w;
+  };
+  Slot ring[D];
+  // loads of step kt; a step past the split's end reads zeros (no memory traffic)
+  auto issue = [&](Slot& sl, int kt) {
+    const bool sv = kt < kend;
+    const int64_t c0 = (int64_t)kt * TK;
+    const bool alive = sv && c0 + acol < p.C;
+    sl.a0 = bload16(ract, alive ? (uint32_t)((arow * p.C + c0 + acol) * 2) : OOB);
+    sl.a1 = bload16(ract, alive ? (uint32_t)(((arow + 32) * p.C + c0 + acol) * 2) : OOB);
+    const int64_t wrow = TRANS ? c0 + wr : wr;
+    const int64_t kgrp = TRANS ? wg : (c0 >> 5) + wg;
+    const bool wlive = sv && (TRANS || c0 + 32 * wg < p.C);
+    const uint32_t coff = wlive ? (uint32_t)(wrow * crow + kgrp * (FP8 ? 32 : 16)) : OOB;
+    sl.w.c0 = bload16(rcode, coff);
+    sl.w.ssh = 0;
+    if constexpr (FP8) {
+      sl.w.c1 = bload16(rcode, wlive ? coff + 16 : OOB);
+      sl.w.sraw = 0;
+    } else {
+      sl.w.c1 = make_uint4(0, 0, 0, 0);
+      const int64_t kabs = TRANS ? (o0 >> 5) + wg : kgrp;
+      if constexpr (FMT == QL_FMT_Q4_0) {
+        const int64_t idx = wrow * srow + kabs;
+        sl.w.sraw = bload4(rscale, wlive ? (uint32_t)((idx * 2) & ~3LL) : OOB);
+        sl.w.ssh = (uint32_t)(idx & 1) * 16;
+      } else {
+        sl.w.sraw = bload4(rscale, wlive ? (uint32_t)((wrow * srow + (kabs >> 1)) * 4) : OOB);
+      }
+    }
+    uint32_t doff;
+    if constexpr (TRANS) doff = (uint32_t)(((c0 + drow) * R + dcol) * 2);
+    else doff = c0 + dcol < p.C ? (uint32_t)((drow * p.C + c0 + dcol) * 2) : OOB;
+    sl.d = bload16(rdown, dload && sv ? doff : OOB);
+  };
+  auto store = [&](const Slot& sl, uint16_t* st) {
+    *reinterpret_cast<uint4*>(st + arow * SA + acol) = sl.a0;
+    *reinterpret_cast<uint4*>(st + (arow + 32) * SA + acol) = sl.a1;
+    float scale;
+    if constexpr (FP8) scale = tscale;
+    else if constexpr (FMT == QL_FMT_Q4_0) scale = decode_scale_q40(sl.w.sraw >> sl.w.ssh);
+    else scale = __uint_as_float(sl.w.sraw);
+    Deq<FMT> dq;
+    dq.prepare(sl.w, wg_in ? scale : 0.0f, p.book);
+    uint16_t* dst = st + A_EL + (TRANS ? wr * SBT : wr * SA) + wg * 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(dst + 8 * i) = dq.piece(i);
+    if (dload) *reinterpret_cast<uint4*>(st + A_EL + B_EL + drow * (TRANS ? SL : SA) + dcol) = sl.d;
+  };
+  // every slot starts defined (the prologue may leave some unused)
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    ring[u].a0 = ring[u].a1 = ring[u].d = ring[u].w.c0 = ring[u].w.c1 = make_uint4(0, 0, 0, 0);
+    ring[u].w.sraw = ring[u].w.ssh = 0;
+  }
+
+  f32x16 acc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
+  f32x4 uacc[RB];
+#pragma unroll
+  for (int jb = 0; jb < RB; ++jb) uacc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const uint16_t* st) {
+    const uint16_t* As = st;
+    const uint16_t* Bs = st + A_EL;
+    const uint16_t* Ds = st + A_EL + B_EL;
+#pragma unroll
+    for (int ks = 0; ks < TK / 16; ++ks) {
+      bf16x8 af[2], bf;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(As + (32 * i + (lane & 31)) * SA + ks * 16 + 8 * (lane >> 5));
+      if constexpr (TRANS) {
+        const int b = lane >> 4, sl = lane & 15;
+        const int col = 32 * wave + 16 * (b & 1) + 4 * (sl & 3);
+        const int row = ks * 16 + 8 * (b >> 1) + (sl >> 2);
+        bf = tr16x8(Bs + row * SBT + col, Bs + (row + 4) * SBT + col);
+      } else {
+        bf = *reinterpret_cast<const bf16x8*>(Bs + (32 * wave + (lane & 31)) * SA + ks * 16 + 8 * (lane >> 5));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af[i], acc[i], 0, 0, 0);
+    }
+    // rank-r projection of rows 16 wave .. 16 wave + 15 over this stage
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(As + (16 * wave + (lane & 15)) * SA + 32 * kp + 8 * (lane >> 4));
+#pragma unroll
+      for (int jb = 0; jb < RB; ++jb) {
+        bf16x8 bd;
+        if constexpr (TRANS) {
+          const int b = lane >> 4, sl = lane & 15;
+          const int row = 32 * kp + 8 * b + (sl >> 2), col = 16 * jb + 4 * (sl & 3);
+          bd = tr16x8(Ds + row * SL + col, Ds + (row + 4) * SL + col);
+        } else {
+          bd = *reinterpret_cast<const bf16x8*>(Ds + (16 * jb + (lane & 15)) * SA + 32 * kp + 8 * (lane >> 4));
+        }
+        uacc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bd, uacc[jb], 0, 0, 0);
+      }
+    }
+  };
+
+  for (int i = tid; i < D_EL; i += NT) {
+    smem[A_EL + B_EL + i] = 0;
+    smem[STAGE + A_EL + B_EL + i] = 0;
+  }
+  // prologue: D stages in flight, the first stored and its slot refilled
+#pragma unroll
+  for (int u = 0; u < D; ++u) issue(ring[u], kbeg + u);
+  lds_barrier();
+  store(ring[0], smem);
+  issue(ring[0], kbeg + D);
+  lds_barrier();
+
+  // step it: store stage it+1 from its ring slot and refill the slot with
+  // stage it+1+D, then compute stage it.  Whole chunks of D steps run
+  // branch-free (slot indices and buffer parities static, D even), so the
+  // waits for each slot count only the loads issued after it.
+  int it = 0;
+  for (; it + D < NKT; it += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      store(ring[(u + 1) % D], smem + ((u + 1) & 1) * STAGE);
+      issue(ring[(u + 1) % D], kbeg + it + u + 1 + D);
+      compute(smem + (u & 1) * STAGE);
+      lds_barrier();
+    }
+  }
+  // the last (at most D) steps: everything they need is already in flight
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    if (it + u < NKT) {
+      if (it + u + 1 < NKT) store(ring[(u + 1) % D], smem + ((u + 1) & 1) * STAGE);
+      compute(smem + (u & 1) * STAGE);
+      lds_barrier();
+    }
+  }
+
+  // fp32 partials: lane holds row (lane & 31) of block i and 4 consecutive columns per 8
+  float* pp = p.part + (int64_t)split * p.M * p.O;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t row = 32 * i + (lane & 31);
+    if (row < p.M) {
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const int64_t col = o0 + 32 * wave + 8 * k4 + 4 * (lane >> 5);
+        if (col < p.O)
+          *reinterpret_cast<float4*>(pp + row * p.O + col) =
+              make_float4(acc[i][4 * k4], acc[i][4 * k4 + 1], acc[i][4 * k4 + 2], acc[i][4 * k4 + 3]);
+      }
+    }
+  }
+  if (ntile == 0) {
+    float* up = p.upart + (int64_t)split * p.M * R;
+#pragma unroll
+    for (int jb = 0; jb < RB; ++jb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * wave + 4 * (lane >> 4) + e;
+        const int j = 16 * jb + (lane & 15);
+        if (j < R && row < p.M) up[row * R + j] = uacc[jb][e];
+      }
+  }
+}
+
+template <int FMT, bool TRANS, int R>
+hipError_t launch_split(const Params& p, int splits, hipStream_t s) {
+  constexpr int B_EL = TRANS ? TK * (128 + 32) : 128 * SA;
+  constexpr int D_EL = TRANS ? BL_ELEMS : AD_ELEMS;
+  constexpr size_t smem = 2 * (size_t)(64 * SA + B_EL + D_EL) * sizeof(uint16_t);
+  static_assert(smem <= 80 * 1024, "two workgroups per CU");
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)qsplit_kernel<FMT, TRANS, R>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((qsplit_kernel<FMT, TRANS, R>), dim3((unsigned)((p.O + 127) / 128), (unsigned)splits),
+                     dim3(256), smem, s, p);
+  return hipGetLastError();
+}
+
+// Split-contraction reduction and epilogue: per output element the partials
+// are summed in split order (deterministic), the LoRA term s . U . up^T is
+// added in fp32 (U = sum of its partials), and the sum is rounded once to
+// bf16.  Column-slab 0 also writes U (forward) or V (dX).  One thread per 4
+// consecutive outputs of one row.
+template <int R>
+__global__ __launch_bounds__(128) void split_reduce_kernel(const float* __restrict__ part,
+                                                           const float* __restrict__ upart, int splits,
+                                                           int64_t M, int64_t O, const uint16_t* __restrict__ up,
+                                                           bool trans, float s, uint16_t* __restrict__ out,
+                                                           float* __restrict__ save) {
+  __shared__ float us[R];
+  const int64_t m = blockIdx.y;
+  const int tid = threadIdx.x;
+  // splits past the last read as zero through the resource bounds
+  const __amdgpu_buffer_rsrc_t rp = rsrc(part, (int64_t)splits * M * O * 4);
+  const __amdgpu_buffer_rsrc_t ru = rsrc(upart, (int64_t)splits * M * R * 4);
+  if (tid < R) {
+    uint32_t v[MAX_SPLITS];
+#pragma unroll
+    for (int sp = 0; sp < MAX_SPLITS; ++sp) v[sp] = bload4(ru, (uint32_t)((((int64_t)sp * M + m) * R + tid) * 4));
+    float u = 0.0f;
+#pragma unroll
+    for (int sp = 0; sp < MAX_SPLITS; ++sp) u += __uint_as_float(v[sp]);
+    if (save && blockIdx.x == 0) save[m * R + tid] = u;
+    us[tid] = s * u;
+  }
+  const int64_t o = (int64_t)blockIdx.x * 512 + tid * 4;
+  const bool live = o < O;
+  // the up-matrix entries of these 4 outputs, as bf16 pairs
+  uint32_t w[4][R / 2];
+  if (live) {
+    if (!trans) {   // B [O, R]: 4 rows of R
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int q = 0; q < R / 8; ++q) {
+          const uint4 v = *reinterpret_cast<const uint4*>(up + (o + c) * R + 8 * q);
+          w[c][4 * q] = v.x; w[c][4 * q + 1] = v.y; w[c][4 * q + 2] = v.z; w[c][4 * q + 3] = v.w;
+        }
+    } else {        // A [R, O]: 4 consecutive entries of each row j
+#pragma unroll
+      for (int j = 0; j < R; j += 2) {
+        const uint2 v0 = *reinterpret_cast<const uint2*>(up + (int64_t)j * O + o);
+        const uint2 v1 = *reinterpret_cast<const uint2*>(up + (int64_t)(j + 1) * O + o);
+        w[0][j / 2] = (v0.x & 0xFFFF) | (v1.x << 16);
+        w[1][j / 2] = (v0.x >> 16) | (v1.x & 0xFFFF0000u);
+        w[2][j / 2] = (v0.y & 0xFFFF) | (v1.y << 16);
+        w[3][j / 2] = (v0.y >> 16) | (v1.y & 0xFFFF0000u);
+      }
+    }
+  }
+  // all partial loads in flight at once, then summed in split order
+  uint4 pv[MAX_SPLITS];
+#pragma unroll
+  for (int sp = 0; sp < MAX_SPLITS; ++sp)
+    pv[sp] = bload16(rp, live ? (uint32_t)((((int64_t)sp * M + m) * O + o) * 4) : OOB);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int sp = 0; sp < MAX_SPLITS; ++sp) {
+    acc.x += __uint_as_float(pv[sp].x); acc.y += __uint_as_float(pv[sp].y);
+    acc.z += __uint_as_float(pv[sp].z); acc.w += __uint_as_float(pv[sp].w);
+  }
+  __syncthreads();
+  if (!live) return;
+  float l[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int q = 0; q < R / 2; ++q) {
+      l[c] += us[2 * q] * __uint_as_float(w[c][q] << 16);
+      l[c] += us[2 * q + 1] * __uint_as_float(w[c][q] & 0xFFFF0000u);
+    }
+  const uint32_t lo = pack_bf16x2(acc.x + l[0], acc.y + l[1]);
+  const uint32_t hi = pack_bf16x2(acc.z + l[2], acc.w + l[3]);
+  *reinterpret_cast<uint2*>(out + m * O + o) = make_uint2(lo, hi);
+}
+
+template <int FMT, bool TRANS, int R>
+hipError_t launch_path(const Params& p, int splits, hipStream_t s) {
+  hipError_t e = launch_split<FMT, TRANS, R>(p, splits, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(split_reduce_kernel<R>, dim3((unsigned)((p.O + 511) / 512), (unsigned)p.M), dim3(128), 0, s,
+                     (const float*)p.part, (const float*)p.upart, splits, p.M, p.O, p.up, TRANS, p.s, p.out, p.save);
+  return hipGetLastError();
+}
+
+template <int FMT, bool TRANS>
+hipError_t launch_r(const Params& p, int r, int splits, hipStream_t s) {
+  switch (r) {
+    case 8: return launch_path<FMT, TRANS, 8>(p, splits, s);
+    case 16: return launch_path<FMT, TRANS, 16>(p, splits, s);
+    default: return launch_path<FMT, TRANS, 32>(p, splits, s);
+  }
+}
+
+}  // namespace
+
+static_assert(MAX_SPLITS == 16, "split_reduce_kernel unrolls over 16 splits");
+
+SplitPlan split_plan(bool trans, int64_t m, int64_t n, int64_t k, int r) {
+  SplitPlan pl;
+  if (m <= 0 || m > SMALL_M) return pl;
+  const int64_t O = trans ? k : n, C = trans ? n : k;
+  const int64_t KT = (C + TK - 1) / TK;
+  const int64_t tn = (O + STN - 1) / STN;
+  int64_t sp = std::min<int64_t>({std::max<int64_t>(1, KT / 4), 512 / tn, (int64_t)MAX_SPLITS});
+  if (sp < 1) sp = 1;
+  pl.sps = (int)((KT + sp - 1) / sp);
+  pl.splits = (int)((KT + pl.sps - 1) / pl.sps);
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  pl.upart_off = al((size_t)pl.splits * m * O * 4);
+  pl.total = pl.upart_off + al((size_t)pl.splits * m * r * 4);
+  return pl;
+}
+
+
+hipError_t launch_split_path(int fmt, bool trans, int r, const Params& p, int splits, hipStream_t s) {
+  switch (fmt) {
+    case QL_FMT_Q4_0: return trans ? launch_r<QL_FMT_Q4_0, true>(p, r, splits, s) : launch_r<QL_FMT_Q4_0, false>(p, r, splits, s);
+    case QL_FMT_NF4: return trans ? launch_r<QL_FMT_NF4, true>(p, r, splits, s) : launch_r<QL_FMT_NF4, false>(p, r, splits, s);
+    default: return trans ? launch_r<QL_FMT_FP8_E4M3, true>(p, r, splits, s) : launch_r<QL_FMT_FP8_E4M3, false>(p, r, splits, s);
+  }
+}
+
+}  // namespace ql
