@@ -358,6 +358,28 @@ void qgemm_kernel(Params p) {
     read_frags(ns, 0);
     mfma_ks(3);
   }
+  // the tile's slice of the up matrix, loaded now so the epilogue does not
+  // wait for it: forward B rows o0 .. o0+TN (contiguous, 8 elements per
+  // piece), dX A[j][o0 .. o0+TN] (8 columns of one row per piece)
+  constexpr int UPP = TN * R / 8;                    // 16-byte pieces
+  constexpr int UPT = (UPP + NT - 1) / NT;
+  uint4 upv[UPT];
+  {
+    const __amdgpu_buffer_rsrc_t rup = TRANS ? rsrc(p.up, (int64_t)R * p.K * 2)
+                                             : rsrc(p.up + o0 * R, (p.N - o0) * R * 2);
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int q = tid + NT * u;
+      uint32_t off = OOB;
+      if constexpr (TRANS) {
+        const int j = q / (TN / 8), c = (q % (TN / 8)) * 8;
+        if (q < UPP && o0 + c < p.K) off = (uint32_t)((j * p.K + o0 + c) * 2);
+      } else {
+        if (q < UPP) off = (uint32_t)(q * 16);
+      }
+      upv[u] = bload16(rup, off);
+    }
+  }
   {
     const uint16_t* cs = smem + ((NKT - 1) & 1) * STAGE;
     read_frags(cs, 1);
@@ -394,12 +416,25 @@ void qgemm_kernel(Params p) {
           Ax[row * SX + R + j] = __builtin_bit_cast(uint16_t, l);
         }
       }
-  for (int idx = tid; idx < TN * R; idx += NT) {
-    const int col = idx / R, j = idx % R;
-    uint16_t v = 0;
-    if (o0 + col < p.O) v = TRANS ? p.up[(int64_t)j * p.K + o0 + col] : p.up[(o0 + col) * R + j];
-    Bx[col * SX + j] = v;
-    Bx[col * SX + R + j] = v;
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) {
+    const int q = tid + NT * u;
+    if (q < UPP) {
+      if constexpr (TRANS) {
+        const int j = q / (TN / 8), c = (q % (TN / 8)) * 8;
+        const uint32_t w[4] = {upv[u].x, upv[u].y, upv[u].z, upv[u].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint16_t v = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+          Bx[(c + e) * SX + j] = v;
+          Bx[(c + e) * SX + R + j] = v;
+        }
+      } else {
+        const int col = q / (R / 8), j = (q % (R / 8)) * 8;
+        *reinterpret_cast<uint4*>(Bx + col * SX + j) = upv[u];
+        *reinterpret_cast<uint4*>(Bx + col * SX + R + j) = upv[u];
+      }
+    }
   }
   lds_barrier();
 #pragma unroll
@@ -417,23 +452,30 @@ void qgemm_kernel(Params p) {
       for (int j = 0; j < NB; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
   }
-  // ---- store bf16: lane holds row (lane & 31) and, per 4 accumulators, 4 consecutive columns
+  // ---- store bf16.  Lane l holds row l % 32 and, in accumulators 4g .. 4g+3,
+  // columns 8g + 4 (l / 32) .. +3.  For each pair of column groups (2p, 2p+1)
+  // lanes l and l + 32 trade halves (v_permlane32_swap): lane l then holds
+  // the 8 columns of group 2p, lane l + 32 those of group 2p+1, and each
+  // writes them with one 16-byte store.
+  const int hl = lane >> 5;
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     const int64_t row = m0 + S::WM * wm + 32 * i + (lane & 31);
-    if (row < p.M) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-          const int64_t col = o0 + S::WN * wn + 32 * j + 8 * k4 + 4 * (lane >> 5);
-          if (col < p.O) {
-            const uint32_t lo = pack_bf16x2(acc[i][j][4 * k4 + 0], acc[i][j][4 * k4 + 1]);
-            const uint32_t hi = pack_bf16x2(acc[i][j][4 * k4 + 2], acc[i][j][4 * k4 + 3]);
-            *reinterpret_cast<uint2*>(p.out + row * p.O + col) = make_uint2(lo, hi);
-          }
-        }
-    }
+      for (int pr = 0; pr < 2; ++pr) {
+        const uint32_t a0 = pack_bf16x2(acc[i][j][8 * pr + 0], acc[i][j][8 * pr + 1]);
+        const uint32_t a1 = pack_bf16x2(acc[i][j][8 * pr + 2], acc[i][j][8 * pr + 3]);
+        const uint32_t b0 = pack_bf16x2(acc[i][j][8 * pr + 4], acc[i][j][8 * pr + 5]);
+        const uint32_t b1 = pack_bf16x2(acc[i][j][8 * pr + 6], acc[i][j][8 * pr + 7]);
+        // lanes >= 32 of the first operand trade places with lanes < 32 of the second
+        const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+        const int64_t col = o0 + S::WN * wn + 32 * j + 8 * (2 * pr + hl);
+        if (row < p.M && col < p.O)
+          *reinterpret_cast<uint4*>(p.out + row * p.O + col) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+      }
   }
 }
 
