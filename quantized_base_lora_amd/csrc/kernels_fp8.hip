@@ -192,6 +192,40 @@ void qgemm8_kernel(P8 p) {
     compute(sm8 + (kt & 1) * S::STAGE);
     lds_barrier();
   }
+  // epilogue operands, loaded now so their latency hides under the last
+  // stage: row scales, the tile's rows of U (fp32, contiguous) and its slice
+  // of the up matrix (forward B rows o0 .. o0+TN; dX A[j][o0 .. o0+TN])
+  constexpr int UQ = TM * R / 4, UQT = UQ / NT > 0 ? UQ / NT : 1;   // 16-byte U pieces
+  constexpr int UPP = TN * R / 8;
+  constexpr int UPT = (UPP + NT - 1) / NT;
+  float rsv[MB];
+  uint4 uv[UQT], upv[UPT];
+  {
+    const __amdgpu_buffer_rsrc_t rrs = rsrc(p.rs + m0, (p.M - m0) * 4);
+    const __amdgpu_buffer_rsrc_t ru = rsrc(p.u + m0 * R, (p.M - m0) * R * 4);
+    const __amdgpu_buffer_rsrc_t rup = TRANS ? rsrc(p.up, (int64_t)R * p.K * 2)
+                                             : rsrc(p.up + o0 * R, (p.N - o0) * R * 2);
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+      rsv[i] = __uint_as_float(bload4(rrs, (uint32_t)((S::WM * wm + 32 * i + (lane & 31)) * 4)));
+#pragma unroll
+    for (int u = 0; u < UQT; ++u) {
+      const int q = tid + NT * u;
+      uv[u] = bload16(ru, q < UQ ? (uint32_t)(q * 16) : OOB);
+    }
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int q = tid + NT * u;
+      uint32_t off = OOB;
+      if constexpr (TRANS) {
+        const int j = q / (TN / 8), c = (q % (TN / 8)) * 8;
+        if (q < UPP && o0 + c < p.K) off = (uint32_t)((j * p.K + o0 + c) * 2);
+      } else {
+        if (q < UPP) off = (uint32_t)(q * 16);
+      }
+      upv[u] = bload16(rup, off);
+    }
+  }
   compute(sm8 + ((KT - 1) & 1) * S::STAGE);
   lds_barrier();
 
@@ -199,8 +233,7 @@ void qgemm8_kernel(P8 p) {
   const float sw = *p.wscale;
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
-    const int64_t row = m0 + S::WM * wm + 32 * i + (lane & 31);
-    const float sc = row < p.M ? sw * p.rs[row] : 0.0f;
+    const float sc = sw * rsv[i];                    // rows past M read 0
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -209,20 +242,43 @@ void qgemm8_kernel(P8 p) {
   constexpr int SX = 2 * R + 8;
   uint16_t* Ax = reinterpret_cast<uint16_t*>(sm8);
   uint16_t* Bx = Ax + TM * SX;
-  for (int idx = tid; idx < TM * R; idx += NT) {
-    const int row = idx / R, j = idx % R;
-    const float su = m0 + row < p.M ? p.s * p.u[(m0 + row) * R + j] : 0.0f;
-    const __bf16 h = (__bf16)su;
-    const __bf16 l = (__bf16)(su - (float)h);
-    Ax[row * SX + j] = __builtin_bit_cast(uint16_t, h);
-    Ax[row * SX + R + j] = __builtin_bit_cast(uint16_t, l);
+  // s.U split into high and low bf16 parts (rows past M read 0)
+#pragma unroll
+  for (int u = 0; u < UQT; ++u) {
+    const int q = tid + NT * u;
+    if (q < UQ) {
+      const int row = q / (R / 4), j = (q % (R / 4)) * 4;
+      const float uu[4] = {__uint_as_float(uv[u].x), __uint_as_float(uv[u].y), __uint_as_float(uv[u].z),
+                           __uint_as_float(uv[u].w)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float su = p.s * uu[e];
+        const __bf16 h = (__bf16)su;
+        const __bf16 l = (__bf16)(su - (float)h);
+        Ax[row * SX + j + e] = __builtin_bit_cast(uint16_t, h);
+        Ax[row * SX + R + j + e] = __builtin_bit_cast(uint16_t, l);
+      }
+    }
   }
-  for (int idx = tid; idx < TN * R; idx += NT) {
-    const int col = idx / R, j = idx % R;
-    uint16_t v = 0;
-    if (o0 + col < p.O) v = TRANS ? p.up[(int64_t)j * p.K + o0 + col] : p.up[(o0 + col) * R + j];
-    Bx[col * SX + j] = v;
-    Bx[col * SX + R + j] = v;
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) {
+    const int q = tid + NT * u;
+    if (q < UPP) {
+      if constexpr (TRANS) {
+        const int j = q / (TN / 8), c = (q % (TN / 8)) * 8;
+        const uint32_t w[4] = {upv[u].x, upv[u].y, upv[u].z, upv[u].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint16_t v = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+          Bx[(c + e) * SX + j] = v;
+          Bx[(c + e) * SX + R + j] = v;
+        }
+      } else {
+        const int col = q / (R / 8), j = (q % (R / 8)) * 8;
+        *reinterpret_cast<uint4*>(Bx + col * SX + j) = upv[u];
+        *reinterpret_cast<uint4*>(Bx + col * SX + R + j) = upv[u];
+      }
+    }
   }
   lds_barrier();
 #pragma unroll
@@ -240,22 +296,26 @@ void qgemm8_kernel(P8 p) {
       for (int j = 0; j < NB; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
   }
+  // bf16 stores: lanes l and l + 32 trade column halves (v_permlane32_swap)
+  // so each writes 8 consecutive columns of its row with one 16-byte store
+  const int hl = lane >> 5;
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     const int64_t row = m0 + S::WM * wm + 32 * i + (lane & 31);
-    if (row < p.M) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-          const int64_t col = o0 + S::WN * wn + 32 * j + 8 * k4 + 4 * (lane >> 5);
-          if (col < p.O) {
-            const uint32_t lo = pack_bf16x2(acc[i][j][4 * k4 + 0], acc[i][j][4 * k4 + 1]);
-            const uint32_t hi = pack_bf16x2(acc[i][j][4 * k4 + 2], acc[i][j][4 * k4 + 3]);
-            *reinterpret_cast<uint2*>(p.out + row * p.O + col) = make_uint2(lo, hi);
-          }
-        }
-    }
+      for (int pr = 0; pr < 2; ++pr) {
+        const uint32_t a0 = pack_bf16x2(acc[i][j][8 * pr + 0], acc[i][j][8 * pr + 1]);
+        const uint32_t a1 = pack_bf16x2(acc[i][j][8 * pr + 2], acc[i][j][8 * pr + 3]);
+        const uint32_t b0 = pack_bf16x2(acc[i][j][8 * pr + 4], acc[i][j][8 * pr + 5]);
+        const uint32_t b1 = pack_bf16x2(acc[i][j][8 * pr + 6], acc[i][j][8 * pr + 7]);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+        const int64_t col = o0 + S::WN * wn + 32 * j + 8 * (2 * pr + hl);
+        if (row < p.M && col < p.O)
+          *reinterpret_cast<uint4*>(p.out + row * p.O + col) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+      }
   }
 }
 
