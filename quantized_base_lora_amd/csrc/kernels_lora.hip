@@ -148,7 +148,10 @@ __global__ __launch_bounds__(NT) void grad_kernel(GradArgs a) {
       step(u);
     }
   }
-  // partial[q][p][j]: lane holds column j = 16 jb + lane%16, rows 4 (lane/16) + e
+  // lane holds column j = 16 jb + lane%16, rows 4 (lane/16) + e.  With one
+  // partition the sum is complete: scale and write the result (out[p][j] or
+  // out[j][p]); otherwise write partial[q][p][j] for the reduction launch.
+  const bool final_out = a.nparts == 1;
   float* dst = pr.part + (int64_t)blockIdx.y * pr.pdim * R;
 #pragma unroll
   for (int jb = 0; jb < RB; ++jb)
@@ -156,7 +159,15 @@ __global__ __launch_bounds__(NT) void grad_kernel(GradArgs a) {
     for (int e = 0; e < 4; ++e) {
       const int64_t prow = p0 + 16 * wave + 4 * (lane >> 4) + e;
       const int j = 16 * jb + (lane & 15);
-      if (prow < pr.pdim && j < R) dst[prow * R + j] = acc[jb][e];
+      if (prow < pr.pdim && j < R) {
+        if (final_out) {
+          const int64_t o = pr.transpose_out ? (int64_t)j * pr.pdim + prow : prow * R + j;
+          const float v = a.s * acc[jb][e];
+          pr.out[o] = a.accumulate ? pr.out[o] + v : v;
+        } else {
+          dst[prow * R + j] = acc[jb][e];
+        }
+      }
     }
 }
 
@@ -256,7 +267,7 @@ hipError_t launch_grads(const GradLaunch& g, hipStream_t s) {
       default: hipLaunchKernelGGL(grad_kernel<32>, grid, dim3(NT), 0, s, a); break;
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || g.nparts == 1) return e;   // one partition: the kernel wrote dA, dB
   } else {
     a.nparts = 0;                                     // no tokens: dA = dB = 0 (or unchanged)
   }

@@ -15,12 +15,13 @@ namespace {
 // workgroup sees only a few contraction steps, so every step's loads must be
 // in flight long before they are needed: a ring of D register stages keeps
 // the loads of steps it+1 .. it+D outstanding while step it computes.  Tile:
-// 64 rows (all tokens) x 128 output columns, four waves side by side (64 x 32
-// each), the contraction split over blockIdx.y; fp32 partial sums out.
-template <int FMT, bool TRANS, int R>
+// all tokens (TM = 32 MBK rows: 32 when M <= 32, else 64) x 128 output
+// columns, four waves side by side (TM x 32 each), the contraction split over
+// blockIdx.y; fp32 partial sums out.
+template <int FMT, bool TRANS, int R, int MBK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void qsplit_kernel(Params p) {
-  constexpr int TM = 64, TN = 128, NT = 256, D = 4;
+  constexpr int TM = 32 * MBK, TN = 128, NT = 256, D = 4;
   static_assert(D % 2 == 0, "buffer parity of a step is its position in the chunk");
   constexpr int SBT = TN + 32;
   constexpr int A_EL = TM * SA;
@@ -60,7 +61,7 @@ void qsplit_kernel(Params p) {
   float tscale = 0.0f;
   if constexpr (FP8) tscale = reinterpret_cast<const float*>(p.scales)[0];
 
-  const int arow = tid >> 3, acol = (tid & 7) * 8;   // act rows arow, arow + 32
+  const int arow = tid >> 3, acol = (tid & 7) * 8;   // act rows arow (and arow + 32 when MBK = 2)
   const int wr = tid / GPR, wg = tid % GPR;          // one W group per thread per step
   const bool wg_in = !TRANS || (o0 + 32 * (wg + 1) <= p.K);
   constexpr int DPR = TRANS ? R / 8 : TK / 8;
@@ -78,7 +79,7 @@ void qsplit_kernel(Params p) {
     const int64_t c0 = (int64_t)kt * TK;
     const bool alive = sv && c0 + acol < p.C;
     sl.a0 = bload16(ract, alive ? (uint32_t)((arow * p.C + c0 + acol) * 2) : OOB);
-    sl.a1 = bload16(ract, alive ? (uint32_t)(((arow + 32) * p.C + c0 + acol) * 2) : OOB);
+    if constexpr (MBK == 2) sl.a1 = bload16(ract, alive ? (uint32_t)(((arow + 32) * p.C + c0 + acol) * 2) : OOB);
     const int64_t wrow = TRANS ? c0 + wr : wr;
     const int64_t kgrp = TRANS ? wg : (c0 >> 5) + wg;
     const bool wlive = sv && (TRANS || c0 + 32 * wg < p.C);
@@ -106,7 +107,7 @@ void qsplit_kernel(Params p) {
   };
   auto store = [&](const Slot& sl, uint16_t* st) {
     *reinterpret_cast<uint4*>(st + arow * SA + acol) = sl.a0;
-    *reinterpret_cast<uint4*>(st + (arow + 32) * SA + acol) = sl.a1;
+    if constexpr (MBK == 2) *reinterpret_cast<uint4*>(st + (arow + 32) * SA + acol) = sl.a1;
     float scale;
     if constexpr (FP8) scale = tscale;
     else if constexpr (FMT == QL_FMT_Q4_0) scale = decode_scale_q40(sl.w.sraw >> sl.w.ssh);
@@ -125,9 +126,9 @@ void qsplit_kernel(Params p) {
     ring[u].w.sraw = ring[u].w.ssh = 0;
   }
 
-  f32x16 acc[2];
+  f32x16 acc[MBK];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MBK; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
   f32x4 uacc[RB];
@@ -140,9 +141,9 @@ void qsplit_kernel(Params p) {
     const uint16_t* Ds = st + A_EL + B_EL;
 #pragma unroll
     for (int ks = 0; ks < TK / 16; ++ks) {
-      bf16x8 af[2], bf;
+      bf16x8 af[MBK], bf;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MBK; ++i)
         af[i] = *reinterpret_cast<const bf16x8*>(As + (32 * i + (lane & 31)) * SA + ks * 16 + 8 * (lane >> 5));
       if constexpr (TRANS) {
         const int b = lane >> 4, sl = lane & 15;
@@ -153,9 +154,11 @@ void qsplit_kernel(Params p) {
         bf = *reinterpret_cast<const bf16x8*>(Bs + (32 * wave + (lane & 31)) * SA + ks * 16 + 8 * (lane >> 5));
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af[i], acc[i], 0, 0, 0);
+      for (int i = 0; i < MBK; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af[i], acc[i], 0, 0, 0);
     }
-    // rank-r projection of rows 16 wave .. 16 wave + 15 over this stage
+    // rank-r projection of rows 16 wave .. 16 wave + 15 over this stage (waves
+    // whose rows lie past the tile have none)
+    if (16 * wave >= TM) return;
 #pragma unroll
     for (int kp = 0; kp < 2; ++kp) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(As + (16 * wave + (lane & 15)) * SA + 32 * kp + 8 * (lane >> 4));
@@ -213,7 +216,7 @@ void qsplit_kernel(Params p) {
   // fp32 partials: lane holds row (lane & 31) of block i and 4 consecutive columns per 8
   float* pp = p.part + (int64_t)split * p.M * p.O;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < MBK; ++i) {
     const int64_t row = 32 * i + (lane & 31);
     if (row < p.M) {
 #pragma unroll
@@ -233,27 +236,33 @@ void qsplit_kernel(Params p) {
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * wave + 4 * (lane >> 4) + e;
         const int j = 16 * jb + (lane & 15);
-        if (j < R && row < p.M) up[row * R + j] = uacc[jb][e];
+        if (j < R && row < p.M && 16 * wave < TM) up[row * R + j] = uacc[jb][e];
       }
   }
 }
 
-template <int FMT, bool TRANS, int R>
-hipError_t launch_split(const Params& p, int splits, hipStream_t s) {
+template <int FMT, bool TRANS, int R, int MBK>
+hipError_t launch_split_m(const Params& p, int splits, hipStream_t s) {
   constexpr int B_EL = TRANS ? TK * (128 + 32) : 128 * SA;
   constexpr int D_EL = TRANS ? BL_ELEMS : AD_ELEMS;
-  constexpr size_t smem = 2 * (size_t)(64 * SA + B_EL + D_EL) * sizeof(uint16_t);
+  constexpr size_t smem = 2 * (size_t)(32 * MBK * SA + B_EL + D_EL) * sizeof(uint16_t);
   static_assert(smem <= 80 * 1024, "two workgroups per CU");
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)qsplit_kernel<FMT, TRANS, R>,
+    hipError_t e = hipFuncSetAttribute((const void*)qsplit_kernel<FMT, TRANS, R, MBK>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((qsplit_kernel<FMT, TRANS, R>), dim3((unsigned)((p.O + 127) / 128), (unsigned)splits),
+  hipLaunchKernelGGL((qsplit_kernel<FMT, TRANS, R, MBK>), dim3((unsigned)((p.O + 127) / 128), (unsigned)splits),
                      dim3(256), smem, s, p);
   return hipGetLastError();
+}
+
+// 32-row tiles when every token fits in one 32x32 MFMA block
+template <int FMT, bool TRANS, int R>
+hipError_t launch_split(const Params& p, int splits, hipStream_t s) {
+  return p.M <= 32 ? launch_split_m<FMT, TRANS, R, 1>(p, splits, s) : launch_split_m<FMT, TRANS, R, 2>(p, splits, s);
 }
 
 // Split-contraction reduction and epilogue: per output element the partials

@@ -193,6 +193,8 @@ CASES = [
     ("small_q40_ragged_k", ofmt.FMT_Q4_0, 17, 1056, 224, 32, 64.0),
     ("small_nf4_splits", ofmt.FMT_NF4, 16, 2048, 320, 16, 32.0),
     ("small_fp8_m33", ofmt.FMT_FP8, 33, 512, 160, 8, 16.0),
+    # 32 tokens: the largest count served by 32-row split tiles; ragged columns
+    ("small_nf4_m32_r32", ofmt.FMT_NF4, 32, 640, 416, 32, 64.0),
 ]
 
 
