@@ -69,13 +69,9 @@ template <int TM_, int TN, int NTH> struct Shape {
   static_assert(MB >= 1 && NB >= 1 && AR >= 1 && UI >= 1, "tile shape");
 };
 
-template <int FMT, bool TRANS, int R, int TM_, int TN, int NTH, bool DR>
+template <int FMT, bool TRANS, int R, int TM_, int TN, int NTH>
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(NTH / 256, NTH / 256)))
 void qgemm_kernel(Params p) {
-  // DR: two register stages, so each global load has two steps to land
-  // (stage kt+3 is loaded while kt computes and kt+1 is stored); one stage
-  // (loads one step ahead) otherwise
-  constexpr int NS = DR ? 2 : 1;
   using S = Shape<TM_, TN, NTH>;
   constexpr int NT = NTH;
   constexpr int TM = S::TM;
@@ -138,26 +134,22 @@ void qgemm_kernel(Params p) {
   const bool dload = tid < 8 * R;                    // TK * R / 8 pieces either way
   const int drow = tid / DPR, dcol = (tid % DPR) * 8;
 
-  uint4 areg[NS][AR];
-  WGroup wreg[NS][WG];
-  uint4 dreg[NS];
+  uint4 areg[AR];
+  WGroup wreg[WG];
 #pragma unroll
-  for (int q = 0; q < NS; ++q) {
-#pragma unroll
-    for (int j = 0; j < WG; ++j) {
-      wreg[q][j].c0 = wreg[q][j].c1 = make_uint4(0, 0, 0, 0);
-      wreg[q][j].sraw = wreg[q][j].ssh = 0;
-    }
-    dreg[q] = make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < WG; ++j) {
+    wreg[j].c0 = wreg[j].c1 = make_uint4(0, 0, 0, 0);
+    wreg[j].sraw = wreg[j].ssh = 0;
   }
+  uint4 dreg = make_uint4(0, 0, 0, 0);
 
   // ---- global loads of stage kt, piece by piece (registers are reloaded as soon as stored)
-  auto load_act = [&](int q, int kt, int i) {
+  auto load_act = [&](int kt, int i) {
     const int64_t c0 = (int64_t)kt * TK;
     const uint32_t off = (uint32_t)(((arow + ARS * i) * p.C + c0 + acol) * 2);
-    areg[q][i] = bload16(ract, c0 + acol < p.C ? off : OOB);
+    areg[i] = bload16(ract, c0 + acol < p.C ? off : OOB);
   };
-  auto load_w = [&](int q, int kt, int j) {
+  auto load_w = [&](int kt, int j) {
     const int64_t c0 = (int64_t)kt * TK;
     // forward: row o0 + wr, K columns c0 + 32 wg; dX: row c0 + wr, K columns o0 + 32 wg
     const int64_t wrow = TRANS ? c0 + wr[j] : wr[j];
@@ -168,47 +160,47 @@ void qgemm_kernel(Params p) {
     // compiler's wait counts stay exact.
     const bool live = wtask && (TRANS || c0 + 32 * wg[j] < p.C);
     const uint32_t coff = live ? (uint32_t)(wrow * crow + kgrp * (FP8 ? 32 : 16)) : OOB;
-    wreg[q][j].c0 = bload16(rcode, coff);
+    wreg[j].c0 = bload16(rcode, coff);
     if constexpr (FP8) {
-      wreg[q][j].c1 = bload16(rcode, live ? coff + 16 : OOB);
+      wreg[j].c1 = bload16(rcode, live ? coff + 16 : OOB);
     } else {
       const int64_t kabs = TRANS ? (o0 >> 5) + wg[j] : kgrp;   // group index along K
       if constexpr (FMT == QL_FMT_Q4_0) {
         const int64_t idx = wrow * srow + kabs;
-        wreg[q][j].sraw = bload4(rscale, live ? (uint32_t)((idx * 2) & ~3LL) : OOB);
-        wreg[q][j].ssh = (uint32_t)(idx & 1) * 16;
+        wreg[j].sraw = bload4(rscale, live ? (uint32_t)((idx * 2) & ~3LL) : OOB);
+        wreg[j].ssh = (uint32_t)(idx & 1) * 16;
       } else {
-        wreg[q][j].sraw = bload4(rscale, live ? (uint32_t)((wrow * srow + (kabs >> 1)) * 4) : OOB);
+        wreg[j].sraw = bload4(rscale, live ? (uint32_t)((wrow * srow + (kabs >> 1)) * 4) : OOB);
       }
     }
   };
-  auto load_adapter = [&](int q, int kt) {
+  auto load_adapter = [&](int kt) {
     const int64_t c0 = (int64_t)kt * TK;
     uint32_t off;
     if constexpr (TRANS) off = (uint32_t)(((c0 + drow) * R + dcol) * 2);
     else off = c0 + dcol < p.C ? (uint32_t)((drow * p.C + c0 + dcol) * 2) : OOB;
-    dreg[q] = bload16(rdown, dload ? off : OOB);
+    dreg = bload16(rdown, dload ? off : OOB);
   };
 
   // ---- stage stores
   Deq<FMT> deq;
-  auto store_act = [&](int q, uint16_t* st, int i) {
-    *reinterpret_cast<uint4*>(st + (arow + ARS * i) * SA + acol) = areg[q][i];
+  auto store_act = [&](uint16_t* st, int i) {
+    *reinterpret_cast<uint4*>(st + (arow + ARS * i) * SA + acol) = areg[i];
   };
-  auto prepare_w = [&](int q, int j) {
+  auto prepare_w = [&](int j) {
     float scale;
     if constexpr (FP8) scale = tscale;
-    else if constexpr (FMT == QL_FMT_Q4_0) scale = decode_scale_q40(wreg[q][j].sraw >> wreg[q][j].ssh);
-    else scale = __uint_as_float(wreg[q][j].sraw);
-    deq.prepare(wreg[q][j], wg_in[j] ? scale : 0.0f, p.book);
+    else if constexpr (FMT == QL_FMT_Q4_0) scale = decode_scale_q40(wreg[j].sraw >> wreg[j].ssh);
+    else scale = __uint_as_float(wreg[j].sraw);
+    deq.prepare(wreg[j], wg_in[j] ? scale : 0.0f, p.book);
   };
   auto store_w = [&](uint16_t* st, int j, int i) {   // elements 8i .. 8i+7 of W group j
     if (!wtask) return;
     uint16_t* dst = st + A_ELEMS + (TRANS ? wr[j] * S::SBT : wr[j] * SA) + wg[j] * 32 + 8 * i;
     *reinterpret_cast<uint4*>(dst) = deq.piece(i);
   };
-  auto store_adapter = [&](int q, uint16_t* st) {
-    if (dload) *reinterpret_cast<uint4*>(st + A_ELEMS + B_ELEMS + drow * (TRANS ? SL : SA) + dcol) = dreg[q];
+  auto store_adapter = [&](uint16_t* st) {
+    if (dload) *reinterpret_cast<uint4*>(st + A_ELEMS + B_ELEMS + drow * (TRANS ? SL : SA) + dcol) = dreg;
   };
 
   // ---- accumulators
@@ -298,76 +290,69 @@ void qgemm_kernel(Params p) {
   }
   lds_barrier();
 
-  // ---- prologue: stage 0 stored, the next stage(s) in flight, first fragments read
+  // ---- prologue: stage 0 stored, stage 1 in flight, first fragments read
 #pragma unroll
-  for (int i = 0; i < AR; ++i) load_act(0, kbeg, i);
+  for (int i = 0; i < AR; ++i) load_act(kbeg, i);
 #pragma unroll
-  for (int j = 0; j < WG; ++j) load_w(0, kbeg, j);
-  load_adapter(0, kbeg);
-  if constexpr (DR) {   // stage 1 into the second slot (steps past the end read zero)
+  for (int j = 0; j < WG; ++j) load_w(kbeg, j);
+  load_adapter(kbeg);
 #pragma unroll
-    for (int i = 0; i < AR; ++i) load_act(1, kbeg + 1, i);
-#pragma unroll
-    for (int j = 0; j < WG; ++j) load_w(1, kbeg + 1, j);
-    load_adapter(1, kbeg + 1);
-  }
-#pragma unroll
-  for (int i = 0; i < AR; ++i) store_act(0, smem, i);
+  for (int i = 0; i < AR; ++i) store_act(smem, i);
 #pragma unroll
   for (int j = 0; j < WG; ++j) {
-    prepare_w(0, j);
+    prepare_w(j);
 #pragma unroll
     for (int i = 0; i < 4; ++i) store_w(smem, j, i);
   }
-  store_adapter(0, smem);
+  store_adapter(smem);
   {
-    const int k1 = DR ? kbeg + 2 : (NKT > 1 ? kbeg + 1 : kbeg);
+    const int k1 = NKT > 1 ? kbeg + 1 : kbeg;
 #pragma unroll
-    for (int i = 0; i < AR; ++i) load_act(0, k1, i);
+    for (int i = 0; i < AR; ++i) load_act(k1, i);
 #pragma unroll
-    for (int j = 0; j < WG; ++j) load_w(0, k1, j);
-    load_adapter(0, k1);
+    for (int j = 0; j < WG; ++j) load_w(k1, j);
+    load_adapter(k1);
   }
   lds_barrier();
   read_frags(smem, 0);
 
-  // ---- steady state.  Step it runs the MFMAs of stage it (buffer cs) while it
-  // writes stage it+1 (from register slot q) into the other buffer ns, which
-  // every wave finished reading before the previous barrier.  The stores are
-  // spread over the first three 16-deep slices, each register being reloaded
-  // (stage kl) as soon as it is stored: with one slot kl = it+2, so every
-  // load has a step to land; with two, kl = it+3 and it has two.  The barrier
-  // sits before the last slice: by then this wave's reads of cs and writes of
-  // ns are complete, and the first fragments of ns are read while the last
-  // slice's MFMAs run.
-  auto step = [&](int it, int q, int kl) {
+  // ---- steady state.  Step kt runs the MFMAs of stage kt (buffer cs) while it
+  // writes stage kt+1 (loaded one step earlier) into the other buffer ns,
+  // which every wave finished reading before the previous barrier.  The
+  // stores are spread over the first three 16-deep slices, each register
+  // being reloaded for stage kt+2 as soon as it is stored, so every load has
+  // a full step to land.  The barrier sits before the last slice: by then
+  // this wave's reads of cs and writes of ns are complete, and the first
+  // fragments of ns are read while the last slice's MFMAs run.
+  for (int it = 0; it + 1 < NKT; ++it) {
     const uint16_t* cs = smem + (it & 1) * STAGE;
     uint16_t* ns = smem + ((it & 1) ^ 1) * STAGE;
+    const int kl = it + 2 < NKT ? kbeg + it + 2 : kend - 1;
     // slice 0: activation tile
     read_frags(cs, 1);
     mfma_ks(0);
 #pragma unroll
     for (int i = 0; i < AR; ++i) {
-      store_act(q, ns, i);
-      load_act(q, kl, i);
+      store_act(ns, i);
+      load_act(kl, i);
     }
     // slice 1: W group 0 (and the adapter piece)
     read_frags(cs, 2);
     mfma_ks(1);
-    prepare_w(q, 0);
+    prepare_w(0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) store_w(ns, 0, i);
-    load_w(q, kl, 0);
-    store_adapter(q, ns);
-    load_adapter(q, kl);
+    load_w(kl, 0);
+    store_adapter(ns);
+    load_adapter(kl);
     // slice 2: W group 1, rank-r projection
     read_frags(cs, 3);
     mfma_ks(2);
     if constexpr (WG > 1) {
-      prepare_w(q, 1);
+      prepare_w(1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) store_w(ns, 1, i);
-      load_w(q, kl, 1);
+      load_w(kl, 1);
     }
     compute_u(cs);
     if constexpr (TRANS && TN == 192) {
@@ -387,18 +372,6 @@ void qgemm_kernel(Params p) {
     // slice 3
     read_frags(ns, 0);
     mfma_ks(3);
-  };
-  if constexpr (DR) {
-    // pairs of steps, so that the slot of each step is static: stage it+1
-    // sits in slot (it+1) % 2
-    int it = 0;
-    for (; it + 2 < NKT; it += 2) {
-      step(it, 1, kbeg + it + 3);
-      step(it + 1, 0, kbeg + it + 4);
-    }
-    if (it + 1 < NKT) step(it, 1, kbeg + it + 3);
-  } else {
-    for (int it = 0; it + 1 < NKT; ++it) step(it, 0, it + 2 < NKT ? kbeg + it + 2 : kend - 1);
   }
   // the tile's slice of the up matrix, loaded now so the epilogue does not
   // wait for it: forward B rows o0 .. o0+TN (contiguous, 8 elements per
@@ -521,7 +494,7 @@ void qgemm_kernel(Params p) {
   }
 }
 
-template <int FMT, bool TRANS, int R, int TM, int TN, int NTH, bool DR = false>
+template <int FMT, bool TRANS, int R, int TM, int TN, int NTH>
 hipError_t launch_t(const Params& p, hipStream_t s) {
   using S = Shape<TM, TN, NTH>;
   constexpr int B_ELEMS = TRANS ? S::BT_ELEMS : S::BF_ELEMS;
@@ -531,13 +504,13 @@ hipError_t launch_t(const Params& p, hipStream_t s) {
   static_assert((size_t)(TM + TN) * (2 * R + 8) * sizeof(uint16_t) <= smem, "epilogue LDS");
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)qgemm_kernel<FMT, TRANS, R, TM, TN, NTH, DR>,
+    hipError_t e = hipFuncSetAttribute((const void*)qgemm_kernel<FMT, TRANS, R, TM, TN, NTH>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t tiles = ((p.O + TN - 1) / TN) * ((p.M + TM - 1) / TM);
-  hipLaunchKernelGGL((qgemm_kernel<FMT, TRANS, R, TM, TN, NTH, DR>), dim3((unsigned)tiles),
+  hipLaunchKernelGGL((qgemm_kernel<FMT, TRANS, R, TM, TN, NTH>), dim3((unsigned)tiles),
                      dim3(NTH), smem, s, p);
   return hipGetLastError();
 }
@@ -569,13 +542,10 @@ hipError_t launch_w(const Params& p, int splits, hipStream_t s) {
 #ifndef QL_GEMM_THREADS
 #define QL_GEMM_THREADS 512
 #endif
-#ifndef QL_GEMM_DR128
-#define QL_GEMM_DR128 true
-#endif
   switch (pick_tn(p.M, p.O)) {
     case 256: return launch_t<FMT, TRANS, R, 256, 256, QL_GEMM_THREADS>(p, s);
     case 192: return launch_t<FMT, TRANS, R, 256, 192, QL_GEMM_THREADS>(p, s);
-    default: return launch_t<FMT, TRANS, R, 256, 128, QL_GEMM_THREADS, QL_GEMM_DR128>(p, s);
+    default: return launch_t<FMT, TRANS, R, 256, 128, QL_GEMM_THREADS>(p, s);
   }
 }
 
