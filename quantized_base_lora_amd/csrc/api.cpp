@@ -216,6 +216,9 @@ int qlora_linear_bwd(const ql_qweight* w, const uint16_t* x, const uint16_t* dy,
   float* pb = reinterpret_cast<float*>(base + L.pb);
   const float sc = alpha / (float)r;
   hipError_t e = hipSuccess;
+  // at most 64 tokens the dX reduction launch also writes dA and dB
+  const bool fuse = m > 0 && dx && split_path_fuses_grads(m);
+  GradFuse gf{x, u_save, d_a, d_b, accumulate != 0};
   if (m > 0 && dx) {
     GemmCall c{};
     c.w = w;
@@ -229,11 +232,12 @@ int qlora_linear_bwd(const ql_qweight* w, const uint16_t* x, const uint16_t* dy,
     c.out = dx;
     c.save = v;
     c.ws = base + L.g;
+    c.grads = fuse ? &gf : nullptr;
     e = launch_qgemm(c, s);
   } else if (m > 0) {
     e = launch_down_proj(dy, m, n, lora_b, r, v, s);
   }
-  if (e == hipSuccess) {
+  if (e == hipSuccess && !fuse) {
     GradLaunch g{};
     g.x = x;
     g.dy = dy;

@@ -65,6 +65,17 @@ hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t s);
 
 // fused base GEMM + LoRA (kernels_gemm.hip)
+// dX with few tokens (split_path_fuses_grads): the reduction launch of the
+// split path also computes the adapter gradients (one launch instead of two)
+struct GradFuse {
+  const uint16_t* x;       // [M, K] layer input
+  const float* u;          // [M, r] U saved by the forward
+  float* d_a;              // [r, K]
+  float* d_b;              // [N, r]
+  int32_t accumulate;
+};
+bool split_path_fuses_grads(int64_t m);
+
 struct GemmCall {
   const ql_qweight* w;
   bool trans;              // false: y = act . W^T (contract K); true: dX = act . W (contract N)
@@ -77,6 +88,7 @@ struct GemmCall {
   uint16_t* out;           // [M, O] bf16, O = output columns
   float* save;             // [M, r] fp32 rank-r projection (U or V), may be null
   void* ws;                // scratch of qgemm_workspace_bytes(trans, m, n, k, r) bytes (small-M path)
+  const GradFuse* grads;   // dX only, with split_path_fuses_grads(m): also write dA, dB (else null)
 };
 hipError_t launch_qgemm(const GemmCall& c, hipStream_t s);
 // scratch the GEMM needs: split-contraction partials when m is small; for the

@@ -140,7 +140,9 @@ struct SplitPlan {
 };
 
 SplitPlan split_plan(bool trans, int64_t m, int64_t n, int64_t k, int r);
-// split kernel plus reduction, for the format, direction and rank of p
-hipError_t launch_split_path(int fmt, bool trans, int r, const Params& p, int splits, hipStream_t s);
+// split kernel plus reduction, for the format, direction and rank of p; with
+// gf (dX only) the reduction also writes dA and dB
+hipError_t launch_split_path(int fmt, bool trans, int r, const Params& p, int splits, const GradFuse* gf,
+                             hipStream_t s);
 
 }  // namespace ql

@@ -537,8 +537,8 @@ int pick_tn(int64_t m, int64_t o) {
 }
 
 template <int FMT, bool TRANS, int R>
-hipError_t launch_w(const Params& p, int splits, hipStream_t s) {
-  if (splits > 0) return launch_split_path(FMT, TRANS, R, p, splits, s);
+hipError_t launch_w(const Params& p, int splits, const GradFuse* gf, hipStream_t s) {
+  if (splits > 0) return launch_split_path(FMT, TRANS, R, p, splits, gf, s);
 #ifndef QL_GEMM_THREADS
 #define QL_GEMM_THREADS 512
 #endif
@@ -550,17 +550,17 @@ hipError_t launch_w(const Params& p, int splits, hipStream_t s) {
 }
 
 template <int FMT, bool TRANS>
-hipError_t launch_r(const Params& p, int r, int splits, hipStream_t s) {
+hipError_t launch_r(const Params& p, int r, int splits, const GradFuse* gf, hipStream_t s) {
   switch (r) {
-    case 8: return launch_w<FMT, TRANS, 8>(p, splits, s);
-    case 16: return launch_w<FMT, TRANS, 16>(p, splits, s);
-    default: return launch_w<FMT, TRANS, 32>(p, splits, s);
+    case 8: return launch_w<FMT, TRANS, 8>(p, splits, gf, s);
+    case 16: return launch_w<FMT, TRANS, 16>(p, splits, gf, s);
+    default: return launch_w<FMT, TRANS, 32>(p, splits, gf, s);
   }
 }
 
 template <int FMT>
-hipError_t launch_f(const Params& p, bool trans, int r, int splits, hipStream_t s) {
-  return trans ? launch_r<FMT, true>(p, r, splits, s) : launch_r<FMT, false>(p, r, splits, s);
+hipError_t launch_f(const Params& p, bool trans, int r, int splits, const GradFuse* gf, hipStream_t s) {
+  return trans ? launch_r<FMT, true>(p, r, splits, gf, s) : launch_r<FMT, false>(p, r, splits, gf, s);
 }
 
 }  // namespace
@@ -633,10 +633,12 @@ hipError_t launch_qgemm(const GemmCall& c, hipStream_t s) {
     p.upart = reinterpret_cast<float*>(reinterpret_cast<char*>(c.ws) + pl.upart_off);
     p.sps = pl.sps;
   }
+  // the adapter gradients ride only on the split path's reduction
+  if (c.grads && (!c.trans || pl.splits == 0)) return hipErrorInvalidValue;
   switch (c.w->format) {
-    case QL_FMT_Q4_0: return launch_f<QL_FMT_Q4_0>(p, c.trans, c.r, pl.splits, s);
-    case QL_FMT_NF4: return launch_f<QL_FMT_NF4>(p, c.trans, c.r, pl.splits, s);
-    default: return launch_f<QL_FMT_FP8_E4M3>(p, c.trans, c.r, pl.splits, s);
+    case QL_FMT_Q4_0: return launch_f<QL_FMT_Q4_0>(p, c.trans, c.r, pl.splits, c.grads, s);
+    case QL_FMT_NF4: return launch_f<QL_FMT_NF4>(p, c.trans, c.r, pl.splits, c.grads, s);
+    default: return launch_f<QL_FMT_FP8_E4M3>(p, c.trans, c.r, pl.splits, c.grads, s);
   }
 }
 

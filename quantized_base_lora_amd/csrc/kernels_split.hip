@@ -343,23 +343,132 @@ __global__ __launch_bounds__(128) void split_reduce_kernel(const float* __restri
   *reinterpret_cast<uint2*>(out + m * O + o) = make_uint2(lo, hi);
 }
 
+// dX reduction with the adapter gradients, at most 32 tokens (all of them in
+// every workgroup).  Workgroup g owns dX columns [16 g, 16 g + 16): it adds
+// the split partials in split order, adds s . V . A in fp32 (V = sum of its
+// split partials, in split order) and rounds once to bf16; it writes the same
+// columns of dA = s . V^T x, and rows [nb g, nb g + nb) of dB = s . dY^T U.
+// Every sum over tokens runs in token order in fp32 (exact bf16 operands),
+// so results are reproducible.
+constexpr int RB_TC = 16;       // dX / dA columns per workgroup
+constexpr int RB_NB = 64;       // at most this many dB rows per workgroup
+constexpr int RB_MAXM = 32;     // tokens (host side: split_path_fuses_grads)
+
+template <int R>
+__global__ __launch_bounds__(256) void split_reduce_bwd_kernel(
+    const float* __restrict__ part, const float* __restrict__ upart, int splits, int64_t M, int64_t K, int64_t N,
+    const uint16_t* __restrict__ adA, float s, uint16_t* __restrict__ dx, const uint16_t* __restrict__ x,
+    const uint16_t* __restrict__ dy, const float* __restrict__ u, float* __restrict__ d_a,
+    float* __restrict__ d_b, int64_t nb, int accumulate) {
+  constexpr int NT = 256, TC = RB_TC, SR = R + 1;
+  __shared__ float vs[RB_MAXM * SR];                  // V [m][j]
+  __shared__ float ush[RB_MAXM * SR];                 // U [m][j]
+  __shared__ float as_[R * TC];                       // A [j][k0 ..]
+  __shared__ uint16_t xs[RB_MAXM * TC];               // x [m][k0 ..] (bf16)
+  __shared__ uint16_t ys[RB_MAXM * RB_NB];            // dY [m][n0 ..] (bf16)
+  const int tid = threadIdx.x;
+  const int64_t k0 = (int64_t)blockIdx.x * TC, n0 = (int64_t)blockIdx.x * nb;
+  const int nn = n0 < N ? (int)(n0 + nb <= N ? nb : N - n0) : 0;   // dB rows of this workgroup
+  const int kc = k0 < K ? (int)(k0 + TC <= K ? TC : K - k0) : 0;  // dX / dA columns
+  const int m_ = (int)M;
+
+  const __amdgpu_buffer_rsrc_t rp = rsrc(part, (int64_t)splits * M * K * 4);
+  const __amdgpu_buffer_rsrc_t ru = rsrc(upart, (int64_t)splits * M * R * 4);
+  for (int idx = tid; idx < m_ * R; idx += NT) {
+    const int m = idx / R, j = idx % R;
+    uint32_t v[MAX_SPLITS];
+#pragma unroll
+    for (int sp = 0; sp < MAX_SPLITS; ++sp) v[sp] = bload4(ru, (uint32_t)((((int64_t)sp * M + m) * R + j) * 4));
+    float t = 0.0f;
+#pragma unroll
+    for (int sp = 0; sp < MAX_SPLITS; ++sp) t += __uint_as_float(v[sp]);
+    vs[m * SR + j] = t;
+    ush[m * SR + j] = u[m * R + j];
+  }
+  for (int idx = tid; idx < R * kc; idx += NT) {
+    const int j = idx / kc, c = idx % kc;
+    as_[j * TC + c] = __uint_as_float((uint32_t)adA[(int64_t)j * K + k0 + c] << 16);
+  }
+  for (int idx = tid; idx < m_ * kc; idx += NT) {
+    const int m = idx / kc, c = idx % kc;
+    xs[m * TC + c] = x[(int64_t)m * K + k0 + c];
+  }
+  for (int idx = tid; idx < m_ * nn; idx += NT) {
+    const int m = idx / nn, c = idx % nn;
+    ys[m * RB_NB + c] = dy[(int64_t)m * N + n0 + c];
+  }
+  __syncthreads();
+
+  // dX: 4 consecutive columns of one token per task (K is a multiple of 32)
+  for (int t = tid; t < m_ * (kc / 4); t += NT) {
+    const int m = t / (kc / 4), c = (t % (kc / 4)) * 4;
+    uint4 pv[MAX_SPLITS];
+#pragma unroll
+    for (int sp = 0; sp < MAX_SPLITS; ++sp)
+      pv[sp] = bload16(rp, (uint32_t)((((int64_t)sp * M + m) * K + k0 + c) * 4));
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sp = 0; sp < MAX_SPLITS; ++sp) {
+      acc[0] += __uint_as_float(pv[sp].x); acc[1] += __uint_as_float(pv[sp].y);
+      acc[2] += __uint_as_float(pv[sp].z); acc[3] += __uint_as_float(pv[sp].w);
+    }
+    float l[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const float sv = s * vs[m * SR + j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) l[e] += sv * as_[j * TC + c + e];
+    }
+    *reinterpret_cast<uint2*>(dx + m * K + k0 + c) =
+        make_uint2(pack_bf16x2(acc[0] + l[0], acc[1] + l[1]), pack_bf16x2(acc[2] + l[2], acc[3] + l[3]));
+  }
+  // dA[j][k] = s . sum_m V[m][j] x[m][k]
+  for (int t = tid; t < R * kc; t += NT) {
+    const int j = t / kc, c = t % kc;
+    float acc = 0.0f;
+    for (int m = 0; m < m_; ++m) acc += vs[m * SR + j] * __uint_as_float((uint32_t)xs[m * TC + c] << 16);
+    const int64_t o = (int64_t)j * K + k0 + c;
+    const float v = s * acc;
+    d_a[o] = accumulate ? d_a[o] + v : v;
+  }
+  // dB[n][j] = s . sum_m dY[m][n] U[m][j]
+  for (int t = tid; t < nn * R; t += NT) {
+    const int c = t / R, j = t % R;
+    float acc = 0.0f;
+    for (int m = 0; m < m_; ++m) acc += __uint_as_float((uint32_t)ys[m * RB_NB + c] << 16) * ush[m * SR + j];
+    const int64_t o = (n0 + c) * R + j;
+    const float v = s * acc;
+    d_b[o] = accumulate ? d_b[o] + v : v;
+  }
+}
+
 template <int FMT, bool TRANS, int R>
-hipError_t launch_path(const Params& p, int splits, hipStream_t s) {
+hipError_t launch_path(const Params& p, int splits, const GradFuse* gf, hipStream_t s) {
   hipError_t e = launch_split<FMT, TRANS, R>(p, splits, s);
   if (e != hipSuccess) return e;
+  if (gf) {
+    // enough workgroups for the dX columns and for at most RB_NB dB rows each
+    const int64_t g = std::max((p.K + RB_TC - 1) / RB_TC, (p.N + RB_NB - 1) / RB_NB);
+    const int64_t nb = (p.N + g - 1) / g;
+    hipLaunchKernelGGL(split_reduce_bwd_kernel<R>, dim3((unsigned)g), dim3(256), 0, s, (const float*)p.part,
+                       (const float*)p.upart, splits, p.M, p.K, p.N, p.up, p.s, p.out, gf->x, p.act, gf->u,
+                       gf->d_a, gf->d_b, nb, gf->accumulate);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(split_reduce_kernel<R>, dim3((unsigned)((p.O + 511) / 512), (unsigned)p.M), dim3(128), 0, s,
                      (const float*)p.part, (const float*)p.upart, splits, p.M, p.O, p.up, TRANS, p.s, p.out, p.save);
   return hipGetLastError();
 }
 
 template <int FMT, bool TRANS>
-hipError_t launch_r(const Params& p, int r, int splits, hipStream_t s) {
+hipError_t launch_r(const Params& p, int r, int splits, const GradFuse* gf, hipStream_t s) {
   switch (r) {
-    case 8: return launch_path<FMT, TRANS, 8>(p, splits, s);
-    case 16: return launch_path<FMT, TRANS, 16>(p, splits, s);
-    default: return launch_path<FMT, TRANS, 32>(p, splits, s);
+    case 8: return launch_path<FMT, TRANS, 8>(p, splits, gf, s);
+    case 16: return launch_path<FMT, TRANS, 16>(p, splits, gf, s);
+    default: return launch_path<FMT, TRANS, 32>(p, splits, gf, s);
   }
 }
+
 
 }  // namespace
 
@@ -382,11 +491,17 @@ SplitPlan split_plan(bool trans, int64_t m, int64_t n, int64_t k, int r) {
 }
 
 
-hipError_t launch_split_path(int fmt, bool trans, int r, const Params& p, int splits, hipStream_t s) {
+// up to 32 tokens one fused launch beats the two (measured); at 64 the
+// per-token loops of the fused kernel cost more than the launch it saves
+bool split_path_fuses_grads(int64_t m) { return m > 0 && m <= 32; }
+
+hipError_t launch_split_path(int fmt, bool trans, int r, const Params& p, int splits, const GradFuse* gf,
+                             hipStream_t s) {
+  if (gf && (!trans || !split_path_fuses_grads(p.M))) return hipErrorInvalidValue;
   switch (fmt) {
-    case QL_FMT_Q4_0: return trans ? launch_r<QL_FMT_Q4_0, true>(p, r, splits, s) : launch_r<QL_FMT_Q4_0, false>(p, r, splits, s);
-    case QL_FMT_NF4: return trans ? launch_r<QL_FMT_NF4, true>(p, r, splits, s) : launch_r<QL_FMT_NF4, false>(p, r, splits, s);
-    default: return trans ? launch_r<QL_FMT_FP8_E4M3, true>(p, r, splits, s) : launch_r<QL_FMT_FP8_E4M3, false>(p, r, splits, s);
+    case QL_FMT_Q4_0: return trans ? launch_r<QL_FMT_Q4_0, true>(p, r, splits, gf, s) : launch_r<QL_FMT_Q4_0, false>(p, r, splits, gf, s);
+    case QL_FMT_NF4: return trans ? launch_r<QL_FMT_NF4, true>(p, r, splits, gf, s) : launch_r<QL_FMT_NF4, false>(p, r, splits, gf, s);
+    default: return trans ? launch_r<QL_FMT_FP8_E4M3, true>(p, r, splits, gf, s) : launch_r<QL_FMT_FP8_E4M3, false>(p, r, splits, gf, s);
   }
 }
 
