@@ -195,6 +195,8 @@ CASES = [
     ("small_fp8_m33", ofmt.FMT_FP8, 33, 512, 160, 8, 16.0),
     # 32 tokens: the largest count served by 32-row split tiles; ragged columns
     ("small_nf4_m32_r32", ofmt.FMT_NF4, 32, 640, 416, 32, 64.0),
+    # FP8 base, rank 8, few tokens: dA and dB written by the dX reduction launch
+    ("small_fp8_m20_r8", ofmt.FMT_FP8, 20, 256, 1216, 8, 16.0),
 ]
 
 
