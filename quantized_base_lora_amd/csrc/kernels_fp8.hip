@@ -347,17 +347,22 @@ hipError_t launch8_w(const P8& p, hipStream_t s) {
 // ------------------------------------------------------------------ rank-r projection
 // out[m][j] = sum_c act[m][c] D(c, j), D(c, j) = A[j][c] (A layout, [R, C]) or
 // B[c][j] (B layout, [C, R]), fp32 accumulation on 32x32x16 bf16 MFMAs.  A
-// workgroup owns 32 rows; its four waves take the 64-wide contraction chunks
-// round robin and their partial sums are added in wave order (fixed).  The
-// activation fragments come straight from global memory; a B-layout chunk
-// goes through the wave's own LDS tile and transposing reads.
+// workgroup owns 32 rows; its eight waves (two per SIMD) take the 64-wide
+// contraction chunks round robin, each with the loads of its next three
+// chunks in flight, and their partial sums are added in wave order (fixed).
+// The activation fragments come straight from global memory; a B-layout
+// chunk goes through the wave's own LDS tile and transposing reads.
+constexpr int RP_NW = 8;        // waves per rank-r projection workgroup
+
 template <int R, bool ALAYOUT>
-__global__ __launch_bounds__(256) void rproj_kernel(const uint16_t* __restrict__ act, int64_t M, int64_t C,
-                                                    const uint16_t* __restrict__ d, float* __restrict__ out) {
-  constexpr int SLD = 48;
-  __shared__ __attribute__((aligned(16))) uint16_t dl[4][64 * SLD];
-  __shared__ float red[4][32][33];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ __launch_bounds__(64 * RP_NW) void rproj_kernel(const uint16_t* __restrict__ act, int64_t M, int64_t C,
+                                                           const uint16_t* __restrict__ d, float* __restrict__ out) {
+  constexpr int SLD = 48, D = 3, NW = RP_NW, NT = 64 * NW;
+  constexpr int DP = ALAYOUT ? 4 : R / 8;            // adapter pieces per lane and chunk
+  __shared__ __attribute__((aligned(16))) uint16_t dl[NW][64 * SLD];
+  __shared__ float red[NW][32][33];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the chunk loop is not divergent
   const int64_t m0 = (int64_t)blockIdx.x * 32;
   const __amdgpu_buffer_rsrc_t ract = rsrc(act + m0 * C, (M - m0) * C * 2);
   const __amdgpu_buffer_rsrc_t rd = rsrc(d, (int64_t)R * C * 2);
@@ -366,40 +371,90 @@ __global__ __launch_bounds__(256) void rproj_kernel(const uint16_t* __restrict__
   f32x16 acc;
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
-  for (int64_t c0 = (int64_t)wave * 64; c0 < C; c0 += 256) {
+  // wave w takes chunks c0 = 64 w + 64 NW i; a ring of D chunks of loads is in
+  // flight (chunks past C read zero through out-of-range offsets)
+  const int nit = (int)((C - 64 * wave + 64 * NW - 1) / (64 * NW));
+  struct Slot {
+    uint4 a[4];
+    uint4 d[DP];
+  };
+  Slot ring[D];
+  auto issue = [&](Slot& sl, int it) {
+    const int64_t c0 = 64 * (int64_t)wave + 64 * NW * (int64_t)it;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int64_t k = c0 + 16 * ks + 8 * (lane >> 5);
+      sl.a[ks] = bload16(ract, k < C ? (uint32_t)(((lane & 31) * C + k) * 2) : OOB);
+      if constexpr (ALAYOUT) {
+        const int j = lane & 31;
+        sl.d[ks] = bload16(rd, (j < R && k < C) ? (uint32_t)((j * C + k) * 2) : OOB);
+      }
+    }
     if constexpr (!ALAYOUT) {
 #pragma unroll
-      for (int t = 0; t < R / 8; ++t) {
+      for (int t = 0; t < DP; ++t) {
         const int q = lane + 64 * t;
         const int row = q / (R / 8), col = (q % (R / 8)) * 8;
-        const uint4 v = bload16(rd, (uint32_t)(((c0 + row) * R + col) * 2));
-        *reinterpret_cast<uint4*>(&dl[wave][row * SLD + col]) = v;
+        sl.d[t] = bload16(rd, c0 + row < C ? (uint32_t)(((c0 + row) * R + col) * 2) : OOB);
+      }
+    }
+  };
+  auto consume = [&](const Slot& sl) {
+    if constexpr (!ALAYOUT) {
+      // the chunk of B [C, R] through this wave's LDS tile (its own region;
+      // one wave's LDS operations complete in order)
+#pragma unroll
+      for (int t = 0; t < DP; ++t) {
+        const int q = lane + 64 * t;
+        const int row = q / (R / 8), col = (q % (R / 8)) * 8;
+        *reinterpret_cast<uint4*>(&dl[wave][row * SLD + col]) = sl.d[t];
       }
     }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int64_t k = c0 + 16 * ks + 8 * (lane >> 5);
-      const bf16x8 af = __builtin_bit_cast(bf16x8, bload16(ract, k < C ? (uint32_t)(((lane & 31) * C + k) * 2) : OOB));
       bf16x8 df;
       if constexpr (ALAYOUT) {
-        const int j = lane & 31;
-        df = __builtin_bit_cast(bf16x8, bload16(rd, (j < R && k < C) ? (uint32_t)((j * C + k) * 2) : OOB));
+        df = __builtin_bit_cast(bf16x8, sl.d[ks]);
       } else {
-        const int b = lane >> 4, sl = lane & 15;
-        const int col = 16 * (b & 1) + 4 * (sl & 3);
-        const int row = 16 * ks + 8 * (b >> 1) + (sl >> 2);
+        const int b = lane >> 4, sl_ = lane & 15;
+        const int col = 16 * (b & 1) + 4 * (sl_ & 3);
+        const int row = 16 * ks + 8 * (b >> 1) + (sl_ >> 2);
         df = tr16x8(&dl[wave][row * SLD + col], &dl[wave][(row + 4) * SLD + col]);
       }
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, df, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sl.a[ks]), df, acc, 0, 0, 0);
+    }
+  };
+  // slot by slot in refill order, and a scheduling barrier after each refill,
+  // so that each chunk waits only for its own loads
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    issue(ring[u], u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  int it = 0;
+  for (; it + D <= nit; it += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      consume(ring[u]);
+      issue(ring[u], it + u + D);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+    if (it + u < nit) consume(ring[u]);
   // lane: column j = lane & 31, rows 8 (e / 4) + 4 (lane / 32) + e % 4
 #pragma unroll
   for (int e = 0; e < 16; ++e) red[wave][8 * (e / 4) + 4 * (lane >> 5) + (e % 4)][lane & 31] = acc[e];
   __syncthreads();
-  for (int i = tid; i < 32 * R; i += 256) {
+  for (int i = tid; i < 32 * R; i += NT) {
     const int m = i / R, j = i % R;
-    if (m0 + m < M) out[(m0 + m) * R + j] = ((red[0][m][j] + red[1][m][j]) + red[2][m][j]) + red[3][m][j];
+    if (m0 + m < M) {
+      float t = red[0][m][j];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) t += red[w][m][j];   // wave order
+      out[(m0 + m) * R + j] = t;
+    }
   }
 }
 
@@ -410,8 +465,8 @@ hipError_t launch_rproj(const uint16_t* act, int64_t m, int64_t c, const uint16_
   if (m == 0) return hipSuccess;
   const dim3 grid((unsigned)((m + 31) / 32));
 #define QL_RPROJ(RR)                                                                                  \
-  if (a_layout) hipLaunchKernelGGL((rproj_kernel<RR, true>), grid, dim3(256), 0, s, act, m, c, d, out); \
-  else hipLaunchKernelGGL((rproj_kernel<RR, false>), grid, dim3(256), 0, s, act, m, c, d, out);
+  if (a_layout) hipLaunchKernelGGL((rproj_kernel<RR, true>), grid, dim3(64 * RP_NW), 0, s, act, m, c, d, out); \
+  else hipLaunchKernelGGL((rproj_kernel<RR, false>), grid, dim3(64 * RP_NW), 0, s, act, m, c, d, out);
   switch (r) {
     case 8: QL_RPROJ(8) break;
     case 16: QL_RPROJ(16) break;
