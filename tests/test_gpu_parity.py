@@ -141,10 +141,12 @@ def test_dequant_all_codes_and_scales(lib):
         assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
 
 
-def test_act_split_bitexact(lib):
+# one wave per row (rows up to 4096 wide, any row count) and the workgroup-per-row kernel
+@pytest.mark.parametrize("shape", [(40, 320), (37, 4096), (6, 4608)])
+def test_act_split_bitexact(lib, shape):
     from quantized_base_lora_amd import binding as B
     g = np.random.default_rng(5)
-    x = g.standard_normal((40, 320), dtype=np.float32)
+    x = g.standard_normal(shape, dtype=np.float32)
     x[3] = 0
     x[4, :7] = 1e-30
     x[5] *= 1e4
