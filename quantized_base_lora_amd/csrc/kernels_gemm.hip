@@ -409,6 +409,16 @@ void qgemm_kernel(Params p) {
   lds_barrier();
 
   // ---------------------------------------------------------------- epilogue
+  // The rank-r accumulators were last written by MFMAs, whose results the
+  // hardware does not interlock against VALU reads: the reader must trail
+  // the MFMA by enough wait states.  The compiler counts them along each path,
+  // but a branch right after the last MFMA (the conditional store of U below)
+  // has been seen to leave too few on the path that skips the store, so the
+  // read saw an unfinished value.  Thirty-two wait states here cover every
+  // MFMA, whatever the path.
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
   // Ax [TM][2R+8]: high and low bf16 parts of s.U; Bx [TN][2R+8]: the up matrix twice.
   constexpr int SX = 2 * R + 8;
   uint16_t* Ax = smem;
@@ -515,22 +525,33 @@ hipError_t launch_t(const Params& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Output tile width for 256-row tiles: the one with the least time in rounds
-// of 256 workgroups (one per CU) times work per tile, the narrower tiles
-// weighted for their lower MFMA efficiency (more LDS traffic per MFMA);
-// ties go to the wider tile.
-int pick_tn(int64_t m, int64_t o) {
-  const int64_t mt = (m + 255) / 256;
-  const int tns[3] = {256, 192, 128};
-  const double eff[3] = {1.0, 0.95, 0.85};
-  int best = 256;
+// Output tile: the one with the least time in rounds of 256 workgroups (one
+// per CU) times work per tile, each shape weighted for its MFMA efficiency
+// (the narrower tiles read more LDS per MFMA); ties go to the earlier entry.
+// 128x128 tiles only pay off when the 256-row tiles would leave CUs idle.
+struct TilePick {
+  int tm, tn;
+};
+TilePick pick_tile(int64_t m, int64_t o) {
+  struct Cand {
+    int tm, tn;
+    double eff;
+  };
+#ifndef QL_NO_TM128
+  const Cand c[4] = {{256, 256, 1.0}, {256, 192, 0.95}, {256, 128, 0.85}, {128, 128, 0.6}};
+  const int nc = 4;
+#else
+  const Cand c[3] = {{256, 256, 1.0}, {256, 192, 0.95}, {256, 128, 0.85}};
+  const int nc = 3;
+#endif
+  TilePick best{256, 256};
   double best_cost = 1e300;
-  for (int i = 0; i < 3; ++i) {
-    const int64_t tiles = mt * ((o + tns[i] - 1) / tns[i]);
-    const double cost = (double)((tiles + 255) / 256) * tns[i] / eff[i];
+  for (int i = 0; i < nc; ++i) {
+    const int64_t tiles = ((m + c[i].tm - 1) / c[i].tm) * ((o + c[i].tn - 1) / c[i].tn);
+    const double cost = (double)((tiles + 255) / 256) * c[i].tm * c[i].tn / c[i].eff;
     if (cost < best_cost * (1 - 1e-9)) {
       best_cost = cost;
-      best = tns[i];
+      best = TilePick{c[i].tm, c[i].tn};
     }
   }
   return best;
@@ -542,7 +563,9 @@ hipError_t launch_w(const Params& p, int splits, const GradFuse* gf, hipStream_t
 #ifndef QL_GEMM_THREADS
 #define QL_GEMM_THREADS 512
 #endif
-  switch (pick_tn(p.M, p.O)) {
+  const TilePick t = pick_tile(p.M, p.O);
+  if (t.tm == 128) return launch_t<FMT, TRANS, R, 128, 128, QL_GEMM_THREADS>(p, s);
+  switch (t.tn) {
     case 256: return launch_t<FMT, TRANS, R, 256, 256, QL_GEMM_THREADS>(p, s);
     case 192: return launch_t<FMT, TRANS, R, 256, 192, QL_GEMM_THREADS>(p, s);
     default: return launch_t<FMT, TRANS, R, 256, 128, QL_GEMM_THREADS>(p, s);
