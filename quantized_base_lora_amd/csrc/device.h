@@ -40,4 +40,18 @@ __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t of
 // Buffer offset that reads as zero (beyond every resource's size).
 constexpr uint32_t OOB = 0x80000000u;
 
+// Place between a kernel's last MFMAs and the epilogue that reads their
+// results.  The hardware does not interlock VALU reads of an MFMA's result
+// registers: the reader must trail the MFMA by enough wait states, which the
+// compiler counts along each path, but a branch right after the last MFMA
+// (a conditional store, say) has been seen to leave too few on the path
+// that skips it, so the read saw an unfinished value.  Thirty-two wait
+// states cover every MFMA, whatever the path; the scheduling barriers keep
+// instructions from moving across them.
+__device__ __forceinline__ void mfma_result_guard() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 }  // namespace ql

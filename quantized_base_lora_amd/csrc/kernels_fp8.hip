@@ -229,6 +229,7 @@ void qgemm8_kernel(P8 p) {
   compute(sm8 + ((KT - 1) & 1) * S::STAGE);
   lds_barrier();
 
+  mfma_result_guard();
   // ---- epilogue: scales, then s . U . up^T on bf16 MFMAs, one rounding to bf16
   const float sw = *p.wscale;
 #pragma unroll
@@ -443,6 +444,7 @@ __global__ __launch_bounds__(64 * RP_NW) void rproj_kernel(const uint16_t* __res
 #pragma unroll
   for (int u = 0; u < D; ++u)
     if (it + u < nit) consume(ring[u]);
+  mfma_result_guard();
   // lane: column j = lane & 31, rows 8 (e / 4) + 4 (lane / 32) + e % 4
 #pragma unroll
   for (int e = 0; e < 16; ++e) red[wave][8 * (e / 4) + 4 * (lane >> 5) + (e % 4)][lane & 31] = acc[e];

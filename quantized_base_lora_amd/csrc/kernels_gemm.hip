@@ -409,16 +409,7 @@ void qgemm_kernel(Params p) {
   lds_barrier();
 
   // ---------------------------------------------------------------- epilogue
-  // The rank-r accumulators were last written by MFMAs, whose results the
-  // hardware does not interlock against VALU reads: the reader must trail
-  // the MFMA by enough wait states.  The compiler counts them along each path,
-  // but a branch right after the last MFMA (the conditional store of U below)
-  // has been seen to leave too few on the path that skips the store, so the
-  // read saw an unfinished value.  Thirty-two wait states here cover every
-  // MFMA, whatever the path.
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
+  mfma_result_guard();   // the conditional store of U below follows the last MFMAs
   // Ax [TM][2R+8]: high and low bf16 parts of s.U; Bx [TN][2R+8]: the up matrix twice.
   constexpr int SX = 2 * R + 8;
   uint16_t* Ax = smem;

@@ -148,6 +148,7 @@ __global__ __launch_bounds__(NT) void grad_kernel(GradArgs a) {
       step(u);
     }
   }
+  mfma_result_guard();
   // lane holds column j = 16 jb + lane%16, rows 4 (lane/16) + e.  With one
   // partition the sum is complete: scale and write the result (out[p][j] or
   // out[j][p]); otherwise write partial[q][p][j] for the reduction launch.

@@ -213,6 +213,7 @@ void qsplit_kernel(Params p) {
     }
   }
 
+  mfma_result_guard();
   // fp32 partials: lane holds row (lane & 31) of block i and 4 consecutive columns per 8
   float* pp = p.part + (int64_t)split * p.M * p.O;
 #pragma unroll
