@@ -528,13 +528,8 @@ TilePick pick_tile(int64_t m, int64_t o) {
     int tm, tn;
     double eff;
   };
-#ifndef QL_NO_TM128
   const Cand c[4] = {{256, 256, 1.0}, {256, 192, 0.95}, {256, 128, 0.85}, {128, 128, 0.6}};
   const int nc = 4;
-#else
-  const Cand c[3] = {{256, 256, 1.0}, {256, 192, 0.95}, {256, 128, 0.85}};
-  const int nc = 3;
-#endif
   TilePick best{256, 256};
   double best_cost = 1e300;
   for (int i = 0; i < nc; ++i) {
