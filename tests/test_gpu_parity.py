@@ -315,23 +315,37 @@ def test_integer_data_bitwise(lib):
     assert np.array_equal(to_np(got["dB"]).astype(np.float64), ref["dB"])
 
 
-def test_deterministic_and_base_untouched(lib):
-    c = H.make_case(384, 512, 256, 16, seed=41)
-    qw, g1 = run_layer(ofmt.FMT_NF4, c, 32.0, 384)
+# every kernel path, run again on the same inputs: bitwise equal results
+DET_CASES = [
+    # name, fmt, m, k, n, r
+    ("nf4_m384_128x128", ofmt.FMT_NF4, 384, 512, 256, 16),
+    ("q40_m24_fused_grads", ofmt.FMT_Q4_0, 24, 512, 320, 32),
+    ("nf4_m64_split", ofmt.FMT_NF4, 64, 1024, 512, 16),
+    ("nf4_m2048_256rows", ofmt.FMT_NF4, 2048, 1024, 8192, 8),
+    ("fp8_m300_fp8_mfma", ofmt.FMT_FP8, 300, 256, 512, 16),
+]
+
+
+@pytest.mark.parametrize("case", DET_CASES, ids=[c[0] for c in DET_CASES])
+def test_deterministic_and_base_untouched(lib, case):
+    name, fmt, m, k, n, r = case
+    c = H.make_case(m, k, n, r, seed=41)
+    qw, g1 = run_layer(fmt, c, 32.0, m)
     before = (qw.codes.clone(), qw.scales.clone())
     from quantized_base_lora_amd import binding as B
     x = H.bits_to_bf16_tensor(c["x"])
     dy = H.bits_to_bf16_tensor(c["dY"])
     a = H.bits_to_bf16_tensor(c["A"])
     b = H.bits_to_bf16_tensor(c["B"])
-    for _ in range(2):
+    for _ in range(3):
         y, u = B.linear_fwd(qw, x, a, b, 32.0)
         dx, da, db = B.linear_bwd(qw, x, dy, u, a, b, 32.0)
         torch.cuda.synchronize()
-        assert torch.equal(y.view(torch.int16), g1["y"].view(torch.int16))
-        assert torch.equal(dx.view(torch.int16), g1["dX"].view(torch.int16))
-        assert torch.equal(da.view(torch.int32), g1["dA"].view(torch.int32))
-        assert torch.equal(db.view(torch.int32), g1["dB"].view(torch.int32))
+        assert torch.equal(y.view(torch.int16), g1["y"].view(torch.int16)), name
+        assert torch.equal(u.view(torch.int32), g1["U"].view(torch.int32)), name
+        assert torch.equal(dx.view(torch.int16), g1["dX"].view(torch.int16)), name
+        assert torch.equal(da.view(torch.int32), g1["dA"].view(torch.int32)), name
+        assert torch.equal(db.view(torch.int32), g1["dB"].view(torch.int32)), name
     assert torch.equal(before[0], qw.codes) and torch.equal(before[1], qw.scales)
 
 
