@@ -11,6 +11,10 @@ Formats:
 * E4M3  -- the OCP 8-bit "E4M3FN" float used for the FP8 base: 1, 4 (bias 7),
   3 bits; subnormals 2**-6 * m/8; no infinities; only S.1111.111 is NaN, so
   the largest finite magnitude is 448.  Encoding saturates to +-448.
+* E2M1  -- the 4-bit float element of the OCP Microscaling (MX) formats and of
+  NVFP4: 1 sign, 2 exponent (bias 1), 1 mantissa bit; exponent field 0 is
+  subnormal (0.5 * m); no infinities or NaN, so the largest magnitude is 6.
+  Encoding saturates to +-6.
 """
 
 import numpy as np
@@ -132,4 +136,35 @@ def e4m3_decode(codes):
     val = np.where(e == 0, m / 8.0 * 2.0 ** -6,
                    (1.0 + m / 8.0) * np.ldexp(1.0, (e - 7).astype(np.int32)))
     val = np.where((e == 15) & (m == 7), np.nan, val)
+    return (s * val).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------- E2M1
+
+E2M1_MAX = 6.0
+
+
+def e2m1_encode(x):
+    """Real values (fp32 or fp64) -> E2M1 codes (uint8, 0..15): nearest, ties to
+    even, saturating to +-6.
+
+    The sign bit is the input's sign bit, so a negative value that rounds to
+    zero gives 0x8 (negative zero).  Inputs must be finite.
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x64)):
+        raise ValueError("E2M1 encode of a non-finite value")
+    r = np.clip(_snap(x64, 0, 1), -E2M1_MAX, E2M1_MAX)
+    ebits, mbits = _fields(r, 1, 1, 0)
+    sign = np.signbit(x64).astype(np.int64)
+    return ((sign << 3) | (ebits << 1) | mbits).astype(np.uint8)
+
+
+def e2m1_decode(codes):
+    """E2M1 codes (low 4 bits) -> fp32 values (exact)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64) & 0xF
+    s = np.where((c >> 3) & 1, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    m = (c & 0x1).astype(np.float64)
+    val = np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * np.ldexp(1.0, (e - 1).astype(np.int32)))
     return (s * val).astype(np.float32)

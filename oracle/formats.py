@@ -9,9 +9,13 @@ of 32 consecutive elements; a group occupies 16 bytes, and byte j of the group
 holds element j in its low nibble and element j + 16 in its high nibble.
 Codes are u8 [N, K/2]; scales are a separate array (structure of arrays).
 
+MXFP4 codes use the other common 4-bit packing: byte i of a row holds element
+2i in its low nibble and element 2i + 1 in its high nibble.
+
 Formats (the legacy-GGUF 4-bit type that the GGUF-recipe page names, the
-bitsandbytes NF4 base named on the Surogate pages and the Soup page, and the
-FP8 E4M3 base of the Surogate FP8 recipe):
+bitsandbytes NF4 base named on the Surogate pages and the Soup page, the
+FP8 E4M3 base of the Surogate FP8 recipe, and the FP4 base behind the
+Surogate pages' NVFP4 (E2M1) recipes and MXFP4 checkpoints):
 
 * Q4_0-style: block of 32, fp16 scale d = fp16(absmax / 7), code
   q = clamp(rint(w / d) + 8, 0, 15), value (q - 8) * d.  A zero block stores
@@ -22,6 +26,14 @@ FP8 E4M3 base of the Surogate FP8 recipe):
   quantization.
 * FP8: per-tensor fp32 scale s = absmax / 448, code = E4M3(w / s) with
   saturation; value E4M3(q) * s.  A zero tensor has s = 0 and codes 0.
+* MXFP4 (the OCP Microscaling definition, which the pages name but do not
+  spell out): block of 32, one E8M0 scale byte e per block standing for
+  X = 2**(e - 127); X = 2**(floor(log2 absmax) - 2), the exponent clamped to
+  [-127, 127] (2 is the largest exponent of E2M1), so the block's largest
+  magnitude lands in [4, 8) before saturation; element code = E2M1(w / X),
+  nearest even, saturating to +-6; value E2M1(q) * X, exact in fp32 and bf16.
+  A zero block stores e = 0 and codes 0.  e = 255 (NaN in E8M0) is never
+  written and decodes to NaN.
 """
 
 import statistics
@@ -30,8 +42,8 @@ import numpy as np
 
 from . import codecs
 
-FMT_Q4_0, FMT_NF4, FMT_FP8 = 1, 2, 3
-BLOCK = {FMT_Q4_0: 32, FMT_NF4: 64}
+FMT_Q4_0, FMT_NF4, FMT_FP8, FMT_MXFP4 = 1, 2, 3, 4
+BLOCK = {FMT_Q4_0: 32, FMT_NF4: 64, FMT_MXFP4: 32}
 
 
 # ----------------------------------------------------------------------------- NF4 book
@@ -86,6 +98,24 @@ def bytes_to_nibbles(b):
     g = b.reshape(n, kh // 16, 16)
     q = np.concatenate([g & 0x0F, g >> 4], axis=2)
     return q.reshape(n, kh * 2).astype(np.uint8)
+
+
+def pairs_to_bytes(q):
+    """Codes u8 [N, K] (values 0..15) -> packed bytes u8 [N, K/2]: element 2i low, 2i + 1 high."""
+    q = np.asarray(q, dtype=np.uint8)
+    n, k = q.shape
+    assert k % 2 == 0
+    return (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+
+
+def bytes_to_pairs(b):
+    """Packed bytes u8 [N, K/2] -> codes u8 [N, K] (inverse of pairs_to_bytes)."""
+    b = np.asarray(b, dtype=np.uint8)
+    n, kh = b.shape
+    q = np.empty((n, 2 * kh), dtype=np.uint8)
+    q[:, 0::2] = b & 0x0F
+    q[:, 1::2] = b >> 4
+    return q
 
 
 def _check_w(w):
@@ -182,6 +212,40 @@ def dequant_fp8(codes, scale):
     return (codecs.e4m3_decode(codes) * np.float32(scale)).astype(np.float32)
 
 
+# ----------------------------------------------------------------------------- MXFP4
+
+def mxfp4_shared_exponent(amax):
+    """Block exponent of the MX conversion: floor(log2 amax) - 2, clamped to
+    [-127, 127]; -127 for a zero block."""
+    a = np.asarray(amax, dtype=np.float64)
+    _, e = np.frexp(a)                           # a = f * 2**e, 0.5 <= f < 1: floor(log2 a) = e - 1
+    shared = np.where(a > 0, e.astype(np.int64) - 1 - 2, -127)
+    return np.clip(shared, -127, 127)
+
+
+def pack_mxfp4(w):
+    """fp32 W [N, K] -> (codes u8 [N, K/2] pair-packed, E8M0 scales u8 [N, K/32])."""
+    w = _check_w(w)
+    n, k = w.shape
+    if k % 32:
+        raise ValueError("K must be a multiple of 32")
+    blk = w.reshape(n, k // 32, 32).astype(np.float64)
+    shared = mxfp4_shared_exponent(np.max(np.abs(blk), axis=2))
+    x = np.ldexp(1.0, shared.astype(np.int32))   # the block scale X
+    q = codecs.e2m1_encode(blk / x[:, :, None])  # division by a power of two: exact in fp64
+    return pairs_to_bytes(q.reshape(n, k)), (shared + 127).astype(np.uint8)
+
+
+def dequant_mxfp4(codes, e8):
+    """(codes, E8M0 scale bytes) -> fp32 W [N, K]: E2M1(q) * 2**(e - 127), exact."""
+    v = codecs.e2m1_decode(bytes_to_pairs(codes)).astype(np.float64)
+    n, k = v.shape
+    e = np.asarray(e8, dtype=np.uint8).astype(np.int64)
+    x = np.where(e == 255, np.nan, np.ldexp(1.0, (e - 127).astype(np.int32)))
+    w = v.reshape(n, k // 32, 32) * x[:, :, None]
+    return w.reshape(n, k).astype(np.float32)
+
+
 # ----------------------------------------------------------------------------- dispatch
 
 def pack(fmt, w):
@@ -191,6 +255,8 @@ def pack(fmt, w):
         return pack_nf4(w)
     if fmt == FMT_FP8:
         return pack_fp8(w)
+    if fmt == FMT_MXFP4:
+        return pack_mxfp4(w)
     raise ValueError(f"unknown format {fmt}")
 
 
@@ -201,6 +267,8 @@ def dequant(fmt, codes, scales):
         return dequant_nf4(codes, scales)
     if fmt == FMT_FP8:
         return dequant_fp8(codes, scales)
+    if fmt == FMT_MXFP4:
+        return dequant_mxfp4(codes, scales)
     raise ValueError(f"unknown format {fmt}")
 
 

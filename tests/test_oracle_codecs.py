@@ -162,3 +162,69 @@ def test_e4m3_golden_points():
 def test_e4m3_zero_keeps_sign(x):
     code = codecs.e4m3_encode(np.float32([x]))[0]
     assert code == (0x80 if np.signbit(np.float32(x)) else 0x00)
+
+
+# ----------------------------------------------------------------------------- E2M1
+
+def _e2m1_table():
+    vals = []
+    with open(os.path.join(GOLDEN, "e2m1_values.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                c, v = line.split()
+                vals.append((int(c), float(v)))
+    assert [c for c, _ in vals] == list(range(16))
+    return np.array([v for _, v in vals]), [np.signbit(v) for _, v in vals]
+
+
+def test_e2m1_decode_matches_published_table():
+    table, neg = _e2m1_table()
+    got = codecs.e2m1_decode(np.arange(16, dtype=np.uint8)).astype(np.float64)
+    assert np.array_equal(got, table)
+    assert list(np.signbit(got)) == neg                   # code 8 is negative zero
+
+
+def _e2m1_brute(x):
+    """Nearest of the 16 E2M1 values by exhaustive search; a tie takes the code
+    whose mantissa bit (bit 0) is 0; magnitudes above 6 saturate."""
+    table, _ = _e2m1_table()
+    out = []
+    for v in np.asarray(x, np.float64):
+        best = None
+        for c in range(16):
+            if (c >> 3) != int(np.signbit(v)):             # same sign half, zero included
+                continue
+            d = abs(abs(v) - abs(table[c]))
+            key = (d, c & 1)
+            if best is None or key < best[0]:
+                best = (key, c)
+        out.append(best[1])
+    return np.array(out, np.uint8)
+
+
+def test_e2m1_encode_every_tie_goes_to_even():
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    want = np.array([0, 2, 2, 4, 4, 6, 6], np.uint8)      # 0, 1, 1, 2, 2, 4, 4
+    assert np.array_equal(codecs.e2m1_encode(mids), want)
+    assert np.array_equal(codecs.e2m1_encode(-mids), want | 8)
+    assert np.array_equal(_e2m1_brute(np.concatenate([mids, -mids])),
+                          np.concatenate([want, want | 8]))
+
+
+def test_e2m1_encode_vs_exhaustive_search():
+    g = np.random.default_rng(5)
+    x = np.concatenate([g.uniform(-8, 8, 4000), g.uniform(-1, 1, 2000),
+                        np.arange(-64, 65) / 8.0])         # every multiple of 1/8 in [-8, 8]
+    assert np.array_equal(codecs.e2m1_encode(x), _e2m1_brute(x))
+
+
+@pytest.mark.parametrize("x,code", [(6.0, 7), (6.5, 7), (7.999, 7), (1e30, 7), (-1e30, 15),
+                                    (0.0, 0), (-0.0, 8), (-1e-30, 8), (0.2499, 0), (0.2501, 1)])
+def test_e2m1_saturation_and_zero_sign(x, code):
+    assert int(codecs.e2m1_encode([x])[0]) == code
+
+
+def test_e2m1_rejects_non_finite():
+    with pytest.raises(ValueError):
+        codecs.e2m1_encode([np.nan])

@@ -1,4 +1,5 @@
-"""Pins for the oracle's NF4 code book, pack rules and dequant.  CPU only."""
+"""Pins for the oracle's NF4 code book, the pack rules and dequant of every base
+format (Q4_0-style, NF4, FP8, MXFP4).  CPU only."""
 
 import os
 import statistics
@@ -6,6 +7,7 @@ import statistics
 import numpy as np
 import pytest
 import scipy.stats
+import torch
 
 from oracle import codecs, formats
 
@@ -225,7 +227,7 @@ def test_fp8_pack_properties():
 
 # ----------------------------------------------------------------------------- re-pack
 
-@pytest.mark.parametrize("fmt", [formats.FMT_Q4_0, formats.FMT_NF4])
+@pytest.mark.parametrize("fmt", [formats.FMT_Q4_0, formats.FMT_NF4, formats.FMT_MXFP4])
 def test_repack_is_idempotent_4bit(fmt):
     g = np.random.default_rng(17 + fmt)
     w = (g.standard_normal((40, 512)) * 0.02).astype(np.float32)
@@ -241,3 +243,144 @@ def test_repack_fp8_codes_identical():
     c2, s2 = formats.pack_fp8(formats.dequant_fp8(c1, s1))
     assert np.array_equal(c1, c2)
     assert abs(float(s2) - float(s1)) <= float(np.spacing(s1))
+
+
+# ----------------------------------------------------------------------------- MXFP4
+
+def test_pair_layout_round_trip_and_positions():
+    g = np.random.default_rng(1)
+    q = g.integers(0, 16, size=(3, 96), dtype=np.uint8)
+    b = formats.pairs_to_bytes(q)
+    assert b.shape == (3, 48)
+    assert np.array_equal(formats.bytes_to_pairs(b), q)
+    for i in range(48):
+        assert b[2, i] == q[2, 2 * i] | (q[2, 2 * i + 1] << 4)
+
+
+def _read_mxfp4_golden():
+    vals, codes, e8, byts = [], [], None, None
+    with open(os.path.join(GOLDEN, "mxfp4_block.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            if line.startswith("scale_e8m0"):
+                e8 = int(line.split()[1])
+            elif line.startswith("bytes"):
+                byts = [int(t, 16) for t in line.split()[1:]]
+            else:
+                _, v, c = line.split()
+                vals.append(np.float32(v))
+                codes.append(int(c))
+    return np.array(vals, np.float32), np.array(codes), e8, np.array(byts, np.uint8)
+
+
+def test_mxfp4_golden_block():
+    w, codes, e8, byts = _read_mxfp4_golden()
+    c, e = formats.pack_mxfp4(w.reshape(1, 32))
+    assert int(e[0, 0]) == e8
+    assert np.array_equal(formats.bytes_to_pairs(c)[0], codes)
+    assert np.array_equal(c[0], byts)
+
+
+def test_mxfp4_scale_decode_vs_torch_e8m0():
+    """Every E8M0 byte decodes to torch's float8_e8m0fnu value (255 is NaN)."""
+    e = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(e.copy()).view(torch.float8_e8m0fnu).float().numpy()
+    codes = np.full((256, 16), 0x22, np.uint8)            # every element E2M1 1.0
+    got = formats.dequant_mxfp4(codes, e[:, None])
+    assert np.array_equal(got[:, 0], ref, equal_nan=True)
+    assert np.array_equal(got[:, 31], ref, equal_nan=True)
+
+
+def _shared_exp_brute(amax):
+    """The integer s with 4 <= amax / 2^s < 8 (search), clamped to [-127, 127]."""
+    if amax == 0:
+        return -127
+    s = -200
+    while not (amax / 2.0 ** s < 8):
+        s += 1
+    assert amax / 2.0 ** s >= 4
+    return min(max(s, -127), 127)
+
+
+def test_mxfp4_pack_vs_brute_force():
+    """Scale by exhaustive search over exponents, each code by exhaustive search
+    over the 16 E2M1 values times that scale (ties to the even mantissa)."""
+    g = np.random.default_rng(23)
+    n = 24
+    mags = np.exp2(g.uniform(-30, 30, size=(n, 1)))
+    w = (g.standard_normal((n, 64)) * mags).astype(np.float32)
+    w[3, :32] = 0.0
+    w[4, 5] = -0.0
+    c, e = formats.pack_mxfp4(w)
+    table = codecs.e2m1_decode(np.arange(16, dtype=np.uint8)).astype(np.float64)
+    q = formats.bytes_to_pairs(c)
+    for row in range(n):
+        for blk in range(2):
+            v = w[row, 32 * blk:32 * blk + 32].astype(np.float64)
+            s = _shared_exp_brute(float(np.max(np.abs(v))))
+            assert int(e[row, blk]) == s + 127
+            x = 2.0 ** s
+            for j in range(32):
+                cands = [cc for cc in range(16) if (cc >> 3) == int(np.signbit(v[j]))]
+                best = min(cands, key=lambda cc: (abs(abs(v[j]) - abs(table[cc]) * x), cc & 1))
+                assert q[row, 32 * blk + j] == best, (row, blk, j)
+
+
+def test_mxfp4_round_trip_is_exact():
+    """W built from random codes and scales, each block holding a +-4 or +-6
+    element: packing recovers the codes and scale bytes, dequant is exact."""
+    g = np.random.default_rng(29)
+    n, k = 16, 128
+    q = g.integers(0, 16, size=(n, k), dtype=np.uint8)
+    q[:, ::32] = g.choice([6, 7, 14, 15], size=(n, k // 32))
+    e = g.integers(1, 253, size=(n, k // 32)).astype(np.uint8)
+    w = formats.dequant_mxfp4(formats.pairs_to_bytes(q), e)
+    c2, e2 = formats.pack_mxfp4(w)
+    assert np.array_equal(e2, e)
+    assert np.array_equal(formats.bytes_to_pairs(c2), q)
+    table = codecs.e2m1_decode(np.arange(16, dtype=np.uint8)).astype(np.float64)
+    x = np.exp2(e.astype(np.float64) - 127)
+    want = table[q].reshape(n, k // 32, 32) * x[:, :, None]
+    assert np.array_equal(w.astype(np.float64), want.reshape(n, k))
+
+
+def test_mxfp4_power_of_two_scaling_moves_only_the_scale():
+    g = np.random.default_rng(31)
+    w = (g.standard_normal((8, 256)) * 0.02).astype(np.float32)
+    c0, e0 = formats.pack_mxfp4(w)
+    for j in (-20, -1, 1, 17):
+        c1, e1 = formats.pack_mxfp4((w * np.float32(2.0 ** j)).astype(np.float32))
+        assert np.array_equal(c1, c0)
+        assert np.array_equal(e1.astype(int), e0.astype(int) + j)
+
+
+def test_mxfp4_zero_and_subnormal_blocks():
+    w = np.zeros((2, 64), np.float32)
+    w[1, 32] = np.float32(2.0 ** -128)                    # 0.5 X at the clamped exponent
+    w[1, 33] = np.float32(-(2.0 ** -126))                 # 2 X
+    w[1, 34] = np.float32(2.0 ** -140)                    # far below 0.25 X: zero
+    c, e = formats.pack_mxfp4(w)
+    assert np.array_equal(e, np.array([[0, 0], [0, 0]], np.uint8))
+    q = formats.bytes_to_pairs(c)
+    assert not q[0].any() and not q[1, :32].any()
+    assert list(q[1, 32:35]) == [1, 12, 0]
+    d = formats.dequant_mxfp4(c, e)
+    assert d[1, 32] == np.float32(2.0 ** -128) and d[1, 33] == np.float32(-(2.0 ** -126))
+
+
+def test_mxfp4_error_bound_and_largest_element():
+    """|w - deq| <= X below the saturation point 6 X and < 2 X above it; the
+    largest element of a block codes to the top binade (4 or 6)."""
+    g = np.random.default_rng(37)
+    w = (g.standard_normal((32, 512)) * np.exp2(g.uniform(-10, 5, (32, 1)))).astype(np.float32)
+    c, e = formats.pack_mxfp4(w)
+    d = formats.dequant_mxfp4(c, e).astype(np.float64)
+    x = np.repeat(np.exp2(e.astype(np.float64) - 127), 32, axis=1)
+    err = np.abs(d - w)
+    small = np.abs(w) <= 6 * x
+    assert np.all(err[small] <= x[small]) and np.all(err[~small] < 2 * x[~small])
+    q = formats.bytes_to_pairs(c).reshape(32, 16, 32) & 7
+    top = np.argmax(np.abs(w).reshape(32, 16, 32), axis=2)
+    assert np.all(np.take_along_axis(q, top[:, :, None], 2) >= 6)
