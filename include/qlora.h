@@ -76,10 +76,25 @@ extern "C" {
  * QL_FMT_FP8_E4M3  OCP E4M3FN codes u8 [N, K] (the Surogate FP8 recipe's base
  *                  format) with one fp32 scale s = absmax / 448; code =
  *                  E4M3(w / s) nearest even, saturating; value E4M3(q) * s.
+ * QL_FMT_MXFP4     OCP Microscaling MXFP4 (the FP4 base behind the Surogate
+ *                  pages' NVFP4 / MXFP4 recipes, whose definition the pages
+ *                  leave to the OCP specification): blocks of 32 along K, one
+ *                  E8M0 scale byte e per block (scales u8 [N, K/32]) standing
+ *                  for X = 2^(e - 127), e - 127 = floor(log2 absmax) - 2
+ *                  clamped to [-127, 127] (a zero block stores e = 0); element
+ *                  code = E2M1(w / X) (1 sign, 2 exponent bits with bias 1, 1
+ *                  mantissa bit; nearest even, saturating to +-6; a negative
+ *                  value that rounds to zero keeps its sign); value
+ *                  E2M1(q) * X, exact in fp32 and in bf16.  Codes are
+ *                  pair-packed, unlike the two formats above: byte i of a row
+ *                  holds element 2i in its low nibble and element 2i + 1 in
+ *                  its high nibble (u8 [N, K/2]).  e = 255 is never written
+ *                  and decodes to NaN.
  */
 #define QL_FMT_Q4_0 1
 #define QL_FMT_NF4 2
 #define QL_FMT_FP8_E4M3 3
+#define QL_FMT_MXFP4 4
 
 /* workspace query operations */
 #define QL_OP_PACK 0
@@ -92,9 +107,9 @@ typedef struct ql_qweight {
   int32_t reserved;      /* must be 0                                       */
   int64_t n_out;         /* N                                               */
   int64_t k_in;          /* K                                               */
-  const uint8_t* codes;  /* Q4_0 / NF4: u8 [N, K/2]; FP8: u8 [N, K]         */
+  const uint8_t* codes;  /* Q4_0 / NF4 / MXFP4: u8 [N, K/2]; FP8: u8 [N, K] */
   const void* scales;    /* Q4_0: fp16 [N, K/32]; NF4: fp32 [N, K/64];
-                            FP8: fp32 [1]                                    */
+                            FP8: fp32 [1]; MXFP4: u8 (E8M0) [N, K/32]        */
 } ql_qweight;
 
 /* ---------------------------------------------------------------- misc */

@@ -39,7 +39,7 @@ int check_sticky() {
 }
 
 int check_shape(int32_t fmt, int64_t n, int64_t k) {
-  if (fmt != QL_FMT_Q4_0 && fmt != QL_FMT_NF4 && fmt != QL_FMT_FP8_E4M3)
+  if (fmt != QL_FMT_Q4_0 && fmt != QL_FMT_NF4 && fmt != QL_FMT_FP8_E4M3 && fmt != QL_FMT_MXFP4)
     return set_error(QL_EUNSUPPORTED, "unknown format %d", fmt);
   if (n <= 0 || k <= 0) return set_error(QL_EINVAL, "n_out and k_in must be positive");
   if (k % block_of(fmt)) return set_error(QL_EINVAL, "k_in=%lld is not a multiple of %d", (long long)k, block_of(fmt));

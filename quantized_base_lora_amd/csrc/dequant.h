@@ -23,8 +23,8 @@ struct Book { float c[16]; };
 // instruction right after a load has to wait for it.
 struct WGroup {
   uint4 c0, c1;      // 4-bit: c0 = 16 bytes; fp8: c0, c1 = 32 bytes
-  uint32_t sraw;     // Q4_0: the dword holding the fp16 scale; NF4: fp32 bits; FP8: unused
-  uint32_t ssh;      // Q4_0: bit offset of the fp16 scale in sraw (0 or 16)
+  uint32_t sraw;     // Q4_0 / MXFP4: the dword holding the fp16 / E8M0 scale; NF4: fp32 bits; FP8: unused
+  uint32_t ssh;      // Q4_0: bit offset of the fp16 scale in sraw (0 or 16); MXFP4: 0, 8, 16 or 24
 };
 
 
@@ -49,18 +49,32 @@ __device__ __forceinline__ void nf4_lookup4(uint32_t q4, const uint32_t* tl, con
   out23 = __builtin_amdgcn_perm(h, l, 0x07030602u);
 }
 
+// Scale words per row of W and bytes per scale, for the 4-bit formats.
+template <int FMT> constexpr int64_t scales_per_row(int64_t k) { return FMT == QL_FMT_NF4 ? k / 64 : k / 32; }
+template <int FMT> constexpr int64_t scale_bytes() {
+  return FMT == QL_FMT_Q4_0 ? 2 : (FMT == QL_FMT_MXFP4 ? 1 : 4);
+}
+
 // Dequantizer of one 32-element group, split so its work can be spread over
 // the MFMAs of a contraction step: prepare() once per group (scale decode,
 // NF4 table), then piece(i) yields elements 8i .. 8i+7 as 4 dwords of bf16
-// pairs.  `scale` is already zero for a group outside W.
+// pairs.  `scale` is already zero for a group outside W; for MXFP4 (whose
+// scale cannot express zero) such a group arrives with its codes cleared.
+// MXFP4 codes are pair-packed, so elements 8i .. 8i+7 are the 4 bytes of code
+// word i, each turned into a bf16 pair by the hardware conversion.
 template <int FMT> struct Deq {
   uint32_t wd[8];
   uint32_t tl[4], th[4];   // NF4: byte planes of the 16-entry bf16 table
   float d, nd8;            // Q4_0: d and -8 d; FP8: the tensor scale in d
 
-  __device__ __forceinline__ void prepare(const WGroup& g, float scale, const Book& book) {
+  __device__ __forceinline__ void prepare(const WGroup& g, float scale, const Book& book, bool in = true) {
     wd[0] = g.c0.x; wd[1] = g.c0.y; wd[2] = g.c0.z; wd[3] = g.c0.w;
     wd[4] = g.c1.x; wd[5] = g.c1.y; wd[6] = g.c1.z; wd[7] = g.c1.w;
+    if constexpr (FMT == QL_FMT_MXFP4) {
+      const uint32_t keep = in ? ~0u : 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wd[i] &= keep;
+    }
     d = scale;
     nd8 = -8.0f * scale;                 // (q - 8) d = fma(q, d, -8d), exact
     if constexpr (FMT == QL_FMT_NF4) {
@@ -78,7 +92,12 @@ template <int FMT> struct Deq {
 
   __device__ __forceinline__ uint4 piece(int i) const {
     uint32_t o[4];
-    if constexpr (FMT == QL_FMT_FP8_E4M3) {
+    if constexpr (FMT == QL_FMT_MXFP4) {
+      o[0] = fp4x2_to_bf16x2<0>(wd[i], d);
+      o[1] = fp4x2_to_bf16x2<1>(wd[i], d);
+      o[2] = fp4x2_to_bf16x2<2>(wd[i], d);
+      o[3] = fp4x2_to_bf16x2<3>(wd[i], d);
+    } else if constexpr (FMT == QL_FMT_FP8_E4M3) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[2 * i + h], false);

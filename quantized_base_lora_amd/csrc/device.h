@@ -15,6 +15,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
 }
 
+// MXFP4: the two E2M1 codes of byte SEL of `codes` (low nibble first) times
+// the E8M0 block scale -> a packed bf16 pair.  The hardware conversion reads
+// only the exponent field of `scale` as the E8M0 byte (0 stands for 2^-127,
+// 255 gives NaN) and is exact: every E2M1 value times a power of two in
+// [2^-127, 2^127] is a bf16 number, subnormal results included.
+__device__ __forceinline__ float e8m0_as_scale(uint32_t e) { return __uint_as_float((e & 0xFFu) << 23); }
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t codes, float scale) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, SEL));
+}
+
 // 8 bf16 along a column of an LDS tile: two transposing 64-bit reads, rows r..r+3 and r+4..r+7
 __device__ __forceinline__ bf16x8 tr16x8(const uint16_t* p0, const uint16_t* p1) {
   s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p0);

@@ -107,8 +107,8 @@ void qgemm_kernel(Params p) {
   const int64_t wrow0 = TRANS ? 0 : o0;              // first W row this tile reads
   const int64_t wcol0 = TRANS ? (FP8 ? o0 : o0 / 2) : 0;
   const __amdgpu_buffer_rsrc_t rcode = rsrc(p.codes + wrow0 * crow + wcol0, (p.N - wrow0) * crow - wcol0);
-  const int64_t srow = FMT == QL_FMT_Q4_0 ? p.K / 32 : p.K / 64;   // scale words per row
-  const int64_t ssz = FMT == QL_FMT_Q4_0 ? 2 : 4;
+  const int64_t srow = scales_per_row<FMT>(p.K);   // scale words per row
+  const int64_t ssz = scale_bytes<FMT>();
   const __amdgpu_buffer_rsrc_t rscale =
       rsrc((const char*)p.scales + wrow0 * srow * ssz, (p.N - wrow0) * srow * ssz);
   const __amdgpu_buffer_rsrc_t rdown = rsrc(p.down, (int64_t)R * p.C * 2);
@@ -169,6 +169,10 @@ void qgemm_kernel(Params p) {
         const int64_t idx = wrow * srow + kabs;
         wreg[j].sraw = bload4(rscale, live ? (uint32_t)((idx * 2) & ~3LL) : OOB);
         wreg[j].ssh = (uint32_t)(idx & 1) * 16;
+      } else if constexpr (FMT == QL_FMT_MXFP4) {
+        const int64_t idx = wrow * srow + kabs;
+        wreg[j].sraw = bload4(rscale, live ? (uint32_t)(idx & ~3LL) : OOB);
+        wreg[j].ssh = (uint32_t)(idx & 3) * 8;
       } else {
         wreg[j].sraw = bload4(rscale, live ? (uint32_t)((wrow * srow + (kabs >> 1)) * 4) : OOB);
       }
@@ -191,8 +195,9 @@ void qgemm_kernel(Params p) {
     float scale;
     if constexpr (FP8) scale = tscale;
     else if constexpr (FMT == QL_FMT_Q4_0) scale = decode_scale_q40(wreg[j].sraw >> wreg[j].ssh);
+    else if constexpr (FMT == QL_FMT_MXFP4) scale = e8m0_as_scale(wreg[j].sraw >> wreg[j].ssh);
     else scale = __uint_as_float(wreg[j].sraw);
-    deq.prepare(wreg[j], wg_in[j] ? scale : 0.0f, p.book);
+    deq.prepare(wreg[j], wg_in[j] ? scale : 0.0f, p.book, wg_in[j]);
   };
   auto store_w = [&](uint16_t* st, int j, int i) {   // elements 8i .. 8i+7 of W group j
     if (!wtask) return;
@@ -647,6 +652,7 @@ hipError_t launch_qgemm(const GemmCall& c, hipStream_t s) {
   switch (c.w->format) {
     case QL_FMT_Q4_0: return launch_f<QL_FMT_Q4_0>(p, c.trans, c.r, pl.splits, c.grads, s);
     case QL_FMT_NF4: return launch_f<QL_FMT_NF4>(p, c.trans, c.r, pl.splits, c.grads, s);
+    case QL_FMT_MXFP4: return launch_f<QL_FMT_MXFP4>(p, c.trans, c.r, pl.splits, c.grads, s);
     default: return launch_f<QL_FMT_FP8_E4M3>(p, c.trans, c.r, pl.splits, c.grads, s);
   }
 }

@@ -3,7 +3,9 @@
 // Formats (see include/qlora.h): Q4_0-style blocks of 32 with an fp16 scale
 // absmax/7 and value (q-8)*d; NF4 blocks of 64 with an fp32 absmax and the
 // normal-quantile book (QLoRA paper, "4-bit NormalFloat"); per-tensor FP8
-// E4M3 with scale absmax/448 (the Surogate FP8 recipe's format).  Every
+// E4M3 with scale absmax/448 (the Surogate FP8 recipe's format); MXFP4
+// blocks of 32 E2M1 codes with an E8M0 power-of-two scale (OCP
+// Microscaling, the FP4 base of the Surogate pages' FP4 recipes).  Every
 // quantization decision is taken in IEEE fp32 with correctly rounded
 // division and ties-to-even rounding, so codes are reproducible bit for bit.
 //
@@ -87,6 +89,16 @@ __device__ __forceinline__ uint16_t bf16_bits(float v) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+// E2M1 code of t (a value already divided by its block scale): nearest of
+// 0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to the even mantissa, saturating at 6;
+// the sign bit is the source's (a negative value that rounds to zero keeps it).
+__device__ __forceinline__ uint32_t e2m1_code(float t, uint32_t sign) {
+  const float a = fabsf(t);
+  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) +
+               (a > 5.0f);
+  return c | (sign << 3);
+}
+
 // ------------------------------------------------------------------ 4-bit pack
 // One thread per 32-element group of a row (16 output bytes).  For NF4 two
 // neighbouring threads share a 64-element block and exchange their maxima.
@@ -129,6 +141,17 @@ __global__ __launch_bounds__(kThreads) void pack4_kernel(const float* __restrict
       q[i] = (uint32_t)t;
     }
     if (valid) reinterpret_cast<uint16_t*>(scales)[gid] = d16;
+  } else if (FMT == QL_FMT_MXFP4) {
+    // block exponent floor(log2 amax) - 2, so the block's largest magnitude
+    // lands in [4, 8) (2 is E2M1's largest exponent); clamped to [-127, 127];
+    // a zero (or subnormal-only) block takes -127.  Dividing by 2^sh is the
+    // exact product with 2^-sh, a normal fp32 number for sh in [-127, 125].
+    const uint32_t eb = __float_as_uint(amax) >> 23;
+    const int sh = eb == 0 ? -127 : min(127, max(-127, (int)eb - 127 - 2));
+    const float inv = __uint_as_float((uint32_t)(127 - min(sh, 126)) << 23);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) q[i] = e2m1_code(v[i] * inv, __float_as_uint(v[i]) >> 31);
+    if (valid) reinterpret_cast<uint8_t*>(scales)[gid] = (uint8_t)(sh + 127);
   } else {
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
@@ -151,7 +174,8 @@ __global__ __launch_bounds__(kThreads) void pack4_kernel(const float* __restrict
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         int j = 4 * i + b;
-        word[i] |= (q[j] | (q[j + 16] << 4)) << (8 * b);
+        if (FMT == QL_FMT_MXFP4) word[i] |= (q[2 * j] | (q[2 * j + 1] << 4)) << (8 * b);   // pair-packed
+        else word[i] |= (q[j] | (q[j + 16] << 4)) << (8 * b);                             // split halves
       }
     }
     *reinterpret_cast<uint4*>(codes + gid * 16) = make_uint4(word[0], word[1], word[2], word[3]);
@@ -233,6 +257,21 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
       uint32_t wd[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[16 * h + i] = e4m3_to_f32((wd[i / 4] >> (8 * (i % 4))) & 0xFF) * s;
+    }
+  } else if (FMT == QL_FMT_MXFP4) {
+    // the conversion the GEMMs use; its bf16 results are exact, so fp32 is the same value
+    uint4 t = *reinterpret_cast<const uint4*>(codes + gid * 16);
+    uint32_t wd[4] = {t.x, t.y, t.z, t.w};
+    const float x = e8m0_as_scale(reinterpret_cast<const uint8_t*>(scales)[gid]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t pr[4] = {fp4x2_to_bf16x2<0>(wd[i], x), fp4x2_to_bf16x2<1>(wd[i], x),
+                              fp4x2_to_bf16x2<2>(wd[i], x), fp4x2_to_bf16x2<3>(wd[i], x)};
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        v[8 * i + 2 * b] = __uint_as_float(pr[b] << 16);
+        v[8 * i + 2 * b + 1] = __uint_as_float(pr[b] & 0xFFFF0000u);
+      }
     }
   } else {
     uint4 t = *reinterpret_cast<const uint4*>(codes + gid * 16);
@@ -419,6 +458,9 @@ hipError_t launch_pack_4bit(int fmt, const float* w, int64_t n, int64_t k, uint8
   if (fmt == QL_FMT_Q4_0)
     hipLaunchKernelGGL(pack4_kernel<QL_FMT_Q4_0>, dim3(grid_for(groups)), dim3(kThreads), 0, s, w,
                        groups, codes, scales, status, mids);
+  else if (fmt == QL_FMT_MXFP4)
+    hipLaunchKernelGGL(pack4_kernel<QL_FMT_MXFP4>, dim3(grid_for(groups)), dim3(kThreads), 0, s, w,
+                       groups, codes, scales, status, mids);
   else
     hipLaunchKernelGGL(pack4_kernel<QL_FMT_NF4>, dim3(grid_for(groups)), dim3(kThreads), 0, s, w,
                        groups, codes, scales, status, mids);
@@ -452,6 +494,10 @@ hipError_t launch_dequant(const ql_qweight& w, float* out_f32, uint16_t* out_bf1
       break;
     case QL_FMT_NF4:
       hipLaunchKernelGGL(dequant_kernel<QL_FMT_NF4>, dim3(grid_for(groups)), dim3(kThreads), 0, s,
+                         w.codes, w.scales, groups, w.k_in, out_f32, out_bf16, lv);
+      break;
+    case QL_FMT_MXFP4:
+      hipLaunchKernelGGL(dequant_kernel<QL_FMT_MXFP4>, dim3(grid_for(groups)), dim3(kThreads), 0, s,
                          w.codes, w.scales, groups, w.k_in, out_f32, out_bf16, lv);
       break;
     default:

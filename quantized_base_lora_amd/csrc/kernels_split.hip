@@ -53,8 +53,8 @@ void qsplit_kernel(Params p) {
   const int64_t wrow0 = TRANS ? 0 : o0;
   const int64_t wcol0 = TRANS ? (FP8 ? o0 : o0 / 2) : 0;
   const __amdgpu_buffer_rsrc_t rcode = rsrc(p.codes + wrow0 * crow + wcol0, (p.N - wrow0) * crow - wcol0);
-  const int64_t srow = FMT == QL_FMT_Q4_0 ? p.K / 32 : p.K / 64;
-  const int64_t ssz = FMT == QL_FMT_Q4_0 ? 2 : 4;
+  const int64_t srow = scales_per_row<FMT>(p.K);
+  const int64_t ssz = scale_bytes<FMT>();
   const __amdgpu_buffer_rsrc_t rscale =
       rsrc((const char*)p.scales + wrow0 * srow * ssz, (p.N - wrow0) * srow * ssz);
   const __amdgpu_buffer_rsrc_t rdown = rsrc(p.down, (int64_t)R * p.C * 2);
@@ -96,6 +96,10 @@ void qsplit_kernel(Params p) {
         const int64_t idx = wrow * srow + kabs;
         sl.w.sraw = bload4(rscale, wlive ? (uint32_t)((idx * 2) & ~3LL) : OOB);
         sl.w.ssh = (uint32_t)(idx & 1) * 16;
+      } else if constexpr (FMT == QL_FMT_MXFP4) {
+        const int64_t idx = wrow * srow + kabs;
+        sl.w.sraw = bload4(rscale, wlive ? (uint32_t)(idx & ~3LL) : OOB);
+        sl.w.ssh = (uint32_t)(idx & 3) * 8;
       } else {
         sl.w.sraw = bload4(rscale, wlive ? (uint32_t)((wrow * srow + (kabs >> 1)) * 4) : OOB);
       }
@@ -111,9 +115,10 @@ void qsplit_kernel(Params p) {
     float scale;
     if constexpr (FP8) scale = tscale;
     else if constexpr (FMT == QL_FMT_Q4_0) scale = decode_scale_q40(sl.w.sraw >> sl.w.ssh);
+    else if constexpr (FMT == QL_FMT_MXFP4) scale = e8m0_as_scale(sl.w.sraw >> sl.w.ssh);
     else scale = __uint_as_float(sl.w.sraw);
     Deq<FMT> dq;
-    dq.prepare(sl.w, wg_in ? scale : 0.0f, p.book);
+    dq.prepare(sl.w, wg_in ? scale : 0.0f, p.book, wg_in);
     uint16_t* dst = st + A_EL + (TRANS ? wr * SBT : wr * SA) + wg * 32;
 #pragma unroll
     for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(dst + 8 * i) = dq.piece(i);
@@ -502,6 +507,7 @@ hipError_t launch_split_path(int fmt, bool trans, int r, const Params& p, int sp
   switch (fmt) {
     case QL_FMT_Q4_0: return trans ? launch_r<QL_FMT_Q4_0, true>(p, r, splits, gf, s) : launch_r<QL_FMT_Q4_0, false>(p, r, splits, gf, s);
     case QL_FMT_NF4: return trans ? launch_r<QL_FMT_NF4, true>(p, r, splits, gf, s) : launch_r<QL_FMT_NF4, false>(p, r, splits, gf, s);
+    case QL_FMT_MXFP4: return trans ? launch_r<QL_FMT_MXFP4, true>(p, r, splits, gf, s) : launch_r<QL_FMT_MXFP4, false>(p, r, splits, gf, s);
     default: return trans ? launch_r<QL_FMT_FP8_E4M3, true>(p, r, splits, gf, s) : launch_r<QL_FMT_FP8_E4M3, false>(p, r, splits, gf, s);
   }
 }

@@ -25,6 +25,8 @@ def _sizes(fmt, n, k):
         return n * k, 4
     if fmt == B.FMT_Q4_0:
         return n * k // 2, n * (k // 32) * 2
+    if fmt == B.FMT_MXFP4:
+        return n * k // 2, n * (k // 32)
     return n * k // 2, n * (k // 64) * 4
 
 

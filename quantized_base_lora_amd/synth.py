@@ -21,7 +21,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-FMT_Q4_0, FMT_NF4, FMT_FP8 = 1, 2, 3
+FMT_Q4_0, FMT_NF4, FMT_FP8, FMT_MXFP4 = 1, 2, 3, 4
 TID_W, TID_A, TID_B, TID_X, TID_DY = 0, 1, 2, 3, 4
 
 
@@ -76,6 +76,9 @@ WORKLOADS = {
                                         2048, 16, 16.0,
                                         "32 Llama-3.1-8B layers, base streamed from pinned host",
                                         extra_m=(16,)),
+    "llama3.1_8b_mxfp4": Workload(5, "llama3.1_8b_mxfp4", FMT_MXFP4, LLAMA31_8B, 4096, 16, 16.0,
+                                  "Llama-3.1-8B decoder layer, MXFP4 base (E2M1, E8M0 per 32)",
+                                  extra_m=(16, 64)),
 }
 
 

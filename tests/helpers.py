@@ -41,6 +41,8 @@ def scales_bytes(fmt, s):
         return np.ascontiguousarray(s, dtype=np.uint16).view(np.uint8).ravel()
     if fmt == ofmt.FMT_NF4:
         return np.ascontiguousarray(s, dtype=np.float32).view(np.uint8).ravel()
+    if fmt == ofmt.FMT_MXFP4:
+        return np.ascontiguousarray(s, dtype=np.uint8).ravel()
     return np.array([s], dtype=np.float32).view(np.uint8)
 
 

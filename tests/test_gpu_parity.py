@@ -17,8 +17,8 @@ from quantized_base_lora_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [ofmt.FMT_Q4_0, ofmt.FMT_NF4, ofmt.FMT_FP8]
-FNAME = {1: "q4_0", 2: "nf4", 3: "fp8"}
+FMTS = [ofmt.FMT_Q4_0, ofmt.FMT_NF4, ofmt.FMT_FP8, ofmt.FMT_MXFP4]
+FNAME = {1: "q4_0", 2: "nf4", 3: "fp8", 4: "mxfp4"}
 
 
 def say(*a):
@@ -48,6 +48,21 @@ def special_weight(fmt, n, k, seed):
         w[2, :64] = np.tile(ofmt.nf4_codebook(), 4) * np.float32(0.031)
         w[3, :15] = ofmt.nf4_thresholds() * np.float32(1.0)
         w[3, 15] = 1.0
+    elif fmt == ofmt.FMT_MXFP4:
+        # block scale 2^-7 (largest magnitude 7.9 * 2^-7 lands in [4, 8)): every
+        # E2M1 rounding tie, both signs, saturation above 6, negative zero and a
+        # negative value that rounds to zero
+        x = np.float32(2.0 ** -7)
+        t = np.float32([7.9, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 6.5, 0.1, 0.0])
+        w[2, :32] = 0
+        w[2, :12] = t * x
+        w[2, 12:23] = -t[1:] * x
+        w[2, 23] = -0.0
+        w[2, 24] = np.float32(-0.2) * x
+        # fp32 subnormals and the smallest block scale: 2^-127 * {0.5, 1, 3, 6}
+        w[3, :32] = 0
+        w[3, :4] = np.float32([0.5, 1.0, 3.0, 6.0]) * np.float32(2.0 ** -64) * np.float32(2.0 ** -63)
+        w[5, :32] = np.float32(1e30) * g.standard_normal(32, dtype=np.float32)
     w[4, :blk] = np.float32(0.01)
     return w
 
@@ -128,6 +143,20 @@ def test_dequant_all_codes_and_scales(lib):
     ref = ofmt.dequant_nf4(codes, sc)
     assert np.array_equal(f.cpu().numpy().view(np.uint32), ref.view(np.uint32))
     assert np.array_equal(H.bf16_tensor_bits(b), codecs.bf16_encode(ref))
+    # MXFP4: all 16 codes against every E8M0 scale byte (255 is NaN)
+    n = 256
+    e8 = np.arange(256, dtype=np.uint8).reshape(n, 1)
+    q = np.tile(np.arange(16, dtype=np.uint8), (n, 2))
+    codes = ofmt.pairs_to_bytes(q)
+    qw = B.QWeight(B.FMT_MXFP4, n, 32, torch.from_numpy(codes).cuda(), torch.from_numpy(e8.copy()).cuda())
+    f, b = B.dequant(qw)
+    ref = ofmt.dequant_mxfp4(codes, e8)
+    got = f.cpu().numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 32 and np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    gb = H.bf16_tensor_bits(b).reshape(n, 32)
+    assert np.array_equal(gb[:255], codecs.bf16_encode(ref[:255]))
     # FP8: all 256 codes (two of them NaN) times a few scales
     for s in np.float32([1.0, 0.02 / 448, 7.77e-3]):
         codes = np.tile(np.arange(256, dtype=np.uint8), (32, 1))
@@ -199,6 +228,13 @@ CASES = [
     ("small_nf4_m32_r32", ofmt.FMT_NF4, 32, 640, 416, 32, 64.0),
     # FP8 base, rank 8, few tokens: dA and dB written by the dX reduction launch
     ("small_fp8_m20_r8", ofmt.FMT_FP8, 20, 256, 1216, 8, 16.0),
+    # MXFP4 base (hardware E2M1 -> bf16 conversion): 128x128 and 256-row tiles with
+    # ragged edges, the split path with 64, 33 and 17 tokens
+    ("mxfp4_ragged_mn", ofmt.FMT_MXFP4, 300, 320, 160, 16, 32.0),
+    ("mxfp4_tiles_r32", ofmt.FMT_MXFP4, 520, 1024, 416, 32, 64.0),
+    ("small_mxfp4_m64_r8", ofmt.FMT_MXFP4, 64, 512, 384, 8, 16.0),
+    ("small_mxfp4_m33", ofmt.FMT_MXFP4, 33, 1056, 224, 16, 32.0),
+    ("small_mxfp4_m17_r32", ofmt.FMT_MXFP4, 17, 2048, 320, 32, 64.0),
 ]
 
 
@@ -323,6 +359,8 @@ DET_CASES = [
     ("nf4_m64_split", ofmt.FMT_NF4, 64, 1024, 512, 16),
     ("nf4_m2048_256rows", ofmt.FMT_NF4, 2048, 1024, 8192, 8),
     ("fp8_m300_fp8_mfma", ofmt.FMT_FP8, 300, 256, 512, 16),
+    ("mxfp4_m640", ofmt.FMT_MXFP4, 640, 512, 768, 16),
+    ("mxfp4_m24_fused_grads", ofmt.FMT_MXFP4, 24, 768, 256, 16),
 ]
 
 
@@ -352,7 +390,7 @@ def test_deterministic_and_base_untouched(lib, case):
 # ----------------------------------------------------------------------------- full-size, sampled
 
 FULL = []
-for wname in ("qwen3_0.6b_nf4", "llama3.1_8b_nf4", "qwen3_8b_fp8"):
+for wname in ("qwen3_0.6b_nf4", "llama3.1_8b_nf4", "qwen3_8b_fp8", "llama3.1_8b_mxfp4"):
     wl = synth.WORKLOADS[wname]
     for pi, p in enumerate(wl.projs):
         FULL.append((wname, pi, wl.m))
