@@ -184,6 +184,54 @@ int qlora_linear_bwd(const ql_qweight* w, const uint16_t* x, const uint16_t* dy,
                      uint16_t* dx, float* d_a, float* d_b, int32_t accumulate,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- adapter optimizer step
+ * One AdamW step on the adapters, every listed tensor in one launch.  The
+ * Surogate README page lists "AdamW 8-bit" among its optimizers and the
+ * GGUF-recipe page ("How it works") trains the adapters with 8-bit AdamW; the
+ * update is decoupled weight decay (Loshchilov & Hutter, "Decoupled Weight
+ * Decay Regularization", Algorithm 2) in the PyTorch / bitsandbytes
+ * convention (decay scaled by the learning rate, applied first).  Per
+ * element, g = grad * grad_scale, t = step (>= 1, counting this update):
+ *   param      *= 1 - lr * weight_decay
+ *   exp_avg     = beta1 * exp_avg + (1 - beta1) * g
+ *   exp_avg_sq  = beta2 * exp_avg_sq + (1 - beta2) * g^2
+ *   param      -= lr / (1 - beta1^t) * exp_avg
+ *                 / (sqrt(exp_avg_sq) / sqrt(1 - beta2^t) + eps)
+ *   param_bf16  = bf16(param), nearest even (skipped when NULL)
+ * in fp32; the per-step constants (1 - lr * weight_decay, 1 - beta,
+ * lr / (1 - beta1^t), 1 / sqrt(1 - beta2^t)) are formed in fp64 on the host
+ * and rounded once.  The
+ * moments are fp32: the 8-bit state format of the pages' optimizer is not
+ * defined there.  param, exp_avg and exp_avg_sq are updated in place; grad is
+ * only read (d_a / d_b of qlora_linear_bwd, fp32).
+ *
+ * tensors: host array of n_tensors (0 .. QL_ADAMW_MAX_TENSORS) descriptors;
+ * every pointer dev, 16-byte aligned, n a multiple of 4 (n = 0 is skipped);
+ * the arrays of one tensor must not overlap each other or another tensor's.
+ * hp: host.  Errors (QL_EINVAL): bad count, pointer or size; step < 1;
+ * beta outside [0, 1); negative lr, eps or weight_decay; non-finite values. */
+#define QL_ADAMW_MAX_TENSORS 32
+
+typedef struct ql_adamw_tensor {
+  float* param;          /* dev fp32 [n], master adapter weights            */
+  const float* grad;     /* dev fp32 [n]                                    */
+  float* exp_avg;        /* dev fp32 [n], first moment                      */
+  float* exp_avg_sq;     /* dev fp32 [n], second moment                     */
+  uint16_t* param_bf16;  /* dev bf16 [n] or NULL: copy for the layer        */
+  int64_t n;             /* elements                                        */
+} ql_adamw_tensor;
+
+typedef struct ql_adamw_hparams {
+  /* fp64, so that 1 - beta2 and the bias corrections are formed from the
+     caller's exact values before the one rounding to fp32 */
+  double lr, beta1, beta2, eps, weight_decay, grad_scale;
+  int32_t step;          /* t >= 1 */
+  int32_t reserved;      /* must be 0 */
+} ql_adamw_hparams;
+
+int ql_adamw_step(const ql_adamw_tensor* tensors, int32_t n_tensors,
+                  const ql_adamw_hparams* hp, void* stream);
+
 /* ---------------------------------------------------------------- a10: layer stream
  * Soup page, opening paragraph: the frozen base lives in host RAM and
  * streams into a small pool of pre-allocated VRAM buffers one decoder layer

@@ -24,8 +24,9 @@ EXPORTS = (
     "ql_last_error", "ql_version", "ql_nf4_levels", "qlora_workspace_bytes", "quant_pack",
     "qlora_dequant", "ql_act_quant_e4m3", "qlora_linear_fwd", "qlora_linear_bwd",
     "ql_pool_create", "layer_stream_prefetch", "ql_pool_acquire", "ql_pool_release",
-    "ql_pool_stats", "ql_pool_debug", "ql_pool_destroy",
+    "ql_pool_stats", "ql_pool_debug", "ql_pool_destroy", "ql_adamw_step",
 )
+ADAMW_MAX_TENSORS = 32
 
 
 class QLError(RuntimeError):
@@ -38,6 +39,17 @@ class QWeightC(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("n_out", ctypes.c_int64), ("k_in", ctypes.c_int64),
                 ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class AdamwTensorC(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("exp_avg", ctypes.c_void_p),
+                ("exp_avg_sq", ctypes.c_void_p), ("param_bf16", ctypes.c_void_p), ("n", ctypes.c_int64)]
+
+
+class AdamwHparamsC(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double), ("grad_scale", ctypes.c_double),
+                ("step", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -71,6 +83,8 @@ def load(path=LIB_PATH):
         "ql_pool_stats": (ctypes.c_int, [P, ctypes.POINTER(I64)]),
         "ql_pool_debug": (ctypes.c_int, [P, I32, I32, I32]),
         "ql_pool_destroy": (ctypes.c_int, [P]),
+        "ql_adamw_step": (ctypes.c_int, [ctypes.POINTER(AdamwTensorC), I32,
+                                         ctypes.POINTER(AdamwHparamsC), P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -288,3 +302,43 @@ class Pool:
             self.close()
         except Exception:
             pass
+
+
+# ----------------------------------------------------------------------------- adapter optimizer
+
+class AdamwPlan:
+    """The descriptor array of a fixed set of adapter tensors, checked once, so
+    that each step is a single library call (the tensors must stay alive)."""
+
+    def __init__(self, tensors):
+        self.tensors = list(tensors)
+        self.arr = _adamw_array(self.tensors)
+
+    def step(self, step, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, grad_scale=1.0,
+             stream=None):
+        hp = AdamwHparamsC(lr, beta1, beta2, eps, weight_decay, grad_scale, int(step), 0)
+        _check(load().ql_adamw_step(self.arr, len(self.tensors), ctypes.byref(hp), _stream(stream)))
+
+
+def adamw_step(tensors, step, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+               grad_scale=1.0, stream=None):
+    """One AdamW step, in place, on every (param, grad, exp_avg, exp_avg_sq,
+    param_bf16 or None) tuple of `tensors` (fp32 device tensors of equal
+    sizes; param_bf16 a bf16 tensor of the same size), in one launch."""
+    AdamwPlan(tensors).step(step, lr, beta1, beta2, eps, weight_decay, grad_scale, stream)
+
+
+def _adamw_array(tensors):
+    arr = (AdamwTensorC * max(1, len(tensors)))()
+    for i, (p, g, m, v, pb) in enumerate(tensors):
+        for name, t in (("param", p), ("grad", g), ("exp_avg", m), ("exp_avg_sq", v)):
+            _need(t, name, torch.float32)
+            if t.numel() != p.numel():
+                raise ValueError(f"{name}: size {t.numel()} differs from param's {p.numel()}")
+        if pb is not None:
+            _need(pb, "param_bf16", torch.bfloat16)
+            if pb.numel() != p.numel():
+                raise ValueError("param_bf16 size differs from param's")
+        arr[i] = AdamwTensorC(p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(),
+                              pb.data_ptr() if pb is not None else None, p.numel())
+    return arr

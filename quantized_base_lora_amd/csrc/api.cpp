@@ -161,6 +161,37 @@ int ql_act_quant_e4m3(const uint16_t* x, int64_t m, int64_t k, uint8_t* hi, uint
   return QL_OK;
 }
 
+int ql_adamw_step(const ql_adamw_tensor* tensors, int32_t n_tensors, const ql_adamw_hparams* hp,
+                  void* stream) {
+  if (n_tensors < 0 || n_tensors > QL_ADAMW_MAX_TENSORS)
+    return set_error(QL_EINVAL, "n_tensors=%d outside [0, %d]", n_tensors, QL_ADAMW_MAX_TENSORS);
+  if (!hp || (n_tensors > 0 && !tensors)) return set_error(QL_EINVAL, "null pointer");
+  if (hp->step < 1) return set_error(QL_EINVAL, "step must be >= 1");
+  if (hp->reserved != 0) return set_error(QL_EINVAL, "hparams.reserved must be 0");
+  const double f[6] = {hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->grad_scale};
+  for (double v : f)
+    if (!(v - v == 0.0)) return set_error(QL_EINVAL, "non-finite hyperparameter");
+  if (hp->lr < 0.0 || hp->eps < 0.0 || hp->weight_decay < 0.0)
+    return set_error(QL_EINVAL, "lr, eps and weight_decay must be >= 0");
+  if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0 && hp->beta2 >= 0.0 && hp->beta2 < 1.0))
+    return set_error(QL_EINVAL, "beta1 and beta2 must lie in [0, 1)");
+  for (int32_t i = 0; i < n_tensors; ++i) {
+    const ql_adamw_tensor& t = tensors[i];
+    if (t.n < 0 || t.n % 4) return set_error(QL_EINVAL, "tensor %d: n=%lld is not a multiple of 4", i, (long long)t.n);
+    if (t.n == 0) continue;
+    if (!t.param || !t.grad || !t.exp_avg || !t.exp_avg_sq)
+      return set_error(QL_EINVAL, "tensor %d: null pointer", i);
+    if (!aligned16(t.param) || !aligned16(t.grad) || !aligned16(t.exp_avg) || !aligned16(t.exp_avg_sq) ||
+        (t.param_bf16 && !aligned16(t.param_bf16)))
+      return set_error(QL_EINVAL, "tensor %d: misaligned pointer", i);
+  }
+  int rc = check_sticky();
+  if (rc) return rc;
+  hipError_t e = launch_adamw(tensors, n_tensors, *hp, as_stream(stream));
+  if (e != hipSuccess) return hip_error(e, "adamw launch");
+  return QL_OK;
+}
+
 int qlora_linear_fwd(const ql_qweight* w, const uint16_t* x, int64_t m, const uint16_t* lora_a,
                      const uint16_t* lora_b, int32_t r, float alpha, uint16_t* y, float* u_save,
                      void* ws, size_t ws_bytes, void* stream) {

@@ -115,6 +115,9 @@ hipError_t launch_qgemm8(const Gemm8Call& c, hipStream_t s);
 hipError_t launch_rproj(const uint16_t* act, int64_t m, int64_t c, const uint16_t* d, bool a_layout, int32_t r,
                         float* out, hipStream_t s);
 
+// adapter optimizer step (kernels_optim.hip); arguments already validated
+hipError_t launch_adamw(const ql_adamw_tensor* ts, int32_t nt, const ql_adamw_hparams& hp, hipStream_t s);
+
 // LoRA-side kernels (kernels_lora.hip)
 // out[m][j] = sum_c x[m][c] * b[c][j]     (fp32), b is [C, r]
 hipError_t launch_down_proj(const uint16_t* x, int64_t m, int64_t c, const uint16_t* b,

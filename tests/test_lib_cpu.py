@@ -112,3 +112,25 @@ def test_pool_argument_errors(lib):
     assert lib.ql_pool_create(ctypes.byref(h), 2, odd, 4096, 3, hosts, sizes_ok) == binding.QL_EINVAL
     assert lib.layer_stream_prefetch(None, 0, None) == binding.QL_EINVAL
     assert lib.ql_pool_destroy(None) == binding.QL_OK
+
+
+def test_adamw_argument_errors(lib):
+    T = binding.AdamwTensorC
+    hp = binding.AdamwHparamsC(1e-3, 0.9, 0.999, 1e-8, 0.0, 1.0, 1, 0)
+    good = T(0x10000, 0x20000, 0x30000, 0x40000, None, 64)
+    arr = (T * 1)(good)
+    step = lib.ql_adamw_step
+    assert step(arr, 33, ctypes.byref(hp), None) == binding.QL_EINVAL
+    assert step(arr, -1, ctypes.byref(hp), None) == binding.QL_EINVAL
+    assert step(arr, 1, None, None) == binding.QL_EINVAL
+    assert step(None, 1, ctypes.byref(hp), None) == binding.QL_EINVAL
+    for field, value in (("step", 0), ("reserved", 1), ("beta1", 1.0), ("beta2", -0.1), ("lr", -1e-3),
+                         ("eps", float("nan")), ("weight_decay", float("inf"))):
+        bad = binding.AdamwHparamsC(1e-3, 0.9, 0.999, 1e-8, 0.0, 1.0, 1, 0)
+        setattr(bad, field, value)
+        assert step(arr, 1, ctypes.byref(bad), None) == binding.QL_EINVAL, field
+    for kw in ({"n": 6}, {"param": None}, {"grad": 0x20008}, {"param_bf16": 0x50004}):
+        t = T(0x10000, 0x20000, 0x30000, 0x40000, None, 64)
+        for k, v in kw.items():
+            setattr(t, k, v)
+        assert step((T * 1)(t), 1, ctypes.byref(hp), None) == binding.QL_EINVAL, kw
