@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--streams", action="store_true",
                     help="run projections that are independent in a decoder layer (q|k|v, gate|up) "
                          "on parallel streams")
+    ap.add_argument("--no-plan", action="store_true",
+                    help="issue each layer call from Python instead of through a recorded launch plan")
     ap.add_argument("--optimizer", action="store_true",
                     help="time the fused AdamW step on the layer's adapters instead of the layer step")
     ap.add_argument("--layers", type=int, default=0,
@@ -415,13 +417,52 @@ def main():
                     join.record(st)
                     stream.wait_event(join)
 
-    # the roofline's kernel timing: eager launches on one stream
-    for i in range(args.warmup):
-        eager_step(i, False)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        eager_step(i, True)
-    torch.cuda.synchronize()
+    # Launch plans (the default for eager launches on one stream): the whole
+    # step recorded once per rotated weight copy and enqueued by one library
+    # call, so host-side call overhead never idles the GPU between launches;
+    # the timing plans bracket each forward call with events.
+    use_plan = not (args.no_plan or args.streams or args.graph)
+    if use_plan:
+        def record(pl, i, timed):
+            evs = []
+            for d in (projs if args.phase != "bwd" else []):
+                if timed:
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    pl.add_event(e0, stream)
+                pl.add_fwd(d["qws"][i], d["x"], d["a"], d["b"], wl.alpha, d["y"], d["u"], d["wsf"])
+                if timed:
+                    pl.add_event(e1, stream)
+                    evs.append((d["p"], e0, e1))
+            for d in (reversed(projs) if args.phase != "fwd" else []):
+                pl.add_bwd(d["qws"][i], d["x"], d["dy"], d["u"], d["a"], d["b"], wl.alpha, d["dx"], d["da"],
+                           d["db"], d["ws"])
+            return evs
+        step_plans, timing_plans = [], []
+        for i in range(copies):
+            pl = B.Plan()
+            record(pl, i, False)
+            step_plans.append(pl)
+            tp = B.Plan()
+            timing_plans.append((tp, record(tp, i, True)))
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            timing_plans[i % copies][0].run(stream)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            tp, evs = timing_plans[i % copies]
+            tp.run(stream)
+            torch.cuda.synchronize()
+            ev_pairs.extend((pp, e0.elapsed_time(e1)) for pp, e0, e1 in evs)
+    else:
+        # the roofline's kernel timing: eager launches on one stream
+        for i in range(args.warmup):
+            eager_step(i, False)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            eager_step(i, True)
+        torch.cuda.synchronize()
+        ev_pairs[:] = [(pp, e0.elapsed_time(e1)) for pp, e0, e1 in ev_pairs]
 
     # the step itself: HIP-graph replays (one graph per rotated weight copy) or eager launches
     graphs = []
@@ -439,6 +480,8 @@ def main():
     def run(i):
         if graphs:
             graphs[i % copies].replay()
+        elif use_plan:
+            step_plans[i % copies].run(stream)
         else:
             layer_step(i)
 
@@ -454,8 +497,8 @@ def main():
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
 
-    fwd_ms = sum(e0.elapsed_time(e1) for _, e0, e1 in ev_pairs)
-    fwd_flops = sum(fwd_kernel_flops(wl, p, m) for p, _, _ in ev_pairs)
+    fwd_ms = sum(t for _, t in ev_pairs)
+    fwd_flops = sum(fwd_kernel_flops(wl, p, m) for p, _ in ev_pairs)
     n_launch = max(1, len(ev_pairs))
     fwd_ms = fwd_ms or float("nan")
     avg_launch_ms = fwd_ms / n_launch
@@ -480,7 +523,9 @@ def main():
         "config": {"workload": wl.notes, "name": wl.name, "tokens": m, "base_format": FMT_NAME[wl.fmt],
                    "rank": wl.r, "alpha": wl.alpha, "projections": [f"{p.name}:{p.k}->{p.n}" for p in wl.projs],
                    "packed_copies_rotated": copies,
-                   "step_mode": ("HIP graph replay" if args.graph else "eager launches") + (
+                   "step_mode": ("HIP graph replay" if args.graph else
+                                 "eager launches, one library call per step (recorded launch plan)" if use_plan
+                                 else "eager launches, one library call per layer call") + (
                        ", q|k|v and gate|up on parallel streams" if args.streams else ", one stream")},
         "layer": {"tflops": flops / (ms / 1e3) / 1e12, "frac_bf16_peak": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
                   "algorithmic_bytes": nbytes, "hbm_gbs": nbytes / (ms / 1e3) / 1e9,
@@ -492,7 +537,7 @@ def main():
                      "flops_per_launch_avg": fwd_flops / n_launch},
     }
     if m <= 64:
-        fwd_bytes = sum(BPW[wl.fmt] * p.n * p.k + m * 2 * (p.k + p.n) for p, _, _ in ev_pairs) / n_launch
+        fwd_bytes = sum(BPW[wl.fmt] * p.n * p.k + m * 2 * (p.k + p.n) for p, _ in ev_pairs) / n_launch
         gbs = fwd_bytes / (avg_launch_ms / 1e3) / 1e9
         out["roofline"].update({"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": gbs / PEAK_HBM_GBS, "bytes_per_launch_avg": fwd_bytes})

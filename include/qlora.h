@@ -184,6 +184,44 @@ int qlora_linear_bwd(const ql_qweight* w, const uint16_t* x, const uint16_t* dy,
                      uint16_t* dx, float* d_a, float* d_b, int32_t accumulate,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- launch plans
+ * A plan records a fixed sequence of forward and backward calls (and event
+ * markers) once; ql_plan_run then enqueues the whole sequence on a stream in
+ * one call, with no per-call host work beyond the kernel launches.  With few
+ * tokens a layer call's kernels take a few microseconds, less than the host
+ * needs to marshal a call from an interpreter, so a step issued call by call
+ * leaves the GPU idle between launches; a plan keeps it fed.  (The Soup page's
+ * one-layer-at-a-time schedule and the Surogate README's "native kernel
+ * dispatch" describe the same need: the host must stay ahead of the GPU.)
+ *
+ * ql_plan_add_fwd / ql_plan_add_bwd take the arguments of qlora_linear_fwd /
+ * qlora_linear_bwd without the stream, validate them exactly as those calls
+ * do (same error codes; nothing is recorded on error) and record the call;
+ * the ql_qweight is copied, every buffer is referenced, so buffers must stay
+ * valid and unchanged in size while the plan is used.  ql_plan_add_event
+ * records a marker: at that point of each run, hipEventRecord(event, stream)
+ * (event: a hipEvent_t owned by the caller).  ql_plan_run enqueues every
+ * recorded step in order on `stream`, with the same kernels and launch
+ * configuration as the direct calls, so results are bitwise the same.  A plan
+ * is host data only (no device memory); one plan serves one host thread. */
+typedef struct ql_plan ql_plan;
+
+int ql_plan_create(ql_plan** plan);
+int ql_plan_add_fwd(ql_plan* plan, const ql_qweight* w, const uint16_t* x,
+                    int64_t m, const uint16_t* lora_a, const uint16_t* lora_b,
+                    int32_t r, float alpha, uint16_t* y, float* u_save, void* ws,
+                    size_t ws_bytes);
+int ql_plan_add_bwd(ql_plan* plan, const ql_qweight* w, const uint16_t* x,
+                    const uint16_t* dy, const float* u_save, int64_t m,
+                    const uint16_t* lora_a, const uint16_t* lora_b, int32_t r,
+                    float alpha, uint16_t* dx, float* d_a, float* d_b,
+                    int32_t accumulate, void* ws, size_t ws_bytes);
+int ql_plan_add_event(ql_plan* plan, void* event);
+/* number of recorded steps (0 for NULL) */
+int ql_plan_size(const ql_plan* plan);
+int ql_plan_run(ql_plan* plan, void* stream);
+int ql_plan_destroy(ql_plan* plan);
+
 /* ---------------------------------------------------------------- adapter optimizer step
  * One AdamW step on the adapters, every listed tensor in one launch.  The
  * Surogate README page lists "AdamW 8-bit" among its optimizers and the

@@ -25,6 +25,8 @@ EXPORTS = (
     "qlora_dequant", "ql_act_quant_e4m3", "qlora_linear_fwd", "qlora_linear_bwd",
     "ql_pool_create", "layer_stream_prefetch", "ql_pool_acquire", "ql_pool_release",
     "ql_pool_stats", "ql_pool_debug", "ql_pool_destroy", "ql_adamw_step",
+    "ql_plan_create", "ql_plan_add_fwd", "ql_plan_add_bwd", "ql_plan_add_event", "ql_plan_size",
+    "ql_plan_run", "ql_plan_destroy",
 )
 ADAMW_MAX_TENSORS = 32
 
@@ -85,6 +87,13 @@ def load(path=LIB_PATH):
         "ql_pool_destroy": (ctypes.c_int, [P]),
         "ql_adamw_step": (ctypes.c_int, [ctypes.POINTER(AdamwTensorC), I32,
                                          ctypes.POINTER(AdamwHparamsC), P]),
+        "ql_plan_create": (ctypes.c_int, [ctypes.POINTER(P)]),
+        "ql_plan_add_fwd": (ctypes.c_int, [P, QW, P, I64, P, P, I32, F, P, P, P, SZ]),
+        "ql_plan_add_bwd": (ctypes.c_int, [P, QW, P, P, P, I64, P, P, I32, F, P, P, P, I32, P, SZ]),
+        "ql_plan_add_event": (ctypes.c_int, [P, P]),
+        "ql_plan_size": (ctypes.c_int, [P]),
+        "ql_plan_run": (ctypes.c_int, [P, P]),
+        "ql_plan_destroy": (ctypes.c_int, [P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -254,6 +263,68 @@ def linear_bwd(qw, x, dy, u, a, b, alpha, need_dx=True, accumulate=False, dx=Non
                                    float(alpha), _ptr(dx) if need_dx else None, _ptr(da), _ptr(db),
                                    1 if accumulate else 0, _ptr(ws), ws.numel(), _stream(stream)))
     return (dx if need_dx else None), da, db
+
+
+class Plan:
+    """A recorded sequence of forward / backward calls (and event markers),
+    enqueued by run() in one library call.  Outputs and workspaces must be
+    given (they are referenced, not allocated); the plan keeps the tensors
+    alive."""
+
+    def __init__(self):
+        self._h = ctypes.c_void_p()
+        _check(load().ql_plan_create(ctypes.byref(self._h)))
+        self._keep = []
+
+    def add_fwd(self, qw, x, a, b, alpha, y, u, ws):
+        m, r = x.shape[0], a.shape[0]
+        _need(x, "x", torch.bfloat16, (m, qw.k))
+        _need(a, "A", torch.bfloat16, (r, qw.k))
+        _need(b, "B", torch.bfloat16, (qw.n, r))
+        _need(y, "y", torch.bfloat16, (m, qw.n))
+        _need(u, "U", torch.float32, (m, r))
+        _check(load().ql_plan_add_fwd(self._h, qw.cstruct, _ptr(x), m, _ptr(a), _ptr(b), r, float(alpha),
+                                      _ptr(y), _ptr(u), _ptr(ws), ws.numel() if ws is not None else 0))
+        self._keep += [qw, x, a, b, y, u, ws]
+
+    def add_bwd(self, qw, x, dy, u, a, b, alpha, dx, da, db, ws, accumulate=False):
+        m, r = x.shape[0], a.shape[0]
+        _need(x, "x", torch.bfloat16, (m, qw.k))
+        _need(dy, "dY", torch.bfloat16, (m, qw.n))
+        _need(u, "U", torch.float32, (m, r))
+        _need(da, "dA", torch.float32, (r, qw.k))
+        _need(db, "dB", torch.float32, (qw.n, r))
+        if dx is not None:
+            _need(dx, "dX", torch.bfloat16, (m, qw.k))
+        _check(load().ql_plan_add_bwd(self._h, qw.cstruct, _ptr(x), _ptr(dy), _ptr(u), m, _ptr(a), _ptr(b), r,
+                                      float(alpha), _ptr(dx), _ptr(da), _ptr(db), 1 if accumulate else 0,
+                                      _ptr(ws), ws.numel()))
+        self._keep += [qw, x, dy, u, a, b, dx, da, db, ws]
+
+    def add_event(self, event, stream=None):
+        """Record `event` (a torch.cuda.Event) at this point of every run; the
+        event is recorded once here so that its handle exists."""
+        event.record(stream if stream is not None else torch.cuda.current_stream())
+        _check(load().ql_plan_add_event(self._h, ctypes.c_void_p(event.cuda_event)))
+        self._keep.append(event)
+
+    def __len__(self):
+        return int(load().ql_plan_size(self._h))
+
+    def run(self, stream=None):
+        _check(load().ql_plan_run(self._h, _stream(stream)))
+
+    def close(self):
+        if self._h:
+            load().ql_plan_destroy(self._h)
+            self._h = ctypes.c_void_p()
+            self._keep = []
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 # ----------------------------------------------------------------------------- layer stream pool

@@ -5,6 +5,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <new>
+#include <vector>
+
 #include "common.h"
 
 namespace ql {
@@ -81,10 +84,151 @@ BwdLayout bwd_layout(int32_t fmt, int64_t n, int64_t k, int64_t m, int32_t r) {
   return l;
 }
 
+
+// Arguments of one forward / backward call; the weight descriptor is copied.
+struct FwdArgs {
+  ql_qweight w;
+  const uint16_t* x;
+  int64_t m;
+  const uint16_t *a, *b;
+  int32_t r;
+  float alpha;
+  uint16_t* y;
+  float* u;
+  void* ws;
+  size_t ws_bytes;
+};
+struct BwdArgs {
+  ql_qweight w;
+  const uint16_t *x, *dy;
+  const float* u;
+  int64_t m;
+  const uint16_t *a, *b;
+  int32_t r;
+  float alpha;
+  uint16_t* dx;
+  float *da, *db;
+  int32_t accumulate;
+  void* ws;
+  size_t ws_bytes;
+};
+
+int check_fwd(const ql_qweight* wp, const FwdArgs& a) {
+  int rc;
+  if ((rc = check_weight(wp)) || (rc = check_rank(a.r))) return rc;
+  if (a.m < 0) return set_error(QL_EINVAL, "m < 0");
+  if (a.m == 0) return QL_OK;
+  if (!a.x || !a.a || !a.b || !a.y || !a.u) return set_error(QL_EINVAL, "null pointer");
+  if (!aligned16(a.x) || !aligned16(a.a) || !aligned16(a.b) || !aligned16(a.y) || !aligned16(a.u))
+    return set_error(QL_EINVAL, "misaligned pointer");
+  const size_t need = qgemm_workspace_bytes(a.w.format, false, a.m, a.w.n_out, a.w.k_in, a.r);
+  if (a.ws_bytes < need) return set_error(QL_EWORKSPACE, "forward needs %zu workspace bytes", need);
+  if (need && (!a.ws || !aligned16(a.ws))) return set_error(QL_EINVAL, "null or misaligned workspace");
+  return QL_OK;
+}
+
+int enqueue_fwd(const FwdArgs& a, hipStream_t s) {
+  if (a.m == 0) return QL_OK;
+  GemmCall c{};
+  c.w = &a.w;
+  c.trans = false;
+  c.act = a.x;
+  c.m = a.m;
+  c.down = a.a;
+  c.up = a.b;
+  c.r = a.r;
+  c.s = a.alpha / (float)a.r;
+  c.out = a.y;
+  c.save = a.u;
+  c.ws = a.ws;
+  hipError_t e = launch_qgemm(c, s);
+  if (e != hipSuccess) return hip_error(e, "forward launch");
+  return QL_OK;
+}
+
+int check_bwd(const ql_qweight* wp, const BwdArgs& a) {
+  int rc;
+  if ((rc = check_weight(wp)) || (rc = check_rank(a.r))) return rc;
+  if (a.m < 0) return set_error(QL_EINVAL, "m < 0");
+  // with m == 0 the token-dimension buffers may be empty (null); dA and dB are still written
+  if ((a.m > 0 && (!a.x || !a.dy || !a.u)) || !a.a || !a.b || !a.da || !a.db || !a.ws)
+    return set_error(QL_EINVAL, "null pointer");
+  if (!aligned16(a.x) || !aligned16(a.dy) || !aligned16(a.u) || !aligned16(a.a) || !aligned16(a.b) ||
+      (a.dx && !aligned16(a.dx)) || !aligned16(a.da) || !aligned16(a.db) || !aligned16(a.ws))
+    return set_error(QL_EINVAL, "misaligned pointer");
+  const BwdLayout L = bwd_layout(a.w.format, a.w.n_out, a.w.k_in, a.m, a.r);
+  if (a.ws_bytes < L.total) return set_error(QL_EWORKSPACE, "backward needs %zu workspace bytes", L.total);
+  return QL_OK;
+}
+
+int enqueue_bwd(const BwdArgs& a, hipStream_t s) {
+  const int64_t n = a.w.n_out, k = a.w.k_in, m = a.m;
+  const BwdLayout L = bwd_layout(a.w.format, n, k, m, a.r);
+  char* base = reinterpret_cast<char*>(a.ws);
+  float* v = reinterpret_cast<float*>(base + L.v);
+  float* pa = reinterpret_cast<float*>(base + L.pa);
+  float* pb = reinterpret_cast<float*>(base + L.pb);
+  const float sc = a.alpha / (float)a.r;
+  hipError_t e = hipSuccess;
+  // at most 32 tokens the dX reduction launch also writes dA and dB
+  const bool fuse = m > 0 && a.dx && split_path_fuses_grads(m);
+  GradFuse gf{a.x, a.u, a.da, a.db, a.accumulate != 0};
+  if (m > 0 && a.dx) {
+    GemmCall c{};
+    c.w = &a.w;
+    c.trans = true;
+    c.act = a.dy;
+    c.m = m;
+    c.down = a.b;
+    c.up = a.a;
+    c.r = a.r;
+    c.s = sc;
+    c.out = a.dx;
+    c.save = v;
+    c.ws = base + L.g;
+    c.grads = fuse ? &gf : nullptr;
+    e = launch_qgemm(c, s);
+  } else if (m > 0) {
+    e = launch_down_proj(a.dy, m, n, a.b, a.r, v, s);
+  }
+  if (e == hipSuccess && !fuse) {
+    GradLaunch g{};
+    g.x = a.x;
+    g.dy = a.dy;
+    g.v = v;
+    g.u = a.u;
+    g.d_a = a.da;
+    g.d_b = a.db;
+    g.part_a = pa;
+    g.part_b = pb;
+    g.m = m;
+    g.k = k;
+    g.n = n;
+    g.r = a.r;
+    g.nparts = L.parts;
+    g.s = sc;
+    g.accumulate = a.accumulate != 0;
+    e = launch_grads(g, s);
+  }
+  if (e != hipSuccess) return hip_error(e, "backward launch");
+  return QL_OK;
+}
+
+struct PlanStep {
+  enum Kind { FWD, BWD, EVENT } kind;
+  FwdArgs fwd;
+  BwdArgs bwd;
+  hipEvent_t event;
+};
+
 }  // namespace
 }  // namespace ql
 
 using namespace ql;
+
+struct ql_plan {
+  std::vector<PlanStep> steps;
+};
 
 extern "C" {
 
@@ -195,99 +339,95 @@ int ql_adamw_step(const ql_adamw_tensor* tensors, int32_t n_tensors, const ql_ad
 int qlora_linear_fwd(const ql_qweight* w, const uint16_t* x, int64_t m, const uint16_t* lora_a,
                      const uint16_t* lora_b, int32_t r, float alpha, uint16_t* y, float* u_save,
                      void* ws, size_t ws_bytes, void* stream) {
-  int rc;
-  if ((rc = check_weight(w)) || (rc = check_rank(r))) return rc;
-  if (m < 0) return set_error(QL_EINVAL, "m < 0");
-  if (m == 0) return QL_OK;
-  if (!x || !lora_a || !lora_b || !y || !u_save) return set_error(QL_EINVAL, "null pointer");
-  if (!aligned16(x) || !aligned16(lora_a) || !aligned16(lora_b) || !aligned16(y) || !aligned16(u_save))
-    return set_error(QL_EINVAL, "misaligned pointer");
-  size_t need = qlora_workspace_bytes(QL_OP_FWD, w->format, w->n_out, w->k_in, m, r);
-  if (ws_bytes < need) return set_error(QL_EWORKSPACE, "forward needs %zu workspace bytes", need);
-  if (need && (!ws || !aligned16(ws))) return set_error(QL_EINVAL, "null or misaligned workspace");
+  FwdArgs a{w ? *w : ql_qweight{}, x, m, lora_a, lora_b, r, alpha, y, u_save, ws, ws_bytes};
+  int rc = check_fwd(w, a);
+  if (rc || m == 0) return rc;
   if ((rc = check_sticky())) return rc;
-  GemmCall c{};
-  c.w = w;
-  c.trans = false;
-  c.act = x;
-  c.m = m;
-  c.down = lora_a;
-  c.up = lora_b;
-  c.r = r;
-  c.s = alpha / (float)r;
-  c.out = y;
-  c.save = u_save;
-  c.ws = ws;
-  hipError_t e = launch_qgemm(c, as_stream(stream));
-  if (e != hipSuccess) return hip_error(e, "forward launch");
-  return QL_OK;
+  return enqueue_fwd(a, as_stream(stream));
 }
 
 int qlora_linear_bwd(const ql_qweight* w, const uint16_t* x, const uint16_t* dy, const float* u_save,
                      int64_t m, const uint16_t* lora_a, const uint16_t* lora_b, int32_t r, float alpha,
                      uint16_t* dx, float* d_a, float* d_b, int32_t accumulate, void* ws,
                      size_t ws_bytes, void* stream) {
-  int rc;
-  if ((rc = check_weight(w)) || (rc = check_rank(r))) return rc;
-  if (m < 0) return set_error(QL_EINVAL, "m < 0");
-  // with m == 0 the token-dimension buffers may be empty (null); dA and dB are still written
-  if ((m > 0 && (!x || !dy || !u_save)) || !lora_a || !lora_b || !d_a || !d_b || !ws)
-    return set_error(QL_EINVAL, "null pointer");
-  if (!aligned16(x) || !aligned16(dy) || !aligned16(u_save) || !aligned16(lora_a) || !aligned16(lora_b) ||
-      (dx && !aligned16(dx)) || !aligned16(d_a) || !aligned16(d_b) || !aligned16(ws))
-    return set_error(QL_EINVAL, "misaligned pointer");
-  const int64_t n = w->n_out, k = w->k_in;
-  BwdLayout L = bwd_layout(w->format, n, k, m, r);
-  if (ws_bytes < L.total) return set_error(QL_EWORKSPACE, "backward needs %zu workspace bytes", L.total);
+  BwdArgs a{w ? *w : ql_qweight{}, x, dy, u_save, m, lora_a, lora_b, r, alpha, dx, d_a, d_b, accumulate, ws,
+            ws_bytes};
+  int rc = check_bwd(w, a);
+  if (rc) return rc;
   if ((rc = check_sticky())) return rc;
+  return enqueue_bwd(a, as_stream(stream));
+}
+
+// ---------------------------------------------------------------- launch plans
+int ql_plan_create(ql_plan** plan) {
+  if (!plan) return set_error(QL_EINVAL, "null plan pointer");
+  *plan = new (std::nothrow) ql_plan();
+  if (!*plan) return set_error(QL_EINVAL, "out of host memory");
+  return QL_OK;
+}
+
+int ql_plan_add_fwd(ql_plan* plan, const ql_qweight* w, const uint16_t* x, int64_t m,
+                    const uint16_t* lora_a, const uint16_t* lora_b, int32_t r, float alpha, uint16_t* y,
+                    float* u_save, void* ws, size_t ws_bytes) {
+  if (!plan) return set_error(QL_EINVAL, "null plan");
+  FwdArgs a{w ? *w : ql_qweight{}, x, m, lora_a, lora_b, r, alpha, y, u_save, ws, ws_bytes};
+  int rc = check_fwd(w, a);
+  if (rc) return rc;
+  PlanStep st{};
+  st.kind = PlanStep::FWD;
+  st.fwd = a;
+  plan->steps.push_back(st);
+  return QL_OK;
+}
+
+int ql_plan_add_bwd(ql_plan* plan, const ql_qweight* w, const uint16_t* x, const uint16_t* dy,
+                    const float* u_save, int64_t m, const uint16_t* lora_a, const uint16_t* lora_b, int32_t r,
+                    float alpha, uint16_t* dx, float* d_a, float* d_b, int32_t accumulate, void* ws,
+                    size_t ws_bytes) {
+  if (!plan) return set_error(QL_EINVAL, "null plan");
+  BwdArgs a{w ? *w : ql_qweight{}, x, dy, u_save, m, lora_a, lora_b, r, alpha, dx, d_a, d_b, accumulate, ws,
+            ws_bytes};
+  int rc = check_bwd(w, a);
+  if (rc) return rc;
+  PlanStep st{};
+  st.kind = PlanStep::BWD;
+  st.bwd = a;
+  plan->steps.push_back(st);
+  return QL_OK;
+}
+
+int ql_plan_add_event(ql_plan* plan, void* event) {
+  if (!plan || !event) return set_error(QL_EINVAL, "null plan or event");
+  PlanStep st{};
+  st.kind = PlanStep::EVENT;
+  st.event = reinterpret_cast<hipEvent_t>(event);
+  plan->steps.push_back(st);
+  return QL_OK;
+}
+
+int ql_plan_size(const ql_plan* plan) { return plan ? (int)plan->steps.size() : 0; }
+
+int ql_plan_run(ql_plan* plan, void* stream) {
+  if (!plan) return set_error(QL_EINVAL, "null plan");
+  int rc = check_sticky();
+  if (rc) return rc;
   hipStream_t s = as_stream(stream);
-  char* base = reinterpret_cast<char*>(ws);
-  float* v = reinterpret_cast<float*>(base + L.v);
-  float* pa = reinterpret_cast<float*>(base + L.pa);
-  float* pb = reinterpret_cast<float*>(base + L.pb);
-  const float sc = alpha / (float)r;
-  hipError_t e = hipSuccess;
-  // at most 64 tokens the dX reduction launch also writes dA and dB
-  const bool fuse = m > 0 && dx && split_path_fuses_grads(m);
-  GradFuse gf{x, u_save, d_a, d_b, accumulate != 0};
-  if (m > 0 && dx) {
-    GemmCall c{};
-    c.w = w;
-    c.trans = true;
-    c.act = dy;
-    c.m = m;
-    c.down = lora_b;
-    c.up = lora_a;
-    c.r = r;
-    c.s = sc;
-    c.out = dx;
-    c.save = v;
-    c.ws = base + L.g;
-    c.grads = fuse ? &gf : nullptr;
-    e = launch_qgemm(c, s);
-  } else if (m > 0) {
-    e = launch_down_proj(dy, m, n, lora_b, r, v, s);
+  for (const PlanStep& st : plan->steps) {
+    switch (st.kind) {
+      case PlanStep::FWD: rc = enqueue_fwd(st.fwd, s); break;
+      case PlanStep::BWD: rc = enqueue_bwd(st.bwd, s); break;
+      default: {
+        hipError_t e = hipEventRecord(st.event, s);
+        rc = e == hipSuccess ? QL_OK : hip_error(e, "plan event record");
+      }
+    }
+    if (rc) return rc;
   }
-  if (e == hipSuccess && !fuse) {
-    GradLaunch g{};
-    g.x = x;
-    g.dy = dy;
-    g.v = v;
-    g.u = u_save;
-    g.d_a = d_a;
-    g.d_b = d_b;
-    g.part_a = pa;
-    g.part_b = pb;
-    g.m = m;
-    g.k = k;
-    g.n = n;
-    g.r = r;
-    g.nparts = L.parts;
-    g.s = sc;
-    g.accumulate = accumulate != 0;
-    e = launch_grads(g, s);
-  }
-  if (e != hipSuccess) return hip_error(e, "backward launch");
+  return QL_OK;
+}
+
+int ql_plan_destroy(ql_plan* plan) {
+  delete plan;
   return QL_OK;
 }
 

@@ -18,6 +18,21 @@ namespace {
 // all tokens (TM = 32 MBK rows: 32 when M <= 32, else 64) x 128 output
 // columns, four waves side by side (TM x 32 each), the contraction split over
 // blockIdx.y; fp32 partial sums out.
+//
+// Forward (y = x.W^T): no W element is used by more than one wave, so W is
+// not staged through LDS.  Each lane loads the codes of its own MFMA
+// B-operand rows (row 32 wave + lane % 32, half lane / 32 of each 32-element
+// group) and dequantizes them straight into operand registers; only the
+// shared activation tile goes through LDS.  The order in which a dot product
+// runs over K is free, so the K elements a lane's operand holds are chosen to
+// be contiguous in memory: for the split-half 4-bit layout that is the
+// standard MFMA order (8 bytes give elements 8h..8h+7 and 16+8h..16+8h+7);
+// for MXFP4 and FP8 slice ks of lane half h holds elements
+// 32 (ks / 2) + 16 h + 8 (ks % 2), and the activation fragment is read in the
+// same order.
+template <int FMT> constexpr bool split_half_codes() { return FMT == QL_FMT_Q4_0 || FMT == QL_FMT_NF4; }
+template <bool TRANS> constexpr int split_b_elems() { return TRANS ? TK * (128 + 32) : 0; }
+
 template <int FMT, bool TRANS, int R, int MBK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void qsplit_kernel(Params p) {
@@ -25,12 +40,15 @@ void qsplit_kernel(Params p) {
   static_assert(D % 2 == 0, "buffer parity of a step is its position in the chunk");
   constexpr int SBT = TN + 32;
   constexpr int A_EL = TM * SA;
-  constexpr int B_EL = TRANS ? TK * SBT : TN * SA;
+  constexpr int B_EL = split_b_elems<TRANS>();
   constexpr int D_EL = TRANS ? BL_ELEMS : AD_ELEMS;
   constexpr int STAGE = A_EL + B_EL + D_EL;
   constexpr int RB = (R + 15) / 16;
   constexpr int GPR = TRANS ? TN / 32 : TK / 32;
   constexpr bool FP8 = FMT == QL_FMT_FP8_E4M3;
+  constexpr bool DIRECT = !TRANS;                    // forward: W straight into operand registers
+  constexpr bool HALVES = split_half_codes<FMT>();
+  static_assert(!DIRECT || TN == 4 * 32, "one 32-row W block per wave");
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -65,13 +83,18 @@ void qsplit_kernel(Params p) {
   const int wr = tid / GPR, wg = tid % GPR;          // one W group per thread per step
   const bool wg_in = !TRANS || (o0 + 32 * (wg + 1) <= p.K);
   constexpr int DPR = TRANS ? R / 8 : TK / 8;
-  const bool dload = tid < 8 * R;
+  // the rank-r projection (U or V) is stored by column tile 0 only, so the
+  // other tiles neither load the down matrix nor run its MFMAs
+  const bool rank_tile = ntile == 0;
+  const bool dload = tid < 8 * R && rank_tile;
   const int drow = tid / DPR, dcol = (tid % DPR) * 8;
 
   struct Slot {
     uint4 a0, a1, d;
-    WGroup w;
+    WGroup w;   // direct forward: c0 (c1 for FP8) = this lane's codes of both groups; sraw / ssh = their scales
+    int kt;
   };
+  const int hsel = lane >> 5;                        // direct forward: which half of each group this lane holds
   Slot ring[D];
   // loads of step kt; a step past the split's end reads zeros (no memory traffic)
   auto issue = [&](Slot& sl, int kt) {
@@ -80,6 +103,34 @@ void qsplit_kernel(Params p) {
     const bool alive = sv && c0 + acol < p.C;
     sl.a0 = bload16(ract, alive ? (uint32_t)((arow * p.C + c0 + acol) * 2) : OOB);
     if constexpr (MBK == 2) sl.a1 = bload16(ract, alive ? (uint32_t)(((arow + 32) * p.C + c0 + acol) * 2) : OOB);
+    sl.kt = kt;
+    if constexpr (DIRECT) {
+      const int64_t wrow = 32 * wave + (lane & 31);  // W row, relative to the tile
+      const bool g0 = sv && c0 < p.C, g1 = sv && c0 + 32 < p.C;
+      if constexpr (FP8) {
+        const uint32_t base = (uint32_t)(wrow * crow + c0 + 16 * hsel);
+        sl.w.c0 = bload16(rcode, g0 ? base : OOB);
+        sl.w.c1 = bload16(rcode, g1 ? base + 32 : OOB);
+        sl.w.sraw = sl.w.ssh = 0;
+      } else {
+        const uint32_t base = (uint32_t)(wrow * crow + c0 / 2 + 8 * hsel);
+        const uint2 q0 = bload8(rcode, g0 ? base : OOB);
+        const uint2 q1 = bload8(rcode, g1 ? base + 16 : OOB);
+        sl.w.c0 = make_uint4(q0.x, q0.y, q1.x, q1.y);
+        sl.w.c1 = make_uint4(0, 0, 0, 0);
+        const int64_t idx = wrow * srow + (c0 >> 5);   // group 0's scale index (NF4: per 64, below)
+        if constexpr (FMT == QL_FMT_Q4_0) {
+          sl.w.sraw = bload2(rscale, g0 ? (uint32_t)(idx * 2) : OOB);
+          sl.w.ssh = bload2(rscale, g1 ? (uint32_t)(idx * 2 + 2) : OOB);
+        } else if constexpr (FMT == QL_FMT_MXFP4) {
+          sl.w.sraw = bload1(rscale, g0 ? (uint32_t)idx : OOB);
+          sl.w.ssh = bload1(rscale, g1 ? (uint32_t)(idx + 1) : OOB);
+        } else {
+          sl.w.sraw = bload4(rscale, g0 ? (uint32_t)((wrow * srow + (c0 >> 6)) * 4) : OOB);
+          sl.w.ssh = 0;
+        }
+      }
+    } else {
     const int64_t wrow = TRANS ? c0 + wr : wr;
     const int64_t kgrp = TRANS ? wg : (c0 >> 5) + wg;
     const bool wlive = sv && (TRANS || c0 + 32 * wg < p.C);
@@ -104,14 +155,48 @@ void qsplit_kernel(Params p) {
         sl.w.sraw = bload4(rscale, wlive ? (uint32_t)((wrow * srow + (kabs >> 1)) * 4) : OOB);
       }
     }
+    }
     uint32_t doff;
     if constexpr (TRANS) doff = (uint32_t)(((c0 + drow) * R + dcol) * 2);
     else doff = c0 + dcol < p.C ? (uint32_t)((drow * p.C + c0 + dcol) * 2) : OOB;
     sl.d = bload16(rdown, dload && sv ? doff : OOB);
   };
-  auto store = [&](const Slot& sl, uint16_t* st) {
+  // direct forward: the lane's codes of a step -> its four B operands (slices ks = 0..3)
+  auto dequant_direct = [&](const Slot& sl, uint4* wb) {
+    const int64_t c0 = (int64_t)sl.kt * TK;
+    const bool g0 = sl.kt < kend && c0 < p.C, g1 = sl.kt < kend && c0 + 32 < p.C;
+    float s0, s1;
+    if constexpr (FP8) s0 = s1 = tscale;
+    else if constexpr (FMT == QL_FMT_Q4_0) { s0 = decode_scale_q40(sl.w.sraw); s1 = decode_scale_q40(sl.w.ssh); }
+    else if constexpr (FMT == QL_FMT_MXFP4) { s0 = e8m0_as_scale(sl.w.sraw); s1 = e8m0_as_scale(sl.w.ssh); }
+    else s0 = s1 = __uint_as_float(sl.w.sraw);   // NF4: one block of 64 (K % 64 == 0, so g1 == g0)
+    constexpr int P1 = HALVES ? 2 : 1;             // piece holding a lane's second slice of a group
+    WGroup q;
+    q.c1 = make_uint4(0, 0, 0, 0);
+    q.sraw = q.ssh = 0;
+    Deq<FMT> dq;
+    q.c0 = FP8 ? sl.w.c0 : make_uint4(sl.w.c0.x, sl.w.c0.y, 0, 0);
+    dq.prepare(q, g0 ? s0 : 0.0f, p.book, g0);
+    wb[0] = dq.piece(0);
+    wb[1] = dq.piece(P1);
+    if constexpr (FMT == QL_FMT_NF4) {
+      dq.wd[0] = sl.w.c0.z;                        // same block, same table
+      dq.wd[1] = sl.w.c0.w;
+    } else {
+      q.c0 = FP8 ? sl.w.c1 : make_uint4(sl.w.c0.z, sl.w.c0.w, 0, 0);
+      dq.prepare(q, g1 ? s1 : 0.0f, p.book, g1);
+    }
+    wb[2] = dq.piece(0);
+    wb[3] = dq.piece(P1);
+  };
+  auto store = [&](const Slot& sl, uint16_t* st, uint4* wb) {
     *reinterpret_cast<uint4*>(st + arow * SA + acol) = sl.a0;
     if constexpr (MBK == 2) *reinterpret_cast<uint4*>(st + (arow + 32) * SA + acol) = sl.a1;
+    if (dload) *reinterpret_cast<uint4*>(st + A_EL + B_EL + drow * (TRANS ? SL : SA) + dcol) = sl.d;
+    if constexpr (DIRECT) {
+      dequant_direct(sl, wb);
+      return;
+    }
     float scale;
     if constexpr (FP8) scale = tscale;
     else if constexpr (FMT == QL_FMT_Q4_0) scale = decode_scale_q40(sl.w.sraw >> sl.w.ssh);
@@ -122,14 +207,19 @@ void qsplit_kernel(Params p) {
     uint16_t* dst = st + A_EL + (TRANS ? wr * SBT : wr * SA) + wg * 32;
 #pragma unroll
     for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(dst + 8 * i) = dq.piece(i);
-    if (dload) *reinterpret_cast<uint4*>(st + A_EL + B_EL + drow * (TRANS ? SL : SA) + dcol) = sl.d;
   };
   // every slot starts defined (the prologue may leave some unused)
 #pragma unroll
   for (int u = 0; u < D; ++u) {
     ring[u].a0 = ring[u].a1 = ring[u].d = ring[u].w.c0 = ring[u].w.c1 = make_uint4(0, 0, 0, 0);
     ring[u].w.sraw = ring[u].w.ssh = 0;
+    ring[u].kt = 0;
   }
+  uint4 wbuf[2][4];                                  // direct forward: B operands of two steps
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wbuf[b][i] = make_uint4(0, 0, 0, 0);
 
   f32x16 acc[MBK];
 #pragma unroll
@@ -140,30 +230,32 @@ void qsplit_kernel(Params p) {
 #pragma unroll
   for (int jb = 0; jb < RB; ++jb) uacc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const uint16_t* st) {
+  auto compute = [&](const uint16_t* st, const uint4* wb) {
     const uint16_t* As = st;
     const uint16_t* Bs = st + A_EL;
     const uint16_t* Ds = st + A_EL + B_EL;
 #pragma unroll
     for (int ks = 0; ks < TK / 16; ++ks) {
       bf16x8 af[MBK], bf;
+      const int koff = (!DIRECT || HALVES) ? ks * 16 + 8 * (lane >> 5)
+                                           : 32 * (ks >> 1) + 16 * (lane >> 5) + 8 * (ks & 1);
 #pragma unroll
       for (int i = 0; i < MBK; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(As + (32 * i + (lane & 31)) * SA + ks * 16 + 8 * (lane >> 5));
-      if constexpr (TRANS) {
+        af[i] = *reinterpret_cast<const bf16x8*>(As + (32 * i + (lane & 31)) * SA + koff);
+      if constexpr (DIRECT) {
+        bf = __builtin_bit_cast(bf16x8, wb[ks]);
+      } else {
         const int b = lane >> 4, sl = lane & 15;
         const int col = 32 * wave + 16 * (b & 1) + 4 * (sl & 3);
         const int row = ks * 16 + 8 * (b >> 1) + (sl >> 2);
         bf = tr16x8(Bs + row * SBT + col, Bs + (row + 4) * SBT + col);
-      } else {
-        bf = *reinterpret_cast<const bf16x8*>(Bs + (32 * wave + (lane & 31)) * SA + ks * 16 + 8 * (lane >> 5));
       }
 #pragma unroll
       for (int i = 0; i < MBK; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af[i], acc[i], 0, 0, 0);
     }
     // rank-r projection of rows 16 wave .. 16 wave + 15 over this stage (waves
-    // whose rows lie past the tile have none)
-    if (16 * wave >= TM) return;
+    // whose rows lie past the tile have none; only column tile 0 keeps it)
+    if (!rank_tile || 16 * wave >= TM) return;
 #pragma unroll
     for (int kp = 0; kp < 2; ++kp) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(As + (16 * wave + (lane & 15)) * SA + 32 * kp + 8 * (lane >> 4));
@@ -190,7 +282,7 @@ void qsplit_kernel(Params p) {
 #pragma unroll
   for (int u = 0; u < D; ++u) issue(ring[u], kbeg + u);
   lds_barrier();
-  store(ring[0], smem);
+  store(ring[0], smem, wbuf[0]);
   issue(ring[0], kbeg + D);
   lds_barrier();
 
@@ -202,9 +294,9 @@ void qsplit_kernel(Params p) {
   for (; it + D < NKT; it += D) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
-      store(ring[(u + 1) % D], smem + ((u + 1) & 1) * STAGE);
+      store(ring[(u + 1) % D], smem + ((u + 1) & 1) * STAGE, wbuf[(u + 1) & 1]);
       issue(ring[(u + 1) % D], kbeg + it + u + 1 + D);
-      compute(smem + (u & 1) * STAGE);
+      compute(smem + (u & 1) * STAGE, wbuf[u & 1]);
       lds_barrier();
     }
   }
@@ -212,8 +304,8 @@ void qsplit_kernel(Params p) {
 #pragma unroll
   for (int u = 0; u < D; ++u) {
     if (it + u < NKT) {
-      if (it + u + 1 < NKT) store(ring[(u + 1) % D], smem + ((u + 1) & 1) * STAGE);
-      compute(smem + (u & 1) * STAGE);
+      if (it + u + 1 < NKT) store(ring[(u + 1) % D], smem + ((u + 1) & 1) * STAGE, wbuf[(u + 1) & 1]);
+      compute(smem + (u & 1) * STAGE, wbuf[u & 1]);
       lds_barrier();
     }
   }
@@ -249,7 +341,7 @@ void qsplit_kernel(Params p) {
 
 template <int FMT, bool TRANS, int R, int MBK>
 hipError_t launch_split_m(const Params& p, int splits, hipStream_t s) {
-  constexpr int B_EL = TRANS ? TK * (128 + 32) : 128 * SA;
+  constexpr int B_EL = split_b_elems<TRANS>();
   constexpr int D_EL = TRANS ? BL_ELEMS : AD_ELEMS;
   constexpr size_t smem = 2 * (size_t)(32 * MBK * SA + B_EL + D_EL) * sizeof(uint16_t);
   static_assert(smem <= 80 * 1024, "two workgroups per CU");

@@ -1,0 +1,66 @@
+"""Launch plans (ql_plan_*): a recorded sequence of forward / backward calls,
+enqueued by one library call, gives bitwise the results of the same calls
+issued one by one (same kernels, same launch configuration), run after run."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import helpers as H
+from oracle import formats as ofmt
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # fmt, m, k, n, r: split path with fused gradients, split path, 128x128 tiles, fp8 matrix cores
+    (ofmt.FMT_NF4, 16, 512, 384, 16),
+    (ofmt.FMT_MXFP4, 64, 1024, 256, 8),
+    (ofmt.FMT_Q4_0, 200, 256, 320, 32),
+    (ofmt.FMT_FP8, 130, 256, 224, 16),
+]
+
+
+def test_plan_matches_direct_calls(lib):
+    from quantized_base_lora_amd import binding as B
+    alpha = 32.0
+    items = []
+    for i, (fmt, m, k, n, r) in enumerate(CASES):
+        print(f"plan case fmt={fmt} m={m} k={k} n={n} r={r}", flush=True)
+        c = H.make_case(m, k, n, r, seed=60 + i)
+        qw = B.quant_pack(fmt, torch.from_numpy(c["W"]).cuda())
+        t = {key: H.bits_to_bf16_tensor(c[key]) for key in ("x", "dY", "A", "B")}
+        y, u = B.linear_fwd(qw, t["x"], t["A"], t["B"], alpha)
+        dx, da, db = B.linear_bwd(qw, t["x"], t["dY"], u, t["A"], t["B"], alpha)
+        out = {"y": torch.empty_like(y), "u": torch.empty_like(u), "dx": torch.empty_like(dx),
+               "da": torch.empty_like(da), "db": torch.empty_like(db),
+               "wsf": torch.empty(max(256, B.workspace_bytes(B.OP_FWD, fmt, n, k, m, r)), dtype=torch.uint8,
+                                  device="cuda"),
+               "wsb": torch.empty(max(256, B.workspace_bytes(B.OP_BWD, fmt, n, k, m, r)), dtype=torch.uint8,
+                                  device="cuda")}
+        items.append((qw, t, {"y": y, "u": u, "dx": dx, "da": da, "db": db}, out))
+    torch.cuda.synchronize()
+    pl = B.Plan()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pl.add_event(e0, stream)
+    for qw, t, _, o in items:
+        pl.add_fwd(qw, t["x"], t["A"], t["B"], alpha, o["y"], o["u"], o["wsf"])
+    for qw, t, _, o in reversed(items):
+        pl.add_bwd(qw, t["x"], t["dY"], o["u"], t["A"], t["B"], alpha, o["dx"], o["da"], o["db"], o["wsb"])
+    pl.add_event(e1, stream)
+    assert len(pl) == 2 * len(items) + 2
+    for run in range(3):
+        for _, _, _, o in items:
+            for key in ("y", "u", "dx", "da", "db"):
+                o[key].fill_(float("nan"))
+        pl.run()
+        torch.cuda.synchronize()
+        assert e0.elapsed_time(e1) > 0
+        for j, (_, _, ref, o) in enumerate(items):
+            for key in ("y", "u", "dx", "da", "db"):
+                a, b = o[key], ref[key]
+                iv = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+                assert torch.equal(a.view(iv), b.view(iv)), (run, j, key)
+    pl.close()

@@ -134,3 +134,30 @@ def test_adamw_argument_errors(lib):
         for k, v in kw.items():
             setattr(t, k, v)
         assert step((T * 1)(t), 1, ctypes.byref(hp), None) == binding.QL_EINVAL, kw
+
+
+def test_plan_argument_errors(lib):
+    P = FAKE
+    qw = _qw()
+    h = ctypes.c_void_p()
+    assert lib.ql_plan_create(None) == binding.QL_EINVAL
+    assert lib.ql_plan_create(ctypes.byref(h)) == binding.QL_OK
+    try:
+        add_f, add_b = lib.ql_plan_add_fwd, lib.ql_plan_add_bwd
+        # the same checks as the direct calls, and nothing recorded on error
+        assert add_f(h, ctypes.byref(qw), P, 16, P, P, 12, 16.0, P, P, None, 0) == binding.QL_EUNSUPPORTED
+        assert add_f(h, ctypes.byref(qw), None, 16, P, P, 16, 16.0, P, P, None, 0) == binding.QL_EINVAL
+        assert add_b(h, ctypes.byref(qw), P, P, P, 1024, P, P, 16, 16.0, P, P, P, 0, P, 0) == binding.QL_EWORKSPACE
+        assert lib.ql_plan_size(h) == 0
+        assert add_f(None, ctypes.byref(qw), P, 16, P, P, 16, 16.0, P, P, None, 0) == binding.QL_EINVAL
+        assert lib.ql_plan_add_event(h, None) == binding.QL_EINVAL
+        # valid calls are recorded (nothing is launched until run)
+        assert add_f(h, ctypes.byref(qw), P, 0, P, P, 16, 16.0, P, P, None, 0) == binding.QL_OK
+        ws = binding.workspace_bytes(binding.OP_BWD, qw.format, qw.n_out, qw.k_in, 16, 16)
+        assert add_b(h, ctypes.byref(qw), P, P, P, 16, P, P, 16, 16.0, P, P, P, 0, P, ws) == binding.QL_OK
+        assert lib.ql_plan_add_event(h, ctypes.c_void_p(0x1234)) == binding.QL_OK
+        assert lib.ql_plan_size(h) == 3
+        assert lib.ql_plan_run(None, None) == binding.QL_EINVAL
+    finally:
+        assert lib.ql_plan_destroy(h) == binding.QL_OK
+    assert lib.ql_plan_size(None) == 0
