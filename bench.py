@@ -424,16 +424,19 @@ def main():
     use_plan = not (args.no_plan or args.streams or args.graph)
     if use_plan:
         def record(pl, i, timed):
+            # timed: one event pair around the step's forward launches, back to back
+            # (an event around every launch adds its own pipeline drain to each)
             evs = []
-            for d in (projs if args.phase != "bwd" else []):
-                if timed:
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    pl.add_event(e0, stream)
+            fwd_projs = projs if args.phase != "bwd" else []
+            if timed and fwd_projs:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                pl.add_event(e0, stream)
+            for d in fwd_projs:
                 pl.add_fwd(d["qws"][i], d["x"], d["a"], d["b"], wl.alpha, d["y"], d["u"], d["wsf"])
-                if timed:
-                    pl.add_event(e1, stream)
-                    evs.append((d["p"], e0, e1))
+            if timed and fwd_projs:
+                pl.add_event(e1, stream)
+                evs.append(([d["p"] for d in fwd_projs], e0, e1))
             for d in (reversed(projs) if args.phase != "fwd" else []):
                 pl.add_bwd(d["qws"][i], d["x"], d["dy"], d["u"], d["a"], d["b"], wl.alpha, d["dx"], d["da"],
                            d["db"], d["ws"])
@@ -453,7 +456,7 @@ def main():
             tp, evs = timing_plans[i % copies]
             tp.run(stream)
             torch.cuda.synchronize()
-            ev_pairs.extend((pp, e0.elapsed_time(e1)) for pp, e0, e1 in evs)
+            ev_pairs.extend((pp, e0.elapsed_time(e1)) for pp, e0, e1 in evs)   # ([projections], ms)
     else:
         # the roofline's kernel timing: eager launches on one stream
         for i in range(args.warmup):
@@ -462,7 +465,7 @@ def main():
         for i in range(args.steps):
             eager_step(i, True)
         torch.cuda.synchronize()
-        ev_pairs[:] = [(pp, e0.elapsed_time(e1)) for pp, e0, e1 in ev_pairs]
+        ev_pairs[:] = [([pp], e0.elapsed_time(e1)) for pp, e0, e1 in ev_pairs]
 
     # the step itself: HIP-graph replays (one graph per rotated weight copy) or eager launches
     graphs = []
@@ -498,8 +501,8 @@ def main():
     ms = start.elapsed_time(end) / args.steps
 
     fwd_ms = sum(t for _, t in ev_pairs)
-    fwd_flops = sum(fwd_kernel_flops(wl, p, m) for p, _ in ev_pairs)
-    n_launch = max(1, len(ev_pairs))
+    fwd_flops = sum(fwd_kernel_flops(wl, p, m) for ps, _ in ev_pairs for p in ps)
+    n_launch = max(1, sum(len(ps) for ps, _ in ev_pairs))
     fwd_ms = fwd_ms or float("nan")
     avg_launch_ms = fwd_ms / n_launch
     achieved = fwd_flops / (fwd_ms / 1e3) / 1e12
@@ -534,10 +537,13 @@ def main():
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "avg_launch_us": avg_launch_ms * 1e3, "launches_timed": n_launch,
+                     "timing": ("HIP events around each step's forward launches (enqueued back to back "
+                                "by one launch plan), total / launches" if use_plan else
+                                "HIP events around each forward call"),
                      "flops_per_launch_avg": fwd_flops / n_launch},
     }
     if m <= 64:
-        fwd_bytes = sum(BPW[wl.fmt] * p.n * p.k + m * 2 * (p.k + p.n) for p, _ in ev_pairs) / n_launch
+        fwd_bytes = sum(BPW[wl.fmt] * p.n * p.k + m * 2 * (p.k + p.n) for ps, _ in ev_pairs for p in ps) / n_launch
         gbs = fwd_bytes / (avg_launch_ms / 1e3) / 1e9
         out["roofline"].update({"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": gbs / PEAK_HBM_GBS, "bytes_per_launch_avg": fwd_bytes})
