@@ -432,14 +432,16 @@ def main():
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 pl.add_event(e0, stream)
-            for d in fwd_projs:
-                pl.add_fwd(d["qws"][i], d["x"], d["a"], d["b"], wl.alpha, d["y"], d["u"], d["wsf"])
+            # calls grouped as a decoder layer allows: q|k|v and gate|up read one input
+            for g in (groups if fwd_projs else []):
+                pl.add_fwd_group([(d["qws"][i], d["x"], d["a"], d["b"], wl.alpha, d["y"], d["u"], d["wsf"])
+                                  for d in g])
             if timed and fwd_projs:
                 pl.add_event(e1, stream)
                 evs.append(([d["p"] for d in fwd_projs], e0, e1))
-            for d in (reversed(projs) if args.phase != "fwd" else []):
-                pl.add_bwd(d["qws"][i], d["x"], d["dy"], d["u"], d["a"], d["b"], wl.alpha, d["dx"], d["da"],
-                           d["db"], d["ws"])
+            for g in (reversed(groups) if args.phase != "fwd" else []):
+                pl.add_bwd_group([(d["qws"][i], d["x"], d["dy"], d["u"], d["a"], d["b"], wl.alpha, d["dx"],
+                                   d["da"], d["db"], d["ws"], False) for d in reversed(g)])
             return evs
         step_plans, timing_plans = [], []
         for i in range(copies):
@@ -527,7 +529,8 @@ def main():
                    "rank": wl.r, "alpha": wl.alpha, "projections": [f"{p.name}:{p.k}->{p.n}" for p in wl.projs],
                    "packed_copies_rotated": copies,
                    "step_mode": ("HIP graph replay" if args.graph else
-                                 "eager launches, one library call per step (recorded launch plan)" if use_plan
+                                 "eager launches, one library call per step (recorded launch plan; "
+                                 "q|k|v and gate|up as grouped calls)" if use_plan
                                  else "eager launches, one library call per layer call") + (
                        ", q|k|v and gate|up on parallel streams" if args.streams else ", one stream")},
         "layer": {"tflops": flops / (ms / 1e3) / 1e12, "frac_bf16_peak": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,

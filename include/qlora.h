@@ -184,6 +184,58 @@ int qlora_linear_bwd(const ql_qweight* w, const uint16_t* x, const uint16_t* dy,
                      uint16_t* dx, float* d_a, float* d_b, int32_t accumulate,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- groups of independent calls
+ * Several independent forward (or backward) calls that share the base
+ * format, the token count m and the rank r, in one call: equivalent to
+ * calling qlora_linear_fwd (qlora_linear_bwd) for each in order, with bitwise
+ * the same results.  At most 64 tokens (the split-contraction path) the
+ * group's base GEMMs run as one split launch and one reduction launch instead
+ * of two launches per call; otherwise the calls are launched one by one.  In
+ * a decoder layer the q, k and v projections (and gate and up) read the same
+ * input and form such a group.
+ *
+ * calls: host array of n (1 .. QL_GROUP_MAX) descriptors with the arguments
+ * of the single calls (pointers and ownership as there).  Every call is
+ * validated as its single call would be (same error codes); in addition all
+ * must use one base format (QL_EINVAL otherwise), and no buffer a call writes
+ * (y, u_save, ws; dx, d_a, d_b, ws) may overlap any buffer of another call of
+ * the group (QL_EINVAL). */
+#define QL_GROUP_MAX 8
+
+typedef struct ql_fwd_call {
+  const ql_qweight* w;     /* host pointer to the weight descriptor         */
+  const uint16_t* x;       /* dev bf16 [m, K]                                */
+  const uint16_t* lora_a;  /* dev bf16 [r, K]                                */
+  const uint16_t* lora_b;  /* dev bf16 [N, r]                                */
+  float alpha;
+  int32_t reserved;        /* must be 0                                      */
+  uint16_t* y;             /* dev bf16 [m, N]                                */
+  float* u_save;           /* dev fp32 [m, r]                                */
+  void* ws;                /* dev scratch, qlora_workspace_bytes(QL_OP_FWD)  */
+  size_t ws_bytes;
+} ql_fwd_call;
+
+typedef struct ql_bwd_call {
+  const ql_qweight* w;
+  const uint16_t* x;       /* dev bf16 [m, K]                                */
+  const uint16_t* dy;      /* dev bf16 [m, N]                                */
+  const float* u_save;     /* dev fp32 [m, r]                                */
+  const uint16_t* lora_a;
+  const uint16_t* lora_b;
+  float alpha;
+  int32_t accumulate;      /* 0 overwrite d_a / d_b, 1 add into them         */
+  uint16_t* dx;            /* dev bf16 [m, K] or NULL                        */
+  float* d_a;              /* dev fp32 [r, K]                                */
+  float* d_b;              /* dev fp32 [N, r]                                */
+  void* ws;                /* dev scratch, qlora_workspace_bytes(QL_OP_BWD)  */
+  size_t ws_bytes;
+} ql_bwd_call;
+
+int qlora_linear_fwd_group(const ql_fwd_call* calls, int32_t n, int64_t m,
+                           int32_t r, void* stream);
+int qlora_linear_bwd_group(const ql_bwd_call* calls, int32_t n, int64_t m,
+                           int32_t r, void* stream);
+
 /* ---------------------------------------------------------------- launch plans
  * A plan records a fixed sequence of forward and backward calls (and event
  * markers) once; ql_plan_run then enqueues the whole sequence on a stream in
@@ -216,6 +268,11 @@ int ql_plan_add_bwd(ql_plan* plan, const ql_qweight* w, const uint16_t* x,
                     const uint16_t* lora_a, const uint16_t* lora_b, int32_t r,
                     float alpha, uint16_t* dx, float* d_a, float* d_b,
                     int32_t accumulate, void* ws, size_t ws_bytes);
+/* a group of independent calls (as qlora_linear_fwd_group / _bwd_group) */
+int ql_plan_add_fwd_group(ql_plan* plan, const ql_fwd_call* calls, int32_t n,
+                          int64_t m, int32_t r);
+int ql_plan_add_bwd_group(ql_plan* plan, const ql_bwd_call* calls, int32_t n,
+                          int64_t m, int32_t r);
 int ql_plan_add_event(ql_plan* plan, void* event);
 /* number of recorded steps (0 for NULL) */
 int ql_plan_size(const ql_plan* plan);

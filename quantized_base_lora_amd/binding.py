@@ -26,8 +26,10 @@ EXPORTS = (
     "ql_pool_create", "layer_stream_prefetch", "ql_pool_acquire", "ql_pool_release",
     "ql_pool_stats", "ql_pool_debug", "ql_pool_destroy", "ql_adamw_step",
     "ql_plan_create", "ql_plan_add_fwd", "ql_plan_add_bwd", "ql_plan_add_event", "ql_plan_size",
-    "ql_plan_run", "ql_plan_destroy",
+    "ql_plan_run", "ql_plan_destroy", "qlora_linear_fwd_group", "qlora_linear_bwd_group",
+    "ql_plan_add_fwd_group", "ql_plan_add_bwd_group",
 )
+GROUP_MAX = 8
 ADAMW_MAX_TENSORS = 32
 
 
@@ -41,6 +43,21 @@ class QWeightC(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("n_out", ctypes.c_int64), ("k_in", ctypes.c_int64),
                 ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class FwdCallC(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("x", ctypes.c_void_p), ("lora_a", ctypes.c_void_p),
+                ("lora_b", ctypes.c_void_p), ("alpha", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("y", ctypes.c_void_p), ("u_save", ctypes.c_void_p), ("ws", ctypes.c_void_p),
+                ("ws_bytes", ctypes.c_size_t)]
+
+
+class BwdCallC(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("x", ctypes.c_void_p), ("dy", ctypes.c_void_p),
+                ("u_save", ctypes.c_void_p), ("lora_a", ctypes.c_void_p), ("lora_b", ctypes.c_void_p),
+                ("alpha", ctypes.c_float), ("accumulate", ctypes.c_int32), ("dx", ctypes.c_void_p),
+                ("d_a", ctypes.c_void_p), ("d_b", ctypes.c_void_p), ("ws", ctypes.c_void_p),
+                ("ws_bytes", ctypes.c_size_t)]
 
 
 class AdamwTensorC(ctypes.Structure):
@@ -94,6 +111,10 @@ def load(path=LIB_PATH):
         "ql_plan_size": (ctypes.c_int, [P]),
         "ql_plan_run": (ctypes.c_int, [P, P]),
         "ql_plan_destroy": (ctypes.c_int, [P]),
+        "qlora_linear_fwd_group": (ctypes.c_int, [ctypes.POINTER(FwdCallC), I32, I64, I32, P]),
+        "qlora_linear_bwd_group": (ctypes.c_int, [ctypes.POINTER(BwdCallC), I32, I64, I32, P]),
+        "ql_plan_add_fwd_group": (ctypes.c_int, [P, ctypes.POINTER(FwdCallC), I32, I64, I32]),
+        "ql_plan_add_bwd_group": (ctypes.c_int, [P, ctypes.POINTER(BwdCallC), I32, I64, I32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -265,6 +286,52 @@ def linear_bwd(qw, x, dy, u, a, b, alpha, need_dx=True, accumulate=False, dx=Non
     return (dx if need_dx else None), da, db
 
 
+def _fwd_calls(items):
+    """items: (qw, x, a, b, alpha, y, u, ws) tuples -> (ctypes array, m, r)."""
+    arr = (FwdCallC * len(items))()
+    m, r = items[0][1].shape[0], items[0][2].shape[0]
+    for i, (qw, x, a, b, alpha, y, u, ws) in enumerate(items):
+        _need(x, "x", torch.bfloat16, (m, qw.k))
+        _need(a, "A", torch.bfloat16, (r, qw.k))
+        _need(b, "B", torch.bfloat16, (qw.n, r))
+        _need(y, "y", torch.bfloat16, (m, qw.n))
+        _need(u, "U", torch.float32, (m, r))
+        arr[i] = FwdCallC(ctypes.addressof(qw._c), x.data_ptr(), a.data_ptr(), b.data_ptr(), float(alpha), 0,
+                          y.data_ptr(), u.data_ptr(), ws.data_ptr() if ws is not None else None,
+                          ws.numel() if ws is not None else 0)
+    return arr, m, r
+
+
+def _bwd_calls(items):
+    """items: (qw, x, dy, u, a, b, alpha, dx, da, db, ws, accumulate) tuples."""
+    arr = (BwdCallC * len(items))()
+    m, r = items[0][1].shape[0], items[0][4].shape[0]
+    for i, (qw, x, dy, u, a, b, alpha, dx, da, db, ws, acc) in enumerate(items):
+        _need(x, "x", torch.bfloat16, (m, qw.k))
+        _need(dy, "dY", torch.bfloat16, (m, qw.n))
+        _need(u, "U", torch.float32, (m, r))
+        _need(da, "dA", torch.float32, (r, qw.k))
+        _need(db, "dB", torch.float32, (qw.n, r))
+        if dx is not None:
+            _need(dx, "dX", torch.bfloat16, (m, qw.k))
+        arr[i] = BwdCallC(ctypes.addressof(qw._c), x.data_ptr(), dy.data_ptr(), u.data_ptr(), a.data_ptr(),
+                          b.data_ptr(), float(alpha), 1 if acc else 0, dx.data_ptr() if dx is not None else None,
+                          da.data_ptr(), db.data_ptr(), ws.data_ptr(), ws.numel())
+    return arr, m, r
+
+
+def linear_fwd_group(items, stream=None):
+    """Independent forward calls of one format, token count and rank in one
+    library call (one split launch and one reduction for all at <= 64 tokens)."""
+    arr, m, r = _fwd_calls(items)
+    _check(load().qlora_linear_fwd_group(arr, len(items), m, r, _stream(stream)))
+
+
+def linear_bwd_group(items, stream=None):
+    arr, m, r = _bwd_calls(items)
+    _check(load().qlora_linear_bwd_group(arr, len(items), m, r, _stream(stream)))
+
+
 class Plan:
     """A recorded sequence of forward / backward calls (and event markers),
     enqueued by run() in one library call.  Outputs and workspaces must be
@@ -300,6 +367,16 @@ class Plan:
                                       float(alpha), _ptr(dx), _ptr(da), _ptr(db), 1 if accumulate else 0,
                                       _ptr(ws), ws.numel()))
         self._keep += [qw, x, dy, u, a, b, dx, da, db, ws]
+
+    def add_fwd_group(self, items):
+        arr, m, r = _fwd_calls(items)
+        _check(load().ql_plan_add_fwd_group(self._h, arr, len(items), m, r))
+        self._keep += [t for it in items for t in it if isinstance(t, (torch.Tensor, QWeight))]
+
+    def add_bwd_group(self, items):
+        arr, m, r = _bwd_calls(items)
+        _check(load().ql_plan_add_bwd_group(self._h, arr, len(items), m, r))
+        self._keep += [t for it in items for t in it if isinstance(t, (torch.Tensor, QWeight))]
 
     def add_event(self, event, stream=None):
         """Record `event` (a torch.cuda.Event) at this point of every run; the

@@ -127,8 +127,7 @@ int check_fwd(const ql_qweight* wp, const FwdArgs& a) {
   return QL_OK;
 }
 
-int enqueue_fwd(const FwdArgs& a, hipStream_t s) {
-  if (a.m == 0) return QL_OK;
+GemmCall fwd_gemm(const FwdArgs& a) {
   GemmCall c{};
   c.w = &a.w;
   c.trans = false;
@@ -141,7 +140,12 @@ int enqueue_fwd(const FwdArgs& a, hipStream_t s) {
   c.out = a.y;
   c.save = a.u;
   c.ws = a.ws;
-  hipError_t e = launch_qgemm(c, s);
+  return c;
+}
+
+int enqueue_fwd(const FwdArgs& a, hipStream_t s) {
+  if (a.m == 0) return QL_OK;
+  hipError_t e = launch_qgemm(fwd_gemm(a), s);
   if (e != hipSuccess) return hip_error(e, "forward launch");
   return QL_OK;
 }
@@ -161,65 +165,206 @@ int check_bwd(const ql_qweight* wp, const BwdArgs& a) {
   return QL_OK;
 }
 
-int enqueue_bwd(const BwdArgs& a, hipStream_t s) {
+// The pieces of a backward call: the dX GEMM (with V and, at most 32 tokens,
+// dA and dB fused into its reduction) and the separate adapter-gradient
+// launch otherwise.
+struct BwdParts {
+  BwdLayout L;
+  float *v, *pa, *pb;
+  bool fuse;
+  GradFuse gf;
+  GemmCall gemm;
+};
+
+void bwd_parts(const BwdArgs& a, BwdParts& b) {
   const int64_t n = a.w.n_out, k = a.w.k_in, m = a.m;
-  const BwdLayout L = bwd_layout(a.w.format, n, k, m, a.r);
+  b.L = bwd_layout(a.w.format, n, k, m, a.r);
   char* base = reinterpret_cast<char*>(a.ws);
-  float* v = reinterpret_cast<float*>(base + L.v);
-  float* pa = reinterpret_cast<float*>(base + L.pa);
-  float* pb = reinterpret_cast<float*>(base + L.pb);
-  const float sc = a.alpha / (float)a.r;
+  b.v = reinterpret_cast<float*>(base + b.L.v);
+  b.pa = reinterpret_cast<float*>(base + b.L.pa);
+  b.pb = reinterpret_cast<float*>(base + b.L.pb);
+  b.fuse = m > 0 && a.dx && split_path_fuses_grads(m);
+  b.gf = GradFuse{a.x, a.u, a.da, a.db, a.accumulate != 0};
+  b.gemm = GemmCall{};
+  GemmCall& c = b.gemm;
+  c.w = &a.w;
+  c.trans = true;
+  c.act = a.dy;
+  c.m = m;
+  c.down = a.b;
+  c.up = a.a;
+  c.r = a.r;
+  c.s = a.alpha / (float)a.r;
+  c.out = a.dx;
+  c.save = b.v;
+  c.ws = base + b.L.g;
+  c.grads = b.fuse ? &b.gf : nullptr;
+}
+
+hipError_t bwd_grads(const BwdArgs& a, const BwdParts& b, hipStream_t s) {
+  if (b.fuse) return hipSuccess;
+  GradLaunch g{};
+  g.x = a.x;
+  g.dy = a.dy;
+  g.v = b.v;
+  g.u = a.u;
+  g.d_a = a.da;
+  g.d_b = a.db;
+  g.part_a = b.pa;
+  g.part_b = b.pb;
+  g.m = a.m;
+  g.k = a.w.k_in;
+  g.n = a.w.n_out;
+  g.r = a.r;
+  g.nparts = b.L.parts;
+  g.s = a.alpha / (float)a.r;
+  g.accumulate = a.accumulate != 0;
+  return launch_grads(g, s);
+}
+
+int enqueue_bwd(const BwdArgs& a, hipStream_t s) {
+  BwdParts b;
+  bwd_parts(a, b);
   hipError_t e = hipSuccess;
-  // at most 32 tokens the dX reduction launch also writes dA and dB
-  const bool fuse = m > 0 && a.dx && split_path_fuses_grads(m);
-  GradFuse gf{a.x, a.u, a.da, a.db, a.accumulate != 0};
-  if (m > 0 && a.dx) {
-    GemmCall c{};
-    c.w = &a.w;
-    c.trans = true;
-    c.act = a.dy;
-    c.m = m;
-    c.down = a.b;
-    c.up = a.a;
-    c.r = a.r;
-    c.s = sc;
-    c.out = a.dx;
-    c.save = v;
-    c.ws = base + L.g;
-    c.grads = fuse ? &gf : nullptr;
-    e = launch_qgemm(c, s);
-  } else if (m > 0) {
-    e = launch_down_proj(a.dy, m, n, a.b, a.r, v, s);
-  }
-  if (e == hipSuccess && !fuse) {
-    GradLaunch g{};
-    g.x = a.x;
-    g.dy = a.dy;
-    g.v = v;
-    g.u = a.u;
-    g.d_a = a.da;
-    g.d_b = a.db;
-    g.part_a = pa;
-    g.part_b = pb;
-    g.m = m;
-    g.k = k;
-    g.n = n;
-    g.r = a.r;
-    g.nparts = L.parts;
-    g.s = sc;
-    g.accumulate = a.accumulate != 0;
-    e = launch_grads(g, s);
-  }
+  if (a.m > 0 && a.dx) e = launch_qgemm(b.gemm, s);
+  else if (a.m > 0) e = launch_down_proj(a.dy, a.m, a.w.n_out, a.b, a.r, b.v, s);
+  if (e == hipSuccess) e = bwd_grads(a, b, s);
   if (e != hipSuccess) return hip_error(e, "backward launch");
   return QL_OK;
 }
 
+// ---- groups of independent calls (one token count and rank)
+bool overlaps(const void* p, size_t pn, const void* q, size_t qn) {
+  if (!p || !q || !pn || !qn) return false;
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + qn && b < a + pn;
+}
+
+struct Span {
+  const void* p;
+  size_t n;
+};
+
+// every buffer a call reads or writes, and which of them it writes
+void fwd_spans(const FwdArgs& a, Span* all, int& na, Span* out, int& no) {
+  const int64_t m = a.m, k = a.w.k_in, n = a.w.n_out, r = a.r;
+  na = no = 0;
+  all[na++] = {a.x, (size_t)(m * k * 2)};
+  all[na++] = {a.a, (size_t)(r * k * 2)};
+  all[na++] = {a.b, (size_t)(n * r * 2)};
+  out[no++] = all[na++] = {a.y, (size_t)(m * n * 2)};
+  out[no++] = all[na++] = {a.u, (size_t)(m * r * 4)};
+  out[no++] = all[na++] = {a.ws, a.ws_bytes};
+}
+void bwd_spans(const BwdArgs& a, Span* all, int& na, Span* out, int& no) {
+  const int64_t m = a.m, k = a.w.k_in, n = a.w.n_out, r = a.r;
+  na = no = 0;
+  all[na++] = {a.x, (size_t)(m * k * 2)};
+  all[na++] = {a.dy, (size_t)(m * n * 2)};
+  all[na++] = {a.u, (size_t)(m * r * 4)};
+  all[na++] = {a.a, (size_t)(r * k * 2)};
+  all[na++] = {a.b, (size_t)(n * r * 2)};
+  out[no++] = all[na++] = {a.dx, a.dx ? (size_t)(m * k * 2) : 0};
+  out[no++] = all[na++] = {a.da, (size_t)(r * k * 4)};
+  out[no++] = all[na++] = {a.db, (size_t)(n * r * 4)};
+  out[no++] = all[na++] = {a.ws, a.ws_bytes};
+}
+
+template <class Args, class SpanFn>
+int check_independent(const Args* a, int n, SpanFn spans) {
+  for (int i = 0; i < n; ++i) {
+    Span ai[10], ao[6];
+    int nai, nao;
+    spans(a[i], ai, nai, ao, nao);
+    for (int j = 0; j < n; ++j) {
+      if (j == i) continue;
+      Span bj[10], bo[6];
+      int nbj, nbo;
+      spans(a[j], bj, nbj, bo, nbo);
+      for (int x = 0; x < nao; ++x)
+        for (int y = 0; y < nbj; ++y)
+          if (overlaps(ao[x].p, ao[x].n, bj[y].p, bj[y].n))
+            return set_error(QL_EINVAL, "group calls %d and %d are not independent (an output of %d overlaps a buffer of %d)",
+                             i, j, i, j);
+    }
+  }
+  return QL_OK;
+}
+
+int enqueue_fwd_group(const FwdArgs* a, int n, hipStream_t s) {
+  if (n <= 0 || a[0].m == 0) return QL_OK;
+  GemmCall c[QL_GROUP_MAX];
+  for (int i = 0; i < n; ++i) c[i] = fwd_gemm(a[i]);
+  hipError_t e = launch_qgemm_group(c, n, s);
+  if (e != hipSuccess) return hip_error(e, "grouped forward launch");
+  return QL_OK;
+}
+
+int enqueue_bwd_group(const BwdArgs* a, int n, hipStream_t s) {
+  bool all_dx = true;
+  for (int i = 0; i < n; ++i) all_dx = all_dx && a[i].dx;
+  if (n <= 1 || a[0].m == 0 || !all_dx) {
+    for (int i = 0; i < n; ++i) {
+      int rc = enqueue_bwd(a[i], s);
+      if (rc) return rc;
+    }
+    return QL_OK;
+  }
+  BwdParts b[QL_GROUP_MAX];
+  GemmCall c[QL_GROUP_MAX];
+  for (int i = 0; i < n; ++i) {
+    bwd_parts(a[i], b[i]);
+    c[i] = b[i].gemm;
+  }
+  hipError_t e = launch_qgemm_group(c, n, s);
+  for (int i = 0; i < n && e == hipSuccess; ++i) e = bwd_grads(a[i], b[i], s);
+  if (e != hipSuccess) return hip_error(e, "grouped backward launch");
+  return QL_OK;
+}
+
 struct PlanStep {
-  enum Kind { FWD, BWD, EVENT } kind;
+  enum Kind { FWD, BWD, EVENT, FWD_GROUP, BWD_GROUP } kind;
   FwdArgs fwd;
   BwdArgs bwd;
   hipEvent_t event;
+  std::vector<FwdArgs> fwds;
+  std::vector<BwdArgs> bwds;
 };
+
+FwdArgs fwd_args(const ql_fwd_call& c, int64_t m, int32_t r) {
+  return FwdArgs{c.w ? *c.w : ql_qweight{}, c.x, m, c.lora_a, c.lora_b, r, c.alpha, c.y, c.u_save, c.ws, c.ws_bytes};
+}
+BwdArgs bwd_args(const ql_bwd_call& c, int64_t m, int32_t r) {
+  return BwdArgs{c.w ? *c.w : ql_qweight{}, c.x, c.dy, c.u_save, m, c.lora_a, c.lora_b, r, c.alpha,
+                 c.dx, c.d_a, c.d_b, c.accumulate, c.ws, c.ws_bytes};
+}
+
+// validates a group: count, every call as a single call, one format, and independence
+int check_fwd_group(const ql_fwd_call* calls, int32_t n, int64_t m, int32_t r, std::vector<FwdArgs>& out) {
+  if (n < 1 || n > QL_GROUP_MAX) return set_error(QL_EINVAL, "group size %d outside [1, %d]", n, QL_GROUP_MAX);
+  if (!calls) return set_error(QL_EINVAL, "null calls");
+  out.clear();
+  for (int i = 0; i < n; ++i) {
+    if (calls[i].reserved != 0) return set_error(QL_EINVAL, "call %d: reserved must be 0", i);
+    out.push_back(fwd_args(calls[i], m, r));
+    int rc = check_fwd(calls[i].w, out.back());
+    if (rc) return rc;
+    if (out.back().w.format != out[0].w.format) return set_error(QL_EINVAL, "group mixes base formats");
+  }
+  return check_independent(out.data(), n, fwd_spans);
+}
+int check_bwd_group(const ql_bwd_call* calls, int32_t n, int64_t m, int32_t r, std::vector<BwdArgs>& out) {
+  if (n < 1 || n > QL_GROUP_MAX) return set_error(QL_EINVAL, "group size %d outside [1, %d]", n, QL_GROUP_MAX);
+  if (!calls) return set_error(QL_EINVAL, "null calls");
+  out.clear();
+  for (int i = 0; i < n; ++i) {
+    out.push_back(bwd_args(calls[i], m, r));
+    int rc = check_bwd(calls[i].w, out.back());
+    if (rc) return rc;
+    if (out.back().w.format != out[0].w.format) return set_error(QL_EINVAL, "group mixes base formats");
+  }
+  return check_independent(out.data(), n, bwd_spans);
+}
 
 }  // namespace
 }  // namespace ql
@@ -358,6 +503,22 @@ int qlora_linear_bwd(const ql_qweight* w, const uint16_t* x, const uint16_t* dy,
   return enqueue_bwd(a, as_stream(stream));
 }
 
+int qlora_linear_fwd_group(const ql_fwd_call* calls, int32_t n, int64_t m, int32_t r, void* stream) {
+  std::vector<FwdArgs> a;
+  int rc = check_fwd_group(calls, n, m, r, a);
+  if (rc || m == 0) return rc;
+  if ((rc = check_sticky())) return rc;
+  return enqueue_fwd_group(a.data(), n, as_stream(stream));
+}
+
+int qlora_linear_bwd_group(const ql_bwd_call* calls, int32_t n, int64_t m, int32_t r, void* stream) {
+  std::vector<BwdArgs> a;
+  int rc = check_bwd_group(calls, n, m, r, a);
+  if (rc) return rc;
+  if ((rc = check_sticky())) return rc;
+  return enqueue_bwd_group(a.data(), n, as_stream(stream));
+}
+
 // ---------------------------------------------------------------- launch plans
 int ql_plan_create(ql_plan** plan) {
   if (!plan) return set_error(QL_EINVAL, "null plan pointer");
@@ -396,6 +557,26 @@ int ql_plan_add_bwd(ql_plan* plan, const ql_qweight* w, const uint16_t* x, const
   return QL_OK;
 }
 
+int ql_plan_add_fwd_group(ql_plan* plan, const ql_fwd_call* calls, int32_t n, int64_t m, int32_t r) {
+  if (!plan) return set_error(QL_EINVAL, "null plan");
+  PlanStep st{};
+  st.kind = PlanStep::FWD_GROUP;
+  int rc = check_fwd_group(calls, n, m, r, st.fwds);
+  if (rc) return rc;
+  plan->steps.push_back(std::move(st));
+  return QL_OK;
+}
+
+int ql_plan_add_bwd_group(ql_plan* plan, const ql_bwd_call* calls, int32_t n, int64_t m, int32_t r) {
+  if (!plan) return set_error(QL_EINVAL, "null plan");
+  PlanStep st{};
+  st.kind = PlanStep::BWD_GROUP;
+  int rc = check_bwd_group(calls, n, m, r, st.bwds);
+  if (rc) return rc;
+  plan->steps.push_back(std::move(st));
+  return QL_OK;
+}
+
 int ql_plan_add_event(ql_plan* plan, void* event) {
   if (!plan || !event) return set_error(QL_EINVAL, "null plan or event");
   PlanStep st{};
@@ -416,6 +597,8 @@ int ql_plan_run(ql_plan* plan, void* stream) {
     switch (st.kind) {
       case PlanStep::FWD: rc = enqueue_fwd(st.fwd, s); break;
       case PlanStep::BWD: rc = enqueue_bwd(st.bwd, s); break;
+      case PlanStep::FWD_GROUP: rc = enqueue_fwd_group(st.fwds.data(), (int)st.fwds.size(), s); break;
+      case PlanStep::BWD_GROUP: rc = enqueue_bwd_group(st.bwds.data(), (int)st.bwds.size(), s); break;
       default: {
         hipError_t e = hipEventRecord(st.event, s);
         rc = e == hipSuccess ? QL_OK : hip_error(e, "plan event record");

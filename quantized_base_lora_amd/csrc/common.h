@@ -91,6 +91,12 @@ struct GemmCall {
   const GradFuse* grads;   // dX only, with split_path_fuses_grads(m): also write dA, dB (else null)
 };
 hipError_t launch_qgemm(const GemmCall& c, hipStream_t s);
+// independent calls of one format, direction, token count and rank on the
+// small-M split path: one split launch and one reduction launch for all of
+// them (bitwise the results of separate calls); other call sets are launched
+// one by one
+bool qgemm_groupable(const GemmCall* calls, int n);
+hipError_t launch_qgemm_group(const GemmCall* calls, int n, hipStream_t s);
 // scratch the GEMM needs: split-contraction partials when m is small; for the
 // FP8 base with more tokens, the activation split (hi, lo planes and row scales)
 size_t qgemm_workspace_bytes(int32_t fmt, bool trans, int64_t m, int64_t n, int64_t k, int32_t r);

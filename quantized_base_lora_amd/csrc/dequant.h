@@ -159,9 +159,19 @@ struct SplitPlan {
 };
 
 SplitPlan split_plan(bool trans, int64_t m, int64_t n, int64_t k, int r);
-// split kernel plus reduction, for the format, direction and rank of p; with
-// gf (dX only) the reduction also writes dA and dB
-hipError_t launch_split_path(int fmt, bool trans, int r, const Params& p, int splits, const GradFuse* gf,
-                             hipStream_t s);
+
+// A group of independent split-path problems of one format, direction, rank
+// and token count, run by one split launch and one reduction launch: each
+// problem keeps its own tiles, split plan and summation order, so its results
+// are bitwise those of a launch of its own.
+constexpr int MAX_GROUP = QL_GROUP_MAX;
+struct SplitGroup {
+  Params p[MAX_GROUP];
+  int32_t splits[MAX_GROUP];
+  int32_t n;
+};
+// split kernel plus reduction for every problem of g; with gf (dX only, one
+// entry per problem) the reduction also writes dA and dB
+hipError_t launch_split_path(int fmt, bool trans, int r, const SplitGroup& g, const GradFuse* gf, hipStream_t s);
 
 }  // namespace ql

@@ -549,8 +549,7 @@ TilePick pick_tile(int64_t m, int64_t o) {
 }
 
 template <int FMT, bool TRANS, int R>
-hipError_t launch_w(const Params& p, int splits, const GradFuse* gf, hipStream_t s) {
-  if (splits > 0) return launch_split_path(FMT, TRANS, R, p, splits, gf, s);
+hipError_t launch_w(const Params& p, hipStream_t s) {
 #ifndef QL_GEMM_THREADS
 #define QL_GEMM_THREADS 512
 #endif
@@ -564,17 +563,17 @@ hipError_t launch_w(const Params& p, int splits, const GradFuse* gf, hipStream_t
 }
 
 template <int FMT, bool TRANS>
-hipError_t launch_r(const Params& p, int r, int splits, const GradFuse* gf, hipStream_t s) {
+hipError_t launch_r(const Params& p, int r, hipStream_t s) {
   switch (r) {
-    case 8: return launch_w<FMT, TRANS, 8>(p, splits, gf, s);
-    case 16: return launch_w<FMT, TRANS, 16>(p, splits, gf, s);
-    default: return launch_w<FMT, TRANS, 32>(p, splits, gf, s);
+    case 8: return launch_w<FMT, TRANS, 8>(p, s);
+    case 16: return launch_w<FMT, TRANS, 16>(p, s);
+    default: return launch_w<FMT, TRANS, 32>(p, s);
   }
 }
 
 template <int FMT>
-hipError_t launch_f(const Params& p, bool trans, int r, int splits, const GradFuse* gf, hipStream_t s) {
-  return trans ? launch_r<FMT, true>(p, r, splits, gf, s) : launch_r<FMT, false>(p, r, splits, gf, s);
+hipError_t launch_f(const Params& p, bool trans, int r, hipStream_t s) {
+  return trans ? launch_r<FMT, true>(p, r, s) : launch_r<FMT, false>(p, r, s);
 }
 
 }  // namespace
@@ -600,8 +599,10 @@ size_t qgemm_workspace_bytes(int32_t fmt, bool trans, int64_t m, int64_t n, int6
   return split_plan(trans, m, n, k, r).total;
 }
 
-hipError_t launch_qgemm(const GemmCall& c, hipStream_t s) {
-  Params p{};
+// the kernel parameters of a call on the bf16 matrix-core paths; splits > 0
+// selects the small-M split path
+static void make_params(const GemmCall& c, Params& p, int& splits) {
+  p = Params{};
   p.act = c.act;
   p.codes = c.w->codes;
   p.scales = c.w->scales;
@@ -615,15 +616,28 @@ hipError_t launch_qgemm(const GemmCall& c, hipStream_t s) {
   p.C = c.trans ? p.N : p.K;
   p.O = c.trans ? p.K : p.N;
   p.s = c.s;
+  const Nf4Table& t = nf4_table();
+  for (int i = 0; i < 16; ++i) p.book.c[i] = t.level[i];
+  const SplitPlan pl = split_plan(c.trans, c.m, p.N, p.K, c.r);
+  splits = pl.splits;
+  if (pl.splits > 0) {
+    p.part = reinterpret_cast<float*>(c.ws);
+    p.upart = reinterpret_cast<float*>(reinterpret_cast<char*>(c.ws) + pl.upart_off);
+    p.sps = pl.sps;
+  }
+}
+
+hipError_t launch_qgemm(const GemmCall& c, hipStream_t s) {
   if (use_fp8_mfma(c.w->format, c.m)) {
     // a1 split of the activation, the rank-r projection (U or V, written to save), fp8 GEMM
-    const Fp8Plan fp = fp8_plan(c.trans, c.m, p.N, p.K);
+    const int64_t N = c.w->n_out, K = c.w->k_in, C = c.trans ? N : K;
+    const Fp8Plan fp = fp8_plan(c.trans, c.m, N, K);
     uint8_t* base = reinterpret_cast<uint8_t*>(c.ws);
     uint8_t* hi = base;
     uint8_t* lo = base + fp.lo_off;
     float* rs = reinterpret_cast<float*>(base + fp.rs_off);
-    hipError_t e = launch_act_quant(c.act, c.m, p.C, hi, lo, rs, s);
-    if (e == hipSuccess) e = launch_rproj(c.act, c.m, p.C, c.down, !c.trans, c.r, c.save, s);
+    hipError_t e = launch_act_quant(c.act, c.m, C, hi, lo, rs, s);
+    if (e == hipSuccess) e = launch_rproj(c.act, c.m, C, c.down, !c.trans, c.r, c.save, s);
     if (e != hipSuccess) return e;
     Gemm8Call g{};
     g.w = c.w;
@@ -639,22 +653,54 @@ hipError_t launch_qgemm(const GemmCall& c, hipStream_t s) {
     g.out = c.out;
     return launch_qgemm8(g, s);
   }
-  const Nf4Table& t = nf4_table();
-  for (int i = 0; i < 16; ++i) p.book.c[i] = t.level[i];
-  const SplitPlan pl = split_plan(c.trans, c.m, p.N, p.K, c.r);
-  if (pl.splits > 0) {
-    p.part = reinterpret_cast<float*>(c.ws);
-    p.upart = reinterpret_cast<float*>(reinterpret_cast<char*>(c.ws) + pl.upart_off);
-    p.sps = pl.sps;
-  }
+  Params p;
+  int splits = 0;
+  make_params(c, p, splits);
   // the adapter gradients ride only on the split path's reduction
-  if (c.grads && (!c.trans || pl.splits == 0)) return hipErrorInvalidValue;
-  switch (c.w->format) {
-    case QL_FMT_Q4_0: return launch_f<QL_FMT_Q4_0>(p, c.trans, c.r, pl.splits, c.grads, s);
-    case QL_FMT_NF4: return launch_f<QL_FMT_NF4>(p, c.trans, c.r, pl.splits, c.grads, s);
-    case QL_FMT_MXFP4: return launch_f<QL_FMT_MXFP4>(p, c.trans, c.r, pl.splits, c.grads, s);
-    default: return launch_f<QL_FMT_FP8_E4M3>(p, c.trans, c.r, pl.splits, c.grads, s);
+  if (c.grads && (!c.trans || splits == 0)) return hipErrorInvalidValue;
+  if (splits > 0) {
+    SplitGroup g{};
+    g.p[0] = p;
+    g.splits[0] = splits;
+    g.n = 1;
+    return launch_split_path(c.w->format, c.trans, c.r, g, c.grads, s);
   }
+  switch (c.w->format) {
+    case QL_FMT_Q4_0: return launch_f<QL_FMT_Q4_0>(p, c.trans, c.r, s);
+    case QL_FMT_NF4: return launch_f<QL_FMT_NF4>(p, c.trans, c.r, s);
+    case QL_FMT_MXFP4: return launch_f<QL_FMT_MXFP4>(p, c.trans, c.r, s);
+    default: return launch_f<QL_FMT_FP8_E4M3>(p, c.trans, c.r, s);
+  }
+}
+
+bool qgemm_groupable(const GemmCall* calls, int n) {
+  if (n < 2 || n > MAX_GROUP) return false;
+  for (int i = 0; i < n; ++i) {
+    const GemmCall& c = calls[i];
+    if (c.w->format != calls[0].w->format || c.trans != calls[0].trans || c.m != calls[0].m ||
+        c.r != calls[0].r || (c.grads != nullptr) != (calls[0].grads != nullptr))
+      return false;
+    if (split_plan(c.trans, c.m, c.w->n_out, c.w->k_in, c.r).splits == 0) return false;
+  }
+  return true;
+}
+
+hipError_t launch_qgemm_group(const GemmCall* calls, int n, hipStream_t s) {
+  if (!qgemm_groupable(calls, n)) {
+    for (int i = 0; i < n; ++i) {
+      hipError_t e = launch_qgemm(calls[i], s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  SplitGroup g{};
+  GradFuse gf[MAX_GROUP];
+  g.n = n;
+  for (int i = 0; i < n; ++i) {
+    make_params(calls[i], g.p[i], g.splits[i]);
+    if (calls[i].grads) gf[i] = *calls[i].grads;
+  }
+  return launch_split_path(calls[0].w->format, calls[0].trans, calls[0].r, g, calls[0].grads ? gf : nullptr, s);
 }
 
 }  // namespace ql

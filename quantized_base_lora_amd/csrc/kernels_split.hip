@@ -33,9 +33,17 @@ namespace {
 template <int FMT> constexpr bool split_half_codes() { return FMT == QL_FMT_Q4_0 || FMT == QL_FMT_NF4; }
 template <bool TRANS> constexpr int split_b_elems() { return TRANS ? TK * (128 + 32) : 0; }
 
+// Launch arguments of a group: the problems and the first workgroup of each.
+struct SplitArgs {
+  Params p[MAX_GROUP];
+  int32_t unit0[MAX_GROUP + 1];   // unit0[n] = grid size
+  int32_t ntiles[MAX_GROUP];
+  int32_t n;
+};
+
 template <int FMT, bool TRANS, int R, int MBK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void qsplit_kernel(Params p) {
+void qsplit_kernel(SplitArgs ga) {
   constexpr int TM = 32 * MBK, TN = 128, NT = 256, D = 4;
   static_assert(D % 2 == 0, "buffer parity of a step is its position in the chunk");
   constexpr int SBT = TN + 32;
@@ -56,10 +64,14 @@ void qsplit_kernel(Params p) {
   // linear workgroup id) in contiguous runs, so adjacent column tiles of one
   // split share their XCD's L2: a dX step reads 64 of the 128 bytes of each
   // W-row line, and the neighbouring tile reads the other half
-  const int nunits = (int)(gridDim.x * gridDim.y);
-  int unit = (int)(blockIdx.y * gridDim.x + blockIdx.x);
-  if ((nunits & 7) == 0) unit = (unit & 7) * (nunits >> 3) + (unit >> 3);
-  const int ntile = unit % (int)gridDim.x, split = unit / (int)gridDim.x;
+  const int bid = (int)blockIdx.x;
+  int pi = 0;                                        // this workgroup's problem (uniform)
+  while (pi + 1 < ga.n && bid >= ga.unit0[pi + 1]) ++pi;
+  const Params& p = ga.p[pi];
+  const int u0 = ga.unit0[pi], nunits = ga.unit0[pi + 1] - u0, nt = ga.ntiles[pi];
+  int unit = bid - u0;
+  if ((nunits & 7) == 0 && (u0 & 7) == 0) unit = (unit & 7) * (nunits >> 3) + (unit >> 3);
+  const int ntile = unit % nt, split = unit / nt;
   const int64_t o0 = (int64_t)ntile * TN;
   const int KT = (int)((p.C + TK - 1) / TK);
   const int kbeg = split * p.sps;
@@ -340,7 +352,7 @@ void qsplit_kernel(Params p) {
 }
 
 template <int FMT, bool TRANS, int R, int MBK>
-hipError_t launch_split_m(const Params& p, int splits, hipStream_t s) {
+hipError_t launch_split_m(const SplitGroup& g, hipStream_t s) {
   constexpr int B_EL = split_b_elems<TRANS>();
   constexpr int D_EL = TRANS ? BL_ELEMS : AD_ELEMS;
   constexpr size_t smem = 2 * (size_t)(32 * MBK * SA + B_EL + D_EL) * sizeof(uint16_t);
@@ -352,15 +364,24 @@ hipError_t launch_split_m(const Params& p, int splits, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((qsplit_kernel<FMT, TRANS, R, MBK>), dim3((unsigned)((p.O + 127) / 128), (unsigned)splits),
-                     dim3(256), smem, s, p);
+  SplitArgs a{};
+  a.n = g.n;
+  int32_t units = 0;
+  for (int i = 0; i < g.n; ++i) {
+    a.p[i] = g.p[i];
+    a.ntiles[i] = (int32_t)((g.p[i].O + 127) / 128);
+    a.unit0[i] = units;
+    units += a.ntiles[i] * g.splits[i];
+  }
+  a.unit0[g.n] = units;
+  hipLaunchKernelGGL((qsplit_kernel<FMT, TRANS, R, MBK>), dim3((unsigned)units), dim3(256), smem, s, a);
   return hipGetLastError();
 }
 
 // 32-row tiles when every token fits in one 32x32 MFMA block
 template <int FMT, bool TRANS, int R>
-hipError_t launch_split(const Params& p, int splits, hipStream_t s) {
-  return p.M <= 32 ? launch_split_m<FMT, TRANS, R, 1>(p, splits, s) : launch_split_m<FMT, TRANS, R, 2>(p, splits, s);
+hipError_t launch_split(const SplitGroup& g, hipStream_t s) {
+  return g.p[0].M <= 32 ? launch_split_m<FMT, TRANS, R, 1>(g, s) : launch_split_m<FMT, TRANS, R, 2>(g, s);
 }
 
 // Split-contraction reduction and epilogue: per output element the partials
@@ -368,14 +389,41 @@ hipError_t launch_split(const Params& p, int splits, hipStream_t s) {
 // added in fp32 (U = sum of its partials), and the sum is rounded once to
 // bf16.  Column-slab 0 also writes U (forward) or V (dX).  One thread per 4
 // consecutive outputs of one row.
+struct ReduceItem {
+  const float* part;
+  const float* upart;
+  const uint16_t* up;
+  uint16_t* out;
+  float* save;
+  int64_t M, O;
+  float s;
+  int32_t splits, xblocks, blk0;   // blk0: first workgroup of this item
+};
+struct ReduceArgs {
+  ReduceItem it[MAX_GROUP];
+  int32_t n;
+  int32_t trans;
+};
+
 template <int R>
-__global__ __launch_bounds__(128) void split_reduce_kernel(const float* __restrict__ part,
-                                                           const float* __restrict__ upart, int splits,
-                                                           int64_t M, int64_t O, const uint16_t* __restrict__ up,
-                                                           bool trans, float s, uint16_t* __restrict__ out,
-                                                           float* __restrict__ save) {
+__global__ __launch_bounds__(128) void split_reduce_kernel(ReduceArgs ra) {
   __shared__ float us[R];
-  const int64_t m = blockIdx.y;
+  const int bid = (int)blockIdx.x;
+  int ii = 0;
+  while (ii + 1 < ra.n && bid >= ra.it[ii + 1].blk0) ++ii;
+  const ReduceItem& I = ra.it[ii];
+  const float* __restrict__ part = I.part;
+  const float* __restrict__ upart = I.upart;
+  const uint16_t* __restrict__ up = I.up;
+  uint16_t* __restrict__ out = I.out;
+  float* __restrict__ save = I.save;
+  const int64_t M = I.M, O = I.O;
+  const int splits = I.splits;
+  const float s = I.s;
+  const bool trans = ra.trans != 0;
+  const int local = bid - I.blk0;
+  const int bx = local % I.xblocks;
+  const int64_t m = local / I.xblocks;
   const int tid = threadIdx.x;
   // splits past the last read as zero through the resource bounds
   const __amdgpu_buffer_rsrc_t rp = rsrc(part, (int64_t)splits * M * O * 4);
@@ -387,10 +435,10 @@ __global__ __launch_bounds__(128) void split_reduce_kernel(const float* __restri
     float u = 0.0f;
 #pragma unroll
     for (int sp = 0; sp < MAX_SPLITS; ++sp) u += __uint_as_float(v[sp]);
-    if (save && blockIdx.x == 0) save[m * R + tid] = u;
+    if (save && bx == 0) save[m * R + tid] = u;
     us[tid] = s * u;
   }
-  const int64_t o = (int64_t)blockIdx.x * 512 + tid * 4;
+  const int64_t o = (int64_t)bx * 512 + tid * 4;
   const bool live = o < O;
   // the up-matrix entries of these 4 outputs, as bf16 pairs
   uint32_t w[4][R / 2];
@@ -452,20 +500,52 @@ constexpr int RB_TC = 16;       // dX / dA columns per workgroup
 constexpr int RB_NB = 64;       // at most this many dB rows per workgroup
 constexpr int RB_MAXM = 32;     // tokens (host side: split_path_fuses_grads)
 
+struct ReduceBwdItem {
+  const float* part;
+  const float* upart;
+  const uint16_t* adA;
+  uint16_t* dx;
+  const uint16_t* x;
+  const uint16_t* dy;
+  const float* u;
+  float* d_a;
+  float* d_b;
+  int64_t M, K, N, nb;
+  float s;
+  int32_t splits, accumulate, blk0;
+};
+struct ReduceBwdArgs {
+  ReduceBwdItem it[MAX_GROUP];
+  int32_t n;
+};
+
 template <int R>
-__global__ __launch_bounds__(256) void split_reduce_bwd_kernel(
-    const float* __restrict__ part, const float* __restrict__ upart, int splits, int64_t M, int64_t K, int64_t N,
-    const uint16_t* __restrict__ adA, float s, uint16_t* __restrict__ dx, const uint16_t* __restrict__ x,
-    const uint16_t* __restrict__ dy, const float* __restrict__ u, float* __restrict__ d_a,
-    float* __restrict__ d_b, int64_t nb, int accumulate) {
+__global__ __launch_bounds__(256) void split_reduce_bwd_kernel(ReduceBwdArgs ra) {
   constexpr int NT = 256, TC = RB_TC, SR = R + 1;
+  const int bid = (int)blockIdx.x;
+  int ii = 0;
+  while (ii + 1 < ra.n && bid >= ra.it[ii + 1].blk0) ++ii;
+  const ReduceBwdItem& I = ra.it[ii];
+  const float* __restrict__ part = I.part;
+  const float* __restrict__ upart = I.upart;
+  const uint16_t* __restrict__ adA = I.adA;
+  uint16_t* __restrict__ dx = I.dx;
+  const uint16_t* __restrict__ x = I.x;
+  const uint16_t* __restrict__ dy = I.dy;
+  const float* __restrict__ u = I.u;
+  float* __restrict__ d_a = I.d_a;
+  float* __restrict__ d_b = I.d_b;
+  const int64_t M = I.M, K = I.K, N = I.N, nb = I.nb;
+  const float s = I.s;
+  const int splits = I.splits, accumulate = I.accumulate;
+  const int64_t gblk = bid - I.blk0;                 // this workgroup's index within its item
   __shared__ float vs[RB_MAXM * SR];                  // V [m][j]
   __shared__ float ush[RB_MAXM * SR];                 // U [m][j]
   __shared__ float as_[R * TC];                       // A [j][k0 ..]
   __shared__ uint16_t xs[RB_MAXM * TC];               // x [m][k0 ..] (bf16)
   __shared__ uint16_t ys[RB_MAXM * RB_NB];            // dY [m][n0 ..] (bf16)
   const int tid = threadIdx.x;
-  const int64_t k0 = (int64_t)blockIdx.x * TC, n0 = (int64_t)blockIdx.x * nb;
+  const int64_t k0 = gblk * TC, n0 = gblk * nb;
   const int nn = n0 < N ? (int)(n0 + nb <= N ? nb : N - n0) : 0;   // dB rows of this workgroup
   const int kc = k0 < K ? (int)(k0 + TC <= K ? TC : K - k0) : 0;  // dX / dA columns
   const int m_ = (int)M;
@@ -541,32 +621,72 @@ __global__ __launch_bounds__(256) void split_reduce_bwd_kernel(
 }
 
 template <int FMT, bool TRANS, int R>
-hipError_t launch_path(const Params& p, int splits, const GradFuse* gf, hipStream_t s) {
-  hipError_t e = launch_split<FMT, TRANS, R>(p, splits, s);
+hipError_t launch_path(const SplitGroup& g, const GradFuse* gf, hipStream_t s) {
+  hipError_t e = launch_split<FMT, TRANS, R>(g, s);
   if (e != hipSuccess) return e;
   if (gf) {
-    // enough workgroups for the dX columns and for at most RB_NB dB rows each
-    const int64_t g = std::max((p.K + RB_TC - 1) / RB_TC, (p.N + RB_NB - 1) / RB_NB);
-    const int64_t nb = (p.N + g - 1) / g;
-    hipLaunchKernelGGL(split_reduce_bwd_kernel<R>, dim3((unsigned)g), dim3(256), 0, s, (const float*)p.part,
-                       (const float*)p.upart, splits, p.M, p.K, p.N, p.up, p.s, p.out, gf->x, p.act, gf->u,
-                       gf->d_a, gf->d_b, nb, gf->accumulate);
+    ReduceBwdArgs ra{};
+    ra.n = g.n;
+    int32_t blocks = 0;
+    for (int i = 0; i < g.n; ++i) {
+      const Params& p = g.p[i];
+      // enough workgroups for the dX columns and for at most RB_NB dB rows each
+      const int64_t nblk = std::max((p.K + RB_TC - 1) / RB_TC, (p.N + RB_NB - 1) / RB_NB);
+      ReduceBwdItem& I = ra.it[i];
+      I.part = p.part;
+      I.upart = p.upart;
+      I.adA = p.up;
+      I.dx = p.out;
+      I.x = gf[i].x;
+      I.dy = p.act;
+      I.u = gf[i].u;
+      I.d_a = gf[i].d_a;
+      I.d_b = gf[i].d_b;
+      I.M = p.M;
+      I.K = p.K;
+      I.N = p.N;
+      I.nb = (p.N + nblk - 1) / nblk;
+      I.s = p.s;
+      I.splits = g.splits[i];
+      I.accumulate = gf[i].accumulate;
+      I.blk0 = blocks;
+      blocks += (int32_t)nblk;
+    }
+    hipLaunchKernelGGL(split_reduce_bwd_kernel<R>, dim3((unsigned)blocks), dim3(256), 0, s, ra);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(split_reduce_kernel<R>, dim3((unsigned)((p.O + 511) / 512), (unsigned)p.M), dim3(128), 0, s,
-                     (const float*)p.part, (const float*)p.upart, splits, p.M, p.O, p.up, TRANS, p.s, p.out, p.save);
+  ReduceArgs ra{};
+  ra.n = g.n;
+  ra.trans = TRANS ? 1 : 0;
+  int32_t blocks = 0;
+  for (int i = 0; i < g.n; ++i) {
+    const Params& p = g.p[i];
+    ReduceItem& I = ra.it[i];
+    I.part = p.part;
+    I.upart = p.upart;
+    I.up = p.up;
+    I.out = p.out;
+    I.save = p.save;
+    I.M = p.M;
+    I.O = p.O;
+    I.s = p.s;
+    I.splits = g.splits[i];
+    I.xblocks = (int32_t)((p.O + 511) / 512);
+    I.blk0 = blocks;
+    blocks += I.xblocks * (int32_t)p.M;
+  }
+  hipLaunchKernelGGL(split_reduce_kernel<R>, dim3((unsigned)blocks), dim3(128), 0, s, ra);
   return hipGetLastError();
 }
 
 template <int FMT, bool TRANS>
-hipError_t launch_r(const Params& p, int r, int splits, const GradFuse* gf, hipStream_t s) {
+hipError_t launch_r(const SplitGroup& g, int r, const GradFuse* gf, hipStream_t s) {
   switch (r) {
-    case 8: return launch_path<FMT, TRANS, 8>(p, splits, gf, s);
-    case 16: return launch_path<FMT, TRANS, 16>(p, splits, gf, s);
-    default: return launch_path<FMT, TRANS, 32>(p, splits, gf, s);
+    case 8: return launch_path<FMT, TRANS, 8>(g, gf, s);
+    case 16: return launch_path<FMT, TRANS, 16>(g, gf, s);
+    default: return launch_path<FMT, TRANS, 32>(g, gf, s);
   }
 }
-
 
 }  // namespace
 
@@ -593,14 +713,16 @@ SplitPlan split_plan(bool trans, int64_t m, int64_t n, int64_t k, int r) {
 // per-token loops of the fused kernel cost more than the launch it saves
 bool split_path_fuses_grads(int64_t m) { return m > 0 && m <= 32; }
 
-hipError_t launch_split_path(int fmt, bool trans, int r, const Params& p, int splits, const GradFuse* gf,
-                             hipStream_t s) {
-  if (gf && (!trans || !split_path_fuses_grads(p.M))) return hipErrorInvalidValue;
+hipError_t launch_split_path(int fmt, bool trans, int r, const SplitGroup& g, const GradFuse* gf, hipStream_t s) {
+  if (g.n < 1 || g.n > MAX_GROUP) return hipErrorInvalidValue;
+  if (gf && (!trans || !split_path_fuses_grads(g.p[0].M))) return hipErrorInvalidValue;
+  for (int i = 1; i < g.n; ++i)
+    if (g.p[i].M != g.p[0].M) return hipErrorInvalidValue;
   switch (fmt) {
-    case QL_FMT_Q4_0: return trans ? launch_r<QL_FMT_Q4_0, true>(p, r, splits, gf, s) : launch_r<QL_FMT_Q4_0, false>(p, r, splits, gf, s);
-    case QL_FMT_NF4: return trans ? launch_r<QL_FMT_NF4, true>(p, r, splits, gf, s) : launch_r<QL_FMT_NF4, false>(p, r, splits, gf, s);
-    case QL_FMT_MXFP4: return trans ? launch_r<QL_FMT_MXFP4, true>(p, r, splits, gf, s) : launch_r<QL_FMT_MXFP4, false>(p, r, splits, gf, s);
-    default: return trans ? launch_r<QL_FMT_FP8_E4M3, true>(p, r, splits, gf, s) : launch_r<QL_FMT_FP8_E4M3, false>(p, r, splits, gf, s);
+    case QL_FMT_Q4_0: return trans ? launch_r<QL_FMT_Q4_0, true>(g, r, gf, s) : launch_r<QL_FMT_Q4_0, false>(g, r, gf, s);
+    case QL_FMT_NF4: return trans ? launch_r<QL_FMT_NF4, true>(g, r, gf, s) : launch_r<QL_FMT_NF4, false>(g, r, gf, s);
+    case QL_FMT_MXFP4: return trans ? launch_r<QL_FMT_MXFP4, true>(g, r, gf, s) : launch_r<QL_FMT_MXFP4, false>(g, r, gf, s);
+    default: return trans ? launch_r<QL_FMT_FP8_E4M3, true>(g, r, gf, s) : launch_r<QL_FMT_FP8_E4M3, false>(g, r, gf, s);
   }
 }
 

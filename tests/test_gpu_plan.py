@@ -64,3 +64,60 @@ def test_plan_matches_direct_calls(lib):
                 iv = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
                 assert torch.equal(a.view(iv), b.view(iv)), (run, j, key)
     pl.close()
+
+
+GROUPS = [
+    # fmt, m, r, [(k, n), ...]: split path with fused gradients, split path at 64 tokens,
+    # 33 tokens (separate gradient launch), and a tile-path group (launched call by call)
+    (ofmt.FMT_NF4, 16, 16, [(512, 384), (512, 128), (512, 128)]),
+    (ofmt.FMT_MXFP4, 64, 8, [(1024, 256), (256, 1024)]),
+    (ofmt.FMT_Q4_0, 33, 32, [(96, 224), (1056, 64), (256, 96)]),
+    (ofmt.FMT_FP8, 24, 16, [(256, 160), (512, 96)]),
+    (ofmt.FMT_NF4, 200, 16, [(256, 192), (128, 64)]),
+]
+
+
+@pytest.mark.parametrize("grp", GROUPS, ids=[f"fmt{g[0]}-m{g[1]}-r{g[2]}-n{len(g[3])}" for g in GROUPS])
+def test_group_matches_single_calls(lib, grp):
+    """A group (direct call and through a plan) gives bitwise the results of
+    its calls made one by one."""
+    from quantized_base_lora_amd import binding as B
+    fmt, m, r, shapes = grp
+    print(f"group fmt={fmt} m={m} r={r} shapes={shapes}", flush=True)
+    alpha = 16.0
+    ref, fi, bi = [], [], []
+    for i, (k, n) in enumerate(shapes):
+        c = H.make_case(m, k, n, r, seed=80 + i)
+        qw = B.quant_pack(fmt, torch.from_numpy(c["W"]).cuda())
+        t = {key: H.bits_to_bf16_tensor(c[key]) for key in ("x", "dY", "A", "B")}
+        y, u = B.linear_fwd(qw, t["x"], t["A"], t["B"], alpha)
+        dx, da, db = B.linear_bwd(qw, t["x"], t["dY"], u, t["A"], t["B"], alpha)
+        ref.append({"y": y, "u": u, "dx": dx, "da": da, "db": db})
+        o = {key: torch.empty_like(v) for key, v in ref[-1].items()}
+        wsf = torch.empty(max(256, B.workspace_bytes(B.OP_FWD, fmt, n, k, m, r)), dtype=torch.uint8, device="cuda")
+        wsb = torch.empty(max(256, B.workspace_bytes(B.OP_BWD, fmt, n, k, m, r)), dtype=torch.uint8, device="cuda")
+        fi.append((qw, t["x"], t["A"], t["B"], alpha, o["y"], o["u"], wsf))
+        # the backward reads the group forward's own U
+        bi.append((qw, t["x"], t["dY"], o["u"], t["A"], t["B"], alpha, o["dx"], o["da"], o["db"], wsb, False))
+    torch.cuda.synchronize()
+
+    def check(tag):
+        torch.cuda.synchronize()
+        for j, (rf, it) in enumerate(zip(ref, bi)):
+            got = {"y": fi[j][5], "u": fi[j][6], "dx": it[7], "da": it[8], "db": it[9]}
+            for key, v in rf.items():
+                iv = torch.int16 if v.dtype == torch.bfloat16 else torch.int32
+                assert torch.equal(got[key].view(iv), v.view(iv)), (tag, j, key)
+
+    B.linear_fwd_group(fi)
+    B.linear_bwd_group(bi)
+    check("direct")
+    pl = B.Plan()
+    pl.add_fwd_group(fi)
+    pl.add_bwd_group(bi)
+    for run in range(2):
+        for it in fi:
+            it[5].fill_(float("nan"))
+        pl.run()
+        check(f"plan run {run}")
+    pl.close()

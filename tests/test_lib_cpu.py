@@ -161,3 +161,49 @@ def test_plan_argument_errors(lib):
     finally:
         assert lib.ql_plan_destroy(h) == binding.QL_OK
     assert lib.ql_plan_size(None) == 0
+
+
+def test_group_argument_errors(lib):
+    """Grouped calls: validated like single calls, one base format, and no
+    call may write a buffer another call of the group reads or writes."""
+    m, r = 16, 16
+    q1 = _qw(codes=0x100000, scales=0x110000)
+    q2 = _qw(codes=0x120000, scales=0x130000)
+    ws = binding.workspace_bytes(binding.OP_FWD, q1.format, q1.n_out, q1.k_in, m, r)
+
+    def call(qw, base):   # every buffer of a call at its own address range
+        return binding.FwdCallC(ctypes.addressof(qw), base, base + 0x10000, base + 0x20000, 16.0, 0,
+                                base + 0x30000, base + 0x40000, base + 0x50000, ws)
+
+    a = call(q1, 0x1000000)
+    b = call(q2, 0x2000000)
+    grp = lib.qlora_linear_fwd_group
+    assert grp((binding.FwdCallC * 2)(a, b), 0, m, r, None) == binding.QL_EINVAL
+    assert grp((binding.FwdCallC * 2)(a, b), 9, m, r, None) == binding.QL_EINVAL
+    assert grp(None, 2, m, r, None) == binding.QL_EINVAL
+    assert grp((binding.FwdCallC * 2)(a, b), 2, m, 12, None) == binding.QL_EUNSUPPORTED
+    # call 1 writes its y onto call 0's input x
+    bad = call(q2, 0x2000000)
+    bad.y = a.x
+    assert grp((binding.FwdCallC * 2)(a, bad), 2, m, r, None) == binding.QL_EINVAL
+    assert "not independent" in _err(lib)
+    # two calls sharing one workspace
+    bad = call(q2, 0x2000000)
+    bad.ws = a.ws
+    assert grp((binding.FwdCallC * 2)(a, bad), 2, m, r, None) == binding.QL_EINVAL
+    # mixed base formats
+    q3 = _qw(fmt=binding.FMT_Q4_0, codes=0x140000, scales=0x150000)
+    c = call(q3, 0x3000000)
+    assert grp((binding.FwdCallC * 2)(a, c), 2, m, r, None) == binding.QL_EINVAL
+    assert "formats" in _err(lib)
+    # reading the same input is allowed (q, k and v share x): the plan records it
+    shared = call(q2, 0x2000000)
+    shared.x = a.x
+    h = ctypes.c_void_p()
+    assert lib.ql_plan_create(ctypes.byref(h)) == binding.QL_OK
+    try:
+        assert lib.ql_plan_add_fwd_group(h, (binding.FwdCallC * 2)(a, shared), 2, m, r) == binding.QL_OK
+        assert lib.ql_plan_add_fwd_group(h, (binding.FwdCallC * 2)(a, bad), 2, m, r) == binding.QL_EINVAL
+        assert lib.ql_plan_size(h) == 1
+    finally:
+        lib.ql_plan_destroy(h)
