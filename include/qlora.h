@@ -190,7 +190,9 @@ int qlora_linear_bwd(const ql_qweight* w, const uint16_t* x, const uint16_t* dy,
  * calling qlora_linear_fwd (qlora_linear_bwd) for each in order, with bitwise
  * the same results.  At most 64 tokens (the split-contraction path) the
  * group's base GEMMs run as one split launch and one reduction launch instead
- * of two launches per call; otherwise the calls are launched one by one.  In
+ * of two launches per call; the backward's adapter gradients of the whole
+ * group take one launch (plus one reduction above 512 tokens) at any token
+ * count; other base GEMMs are launched one by one.  In
  * a decoder layer the q, k and v projections (and gate and up) read the same
  * input and form such a group.
  *

@@ -201,8 +201,7 @@ void bwd_parts(const BwdArgs& a, BwdParts& b) {
   c.grads = b.fuse ? &b.gf : nullptr;
 }
 
-hipError_t bwd_grads(const BwdArgs& a, const BwdParts& b, hipStream_t s) {
-  if (b.fuse) return hipSuccess;
+GradLaunch grad_launch(const BwdArgs& a, const BwdParts& b) {
   GradLaunch g{};
   g.x = a.x;
   g.dy = a.dy;
@@ -219,7 +218,12 @@ hipError_t bwd_grads(const BwdArgs& a, const BwdParts& b, hipStream_t s) {
   g.nparts = b.L.parts;
   g.s = a.alpha / (float)a.r;
   g.accumulate = a.accumulate != 0;
-  return launch_grads(g, s);
+  return g;
+}
+
+hipError_t bwd_grads(const BwdArgs& a, const BwdParts& b, hipStream_t s) {
+  if (b.fuse) return hipSuccess;
+  return launch_grads(grad_launch(a, b), s);
 }
 
 int enqueue_bwd(const BwdArgs& a, hipStream_t s) {
@@ -317,7 +321,11 @@ int enqueue_bwd_group(const BwdArgs* a, int n, hipStream_t s) {
     c[i] = b[i].gemm;
   }
   hipError_t e = launch_qgemm_group(c, n, s);
-  for (int i = 0; i < n && e == hipSuccess; ++i) e = bwd_grads(a[i], b[i], s);
+  if (e == hipSuccess && !b[0].fuse) {   // one token count: all fused or none
+    GradLaunch g[QL_GROUP_MAX];
+    for (int i = 0; i < n; ++i) g[i] = grad_launch(a[i], b[i]);
+    e = launch_grads_group(g, n, s);
+  }
   if (e != hipSuccess) return hip_error(e, "grouped backward launch");
   return QL_OK;
 }

@@ -144,6 +144,9 @@ struct GradLaunch {
   int32_t accumulate;
 };
 hipError_t launch_grads(const GradLaunch& g, hipStream_t s);
+// the gradients of n calls with one token count, rank and partition plan in
+// one launch (and one reduction launch)
+hipError_t launch_grads_group(const GradLaunch* g, int n, hipStream_t s);
 int32_t grad_parts(int64_t m);
 int64_t grad_tiles(int64_t pdim);
 

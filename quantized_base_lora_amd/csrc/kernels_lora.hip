@@ -4,7 +4,8 @@
 //
 // Both have the form out[p][j] = s . sum_m X[m][p] . Q[m][j] with X a bf16
 // activation ([M, K] or [M, N]) and Q an fp32 rank-r projection ([M, r]);
-// one launch serves both (blockIdx.z).  A workgroup owns 64 columns p and one
+// one launch serves both, for up to QL_GROUP_MAX calls at once (a problem
+// table in the kernel arguments).  A workgroup owns 64 columns p and one
 // of P fixed partitions of M; it streams its rows through LDS in steps of
 // 64 (loads running three steps ahead) and accumulates on 16x16x32 bf16
 // MFMAs, with X reaching the A operand through LDS transpose reads and Q
@@ -35,15 +36,21 @@ struct GradProb {
   float* part;
   int64_t pdim;
   int32_t transpose_out;
+  float s;
+  int32_t accumulate;
+  int32_t blk0;          // first workgroup of this problem (its tiles x partitions)
+  int32_t rblk0;         // first workgroup of this problem in the reduction launch
 };
 
+// dA and dB of up to QL_GROUP_MAX calls with one token count and rank: the
+// problems of a launch share m, the partition plan and r.
+constexpr int MAX_PROB = 2 * QL_GROUP_MAX;
 struct GradArgs {
-  GradProb prob[2];
+  GradProb prob[MAX_PROB];
+  int32_t nprob;
   int64_t m;
   int64_t chunk;
   int32_t nparts;
-  float s;
-  int32_t accumulate;
   int32_t r;
 };
 
@@ -55,11 +62,15 @@ __global__ __launch_bounds__(NT) void grad_kernel(GradArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Qh[TMC * SQ];
   __shared__ __attribute__((aligned(16))) uint16_t Ql[TMC * SQ];
 
-  const GradProb& pr = a.prob[blockIdx.z];
-  const int64_t p0 = (int64_t)blockIdx.x * TP;
-  if (p0 >= pr.pdim) return;                         // whole workgroup: this problem is narrower
+  const int bid = (int)blockIdx.x;
+  int pi = 0;                                        // this workgroup's problem (uniform)
+  while (pi + 1 < a.nprob && bid >= a.prob[pi + 1].blk0) ++pi;
+  const GradProb& pr = a.prob[pi];
+  const int local = bid - pr.blk0;
+  const int part = local % a.nparts;                 // partition of M
+  const int64_t p0 = (int64_t)(local / a.nparts) * TP;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t mq0 = (int64_t)blockIdx.y * a.chunk;
+  const int64_t mq0 = (int64_t)part * a.chunk;
   const int64_t mq1 = mq0 + a.chunk < a.m ? mq0 + a.chunk : a.m;
 
   for (int i = tid; i < TMC * SQ; i += NT) { Qh[i] = 0; Ql[i] = 0; }
@@ -153,7 +164,7 @@ __global__ __launch_bounds__(NT) void grad_kernel(GradArgs a) {
   // partition the sum is complete: scale and write the result (out[p][j] or
   // out[j][p]); otherwise write partial[q][p][j] for the reduction launch.
   const bool final_out = a.nparts == 1;
-  float* dst = pr.part + (int64_t)blockIdx.y * pr.pdim * R;
+  float* dst = pr.part + (int64_t)part * pr.pdim * R;
 #pragma unroll
   for (int jb = 0; jb < RB; ++jb)
 #pragma unroll
@@ -163,8 +174,8 @@ __global__ __launch_bounds__(NT) void grad_kernel(GradArgs a) {
       if (prow < pr.pdim && j < R) {
         if (final_out) {
           const int64_t o = pr.transpose_out ? (int64_t)j * pr.pdim + prow : prow * R + j;
-          const float v = a.s * acc[jb][e];
-          pr.out[o] = a.accumulate ? pr.out[o] + v : v;
+          const float v = pr.s * acc[jb][e];
+          pr.out[o] = pr.accumulate ? pr.out[o] + v : v;
         } else {
           dst[prow * R + j] = acc[jb][e];
         }
@@ -175,9 +186,12 @@ __global__ __launch_bounds__(NT) void grad_kernel(GradArgs a) {
 // out[p][j] (or out[j][p]) = s * sum_q part[q][p][j], q in partition order; one
 // thread per output element, the partials read 8 at a time.
 __global__ __launch_bounds__(NT) void grad_reduce_kernel(GradArgs a) {
-  const GradProb& pr = a.prob[blockIdx.y];
+  const int bid = (int)blockIdx.x;
+  int pb = 0;
+  while (pb + 1 < a.nprob && bid >= a.prob[pb + 1].rblk0) ++pb;
+  const GradProb& pr = a.prob[pb];
   const int64_t total = pr.pdim * a.r;
-  const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
+  const int64_t i = (int64_t)(bid - pr.rblk0) * NT + threadIdx.x;
   if (i >= total) return;
   const float* src = pr.part + i;
   float sum = 0.0f;
@@ -193,8 +207,8 @@ __global__ __launch_bounds__(NT) void grad_reduce_kernel(GradArgs a) {
   const int64_t pi = i / a.r;
   const int j = (int)(i % a.r);
   const int64_t o = pr.transpose_out ? (int64_t)j * pr.pdim + pi : i;
-  const float v = a.s * sum;
-  pr.out[o] = a.accumulate ? pr.out[o] + v : v;
+  const float v = pr.s * sum;
+  pr.out[o] = pr.accumulate ? pr.out[o] + v : v;
 }
 
 // out[m][j] = sum_c x[m][c] * b[c][j]; one workgroup per row (used when dX is not wanted).
@@ -248,33 +262,45 @@ hipError_t launch_down_proj(const uint16_t* x, int64_t m, int64_t c, const uint1
   return hipGetLastError();
 }
 
-hipError_t launch_grads(const GradLaunch& g, hipStream_t s) {
+hipError_t launch_grads_group(const GradLaunch* g, int n, hipStream_t s) {
+  if (n < 1 || n > QL_GROUP_MAX) return hipErrorInvalidValue;
   GradArgs a{};
-  a.prob[0] = GradProb{g.x, g.v, g.d_a, g.part_a, g.k, 1};
-  a.prob[1] = GradProb{g.dy, g.u, g.d_b, g.part_b, g.n, 0};
-  a.r = g.r;
-  a.m = g.m;
-  a.nparts = g.nparts;
-  int64_t chunk = (g.m + g.nparts - 1) / g.nparts;
+  a.nprob = 2 * n;
+  a.r = g[0].r;
+  a.m = g[0].m;
+  a.nparts = g[0].nparts;
+  int64_t chunk = (g[0].m + g[0].nparts - 1) / g[0].nparts;
   a.chunk = (chunk + TMC - 1) / TMC * TMC;
-  a.s = g.s;
-  a.accumulate = g.accumulate;
-  const int64_t tiles = grad_tiles(g.k > g.n ? g.k : g.n);
-  dim3 grid((unsigned)tiles, (unsigned)g.nparts, 2);
-  if (g.m > 0) {
-    switch (g.r) {
-      case 8: hipLaunchKernelGGL(grad_kernel<8>, grid, dim3(NT), 0, s, a); break;
-      case 16: hipLaunchKernelGGL(grad_kernel<16>, grid, dim3(NT), 0, s, a); break;
-      default: hipLaunchKernelGGL(grad_kernel<32>, grid, dim3(NT), 0, s, a); break;
+  int32_t blocks = 0, rblocks = 0;
+  for (int i = 0; i < n; ++i) {
+    if (g[i].m != a.m || g[i].r != a.r || g[i].nparts != a.nparts) return hipErrorInvalidValue;
+    const float sc = g[i].s;
+    const int32_t acc = g[i].accumulate;
+    a.prob[2 * i] = GradProb{g[i].x, g[i].v, g[i].d_a, g[i].part_a, g[i].k, 1, sc, acc, 0, 0};
+    a.prob[2 * i + 1] = GradProb{g[i].dy, g[i].u, g[i].d_b, g[i].part_b, g[i].n, 0, sc, acc, 0, 0};
+  }
+  for (int i = 0; i < a.nprob; ++i) {
+    GradProb& pr = a.prob[i];
+    pr.blk0 = blocks;
+    blocks += (int32_t)grad_tiles(pr.pdim) * a.nparts;
+    pr.rblk0 = rblocks;
+    rblocks += (int32_t)((pr.pdim * a.r + NT - 1) / NT);
+  }
+  if (a.m > 0) {
+    switch (a.r) {
+      case 8: hipLaunchKernelGGL(grad_kernel<8>, dim3((unsigned)blocks), dim3(NT), 0, s, a); break;
+      case 16: hipLaunchKernelGGL(grad_kernel<16>, dim3((unsigned)blocks), dim3(NT), 0, s, a); break;
+      default: hipLaunchKernelGGL(grad_kernel<32>, dim3((unsigned)blocks), dim3(NT), 0, s, a); break;
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || g.nparts == 1) return e;   // one partition: the kernel wrote dA, dB
+    if (e != hipSuccess || a.nparts == 1) return e;   // one partition: the kernel wrote dA, dB
   } else {
     a.nparts = 0;                                     // no tokens: dA = dB = 0 (or unchanged)
   }
-  const int64_t big = (g.k > g.n ? g.k : g.n) * g.r;
-  hipLaunchKernelGGL(grad_reduce_kernel, dim3((unsigned)((big + NT - 1) / NT), 2), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(grad_reduce_kernel, dim3((unsigned)rblocks), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
+
+hipError_t launch_grads(const GradLaunch& g, hipStream_t s) { return launch_grads_group(&g, 1, s); }
 
 }  // namespace ql
