@@ -121,3 +121,61 @@ def test_group_matches_single_calls(lib, grp):
         pl.run()
         check(f"plan run {run}")
     pl.close()
+
+
+def test_group_edge_cases(lib):
+    """Groups with accumulate, with one call, without dX, and with no tokens
+    behave as the same single calls."""
+    from quantized_base_lora_amd import binding as B
+    fmt, r, alpha = ofmt.FMT_NF4, 16, 32.0
+    shapes = [(256, 128), (128, 192)]
+
+    def setup(m, seed):
+        items = []
+        for i, (k, n) in enumerate(shapes):
+            c = H.make_case(max(m, 1), k, n, r, seed=seed + i)
+            qw = B.quant_pack(fmt, torch.from_numpy(c["W"]).cuda())
+            t = {key: H.bits_to_bf16_tensor(c[key])[:m] if key in ("x", "dY") else H.bits_to_bf16_tensor(c[key])
+                 for key in ("x", "dY", "A", "B")}
+            items.append((qw, t, k, n))
+        return items
+
+    for m in (24, 48, 0):
+        print(f"group edge cases m={m}", flush=True)
+        items = setup(m, 90)
+        # reference: single calls, accumulating onto given dA / dB, and a call without dX
+        ref = []
+        for qw, t, k, n in items:
+            y, u = B.linear_fwd(qw, t["x"], t["A"], t["B"], alpha)
+            da0 = torch.full((r, k), 0.25, device="cuda")
+            db0 = torch.full((n, r), -0.5, device="cuda")
+            dx, da, db = B.linear_bwd(qw, t["x"], t["dY"], u, t["A"], t["B"], alpha, accumulate=True,
+                                      da=da0.clone(), db=db0.clone())
+            _, da2, db2 = B.linear_bwd(qw, t["x"], t["dY"], u, t["A"], t["B"], alpha, need_dx=False)
+            ref.append(dict(y=y, u=u, dx=dx, da=da, db=db, da2=da2, db2=db2))
+        got = []
+        fi, bi, bn = [], [], []
+        for (qw, t, k, n), rf in zip(items, ref):
+            o = dict(y=torch.empty_like(rf["y"]), u=torch.empty_like(rf["u"]), dx=torch.empty_like(rf["dx"]),
+                     da=torch.full((r, k), 0.25, device="cuda"), db=torch.full((n, r), -0.5, device="cuda"),
+                     da2=torch.empty((r, k), device="cuda"), db2=torch.empty((n, r), device="cuda"),
+                     wsf=torch.empty(max(256, B.workspace_bytes(B.OP_FWD, fmt, n, k, m, r)), dtype=torch.uint8,
+                                     device="cuda"),
+                     wsb=torch.empty(max(256, B.workspace_bytes(B.OP_BWD, fmt, n, k, m, r)), dtype=torch.uint8,
+                                     device="cuda"),
+                     wsb2=torch.empty(max(256, B.workspace_bytes(B.OP_BWD, fmt, n, k, m, r)), dtype=torch.uint8,
+                                      device="cuda"))
+            got.append(o)
+            fi.append((qw, t["x"], t["A"], t["B"], alpha, o["y"], o["u"], o["wsf"]))
+            bi.append((qw, t["x"], t["dY"], o["u"], t["A"], t["B"], alpha, o["dx"], o["da"], o["db"], o["wsb"], True))
+            bn.append((qw, t["x"], t["dY"], o["u"], t["A"], t["B"], alpha, None, o["da2"], o["db2"], o["wsb2"], False))
+        B.linear_fwd_group(fi[:1])            # a group of one
+        B.linear_fwd_group(fi[1:])
+        B.linear_bwd_group(bi)                # accumulate into the given dA / dB
+        B.linear_bwd_group(bn)                # no dX
+        torch.cuda.synchronize()
+        for j, (rf, o) in enumerate(zip(ref, got)):
+            for key in ("y", "u", "dx", "da", "db", "da2", "db2"):
+                a, b = o[key], rf[key]
+                iv = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+                assert torch.equal(a.view(iv), b.view(iv)), (m, j, key)
