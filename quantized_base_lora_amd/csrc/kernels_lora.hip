@@ -54,8 +54,13 @@ struct GradArgs {
   int32_t r;
 };
 
+// four workgroups per CU (register budget of four waves per SIMD) for ranks up
+// to 16; rank 32 needs more registers
+template <int R> constexpr int grad_waves() { return R <= 16 ? 4 : 2; }
+
 template <int R>
-__global__ __launch_bounds__(NT) void grad_kernel(GradArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(grad_waves<R>(), grad_waves<R>())))
+void grad_kernel(GradArgs a) {
   constexpr int RB = (R + 15) / 16;
   constexpr int QPT = R / 4;                         // Q floats per thread per step
   __shared__ __attribute__((aligned(16))) uint16_t Xs[TMC * SX];
@@ -85,7 +90,7 @@ __global__ __launch_bounds__(NT) void grad_kernel(GradArgs a) {
   // loads run DEPTH - 1 steps ahead of the LDS stores (a ring of register sets).
   // Reads past the partition or past the last column go to an out-of-range
   // buffer offset and return zero, so no loaded value is inspected at issue.
-  constexpr int DEPTH = 4;
+  constexpr int DEPTH = grad_waves<R>() == 4 ? 3 : 4;   // ring depth that fits the register budget
   const __amdgpu_buffer_rsrc_t rx = rsrc(pr.x + mq0 * pr.pdim, (mq1 - mq0) * pr.pdim * 2);
   const __amdgpu_buffer_rsrc_t rq = rsrc(pr.q + mq0 * R, (mq1 - mq0) * R * 4);
   const int NS = (int)((mq1 - mq0 + TMC - 1) / TMC);
