@@ -21,16 +21,14 @@ namespace {
 //
 // Forward (y = x.W^T): no W element is used by more than one wave, so W is
 // not staged through LDS.  Each lane loads the codes of its own MFMA
-// B-operand rows (row 32 wave + lane % 32, half lane / 32 of each 32-element
-// group) and dequantizes them straight into operand registers; only the
-// shared activation tile goes through LDS.  The order in which a dot product
-// runs over K is free, so the K elements a lane's operand holds are chosen to
-// be contiguous in memory: for the split-half 4-bit layout that is the
-// standard MFMA order (8 bytes give elements 8h..8h+7 and 16+8h..16+8h+7);
-// for MXFP4 and FP8 slice ks of lane half h holds elements
-// 32 (ks / 2) + 16 h + 8 (ks % 2), and the activation fragment is read in the
-// same order.
-template <int FMT> constexpr bool split_half_codes() { return FMT == QL_FMT_Q4_0 || FMT == QL_FMT_NF4; }
+// B-operand row (row 32 wave + lane % 32): one whole 32-element group per
+// step, group h = lane / 32 of the step's two, in one 16-byte load (32 for
+// FP8) with one scale, and dequantizes it straight into operand registers;
+// only the shared activation tile goes through LDS.  The order in which a dot
+// product runs over K is free, so slice ks of lane half h holds elements
+// 32 h + 8 ks .. 32 h + 8 ks + 7 of the step (the dequantizer's pieces of the
+// group in order, whatever the format's nibble layout), and the activation
+// fragment is read in the same order.
 template <bool TRANS> constexpr int split_b_elems() { return TRANS ? TK * (128 + 32) : 0; }
 
 // Launch arguments of a group: the problems and the first workgroup of each.
@@ -55,7 +53,6 @@ void qsplit_kernel(SplitArgs ga) {
   constexpr int GPR = TRANS ? TN / 32 : TK / 32;
   constexpr bool FP8 = FMT == QL_FMT_FP8_E4M3;
   constexpr bool DIRECT = !TRANS;                    // forward: W straight into operand registers
-  constexpr bool HALVES = split_half_codes<FMT>();
   static_assert(!DIRECT || TN == 4 * 32, "one 32-row W block per wave");
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
@@ -106,7 +103,7 @@ void qsplit_kernel(SplitArgs ga) {
     WGroup w;   // direct forward: c0 (c1 for FP8) = this lane's codes of both groups; sraw / ssh = their scales
     int kt;
   };
-  const int hsel = lane >> 5;                        // direct forward: which half of each group this lane holds
+  const int hsel = lane >> 5;                        // direct forward: which group of the step this lane holds
   Slot ring[D];
   // loads of step kt; a step past the split's end reads zeros (no memory traffic)
   auto issue = [&](Slot& sl, int kt) {
@@ -118,30 +115,21 @@ void qsplit_kernel(SplitArgs ga) {
     sl.kt = kt;
     if constexpr (DIRECT) {
       const int64_t wrow = 32 * wave + (lane & 31);  // W row, relative to the tile
-      const bool g0 = sv && c0 < p.C, g1 = sv && c0 + 32 < p.C;
+      const bool gl = sv && c0 + 32 * hsel < p.C;    // this lane's group lies inside K
       if constexpr (FP8) {
-        const uint32_t base = (uint32_t)(wrow * crow + c0 + 16 * hsel);
-        sl.w.c0 = bload16(rcode, g0 ? base : OOB);
-        sl.w.c1 = bload16(rcode, g1 ? base + 32 : OOB);
-        sl.w.sraw = sl.w.ssh = 0;
+        const uint32_t base = (uint32_t)(wrow * crow + c0 + 32 * hsel);
+        sl.w.c0 = bload16(rcode, gl ? base : OOB);
+        sl.w.c1 = bload16(rcode, gl ? base + 16 : OOB);
+        sl.w.sraw = 0;
       } else {
-        const uint32_t base = (uint32_t)(wrow * crow + c0 / 2 + 8 * hsel);
-        const uint2 q0 = bload8(rcode, g0 ? base : OOB);
-        const uint2 q1 = bload8(rcode, g1 ? base + 16 : OOB);
-        sl.w.c0 = make_uint4(q0.x, q0.y, q1.x, q1.y);
+        sl.w.c0 = bload16(rcode, gl ? (uint32_t)(wrow * crow + c0 / 2 + 16 * hsel) : OOB);
         sl.w.c1 = make_uint4(0, 0, 0, 0);
-        const int64_t idx = wrow * srow + (c0 >> 5);   // group 0's scale index (NF4: per 64, below)
-        if constexpr (FMT == QL_FMT_Q4_0) {
-          sl.w.sraw = bload2(rscale, g0 ? (uint32_t)(idx * 2) : OOB);
-          sl.w.ssh = bload2(rscale, g1 ? (uint32_t)(idx * 2 + 2) : OOB);
-        } else if constexpr (FMT == QL_FMT_MXFP4) {
-          sl.w.sraw = bload1(rscale, g0 ? (uint32_t)idx : OOB);
-          sl.w.ssh = bload1(rscale, g1 ? (uint32_t)(idx + 1) : OOB);
-        } else {
-          sl.w.sraw = bload4(rscale, g0 ? (uint32_t)((wrow * srow + (c0 >> 6)) * 4) : OOB);
-          sl.w.ssh = 0;
-        }
+        const int64_t idx = wrow * srow + (c0 >> 5) + hsel;   // the group's scale index (NF4: per 64, below)
+        if constexpr (FMT == QL_FMT_Q4_0) sl.w.sraw = bload2(rscale, gl ? (uint32_t)(idx * 2) : OOB);
+        else if constexpr (FMT == QL_FMT_MXFP4) sl.w.sraw = bload1(rscale, gl ? (uint32_t)idx : OOB);
+        else sl.w.sraw = bload4(rscale, gl ? (uint32_t)((wrow * srow + (c0 >> 6)) * 4) : OOB);
       }
+      sl.w.ssh = 0;
     } else {
     const int64_t wrow = TRANS ? c0 + wr : wr;
     const int64_t kgrp = TRANS ? wg : (c0 >> 5) + wg;
@@ -173,33 +161,19 @@ void qsplit_kernel(SplitArgs ga) {
     else doff = c0 + dcol < p.C ? (uint32_t)((drow * p.C + c0 + dcol) * 2) : OOB;
     sl.d = bload16(rdown, dload && sv ? doff : OOB);
   };
-  // direct forward: the lane's codes of a step -> its four B operands (slices ks = 0..3)
+  // direct forward: the lane's group of a step -> its four B operands (slices ks = 0..3)
   auto dequant_direct = [&](const Slot& sl, uint4* wb) {
     const int64_t c0 = (int64_t)sl.kt * TK;
-    const bool g0 = sl.kt < kend && c0 < p.C, g1 = sl.kt < kend && c0 + 32 < p.C;
-    float s0, s1;
-    if constexpr (FP8) s0 = s1 = tscale;
-    else if constexpr (FMT == QL_FMT_Q4_0) { s0 = decode_scale_q40(sl.w.sraw); s1 = decode_scale_q40(sl.w.ssh); }
-    else if constexpr (FMT == QL_FMT_MXFP4) { s0 = e8m0_as_scale(sl.w.sraw); s1 = e8m0_as_scale(sl.w.ssh); }
-    else s0 = s1 = __uint_as_float(sl.w.sraw);   // NF4: one block of 64 (K % 64 == 0, so g1 == g0)
-    constexpr int P1 = HALVES ? 2 : 1;             // piece holding a lane's second slice of a group
-    WGroup q;
-    q.c1 = make_uint4(0, 0, 0, 0);
-    q.sraw = q.ssh = 0;
+    const bool gl = sl.kt < kend && c0 + 32 * hsel < p.C;
+    float sc;
+    if constexpr (FP8) sc = tscale;
+    else if constexpr (FMT == QL_FMT_Q4_0) sc = decode_scale_q40(sl.w.sraw);
+    else if constexpr (FMT == QL_FMT_MXFP4) sc = e8m0_as_scale(sl.w.sraw);
+    else sc = __uint_as_float(sl.w.sraw);
     Deq<FMT> dq;
-    q.c0 = FP8 ? sl.w.c0 : make_uint4(sl.w.c0.x, sl.w.c0.y, 0, 0);
-    dq.prepare(q, g0 ? s0 : 0.0f, p.book, g0);
-    wb[0] = dq.piece(0);
-    wb[1] = dq.piece(P1);
-    if constexpr (FMT == QL_FMT_NF4) {
-      dq.wd[0] = sl.w.c0.z;                        // same block, same table
-      dq.wd[1] = sl.w.c0.w;
-    } else {
-      q.c0 = FP8 ? sl.w.c1 : make_uint4(sl.w.c0.z, sl.w.c0.w, 0, 0);
-      dq.prepare(q, g1 ? s1 : 0.0f, p.book, g1);
-    }
-    wb[2] = dq.piece(0);
-    wb[3] = dq.piece(P1);
+    dq.prepare(sl.w, gl ? sc : 0.0f, p.book, gl);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wb[i] = dq.piece(i);
   };
   auto store = [&](const Slot& sl, uint16_t* st, uint4* wb) {
     *reinterpret_cast<uint4*>(st + arow * SA + acol) = sl.a0;
@@ -249,8 +223,7 @@ void qsplit_kernel(SplitArgs ga) {
 #pragma unroll
     for (int ks = 0; ks < TK / 16; ++ks) {
       bf16x8 af[MBK], bf;
-      const int koff = (!DIRECT || HALVES) ? ks * 16 + 8 * (lane >> 5)
-                                           : 32 * (ks >> 1) + 16 * (lane >> 5) + 8 * (ks & 1);
+      const int koff = DIRECT ? 32 * (lane >> 5) + 8 * ks : ks * 16 + 8 * (lane >> 5);
 #pragma unroll
       for (int i = 0; i < MBK; ++i)
         af[i] = *reinterpret_cast<const bf16x8*>(As + (32 * i + (lane & 31)) * SA + koff);
