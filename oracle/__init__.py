@@ -10,9 +10,10 @@ What it holds, each written from the definition it cites:
 * ``codecs``  -- bf16 / fp16 / OCP E4M3FN encode and decode, value-based
   (round to nearest, ties to even), with no use of library casts.
 * ``formats`` -- the NF4 code book (QLoRA paper, "4-bit NormalFloat"
-  construction), and pack / dequant of the four base formats
+  construction), and pack / dequant of the five base formats
   (Q4_0-style blocks of 32, NF4 blocks of 64, per-tensor FP8 E4M3, MXFP4
-  blocks of 32 E2M1 codes with an E8M0 scale).
+  blocks of 32 E2M1 codes with an E8M0 scale, Q8_0-style blocks of 32 int8
+  codes with an fp16 scale).
 * ``lora``    -- forward and backward of y = x.W^T + (alpha/r).(x.A^T).B^T and
   the per-token two-term E4M3 split of activations for the FP8 base.
 * ``adamw``   -- one AdamW step (decoupled weight decay) on the adapters and

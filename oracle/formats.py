@@ -26,6 +26,15 @@ Surogate pages' NVFP4 (E2M1) recipes and MXFP4 checkpoints):
   quantization.
 * FP8: per-tensor fp32 scale s = absmax / 448, code = E4M3(w / s) with
   saturation; value E4M3(q) * s.  A zero tensor has s = 0 and codes 0.
+* Q8_0-style (the 8-bit member of the same legacy GGUF family; the plain
+  reading of "GGUF Q8_0", which the GGUF-recipe page names as a base but does
+  not define): block of 32, fp16 scale d = fp16(absmax / 127), code
+  q = clamp(rint(w / d), -127, 127) (ties to even), stored as a two's
+  complement byte, one per element (u8 [N, K]); value q * d, exact in fp32.
+  A zero block stores d = 0 and codes 0.  While d is a normal fp16 number
+  |w / d| <= 127 (1 + 2**-11), so the clamp acts only on blocks whose scale
+  rounded down to an fp16 subnormal; -128 is never written, and dequant still
+  accepts it.
 * MXFP4 (the OCP Microscaling definition, which the pages name but do not
   spell out): block of 32, one E8M0 scale byte e per block standing for
   X = 2**(e - 127); X = 2**(floor(log2 absmax) - 2), the exponent clamped to
@@ -42,8 +51,8 @@ import numpy as np
 
 from . import codecs
 
-FMT_Q4_0, FMT_NF4, FMT_FP8, FMT_MXFP4 = 1, 2, 3, 4
-BLOCK = {FMT_Q4_0: 32, FMT_NF4: 64, FMT_MXFP4: 32}
+FMT_Q4_0, FMT_NF4, FMT_FP8, FMT_MXFP4, FMT_Q8_0 = 1, 2, 3, 4, 5
+BLOCK = {FMT_Q4_0: 32, FMT_NF4: 64, FMT_MXFP4: 32, FMT_Q8_0: 32}
 
 
 # ----------------------------------------------------------------------------- NF4 book
@@ -162,6 +171,39 @@ def dequant_q4_0(codes, scales_fp16_bits):
     return w.reshape(n, k).astype(np.float32)
 
 
+# ----------------------------------------------------------------------------- Q8_0
+
+def pack_q8_0(w):
+    """fp32 W [N, K] -> (codes u8 [N, K] (int8 two's complement), scales fp16 bits u16 [N, K/32])."""
+    w = _check_w(w)
+    n, k = w.shape
+    if k % 32:
+        raise ValueError("K must be a multiple of 32")
+    blk = w.reshape(n, k // 32, 32)
+    amax = np.max(np.abs(blk), axis=2)                      # exact
+    d32 = (amax / np.float32(127.0)).astype(np.float32)     # IEEE fp32 divide
+    d_bits, over = codecs.fp16_encode(d32)
+    if np.any(over):
+        raise OverflowError("Q8_0 scale overflows fp16")
+    d = codecs.fp16_decode(d_bits)                          # the stored scale, as fp32
+    nz = d != 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = (blk / d[:, :, None]).astype(np.float32)    # IEEE fp32 divide
+    ratio = np.where(nz[:, :, None], ratio, np.float32(0.0))
+    q = np.clip(np.rint(ratio).astype(np.int64), -127, 127)
+    codes = q.reshape(n, k).astype(np.int8).view(np.uint8)
+    return codes, d_bits
+
+
+def dequant_q8_0(codes, scales_fp16_bits):
+    """(codes, fp16 scale bits) -> fp32 W [N, K]: q * d, exact in fp32."""
+    q = np.asarray(codes, dtype=np.uint8).view(np.int8).astype(np.float32)
+    n, k = q.shape
+    d = codecs.fp16_decode(scales_fp16_bits).astype(np.float32)
+    w = q.reshape(n, k // 32, 32) * d[:, :, None]
+    return w.reshape(n, k).astype(np.float32)
+
+
 # ----------------------------------------------------------------------------- NF4
 
 def pack_nf4(w, book=None):
@@ -257,6 +299,8 @@ def pack(fmt, w):
         return pack_fp8(w)
     if fmt == FMT_MXFP4:
         return pack_mxfp4(w)
+    if fmt == FMT_Q8_0:
+        return pack_q8_0(w)
     raise ValueError(f"unknown format {fmt}")
 
 
@@ -269,6 +313,8 @@ def dequant(fmt, codes, scales):
         return dequant_fp8(codes, scales)
     if fmt == FMT_MXFP4:
         return dequant_mxfp4(codes, scales)
+    if fmt == FMT_Q8_0:
+        return dequant_q8_0(codes, scales)
     raise ValueError(f"unknown format {fmt}")
 
 

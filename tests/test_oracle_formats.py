@@ -384,3 +384,97 @@ def test_mxfp4_error_bound_and_largest_element():
     q = formats.bytes_to_pairs(c).reshape(32, 16, 32) & 7
     top = np.argmax(np.abs(w).reshape(32, 16, 32), axis=2)
     assert np.all(np.take_along_axis(q, top[:, :, None], 2) >= 6)
+
+
+# ----------------------------------------------------------------------------- Q8_0
+
+def _read_q80_golden():
+    scale, vals, codes = None, [], []
+    for line in open(os.path.join(GOLDEN, "q8_0_block.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        if line.startswith("scale_fp16_bits"):
+            scale = int(line.split()[1], 16)
+            continue
+        _, v, c = line.split()
+        vals.append(np.float32(v))
+        codes.append(int(c, 16))
+    return np.array(vals, np.float32).reshape(1, 32), np.array(codes, np.uint8).reshape(1, 32), scale
+
+
+def test_q80_golden_block():
+    w, want, scale = _read_q80_golden()
+    codes, s = formats.pack_q8_0(w)
+    assert int(s[0, 0]) == scale
+    assert np.array_equal(codes, want)
+    d = codecs.fp16_decode(np.uint16(scale))
+    assert np.array_equal(formats.dequant_q8_0(codes, s), want.view(np.int8).astype(np.float32) * d)
+
+
+def test_q80_dequant_exhaustive_codes_and_scales():
+    """Every code byte against every finite fp16 scale: w / d == q exactly
+    (an 8-bit integer times an 11-bit significand is exact in fp32)."""
+    d_bits = np.arange(0, 0x7C00, dtype=np.uint16)
+    d_bits = np.concatenate([d_bits, d_bits | 0x8000])
+    n = d_bits.size
+    q = np.tile(np.arange(256, dtype=np.uint8), (1, 1))
+    for lo in range(0, n, 4096):
+        db = d_bits[lo:lo + 4096]
+        codes = np.tile(np.arange(256, dtype=np.uint8), (db.size, 1))[:, :256]
+        w = formats.dequant_q8_0(codes, np.repeat(db.reshape(-1, 1), 8, axis=1))
+        d = codecs.fp16_decode(db).astype(np.float64).reshape(-1, 1)
+        qv = codes.view(np.int8).astype(np.float64)
+        assert np.array_equal(w.astype(np.float64), qv * d)
+
+
+def test_q80_pack_is_nearest_with_ties_to_even():
+    """Against a brute-force search over all 255 codes of each element, given
+    the stored scale; equal distances go to the even code."""
+    g = np.random.default_rng(17)
+    w = (g.standard_normal((16, 256)) * 0.02).astype(np.float32)
+    w[3, :32] = (np.arange(32, dtype=np.float32) - 15.5) * np.float32(2.0 ** -7)   # half-integer ties
+    w[3, 0] = np.float32(127 * 2.0 ** -7)
+    codes, s = formats.pack_q8_0(w)
+    d = codecs.fp16_decode(s).astype(np.float64)
+    cand = np.arange(-127, 128, dtype=np.float64)
+    for i in range(w.shape[0]):
+        for b in range(w.shape[1] // 32):
+            blk = w[i, 32 * b:32 * b + 32].astype(np.float64)
+            ratio = (w[i, 32 * b:32 * b + 32] / np.float32(d[i, b])).astype(np.float32).astype(np.float64)
+            dist = np.abs(ratio[:, None] - cand[None, :])
+            best = dist.min(axis=1, keepdims=True)
+            ok = dist == best
+            pick = np.where(ok.sum(axis=1) > 1, cand[np.argmax(ok & (cand % 2 == 0), axis=1)], cand[np.argmax(ok, axis=1)])
+            got = codes[i, 32 * b:32 * b + 32].view(np.int8).astype(np.float64)
+            assert np.array_equal(got, pick), (i, b)
+            assert np.all(np.abs(blk - got * d[i, b]) <= d[i, b] / 2 * (1 + 1e-6))
+
+
+def test_q80_zero_tiny_and_subnormal_scale_blocks():
+    w = np.zeros((3, 64), np.float32)
+    w[1, :32] = np.float32(8.5e-8 * 127) * np.linspace(-1, 1, 32, dtype=np.float32)   # scale rounds down to 2^-24
+    w[2, 32:] = np.float32(1e-12)                                                       # scale rounds to 0
+    codes, s = formats.pack_q8_0(w)
+    assert np.all(s[0] == 0) and not codes[0].any()
+    assert int(s[1, 0]) == 0x0001                            # the smallest fp16 subnormal
+    q = codes[1, :32].view(np.int8)
+    assert q.max() == 127 and q.min() == -127                # the clamp acts here
+    assert int(s[2, 1]) == 0 and not codes[2, 32:].any()
+
+
+def test_q80_repack_is_idempotent():
+    g = np.random.default_rng(23)
+    w = (g.standard_normal((32, 512)) * 0.02).astype(np.float32)
+    c, s = formats.pack_q8_0(w)
+    c2, s2 = formats.pack_q8_0(formats.dequant_q8_0(c, s))
+    assert np.array_equal(c, c2) and np.array_equal(s, s2)
+
+
+def test_q80_scale_overflow_and_nonfinite():
+    with pytest.raises(OverflowError):
+        formats.pack_q8_0(np.full((1, 32), 1e7, np.float32))
+    w = np.zeros((1, 32), np.float32)
+    w[0, 3] = np.inf
+    with pytest.raises(ValueError):
+        formats.pack_q8_0(w)
