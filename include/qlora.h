@@ -90,11 +90,19 @@ extern "C" {
  *                  holds element 2i in its low nibble and element 2i + 1 in
  *                  its high nibble (u8 [N, K/2]).  e = 255 is never written
  *                  and decodes to NaN.
+ * QL_FMT_Q8_0      the 8-bit member of the legacy GGUF block family (the
+ *                  GGUF page's Q8_0 base, whose layout the page does not
+ *                  give): blocks of 32 along K, scales fp16 [N, K/32],
+ *                  d = fp16(absmax / 127), code q = clamp(rint(w/d), -127,
+ *                  127) (ties to even) stored as a two's complement byte, one
+ *                  per element (u8 [N, K]); value q * d; a zero block stores
+ *                  d = 0 and codes 0.
  */
 #define QL_FMT_Q4_0 1
 #define QL_FMT_NF4 2
 #define QL_FMT_FP8_E4M3 3
 #define QL_FMT_MXFP4 4
+#define QL_FMT_Q8_0 5
 
 /* workspace query operations */
 #define QL_OP_PACK 0
@@ -107,8 +115,9 @@ typedef struct ql_qweight {
   int32_t reserved;      /* must be 0                                       */
   int64_t n_out;         /* N                                               */
   int64_t k_in;          /* K                                               */
-  const uint8_t* codes;  /* Q4_0 / NF4 / MXFP4: u8 [N, K/2]; FP8: u8 [N, K] */
-  const void* scales;    /* Q4_0: fp16 [N, K/32]; NF4: fp32 [N, K/64];
+  const uint8_t* codes;  /* Q4_0 / NF4 / MXFP4: u8 [N, K/2]; FP8 / Q8_0:
+                            u8 [N, K]                                        */
+  const void* scales;    /* Q4_0 / Q8_0: fp16 [N, K/32]; NF4: fp32 [N, K/64];
                             FP8: fp32 [1]; MXFP4: u8 (E8M0) [N, K/32]        */
 } ql_qweight;
 
@@ -135,7 +144,7 @@ size_t qlora_workspace_bytes(int32_t op, int32_t format, int64_t n_out,
  * Once per weight, not per step.  Blocks until the packed data is written
  * (so that non-finite input can be reported): returns QL_ENONFINITE if W
  * holds NaN or Inf (codes and scales are then unspecified), QL_EOVERFLOW if
- * a Q4_0 scale would exceed the fp16 range.  ws: dev scratch of at least
+ * a Q4_0 or Q8_0 scale would exceed the fp16 range.  ws: dev scratch of at least
  * qlora_workspace_bytes(QL_OP_PACK, ...) bytes. */
 int quant_pack(int32_t format, const float* w, int64_t n_out, int64_t k_in,
                uint8_t* codes, void* scales, void* ws, size_t ws_bytes,

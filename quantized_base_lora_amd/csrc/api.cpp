@@ -42,7 +42,7 @@ int check_sticky() {
 }
 
 int check_shape(int32_t fmt, int64_t n, int64_t k) {
-  if (fmt != QL_FMT_Q4_0 && fmt != QL_FMT_NF4 && fmt != QL_FMT_FP8_E4M3 && fmt != QL_FMT_MXFP4)
+  if (fmt != QL_FMT_Q4_0 && fmt != QL_FMT_NF4 && fmt != QL_FMT_FP8_E4M3 && fmt != QL_FMT_MXFP4 && fmt != QL_FMT_Q8_0)
     return set_error(QL_EUNSUPPORTED, "unknown format %d", fmt);
   if (n <= 0 || k <= 0) return set_error(QL_EINVAL, "n_out and k_in must be positive");
   if (k % block_of(fmt)) return set_error(QL_EINVAL, "k_in=%lld is not a multiple of %d", (long long)k, block_of(fmt));
@@ -421,7 +421,7 @@ int quant_pack(int32_t format, const float* w, int64_t n_out, int64_t k_in, uint
     e = launch_pack_fp8(w, n_out, k_in, codes, reinterpret_cast<float*>(scales), st, s);
   } else {
     e = launch_zero_u32(st, 2, s);
-    if (e == hipSuccess) e = launch_pack_4bit(format, w, n_out, k_in, codes, scales, st + 1, s);
+    if (e == hipSuccess) e = launch_pack_blocks(format, w, n_out, k_in, codes, scales, st + 1, s);
   }
   if (e != hipSuccess) return hip_error(e, "quant_pack launch");
   QL_HIP(hipStreamSynchronize(s));
@@ -429,7 +429,7 @@ int quant_pack(int32_t format, const float* w, int64_t n_out, int64_t k_in, uint
   QL_HIP(hipMemcpy(flags, ws, sizeof flags, hipMemcpyDeviceToHost));
   uint32_t f = flags[1];
   if (f & 1u) return set_error(QL_ENONFINITE, "base weight holds NaN or Inf");
-  if (f & 2u) return set_error(QL_EOVERFLOW, "a Q4_0 block scale overflows fp16");
+  if (f & 2u) return set_error(QL_EOVERFLOW, "a block scale overflows fp16");
   return QL_OK;
 }
 

@@ -52,9 +52,10 @@ int hip_error(hipError_t e, const char* what);
 // All take already-validated arguments and enqueue on `stream`.
 
 // pack / dequant / activation split (kernels_pack.hip)
-hipError_t launch_pack_4bit(int fmt, const float* w, int64_t n, int64_t k,
-                            uint8_t* codes, void* scales, uint32_t* status,
-                            hipStream_t s);
+// block formats (Q4_0, NF4, MXFP4, Q8_0): one thread per 32-element group
+hipError_t launch_pack_blocks(int fmt, const float* w, int64_t n, int64_t k,
+                              uint8_t* codes, void* scales, uint32_t* status,
+                              hipStream_t s);
 hipError_t launch_pack_fp8(const float* w, int64_t n, int64_t k, uint8_t* codes,
                            float* scale, uint32_t* ws, hipStream_t s);
 hipError_t launch_dequant(const ql_qweight& w, float* out_f32, uint16_t* out_bf16,

@@ -23,7 +23,7 @@ struct Book { float c[16]; };
 // instruction right after a load has to wait for it.
 struct WGroup {
   uint4 c0, c1;      // 4-bit: c0 = 16 bytes; fp8: c0, c1 = 32 bytes
-  uint32_t sraw;     // Q4_0 / MXFP4: the dword holding the fp16 / E8M0 scale; NF4: fp32 bits; FP8: unused
+  uint32_t sraw;     // Q4_0, Q8_0 / MXFP4: the dword holding the fp16 / E8M0 scale; NF4: fp32 bits; FP8: unused
   uint32_t ssh;      // Q4_0: bit offset of the fp16 scale in sraw (0 or 16); MXFP4: 0, 8, 16 or 24
 };
 
@@ -52,8 +52,12 @@ __device__ __forceinline__ void nf4_lookup4(uint32_t q4, const uint32_t* tl, con
 // Scale words per row of W and bytes per scale, for the 4-bit formats.
 template <int FMT> constexpr int64_t scales_per_row(int64_t k) { return FMT == QL_FMT_NF4 ? k / 64 : k / 32; }
 template <int FMT> constexpr int64_t scale_bytes() {
-  return FMT == QL_FMT_Q4_0 ? 2 : (FMT == QL_FMT_MXFP4 ? 1 : 4);
+  return (FMT == QL_FMT_Q4_0 || FMT == QL_FMT_Q8_0) ? 2 : (FMT == QL_FMT_MXFP4 ? 1 : 4);
 }
+// formats with one code byte per element (a 32-element group is 32 bytes)
+template <int FMT> constexpr bool byte_codes() { return FMT == QL_FMT_FP8_E4M3 || FMT == QL_FMT_Q8_0; }
+// formats with an fp16 scale per 32-element group
+template <int FMT> constexpr bool fp16_scales() { return FMT == QL_FMT_Q4_0 || FMT == QL_FMT_Q8_0; }
 
 // Dequantizer of one 32-element group, split so its work can be spread over
 // the MFMAs of a contraction step: prepare() once per group (scale decode,
@@ -65,7 +69,7 @@ template <int FMT> constexpr int64_t scale_bytes() {
 template <int FMT> struct Deq {
   uint32_t wd[8];
   uint32_t tl[4], th[4];   // NF4: byte planes of the 16-entry bf16 table
-  float d, nd8;            // Q4_0: d and -8 d; FP8: the tensor scale in d
+  float d, nd8;            // Q4_0: d and -8 d; Q8_0: d and -128 d; FP8: the tensor scale in d
 
   __device__ __forceinline__ void prepare(const WGroup& g, float scale, const Book& book, bool in = true) {
     wd[0] = g.c0.x; wd[1] = g.c0.y; wd[2] = g.c0.z; wd[3] = g.c0.w;
@@ -76,7 +80,7 @@ template <int FMT> struct Deq {
       for (int i = 0; i < 4; ++i) wd[i] &= keep;
     }
     d = scale;
-    nd8 = -8.0f * scale;                 // (q - 8) d = fma(q, d, -8d), exact
+    nd8 = (FMT == QL_FMT_Q8_0 ? -128.0f : -8.0f) * scale;   // (q - 8) d = fma(q, d, -8d), exact
     if constexpr (FMT == QL_FMT_NF4) {
       // per-thread table of bf16_RNE(fl32(c[q] * a)), split into byte planes
       uint32_t pr[8];
@@ -97,6 +101,18 @@ template <int FMT> struct Deq {
       o[1] = fp4x2_to_bf16x2<1>(wd[i], d);
       o[2] = fp4x2_to_bf16x2<2>(wd[i], d);
       o[3] = fp4x2_to_bf16x2<3>(wd[i], d);
+    } else if constexpr (FMT == QL_FMT_Q8_0) {
+      // two's complement bytes biased to u = q + 128; u d - 128 d = q d exactly
+      // (an 8-bit integer times an 11-bit significand), rounded once to bf16
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t u = wd[2 * i + h] ^ 0x80808080u;
+        float e[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) e[b] = fmaf((float)((u >> (8 * b)) & 0xFF), d, nd8);
+        o[2 * h] = pack_bf16x2(e[0], e[1]);
+        o[2 * h + 1] = pack_bf16x2(e[2], e[3]);
+      }
     } else if constexpr (FMT == QL_FMT_FP8_E4M3) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {

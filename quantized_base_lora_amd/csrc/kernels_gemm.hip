@@ -84,6 +84,7 @@ void qgemm_kernel(Params p) {
   constexpr int MB = S::MB, NB = S::NB, WG = S::WG;
   constexpr int GPR = TRANS ? TN / 32 : TK / 32;     // W groups per W-tile row
   constexpr bool FP8 = FMT == QL_FMT_FP8_E4M3;
+  constexpr bool BYTES = byte_codes<FMT>();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -103,9 +104,9 @@ void qgemm_kernel(Params p) {
 
   // ---- buffer resources (bases rebased to this tile, so 32-bit offsets suffice)
   const __amdgpu_buffer_rsrc_t ract = rsrc(p.act + m0 * p.C, (p.M - m0) * p.C * 2);
-  const int64_t crow = FP8 ? p.K : p.K / 2;          // code bytes per row of W
+  const int64_t crow = BYTES ? p.K : p.K / 2;        // code bytes per row of W
   const int64_t wrow0 = TRANS ? 0 : o0;              // first W row this tile reads
-  const int64_t wcol0 = TRANS ? (FP8 ? o0 : o0 / 2) : 0;
+  const int64_t wcol0 = TRANS ? (BYTES ? o0 : o0 / 2) : 0;
   const __amdgpu_buffer_rsrc_t rcode = rsrc(p.codes + wrow0 * crow + wcol0, (p.N - wrow0) * crow - wcol0);
   const int64_t srow = scales_per_row<FMT>(p.K);   // scale words per row
   const int64_t ssz = scale_bytes<FMT>();
@@ -159,13 +160,12 @@ void qgemm_kernel(Params p) {
     // traffic): every path then has the same loads in flight and the
     // compiler's wait counts stay exact.
     const bool live = wtask && (TRANS || c0 + 32 * wg[j] < p.C);
-    const uint32_t coff = live ? (uint32_t)(wrow * crow + kgrp * (FP8 ? 32 : 16)) : OOB;
+    const uint32_t coff = live ? (uint32_t)(wrow * crow + kgrp * (BYTES ? 32 : 16)) : OOB;
     wreg[j].c0 = bload16(rcode, coff);
-    if constexpr (FP8) {
-      wreg[j].c1 = bload16(rcode, live ? coff + 16 : OOB);
-    } else {
+    if constexpr (BYTES) wreg[j].c1 = bload16(rcode, live ? coff + 16 : OOB);
+    if constexpr (!FP8) {
       const int64_t kabs = TRANS ? (o0 >> 5) + wg[j] : kgrp;   // group index along K
-      if constexpr (FMT == QL_FMT_Q4_0) {
+      if constexpr (fp16_scales<FMT>()) {
         const int64_t idx = wrow * srow + kabs;
         wreg[j].sraw = bload4(rscale, live ? (uint32_t)((idx * 2) & ~3LL) : OOB);
         wreg[j].ssh = (uint32_t)(idx & 1) * 16;
@@ -194,7 +194,7 @@ void qgemm_kernel(Params p) {
   auto prepare_w = [&](int j) {
     float scale;
     if constexpr (FP8) scale = tscale;
-    else if constexpr (FMT == QL_FMT_Q4_0) scale = decode_scale_q40(wreg[j].sraw >> wreg[j].ssh);
+    else if constexpr (fp16_scales<FMT>()) scale = decode_scale_q40(wreg[j].sraw >> wreg[j].ssh);
     else if constexpr (FMT == QL_FMT_MXFP4) scale = e8m0_as_scale(wreg[j].sraw >> wreg[j].ssh);
     else scale = __uint_as_float(wreg[j].sraw);
     deq.prepare(wreg[j], wg_in[j] ? scale : 0.0f, p.book, wg_in[j]);
@@ -669,6 +669,7 @@ hipError_t launch_qgemm(const GemmCall& c, hipStream_t s) {
     case QL_FMT_Q4_0: return launch_f<QL_FMT_Q4_0>(p, c.trans, c.r, s);
     case QL_FMT_NF4: return launch_f<QL_FMT_NF4>(p, c.trans, c.r, s);
     case QL_FMT_MXFP4: return launch_f<QL_FMT_MXFP4>(p, c.trans, c.r, s);
+    case QL_FMT_Q8_0: return launch_f<QL_FMT_Q8_0>(p, c.trans, c.r, s);
     default: return launch_f<QL_FMT_FP8_E4M3>(p, c.trans, c.r, s);
   }
 }

@@ -5,7 +5,9 @@
 // normal-quantile book (QLoRA paper, "4-bit NormalFloat"); per-tensor FP8
 // E4M3 with scale absmax/448 (the Surogate FP8 recipe's format); MXFP4
 // blocks of 32 E2M1 codes with an E8M0 power-of-two scale (OCP
-// Microscaling, the FP4 base of the Surogate pages' FP4 recipes).  Every
+// Microscaling, the FP4 base of the Surogate pages' FP4 recipes); Q8_0
+// blocks of 32 int8 codes with an fp16 scale absmax/127 (the 8-bit member
+// of the legacy GGUF family).  Every
 // quantization decision is taken in IEEE fp32 with correctly rounded
 // division and ties-to-even rounding, so codes are reproducible bit for bit.
 //
@@ -99,9 +101,10 @@ __device__ __forceinline__ uint32_t e2m1_code(float t, uint32_t sign) {
   return c | (sign << 3);
 }
 
-// ------------------------------------------------------------------ 4-bit pack
-// One thread per 32-element group of a row (16 output bytes).  For NF4 two
-// neighbouring threads share a 64-element block and exchange their maxima.
+// ------------------------------------------------------------------ block pack
+// One thread per 32-element group of a row (16 output bytes; 32 for Q8_0).
+// For NF4 two neighbouring threads share a 64-element block and exchange
+// their maxima.
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void pack4_kernel(const float* __restrict__ w, int64_t groups,
                                                          uint8_t* __restrict__ codes,
@@ -141,6 +144,16 @@ __global__ __launch_bounds__(kThreads) void pack4_kernel(const float* __restrict
       q[i] = (uint32_t)t;
     }
     if (valid) reinterpret_cast<uint16_t*>(scales)[gid] = d16;
+  } else if (FMT == QL_FMT_Q8_0) {
+    uint16_t d16 = f32_to_f16(fdiv_rn(amax, 127.0f), &ovf);
+    float d = f16_to_f32(d16);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float t = (d == 0.0f) ? 0.0f : rintf(fdiv_rn(v[i], d));
+      t = fminf(fmaxf(t, -127.0f), 127.0f);
+      q[i] = (uint32_t)(int32_t)t & 0xFFu;           // two's complement byte
+    }
+    if (valid) reinterpret_cast<uint16_t*>(scales)[gid] = d16;
   } else if (FMT == QL_FMT_MXFP4) {
     // block exponent floor(log2 amax) - 2, so the block's largest magnitude
     // lands in [4, 8) (2 is E2M1's largest exponent); clamped to [-127, 127];
@@ -166,7 +179,16 @@ __global__ __launch_bounds__(kThreads) void pack4_kernel(const float* __restrict
     }
     if (valid && (gid & 1) == 0) reinterpret_cast<float*>(scales)[gid >> 1] = amax;
   }
-  if (valid) {
+  if (valid && FMT == QL_FMT_Q8_0) {
+    uint32_t word[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) word[i] = q[4 * i] | (q[4 * i + 1] << 8) | (q[4 * i + 2] << 16) | (q[4 * i + 3] << 24);
+    uint4* dst = reinterpret_cast<uint4*>(codes + gid * 32);
+    dst[0] = make_uint4(word[0], word[1], word[2], word[3]);
+    dst[1] = make_uint4(word[4], word[5], word[6], word[7]);
+    if (bad) atomicOr(status, 1u);
+    if (ovf) atomicOr(status, 2u);
+  } else if (valid) {
     uint32_t word[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -257,6 +279,16 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
       uint32_t wd[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[16 * h + i] = e4m3_to_f32((wd[i / 4] >> (8 * (i % 4))) & 0xFF) * s;
+    }
+  } else if (FMT == QL_FMT_Q8_0) {
+    const float d = f16_to_f32(reinterpret_cast<const uint16_t*>(scales)[gid]);
+    const uint4* src = reinterpret_cast<const uint4*>(codes + gid * 32);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint4 t = src[h];
+      uint32_t wd[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[16 * h + i] = (float)(int8_t)((wd[i / 4] >> (8 * (i % 4))) & 0xFF) * d;
     }
   } else if (FMT == QL_FMT_MXFP4) {
     // the conversion the GEMMs use; its bf16 results are exact, so fp32 is the same value
@@ -449,8 +481,8 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t s
 
 hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s) { return launch_fill_u32(p, n, 0u, s); }
 
-hipError_t launch_pack_4bit(int fmt, const float* w, int64_t n, int64_t k, uint8_t* codes,
-                            void* scales, uint32_t* status, hipStream_t s) {
+hipError_t launch_pack_blocks(int fmt, const float* w, int64_t n, int64_t k, uint8_t* codes,
+                              void* scales, uint32_t* status, hipStream_t s) {
   int64_t groups = n * (k / 32);
   Mids mids{};
   const Nf4Table& t = nf4_table();
@@ -460,6 +492,9 @@ hipError_t launch_pack_4bit(int fmt, const float* w, int64_t n, int64_t k, uint8
                        groups, codes, scales, status, mids);
   else if (fmt == QL_FMT_MXFP4)
     hipLaunchKernelGGL(pack4_kernel<QL_FMT_MXFP4>, dim3(grid_for(groups)), dim3(kThreads), 0, s, w,
+                       groups, codes, scales, status, mids);
+  else if (fmt == QL_FMT_Q8_0)
+    hipLaunchKernelGGL(pack4_kernel<QL_FMT_Q8_0>, dim3(grid_for(groups)), dim3(kThreads), 0, s, w,
                        groups, codes, scales, status, mids);
   else
     hipLaunchKernelGGL(pack4_kernel<QL_FMT_NF4>, dim3(grid_for(groups)), dim3(kThreads), 0, s, w,
@@ -498,6 +533,10 @@ hipError_t launch_dequant(const ql_qweight& w, float* out_f32, uint16_t* out_bf1
       break;
     case QL_FMT_MXFP4:
       hipLaunchKernelGGL(dequant_kernel<QL_FMT_MXFP4>, dim3(grid_for(groups)), dim3(kThreads), 0, s,
+                         w.codes, w.scales, groups, w.k_in, out_f32, out_bf16, lv);
+      break;
+    case QL_FMT_Q8_0:
+      hipLaunchKernelGGL(dequant_kernel<QL_FMT_Q8_0>, dim3(grid_for(groups)), dim3(kThreads), 0, s,
                          w.codes, w.scales, groups, w.k_in, out_f32, out_bf16, lv);
       break;
     default:

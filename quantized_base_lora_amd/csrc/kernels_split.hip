@@ -52,6 +52,7 @@ void qsplit_kernel(SplitArgs ga) {
   constexpr int RB = (R + 15) / 16;
   constexpr int GPR = TRANS ? TN / 32 : TK / 32;
   constexpr bool FP8 = FMT == QL_FMT_FP8_E4M3;
+  constexpr bool BYTES = byte_codes<FMT>();
   constexpr bool DIRECT = !TRANS;                    // forward: W straight into operand registers
   static_assert(!DIRECT || TN == 4 * 32, "one 32-row W block per wave");
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
@@ -76,9 +77,9 @@ void qsplit_kernel(SplitArgs ga) {
   const int NKT = kend - kbeg;
 
   const __amdgpu_buffer_rsrc_t ract = rsrc(p.act, p.M * p.C * 2);
-  const int64_t crow = FP8 ? p.K : p.K / 2;
+  const int64_t crow = BYTES ? p.K : p.K / 2;
   const int64_t wrow0 = TRANS ? 0 : o0;
-  const int64_t wcol0 = TRANS ? (FP8 ? o0 : o0 / 2) : 0;
+  const int64_t wcol0 = TRANS ? (BYTES ? o0 : o0 / 2) : 0;
   const __amdgpu_buffer_rsrc_t rcode = rsrc(p.codes + wrow0 * crow + wcol0, (p.N - wrow0) * crow - wcol0);
   const int64_t srow = scales_per_row<FMT>(p.K);
   const int64_t ssz = scale_bytes<FMT>();
@@ -116,11 +117,12 @@ void qsplit_kernel(SplitArgs ga) {
     if constexpr (DIRECT) {
       const int64_t wrow = 32 * wave + (lane & 31);  // W row, relative to the tile
       const bool gl = sv && c0 + 32 * hsel < p.C;    // this lane's group lies inside K
-      if constexpr (FP8) {
+      if constexpr (BYTES) {
         const uint32_t base = (uint32_t)(wrow * crow + c0 + 32 * hsel);
         sl.w.c0 = bload16(rcode, gl ? base : OOB);
         sl.w.c1 = bload16(rcode, gl ? base + 16 : OOB);
-        sl.w.sraw = 0;
+        const int64_t idx = wrow * srow + (c0 >> 5) + hsel;
+        sl.w.sraw = FP8 ? 0u : bload2(rscale, gl ? (uint32_t)(idx * 2) : OOB);
       } else {
         sl.w.c0 = bload16(rcode, gl ? (uint32_t)(wrow * crow + c0 / 2 + 16 * hsel) : OOB);
         sl.w.c1 = make_uint4(0, 0, 0, 0);
@@ -134,16 +136,15 @@ void qsplit_kernel(SplitArgs ga) {
     const int64_t wrow = TRANS ? c0 + wr : wr;
     const int64_t kgrp = TRANS ? wg : (c0 >> 5) + wg;
     const bool wlive = sv && (TRANS || c0 + 32 * wg < p.C);
-    const uint32_t coff = wlive ? (uint32_t)(wrow * crow + kgrp * (FP8 ? 32 : 16)) : OOB;
+    const uint32_t coff = wlive ? (uint32_t)(wrow * crow + kgrp * (BYTES ? 32 : 16)) : OOB;
     sl.w.c0 = bload16(rcode, coff);
     sl.w.ssh = 0;
+    sl.w.c1 = BYTES ? bload16(rcode, wlive ? coff + 16 : OOB) : make_uint4(0, 0, 0, 0);
     if constexpr (FP8) {
-      sl.w.c1 = bload16(rcode, wlive ? coff + 16 : OOB);
       sl.w.sraw = 0;
     } else {
-      sl.w.c1 = make_uint4(0, 0, 0, 0);
       const int64_t kabs = TRANS ? (o0 >> 5) + wg : kgrp;
-      if constexpr (FMT == QL_FMT_Q4_0) {
+      if constexpr (fp16_scales<FMT>()) {
         const int64_t idx = wrow * srow + kabs;
         sl.w.sraw = bload4(rscale, wlive ? (uint32_t)((idx * 2) & ~3LL) : OOB);
         sl.w.ssh = (uint32_t)(idx & 1) * 16;
@@ -167,7 +168,7 @@ void qsplit_kernel(SplitArgs ga) {
     const bool gl = sl.kt < kend && c0 + 32 * hsel < p.C;
     float sc;
     if constexpr (FP8) sc = tscale;
-    else if constexpr (FMT == QL_FMT_Q4_0) sc = decode_scale_q40(sl.w.sraw);
+    else if constexpr (fp16_scales<FMT>()) sc = decode_scale_q40(sl.w.sraw);
     else if constexpr (FMT == QL_FMT_MXFP4) sc = e8m0_as_scale(sl.w.sraw);
     else sc = __uint_as_float(sl.w.sraw);
     Deq<FMT> dq;
@@ -185,7 +186,7 @@ void qsplit_kernel(SplitArgs ga) {
     }
     float scale;
     if constexpr (FP8) scale = tscale;
-    else if constexpr (FMT == QL_FMT_Q4_0) scale = decode_scale_q40(sl.w.sraw >> sl.w.ssh);
+    else if constexpr (fp16_scales<FMT>()) scale = decode_scale_q40(sl.w.sraw >> sl.w.ssh);
     else if constexpr (FMT == QL_FMT_MXFP4) scale = e8m0_as_scale(sl.w.sraw >> sl.w.ssh);
     else scale = __uint_as_float(sl.w.sraw);
     Deq<FMT> dq;
@@ -695,6 +696,7 @@ hipError_t launch_split_path(int fmt, bool trans, int r, const SplitGroup& g, co
     case QL_FMT_Q4_0: return trans ? launch_r<QL_FMT_Q4_0, true>(g, r, gf, s) : launch_r<QL_FMT_Q4_0, false>(g, r, gf, s);
     case QL_FMT_NF4: return trans ? launch_r<QL_FMT_NF4, true>(g, r, gf, s) : launch_r<QL_FMT_NF4, false>(g, r, gf, s);
     case QL_FMT_MXFP4: return trans ? launch_r<QL_FMT_MXFP4, true>(g, r, gf, s) : launch_r<QL_FMT_MXFP4, false>(g, r, gf, s);
+    case QL_FMT_Q8_0: return trans ? launch_r<QL_FMT_Q8_0, true>(g, r, gf, s) : launch_r<QL_FMT_Q8_0, false>(g, r, gf, s);
     default: return trans ? launch_r<QL_FMT_FP8_E4M3, true>(g, r, gf, s) : launch_r<QL_FMT_FP8_E4M3, false>(g, r, gf, s);
   }
 }

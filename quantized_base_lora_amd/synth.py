@@ -21,7 +21,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-FMT_Q4_0, FMT_NF4, FMT_FP8, FMT_MXFP4 = 1, 2, 3, 4
+FMT_Q4_0, FMT_NF4, FMT_FP8, FMT_MXFP4, FMT_Q8_0 = 1, 2, 3, 4, 5
 TID_W, TID_A, TID_B, TID_X, TID_DY = 0, 1, 2, 3, 4
 
 
@@ -79,6 +79,9 @@ WORKLOADS = {
     "llama3.1_8b_mxfp4": Workload(5, "llama3.1_8b_mxfp4", FMT_MXFP4, LLAMA31_8B, 4096, 16, 16.0,
                                   "Llama-3.1-8B decoder layer, MXFP4 base (E2M1, E8M0 per 32)",
                                   extra_m=(16, 64)),
+    "llama3.1_8b_q8_0": Workload(6, "llama3.1_8b_q8_0", FMT_Q8_0, LLAMA31_8B, 4096, 16, 16.0,
+                                 "Llama-3.1-8B decoder layer, Q8_0-style base (int8, fp16 per 32)",
+                                 extra_m=(16, 64)),
 }
 
 

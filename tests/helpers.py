@@ -37,7 +37,7 @@ def oracle_packed(fmt, w):
 
 def scales_bytes(fmt, s):
     """Oracle scales as raw bytes in the library's layout."""
-    if fmt == ofmt.FMT_Q4_0:
+    if fmt in (ofmt.FMT_Q4_0, ofmt.FMT_Q8_0):
         return np.ascontiguousarray(s, dtype=np.uint16).view(np.uint8).ravel()
     if fmt == ofmt.FMT_NF4:
         return np.ascontiguousarray(s, dtype=np.float32).view(np.uint8).ravel()

@@ -17,8 +17,8 @@ from quantized_base_lora_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [ofmt.FMT_Q4_0, ofmt.FMT_NF4, ofmt.FMT_FP8, ofmt.FMT_MXFP4]
-FNAME = {1: "q4_0", 2: "nf4", 3: "fp8", 4: "mxfp4"}
+FMTS = [ofmt.FMT_Q4_0, ofmt.FMT_NF4, ofmt.FMT_FP8, ofmt.FMT_MXFP4, ofmt.FMT_Q8_0]
+FNAME = {1: "q4_0", 2: "nf4", 3: "fp8", 4: "mxfp4", 5: "q8_0"}
 
 
 def say(*a):
@@ -63,6 +63,12 @@ def special_weight(fmt, n, k, seed):
         w[3, :32] = 0
         w[3, :4] = np.float32([0.5, 1.0, 3.0, 6.0]) * np.float32(2.0 ** -64) * np.float32(2.0 ** -63)
         w[5, :32] = np.float32(1e30) * g.standard_normal(32, dtype=np.float32)
+    elif fmt == ofmt.FMT_Q8_0:
+        # scale exactly 2^-7: rounding ties on half-integers of d in both signs
+        w[2, :32] = (np.arange(32, dtype=np.float32) - 15.5) * np.float32(2.0 ** -7)
+        w[2, 0] = np.float32(127 * 2.0 ** -7)
+        # a scale that rounds down to the smallest fp16 subnormal: the clamp acts
+        w[3, :32] = np.float32(8.5e-8 * 127) * np.linspace(-1, 1, 32, dtype=np.float32)
     w[4, :blk] = np.float32(0.01)
     return w
 
@@ -95,11 +101,12 @@ def test_pack_rejects_nonfinite(lib, fmt):
         assert e.value.code == B.QL_ENONFINITE
 
 
-def test_pack_q40_scale_overflow(lib):
+@pytest.mark.parametrize("fmt,big", [(ofmt.FMT_Q4_0, 1e6), (ofmt.FMT_Q8_0, 1e7)])
+def test_pack_fp16_scale_overflow(lib, fmt, big):
     from quantized_base_lora_amd import binding as B
-    w = np.full((32, 32), 1e6, np.float32)
+    w = np.full((32, 32), big, np.float32)
     with pytest.raises(B.QLError) as e:
-        pack_gpu(lib, ofmt.FMT_Q4_0, w)
+        pack_gpu(lib, fmt, w)
     assert e.value.code == B.QL_EOVERFLOW
 
 
@@ -124,6 +131,7 @@ def test_dequant_all_codes_and_scales(lib):
     d_bits = np.unique(np.concatenate([np.arange(0, 0x7C00, 61), [0x0001, 0x03FF, 0x0400, 0x7BFF]])).astype(np.uint16)
     n = (d_bits.size + 31) // 32 * 32
     d_bits = np.resize(d_bits, n)
+    d_bits_q40 = d_bits
     q = np.tile(np.arange(16, dtype=np.uint8), (n, 2))
     codes = ofmt.nibbles_to_bytes(q)
     qw = B.QWeight(B.FMT_Q4_0, n, 32, torch.from_numpy(codes).cuda(),
@@ -141,6 +149,15 @@ def test_dequant_all_codes_and_scales(lib):
     qw = B.QWeight(B.FMT_NF4, n, 64, torch.from_numpy(codes).cuda(), torch.from_numpy(sc).cuda())
     f, b = B.dequant(qw)
     ref = ofmt.dequant_nf4(codes, sc)
+    assert np.array_equal(f.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(H.bf16_tensor_bits(b), codecs.bf16_encode(ref))
+    # Q8_0: all 256 code bytes against the same fp16 scale grid as Q4_0
+    n = d_bits_q40.size
+    codes = np.tile(np.arange(256, dtype=np.uint8), (n, 1))
+    qw = B.QWeight(B.FMT_Q8_0, n, 256, torch.from_numpy(codes).cuda(),
+                   torch.from_numpy(np.repeat(d_bits_q40.view(np.int16).reshape(n, 1), 8, axis=1).copy()).cuda())
+    f, b = B.dequant(qw)
+    ref = ofmt.dequant_q8_0(codes, np.repeat(d_bits_q40.reshape(n, 1), 8, axis=1))
     assert np.array_equal(f.cpu().numpy().view(np.uint32), ref.view(np.uint32))
     assert np.array_equal(H.bf16_tensor_bits(b), codecs.bf16_encode(ref))
     # MXFP4: all 16 codes against every E8M0 scale byte (255 is NaN)
@@ -235,6 +252,11 @@ CASES = [
     ("small_mxfp4_m64_r8", ofmt.FMT_MXFP4, 64, 512, 384, 8, 16.0),
     ("small_mxfp4_m33", ofmt.FMT_MXFP4, 33, 1056, 224, 16, 32.0),
     ("small_mxfp4_m17_r32", ofmt.FMT_MXFP4, 17, 2048, 320, 32, 64.0),
+    # Q8_0 base (int8 codes, fp16 scale per 32): tiles with ragged edges, split path
+    ("q80_ragged_mnk", ofmt.FMT_Q8_0, 300, 352, 160, 16, 32.0),
+    ("q80_tiles_r8", ofmt.FMT_Q8_0, 520, 1024, 416, 8, 16.0),
+    ("small_q80_m64_r32", ofmt.FMT_Q8_0, 64, 1056, 224, 32, 64.0),
+    ("small_q80_m20", ofmt.FMT_Q8_0, 20, 2048, 320, 16, 32.0),
 ]
 
 
@@ -361,6 +383,7 @@ DET_CASES = [
     ("fp8_m300_fp8_mfma", ofmt.FMT_FP8, 300, 256, 512, 16),
     ("mxfp4_m640", ofmt.FMT_MXFP4, 640, 512, 768, 16),
     ("mxfp4_m24_fused_grads", ofmt.FMT_MXFP4, 24, 768, 256, 16),
+    ("q80_m640", ofmt.FMT_Q8_0, 640, 512, 768, 16),
 ]
 
 
@@ -390,7 +413,7 @@ def test_deterministic_and_base_untouched(lib, case):
 # ----------------------------------------------------------------------------- full-size, sampled
 
 FULL = []
-for wname in ("qwen3_0.6b_nf4", "llama3.1_8b_nf4", "qwen3_8b_fp8", "llama3.1_8b_mxfp4"):
+for wname in ("qwen3_0.6b_nf4", "llama3.1_8b_nf4", "qwen3_8b_fp8", "llama3.1_8b_mxfp4", "llama3.1_8b_q8_0"):
     wl = synth.WORKLOADS[wname]
     for pi, p in enumerate(wl.projs):
         FULL.append((wname, pi, wl.m))
