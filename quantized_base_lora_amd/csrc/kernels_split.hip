@@ -325,6 +325,253 @@ void qsplit_kernel(SplitArgs ga) {
   }
 }
 
+// Forward with at most 16 tokens: 16x16x32 MFMAs (no rows spent on absent
+// tokens) over contraction steps of 128.  The tile is 16 tokens x 128
+// columns; wave w owns columns 32 w .. 32 w + 31 as two 16-column blocks.
+// Lane l feeds row l % 16 of each block with group l / 16 (32 elements, one
+// 16-byte load for 4-bit codes) of the step, so a load instruction covers 16
+// W rows with 64 contiguous bytes each; slice s of the MFMA takes pieces s of
+// those groups, i.e. elements 32 (l / 16) + 8 s .. + 7 of the step, and the
+// activation fragment is read in the same order.  Split and reduction as in
+// qsplit_kernel (steps counted in 128s: sps = this kernel's steps per split).
+constexpr int TK2 = 128;
+constexpr int SA2 = TK2 + 8;                        // 272-byte rows
+
+template <int FMT, int R>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void qsplit16_kernel(SplitArgs ga) {
+  constexpr int TN = 128, NT = 256, D = 4;
+  constexpr int A_EL = 16 * SA2;
+  constexpr int D_EL = 32 * SA2;                    // adapter A rows j < R (the rest stay zero)
+  constexpr int STAGE = A_EL + D_EL;
+  constexpr int RB = (R + 15) / 16;
+  constexpr int DPT = (R * TK2 / 8 + NT - 1) / NT;  // 16-byte adapter pieces per thread
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bid = (int)blockIdx.x;
+  int pi = 0;
+  while (pi + 1 < ga.n && bid >= ga.unit0[pi + 1]) ++pi;
+  const Params& p = ga.p[pi];
+  const int u0 = ga.unit0[pi], nunits = ga.unit0[pi + 1] - u0, nt = ga.ntiles[pi];
+  int unit = bid - u0;
+  if ((nunits & 7) == 0 && (u0 & 7) == 0) unit = (unit & 7) * (nunits >> 3) + (unit >> 3);
+  const int ntile = unit % nt, split = unit / nt;
+  const int64_t o0 = (int64_t)ntile * TN;
+  const int KT = (int)((p.C + TK2 - 1) / TK2);
+  const int kbeg = split * p.sps;
+  const int kend = min(KT, kbeg + p.sps);
+  const int NKT = kend - kbeg;
+
+  const __amdgpu_buffer_rsrc_t ract = rsrc(p.act, p.M * p.C * 2);
+  const int64_t crow = p.K / 2;                     // 4-bit codes
+  const __amdgpu_buffer_rsrc_t rcode = rsrc(p.codes + o0 * crow, (p.N - o0) * crow);
+  const int64_t srow = scales_per_row<FMT>(p.K);
+  const int64_t ssz = scale_bytes<FMT>();
+  const __amdgpu_buffer_rsrc_t rscale = rsrc((const char*)p.scales + o0 * srow * ssz, (p.N - o0) * srow * ssz);
+  const __amdgpu_buffer_rsrc_t rdown = rsrc(p.down, (int64_t)R * p.C * 2);
+
+  const int arow = tid >> 4, acol = (tid & 15) * 8;  // activation: one 16-byte piece per thread
+  const int q = lane >> 4;                           // this lane's group of the step
+  const bool rank_tile = ntile == 0;
+
+  struct Slot {
+    uint4 a, d[DPT];
+    WGroup w[2];                                     // the lane's group of block 0 and block 1
+    int kt;
+  };
+  Slot ring[D];
+  auto issue = [&](Slot& sl, int kt) {
+    const bool sv = kt < kend;
+    const int64_t c0 = (int64_t)kt * TK2;
+    sl.kt = kt;
+    sl.a = bload16(ract, sv && arow < p.M && c0 + acol < p.C ? (uint32_t)((arow * p.C + c0 + acol) * 2) : OOB);
+    const bool gl = sv && c0 + 32 * q < p.C;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t wrow = 32 * wave + 16 * b + (lane & 15);   // W row, relative to the tile
+      sl.w[b].c0 = bload16(rcode, gl ? (uint32_t)(wrow * crow + c0 / 2 + 16 * q) : OOB);
+      sl.w[b].c1 = make_uint4(0, 0, 0, 0);
+      const int64_t idx = wrow * srow + (c0 >> 5) + q;
+      if constexpr (fp16_scales<FMT>()) sl.w[b].sraw = bload2(rscale, gl ? (uint32_t)(idx * 2) : OOB);
+      else if constexpr (FMT == QL_FMT_MXFP4) sl.w[b].sraw = bload1(rscale, gl ? (uint32_t)idx : OOB);
+      else sl.w[b].sraw = bload4(rscale, gl ? (uint32_t)((wrow * srow + ((c0 + 32 * q) >> 6)) * 4) : OOB);
+      sl.w[b].ssh = 0;
+    }
+#pragma unroll
+    for (int t = 0; t < DPT; ++t) {
+      const int pc = tid + NT * t, j = pc / (TK2 / 8), c = (pc % (TK2 / 8)) * 8;
+      const bool live = rank_tile && sv && pc < R * (TK2 / 8) && c0 + c < p.C;
+      sl.d[t] = bload16(rdown, live ? (uint32_t)((j * p.C + c0 + c) * 2) : OOB);
+    }
+  };
+  // the lane's two groups of a step -> B operands wb[block][slice]
+  auto store = [&](const Slot& sl, uint16_t* st, uint4 (*wb)[4]) {
+    *reinterpret_cast<uint4*>(st + arow * SA2 + acol) = sl.a;
+    if (rank_tile) {
+#pragma unroll
+      for (int t = 0; t < DPT; ++t) {
+        const int pc = tid + NT * t, j = pc / (TK2 / 8), c = (pc % (TK2 / 8)) * 8;
+        if (pc < R * (TK2 / 8)) *reinterpret_cast<uint4*>(st + A_EL + j * SA2 + c) = sl.d[t];
+      }
+    }
+    const bool gl = sl.kt < kend && (int64_t)sl.kt * TK2 + 32 * q < p.C;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float sc;
+      if constexpr (fp16_scales<FMT>()) sc = decode_scale_q40(sl.w[b].sraw);
+      else if constexpr (FMT == QL_FMT_MXFP4) sc = e8m0_as_scale(sl.w[b].sraw);
+      else sc = __uint_as_float(sl.w[b].sraw);
+      Deq<FMT> dq;
+      dq.prepare(sl.w[b], gl ? sc : 0.0f, p.book, gl);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wb[b][i] = dq.piece(i);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    ring[u].a = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < DPT; ++t) ring[u].d[t] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      ring[u].w[b].c0 = ring[u].w[b].c1 = make_uint4(0, 0, 0, 0);
+      ring[u].w[b].sraw = ring[u].w[b].ssh = 0;
+    }
+    ring[u].kt = 0;
+  }
+  uint4 wbuf[2][2][4];                               // B operands of two steps
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wbuf[h][b][i] = make_uint4(0, 0, 0, 0);
+
+  f32x4 acc[2], uacc[RB];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int jb = 0; jb < RB; ++jb) uacc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const uint16_t* st, uint4 (*wb)[4]) {
+    const uint16_t* As = st;
+    const uint16_t* Ds = st + A_EL;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(As + (lane & 15) * SA2 + 32 * q + 8 * sl);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wb[b][sl]), af, acc[b], 0, 0, 0);
+    }
+    // rank-r projection of the 16 tokens over this step (column tile 0, wave 0)
+    if (!rank_tile || wave != 0) return;
+#pragma unroll
+    for (int kp = 0; kp < TK2 / 32; ++kp) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(As + (lane & 15) * SA2 + 32 * kp + 8 * q);
+#pragma unroll
+      for (int jb = 0; jb < RB; ++jb) {
+        const bf16x8 bd = *reinterpret_cast<const bf16x8*>(Ds + (16 * jb + (lane & 15)) * SA2 + 32 * kp + 8 * q);
+        uacc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bd, uacc[jb], 0, 0, 0);
+      }
+    }
+  };
+
+  for (int i = tid; i < STAGE; i += NT) {
+    smem[i] = 0;
+    smem[STAGE + i] = 0;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int u = 0; u < D; ++u) issue(ring[u], kbeg + u);
+  store(ring[0], smem, wbuf[0]);
+  issue(ring[0], kbeg + D);
+  lds_barrier();
+
+  int it = 0;
+  for (; it + D < NKT; it += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      store(ring[(u + 1) % D], smem + ((u + 1) & 1) * STAGE, wbuf[(u + 1) & 1]);
+      issue(ring[(u + 1) % D], kbeg + it + u + 1 + D);
+      compute(smem + (u & 1) * STAGE, wbuf[u & 1]);
+      lds_barrier();
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    if (it + u < NKT) {
+      if (it + u + 1 < NKT) store(ring[(u + 1) % D], smem + ((u + 1) & 1) * STAGE, wbuf[(u + 1) & 1]);
+      compute(smem + (u & 1) * STAGE, wbuf[u & 1]);
+      lds_barrier();
+    }
+  }
+
+  mfma_result_guard();
+  // fp32 partials: lane holds token lane % 16 and 4 consecutive columns of each block
+  float* pp = p.part + (int64_t)split * p.M * p.O;
+  const int64_t m = lane & 15;
+  if (m < p.M) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t col = o0 + 32 * wave + 16 * b + 4 * q;
+      if (col < p.O) *reinterpret_cast<float4*>(pp + m * p.O + col) = make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+    }
+  }
+  if (rank_tile && wave == 0) {
+    float* up = p.upart + (int64_t)split * p.M * R;
+#pragma unroll
+    for (int jb = 0; jb < RB; ++jb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 4 * q + e;
+        const int j = 16 * jb + (lane & 15);
+        if (j < R && row < p.M) up[row * R + j] = uacc[jb][e];
+      }
+  }
+}
+
+// steps of 128 per split for the 16-token kernel, from the 64-step plan (never
+// more splits than the plan's, so its workspace suffices); 0 if unsuited
+inline int split16_plan(const Params& p, int splits, int& sps2) {
+  const int KT = (int)((p.C + TK - 1) / TK);
+  const int sps = (KT + splits - 1) / splits;
+  sps2 = (sps + 1) / 2;
+  const int KT2 = (int)((p.C + TK2 - 1) / TK2);
+  const int s2 = (KT2 + sps2 - 1) / sps2;
+  return s2 <= splits ? s2 : 0;
+}
+
+template <int FMT, int R>
+hipError_t launch_split16(SplitGroup& g, hipStream_t s) {
+  static_assert(!byte_codes<FMT>(), "4-bit formats only");
+  constexpr size_t smem = 2 * (size_t)(16 * SA2 + 32 * SA2) * sizeof(uint16_t);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)qsplit16_kernel<FMT, R>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  SplitArgs a{};
+  a.n = g.n;
+  int32_t units = 0;
+  for (int i = 0; i < g.n; ++i) {
+    int sps2 = 0;
+    const int s2 = split16_plan(g.p[i], g.splits[i], sps2);
+    if (s2 == 0) return hipErrorInvalidValue;
+    a.p[i] = g.p[i];
+    a.p[i].sps = sps2;
+    g.splits[i] = s2;                                // the reduction adds this many partials
+    a.ntiles[i] = (int32_t)((g.p[i].O + 127) / 128);
+    a.unit0[i] = units;
+    units += a.ntiles[i] * s2;
+  }
+  a.unit0[g.n] = units;
+  hipLaunchKernelGGL((qsplit16_kernel<FMT, R>), dim3((unsigned)units), dim3(256), smem, s, a);
+  return hipGetLastError();
+}
+
 template <int FMT, bool TRANS, int R, int MBK>
 hipError_t launch_split_m(const SplitGroup& g, hipStream_t s) {
   constexpr int B_EL = split_b_elems<TRANS>();
@@ -354,7 +601,17 @@ hipError_t launch_split_m(const SplitGroup& g, hipStream_t s) {
 
 // 32-row tiles when every token fits in one 32x32 MFMA block
 template <int FMT, bool TRANS, int R>
-hipError_t launch_split(const SplitGroup& g, hipStream_t s) {
+hipError_t launch_split(SplitGroup& g, hipStream_t s) {
+  // the 16-token kernel holds a ring of four steps of two groups per lane:
+  // 4-bit codes fit the registers, one-byte codes (FP8, Q8_0) would spill
+  if constexpr (!TRANS && !byte_codes<FMT>()) {
+    bool fits = g.p[0].M <= 16;
+    for (int i = 0; i < g.n && fits; ++i) {
+      int sps2;
+      fits = split16_plan(g.p[i], g.splits[i], sps2) > 0;
+    }
+    if (fits) return launch_split16<FMT, R>(g, s);
+  }
   return g.p[0].M <= 32 ? launch_split_m<FMT, TRANS, R, 1>(g, s) : launch_split_m<FMT, TRANS, R, 2>(g, s);
 }
 
@@ -595,7 +852,8 @@ __global__ __launch_bounds__(256) void split_reduce_bwd_kernel(ReduceBwdArgs ra)
 }
 
 template <int FMT, bool TRANS, int R>
-hipError_t launch_path(const SplitGroup& g, const GradFuse* gf, hipStream_t s) {
+hipError_t launch_path(const SplitGroup& g0, const GradFuse* gf, hipStream_t s) {
+  SplitGroup g = g0;                                 // the split launch may set how many partials each problem has
   hipError_t e = launch_split<FMT, TRANS, R>(g, s);
   if (e != hipSuccess) return e;
   if (gf) {

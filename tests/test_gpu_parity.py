@@ -443,3 +443,28 @@ def test_full_size_sampled(lib, wname, pi, m):
         e = H.rel(g, ref[key])
         say(f"  {key}: rel err {e:.3e}")
         assert e <= tol, (key, e)
+
+
+# at most 16 tokens the forward runs on 16x16x32 MFMAs over steps of 128:
+# every format, ragged K (a step with live and dead groups), ragged N, one token
+SMALL16 = [
+    ("s16_nf4_k1088", ofmt.FMT_NF4, 16, 1088, 224, 16, 32.0),
+    ("s16_q40_m5_k1056", ofmt.FMT_Q4_0, 5, 1056, 160, 32, 64.0),
+    ("s16_fp8_m16", ofmt.FMT_FP8, 16, 768, 352, 8, 16.0),
+    ("s16_mxfp4_m9_k4128", ofmt.FMT_MXFP4, 9, 4128, 96, 16, 32.0),
+    ("s16_q80_m1", ofmt.FMT_Q8_0, 1, 2080, 416, 32, 64.0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL16, ids=[c[0] for c in SMALL16])
+def test_layer_parity_16_tokens(lib, case):
+    name, fmt, m, k, n, r, alpha = case
+    say(f"16-token parity {name}: fmt={FNAME[fmt]} m={m} k={k} n={n} r={r}")
+    c = H.make_case(m, k, n, r, seed=zlib.crc32(name.encode()) % 1000)
+    _, got = run_layer(fmt, c, alpha, m)
+    _, _, wd = H.oracle_packed(fmt, c["W"])
+    ref = H.oracle_layer(c, wd, alpha)
+    for key in ("y", "U", "dX", "dA", "dB"):
+        e = H.rel(to_np(got[key]), ref[key])
+        say(f"  {key}: rel err {e:.3e}")
+        assert e <= H.FWD_TOL, (key, e)
