@@ -16,8 +16,11 @@ namespace {
 // in flight long before they are needed: a ring of D register stages keeps
 // the loads of steps it+1 .. it+D outstanding while step it computes.  Tile:
 // all tokens (TM = 32 MBK rows: 32 when M <= 32, else 64) x 128 output
-// columns, four waves side by side (TM x 32 each), the contraction split over
-// blockIdx.y; fp32 partial sums out.
+// columns, four waves side by side (TM x 32 each), the contraction split
+// across workgroups; fp32 partial sums out.  One launch serves a group of
+// independent problems: each workgroup finds its problem, column tile and
+// split in a table in the kernel arguments.  (The forward with at most 16
+// tokens and a 4-bit base runs qsplit16_kernel below instead.)
 //
 // Forward (y = x.W^T): no W element is used by more than one wave, so W is
 // not staged through LDS.  Each lane loads the codes of its own MFMA
