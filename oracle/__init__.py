@@ -18,6 +18,8 @@ What it holds, each written from the definition it cites:
   the per-token two-term E4M3 split of activations for the FP8 base.
 * ``adamw``   -- one AdamW step (decoupled weight decay) on the adapters and
   the bf16 copy of the updated parameters.
+* ``stacked`` -- forward and backward with frozen lower adapters under one
+  trainable top adapter.
 
 Precision: packing decisions (scales, codes) are taken in IEEE fp32, the
 precision the GPU packer uses, so codes can be compared bit for bit.  The
@@ -30,4 +32,4 @@ than itself: library codecs, closed forms, invariants, finite differences,
 integer-exact data and brute force.
 """
 
-from . import adamw, codecs, formats, lora  # noqa: F401
+from . import adamw, codecs, formats, lora, stacked  # noqa: F401
