@@ -290,6 +290,37 @@ int ql_plan_size(const ql_plan* plan);
 int ql_plan_run(ql_plan* plan, void* stream);
 int ql_plan_destroy(ql_plan* plan);
 
+/* ---------------------------------------------------------------- stacked adapters
+ * Frozen lower adapters under one trainable top adapter (the Surogate review
+ * page's stacked LoRA: adapters trained on top of other adapters with no
+ * offline merge; the README's "LoRA & QLoRA" row).  With adapter i = (A_i
+ * [r_i, K], B_i [N, r_i], s_i = alpha_i / r_i), the top one last,
+ *   y = x.W^T + sum_i s_i.(x.A_i^T).B_i^T  equals one adapter of rank
+ *   R = sum_i r_i:  A = [A_1; ...; A_top],  B = [c_1 B_1, ..., B_top],
+ *   c_i = s_i / s_top, scale s_top (alpha_cat = s_top * R),
+ * and so does dX; the top adapter's gradients are rows [R - r_top, R) of dA
+ * and columns [R - r_top, R) of dB of the backward call with (A, B, R,
+ * alpha_cat).  ql_stack_adapters writes A (a_cat, dev bf16 [R, K]) and B
+ * (b_cat, dev bf16 [N, R]) once per change of the adapters: A's rows and the
+ * top block of B are copied, each frozen block of B is bf16(fl32(c_i) * B_i)
+ * (exact when c_i is a power of two).  *alpha_cat (host) receives alpha_cat.
+ * adapters: host array of n (2 .. QL_STACK_MAX) descriptors, device
+ * pointers 16-byte aligned.  QL_EUNSUPPORTED if R is not 8, 16 or 32;
+ * QL_EINVAL for a null or misaligned pointer, r_i < 1, alpha_i not finite
+ * and positive. */
+#define QL_STACK_MAX 8
+
+typedef struct ql_adapter {
+  const uint16_t* lora_a;  /* dev bf16 [r, K]                               */
+  const uint16_t* lora_b;  /* dev bf16 [N, r]                               */
+  int32_t r;
+  float alpha;
+} ql_adapter;
+
+int ql_stack_adapters(const ql_adapter* adapters, int32_t n, int64_t n_out,
+                      int64_t k_in, uint16_t* a_cat, uint16_t* b_cat,
+                      float* alpha_cat, void* stream);
+
 /* ---------------------------------------------------------------- adapter optimizer step
  * One AdamW step on the adapters, every listed tensor in one launch.  The
  * Surogate README page lists "AdamW 8-bit" among its optimizers and the

@@ -27,8 +27,9 @@ EXPORTS = (
     "ql_pool_stats", "ql_pool_debug", "ql_pool_destroy", "ql_adamw_step",
     "ql_plan_create", "ql_plan_add_fwd", "ql_plan_add_bwd", "ql_plan_add_event", "ql_plan_size",
     "ql_plan_run", "ql_plan_destroy", "qlora_linear_fwd_group", "qlora_linear_bwd_group",
-    "ql_plan_add_fwd_group", "ql_plan_add_bwd_group",
+    "ql_plan_add_fwd_group", "ql_plan_add_bwd_group", "ql_stack_adapters",
 )
+STACK_MAX = 8
 GROUP_MAX = 8
 ADAMW_MAX_TENSORS = 32
 
@@ -58,6 +59,11 @@ class BwdCallC(ctypes.Structure):
                 ("alpha", ctypes.c_float), ("accumulate", ctypes.c_int32), ("dx", ctypes.c_void_p),
                 ("d_a", ctypes.c_void_p), ("d_b", ctypes.c_void_p), ("ws", ctypes.c_void_p),
                 ("ws_bytes", ctypes.c_size_t)]
+
+
+class AdapterC(ctypes.Structure):
+    _fields_ = [("lora_a", ctypes.c_void_p), ("lora_b", ctypes.c_void_p), ("r", ctypes.c_int32),
+                ("alpha", ctypes.c_float)]
 
 
 class AdamwTensorC(ctypes.Structure):
@@ -115,6 +121,8 @@ def load(path=LIB_PATH):
         "qlora_linear_bwd_group": (ctypes.c_int, [ctypes.POINTER(BwdCallC), I32, I64, I32, P]),
         "ql_plan_add_fwd_group": (ctypes.c_int, [P, ctypes.POINTER(FwdCallC), I32, I64, I32]),
         "ql_plan_add_bwd_group": (ctypes.c_int, [P, ctypes.POINTER(BwdCallC), I32, I64, I32]),
+        "ql_stack_adapters": (ctypes.c_int, [ctypes.POINTER(AdapterC), I32, I64, I64, P, P,
+                                             ctypes.POINTER(ctypes.c_float), P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -493,3 +501,34 @@ def _adamw_array(tensors):
         arr[i] = AdamwTensorC(p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(),
                               pb.data_ptr() if pb is not None else None, p.numel())
     return arr
+
+
+# ----------------------------------------------------------------------------- stacked adapters
+
+def stack_adapters(adapters, stream=None):
+    """Frozen lower adapters under a trainable top one (the last of
+    `adapters`, a list of (A bf16 [r, K], B bf16 [N, r], alpha)) as one
+    adapter: returns (A_cat bf16 [R, K], B_cat bf16 [N, R], alpha_cat) for the
+    layer calls; the top adapter's gradients are the last r_top rows of dA and
+    columns of dB (see top_grads)."""
+    n = len(adapters)
+    k, nout = adapters[0][0].shape[1], adapters[0][1].shape[0]
+    arr = (AdapterC * n)()
+    for i, (a, b, alpha) in enumerate(adapters):
+        r = a.shape[0]
+        _need(a, "A", torch.bfloat16, (r, k))
+        _need(b, "B", torch.bfloat16, (nout, r))
+        arr[i] = AdapterC(a.data_ptr(), b.data_ptr(), r, float(alpha))
+    R = sum(a.shape[0] for a, _, _ in adapters)
+    dev = adapters[0][0].device
+    a_cat = torch.empty((R, k), dtype=torch.bfloat16, device=dev)
+    b_cat = torch.empty((nout, R), dtype=torch.bfloat16, device=dev)
+    alpha_cat = ctypes.c_float()
+    _check(load().ql_stack_adapters(arr, n, nout, k, _ptr(a_cat), _ptr(b_cat), ctypes.byref(alpha_cat),
+                                    _stream(stream)))
+    return a_cat, b_cat, alpha_cat.value
+
+
+def top_grads(da, db, r_top):
+    """The top adapter's (dA, dB) inside the stacked call's gradients (views)."""
+    return da[-r_top:], db[:, -r_top:]

@@ -458,6 +458,30 @@ int ql_act_quant_e4m3(const uint16_t* x, int64_t m, int64_t k, uint8_t* hi, uint
   return QL_OK;
 }
 
+int ql_stack_adapters(const ql_adapter* adapters, int32_t n, int64_t n_out, int64_t k_in, uint16_t* a_cat,
+                      uint16_t* b_cat, float* alpha_cat, void* stream) {
+  if (n < 2 || n > QL_STACK_MAX) return set_error(QL_EINVAL, "stack of %d adapters outside [2, %d]", n, QL_STACK_MAX);
+  if (!adapters || !a_cat || !b_cat || !alpha_cat) return set_error(QL_EINVAL, "null pointer");
+  if (n_out <= 0 || k_in <= 0) return set_error(QL_EINVAL, "n_out and k_in must be positive");
+  if (!aligned16(a_cat) || !aligned16(b_cat)) return set_error(QL_EINVAL, "misaligned output");
+  int32_t R = 0;
+  for (int i = 0; i < n; ++i) {
+    const ql_adapter& a = adapters[i];
+    if (!a.lora_a || !a.lora_b || !aligned16(a.lora_a) || !aligned16(a.lora_b))
+      return set_error(QL_EINVAL, "adapter %d: null or misaligned pointer", i);
+    if (a.r < 1 || a.r > 32) return set_error(QL_EINVAL, "adapter %d: rank %d", i, a.r);
+    if (!(a.alpha > 0.0f) || !(a.alpha - a.alpha == 0.0f))
+      return set_error(QL_EINVAL, "adapter %d: alpha must be finite and positive", i);
+    R += a.r;
+  }
+  if (R != 8 && R != 16 && R != 32) return set_error(QL_EUNSUPPORTED, "stacked rank %d not in {8,16,32}", R);
+  int rc = check_sticky();
+  if (rc) return rc;
+  hipError_t e = launch_stack(adapters, n, n_out, k_in, a_cat, b_cat, alpha_cat, as_stream(stream));
+  if (e != hipSuccess) return hip_error(e, "stack launch");
+  return QL_OK;
+}
+
 int ql_adamw_step(const ql_adamw_tensor* tensors, int32_t n_tensors, const ql_adamw_hparams* hp,
                   void* stream) {
   if (n_tensors < 0 || n_tensors > QL_ADAMW_MAX_TENSORS)

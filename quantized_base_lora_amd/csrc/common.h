@@ -122,6 +122,10 @@ hipError_t launch_qgemm8(const Gemm8Call& c, hipStream_t s);
 hipError_t launch_rproj(const uint16_t* act, int64_t m, int64_t c, const uint16_t* d, bool a_layout, int32_t r,
                         float* out, hipStream_t s);
 
+// stacked adapters -> one concatenated adapter (kernels_stack.hip); arguments already validated
+hipError_t launch_stack(const ql_adapter* ad, int32_t n, int64_t n_out, int64_t k_in, uint16_t* a_cat,
+                        uint16_t* b_cat, float* alpha_cat, hipStream_t st);
+
 // adapter optimizer step (kernels_optim.hip); arguments already validated
 hipError_t launch_adamw(const ql_adamw_tensor* ts, int32_t nt, const ql_adamw_hparams& hp, hipStream_t s);
 

@@ -207,3 +207,23 @@ def test_group_argument_errors(lib):
         assert lib.ql_plan_size(h) == 1
     finally:
         lib.ql_plan_destroy(h)
+
+
+def test_stack_argument_errors(lib):
+    A = binding.AdapterC
+    ok = [A(0x10000, 0x20000, 8, 16.0), A(0x30000, 0x40000, 8, 16.0)]
+    alpha = ctypes.c_float()
+    st = lib.ql_stack_adapters
+    P = FAKE
+    assert st((A * 2)(*ok), 1, 64, 128, P, P, ctypes.byref(alpha), None) == binding.QL_EINVAL
+    assert st((A * 2)(*ok), 9, 64, 128, P, P, ctypes.byref(alpha), None) == binding.QL_EINVAL
+    assert st((A * 2)(*ok), 2, 64, 128, P, None, ctypes.byref(alpha), None) == binding.QL_EINVAL
+    assert st((A * 2)(*ok), 2, 64, 128, P, P, None, None) == binding.QL_EINVAL
+    assert st((A * 2)(ok[0], A(0x30000, 0x40000, 4, 16.0)), 2, 64, 128, P, P, ctypes.byref(alpha), None) \
+        == binding.QL_EUNSUPPORTED
+    assert st((A * 2)(ok[0], A(0x30000, 0x40008, 8, 16.0)), 2, 64, 128, P, P, ctypes.byref(alpha), None) \
+        == binding.QL_EINVAL
+    assert st((A * 2)(ok[0], A(0x30000, 0x40000, 8, -1.0)), 2, 64, 128, P, P, ctypes.byref(alpha), None) \
+        == binding.QL_EINVAL
+    assert st((A * 2)(ok[0], A(0x30000, 0x40000, 0, 16.0)), 2, 64, 128, P, P, ctypes.byref(alpha), None) \
+        == binding.QL_EINVAL
