@@ -501,6 +501,16 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
+    # spread of single steps, from a separate pass with an event between steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        run(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    spread = {"p10": float(np.percentile(per_step, 10)), "median": float(np.median(per_step)),
+              "p90": float(np.percentile(per_step, 90)), "pass": "separate, one event between steps"}
 
     fwd_ms = sum(t for _, t in ev_pairs)
     fwd_flops = sum(fwd_kernel_flops(wl, p, m) for ps, _ in ev_pairs for p in ps)
@@ -520,6 +530,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_spread": spread,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
