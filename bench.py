@@ -438,7 +438,9 @@ def main():
                                   for d in g])
             if timed and fwd_projs:
                 pl.add_event(e1, stream)
-                evs.append(([d["p"] for d in fwd_projs], e0, e1))
+                # a group is one launch (pair) unless the FP8 base above 64 tokens runs call by call
+                nl = len(fwd_projs) if (wl.fmt == 3 and m > 64) else sum(1 for g in groups if g)
+                evs.append(([d["p"] for d in fwd_projs], nl, e0, e1))
             for g in (reversed(groups) if args.phase != "fwd" else []):
                 pl.add_bwd_group([(d["qws"][i], d["x"], d["dy"], d["u"], d["a"], d["b"], wl.alpha, d["dx"],
                                    d["da"], d["db"], d["ws"], False) for d in reversed(g)])
@@ -458,7 +460,7 @@ def main():
             tp, evs = timing_plans[i % copies]
             tp.run(stream)
             torch.cuda.synchronize()
-            ev_pairs.extend((pp, e0.elapsed_time(e1)) for pp, e0, e1 in evs)   # ([projections], ms)
+            ev_pairs.extend((pp, nl, e0.elapsed_time(e1)) for pp, nl, e0, e1 in evs)   # ([projections], launches, ms)
     else:
         # the roofline's kernel timing: eager launches on one stream
         for i in range(args.warmup):
@@ -467,7 +469,7 @@ def main():
         for i in range(args.steps):
             eager_step(i, True)
         torch.cuda.synchronize()
-        ev_pairs[:] = [([pp], e0.elapsed_time(e1)) for pp, e0, e1 in ev_pairs]
+        ev_pairs[:] = [([pp], 1, e0.elapsed_time(e1)) for pp, e0, e1 in ev_pairs]
 
     # the step itself: HIP-graph replays (one graph per rotated weight copy) or eager launches
     graphs = []
@@ -512,9 +514,10 @@ def main():
     spread = {"p10": float(np.percentile(per_step, 10)), "median": float(np.median(per_step)),
               "p90": float(np.percentile(per_step, 90)), "pass": "separate, one event between steps"}
 
-    fwd_ms = sum(t for _, t in ev_pairs)
-    fwd_flops = sum(fwd_kernel_flops(wl, p, m) for ps, _ in ev_pairs for p in ps)
-    n_launch = max(1, sum(len(ps) for ps, _ in ev_pairs))
+    fwd_ms = sum(t for _, _, t in ev_pairs)
+    fwd_flops = sum(fwd_kernel_flops(wl, p, m) for ps, _, _ in ev_pairs for p in ps)
+    n_launch = max(1, sum(nl for _, nl, _ in ev_pairs))
+    n_calls = max(1, sum(len(ps) for ps, _, _ in ev_pairs))
     fwd_ms = fwd_ms or float("nan")
     avg_launch_ms = fwd_ms / n_launch
     achieved = fwd_flops / (fwd_ms / 1e3) / 1e12
@@ -550,14 +553,15 @@ def main():
         "roofline": {"kernel": "qgemm_kernel (forward: dequant GEMM + fused LoRA)", "bound": "mfma",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "avg_launch_us": avg_launch_ms * 1e3, "launches_timed": n_launch,
+                     "avg_launch_us": avg_launch_ms * 1e3, "launches_timed": n_launch, "calls_timed": n_calls,
                      "timing": ("HIP events around each step's forward launches (enqueued back to back "
-                                "by one launch plan), total / launches" if use_plan else
+                                "by one launch plan; q|k|v and gate|up one launch each), total / launches"
+                                if use_plan else
                                 "HIP events around each forward call"),
                      "flops_per_launch_avg": fwd_flops / n_launch},
     }
     if m <= 64:
-        fwd_bytes = sum(BPW[wl.fmt] * p.n * p.k + m * 2 * (p.k + p.n) for ps, _ in ev_pairs for p in ps) / n_launch
+        fwd_bytes = sum(BPW[wl.fmt] * p.n * p.k + m * 2 * (p.k + p.n) for ps, _, _ in ev_pairs for p in ps) / n_launch
         gbs = fwd_bytes / (avg_launch_ms / 1e3) / 1e9
         out["roofline"].update({"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": gbs / PEAK_HBM_GBS, "bytes_per_launch_avg": fwd_bytes})

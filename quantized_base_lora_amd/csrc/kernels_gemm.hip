@@ -39,6 +39,14 @@
 // MFMA (B first), so each lane ends up with 4 consecutive output columns per
 // row and writes them with one 8-byte store.  Workgroups are remapped so each
 // XCD (own L2) works on a contiguous run of tiles.
+//
+// One launch can run several independent calls of one format, direction,
+// token count and rank (q|k|v, gate|up of a decoder layer): a problem table
+// in the kernel arguments, each problem its own run of tiles, ordered by
+// contraction length so the longest tiles are dispatched first.  Each output
+// element is computed exactly as in a launch of its own, whatever the tile
+// shape, so grouped results are bitwise those of separate calls; what the
+// group saves is the ramp-up and drain of every launch but one.
 #include <algorithm>
 
 #include "dequant.h"
@@ -69,9 +77,17 @@ template <int TM_, int TN, int NTH> struct Shape {
   static_assert(MB >= 1 && NB >= 1 && AR >= 1 && UI >= 1, "tile shape");
 };
 
+// problems of one launch: workgroups [tile0[g], tile0[g + 1]) own the tiles of
+// problem g (tile0[n] = grid size)
+struct GemmArgs {
+  Params p[MAX_GROUP];
+  int32_t tile0[MAX_GROUP + 1];
+  int32_t n;
+};
+
 template <int FMT, bool TRANS, int R, int TM_, int TN, int NTH>
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(NTH / 256, NTH / 256)))
-void qgemm_kernel(Params p) {
+void qgemm_kernel(GemmArgs ga) {
   using S = Shape<TM_, TN, NTH>;
   constexpr int NT = NTH;
   constexpr int TM = S::TM;
@@ -91,12 +107,17 @@ void qgemm_kernel(Params p) {
   const int wave = tid >> 6;
   const int wm = wave / S::WAVES_N, wn = wave % S::WAVES_N;
 
-  // ---- tile assignment: contiguous runs of tiles per XCD (workgroups go round-robin over 8 XCDs)
+  // ---- problem and tile: each problem's tiles in contiguous runs per XCD
+  // (workgroups go round-robin over the 8 XCDs; a run of a multiple of 8
+  // workgroups starting at a multiple of 8 keeps that order)
+  const int bid = (int)blockIdx.x;
+  int pi = 0;
+  while (pi + 1 < ga.n && bid >= ga.tile0[pi + 1]) ++pi;
+  const Params& p = ga.p[pi];
+  const int t0 = ga.tile0[pi], tiles = ga.tile0[pi + 1] - t0;
   const int nt = (int)((p.O + TN - 1) / TN);
-  const int mt = (int)((p.M + TM - 1) / TM);
-  const int tiles = nt * mt;
-  int t = blockIdx.x;
-  if ((tiles & 7) == 0) t = (t & 7) * (tiles >> 3) + (t >> 3);
+  int t = bid - t0;
+  if ((tiles & 7) == 0 && (t0 & 7) == 0) t = (t & 7) * (tiles >> 3) + (t >> 3);
   const int64_t o0 = (int64_t)(t % nt) * TN;
   const int64_t m0 = (int64_t)(t / nt) * TM;
   const int KT = (int)((p.C + TK - 1) / TK);
@@ -501,7 +522,7 @@ void qgemm_kernel(Params p) {
 }
 
 template <int FMT, bool TRANS, int R, int TM, int TN, int NTH>
-hipError_t launch_t(const Params& p, hipStream_t s) {
+hipError_t launch_t(const GemmArgs& g, hipStream_t s) {
   using S = Shape<TM, TN, NTH>;
   constexpr int B_ELEMS = TRANS ? S::BT_ELEMS : S::BF_ELEMS;
   constexpr int D_ELEMS = TRANS ? BL_ELEMS : AD_ELEMS;
@@ -515,9 +536,15 @@ hipError_t launch_t(const Params& p, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int64_t tiles = ((p.O + TN - 1) / TN) * ((p.M + TM - 1) / TM);
+  GemmArgs a = g;
+  int64_t tiles = 0;
+  for (int i = 0; i < a.n; ++i) {
+    a.tile0[i] = (int32_t)tiles;
+    tiles += ((a.p[i].O + TN - 1) / TN) * ((a.p[i].M + TM - 1) / TM);
+  }
+  a.tile0[a.n] = (int32_t)tiles;
   hipLaunchKernelGGL((qgemm_kernel<FMT, TRANS, R, TM, TN, NTH>), dim3((unsigned)tiles),
-                     dim3(NTH), smem, s, p);
+                     dim3(NTH), smem, s, a);
   return hipGetLastError();
 }
 
@@ -525,10 +552,11 @@ hipError_t launch_t(const Params& p, hipStream_t s) {
 // per CU) times work per tile, each shape weighted for its MFMA efficiency
 // (the narrower tiles read more LDS per MFMA); ties go to the earlier entry.
 // 128x128 tiles only pay off when the 256-row tiles would leave CUs idle.
+// A group counts its tiles in units of its longest contraction.
 struct TilePick {
   int tm, tn;
 };
-TilePick pick_tile(int64_t m, int64_t o) {
+TilePick pick_tile(const GemmArgs& g) {
   struct Cand {
     int tm, tn;
     double eff;
@@ -537,9 +565,14 @@ TilePick pick_tile(int64_t m, int64_t o) {
   const int nc = 4;
   TilePick best{256, 256};
   double best_cost = 1e300;
+  int64_t cmax = 1;
+  for (int j = 0; j < g.n; ++j) cmax = std::max<int64_t>(cmax, g.p[j].C);
   for (int i = 0; i < nc; ++i) {
-    const int64_t tiles = ((m + c[i].tm - 1) / c[i].tm) * ((o + c[i].tn - 1) / c[i].tn);
-    const double cost = (double)((tiles + 255) / 256) * c[i].tm * c[i].tn / c[i].eff;
+    int64_t work = 0;                                // tiles x contraction length
+    for (int j = 0; j < g.n; ++j)
+      work += ((g.p[j].M + c[i].tm - 1) / c[i].tm) * ((g.p[j].O + c[i].tn - 1) / c[i].tn) * g.p[j].C;
+    const int64_t rounds = (work + 256 * cmax - 1) / (256 * cmax);
+    const double cost = (double)rounds * c[i].tm * c[i].tn / c[i].eff;
     if (cost < best_cost * (1 - 1e-9)) {
       best_cost = cost;
       best = TilePick{c[i].tm, c[i].tn};
@@ -549,31 +582,41 @@ TilePick pick_tile(int64_t m, int64_t o) {
 }
 
 template <int FMT, bool TRANS, int R>
-hipError_t launch_w(const Params& p, hipStream_t s) {
+hipError_t launch_w(const GemmArgs& g, hipStream_t s) {
 #ifndef QL_GEMM_THREADS
 #define QL_GEMM_THREADS 512
 #endif
-  const TilePick t = pick_tile(p.M, p.O);
-  if (t.tm == 128) return launch_t<FMT, TRANS, R, 128, 128, QL_GEMM_THREADS>(p, s);
+  const TilePick t = pick_tile(g);
+  if (t.tm == 128) return launch_t<FMT, TRANS, R, 128, 128, QL_GEMM_THREADS>(g, s);
   switch (t.tn) {
-    case 256: return launch_t<FMT, TRANS, R, 256, 256, QL_GEMM_THREADS>(p, s);
-    case 192: return launch_t<FMT, TRANS, R, 256, 192, QL_GEMM_THREADS>(p, s);
-    default: return launch_t<FMT, TRANS, R, 256, 128, QL_GEMM_THREADS>(p, s);
+    case 256: return launch_t<FMT, TRANS, R, 256, 256, QL_GEMM_THREADS>(g, s);
+    case 192: return launch_t<FMT, TRANS, R, 256, 192, QL_GEMM_THREADS>(g, s);
+    default: return launch_t<FMT, TRANS, R, 256, 128, QL_GEMM_THREADS>(g, s);
   }
 }
 
 template <int FMT, bool TRANS>
-hipError_t launch_r(const Params& p, int r, hipStream_t s) {
+hipError_t launch_r(const GemmArgs& g, int r, hipStream_t s) {
   switch (r) {
-    case 8: return launch_w<FMT, TRANS, 8>(p, s);
-    case 16: return launch_w<FMT, TRANS, 16>(p, s);
-    default: return launch_w<FMT, TRANS, 32>(p, s);
+    case 8: return launch_w<FMT, TRANS, 8>(g, s);
+    case 16: return launch_w<FMT, TRANS, 16>(g, s);
+    default: return launch_w<FMT, TRANS, 32>(g, s);
   }
 }
 
 template <int FMT>
-hipError_t launch_f(const Params& p, bool trans, int r, hipStream_t s) {
-  return trans ? launch_r<FMT, true>(p, r, s) : launch_r<FMT, false>(p, r, s);
+hipError_t launch_f(const GemmArgs& g, bool trans, int r, hipStream_t s) {
+  return trans ? launch_r<FMT, true>(g, r, s) : launch_r<FMT, false>(g, r, s);
+}
+
+hipError_t launch_tiles(int fmt, const GemmArgs& g, bool trans, int r, hipStream_t s) {
+  switch (fmt) {
+    case QL_FMT_Q4_0: return launch_f<QL_FMT_Q4_0>(g, trans, r, s);
+    case QL_FMT_NF4: return launch_f<QL_FMT_NF4>(g, trans, r, s);
+    case QL_FMT_MXFP4: return launch_f<QL_FMT_MXFP4>(g, trans, r, s);
+    case QL_FMT_Q8_0: return launch_f<QL_FMT_Q8_0>(g, trans, r, s);
+    default: return launch_f<QL_FMT_FP8_E4M3>(g, trans, r, s);
+  }
 }
 
 }  // namespace
@@ -665,23 +708,26 @@ hipError_t launch_qgemm(const GemmCall& c, hipStream_t s) {
     g.n = 1;
     return launch_split_path(c.w->format, c.trans, c.r, g, c.grads, s);
   }
-  switch (c.w->format) {
-    case QL_FMT_Q4_0: return launch_f<QL_FMT_Q4_0>(p, c.trans, c.r, s);
-    case QL_FMT_NF4: return launch_f<QL_FMT_NF4>(p, c.trans, c.r, s);
-    case QL_FMT_MXFP4: return launch_f<QL_FMT_MXFP4>(p, c.trans, c.r, s);
-    case QL_FMT_Q8_0: return launch_f<QL_FMT_Q8_0>(p, c.trans, c.r, s);
-    default: return launch_f<QL_FMT_FP8_E4M3>(p, c.trans, c.r, s);
-  }
+  GemmArgs g{};
+  g.p[0] = p;
+  g.n = 1;
+  return launch_tiles(c.w->format, g, c.trans, c.r, s);
 }
 
+// one launch (pair) for the group: one format, direction, token count and
+// rank, and one path for all (the small-M split path, or the bf16 tile kernel;
+// the FP8 base's fp8 path above SMALL_M runs call by call)
 bool qgemm_groupable(const GemmCall* calls, int n) {
   if (n < 2 || n > MAX_GROUP) return false;
+  const GemmCall& c0 = calls[0];
+  const bool split = split_plan(c0.trans, c0.m, c0.w->n_out, c0.w->k_in, c0.r).splits > 0;
+  if (!split && (use_fp8_mfma(c0.w->format, c0.m) || c0.grads)) return false;
   for (int i = 0; i < n; ++i) {
     const GemmCall& c = calls[i];
-    if (c.w->format != calls[0].w->format || c.trans != calls[0].trans || c.m != calls[0].m ||
-        c.r != calls[0].r || (c.grads != nullptr) != (calls[0].grads != nullptr))
+    if (c.w->format != c0.w->format || c.trans != c0.trans || c.m != c0.m || c.r != c0.r ||
+        (c.grads != nullptr) != (c0.grads != nullptr))
       return false;
-    if (split_plan(c.trans, c.m, c.w->n_out, c.w->k_in, c.r).splits == 0) return false;
+    if ((split_plan(c.trans, c.m, c.w->n_out, c.w->k_in, c.r).splits > 0) != split) return false;
   }
   return true;
 }
@@ -694,11 +740,25 @@ hipError_t launch_qgemm_group(const GemmCall* calls, int n, hipStream_t s) {
     }
     return hipSuccess;
   }
+  int splits[MAX_GROUP];
+  Params ps[MAX_GROUP];
+  for (int i = 0; i < n; ++i) make_params(calls[i], ps[i], splits[i]);
+  if (splits[0] == 0) {
+    // tile kernel: longest contraction first (stable), so its tiles start first
+    int order[MAX_GROUP];
+    for (int i = 0; i < n; ++i) order[i] = i;
+    std::stable_sort(order, order + n, [&](int a, int b) { return ps[a].C > ps[b].C; });
+    GemmArgs g{};
+    g.n = n;
+    for (int i = 0; i < n; ++i) g.p[i] = ps[order[i]];
+    return launch_tiles(calls[0].w->format, g, calls[0].trans, calls[0].r, s);
+  }
   SplitGroup g{};
   GradFuse gf[MAX_GROUP];
   g.n = n;
   for (int i = 0; i < n; ++i) {
-    make_params(calls[i], g.p[i], g.splits[i]);
+    g.p[i] = ps[i];
+    g.splits[i] = splits[i];
     if (calls[i].grads) gf[i] = *calls[i].grads;
   }
   return launch_split_path(calls[0].w->format, calls[0].trans, calls[0].r, g, calls[0].grads ? gf : nullptr, s);

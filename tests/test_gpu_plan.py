@@ -68,12 +68,21 @@ def test_plan_matches_direct_calls(lib):
 
 GROUPS = [
     # fmt, m, r, [(k, n), ...]: split path with fused gradients, split path at 64 tokens,
-    # 33 tokens (separate gradient launch), and a tile-path group (launched call by call)
+    # 33 tokens (separate gradient launch), then tile-kernel groups (one launch per
+    # group): ragged row and column tiles, contractions of different lengths in both
+    # directions (the table is reordered, longest first), a q|k|v-shaped group whose
+    # tile counts are multiples of 8 (per-problem XCD remap), and the FP8 base above
+    # 64 tokens (call by call)
     (ofmt.FMT_NF4, 16, 16, [(512, 384), (512, 128), (512, 128)]),
     (ofmt.FMT_MXFP4, 64, 8, [(1024, 256), (256, 1024)]),
     (ofmt.FMT_Q4_0, 33, 32, [(96, 224), (1056, 64), (256, 96)]),
     (ofmt.FMT_FP8, 24, 16, [(256, 160), (512, 96)]),
     (ofmt.FMT_NF4, 200, 16, [(256, 192), (128, 64)]),
+    (ofmt.FMT_MXFP4, 300, 8, [(256, 448), (512, 128), (128, 320)]),
+    (ofmt.FMT_Q8_0, 520, 32, [(192, 96), (640, 288)]),
+    (ofmt.FMT_Q4_0, 129, 16, [(64, 64), (320, 1088), (64, 256), (128, 32)]),
+    (ofmt.FMT_NF4, 2048, 16, [(1024, 2048), (1024, 1024), (1024, 1024)]),
+    (ofmt.FMT_FP8, 96, 16, [(256, 160), (512, 96)]),
 ]
 
 
