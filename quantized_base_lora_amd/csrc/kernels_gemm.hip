@@ -62,6 +62,13 @@ template <int TM_, int TN, int NTH> struct Shape {
   static constexpr int NW = NTH / 64;
   static constexpr int A_ELEMS = TM * SA;
   static constexpr int SBT = TN + 32;                 // dX W tile [TK][TN] stride (576 / 320 B rows)
+  // dX W tile: 16-byte piece p of 32-element group g in row w is stored at
+  // piece p ^ wswz(w, g).  Unswizzled, the 16-byte dequantization stores of a
+  // wave (8 rows x 8 groups for TN = 256) fall on a quarter of the LDS banks
+  // (rows 576 B apart, groups 64 B apart), 4- to 5-way conflicts; swizzled
+  // they spread over all banks, and the transposing fragment reads (4
+  // consecutive bytes-8 runs of 4 rows per 16 lanes) stay conflict-free.
+  __device__ static int wswz(int row, int grp) { return TN == 256 ? ((row + 2 * (grp >> 2)) & 3) : (grp & 3); }
   static constexpr int BF_ELEMS = TN * SA;
   static constexpr int BT_ELEMS = TK * SBT;
   static constexpr int WAVES_N = (NW == 8 && TN == 256) ? 4 : 2;
@@ -144,12 +151,14 @@ void qgemm_kernel(GemmArgs ga) {
   const bool wtask = !S::WPART || tid < S::WGT;     // wave-uniform
   int wr[WG], wg[WG];                                // W groups: row of the W tile, group in that row
   bool wg_in[WG];                                    // dX: the group's output columns lie inside K
+  int wsx[WG];                                       // dX: piece swizzle of the group, in elements
 #pragma unroll
   for (int j = 0; j < WG; ++j) {
     const int g = tid + NT * j;
     wr[j] = g / GPR;
     wg[j] = g % GPR;
     wg_in[j] = !TRANS || (o0 + 32 * (wg[j] + 1) <= p.K);
+    wsx[j] = TRANS ? S::wswz(wr[j], wg[j]) << 3 : 0;
   }
   // adapter tile pieces (16 bytes): forward A[j][c0 + 8c ..]; dX B[c0 + row][8c ..]
   constexpr int DPR = TRANS ? R / 8 : TK / 8;        // pieces per adapter row
@@ -222,7 +231,8 @@ void qgemm_kernel(GemmArgs ga) {
   };
   auto store_w = [&](uint16_t* st, int j, int i) {   // elements 8i .. 8i+7 of W group j
     if (!wtask) return;
-    uint16_t* dst = st + A_ELEMS + (TRANS ? wr[j] * S::SBT : wr[j] * SA) + wg[j] * 32 + 8 * i;
+    const int po = TRANS ? (8 * i) ^ wsx[j] : 8 * i;
+    uint16_t* dst = st + A_ELEMS + (TRANS ? wr[j] * S::SBT : wr[j] * SA) + wg[j] * 32 + po;
     *reinterpret_cast<uint4*>(dst) = deq.piece(i);
   };
   auto store_adapter = [&](uint16_t* st) {
@@ -258,8 +268,9 @@ void qgemm_kernel(GemmArgs ga) {
       if constexpr (TRANS) {
         const int b = lane >> 4, sl = lane & 15;
         const int col = S::WN * wn + 32 * j + 16 * (b & 1) + 4 * (sl & 3);
-        const int row = ks * 16 + 8 * (b >> 1) + (sl >> 2);
-        fb[h][j] = tr16x8(Bs + row * S::SBT + col, Bs + (row + 4) * S::SBT + col);
+        const int row = ks * 16 + 8 * (b >> 1) + (sl >> 2);   // rows row and row + 4: one swizzle
+        const int pcol = col ^ (S::wswz(row, col >> 5) << 3);   // bits 3-4 of col: the piece
+        fb[h][j] = tr16x8(Bs + row * S::SBT + pcol, Bs + (row + 4) * S::SBT + pcol);
       } else {
         fb[h][j] = *reinterpret_cast<const bf16x8*>(Bs + (S::WN * wn + 32 * j + (lane & 31)) * SA + ks * 16 + 8 * (lane >> 5));
       }
