@@ -221,18 +221,20 @@ GradLaunch grad_launch(const BwdArgs& a, const BwdParts& b) {
   return g;
 }
 
-hipError_t bwd_grads(const BwdArgs& a, const BwdParts& b, hipStream_t s) {
+hipError_t bwd_grads(const BwdArgs& a, const BwdParts& b, hipStream_t s, GradReduceSet* defer) {
   if (b.fuse) return hipSuccess;
-  return launch_grads(grad_launch(a, b), s);
+  const GradLaunch g = grad_launch(a, b);
+  return launch_grads_group(&g, 1, s, defer);
 }
 
-int enqueue_bwd(const BwdArgs& a, hipStream_t s) {
+// defer: hold the gradient reduction back in that set (launch plans)
+int enqueue_bwd(const BwdArgs& a, hipStream_t s, GradReduceSet* defer = nullptr) {
   BwdParts b;
   bwd_parts(a, b);
   hipError_t e = hipSuccess;
   if (a.m > 0 && a.dx) e = launch_qgemm(b.gemm, s);
   else if (a.m > 0) e = launch_down_proj(a.dy, a.m, a.w.n_out, a.b, a.r, b.v, s);
-  if (e == hipSuccess) e = bwd_grads(a, b, s);
+  if (e == hipSuccess) e = bwd_grads(a, b, s, defer);
   if (e != hipSuccess) return hip_error(e, "backward launch");
   return QL_OK;
 }
@@ -304,12 +306,12 @@ int enqueue_fwd_group(const FwdArgs* a, int n, hipStream_t s) {
   return QL_OK;
 }
 
-int enqueue_bwd_group(const BwdArgs* a, int n, hipStream_t s) {
+int enqueue_bwd_group(const BwdArgs* a, int n, hipStream_t s, GradReduceSet* defer = nullptr) {
   bool all_dx = true;
   for (int i = 0; i < n; ++i) all_dx = all_dx && a[i].dx;
   if (n <= 1 || a[0].m == 0 || !all_dx) {
     for (int i = 0; i < n; ++i) {
-      int rc = enqueue_bwd(a[i], s);
+      int rc = enqueue_bwd(a[i], s, defer);
       if (rc) return rc;
     }
     return QL_OK;
@@ -324,7 +326,7 @@ int enqueue_bwd_group(const BwdArgs* a, int n, hipStream_t s) {
   if (e == hipSuccess && !b[0].fuse) {   // one token count: all fused or none
     GradLaunch g[QL_GROUP_MAX];
     for (int i = 0; i < n; ++i) g[i] = grad_launch(a[i], b[i]);
-    e = launch_grads_group(g, n, s);
+    e = launch_grads_group(g, n, s, defer);
   }
   if (e != hipSuccess) return hip_error(e, "grouped backward launch");
   return QL_OK;
@@ -625,12 +627,51 @@ int ql_plan_run(ql_plan* plan, void* stream) {
   int rc = check_sticky();
   if (rc) return rc;
   hipStream_t s = as_stream(stream);
+  // The adapter-gradient reductions of backward steps are held back and run
+  // as one launch: before the first later step that touches a buffer they
+  // write (dA, dB) or writes a buffer they read (the partials in a backward
+  // workspace), before an event, and at the end of the plan.  The reductions
+  // are the same kernels on the same partials, so results are bitwise those
+  // of the calls made one by one.
+  GradReduceSet pend;
   for (const PlanStep& st : plan->steps) {
+    bool flush = st.kind == PlanStep::EVENT;
+    if (!flush && pend.n > 0) {
+      std::vector<Span> all, out;
+      auto add_fwd = [&](const FwdArgs& f) {
+        Span ai[10], ao[6];
+        int na, no;
+        fwd_spans(f, ai, na, ao, no);
+        all.insert(all.end(), ai, ai + na);
+        out.insert(out.end(), ao, ao + no);
+      };
+      auto add_bwd = [&](const BwdArgs& b) {
+        Span ai[10], ao[6];
+        int na, no;
+        bwd_spans(b, ai, na, ao, no);
+        all.insert(all.end(), ai, ai + na);
+        out.insert(out.end(), ao, ao + no);
+      };
+      if (st.kind == PlanStep::FWD) add_fwd(st.fwd);
+      if (st.kind == PlanStep::BWD) add_bwd(st.bwd);
+      for (const FwdArgs& f : st.fwds) add_fwd(f);
+      for (const BwdArgs& b : st.bwds) add_bwd(b);
+      for (int i = 0; i < pend.n && !flush; ++i) {
+        const GradReduceSet::Item& it = pend.item[i];
+        const size_t ob = (size_t)it.pdim * pend.r * 4, pb = ob * pend.nparts;
+        for (const Span& x : all) flush = flush || overlaps(x.p, x.n, it.out, ob);
+        for (const Span& x : out) flush = flush || overlaps(x.p, x.n, it.part, pb);
+      }
+    }
+    if (flush && pend.n > 0) {
+      hipError_t e = launch_grad_reduce(pend, s);
+      if (e != hipSuccess) return hip_error(e, "plan gradient reduction");
+    }
     switch (st.kind) {
       case PlanStep::FWD: rc = enqueue_fwd(st.fwd, s); break;
-      case PlanStep::BWD: rc = enqueue_bwd(st.bwd, s); break;
+      case PlanStep::BWD: rc = enqueue_bwd(st.bwd, s, &pend); break;
       case PlanStep::FWD_GROUP: rc = enqueue_fwd_group(st.fwds.data(), (int)st.fwds.size(), s); break;
-      case PlanStep::BWD_GROUP: rc = enqueue_bwd_group(st.bwds.data(), (int)st.bwds.size(), s); break;
+      case PlanStep::BWD_GROUP: rc = enqueue_bwd_group(st.bwds.data(), (int)st.bwds.size(), s, &pend); break;
       default: {
         hipError_t e = hipEventRecord(st.event, s);
         rc = e == hipSuccess ? QL_OK : hip_error(e, "plan event record");
@@ -638,7 +679,8 @@ int ql_plan_run(ql_plan* plan, void* stream) {
     }
     if (rc) return rc;
   }
-  return QL_OK;
+  hipError_t e = launch_grad_reduce(pend, s);
+  return e == hipSuccess ? QL_OK : hip_error(e, "plan gradient reduction");
 }
 
 int ql_plan_destroy(ql_plan* plan) {

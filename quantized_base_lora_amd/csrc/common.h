@@ -149,9 +149,28 @@ struct GradLaunch {
   int32_t accumulate;
 };
 hipError_t launch_grads(const GradLaunch& g, hipStream_t s);
+// Reductions of adapter-gradient partials held back so that those of
+// consecutive backward calls run as one launch (a launch plan gathers them).
+// The items of a set share the rank and the partition count.
+struct GradReduceSet {
+  struct Item {
+    const float* part;       // [nparts, pdim, r]
+    float* out;              // [pdim, r], or [r, pdim] with transpose_out
+    int64_t pdim;
+    int32_t transpose_out;
+    float s;
+    int32_t accumulate;
+  };
+  Item item[2 * QL_GROUP_MAX];
+  int32_t n = 0, r = 0, nparts = 0;
+};
 // the gradients of n calls with one token count, rank and partition plan in
-// one launch (and one reduction launch)
-hipError_t launch_grads_group(const GradLaunch* g, int n, hipStream_t s);
+// one launch (and one reduction launch).  With `defer`, a reduction that is
+// needed (M > 0, more than one partition) is added to the set instead of
+// launched; a set it does not fit is launched first.
+hipError_t launch_grads_group(const GradLaunch* g, int n, hipStream_t s, GradReduceSet* defer = nullptr);
+// launches the set's reductions as one launch (nothing if it is empty) and empties it
+hipError_t launch_grad_reduce(GradReduceSet& d, hipStream_t s);
 int32_t grad_parts(int64_t m);
 int64_t grad_tiles(int64_t pdim);
 

@@ -267,7 +267,25 @@ hipError_t launch_down_proj(const uint16_t* x, int64_t m, int64_t c, const uint1
   return hipGetLastError();
 }
 
-hipError_t launch_grads_group(const GradLaunch* g, int n, hipStream_t s) {
+hipError_t launch_grad_reduce(GradReduceSet& d, hipStream_t s) {
+  if (d.n == 0) return hipSuccess;
+  GradArgs a{};
+  a.nprob = d.n;
+  a.r = d.r;
+  a.nparts = d.nparts;
+  int32_t rblocks = 0;
+  for (int i = 0; i < d.n; ++i) {
+    const GradReduceSet::Item& it = d.item[i];
+    a.prob[i] = GradProb{nullptr, nullptr, it.out, const_cast<float*>(it.part), it.pdim, it.transpose_out,
+                         it.s, it.accumulate, 0, rblocks};
+    rblocks += (int32_t)((it.pdim * d.r + NT - 1) / NT);
+  }
+  d.n = 0;
+  hipLaunchKernelGGL(grad_reduce_kernel, dim3((unsigned)rblocks), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_grads_group(const GradLaunch* g, int n, hipStream_t s, GradReduceSet* defer) {
   if (n < 1 || n > QL_GROUP_MAX) return hipErrorInvalidValue;
   GradArgs a{};
   a.nprob = 2 * n;
@@ -291,6 +309,12 @@ hipError_t launch_grads_group(const GradLaunch* g, int n, hipStream_t s) {
     pr.rblk0 = rblocks;
     rblocks += (int32_t)((pr.pdim * a.r + NT - 1) / NT);
   }
+  const bool held = defer && a.m > 0 && a.nparts > 1;
+  if (held && defer->n > 0 &&
+      (defer->r != a.r || defer->nparts != a.nparts || defer->n + a.nprob > MAX_PROB)) {
+    hipError_t e = launch_grad_reduce(*defer, s);
+    if (e != hipSuccess) return e;
+  }
   if (a.m > 0) {
     switch (a.r) {
       case 8: hipLaunchKernelGGL(grad_kernel<8>, dim3((unsigned)blocks), dim3(NT), 0, s, a); break;
@@ -299,6 +323,15 @@ hipError_t launch_grads_group(const GradLaunch* g, int n, hipStream_t s) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nparts == 1) return e;   // one partition: the kernel wrote dA, dB
+    if (held) {
+      defer->r = a.r;
+      defer->nparts = a.nparts;
+      for (int i = 0; i < a.nprob; ++i) {
+        const GradProb& pr = a.prob[i];
+        defer->item[defer->n++] = GradReduceSet::Item{pr.part, pr.out, pr.pdim, pr.transpose_out, pr.s, pr.accumulate};
+      }
+      return hipSuccess;
+    }
   } else {
     a.nparts = 0;                                     // no tokens: dA = dB = 0 (or unchanged)
   }

@@ -188,3 +188,91 @@ def test_group_edge_cases(lib):
                 a, b = o[key], rf[key]
                 iv = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
                 assert torch.equal(a.view(iv), b.view(iv)), (m, j, key)
+
+
+def test_plan_held_back_reductions(lib):
+    """A plan holds the adapter-gradient reductions of its backward steps back
+    and runs them as one launch.  Each rule that launches them early is hit
+    here: a later step accumulating into the same dA / dB, a later step
+    reusing a held step's workspace, an event, another partition count, a set
+    that is full (16 reductions) and the end of the plan.  Every output must
+    equal, bit for bit, the same calls made one by one."""
+    from quantized_base_lora_amd import binding as B
+    fmt, r, alpha = ofmt.FMT_NF4, 16, 16.0
+    # 1100 and 1500 tokens: three partitions of M; 600: two
+    specs = [(1100, 256, 192), (1100, 128, 320), (1100, 320, 64), (1100, 192, 128), (1100, 64, 256),
+             (1100, 256, 64), (1100, 128, 128), (1100, 64, 192), (1100, 192, 96), (600, 128, 192)]
+    calls = []
+    wsb = max(256, max(B.workspace_bytes(B.OP_BWD, fmt, n, k, m, r) for m, k, n in specs))
+    for i, (m, k, n) in enumerate(specs):
+        print(f"held reductions call {i}: m={m} k={k} n={n}", flush=True)
+        c = H.make_case(m, k, n, r, seed=120 + i)
+        qw = B.quant_pack(fmt, torch.from_numpy(c["W"]).cuda())
+        t = {key: H.bits_to_bf16_tensor(c[key]) for key in ("x", "dY", "A", "B")}
+        _, u = B.linear_fwd(qw, t["x"], t["A"], t["B"], alpha)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        calls.append({"qw": qw, "t": t, "u": u, "ws": ws, "m": m, "k": k, "n": n})
+    torch.cuda.synchronize()
+
+    def outs(c):
+        return {"dx": torch.empty((c["m"], c["k"]), dtype=torch.bfloat16, device="cuda"),
+                "da": torch.empty((r, c["k"]), dtype=torch.float32, device="cuda"),
+                "db": torch.empty((c["n"], r), dtype=torch.float32, device="cuda")}
+
+    def item(i, o, ws=None, acc=False):
+        c = calls[i]
+        t = c["t"]
+        return (c["qw"], t["x"], t["dY"], c["u"], t["A"], t["B"], alpha, o["dx"], o["da"], o["db"],
+                ws if ws is not None else c["ws"], acc)
+
+    # the sequence: (kind, [(call, output slot, workspace of call or None, accumulate)])
+    seq = [
+        ("bwd", [(0, "a", None, False)]),
+        ("group", [(1, "b", None, False), (2, "c", None, False)]),
+        ("bwd", [(0, "a", None, True)]),                  # accumulates into held dA / dB of step 1
+        ("bwd", [(3, "d", None, False)]),
+        ("bwd", [(4, "e", 3, False)]),                    # reuses the held workspace of call 3
+        ("event", []),
+        ("group", [(5, "f", None, False), (6, "g", None, False), (7, "h", None, False)]),
+        ("bwd", [(9, "j", None, False)]),                 # two partitions, not three
+        ("group", [(1, "k", None, False), (2, "l", None, False), (3, "m", None, False), (4, "n", None, False),
+                   (5, "o", None, False), (6, "p", None, False), (7, "q", None, False), (8, "r", None, False)]),
+        ("bwd", [(0, "s", None, False)]),                 # the set above is full
+    ]
+    slots = {}
+    for _, its in seq:
+        for ci, slot, _, _ in its:
+            slots.setdefault(slot, outs(calls[ci]))
+    ref = {}
+    # one by one (direct calls), in the same order and with the same workspaces
+    for kind, its in seq:
+        for ci, slot, wsi, acc in its:
+            c = calls[ci]
+            o = ref.setdefault(slot, outs(c))
+            it = item(ci, o, calls[wsi]["ws"] if wsi is not None else None, acc)
+            B.linear_bwd(c["qw"], c["t"]["x"], c["t"]["dY"], c["u"], c["t"]["A"], c["t"]["B"], alpha,
+                         accumulate=acc, dx=o["dx"], da=o["da"], db=o["db"], ws=it[10])
+    torch.cuda.synchronize()
+    pl = B.Plan()
+    stream = torch.cuda.current_stream()
+    ev = torch.cuda.Event()
+    for kind, its in seq:
+        if kind == "event":
+            pl.add_event(ev, stream)
+        elif kind == "bwd":
+            ci, slot, wsi, acc = its[0]
+            pl.add_bwd(*item(ci, slots[slot], calls[wsi]["ws"] if wsi is not None else None, acc))
+        else:
+            pl.add_bwd_group([item(ci, slots[slot], calls[wsi]["ws"] if wsi is not None else None, acc)
+                              for ci, slot, wsi, acc in its])
+    for run in range(2):
+        for o in slots.values():
+            for v in o.values():
+                v.fill_(float("nan"))
+        pl.run()
+        torch.cuda.synchronize()
+        for slot, o in slots.items():
+            for key, v in o.items():
+                iv = torch.int16 if v.dtype == torch.bfloat16 else torch.int32
+                assert torch.equal(v.view(iv), ref[slot][key].view(iv)), (run, slot, key)
+    pl.close()
