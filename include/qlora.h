@@ -265,8 +265,14 @@ int qlora_linear_bwd_group(const ql_bwd_call* calls, int32_t n, int64_t m,
  * records a marker: at that point of each run, hipEventRecord(event, stream)
  * (event: a hipEvent_t owned by the caller).  ql_plan_run enqueues every
  * recorded step in order on `stream`, with the same kernels and launch
- * configuration as the direct calls, so results are bitwise the same.  A plan
- * is host data only (no device memory); one plan serves one host thread. */
+ * configuration as the direct calls, so results are bitwise the same; the
+ * one difference is when the dA/dB reductions of backward steps are
+ * enqueued: they are gathered into one launch, issued before any later step
+ * that touches their outputs or overwrites their workspaces, before every
+ * event marker and at the end of the run.  Every output is therefore
+ * complete at the plan's end and at each of its events, as with direct
+ * calls.  A plan is host data only (no device memory); one plan serves one
+ * host thread. */
 typedef struct ql_plan ql_plan;
 
 int ql_plan_create(ql_plan** plan);
