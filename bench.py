@@ -423,44 +423,44 @@ def main():
     # the timing plans bracket each forward call with events.
     use_plan = not (args.no_plan or args.streams or args.graph)
     if use_plan:
-        def record(pl, i, timed):
-            # timed: one event pair around the step's forward launches, back to back
-            # (an event around every launch adds its own pipeline drain to each)
-            evs = []
-            fwd_projs = projs if args.phase != "bwd" else []
-            if timed and fwd_projs:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                pl.add_event(e0, stream)
+        def record(pl, i):
             # calls grouped as a decoder layer allows: q|k|v and gate|up read one input
-            for g in (groups if fwd_projs else []):
+            for g in (groups if args.phase != "bwd" else []):
                 pl.add_fwd_group([(d["qws"][i], d["x"], d["a"], d["b"], wl.alpha, d["y"], d["u"], d["wsf"])
                                   for d in g])
-            if timed and fwd_projs:
-                pl.add_event(e1, stream)
-                # a group is one launch (pair) unless the FP8 base above 64 tokens runs call by call
-                nl = len(fwd_projs) if (wl.fmt == 3 and m > 64) else sum(1 for g in groups if g)
-                evs.append(([d["p"] for d in fwd_projs], nl, e0, e1))
             for g in (reversed(groups) if args.phase != "fwd" else []):
                 pl.add_bwd_group([(d["qws"][i], d["x"], d["dy"], d["u"], d["a"], d["b"], wl.alpha, d["dx"],
                                    d["da"], d["db"], d["ws"], False) for d in reversed(g)])
-            return evs
-        step_plans, timing_plans = [], []
+        step_plans = []
         for i in range(copies):
             pl = B.Plan()
-            record(pl, i, False)
+            record(pl, i)
             step_plans.append(pl)
-            tp = B.Plan()
-            timing_plans.append((tp, record(tp, i, True)))
+        # the roofline's kernel timing: the forward launches of K steps back to back
+        # (weight copies rotated as the steps rotate them), one event pair around
+        # all of them, so the event markers' own cost (a few microseconds each)
+        # is spread over every launch instead of falling on each step's four
+        fwd_projs = projs if args.phase != "bwd" else []
+        if fwd_projs:
+            roof = B.Plan()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            roof.add_event(e0, stream)
+            for i in range(args.steps):
+                for g in groups:
+                    roof.add_fwd_group([(d["qws"][i % copies], d["x"], d["a"], d["b"], wl.alpha, d["y"], d["u"],
+                                         d["wsf"]) for d in g])
+            roof.add_event(e1, stream)
+            # a group is one launch (pair) unless the FP8 base above 64 tokens runs call by call
+            nl = (len(fwd_projs) if (wl.fmt == 3 and m > 64) else len(groups)) * args.steps
         torch.cuda.synchronize()
         for i in range(args.warmup):
-            timing_plans[i % copies][0].run(stream)
-        torch.cuda.synchronize()
-        for i in range(args.steps):
-            tp, evs = timing_plans[i % copies]
-            tp.run(stream)
+            step_plans[i % copies].run(stream)
+        if fwd_projs:
+            roof.run(stream)                   # untimed pass
+            roof.run(stream)
             torch.cuda.synchronize()
-            ev_pairs.extend((pp, nl, e0.elapsed_time(e1)) for pp, nl, e0, e1 in evs)   # ([projections], launches, ms)
+            ev_pairs.append(([d["p"] for d in fwd_projs] * args.steps, nl, e0.elapsed_time(e1)))
     else:
         # the roofline's kernel timing: eager launches on one stream
         for i in range(args.warmup):
@@ -554,8 +554,8 @@ def main():
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "avg_launch_us": avg_launch_ms * 1e3, "launches_timed": n_launch, "calls_timed": n_calls,
-                     "timing": ("HIP events around each step's forward launches (enqueued back to back "
-                                "by one launch plan; q|k|v and gate|up one launch each), total / launches"
+                     "timing": ("one HIP event pair around the forward launches of K steps, enqueued back "
+                                "to back by one launch plan (q|k|v and gate|up one launch each), total / launches"
                                 if use_plan else
                                 "HIP events around each forward call"),
                      "flops_per_launch_avg": fwd_flops / n_launch},
