@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "QLoRA-linear fwd+bwd tokens/s per layer; % bf16 MFMA peak, % HBM BW"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 FMT_NAME = {1: "q4_0", 2: "nf4", 3: "fp8_e4m3", 4: "mxfp4", 5: "q8_0"}
 BPW = {1: 18 / 32, 2: 0.5 + 4 / 64, 3: 1.0, 4: 17 / 32, 5: 34 / 32}
@@ -560,6 +561,15 @@ def main():
                                 "HIP events around each forward call"),
                      "flops_per_launch_avg": fwd_flops / n_launch},
     }
+    if wl.fmt == 3 and m > 64 and ev_pairs:
+        # the FP8 base above 64 tokens: activation split, rank-r projection and the
+        # fp8 GEMM (two E4M3 products per output, hi and lo terms) per call; the
+        # algorithmic FLOPs against the fp8 peak
+        out["dtype"] = "fp8_e4m3"
+        out["roofline"].update({"kernel": "qgemm8_kernel (forward: fp8 GEMM over the two-term E4M3 activation "
+                                          "split, with act_quant_kernel and rproj_kernel per call)",
+                                "peak": PEAK_FP8_TFLOPS, "frac": achieved / PEAK_FP8_TFLOPS,
+                                "executed_fp8_flops_per_algorithmic": 2})
     if m <= 64:
         fwd_bytes = sum(BPW[wl.fmt] * p.n * p.k + m * 2 * (p.k + p.n) for ps, _, _ in ev_pairs for p in ps) / n_launch
         gbs = fwd_bytes / (avg_launch_ms / 1e3) / 1e9
