@@ -120,13 +120,25 @@ void grad_kernel(GradArgs a) {
     lds_barrier();                                    // previous step's readers are done
 #pragma unroll
     for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(Xs + (xr + 32 * i) * SX + xc) = xv[u][i];
+    // this thread's QPT consecutive Q values as hi / lo bf16 pairs, packed into
+    // 32-bit words and stored 8 bytes at a time (4 for rank 8)
+    uint32_t hw[QPT / 2], lw[QPT / 2];
 #pragma unroll
-    for (int t = 0; t < QPT; ++t) {
-      const float q = __uint_as_float(qv[u][t]);
-      const __bf16 h = (__bf16)q;
-      const __bf16 l = (__bf16)(q - (float)h);
-      Qh[qr * SQ + qc + t] = __builtin_bit_cast(uint16_t, h);
-      Ql[qr * SQ + qc + t] = __builtin_bit_cast(uint16_t, l);
+    for (int t = 0; t < QPT; t += 2) {
+      const float q0 = __uint_as_float(qv[u][t]), q1 = __uint_as_float(qv[u][t + 1]);
+      const float h0 = (float)(__bf16)q0, h1 = (float)(__bf16)q1;
+      hw[t / 2] = pack_bf16x2(h0, h1);
+      lw[t / 2] = pack_bf16x2(q0 - h0, q1 - h1);
+    }
+    if constexpr (QPT == 2) {
+      *reinterpret_cast<uint32_t*>(Qh + qr * SQ + qc) = hw[0];
+      *reinterpret_cast<uint32_t*>(Ql + qr * SQ + qc) = lw[0];
+    } else {
+#pragma unroll
+      for (int t = 0; t < QPT / 2; t += 2) {
+        *reinterpret_cast<uint2*>(Qh + qr * SQ + qc + 2 * t) = make_uint2(hw[t], hw[t + 1]);
+        *reinterpret_cast<uint2*>(Ql + qr * SQ + qc + 2 * t) = make_uint2(lw[t], lw[t + 1]);
+      }
     }
     lds_barrier();
 #pragma unroll
