@@ -12,6 +12,7 @@ run on) and the CPU oracle timed on this host on a bounded sample.
 """
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -42,6 +43,9 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=0, help="tokens in the CPU oracle sample (0: all)")
     ap.add_argument("--copies", type=int, default=0, help="packed weight copies rotated per step (0: auto)")
     ap.add_argument("--proj", default=None, help="run only this projection (profiling)")
+    ap.add_argument("--exclude", default="",
+                    help="comma-separated projections left out of the layer (e.g. o), in the timing and in "
+                         "every per-layer figure")
     ap.add_argument("--phase", default="both", choices=["both", "fwd", "bwd"], help="profiling: one pass only")
     ap.add_argument("--graph", action="store_true",
                     help="time HIP-graph replays of the step instead of eager launches")
@@ -338,8 +342,9 @@ def main():
     # inputs, packed bases and preallocated outputs / workspaces
     projs = []
     packed_bytes = 0
+    excluded = set(filter(None, args.exclude.split(",")))
     for pi, p in enumerate(wl.projs):
-        if args.proj and p.name != args.proj:
+        if (args.proj and p.name != args.proj) or p.name in excluded:
             continue
         c = synth.layer_tensors(wl, pi, m=m)
         qw = B.quant_pack(wl.fmt, torch.from_numpy(c["W"]).to(dev))
@@ -355,6 +360,9 @@ def main():
              "wsf": torch.empty(max(256, B.workspace_bytes(B.OP_FWD, wl.fmt, p.n, p.k, m, wl.r)),
                                 dtype=torch.uint8, device=dev)}
         projs.append(d)
+    if excluded:
+        # per-layer accounting over the projections that run (inputs keep their seeds)
+        wl = dataclasses.replace(wl, projs=tuple(p for p in wl.projs if p.name not in excluded))
     # rotate packed copies so weight reads come from HBM, not the 256 MB MALL
     copies = args.copies or max(1, min(8, int(np.ceil(512e6 / packed_bytes))))
     for d in projs:
@@ -542,7 +550,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.notes, "name": wl.name, "tokens": m, "base_format": FMT_NAME[wl.fmt],
                    "rank": wl.r, "alpha": wl.alpha, "projections": [f"{p.name}:{p.k}->{p.n}" for p in wl.projs],
-                   "packed_copies_rotated": copies,
+                   "packed_copies_rotated": copies, "excluded_projections": sorted(excluded),
                    "step_mode": ("HIP graph replay" if args.graph else
                                  "eager launches, one library call per step (recorded launch plan; "
                                  "q|k|v and gate|up as grouped calls)" if use_plan
