@@ -412,7 +412,9 @@ void qgemm_kernel(GemmArgs ga) {
   }
   // the tile's slice of the up matrix, loaded now so the epilogue does not
   // wait for it: forward B rows o0 .. o0+TN (contiguous, 8 elements per
-  // piece), dX A[j][o0 .. o0+TN] (8 columns of one row per piece)
+  // piece), dX A[j][o0 .. o0+TN] (8 columns of one row per piece; consecutive
+  // lanes take consecutive rows j, so their 2-byte transposed stores into the
+  // epilogue tile are adjacent instead of 8 tile rows apart)
   constexpr int UPP = TN * R / 8;                    // 16-byte pieces
   constexpr int UPT = (UPP + NT - 1) / NT;
   uint4 upv[UPT];
@@ -424,7 +426,7 @@ void qgemm_kernel(GemmArgs ga) {
       const int q = tid + NT * u;
       uint32_t off = OOB;
       if constexpr (TRANS) {
-        const int j = q / (TN / 8), c = (q % (TN / 8)) * 8;
+        const int j = q % R, c = (q / R) * 8;
         if (q < UPP && o0 + c < p.K) off = (uint32_t)((j * p.K + o0 + c) * 2);
       } else {
         if (q < UPP) off = (uint32_t)(q * 16);
@@ -474,7 +476,7 @@ void qgemm_kernel(GemmArgs ga) {
     const int q = tid + NT * u;
     if (q < UPP) {
       if constexpr (TRANS) {
-        const int j = q / (TN / 8), c = (q % (TN / 8)) * 8;
+        const int j = q % R, c = (q / R) * 8;
         const uint32_t w[4] = {upv[u].x, upv[u].y, upv[u].z, upv[u].w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
