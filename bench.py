@@ -240,15 +240,21 @@ def bench_stack(args, wl, m):
         acts.append(al)
         outs.append(ol)
     stream = torch.cuda.current_stream()
+    # independent projections of a decoder layer as grouped calls (q|k|v, gate|up)
+    names = [p.name for p in wl.projs]
+    groups = [[names.index(n) for n in g if n in names] for g in (["q", "k", "v"], ["o"], ["gate", "up"], ["down"])]
+    groups = [g for g in groups if g]
+    if sorted(i for g in groups for i in g) != list(range(len(names))):
+        groups = None
 
     def timed(st, steps, warmup):
         for _ in range(warmup):
-            st.run(acts, outs)
+            st.run(acts, outs, groups)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(steps):
-            st.run(acts, outs)
+            st.run(acts, outs, groups)
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
@@ -293,7 +299,8 @@ def bench_stack(args, wl, m):
         "data": "synthetic",
         "config": {"workload": wl.notes, "name": wl.name, "tokens": m, "layers": L,
                    "base_format": FMT_NAME[wl.fmt], "rank": wl.r, "alpha": wl.alpha,
-                   "layer_image_bytes": layout.nbytes, "slots": 2},
+                   "layer_image_bytes": layout.nbytes, "slots": 2,
+                   "calls": "grouped q|k|v, o, gate|up, down" if groups else "one call per projection"},
         "stack": {"resident_ms_per_step": ms_res, "resident_tokens_per_s": m / (ms_res / 1e3),
                   "streamed_over_resident": ms_st / ms_res,
                   "copies_per_step": copies_per_step,

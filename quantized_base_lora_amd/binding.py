@@ -333,7 +333,8 @@ def _bwd_calls(items):
 
 def linear_fwd_group(items, stream=None):
     """Independent forward calls of one format, token count and rank in one
-    library call (one split launch and one reduction for all at <= 64 tokens)."""
+    library call (one launch for all on the tile path above 64 tokens; one
+    split launch and one reduction at <= 64 tokens)."""
     arr, m, r = _fwd_calls(items)
     _check(load().qlora_linear_fwd_group(arr, len(items), m, r, _stream(stream)))
 

@@ -95,26 +95,41 @@ class Stack:
         if not self.resident and 0 <= layer < self.n_layers:
             self.pool.prefetch(layer, self.copy_stream)
 
-    def run(self, acts, outs):
+    def run(self, acts, outs, groups=None):
         """acts[l][p] = dict(x, dy, a, b) device tensors; outs[l][p] = dict of
         preallocated y, u, dx, da, db and ws (backward workspace) tensors,
-        written in place, and optionally wsf (forward workspace)."""
+        written in place, and optionally wsf (forward workspace; needed by
+        grouped calls of at most 64 tokens).  groups: lists of projection
+        indices whose calls are independent (q|k|v, gate|up of a decoder
+        layer) and run as one grouped call each, in the order given (backward
+        in reverse); default: one call per projection."""
         L = self.n_layers
+        gs = groups or [[p] for p in range(len(self.layout.projs))]
         self._ahead(0)
         for l in range(L):
             self._ahead(l + 1)
             ws = self._weights(l)
-            for p, qw in enumerate(ws):
-                a, o = acts[l][p], outs[l][p]
-                B.linear_fwd(qw, a["x"], a["a"], a["b"], self.alpha, y=o["y"], u=o["u"], ws=o.get("wsf"))
+            for g in gs:
+                items = [(ws[p], acts[l][p]["x"], acts[l][p]["a"], acts[l][p]["b"], self.alpha,
+                          outs[l][p]["y"], outs[l][p]["u"], outs[l][p].get("wsf")) for p in g]
+                if len(items) == 1:
+                    qw, x, a, b, alpha, y, u, wsf = items[0]
+                    B.linear_fwd(qw, x, a, b, alpha, y=y, u=u, ws=wsf)
+                else:
+                    B.linear_fwd_group(items)
             self._done(l)
         for l in reversed(range(L)):
             self._ahead(l - 1)
             ws = self._weights(l)
-            for p, qw in enumerate(ws):
-                a, o = acts[l][p], outs[l][p]
-                B.linear_bwd(qw, a["x"], a["dy"], o["u"], a["a"], a["b"], self.alpha,
-                             dx=o["dx"], da=o["da"], db=o["db"], ws=o["ws"])
+            for g in reversed(gs):
+                items = [(ws[p], acts[l][p]["x"], acts[l][p]["dy"], outs[l][p]["u"], acts[l][p]["a"],
+                          acts[l][p]["b"], self.alpha, outs[l][p]["dx"], outs[l][p]["da"], outs[l][p]["db"],
+                          outs[l][p]["ws"], False) for p in g]
+                if len(items) == 1:
+                    qw, x, dy, u, a, b, alpha, dx, da, db, wsb, _ = items[0]
+                    B.linear_bwd(qw, x, dy, u, a, b, alpha, dx=dx, da=da, db=db, ws=wsb)
+                else:
+                    B.linear_bwd_group(items)
             self._done(l)
 
     def close(self):

@@ -98,6 +98,17 @@ def test_streamed_equals_resident_bitwise(lib):
         assert stats["copies"] == 2 * L - 2, stats          # fwd L copies, bwd L-2 (two layers stay)
         assert stats["bytes"] == stats["copies"] * layout.nbytes
         st.close()
+    # grouped calls (projections a and c in one call) over the streamed base give
+    # the same bits as the resident one-call-per-projection run
+    say("streamed run, grouped calls")
+    st = stack.Stack(layout, R, ALPHA, images_host=host, n_slots=2)
+    st.pool.debug(delay_us=3000, poison=True)
+    o_st = new_outs()
+    st.run(acts, o_st, groups=[[0, 2], [1]])
+    torch.cuda.synchronize()
+    ok, where = same(o_res, o_st)
+    assert ok, where
+    st.close()
     # the outputs are the real thing: max abs difference 0.0 and finite
     assert all(torch.isfinite(o_res[l][p]["y"].float()).all() for l in range(L) for p in range(len(PROJS)))
 
