@@ -250,7 +250,9 @@ int qlora_linear_bwd_group(const ql_bwd_call* calls, int32_t n, int64_t m,
 /* ---------------------------------------------------------------- launch plans
  * A plan records a fixed sequence of forward and backward calls (and event
  * markers) once; ql_plan_run then enqueues the whole sequence on a stream in
- * one call, with no per-call host work beyond the kernel launches.  With few
+ * one call; arguments are validated when recorded, so a run does little host
+ * work beyond the kernel launches (and a buffer-overlap test while gradient
+ * reductions are held back, see below).  With few
  * tokens a layer call's kernels take a few microseconds, less than the host
  * needs to marshal a call from an interpreter, so a step issued call by call
  * leaves the GPU idle between launches; a plan keeps it fed.  (The Soup page's
