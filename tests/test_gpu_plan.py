@@ -193,13 +193,13 @@ def test_group_edge_cases(lib):
 def test_plan_held_back_reductions(lib):
     """A plan holds the adapter-gradient reductions of its backward steps back
     and runs them as one launch.  Each rule that launches them early is hit
-    here: a later step accumulating into the same dA / dB, a later step
-    reusing a held step's workspace, an event, another partition count, a set
+    here: a later step accumulating into the same dA / dB, later forward and
+    backward steps reusing a held step's workspace, an event, another partition count, a set
     that is full (16 reductions) and the end of the plan.  Every output must
     equal, bit for bit, the same calls made one by one."""
     from quantized_base_lora_amd import binding as B
     fmt, r, alpha = ofmt.FMT_NF4, 16, 16.0
-    # 1100 and 1500 tokens: three partitions of M; 600: two
+    # 1100 tokens: three partitions of M; 600: two
     specs = [(1100, 256, 192), (1100, 128, 320), (1100, 320, 64), (1100, 192, 128), (1100, 64, 256),
              (1100, 256, 64), (1100, 128, 128), (1100, 64, 192), (1100, 192, 96), (600, 128, 192)]
     calls = []
@@ -231,6 +231,7 @@ def test_plan_held_back_reductions(lib):
         ("group", [(1, "b", None, False), (2, "c", None, False)]),
         ("bwd", [(0, "a", None, True)]),                  # accumulates into held dA / dB of step 1
         ("bwd", [(3, "d", None, False)]),
+        ("fwd", [(5, "F", 3, False)]),                    # a forward whose workspace is call 3's, held
         ("bwd", [(4, "e", 3, False)]),                    # reuses the held workspace of call 3
         ("event", []),
         ("group", [(5, "f", None, False), (6, "g", None, False), (7, "h", None, False)]),
@@ -239,15 +240,29 @@ def test_plan_held_back_reductions(lib):
                    (5, "o", None, False), (6, "p", None, False), (7, "q", None, False), (8, "r", None, False)]),
         ("bwd", [(0, "s", None, False)]),                 # the set above is full
     ]
+    def fouts(c):
+        return {"y": torch.empty((c["m"], c["n"]), dtype=torch.bfloat16, device="cuda"),
+                "u": torch.empty((c["m"], r), dtype=torch.float32, device="cuda")}
+
+    def fitem(i, o, ws):
+        c = calls[i]
+        t = c["t"]
+        return (c["qw"], t["x"], t["A"], t["B"], alpha, o["y"], o["u"], ws)
+
     slots = {}
-    for _, its in seq:
+    for kind, its in seq:
         for ci, slot, _, _ in its:
-            slots.setdefault(slot, outs(calls[ci]))
+            slots.setdefault(slot, fouts(calls[ci]) if kind == "fwd" else outs(calls[ci]))
     ref = {}
     # one by one (direct calls), in the same order and with the same workspaces
     for kind, its in seq:
         for ci, slot, wsi, acc in its:
             c = calls[ci]
+            if kind == "fwd":
+                o = ref.setdefault(slot, fouts(c))
+                B.linear_fwd(c["qw"], c["t"]["x"], c["t"]["A"], c["t"]["B"], alpha, y=o["y"], u=o["u"],
+                             ws=calls[wsi]["ws"])
+                continue
             o = ref.setdefault(slot, outs(c))
             it = item(ci, o, calls[wsi]["ws"] if wsi is not None else None, acc)
             B.linear_bwd(c["qw"], c["t"]["x"], c["t"]["dY"], c["u"], c["t"]["A"], c["t"]["B"], alpha,
@@ -259,6 +274,9 @@ def test_plan_held_back_reductions(lib):
     for kind, its in seq:
         if kind == "event":
             pl.add_event(ev, stream)
+        elif kind == "fwd":
+            ci, slot, wsi, _ = its[0]
+            pl.add_fwd(*fitem(ci, slots[slot], calls[wsi]["ws"]))
         elif kind == "bwd":
             ci, slot, wsi, acc = its[0]
             pl.add_bwd(*item(ci, slots[slot], calls[wsi]["ws"] if wsi is not None else None, acc))
