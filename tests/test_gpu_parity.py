@@ -424,9 +424,10 @@ for wname in ("qwen3_0.6b_nf4", "llama3.1_8b_nf4", "qwen3_8b_fp8", "llama3.1_8b_
 
 @pytest.mark.parametrize("wname,pi,m", FULL, ids=[f"{w}-{synth.WORKLOADS[w].projs[p].name}-m{m}" for w, p, m in FULL])
 def test_full_size_sampled(lib, wname, pi, m):
-    """Full-size projections in the benchmark's launch configuration; y and dX
-    checked on 8 sampled rows (each row depends on its own inputs only), U on
-    the same rows, dA and dB in full."""
+    """Full-size projections, each as a single call (the benchmark's grouped
+    launches equal these bit for bit: test_gpu_plan.py); y and dX checked on 8
+    sampled rows (each row depends on its own inputs only), U on the same
+    rows, dA and dB in full."""
     wl = synth.WORKLOADS[wname]
     p = wl.projs[pi]
     say(f"full-size {wname} {p.name} K={p.k} N={p.n} M={m}")

@@ -294,3 +294,66 @@ def test_plan_held_back_reductions(lib):
                 iv = torch.int16 if v.dtype == torch.bfloat16 else torch.int32
                 assert torch.equal(v.view(iv), ref[slot][key].view(iv)), (run, slot, key)
     pl.close()
+
+
+BENCH_LAYERS = [("qwen3_0.6b_nf4", 8192), ("llama3.1_8b_mxfp4", 16), ("llama3.1_8b_q8_0", 64)]
+
+
+@pytest.mark.parametrize("wname,m", BENCH_LAYERS, ids=[f"{w}-m{m}" for w, m in BENCH_LAYERS])
+def test_bench_launch_configuration_matches_single_calls(lib, wname, m):
+    """The layer step exactly as the benchmark times it (a launch plan: the
+    forward of q|k|v, o, gate|up, down as grouped calls, then their backward
+    in reverse, gradient reductions held back) gives bit for bit the outputs
+    of the seven projections called one by one, which the full-size parity
+    tests compare with the oracle."""
+    from quantized_base_lora_amd import binding as B, synth
+    wl = synth.WORKLOADS[wname]
+    say_ = lambda *a: print(*a, flush=True)  # noqa: E731
+    say_(f"bench configuration {wname} m={m}")
+    d = []
+    for pi, p in enumerate(wl.projs):
+        c = synth.layer_tensors(wl, pi, m=m)
+        qw = B.quant_pack(wl.fmt, torch.from_numpy(c["W"]).cuda())
+        del c["W"]
+        t = {key: H.bits_to_bf16_tensor(c[key]) for key in ("x", "dY", "A", "B")}
+        e = {"p": p, "qw": qw, "t": t}
+        for tag in ("ref", "got"):
+            e[tag] = {"y": torch.empty((m, p.n), dtype=torch.bfloat16, device="cuda"),
+                      "u": torch.empty((m, wl.r), dtype=torch.float32, device="cuda"),
+                      "dx": torch.empty((m, p.k), dtype=torch.bfloat16, device="cuda"),
+                      "da": torch.empty((wl.r, p.k), dtype=torch.float32, device="cuda"),
+                      "db": torch.empty((p.n, wl.r), dtype=torch.float32, device="cuda"),
+                      "wsf": torch.empty(max(256, B.workspace_bytes(B.OP_FWD, wl.fmt, p.n, p.k, m, wl.r)),
+                                         dtype=torch.uint8, device="cuda"),
+                      "ws": torch.empty(max(256, B.workspace_bytes(B.OP_BWD, wl.fmt, p.n, p.k, m, wl.r)),
+                                        dtype=torch.uint8, device="cuda")}
+        d.append(e)
+    by = {e["p"].name: e for e in d}
+    groups = [[by[n] for n in g] for g in (["q", "k", "v"], ["o"], ["gate", "up"], ["down"])]
+    for e in d:                                    # one by one
+        t, o = e["t"], e["ref"]
+        B.linear_fwd(e["qw"], t["x"], t["A"], t["B"], wl.alpha, y=o["y"], u=o["u"], ws=o["wsf"])
+    for e in reversed(d):
+        t, o = e["t"], e["ref"]
+        B.linear_bwd(e["qw"], t["x"], t["dY"], o["u"], t["A"], t["B"], wl.alpha, dx=o["dx"], da=o["da"],
+                     db=o["db"], ws=o["ws"])
+    pl = B.Plan()                                  # as the benchmark records a step
+    for g in groups:
+        pl.add_fwd_group([(e["qw"], e["t"]["x"], e["t"]["A"], e["t"]["B"], wl.alpha, e["got"]["y"], e["got"]["u"],
+                           e["got"]["wsf"]) for e in g])
+    for g in reversed(groups):
+        pl.add_bwd_group([(e["qw"], e["t"]["x"], e["t"]["dY"], e["got"]["u"], e["t"]["A"], e["t"]["B"], wl.alpha,
+                           e["got"]["dx"], e["got"]["da"], e["got"]["db"], e["got"]["ws"], False)
+                          for e in reversed(g)])
+    for run in range(2):
+        for e in d:
+            for key in ("y", "u", "dx", "da", "db"):
+                e["got"][key].fill_(float("nan"))
+        pl.run()
+        torch.cuda.synchronize()
+        for e in d:
+            for key in ("y", "u", "dx", "da", "db"):
+                a, b = e["got"][key], e["ref"][key]
+                iv = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+                assert torch.equal(a.view(iv), b.view(iv)), (run, e["p"].name, key)
+    pl.close()
