@@ -125,8 +125,18 @@ void qgemm_kernel(GemmArgs ga) {
   const int nt = (int)((p.O + TN - 1) / TN);
   int t = bid - t0;
   if ((tiles & 7) == 0 && (t0 & 7) == 0) t = (t & 7) * (tiles >> 3) + (t >> 3);
-  const int64_t o0 = (int64_t)(t % nt) * TN;
-  const int64_t m0 = (int64_t)(t / nt) * TM;
+  // tiles in groups of GM row blocks, column by column within a group: the
+  // 32 workgroups an XCD runs at once then cover a few row blocks by several
+  // column tiles instead of one row block by 32 column tiles, so its L2 sees
+  // less of W per tile (for wide layers the whole of W passed through every
+  // XCD's L2 for each row block)
+  constexpr int GM = 4;
+  const int mt = tiles / nt;
+  const int grp = t / (GM * nt), fm = grp * GM;
+  const int gm = mt - fm < GM ? mt - fm : GM;        // row blocks in this group
+  const int tg = t - grp * GM * nt;
+  const int64_t o0 = (int64_t)(tg / gm) * TN;
+  const int64_t m0 = (int64_t)(fm + tg % gm) * TM;
   const int KT = (int)((p.C + TK - 1) / TK);
   const int kbeg = 0, kend = KT, NKT = KT;          // contraction steps of this workgroup
 
