@@ -30,6 +30,10 @@
  *   - Device pointers must be 16-byte aligned; M, N, K >= 1 (M may be 0:
  *     then nothing is launched), K and N multiples of the format's block
  *     (64 for NF4, 32 otherwise), r in {8, 16, 32}.
+ *   - Size limits (the kernels address memory through 32-bit buffer
+ *     offsets): N and K at most QL_MAX_FEATURES and the codes array of a
+ *     weight below 2 GiB; larger shapes are refused with QL_EUNSUPPORTED
+ *     (by every call that takes a weight or a shape, quant_pack included).
  *   - The quantized base is const: no call writes codes or scales.
  *   - Results do not depend on pointer values, only on shapes and data
  *     (fixed launch configuration and fixed reduction order per shape), so
@@ -56,6 +60,9 @@ extern "C" {
 #define QL_ENONFINITE (-5)    /* quant_pack saw NaN or Inf in W             */
 #define QL_ESTATE (-6)        /* stream-pool misuse                         */
 #define QL_EOVERFLOW (-7)     /* quant_pack: a Q4_0 scale overflows fp16    */
+
+/* largest N or K a weight may have (see the size limits above) */
+#define QL_MAX_FEATURES 524288
 
 /* ---------------------------------------------------------------- formats
  * 4-bit code layout (Q4_0 and NF4): codes are u8 [N, K/2]; each row is cut
@@ -140,6 +147,9 @@ size_t qlora_workspace_bytes(int32_t op, int32_t format, int64_t n_out,
                              int64_t k_in, int64_t m, int32_t r);
 
 /* ---------------------------------------------------------------- a0: pack
+ * (Surogate README page, "LoRA & QLoRA" row of the capability table: the base
+ * is quantized on load to FP8 or NF4; GGUF-recipe page, "How it works": the
+ * base stays in its compressed block form while training.)
  * Quantize fp32 W (dev [N, K]) into codes and scales (dev, layouts above).
  * Once per weight, not per step.  Blocks until the packed data is written
  * (so that non-finite input can be reported): returns QL_ENONFINITE if W
@@ -378,9 +388,10 @@ int ql_adamw_step(const ql_adamw_tensor* tensors, int32_t n_tensors,
                   const ql_adamw_hparams* hp, void* stream);
 
 /* ---------------------------------------------------------------- a10: layer stream
- * Soup page, opening paragraph: the frozen base lives in host RAM and
- * streams into a small pool of pre-allocated VRAM buffers one decoder layer
- * at a time, prefetched one layer ahead on a dedicated stream.
+ * (Soup page, opening paragraph.)  The frozen base is kept in page-locked
+ * host memory; a few device slots, allocated once by the caller, each hold
+ * one decoder layer's packed weights, and the copy of the next layer runs on
+ * a side stream while the current one computes.
  *
  * The caller allocates n_slots device buffers of slot_bytes each (slot_dev,
  * 256-byte aligned) and n_layers pinned host images (layer_host, page-locked,
@@ -419,6 +430,9 @@ int ql_pool_stats(const ql_pool* pool, int64_t* out3);
  * compute-stream wait (a deliberate race, for a negative control only). */
 int ql_pool_debug(ql_pool* pool, int32_t delay_us, int32_t poison,
                   int32_t skip_wait);
+/* Blocks until every copy the pool has enqueued has finished, then frees the
+ * pool's events and bookkeeping (the caller's slots and images are not
+ * touched).  QL_EHIP if waiting for a copy failed; the pool is freed anyway. */
 int ql_pool_destroy(ql_pool* pool);
 
 #ifdef __cplusplus

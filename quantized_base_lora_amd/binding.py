@@ -5,6 +5,7 @@ HIP stream; every arithmetic step runs in the library's HIP kernels.  If the
 library is missing this module raises; there is no CPU fallback.
 """
 
+import contextlib
 import ctypes
 import os
 
@@ -141,6 +142,13 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Allocation context for a call's temporaries: the caching allocator then
+    ties them to the stream the library enqueues on, so a temporary freed on
+    return is not reused by other work until that stream has passed the call."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
@@ -225,9 +233,10 @@ def quant_pack(fmt, w, out=None, ws=None, stream=None):
     """Pack fp32 W [N, K] (device) into a QWeight (blocks until done)."""
     _need(w, "w", torch.float32)
     n, k = w.shape
-    qw = out if out is not None else QWeight.alloc(fmt, n, k, device=w.device)
-    if ws is None:
-        ws = torch.empty(workspace_bytes(OP_PACK, fmt, n, k), dtype=torch.uint8, device=w.device)
+    with _on(stream):
+        qw = out if out is not None else QWeight.alloc(fmt, n, k, device=w.device)
+        if ws is None:
+            ws = torch.empty(workspace_bytes(OP_PACK, fmt, n, k), dtype=torch.uint8, device=w.device)
     _check(load().quant_pack(fmt, _ptr(w), n, k, _ptr(qw.codes), _ptr(qw.scales), _ptr(ws),
                              ws.numel(), _stream(stream)))
     return qw
@@ -235,8 +244,9 @@ def quant_pack(fmt, w, out=None, ws=None, stream=None):
 
 def dequant(qw, want_f32=True, want_bf16=True, stream=None):
     dev = qw.codes.device
-    f = torch.empty((qw.n, qw.k), dtype=torch.float32, device=dev) if want_f32 else None
-    b = torch.empty((qw.n, qw.k), dtype=torch.bfloat16, device=dev) if want_bf16 else None
+    with _on(stream):
+        f = torch.empty((qw.n, qw.k), dtype=torch.float32, device=dev) if want_f32 else None
+        b = torch.empty((qw.n, qw.k), dtype=torch.bfloat16, device=dev) if want_bf16 else None
     _check(load().qlora_dequant(qw.cstruct, _ptr(f), _ptr(b), _stream(stream)))
     return f, b
 
@@ -244,9 +254,10 @@ def dequant(qw, want_f32=True, want_bf16=True, stream=None):
 def act_quant_e4m3(x, stream=None):
     _need(x, "x", torch.bfloat16)
     m, k = x.shape
-    hi = torch.empty((m, k), dtype=torch.uint8, device=x.device)
-    lo = torch.empty((m, k), dtype=torch.uint8, device=x.device)
-    s = torch.empty(m, dtype=torch.float32, device=x.device)
+    with _on(stream):
+        hi = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+        lo = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+        s = torch.empty(m, dtype=torch.float32, device=x.device)
     _check(load().ql_act_quant_e4m3(_ptr(x), m, k, _ptr(hi), _ptr(lo), _ptr(s), _stream(stream)))
     return hi, lo, s
 
@@ -260,13 +271,14 @@ def linear_fwd(qw, x, a, b, alpha, y=None, u=None, ws=None, stream=None):
     _need(x, "x", torch.bfloat16, (m, qw.k))
     _need(a, "A", torch.bfloat16, (r, qw.k))
     _need(b, "B", torch.bfloat16, (qw.n, r))
-    if y is None:
-        y = torch.empty((m, qw.n), dtype=torch.bfloat16, device=x.device)
-    if u is None:
-        u = torch.empty((m, r), dtype=torch.float32, device=x.device)
     need = workspace_bytes(OP_FWD, qw.fmt, qw.n, qw.k, m, r)
-    if ws is None and need:
-        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    with _on(stream):
+        if y is None:
+            y = torch.empty((m, qw.n), dtype=torch.bfloat16, device=x.device)
+        if u is None:
+            u = torch.empty((m, r), dtype=torch.float32, device=x.device)
+        if ws is None and need:
+            ws = torch.empty(need, dtype=torch.uint8, device=x.device)
     _check(load().qlora_linear_fwd(qw.cstruct, _ptr(x), m, _ptr(a), _ptr(b), r, float(alpha),
                                    _ptr(y), _ptr(u), _ptr(ws), ws.numel() if ws is not None else 0,
                                    _stream(stream)))
@@ -282,15 +294,16 @@ def linear_bwd(qw, x, dy, u, a, b, alpha, need_dx=True, accumulate=False, dx=Non
     _need(dy, "dY", torch.bfloat16, (m, qw.n))
     _need(u, "U", torch.float32, (m, r))
     dev = x.device
-    if need_dx and dx is None:
-        dx = torch.empty((m, qw.k), dtype=torch.bfloat16, device=dev)
-    if da is None:
-        da = torch.zeros((r, qw.k), dtype=torch.float32, device=dev)
-    if db is None:
-        db = torch.zeros((qw.n, r), dtype=torch.float32, device=dev)
     need = workspace_bytes(OP_BWD, qw.fmt, qw.n, qw.k, m, r)
-    if ws is None:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    with _on(stream):
+        if need_dx and dx is None:
+            dx = torch.empty((m, qw.k), dtype=torch.bfloat16, device=dev)
+        if da is None:
+            da = torch.zeros((r, qw.k), dtype=torch.float32, device=dev)
+        if db is None:
+            db = torch.zeros((qw.n, r), dtype=torch.float32, device=dev)
+        if ws is None:
+            ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _check(load().qlora_linear_bwd(qw.cstruct, _ptr(x), _ptr(dy), _ptr(u), m, _ptr(a), _ptr(b), r,
                                    float(alpha), _ptr(dx) if need_dx else None, _ptr(da), _ptr(db),
                                    1 if accumulate else 0, _ptr(ws), ws.numel(), _stream(stream)))

@@ -47,6 +47,15 @@ int check_shape(int32_t fmt, int64_t n, int64_t k) {
   if (n <= 0 || k <= 0) return set_error(QL_EINVAL, "n_out and k_in must be positive");
   if (k % block_of(fmt)) return set_error(QL_EINVAL, "k_in=%lld is not a multiple of %d", (long long)k, block_of(fmt));
   if (n % 32) return set_error(QL_EINVAL, "n_out=%lld is not a multiple of 32", (long long)n);
+  // every buffer offset a kernel forms must fit 31 bits: rows of at most
+  // QL_MAX_FEATURES elements (a 256-row tile, a 512-row gradient partition and
+  // 16 split partials of 64 tokens stay below 2 GiB) and codes below 2 GiB
+  if (n > QL_MAX_FEATURES || k > QL_MAX_FEATURES)
+    return set_error(QL_EUNSUPPORTED, "n_out=%lld, k_in=%lld: at most %d features per side", (long long)n,
+                     (long long)k, QL_MAX_FEATURES);
+  const int64_t code_bytes = (fmt == QL_FMT_FP8_E4M3 || fmt == QL_FMT_Q8_0) ? n * k : n * k / 2;
+  if (code_bytes > 0x7FFFFFFFLL)
+    return set_error(QL_EUNSUPPORTED, "codes of %lld bytes: at most 2 GiB - 1 per weight", (long long)code_bytes);
   return QL_OK;
 }
 

@@ -33,8 +33,10 @@ struct Slot {
   uint64_t release_tick = 0;
 };
 
+// test hook: the delay travels in the pointer argument itself, so the host
+// function reads no pool memory (the pool may be gone by the time it runs)
 void sleep_host(void* arg) {
-  int us = *reinterpret_cast<int*>(arg);
+  const int us = (int)reinterpret_cast<intptr_t>(arg);
   std::this_thread::sleep_for(std::chrono::microseconds(us));
 }
 }  // namespace
@@ -110,7 +112,8 @@ int layer_stream_prefetch(ql_pool* p, int32_t layer, void* copy_stream) {
                                    (int64_t)(p->slot_bytes / 4), 0xFFFFFFFFu, cs);
     if (e != hipSuccess) return hip_error(e, "pool poison fill");
   }
-  if (p->delay_us > 0) QL_HIP(hipLaunchHostFunc(cs, sleep_host, &p->delay_us));
+  if (p->delay_us > 0)
+    QL_HIP(hipLaunchHostFunc(cs, sleep_host, reinterpret_cast<void*>((intptr_t)p->delay_us)));
   const size_t nb = p->layer_bytes[layer];
   QL_HIP(hipMemcpyAsync(p->slot_dev[pick], p->layer_host[layer], nb, hipMemcpyHostToDevice, cs));
   QL_HIP(hipEventRecord(s.ready, cs));
@@ -165,14 +168,22 @@ int ql_pool_debug(ql_pool* p, int32_t delay_us, int32_t poison, int32_t skip_wai
   return QL_OK;
 }
 
+// Waits until every copy the pool enqueued has finished (each slot's last
+// ready event), so no queued copy or test hook outlives the pool's events.
 int ql_pool_destroy(ql_pool* p) {
   if (!p) return QL_OK;
+  hipError_t first = hipSuccess;
+  for (auto& s : p->slots)
+    if (s.ready && s.state != EMPTY) {
+      hipError_t e = hipEventSynchronize(s.ready);
+      if (first == hipSuccess) first = e;
+    }
   for (auto& s : p->slots) {
     if (s.ready) (void)hipEventDestroy(s.ready);
     if (s.freed) (void)hipEventDestroy(s.freed);
   }
   delete p;
-  return QL_OK;
+  return first == hipSuccess ? QL_OK : hip_error(first, "pool destroy: waiting for queued copies");
 }
 
 }  // extern "C"

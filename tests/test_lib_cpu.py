@@ -99,6 +99,29 @@ def test_layer_argument_errors(lib):
     assert lib.ql_act_quant_e4m3(P, 4, 24, P, P, P, None) == binding.QL_EINVAL
 
 
+def test_size_limits_refused(lib):
+    """Shapes whose 32-bit buffer offsets would overflow are refused before
+    any launch: more than QL_MAX_FEATURES per side, or codes of 2 GiB or more
+    (the one-byte formats reach it first)."""
+    P = FAKE
+    big = 524288
+    assert lib.quant_pack(binding.FMT_NF4, P, 64, 2 * big, P, P, P, 256, None) == binding.QL_EUNSUPPORTED
+    assert "features" in _err(lib)
+    assert lib.quant_pack(binding.FMT_Q4_0, P, 2 * big, 64, P, P, P, 256, None) == binding.QL_EUNSUPPORTED
+    # 65536 x 32768 one-byte codes = 2 GiB: refused; the 4-bit form (1 GiB) passes the size check
+    assert lib.quant_pack(binding.FMT_Q8_0, P, 65536, 32768, P, P, P, 256, None) == binding.QL_EUNSUPPORTED
+    assert "2 GiB" in _err(lib)
+    assert lib.quant_pack(binding.FMT_Q4_0, P, 65536, 32768, P, P, P, 8, None) == binding.QL_EWORKSPACE
+    qw = _qw(binding.FMT_FP8, 65536, 32768)
+    assert lib.qlora_linear_fwd(ctypes.byref(qw), P, 16, P, P, 16, 16.0, P, P, None, 0, None) == binding.QL_EUNSUPPORTED
+    qw = _qw(binding.FMT_NF4, 64, 2 * big)
+    assert lib.qlora_linear_bwd(ctypes.byref(qw), P, P, P, 16, P, P, 16, 16.0, P, P, P, 0, P, 1 << 30,
+                                None) == binding.QL_EUNSUPPORTED
+    assert lib.qlora_dequant(ctypes.byref(qw), P, P, None) == binding.QL_EUNSUPPORTED
+    # the largest accepted side
+    assert lib.quant_pack(binding.FMT_NF4, P, 64, big, P, P, P, 8, None) == binding.QL_EWORKSPACE
+
+
 def test_pool_argument_errors(lib):
     h = ctypes.c_void_p()
     slots = (ctypes.c_void_p * 2)(0x10000, 0x10100)
