@@ -2,19 +2,31 @@
 
 One step = forward of every projection of a decoder layer (7 LoRA linears over
 a frozen quantized base), then backward of every projection (dX, dA, dB), on
-synthetic seeded inputs resident in HBM.  Reported value: tokens/s per layer.
+synthetic seeded inputs resident in HBM, issued in the launch configuration
+of layer.LayerStep (a recorded launch plan, q|k|v and gate|up grouped).
+Reported value: tokens/s per layer.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--m M]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+        every workload in one JSON line: the headline is the largest layer,
+        the Qwen3-8B layer with an FP8 E4M3 base at 8192 tokens; the single
+        256->256 linear, the Qwen3-0.6B NF4 layer (8192 tokens), the
+        Llama-3.1-8B NF4 layer (4096, 64, 16 tokens) and the 32-layer
+        Llama-3.1-8B stack streamed from pinned host memory (2048 and 16
+        tokens, checked bit for bit against the resident stack) are
+        sub-records under "configs"
+    python bench.py --workload NAME [--m M] [--layers L]   one workload only
+    python bench.py --optimizer --workload NAME            the fused AdamW step
 
-Prints ONE JSON line.  Besides the headline value it carries the roofline of
-the dominant kernel (its launches bracketed by HIP events on the stream they
-run on) and the CPU oracle timed on this host on a bounded sample.
+Each record carries the roofline of its dominant kernel (the forward
+launches of its steps, back to back, bracketed by one HIP event pair on the
+stream they run on); the headline also carries the CPU oracle timed on this
+host (one thread and all cores) on a bounded sample.
 """
 
 import argparse
-import dataclasses
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -30,6 +42,13 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 FMT_NAME = {1: "q4_0", 2: "nf4", 3: "fp8_e4m3", 4: "mxfp4", 5: "q8_0"}
 BPW = {1: 18 / 32, 2: 0.5 + 4 / 64, 3: 1.0, 4: 17 / 32, 5: 34 / 32}
+ROTATE_BYTES = 512e6           # packed weight copies rotated per config (the MALL is 256 MB)
+MAX_CFG_STEPS = 20000          # sub-record steps: enough to pass over every rotated copy
+
+HEADLINE = ("qwen3_8b_fp8", 8192)
+LAYER_CONFIGS = [("single256_q40", 64), ("qwen3_0.6b_nf4", 8192), ("llama3.1_8b_nf4", 4096),
+                 ("llama3.1_8b_nf4", 64), ("llama3.1_8b_nf4", 16), ("qwen3_8b_fp8", 8192)]
+STACK_WORKLOAD, STACK_LAYERS, STACK_TOKENS = "llama3.1_8b_nf4_stack32", 32, (2048, 16)
 
 
 def parse():
@@ -37,23 +56,17 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="qwen3_0.6b_nf4")
+    ap.add_argument("--workload", default=None, help="one workload only (default: every workload)")
     ap.add_argument("--m", type=int, default=None, help="tokens (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=0, help="tokens in the CPU oracle sample (0: all)")
-    ap.add_argument("--copies", type=int, default=0, help="packed weight copies rotated per step (0: auto)")
+    ap.add_argument("--cpu-tokens", type=int, default=64, help="tokens in the CPU oracle sample")
+    ap.add_argument("--copies", type=int, default=0, help="packed weight copies rotated (0: >= 512 MB)")
     ap.add_argument("--proj", default=None, help="run only this projection (profiling)")
     ap.add_argument("--exclude", default="",
                     help="comma-separated projections left out of the layer (e.g. o), in the timing and in "
                          "every per-layer figure")
     ap.add_argument("--phase", default="both", choices=["both", "fwd", "bwd"], help="profiling: one pass only")
-    ap.add_argument("--graph", action="store_true",
-                    help="time HIP-graph replays of the step instead of eager launches")
-    ap.add_argument("--streams", action="store_true",
-                    help="run projections that are independent in a decoder layer (q|k|v, gate|up) "
-                         "on parallel streams")
-    ap.add_argument("--no-plan", action="store_true",
-                    help="issue each layer call from Python instead of through a recorded launch plan")
+    ap.add_argument("--no-stack", action="store_true", help="leave the streamed stack out of the full run")
     ap.add_argument("--optimizer", action="store_true",
                     help="time the fused AdamW step on the layer's adapters instead of the layer step")
     ap.add_argument("--layers", type=int, default=0,
@@ -63,6 +76,8 @@ def parse():
                          "to calibrate HBM byte counters) and exit")
     return ap.parse_args()
 
+
+# ----------------------------------------------------------------------------- accounting
 
 def layer_flops(wl, m):
     return sum(m * (4 * p.n * p.k + 6 * wl.r * (p.k + p.n)) for p in wl.projs)
@@ -80,17 +95,25 @@ def fwd_kernel_flops(wl, p, m):
     return m * (2 * p.n * p.k + 2 * wl.r * (p.k + p.n))
 
 
+def fwd_kernel_bytes(wl, p, m):
+    """Algorithmic bytes of one forward call: the packed base, x and A read,
+    y written (bf16), U written (fp32), B read."""
+    return BPW[wl.fmt] * p.n * p.k + 2 * m * (p.k + p.n) + 4 * m * wl.r + 2 * wl.r * (p.k + p.n)
+
+
 def source_hash():
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "quantized_base_lora_amd", "csrc", "kernels_gemm.hip"), "rb") as f:
-        h.update(f.read())
+    csrc = os.path.join(ROOT, "quantized_base_lora_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(workload, m):
+def traffic_from_profile(key):
     """HBM bytes per dominant-kernel launch from committed rocprofv3 counters,
-    if they were taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "qgemm_fwd_counters.json")
+    if they were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "fwd_counters.json")
     try:
         with open(path) as f:
             d = json.load(f)
@@ -98,9 +121,284 @@ def traffic_from_profile(workload, m):
         return None
     if d.get("kernel_source_sha") != source_hash():
         return None
-    e = d.get("workloads", {}).get(f"{workload}@{m}")
+    e = d.get("configs", {}).get(key)
     return None if e is None else e.get("hbm_bytes_per_launch")
 
+
+def copies_for(packed_bytes, override=0):
+    return override or max(1, math.ceil(ROTATE_BYTES / max(1, packed_bytes)))
+
+
+def roofline_kind(wl, m):
+    if m <= 64:
+        return {"kernel": "qsplit16_kernel / qsplit_kernel + split_reduce_kernel (forward: split-contraction "
+                          "dequant GEMM, fixed-order reduction with the fused LoRA term)",
+                "bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    if wl.fmt == 3:
+        return {"kernel": "qgemm8_kernel with act_quant_kernel and rproj_kernel (forward: fp8 GEMM over the "
+                          "two-term E4M3 activation split, rank-r projection, fused LoRA term)",
+                "bound": "mfma", "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "executed_fp8_flops_per_algorithmic": 2}
+    return {"kernel": "qgemm_kernel (forward: dequant GEMM + fused LoRA)", "bound": "mfma",
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+
+
+# ----------------------------------------------------------------------------- one layer
+
+def bench_layer(args, wl, m, steps, exclude=(), only=None):
+    """Time one layer config; returns its record (without cpu_baseline)."""
+    import torch
+
+    from quantized_base_lora_amd import binding as B, layer
+
+    est = sum(BPW[wl.fmt] * p.n * p.k for p in wl.projs
+              if p.name not in exclude and (only is None or p.name == only))
+    copies = copies_for(est, args.copies)
+    ls = layer.LayerStep(wl, m, copies=copies, exclude=exclude, only=only)
+    packed = ls.packed_bytes()
+    if exclude or only:
+        import dataclasses
+        wl = dataclasses.replace(wl, projs=tuple(d["p"] for d in ls.projs))
+    stream = torch.cuda.Stream()             # default priority
+    torch.cuda.set_stream(stream)
+    plans = ls.plans(args.phase)
+    torch.cuda.synchronize()
+
+    # the roofline's kernel timing: the forward launches of `steps` steps back to
+    # back, weight copies rotated as the steps rotate them, one event pair around
+    # all of them (an event per step would add its own cost to every step)
+    roof = None
+    if args.phase != "bwd":
+        roof = B.Plan()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        roof.add_event(e0, stream)
+        for i in range(steps):
+            for g in ls.groups:
+                roof.add_fwd_group(ls.fwd_items(g, i))
+        roof.add_event(e1, stream)
+
+    for i in range(args.warmup):
+        plans[i % copies].run(stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        plans[i % copies].run(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    # spread of single steps, from a separate pass with an event between steps
+    ns = min(steps, 200)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)]
+    evs[0].record(stream)
+    for i in range(ns):
+        plans[i % copies].run(stream)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(ns)])
+    spread = {"p10": float(np.percentile(per_step, 10)), "median": float(np.median(per_step)),
+              "p90": float(np.percentile(per_step, 90)), "steps": ns,
+              "pass": "separate, one event between steps"}
+
+    rec = {"workload": wl.notes, "name": wl.name, "tokens": m, "base_format": FMT_NAME[wl.fmt],
+           "rank": wl.r, "alpha": wl.alpha, "projections": [f"{p.name}:{p.k}->{p.n}" for p in wl.projs],
+           "steps": steps, "warmup": args.warmup, "ms_per_step": ms, "tokens_per_s": m / (ms / 1e3),
+           "ms_per_step_spread": spread, "packed_bytes_per_copy": packed, "packed_copies_rotated": copies,
+           "rotated_bytes": packed * copies, "copies_touched_in_timed_steps": min(copies, steps),
+           "step_mode": "eager launches, one library call per step (recorded launch plan; q|k|v and "
+                        "gate|up as grouped calls), one stream"}
+    flops, nbytes = layer_flops(wl, m), layer_bytes(wl, m)
+    rec["layer"] = {"tflops": flops / (ms / 1e3) / 1e12, "frac_bf16_peak": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+                    "algorithmic_bytes": nbytes, "hbm_gbs": nbytes / (ms / 1e3) / 1e9,
+                    "frac_hbm_peak": nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS}
+    if roof is not None:
+        roof.run(stream)                       # untimed pass
+        roof.run(stream)
+        torch.cuda.synchronize()
+        fwd_ms = e0.elapsed_time(e1)
+        n_launch = ls.fwd_launches_per_step() * steps
+        n_calls = len(ls.projs) * steps
+        avg_ms = fwd_ms / n_launch
+        r = roofline_kind(wl, m)
+        if r["bound"] == "hbm":
+            per_launch = sum(fwd_kernel_bytes(wl, d["p"], m) for d in ls.projs) * steps / n_launch
+            achieved = per_launch / (avg_ms / 1e3) / 1e9
+            r["bytes_per_launch_avg"] = per_launch
+        else:
+            per_launch = sum(fwd_kernel_flops(wl, d["p"], m) for d in ls.projs) * steps / n_launch
+            achieved = per_launch / (avg_ms / 1e3) / 1e12
+            r["flops_per_launch_avg"] = per_launch
+        r.update({"achieved": achieved, "frac": achieved / r["peak"],
+                  "traffic": traffic_from_profile(f"{wl.name}@{m}"),
+                  "avg_launch_us": avg_ms * 1e3, "launches_timed": n_launch, "calls_timed": n_calls,
+                  "timing": "one HIP event pair around the forward launches of the config's steps, enqueued "
+                            "back to back by one launch plan, total / launches"})
+        rec["roofline"] = r
+        roof.close()
+    ls.close()
+    del ls, plans
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+# ----------------------------------------------------------------------------- the streamed stack
+
+def h2d_bandwidth(stream):
+    """Pinned host -> device bandwidth, 1 GiB copies, in this process."""
+    import torch
+    hb = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    db = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    db.copy_(hb, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(3):
+        db.copy_(hb, non_blocking=True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return 3 * (1 << 30) / (e0.elapsed_time(e1) / 1e3) / 1e9
+
+
+def bench_stack(args, wl, n_layers, tokens, steps):
+    """The layer stack: L layers, forward 0..L-1 then backward L-1..0, the
+    packed bases resident in HBM or streamed from pinned host memory through
+    two device slots (one layer ahead on a side stream).  The streamed run's
+    outputs (every output of every layer, from its last timed step) are
+    compared bit for bit with the resident run's.  Returns one record per
+    token count."""
+    import torch
+
+    from quantized_base_lora_amd import stack
+
+    t0 = time.time()
+    layout, host, _ = stack.build_host_images(wl, n_layers)
+    prep_s = time.time() - t0
+    stream = torch.cuda.current_stream()
+    h2d_gbs = h2d_bandwidth(stream)
+    groups = stack.layer_groups(wl.projs)
+
+    def timed(st, acts, outs):
+        for _ in range(args.warmup):
+            st.run(acts, outs, groups)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            st.run(acts, outs, groups)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    recs = []
+    for m in tokens:
+        acts = stack.layer_inputs(wl, m, n_layers)
+        o_res = stack.layer_outputs(wl, m, n_layers)
+        dev_imgs = [h.to("cuda") for h in host]
+        ms_res = timed(stack.Stack(layout, wl.r, wl.alpha, images_dev=dev_imgs), acts, o_res)
+        del dev_imgs
+        torch.cuda.empty_cache()
+        o_st = stack.layer_outputs(wl, m, n_layers)
+        st = stack.Stack(layout, wl.r, wl.alpha, images_host=host, n_slots=2)
+        ms_st = timed(st, acts, o_st)
+        stats = st.pool.stats()
+        st.close()
+        equal, first, worst = stack.compare_outputs(o_res, o_st)
+        n_out = n_layers * len(wl.projs) * len(stack.OUTPUT_KEYS)
+        del acts, o_res, o_st
+        torch.cuda.empty_cache()
+        copies_per_step = 2 * n_layers - 2
+        copy_ms = copies_per_step * layout.nbytes / (h2d_gbs * 1e9) * 1e3
+        recs.append({
+            "workload": wl.notes, "name": wl.name, "tokens": m, "layers": n_layers,
+            "base_format": FMT_NAME[wl.fmt], "rank": wl.r, "alpha": wl.alpha,
+            "steps": steps, "warmup": args.warmup, "ms_per_step": ms_st, "tokens_per_s": m / (ms_st / 1e3),
+            "layer_image_bytes": layout.nbytes, "slots": 2,
+            "calls": "grouped q|k|v, o, gate|up, down" if groups else "one call per projection",
+            "resident_ms_per_step": ms_res, "resident_tokens_per_s": m / (ms_res / 1e3),
+            "streamed_over_resident": ms_st / ms_res, "copies_per_step": copies_per_step,
+            "streamed_bytes_per_step": copies_per_step * layout.nbytes, "pinned_h2d_gbs": h2d_gbs,
+            "copy_ms_at_measured_h2d": copy_ms, "overlap_efficiency": max(copy_ms, ms_res) / ms_st,
+            "roofline": {"kernel": "host-to-device copies of the layer images (PCIe)", "bound": "pcie",
+                         "achieved": copies_per_step * layout.nbytes / (ms_st / 1e3) / 1e9,
+                         "peak": h2d_gbs, "unit": "GB/s",
+                         "frac": copies_per_step * layout.nbytes / (ms_st / 1e3) / 1e9 / h2d_gbs,
+                         "peak_is": "pinned H2D bandwidth measured in this run"},
+            "check": {"streamed_equals_resident_bitwise": bool(equal), "max_abs_diff": worst,
+                      "outputs_compared": n_out, "first_mismatch": first,
+                      "what": "every y, U, dX, dA, dB of every layer, last timed step of each run"},
+            "pool_stats_total": stats, "host_prep_s": prep_s})
+    del host
+    return recs
+
+
+# ----------------------------------------------------------------------------- oracle on the host
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, m, tokens, min_seconds=5.0):
+    """The oracle (numpy, fp64 products) on a bounded sample of the layer:
+    the first `tokens` tokens of the same seeded inputs (drawn on the GPU and
+    copied to the host), every projection's base packed and dequantized by the
+    oracle beforehand (untimed); then forward + backward of every projection,
+    repeated until min_seconds of wall time, once on one thread and once on
+    every core the process may use."""
+    import torch
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import formats as ofmt, lora as olora
+    from quantized_base_lora_amd import synth
+
+    t0 = time.time()
+    prep = []
+    for pi in range(len(wl.projs)):
+        t = synth.layer_tensors_torch(wl, pi, m=m)
+        w = t["W"].cpu().numpy()
+        codes, scales = ofmt.pack(wl.fmt, w)
+        wd = ofmt.dequant(wl.fmt, codes, scales)
+        del w, codes, scales
+        prep.append(tuple(t[k][:tokens].float().cpu().numpy() if k in ("x", "dY") else t[k].float().cpu().numpy()
+                          for k in ("x", "dY", "A", "B")) + (wd,))
+        del t
+    torch.cuda.empty_cache()
+    prep_s = time.time() - t0
+
+    def run(limit):
+        passes, dt = 0, 0.0
+        with threadpool_limits(limit):
+            while dt < min_seconds and passes < 50:
+                t1 = time.perf_counter()
+                for x, dy, a, b, wd in prep:
+                    olora.forward(x, wd, a, b, wl.alpha)
+                    olora.backward(x, dy, wd, a, b, wl.alpha)
+                dt += time.perf_counter() - t1
+                passes += 1
+        return tokens * passes / dt, passes, dt
+
+    one, p1, d1 = run(1)
+    cores = len(os.sched_getaffinity(0))
+    allc, pa, da = run(cores)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] + [1])
+    return {"value": allc, "unit": "tokens/s", "cores": int(min(cores, threads)), "kind": "oracle",
+            "single_thread": {"value": one, "unit": "tokens/s", "cores": 1, "passes": p1, "seconds": d1},
+            "all_cores": {"value": allc, "unit": "tokens/s", "cores": cores, "passes": pa, "seconds": da},
+            "cpu_model": cpu_model(), "host_cpus_visible": cores, "untimed_prep_s": prep_s,
+            "sample": f"first {tokens} of the {m} tokens of the same layer (all {len(wl.projs)} projections, "
+                      f"forward + backward, fp64 products; every base packed and dequantized by the oracle "
+                      f"beforehand, untimed); tokens/s scales linearly in tokens"}
+
+
+# ----------------------------------------------------------------------------- AdamW mode
 
 def optimizer_bench(args, wl):
     """The fused AdamW step over all adapter tensors of one layer (A and B of
@@ -116,7 +414,7 @@ def optimizer_bench(args, wl):
         sizes += [wl.r * p.k, p.n * wl.r]
     n_el = sum(sizes)
     per_el = 30
-    copies = max(1, int(np.ceil(512e6 / (n_el * 18))))
+    copies = max(1, int(np.ceil(ROTATE_BYTES / (n_el * 18))))
     gen = torch.Generator(device=dev).manual_seed(1)
     sets = []
     for _ in range(copies):
@@ -158,159 +456,20 @@ def optimizer_bench(args, wl):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(wl, tokens, min_seconds=10.0):
-    """The oracle (numpy, fp64 products) on `tokens` tokens of the same layer:
-    W dequantized once beforehand, then forward + backward of every
-    projection, repeated until at least min_seconds of wall time."""
-    from threadpoolctl import threadpool_info
+# ----------------------------------------------------------------------------- main
 
-    from oracle import formats as ofmt, lora as olora
-    from quantized_base_lora_amd import synth
-    f32 = synth.bf16_bits_to_f32
-    prep = []
-    for pi, _ in enumerate(wl.projs):
-        c = synth.layer_tensors(wl, pi, m=tokens)
-        codes, scales = ofmt.pack(wl.fmt, c["W"])
-        wd = ofmt.dequant(wl.fmt, codes, scales)
-        prep.append((f32(c["x"]), f32(c["dY"]), wd, f32(c["A"]), f32(c["B"])))
-    passes, dt = 0, 0.0
-    while dt < min_seconds and passes < 50:
-        t0 = time.perf_counter()
-        for x, dy, wd, a, b in prep:
-            olora.forward(x, wd, a, b, wl.alpha)
-            olora.backward(x, dy, wd, a, b, wl.alpha)
-        dt += time.perf_counter() - t0
-        passes += 1
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": tokens * passes / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{tokens} tokens of the same layer (all {len(wl.projs)} projections, fwd+bwd, "
-                      f"fp64 products, W dequantized beforehand), {passes} passes in {dt:.2f} s wall; "
-                      f"BLAS threads {threads}, host cpus visible {len(os.sched_getaffinity(0))}"}
-
-
-def bench_stack(args, wl, m):
-    """The layer stack: L Llama-shaped layers, forward 0..L-1 then backward
-    L-1..0, with the packed bases resident in VRAM or streamed from pinned
-    host memory through two device slots (one layer ahead on a side stream).
-    Bases are random normal W packed on the GPU; activations and adapters are
-    seeded normals generated on the GPU (their values do not affect timing)."""
-    import torch
-
-    from quantized_base_lora_amd import binding as B, stack
-
-    dev = torch.device("cuda:0")
-    L = args.layers
-    layout = stack.LayerLayout(wl.fmt, wl.projs)
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(1234)
-    host = []
-    t0 = time.time()
-    for layer in range(L):
-        qws = []
-        for p in wl.projs:
-            w = torch.randn((p.n, p.k), generator=gen, device=dev, dtype=torch.float32) * 0.02
-            qws.append(B.quant_pack(wl.fmt, w))
-            del w
-        img = layout.image_from(qws)
-        h = torch.empty(layout.nbytes, dtype=torch.uint8, pin_memory=True)
-        h.copy_(img)
-        host.append(h)
-        del img, qws
-    torch.cuda.synchronize()
-    prep_s = time.time() - t0
-
-    def bf16(shape, std):
-        return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * std).to(torch.bfloat16)
-
-    acts, outs = [], []
-    for layer in range(L):
-        al, ol = [], []
-        for p in wl.projs:
-            al.append({"x": bf16((m, p.k), 1.0), "dy": bf16((m, p.n), 1.0),
-                       "a": bf16((wl.r, p.k), p.k ** -0.5), "b": bf16((p.n, wl.r), 0.01)})
-            ol.append({"y": torch.empty((m, p.n), dtype=torch.bfloat16, device=dev),
-                       "u": torch.empty((m, wl.r), dtype=torch.float32, device=dev),
-                       "dx": torch.empty((m, p.k), dtype=torch.bfloat16, device=dev),
-                       "da": torch.empty((wl.r, p.k), dtype=torch.float32, device=dev),
-                       "db": torch.empty((p.n, wl.r), dtype=torch.float32, device=dev),
-                       "ws": torch.empty(max(256, B.workspace_bytes(B.OP_BWD, wl.fmt, p.n, p.k, m, wl.r)),
-                                         dtype=torch.uint8, device=dev),
-                       "wsf": torch.empty(max(256, B.workspace_bytes(B.OP_FWD, wl.fmt, p.n, p.k, m, wl.r)),
-                                          dtype=torch.uint8, device=dev)})
-        acts.append(al)
-        outs.append(ol)
-    stream = torch.cuda.current_stream()
-    # independent projections of a decoder layer as grouped calls (q|k|v, gate|up)
-    names = [p.name for p in wl.projs]
-    groups = [[names.index(n) for n in g if n in names] for g in (["q", "k", "v"], ["o"], ["gate", "up"], ["down"])]
-    groups = [g for g in groups if g]
-    if sorted(i for g in groups for i in g) != list(range(len(names))):
-        groups = None
-
-    def timed(st, steps, warmup):
-        for _ in range(warmup):
-            st.run(acts, outs, groups)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            st.run(acts, outs, groups)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
-
-    # pinned host -> device bandwidth, 1 GiB, in the same process
-    hb = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
-    db = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    db.copy_(hb, non_blocking=True)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(3):
-        db.copy_(hb, non_blocking=True)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    h2d_gbs = 3 * (1 << 30) / (e0.elapsed_time(e1) / 1e3) / 1e9
-    del hb, db
-
-    dev_imgs = [h.to(dev) for h in host]
-    res = stack.Stack(layout, wl.r, wl.alpha, images_dev=dev_imgs)
-    ms_res = timed(res, args.steps, args.warmup)
-    del res, dev_imgs
-    torch.cuda.empty_cache()
-    st = stack.Stack(layout, wl.r, wl.alpha, images_host=host, n_slots=2)
-    ms_st = timed(st, args.steps, args.warmup)
-    stats = st.pool.stats()
-    st.close()
-    copies_per_step = 2 * L - 2
-    copy_ms = copies_per_step * layout.nbytes / (h2d_gbs * 1e9) * 1e3
-    out = {
-        "metric": "QLoRA stack fwd+bwd tokens/s, base streamed from pinned host",
-        "value": m / (ms_st / 1e3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_st,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": wl.notes, "name": wl.name, "tokens": m, "layers": L,
-                   "base_format": FMT_NAME[wl.fmt], "rank": wl.r, "alpha": wl.alpha,
-                   "layer_image_bytes": layout.nbytes, "slots": 2,
-                   "calls": "grouped q|k|v, o, gate|up, down" if groups else "one call per projection"},
-        "stack": {"resident_ms_per_step": ms_res, "resident_tokens_per_s": m / (ms_res / 1e3),
-                  "streamed_over_resident": ms_st / ms_res,
-                  "copies_per_step": copies_per_step,
-                  "streamed_bytes_per_step": copies_per_step * layout.nbytes,
-                  "pinned_h2d_gbs": h2d_gbs,
-                  "copy_ms_at_measured_h2d": copy_ms,
-                  "overlap_efficiency": max(copy_ms, ms_res) / ms_st,
-                  "pool_stats_total": stats, "host_prep_s": prep_s},
-    }
-    print(json.dumps(out), flush=True)
+def line_from(rec, args, steps):
+    """The JSON line's top level from one layer record."""
+    dtype = "fp8_e4m3 base on fp8 MFMA, bf16 activations and adapters" if rec["base_format"] == "fp8_e4m3" \
+        else "bf16"
+    return {"metric": METRIC, "value": rec["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+            "warmup": args.warmup, "ms_per_step": rec["ms_per_step"],
+            "ms_per_step_spread": rec.get("ms_per_step_spread"), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+            "config": {k: rec[k] for k in ("workload", "name", "tokens", "base_format", "rank", "alpha",
+                                           "projections", "packed_copies_rotated", "rotated_bytes",
+                                           "step_mode") if k in rec},
+            "layer": rec.get("layer"), "roofline": rec.get("roofline")}
 
 
 def main():
@@ -333,265 +492,58 @@ def main():
     from quantized_base_lora_amd import binding as B, synth
 
     B.load()
-    wl = synth.WORKLOADS[args.workload]
-    m = args.m or wl.m
-    if args.layers:
-        return bench_stack(args, wl, m)
-    if args.optimizer:
-        return optimizer_bench(args, wl)
-    dev = torch.device("cuda:0")
-    stream = torch.cuda.Stream()             # default priority; capturable (not the legacy stream)
-    torch.cuda.set_stream(stream)
+    if args.workload is not None:
+        wl = synth.WORKLOADS[args.workload]
+        m = args.m or wl.m
+        if args.optimizer:
+            return optimizer_bench(args, wl)
+        if args.layers:
+            for rec in bench_stack(args, wl, args.layers, (m,), args.steps):
+                out = {"metric": "QLoRA stack fwd+bwd tokens/s, base streamed from pinned host",
+                       "value": rec["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+                       "warmup": args.warmup, "ms_per_step": rec["ms_per_step"], "higher_is_better": True,
+                       "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                       "config": {"workload": rec["workload"], "tokens": m, "layers": args.layers}, "stack": rec}
+                print(json.dumps(out), flush=True)
+            return
+        excluded = tuple(filter(None, args.exclude.split(",")))
+        rec = bench_layer(args, wl, m, args.steps, exclude=excluded, only=args.proj)
+        out = line_from(rec, args, args.steps)
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline(wl, m, min(args.cpu_tokens, m))
+        print(json.dumps(out), flush=True)
+        return
 
-    def t(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    # inputs, packed bases and preallocated outputs / workspaces
-    projs = []
-    packed_bytes = 0
-    excluded = set(filter(None, args.exclude.split(",")))
-    for pi, p in enumerate(wl.projs):
-        if (args.proj and p.name != args.proj) or p.name in excluded:
-            continue
-        c = synth.layer_tensors(wl, pi, m=m)
-        qw = B.quant_pack(wl.fmt, torch.from_numpy(c["W"]).to(dev))
-        packed_bytes += qw.nbytes()
-        d = {"p": p, "qws": [qw], "x": t(c["x"]), "dy": t(c["dY"]), "a": t(c["A"]), "b": t(c["B"]),
-             "y": torch.empty((m, p.n), dtype=torch.bfloat16, device=dev),
-             "u": torch.empty((m, wl.r), dtype=torch.float32, device=dev),
-             "dx": torch.empty((m, p.k), dtype=torch.bfloat16, device=dev),
-             "da": torch.empty((wl.r, p.k), dtype=torch.float32, device=dev),
-             "db": torch.empty((p.n, wl.r), dtype=torch.float32, device=dev),
-             "ws": torch.empty(max(256, B.workspace_bytes(B.OP_BWD, wl.fmt, p.n, p.k, m, wl.r)),
-                               dtype=torch.uint8, device=dev),
-             "wsf": torch.empty(max(256, B.workspace_bytes(B.OP_FWD, wl.fmt, p.n, p.k, m, wl.r)),
-                                dtype=torch.uint8, device=dev)}
-        projs.append(d)
-    if excluded:
-        # per-layer accounting over the projections that run (inputs keep their seeds)
-        wl = dataclasses.replace(wl, projs=tuple(p for p in wl.projs if p.name not in excluded))
-    # rotate packed copies so weight reads come from HBM, not the 256 MB MALL
-    copies = args.copies or max(1, min(8, int(np.ceil(512e6 / packed_bytes))))
-    for d in projs:
-        base = d["qws"][0]
-        for _ in range(copies - 1):
-            q2 = B.QWeight(base.fmt, base.n, base.k, base.codes.clone(), base.scales.clone())
-            d["qws"].append(q2)
-    torch.cuda.synchronize()
-
-    ev_pairs = []
-
-    def fwd(d, i, st):
-        B.linear_fwd(d["qws"][i % copies], d["x"], d["a"], d["b"], wl.alpha, y=d["y"], u=d["u"], ws=d["wsf"],
-                     stream=st)
-
-    def bwd(d, i, st):
-        B.linear_bwd(d["qws"][i % copies], d["x"], d["dy"], d["u"], d["a"], d["b"], wl.alpha, dx=d["dx"],
-                     da=d["da"], db=d["db"], ws=d["ws"], stream=st)
-
-    def eager_step(i, timed):
-        """One stream; each forward launch bracketed by events (the roofline's kernel timing)."""
-        for d in (projs if args.phase != "bwd" else []):
-            if timed:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-            fwd(d, i, stream)
-            if timed:
-                e1.record(stream)
-                ev_pairs.append((d["p"], e0, e1))
-        for d in (reversed(projs) if args.phase != "fwd" else []):
-            bwd(d, i, stream)
-
-    # groups of projections with no data dependence in a decoder layer
-    by_name = {d["p"].name: d for d in projs}
-    order = [g for g in (["q", "k", "v"], ["o"], ["gate", "up"], ["down"])]
-    groups = [[by_name[n] for n in g if n in by_name] for g in order]
-    groups = [g for g in groups if g] or [[d] for d in projs]
-    side = [torch.cuda.Stream() for _ in range(max(len(g) for g in groups))]
-
-    def layer_step(i):
-        """fwd groups in order, then bwd groups in reverse; a group's members on parallel streams."""
-        phases = []
-        if args.phase != "bwd":
-            phases.append((groups, fwd))
-        if args.phase != "fwd":
-            phases.append((list(reversed(groups)), bwd))
-        for gs, fn in phases:
-            for g in gs:
-                if len(g) == 1 or not args.streams:
-                    for d in g:
-                        fn(d, i, stream)
-                    continue
-                fork = torch.cuda.Event()
-                fork.record(stream)
-                for d, st in zip(g, side):
-                    st.wait_event(fork)
-                    fn(d, i, st)
-                for st in side[:len(g)]:
-                    join = torch.cuda.Event()
-                    join.record(st)
-                    stream.wait_event(join)
-
-    # Launch plans (the default for eager launches on one stream): the whole
-    # step recorded once per rotated weight copy and enqueued by one library
-    # call, so host-side call overhead never idles the GPU between launches;
-    # the timing plans bracket each forward call with events.
-    use_plan = not (args.no_plan or args.streams or args.graph)
-    if use_plan:
-        def record(pl, i):
-            # calls grouped as a decoder layer allows: q|k|v and gate|up read one input
-            for g in (groups if args.phase != "bwd" else []):
-                pl.add_fwd_group([(d["qws"][i], d["x"], d["a"], d["b"], wl.alpha, d["y"], d["u"], d["wsf"])
-                                  for d in g])
-            for g in (reversed(groups) if args.phase != "fwd" else []):
-                pl.add_bwd_group([(d["qws"][i], d["x"], d["dy"], d["u"], d["a"], d["b"], wl.alpha, d["dx"],
-                                   d["da"], d["db"], d["ws"], False) for d in reversed(g)])
-        step_plans = []
-        for i in range(copies):
-            pl = B.Plan()
-            record(pl, i)
-            step_plans.append(pl)
-        # the roofline's kernel timing: the forward launches of K steps back to back
-        # (weight copies rotated as the steps rotate them), one event pair around
-        # all of them, so the event markers' own cost (a few microseconds each)
-        # is spread over every launch instead of falling on each step's four
-        fwd_projs = projs if args.phase != "bwd" else []
-        if fwd_projs:
-            roof = B.Plan()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            roof.add_event(e0, stream)
-            for i in range(args.steps):
-                for g in groups:
-                    roof.add_fwd_group([(d["qws"][i % copies], d["x"], d["a"], d["b"], wl.alpha, d["y"], d["u"],
-                                         d["wsf"]) for d in g])
-            roof.add_event(e1, stream)
-            # a group is one launch (pair) unless the FP8 base above 64 tokens runs call by call
-            nl = (len(fwd_projs) if (wl.fmt == 3 and m > 64) else len(groups)) * args.steps
-        torch.cuda.synchronize()
-        for i in range(args.warmup):
-            step_plans[i % copies].run(stream)
-        if fwd_projs:
-            roof.run(stream)                   # untimed pass
-            roof.run(stream)
-            torch.cuda.synchronize()
-            ev_pairs.append(([d["p"] for d in fwd_projs] * args.steps, nl, e0.elapsed_time(e1)))
-    else:
-        # the roofline's kernel timing: eager launches on one stream
-        for i in range(args.warmup):
-            eager_step(i, False)
-        torch.cuda.synchronize()
-        for i in range(args.steps):
-            eager_step(i, True)
-        torch.cuda.synchronize()
-        ev_pairs[:] = [([pp], 1, e0.elapsed_time(e1)) for pp, e0, e1 in ev_pairs]
-
-    # the step itself: HIP-graph replays (one graph per rotated weight copy) or eager launches
-    graphs = []
-    if args.graph:
-        for i in range(copies):
-            layer_step(i)                      # warm the side streams outside capture
-        torch.cuda.synchronize()
-        for i in range(copies):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                layer_step(i)
-            graphs.append(g)
-        torch.cuda.synchronize()
-
-    def run(i):
-        if graphs:
-            graphs[i % copies].replay()
-        elif use_plan:
-            step_plans[i % copies].run(stream)
+    # every workload: the headline layer timed with exactly --steps steps, the
+    # others with enough steps to pass over every rotated weight copy
+    configs = {}
+    head = None
+    for name, m in LAYER_CONFIGS:
+        wl = synth.WORKLOADS[name]
+        key = f"{name}@{m}"
+        if (name, m) == HEADLINE:
+            steps = args.steps
         else:
-            layer_step(i)
-
-    for i in range(args.warmup):
-        run(i)
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(args.steps):
-        run(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    # spread of single steps, from a separate pass with an event between steps
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    evs[0].record(stream)
-    for i in range(args.steps):
-        run(i)
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
-    spread = {"p10": float(np.percentile(per_step, 10)), "median": float(np.median(per_step)),
-              "p90": float(np.percentile(per_step, 90)), "pass": "separate, one event between steps"}
-
-    fwd_ms = sum(t for _, _, t in ev_pairs)
-    fwd_flops = sum(fwd_kernel_flops(wl, p, m) for ps, _, _ in ev_pairs for p in ps)
-    n_launch = max(1, sum(nl for _, nl, _ in ev_pairs))
-    n_calls = max(1, sum(len(ps) for ps, _, _ in ev_pairs))
-    fwd_ms = fwd_ms or float("nan")
-    avg_launch_ms = fwd_ms / n_launch
-    achieved = fwd_flops / (fwd_ms / 1e3) / 1e12
-    traffic = traffic_from_profile(args.workload, m)
-
-    flops = layer_flops(wl, m)
-    nbytes = layer_bytes(wl, m)
-    out = {
-        "metric": METRIC,
-        "value": m / (ms / 1e3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "ms_per_step_spread": spread,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": wl.notes, "name": wl.name, "tokens": m, "base_format": FMT_NAME[wl.fmt],
-                   "rank": wl.r, "alpha": wl.alpha, "projections": [f"{p.name}:{p.k}->{p.n}" for p in wl.projs],
-                   "packed_copies_rotated": copies, "excluded_projections": sorted(excluded),
-                   "step_mode": ("HIP graph replay" if args.graph else
-                                 "eager launches, one library call per step (recorded launch plan; "
-                                 "q|k|v and gate|up as grouped calls)" if use_plan
-                                 else "eager launches, one library call per layer call") + (
-                       ", q|k|v and gate|up on parallel streams" if args.streams else ", one stream")},
-        "layer": {"tflops": flops / (ms / 1e3) / 1e12, "frac_bf16_peak": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
-                  "algorithmic_bytes": nbytes, "hbm_gbs": nbytes / (ms / 1e3) / 1e9,
-                  "frac_hbm_peak": nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS},
-        "roofline": {"kernel": "qgemm_kernel (forward: dequant GEMM + fused LoRA)", "bound": "mfma",
-                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "avg_launch_us": avg_launch_ms * 1e3, "launches_timed": n_launch, "calls_timed": n_calls,
-                     "timing": ("one HIP event pair around the forward launches of K steps, enqueued back "
-                                "to back by one launch plan (q|k|v and gate|up one launch each), total / launches"
-                                if use_plan else
-                                "HIP events around each forward call"),
-                     "flops_per_launch_avg": fwd_flops / n_launch},
-    }
-    if wl.fmt == 3 and m > 64 and ev_pairs:
-        # the FP8 base above 64 tokens: activation split, rank-r projection and the
-        # fp8 GEMM (two E4M3 products per output, hi and lo terms) per call; the
-        # algorithmic FLOPs against the fp8 peak
-        out["dtype"] = "fp8_e4m3"
-        out["roofline"].update({"kernel": "qgemm8_kernel (forward: fp8 GEMM over the two-term E4M3 activation "
-                                          "split, with act_quant_kernel and rproj_kernel per call)",
-                                "peak": PEAK_FP8_TFLOPS, "frac": achieved / PEAK_FP8_TFLOPS,
-                                "executed_fp8_flops_per_algorithmic": 2})
-    if m <= 64:
-        fwd_bytes = sum(BPW[wl.fmt] * p.n * p.k + m * 2 * (p.k + p.n) for ps, _, _ in ev_pairs for p in ps) / n_launch
-        gbs = fwd_bytes / (avg_launch_ms / 1e3) / 1e9
-        out["roofline"].update({"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                "frac": gbs / PEAK_HBM_GBS, "bytes_per_launch_avg": fwd_bytes})
+            probe_bytes = sum(BPW[wl.fmt] * p.n * p.k for p in wl.projs)
+            steps = min(MAX_CFG_STEPS, max(args.steps, copies_for(probe_bytes, args.copies)))
+        print(f"[bench] {key}: {steps} steps", file=sys.stderr, flush=True)
+        rec = bench_layer(args, wl, m, steps)
+        configs[key] = rec
+        if (name, m) == HEADLINE:
+            head = rec
+    if not args.no_stack:
+        wl = synth.WORKLOADS[STACK_WORKLOAD]
+        print(f"[bench] {STACK_WORKLOAD}: {STACK_LAYERS} layers at {STACK_TOKENS} tokens", file=sys.stderr,
+              flush=True)
+        for rec in bench_stack(args, wl, STACK_LAYERS, STACK_TOKENS, min(args.steps, 5)):
+            configs[f"{STACK_WORKLOAD}@{rec['tokens']}"] = rec
+    out = line_from(head, args, args.steps)
+    out["config"]["headline"] = "the largest single-GPU layer config (6.44 TFLOP per step)"
+    out["configs"] = configs
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, min(args.cpu_tokens, m) if args.cpu_tokens else m)
+        print("[bench] cpu oracle sample", file=sys.stderr, flush=True)
+        wl = synth.WORKLOADS[HEADLINE[0]]
+        out["cpu_baseline"] = cpu_baseline(wl, HEADLINE[1], min(args.cpu_tokens, HEADLINE[1]))
     print(json.dumps(out), flush=True)
 
 

@@ -11,7 +11,8 @@ copy and the kernels see the same layout wherever the image lives.
 
 import torch
 
-from . import binding as B
+from . import binding as B, synth
+from .layer import GROUPS
 
 ALIGN = 256
 
@@ -135,3 +136,95 @@ class Stack:
     def close(self):
         if not self.resident:
             self.pool.close()
+
+
+# ----------------------------------------------------------------------------- a stack of model layers
+
+def build_host_images(wl, n_layers, keep_w=(), device="cuda"):
+    """Pinned host images of n_layers layers of workload wl: layer l's
+    projection weights are drawn on the GPU (synth.layer_tensors_torch with
+    layer=l), packed by the library, laid out in one image and copied to
+    page-locked host memory.  Returns (layout, images, kept) with kept[(l, p)]
+    the fp32 weight of projection p of each layer l in keep_w (host)."""
+    layout = LayerLayout(wl.fmt, wl.projs)
+    host, kept = [], {}
+    for layer in range(n_layers):
+        qws = []
+        for pi in range(len(wl.projs)):
+            w = synth.layer_tensors_torch(wl, pi, layer=layer, device=device, want=("W",))["W"]
+            qws.append(B.quant_pack(wl.fmt, w))
+            if layer in keep_w:
+                kept[(layer, pi)] = w.cpu()
+            del w
+        img = layout.image_from(qws, device=device)
+        h = torch.empty(layout.nbytes, dtype=torch.uint8, pin_memory=True)
+        h.copy_(img)
+        host.append(h)
+        del img, qws
+    torch.cuda.synchronize()
+    return layout, host, kept
+
+
+def layer_inputs(wl, m, n_layers, device="cuda"):
+    """acts[l][p] = dict(x, dy, a, b): layer l's seeded inputs at m tokens."""
+    acts = []
+    for layer in range(n_layers):
+        al = []
+        for pi in range(len(wl.projs)):
+            t = synth.layer_tensors_torch(wl, pi, m=m, layer=layer, device=device, want=("A", "B", "x", "dY"))
+            al.append({"x": t["x"], "dy": t["dY"], "a": t["A"], "b": t["B"]})
+        acts.append(al)
+    return acts
+
+
+def layer_outputs(wl, m, n_layers, device="cuda"):
+    """outs[l][p]: preallocated y, u, dx, da, db and the workspaces ws, wsf."""
+    outs = []
+    for _ in range(n_layers):
+        ol = []
+        for p in wl.projs:
+            ol.append({"y": torch.empty((m, p.n), dtype=torch.bfloat16, device=device),
+                       "u": torch.empty((m, wl.r), dtype=torch.float32, device=device),
+                       "dx": torch.empty((m, p.k), dtype=torch.bfloat16, device=device),
+                       "da": torch.empty((wl.r, p.k), dtype=torch.float32, device=device),
+                       "db": torch.empty((p.n, wl.r), dtype=torch.float32, device=device),
+                       "ws": torch.empty(max(256, B.workspace_bytes(B.OP_BWD, wl.fmt, p.n, p.k, m, wl.r)),
+                                         dtype=torch.uint8, device=device),
+                       "wsf": torch.empty(max(256, B.workspace_bytes(B.OP_FWD, wl.fmt, p.n, p.k, m, wl.r)),
+                                          dtype=torch.uint8, device=device)})
+        outs.append(ol)
+    return outs
+
+
+def layer_groups(projs):
+    """Indices of the calls that run grouped in a decoder layer (q|k|v, o,
+    gate|up, down), or None when the projections are not those of one."""
+    names = [p.name for p in projs]
+    groups = [[names.index(n) for n in g if n in names] for g in GROUPS]
+    groups = [g for g in groups if g]
+    if sorted(i for g in groups for i in g) != list(range(len(names))):
+        return None
+    return groups
+
+
+OUTPUT_KEYS = ("y", "u", "dx", "da", "db")
+
+
+def compare_outputs(o1, o2):
+    """Bitwise comparison of every output of every layer of two runs.
+    Returns (equal, first mismatch (layer, projection, key) or None, max abs
+    difference over all outputs as a float)."""
+    equal, first, worst = True, None, 0.0
+    for layer in range(len(o1)):
+        for pi in range(len(o1[layer])):
+            for key in OUTPUT_KEYS:
+                a, b = o1[layer][pi][key], o2[layer][pi][key]
+                ia = a.view(torch.int16 if a.dtype == torch.bfloat16 else torch.int32)
+                ib = b.view(torch.int16 if b.dtype == torch.bfloat16 else torch.int32)
+                if not torch.equal(ia, ib):
+                    if equal:
+                        first = (layer, pi, key)
+                    equal = False
+                    d = (a.float() - b.float()).abs().max().item()
+                    worst = max(worst, d if d == d else float("inf"))
+    return equal, first, worst

@@ -85,6 +85,40 @@ WORKLOADS = {
 }
 
 
+def torch_seed(wid, layer, proj, tid):
+    """Seed of one tensor's draw on the GPU (distinct per workload, layer,
+    projection and tensor id)."""
+    return 1 + int(tid) + 10 * (int(proj) + 100 * (int(layer) + 1000 * int(wid)))
+
+
+def layer_tensors_torch(w: Workload, proj_idx: int, m: int = None, layer: int = 0, device="cuda",
+                        want=("W", "A", "B", "x", "dY")):
+    """The inputs of one projection drawn on the GPU with torch's seeded
+    generator (same distributions as layer_tensors; fast at full model sizes):
+    dict of torch tensors W fp32 [N, K], and bf16 A [r, K], B [N, r], x [m, K],
+    dY [m, N] (fp32 draws rounded to bf16, nearest even).  The oracle gets the
+    same values by copying these tensors to the host."""
+    import torch
+
+    p = w.projs[proj_idx]
+    m = w.m if m is None else m
+
+    def draw(tid, shape, std):
+        g = torch.Generator(device=device)
+        g.manual_seed(torch_seed(w.wid, layer, proj_idx, tid))
+        return torch.randn(shape, generator=g, device=device, dtype=torch.float32) * float(std)
+
+    spec = {"W": (TID_W, (p.n, p.k), 0.02, False), "A": (TID_A, (w.r, p.k), np.sqrt(1.0 / p.k), True),
+            "B": (TID_B, (p.n, w.r), 0.01, True), "x": (TID_X, (m, p.k), 1.0, True),
+            "dY": (TID_DY, (m, p.n), 1.0, True)}
+    out = {}
+    for name in want:
+        tid, shape, std, bf16 = spec[name]
+        t = draw(tid, shape, std)
+        out[name] = t.to(torch.bfloat16) if bf16 else t
+    return out
+
+
 def rng(wid, layer, proj, tid):
     return np.random.default_rng([int(wid), int(layer), int(proj), int(tid)])
 

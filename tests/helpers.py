@@ -68,3 +68,23 @@ def oracle_layer(case, wd, alpha, rows=None):
 
 def rel(got, ref):
     return olora.rel_err(got, ref)
+
+
+def f32_host(t):
+    """A device tensor's values as a host fp32 array (bf16 widens exactly)."""
+    return t.detach().float().cpu().numpy()
+
+
+def oracle_outputs(x, dy, a, b, wd, alpha):
+    """fp64 oracle outputs of one projection from device inputs (x, dY, A, B
+    bf16 tensors) and the dequantized base wd (host fp32): y, U, dX, dA, dB."""
+    xf, dyf, af, bf = (f32_host(t) for t in (x, dy, a, b))
+    y, u = olora.forward(xf, wd, af, bf, alpha)
+    dx, da, db = olora.backward(xf, dyf, wd, af, bf, alpha)
+    return {"y": y, "U": u, "dX": dx, "dA": da, "dB": db}
+
+
+def packed_equal(fmt, codes_bytes, scales_bytes_, c, s):
+    """Library-packed bytes against the oracle's codes and scales."""
+    return (np.array_equal(np.asarray(codes_bytes).ravel(), np.ascontiguousarray(c).ravel())
+            and np.array_equal(np.asarray(scales_bytes_).ravel(), scales_bytes(fmt, s)))

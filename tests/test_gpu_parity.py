@@ -257,6 +257,11 @@ CASES = [
     ("q80_tiles_r8", ofmt.FMT_Q8_0, 520, 1024, 416, 8, 16.0),
     ("small_q80_m64_r32", ofmt.FMT_Q8_0, 64, 1056, 224, 32, 64.0),
     ("small_q80_m20", ofmt.FMT_Q8_0, 20, 2048, 320, 16, 32.0),
+    # 128x128 tiles, 10 row blocks x 16 column tiles = 160 tiles: the per-XCD
+    # tile runs are active (tiles % 8 == 0) and the row blocks fall into
+    # groups of 4 + 4 + 2; forward in the first case, dX in the second
+    ("nf4_xcd_runs_fwd", ofmt.FMT_NF4, 1280, 256, 2048, 16, 32.0),
+    ("nf4_xcd_runs_dx", ofmt.FMT_NF4, 1280, 2048, 256, 16, 32.0),
 ]
 
 
@@ -408,42 +413,6 @@ def test_deterministic_and_base_untouched(lib, case):
         assert torch.equal(da.view(torch.int32), g1["dA"].view(torch.int32)), name
         assert torch.equal(db.view(torch.int32), g1["dB"].view(torch.int32)), name
     assert torch.equal(before[0], qw.codes) and torch.equal(before[1], qw.scales)
-
-
-# ----------------------------------------------------------------------------- full-size, sampled
-
-FULL = []
-for wname in ("qwen3_0.6b_nf4", "llama3.1_8b_nf4", "qwen3_8b_fp8", "llama3.1_8b_mxfp4", "llama3.1_8b_q8_0"):
-    wl = synth.WORKLOADS[wname]
-    for pi, p in enumerate(wl.projs):
-        FULL.append((wname, pi, wl.m))
-    for m in wl.extra_m:
-        FULL.append((wname, 6, m))
-        FULL.append((wname, 0, m))
-
-
-@pytest.mark.parametrize("wname,pi,m", FULL, ids=[f"{w}-{synth.WORKLOADS[w].projs[p].name}-m{m}" for w, p, m in FULL])
-def test_full_size_sampled(lib, wname, pi, m):
-    """Full-size projections, each as a single call (the benchmark's grouped
-    launches equal these bit for bit: test_gpu_plan.py); y and dX checked on 8
-    sampled rows (each row depends on its own inputs only), U on the same
-    rows, dA and dB in full."""
-    wl = synth.WORKLOADS[wname]
-    p = wl.projs[pi]
-    say(f"full-size {wname} {p.name} K={p.k} N={p.n} M={m}")
-    c = synth.layer_tensors(wl, pi, m=m)
-    _, got = run_layer(wl.fmt, c, wl.alpha, m)
-    rows = np.sort(np.random.default_rng(pi).choice(m, min(8, m), replace=False))
-    _, _, wd = H.oracle_packed(wl.fmt, c["W"])
-    ref = H.oracle_layer(c, wd, wl.alpha, rows=rows)
-    tol_base = H.FP8_TOL if wl.fmt == ofmt.FMT_FP8 else H.FWD_TOL
-    for key, tol in (("y", tol_base), ("U", H.FWD_TOL), ("dX", tol_base), ("dA", H.FWD_TOL), ("dB", H.FWD_TOL)):
-        g = to_np(got[key])
-        if key in ("y", "U", "dX"):
-            g = g[rows]
-        e = H.rel(g, ref[key])
-        say(f"  {key}: rel err {e:.3e}")
-        assert e <= tol, (key, e)
 
 
 # at most 16 tokens the forward runs on 16x16x32 MFMAs over steps of 128:

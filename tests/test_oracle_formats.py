@@ -478,3 +478,35 @@ def test_q80_scale_overflow_and_nonfinite():
     w[0, 3] = np.inf
     with pytest.raises(ValueError):
         formats.pack_q8_0(w)
+
+
+# ----------------------------------------------------------------------------- FP8 pack golden
+
+def _read_fp8_golden():
+    scale, vals, codes = None, [], []
+    for line in open(os.path.join(GOLDEN, "fp8_block.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        if line.startswith("scale_fp32_bits"):
+            scale = int(line.split()[1], 16)
+            continue
+        _, v, c = line.split()
+        vals.append(np.float32(v))
+        codes.append(int(c, 16))
+    return np.array(vals, np.float32).reshape(1, 32), np.array(codes, np.uint8).reshape(1, 32), scale
+
+
+def test_fp8_golden_block():
+    """The hand-packed FP8 tensor: the scale rule (absmax / 448), every code
+    including ties to even in the normal and subnormal ranges, a negative
+    value rounding to zero, and a ratio that is not exact in fp32."""
+    w, want, scale = _read_fp8_golden()
+    codes, s = formats.pack_fp8(w)
+    assert np.float32(s).view(np.uint32) == scale
+    assert np.array_equal(codes, want)
+    # decoded values: the code's E4M3 value times 2^-7, e.g. 0x79 -> 288 / 128
+    d = formats.dequant_fp8(codes, s)
+    assert d[0, 8] == np.float32(2.25) and d[0, 9] == np.float32(2.5) and d[0, 10] == np.float32(13 / 128)
+    assert d[0, 0] == np.float32(3.5) and d[0, 11] == np.float32(-0.125)
+    assert np.signbit(d[0, 7]) and d[0, 7] == 0
