@@ -203,6 +203,28 @@ int qlora_linear_bwd(const ql_qweight* w, const uint16_t* x, const uint16_t* dy,
                      uint16_t* dx, float* d_a, float* d_b, int32_t accumulate,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- backward without a workspace
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * as qlora_linear_bwd (same kernels and launch configuration, so bitwise the
+ * same results) except that the scratch is a fixed array inside the library,
+ * QL_NOALLOC_SCRATCH_BYTES per GPU, held from module load until the process
+ * ends, instead of ws / ws_bytes.  The call allocates nothing.
+ * QL_EUNSUPPORTED (nothing enqueued) if the shape needs more scratch than
+ * that, i.e. qlora_workspace_bytes(QL_OP_BWD, ...) > QL_NOALLOC_SCRATCH_BYTES:
+ * every 4-bit base up to 8192 tokens at Llama-3.1-8B widths fits, the FP8
+ * base above about 2000 tokens at Qwen3-8B widths does not.  Every call on one
+ * GPU uses that GPU's one array: calls that overlap in time on one GPU (other
+ * streams, other host threads) race on it and must be ordered by the caller.
+ * Other arguments and errors as qlora_linear_bwd. */
+#define QL_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)
+
+int qlora_linear_bwd_noalloc(const ql_qweight* w, const uint16_t* x,
+                             const uint16_t* dy, const float* u_save, int64_t m,
+                             const uint16_t* lora_a, const uint16_t* lora_b,
+                             int32_t r, float alpha, uint16_t* dx, float* d_a,
+                             float* d_b, int32_t accumulate, void* stream);
+
 /* ---------------------------------------------------------------- groups of independent calls
  * Several independent forward (or backward) calls that share the base
  * format, the token count m and the rank r, in one call: equivalent to

@@ -28,8 +28,9 @@ EXPORTS = (
     "ql_pool_stats", "ql_pool_debug", "ql_pool_destroy", "ql_adamw_step",
     "ql_plan_create", "ql_plan_add_fwd", "ql_plan_add_bwd", "ql_plan_add_event", "ql_plan_size",
     "ql_plan_run", "ql_plan_destroy", "qlora_linear_fwd_group", "qlora_linear_bwd_group",
-    "ql_plan_add_fwd_group", "ql_plan_add_bwd_group", "ql_stack_adapters",
+    "ql_plan_add_fwd_group", "ql_plan_add_bwd_group", "ql_stack_adapters", "qlora_linear_bwd_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 STACK_MAX = 8
 GROUP_MAX = 8
 ADAMW_MAX_TENSORS = 32
@@ -101,6 +102,7 @@ def load(path=LIB_PATH):
         "ql_act_quant_e4m3": (ctypes.c_int, [P, I64, I64, P, P, P, P]),
         "qlora_linear_fwd": (ctypes.c_int, [QW, P, I64, P, P, I32, F, P, P, P, SZ, P]),
         "qlora_linear_bwd": (ctypes.c_int, [QW, P, P, P, I64, P, P, I32, F, P, P, P, I32, P, SZ, P]),
+        "qlora_linear_bwd_noalloc": (ctypes.c_int, [QW, P, P, P, I64, P, P, I32, F, P, P, P, I32, P]),
         "ql_pool_create": (ctypes.c_int, [ctypes.POINTER(P), I32, ctypes.POINTER(P), SZ, I32,
                                           ctypes.POINTER(P), ctypes.POINTER(SZ)]),
         "layer_stream_prefetch": (ctypes.c_int, [P, I32, P]),
@@ -308,6 +310,25 @@ def linear_bwd(qw, x, dy, u, a, b, alpha, need_dx=True, accumulate=False, dx=Non
                                    float(alpha), _ptr(dx) if need_dx else None, _ptr(da), _ptr(db),
                                    1 if accumulate else 0, _ptr(ws), ws.numel(), _stream(stream)))
     return (dx if need_dx else None), da, db
+
+
+def linear_bwd_noalloc(qw, x, dy, u, a, b, alpha, dx, da, db, accumulate=False, stream=None):
+    """The backward without a workspace: the library's own fixed scratch
+    array is used (shared by every such call on the GPU), and this wrapper
+    allocates nothing either, so every output is the caller's."""
+    m = x.shape[0]
+    r = a.shape[0]
+    _need(x, "x", torch.bfloat16, (m, qw.k))
+    _need(dy, "dY", torch.bfloat16, (m, qw.n))
+    _need(u, "U", torch.float32, (m, r))
+    _need(da, "dA", torch.float32, (r, qw.k))
+    _need(db, "dB", torch.float32, (qw.n, r))
+    if dx is not None:
+        _need(dx, "dX", torch.bfloat16, (m, qw.k))
+    _check(load().qlora_linear_bwd_noalloc(qw.cstruct, _ptr(x), _ptr(dy), _ptr(u), m, _ptr(a), _ptr(b), r,
+                                           float(alpha), _ptr(dx), _ptr(da), _ptr(db), 1 if accumulate else 0,
+                                           _stream(stream)))
+    return dx, da, db
 
 
 def _fwd_calls(items):

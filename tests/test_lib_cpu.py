@@ -122,6 +122,20 @@ def test_size_limits_refused(lib):
     assert lib.quant_pack(binding.FMT_NF4, P, 64, big, P, P, P, 8, None) == binding.QL_EWORKSPACE
 
 
+def test_noalloc_backward_refuses_oversized_scratch(lib):
+    """The allocation-free backward refuses, before touching a GPU, a shape
+    whose scratch exceeds its fixed array (the FP8 base at 8192 tokens needs
+    its activation split planes: 236 MB)."""
+    P = FAKE
+    need = binding.workspace_bytes(binding.OP_BWD, binding.FMT_FP8, 12288, 4096, 8192, 32)
+    assert need > binding.NOALLOC_SCRATCH_BYTES
+    qw = _qw(binding.FMT_FP8, 12288, 4096)
+    rc = lib.qlora_linear_bwd_noalloc(ctypes.byref(qw), P, P, P, 8192, P, P, 32, 64.0, P, P, P, 0, None)
+    assert rc == binding.QL_EUNSUPPORTED
+    assert "scratch" in _err(lib)
+    assert lib.qlora_linear_bwd_noalloc(None, P, P, P, 16, P, P, 16, 16.0, P, P, P, 0, None) == binding.QL_EINVAL
+
+
 def test_pool_argument_errors(lib):
     h = ctypes.c_void_p()
     slots = (ctypes.c_void_p * 2)(0x10000, 0x10100)
