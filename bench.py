@@ -71,6 +71,9 @@ def parse():
                     help="time the fused AdamW step on the layer's adapters instead of the layer step")
     ap.add_argument("--layers", type=int, default=0,
                     help="stack mode: this many layers, resident vs streamed from pinned host")
+    ap.add_argument("--hbm-ceiling", action="store_true",
+                    help="only measure plain streaming kernels (device copy, read-only reduction) over 4 GiB "
+                         "and exit: the HBM ceiling the kernels are compared with")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device (a plain copy kernel of known size, "
                          "to calibrate HBM byte counters) and exit")
@@ -456,6 +459,35 @@ def optimizer_bench(args, wl):
     print(json.dumps(out), flush=True)
 
 
+# ----------------------------------------------------------------------------- HBM ceiling
+
+def hbm_ceiling(args):
+    """Plain streaming kernels on 4 GiB (16x the MALL): a device-to-device
+    copy (read + write) and a read-only reduction (torch's sum), each timed
+    with HIP events over several repetitions; bytes moved / time."""
+    import torch
+    n = 4 << 30
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, fn, nbytes in (("copy", lambda: b.copy_(a), 2 * n), ("read_sum", lambda: a.sum(), n)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"gbs": nbytes / (ms / 1e3) / 1e9, "ms": ms, "bytes": nbytes,
+                     "frac_of_8000": nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS}
+    print(json.dumps({"hbm_ceiling": out, "buffer_bytes": n}), flush=True)
+
+
 # ----------------------------------------------------------------------------- main
 
 def line_from(rec, args, steps):
@@ -488,6 +520,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
         return
+
+    if args.hbm_ceiling:
+        return hbm_ceiling(args)
 
     from quantized_base_lora_amd import binding as B, synth
 
