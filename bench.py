@@ -69,6 +69,7 @@ def parse():
     ap.add_argument("--no-stack", action="store_true", help="leave the streamed stack out of the full run")
     ap.add_argument("--optimizer", action="store_true",
                     help="time the fused AdamW step on the layer's adapters instead of the layer step")
+    ap.add_argument("--state8", action="store_true", help="with --optimizer: the 8-bit block-wise state")
     ap.add_argument("--layers", type=int, default=0,
                     help="stack mode: this many layers, resident vs streamed from pinned host")
     ap.add_argument("--hbm-ceiling", action="store_true",
@@ -416,18 +417,24 @@ def optimizer_bench(args, wl):
     for p in wl.projs:
         sizes += [wl.r * p.k, p.n * wl.r]
     n_el = sum(sizes)
-    per_el = 30
-    copies = max(1, int(np.ceil(ROTATE_BYTES / (n_el * 18))))
+    # 8-bit state: param, grad read (8), codes read (2), param and codes written (6), bf16 copy (2);
+    # fp32 state: param, grad, m, v read (16), param, m, v written (12), bf16 copy (2)
+    per_el = 18 if args.state8 else 30
+    copies = max(1, int(np.ceil(ROTATE_BYTES / (n_el * (10 if args.state8 else 18)))))
     gen = torch.Generator(device=dev).manual_seed(1)
     sets = []
     for _ in range(copies):
         ts = []
         for n in sizes:
-            ts.append((torch.randn(n, device=dev, generator=gen) * 0.02, torch.randn(n, device=dev, generator=gen) * 1e-3,
-                       torch.zeros(n, device=dev), torch.zeros(n, device=dev),
-                       torch.empty(n, dtype=torch.bfloat16, device=dev)))
+            p0 = torch.randn(n, device=dev, generator=gen) * 0.02
+            g0 = torch.randn(n, device=dev, generator=gen) * 1e-3
+            pb = torch.empty(n, dtype=torch.bfloat16, device=dev)
+            if args.state8:
+                ts.append((p0, g0, B.Adamw8State(n, device=dev), pb))
+            else:
+                ts.append((p0, g0, torch.zeros(n, device=dev), torch.zeros(n, device=dev), pb))
         sets.append(ts)
-    plans = [B.AdamwPlan(ts) for ts in sets]
+    plans = [(B.Adamw8Plan(ts) if args.state8 else B.AdamwPlan(ts)) for ts in sets]
     stream = torch.cuda.Stream()
     torch.cuda.set_stream(stream)
     for i in range(args.warmup):
@@ -448,13 +455,15 @@ def optimizer_bench(args, wl):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / args.steps
     gbs = n_el * per_el / (us / 1e6) / 1e9
-    out = {"metric": "fused AdamW adapter step, algorithmic HBM GB/s", "value": gbs, "unit": "GB/s",
+    out = {"metric": "fused AdamW adapter step" + (" (8-bit block-wise state)" if args.state8 else "") +
+                     ", algorithmic HBM GB/s", "value": gbs, "unit": "GB/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "us_per_step": us,
            "higher_is_better": True, "dtype": "f32", "data": "synthetic",
            "config": {"workload": f"adapters of one {wl.notes}", "tensors": len(sizes), "elements": n_el,
                       "bytes_per_element": per_el, "state_copies_rotated": copies,
                       "step_mode": "HIP graph of the launches, replayed"},
-           "roofline": {"kernel": "adamw_kernel", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+           "roofline": {"kernel": "adamw8_kernel" if args.state8 else "adamw_kernel", "bound": "hbm",
+                        "achieved": gbs, "peak": PEAK_HBM_GBS,
                         "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None}}
     print(json.dumps(out), flush=True)
 

@@ -409,6 +409,50 @@ typedef struct ql_adamw_hparams {
 int ql_adamw_step(const ql_adamw_tensor* tensors, int32_t n_tensors,
                   const ql_adamw_hparams* hp, void* stream);
 
+/* ---------------------------------------------------------------- adapter optimizer step, 8-bit state
+ * The same AdamW step with 8-bit moments, the state format of the pages' 8-bit
+ * AdamW (Surogate README page, "Optimizers & monitoring" row; GGUF-recipe page,
+ * "How it works") taken from Dettmers et al., "8-bit Optimizers via Block-wise
+ * Quantization": each moment is stored as one code per element plus one fp32
+ * scale (the block's largest magnitude) per QL_ADAMW8_BLOCK consecutive
+ * elements; a code stands for level * scale, level from the dynamic tree type:
+ * magnitude bits = z zero bits, a one bit, f bits holding q, level
+ * 10^-z * (0.1 + 0.9 (q + 1) / 2^f), all-zero bits 0 (ql_dyn8_levels).  The
+ * first moment uses the signed type (bit 7 the sign, 7 magnitude bits), the
+ * second the unsigned one (8 magnitude bits).  Per element: dequantize, the
+ * update of ql_adamw_step in fp32 (the parameter moves with the fp32 moments),
+ * then per block: scale = largest |new moment|, code = number of decision
+ * thresholds fl32(fl32(l_i + l_i+1) * 0.5) below |m / scale| (IEEE divide; a
+ * value on a threshold takes the lower code), sign bit for a negative first
+ * moment with a non-zero code; a block whose scale is 0 stores codes 0.
+ * Every fp32 operation rounds once, in a fixed order, so results are
+ * reproducible bit for bit.  A zero state (codes 0, scales 0) is the start.
+ *
+ * tensors: host array of n_tensors (0 .. QL_ADAMW_MAX_TENSORS) descriptors;
+ * n a multiple of 8 (0 skips the tensor); param, grad, param_bf16 dev and
+ * 16-byte aligned, codes dev and 8-byte aligned, scales dev fp32
+ * [ceil(n / QL_ADAMW8_BLOCK)].  hp and errors as ql_adamw_step. */
+#define QL_ADAMW8_BLOCK 2048
+
+typedef struct ql_adamw8_tensor {
+  float* param;              /* dev fp32 [n], master adapter weights        */
+  const float* grad;         /* dev fp32 [n]                                */
+  uint8_t* exp_avg;          /* dev u8 [n], first-moment codes (signed)     */
+  float* exp_avg_absmax;     /* dev fp32 [ceil(n / QL_ADAMW8_BLOCK)]        */
+  uint8_t* exp_avg_sq;       /* dev u8 [n], second-moment codes (unsigned)  */
+  float* exp_avg_sq_absmax;  /* dev fp32 [ceil(n / QL_ADAMW8_BLOCK)]        */
+  uint16_t* param_bf16;      /* dev bf16 [n] or NULL: copy for the layer    */
+  int64_t n;                 /* elements                                    */
+} ql_adamw8_tensor;
+
+int ql_adamw8_step(const ql_adamw8_tensor* tensors, int32_t n_tensors,
+                   const ql_adamw_hparams* hp, void* stream);
+
+/* The levels of the 8-bit state type, indexed by the magnitude bits
+ * (ascending): is_signed != 0 gives the 128 magnitudes of the signed type,
+ * 0 the 256 levels of the unsigned one.  out: host floats.  Needs no GPU. */
+int ql_dyn8_levels(int32_t is_signed, float* out);
+
 /* ---------------------------------------------------------------- a10: layer stream
  * (Soup page, opening paragraph.)  The frozen base is kept in page-locked
  * host memory; a few device slots, allocated once by the caller, each hold

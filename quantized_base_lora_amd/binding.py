@@ -29,7 +29,9 @@ EXPORTS = (
     "ql_plan_create", "ql_plan_add_fwd", "ql_plan_add_bwd", "ql_plan_add_event", "ql_plan_size",
     "ql_plan_run", "ql_plan_destroy", "qlora_linear_fwd_group", "qlora_linear_bwd_group",
     "ql_plan_add_fwd_group", "ql_plan_add_bwd_group", "ql_stack_adapters", "qlora_linear_bwd_noalloc",
+    "ql_adamw8_step", "ql_dyn8_levels",
 )
+ADAMW8_BLOCK = 2048
 NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 STACK_MAX = 8
 GROUP_MAX = 8
@@ -71,6 +73,12 @@ class AdapterC(ctypes.Structure):
 class AdamwTensorC(ctypes.Structure):
     _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("exp_avg", ctypes.c_void_p),
                 ("exp_avg_sq", ctypes.c_void_p), ("param_bf16", ctypes.c_void_p), ("n", ctypes.c_int64)]
+
+
+class Adamw8TensorC(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("exp_avg", ctypes.c_void_p),
+                ("exp_avg_absmax", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p),
+                ("exp_avg_sq_absmax", ctypes.c_void_p), ("param_bf16", ctypes.c_void_p), ("n", ctypes.c_int64)]
 
 
 class AdamwHparamsC(ctypes.Structure):
@@ -124,6 +132,9 @@ def load(path=LIB_PATH):
         "qlora_linear_bwd_group": (ctypes.c_int, [ctypes.POINTER(BwdCallC), I32, I64, I32, P]),
         "ql_plan_add_fwd_group": (ctypes.c_int, [P, ctypes.POINTER(FwdCallC), I32, I64, I32]),
         "ql_plan_add_bwd_group": (ctypes.c_int, [P, ctypes.POINTER(BwdCallC), I32, I64, I32]),
+        "ql_adamw8_step": (ctypes.c_int, [ctypes.POINTER(Adamw8TensorC), I32,
+                                          ctypes.POINTER(AdamwHparamsC), P]),
+        "ql_dyn8_levels": (ctypes.c_int, [I32, P]),
         "ql_stack_adapters": (ctypes.c_int, [ctypes.POINTER(AdapterC), I32, I64, I64, P, P,
                                              ctypes.POINTER(ctypes.c_float), P]),
     }
@@ -536,6 +547,56 @@ def _adamw_array(tensors):
         arr[i] = AdamwTensorC(p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(),
                               pb.data_ptr() if pb is not None else None, p.numel())
     return arr
+
+
+class Adamw8State:
+    """8-bit block-wise AdamW state of one tensor of n elements: first- and
+    second-moment codes (u8 [n]) and their per-block scales (fp32
+    [ceil(n / 2048)]); zero codes and scales are the zero state."""
+
+    def __init__(self, n, device="cuda"):
+        nb = -(-int(n) // ADAMW8_BLOCK)
+        self.n = int(n)
+        self.m = torch.zeros(n, dtype=torch.uint8, device=device)
+        self.m_absmax = torch.zeros(nb, dtype=torch.float32, device=device)
+        self.v = torch.zeros(n, dtype=torch.uint8, device=device)
+        self.v_absmax = torch.zeros(nb, dtype=torch.float32, device=device)
+
+
+class Adamw8Plan:
+    """The descriptor array of a fixed set of (param, grad, Adamw8State,
+    param_bf16 or None) tensors, checked once, so that each step is a single
+    library call (the tensors must stay alive)."""
+
+    def __init__(self, tensors):
+        self.tensors = list(tensors)
+        arr = (Adamw8TensorC * max(1, len(self.tensors)))()
+        for i, (p, g, st, pb) in enumerate(self.tensors):
+            for name, t in (("param", p), ("grad", g)):
+                _need(t, name, torch.float32)
+                if t.numel() != p.numel():
+                    raise ValueError(f"{name}: size {t.numel()} differs from param's {p.numel()}")
+            if st.n != p.numel():
+                raise ValueError("state size differs from param's")
+            if pb is not None:
+                _need(pb, "param_bf16", torch.bfloat16)
+            arr[i] = Adamw8TensorC(p.data_ptr(), g.data_ptr(), st.m.data_ptr(), st.m_absmax.data_ptr(),
+                                   st.v.data_ptr(), st.v_absmax.data_ptr(),
+                                   pb.data_ptr() if pb is not None else None, p.numel())
+        self.arr = arr
+
+    def step(self, step, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, grad_scale=1.0,
+             stream=None):
+        hp = AdamwHparamsC(lr, beta1, beta2, eps, weight_decay, grad_scale, int(step), 0)
+        _check(load().ql_adamw8_step(self.arr, len(self.tensors), ctypes.byref(hp), _stream(stream)))
+
+
+def dyn8_levels(signed):
+    """The library's levels of the 8-bit state type (host call, needs no GPU)."""
+    n = 128 if signed else 256
+    buf = (ctypes.c_float * n)()
+    _check(load().ql_dyn8_levels(1 if signed else 0, buf))
+    return [float(v) for v in buf]
 
 
 # ----------------------------------------------------------------------------- stacked adapters

@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "common.h"
+#include "dyn8.h"
 
 namespace ql {
 
@@ -521,6 +522,51 @@ int ql_adamw_step(const ql_adamw_tensor* tensors, int32_t n_tensors, const ql_ad
   if (rc) return rc;
   hipError_t e = launch_adamw(tensors, n_tensors, *hp, as_stream(stream));
   if (e != hipSuccess) return hip_error(e, "adamw launch");
+  return QL_OK;
+}
+
+// hyperparameters shared by both AdamW variants
+static int check_adamw_hparams(const ql_adamw_hparams* hp) {
+  if (hp->step < 1) return set_error(QL_EINVAL, "step must be >= 1");
+  if (hp->reserved != 0) return set_error(QL_EINVAL, "hparams.reserved must be 0");
+  const double f[6] = {hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->grad_scale};
+  for (double v : f)
+    if (!(v - v == 0.0)) return set_error(QL_EINVAL, "non-finite hyperparameter");
+  if (hp->lr < 0.0 || hp->eps < 0.0 || hp->weight_decay < 0.0)
+    return set_error(QL_EINVAL, "lr, eps and weight_decay must be >= 0");
+  if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0 && hp->beta2 >= 0.0 && hp->beta2 < 1.0))
+    return set_error(QL_EINVAL, "beta1 and beta2 must lie in [0, 1)");
+  return QL_OK;
+}
+
+int ql_adamw8_step(const ql_adamw8_tensor* tensors, int32_t n_tensors, const ql_adamw_hparams* hp,
+                   void* stream) {
+  if (n_tensors < 0 || n_tensors > QL_ADAMW_MAX_TENSORS)
+    return set_error(QL_EINVAL, "n_tensors=%d outside [0, %d]", n_tensors, QL_ADAMW_MAX_TENSORS);
+  if (!hp || (n_tensors > 0 && !tensors)) return set_error(QL_EINVAL, "null pointer");
+  int rc = check_adamw_hparams(hp);
+  if (rc) return rc;
+  for (int32_t i = 0; i < n_tensors; ++i) {
+    const ql_adamw8_tensor& t = tensors[i];
+    if (t.n < 0 || t.n % 8) return set_error(QL_EINVAL, "tensor %d: n=%lld is not a multiple of 8", i, (long long)t.n);
+    if (t.n == 0) continue;
+    if (!t.param || !t.grad || !t.exp_avg || !t.exp_avg_absmax || !t.exp_avg_sq || !t.exp_avg_sq_absmax)
+      return set_error(QL_EINVAL, "tensor %d: null pointer", i);
+    if (!aligned16(t.param) || !aligned16(t.grad) || (t.param_bf16 && !aligned16(t.param_bf16)) ||
+        ((uintptr_t)t.exp_avg & 7u) || ((uintptr_t)t.exp_avg_sq & 7u) || ((uintptr_t)t.exp_avg_absmax & 3u) ||
+        ((uintptr_t)t.exp_avg_sq_absmax & 3u))
+      return set_error(QL_EINVAL, "tensor %d: misaligned pointer", i);
+  }
+  if ((rc = check_sticky())) return rc;
+  hipError_t e = launch_adamw8(tensors, n_tensors, *hp, as_stream(stream));
+  if (e != hipSuccess) return hip_error(e, "adamw8 launch");
+  return QL_OK;
+}
+
+int ql_dyn8_levels(int32_t is_signed, float* out) {
+  if (!out) return set_error(QL_EINVAL, "null output");
+  const Dyn8Table& t = dyn8_table(is_signed != 0);
+  memcpy(out, t.level, (size_t)t.count * sizeof(float));
   return QL_OK;
 }
 

@@ -128,6 +128,10 @@ hipError_t launch_stack(const ql_adapter* ad, int32_t n, int64_t n_out, int64_t 
 
 // adapter optimizer step (kernels_optim.hip); arguments already validated
 hipError_t launch_adamw(const ql_adamw_tensor* ts, int32_t nt, const ql_adamw_hparams& hp, hipStream_t s);
+hipError_t launch_adamw8(const ql_adamw8_tensor* ts, int32_t nt, const ql_adamw_hparams& hp, hipStream_t s);
+// the levels of the 8-bit state type (dyn8.h), built at compile time
+struct Dyn8Table;
+const Dyn8Table& dyn8_table(bool is_signed);
 
 // LoRA-side kernels (kernels_lora.hip)
 // out[m][j] = sum_c x[m][c] * b[c][j]     (fp32), b is [C, r]

@@ -50,6 +50,33 @@ def test_nf4_levels_equal_oracle_bitwise():
     assert np.array_equal(ours.view(np.uint32), ofmt.nf4_codebook().view(np.uint32))
 
 
+@pytest.mark.parametrize("signed", [True, False])
+def test_dyn8_levels_equal_oracle_bitwise(signed):
+    """The library's 8-bit optimizer-state levels, built by its own routine at
+    compile time, equal the oracle's bit for bit."""
+    from oracle import adamw8
+    ours = np.array(binding.dyn8_levels(signed), dtype=np.float32)
+    assert np.array_equal(ours.view(np.uint32), adamw8.dynamic_levels(signed).view(np.uint32))
+
+
+def test_adamw8_argument_errors(lib):
+    P = FAKE.value
+    hp = binding.AdamwHparamsC(1e-3, 0.9, 0.999, 1e-8, 0.0, 1.0, 1, 0)
+    t = (binding.Adamw8TensorC * 1)(binding.Adamw8TensorC(P, P, P, P, P, P, None, 12))
+    assert lib.ql_adamw8_step(t, 1, ctypes.byref(hp), None) == binding.QL_EINVAL     # n % 8
+    assert "multiple of 8" in _err(lib)
+    t = (binding.Adamw8TensorC * 1)(binding.Adamw8TensorC(P, P, P + 4, P, P, P, None, 16))
+    assert lib.ql_adamw8_step(t, 1, ctypes.byref(hp), None) == binding.QL_EINVAL     # codes not 8-byte aligned
+    t = (binding.Adamw8TensorC * 1)(binding.Adamw8TensorC(P, None, P, P, P, P, None, 16))
+    assert lib.ql_adamw8_step(t, 1, ctypes.byref(hp), None) == binding.QL_EINVAL
+    bad = binding.AdamwHparamsC(1e-3, 1.0, 0.999, 1e-8, 0.0, 1.0, 1, 0)
+    t = (binding.Adamw8TensorC * 1)(binding.Adamw8TensorC(P, P, P, P, P, P, None, 16))
+    assert lib.ql_adamw8_step(t, 1, ctypes.byref(bad), None) == binding.QL_EINVAL
+    bad = binding.AdamwHparamsC(1e-3, 0.9, 0.999, 1e-8, 0.0, 1.0, 0, 0)
+    assert lib.ql_adamw8_step(t, 1, ctypes.byref(bad), None) == binding.QL_EINVAL
+    assert lib.ql_adamw8_step(t, 33, ctypes.byref(hp), None) == binding.QL_EINVAL
+
+
 def test_workspace_query(lib):
     assert binding.workspace_bytes(binding.OP_PACK, binding.FMT_NF4, 64, 64) >= 8
     a = binding.workspace_bytes(binding.OP_BWD, binding.FMT_NF4, 1024, 2048, 1000, 16)
