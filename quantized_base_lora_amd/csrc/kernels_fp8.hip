@@ -28,7 +28,7 @@ constexpr int TM = 256, TK = 64, NT = 512;
 constexpr int SB = 80;                 // act planes and forward W tile: row stride in bytes
 
 template <int TN, bool TRANS> struct Shape8 {
-  static constexpr int WAVES_N = TN == 256 ? 4 : 2;
+  static constexpr int WAVES_N = 2;                  // wave blocks 64 x TN/2: the two activation planes are the larger operand
   static constexpr int WAVES_M = 8 / WAVES_N;
   static constexpr int WM = TM / WAVES_M, WN = TN / WAVES_N;
   static constexpr int MB = WM / 32, NB = WN / 32;
