@@ -149,52 +149,3 @@ def act_join_e4m3(hi, lo, s, dtype=np.float64):
     h = codecs.e4m3_decode(hi).astype(dtype)
     l_ = codecs.e4m3_decode(lo).astype(dtype)
     return np.asarray(s, dtype)[:, None] * (h + l_ / LO_SHIFT)
-
-
-ACT_BLOCK = 32        # elements per block scale along the contraction
-ACT_E_MIN = -123      # the low term's scale 2^(e - 4) must stay an E8M0 value (>= 2^-127)
-
-
-def act_split_e4m3_blocks(x):
-    """Two-term E4M3 split with one power-of-two scale per row and per block
-    of 32 consecutive elements along the contraction (the form of the scaled
-    fp8 matrix cores' E8M0 block-scale operand).
-
-    For row m and block b (columns 32b .. 32b + 31) with a = max|x| > 0 over
-    the block: e = max(smallest integer with 448 * 2^e >= a, -123) (-123 keeps
-    the low term's scale 2^(e - 4) representable); t = x * 2^-e (exact, or a
-    value below every E4M3 code); hi = E4M3(t), lo = E4M3(fl32(t - hi) * 16),
-    so x ~= 2^e (hi + lo / 16).  A zero block has e = 0 and zero codes.
-    Returns (hi u8 [M, K], lo u8 [M, K], e int32 [M, K / 32]).  The same
-    reading as act_split_e4m3 with the scale taken per block instead of per
-    row; it is an approximation, checked by its error bound."""
-    xf = np.asarray(x, dtype=np.float32)
-    m, k = xf.shape
-    if k % ACT_BLOCK:
-        raise ValueError("K must be a multiple of 32")
-    nb = k // ACT_BLOCK
-    blk = xf.reshape(m, nb, ACT_BLOCK)
-    amax = np.max(np.abs(blk), axis=2)
-    e = np.zeros((m, nb), np.int32)
-    t = np.zeros_like(blk)
-    for i in range(m):
-        for b in range(nb):
-            if amax[i, b] > 0:
-                e[i, b] = max(act_row_exponent(amax[i, b]), ACT_E_MIN)
-                t[i, b] = np.ldexp(blk[i, b].astype(np.float64), -int(e[i, b])).astype(np.float32)
-    t = t.reshape(m, k)
-    hi = codecs.e4m3_encode(t)
-    res = (t - codecs.e4m3_decode(hi)).astype(np.float32)
-    lo = codecs.e4m3_encode((res * np.float32(LO_SHIFT)).astype(np.float32))
-    nz = np.repeat(amax > 0, ACT_BLOCK, axis=1)
-    hi = np.where(nz, hi, np.uint8(0)).astype(np.uint8)
-    lo = np.where(nz, lo, np.uint8(0)).astype(np.uint8)
-    return hi, lo, e
-
-
-def act_join_e4m3_blocks(hi, lo, e, dtype=np.float64):
-    """Value represented by a block split: 2^e (hi + lo / 16), e per 32 columns."""
-    h = codecs.e4m3_decode(hi).astype(dtype)
-    l_ = codecs.e4m3_decode(lo).astype(dtype)
-    sc = np.repeat(np.ldexp(1.0, np.asarray(e, np.int64)).astype(dtype), ACT_BLOCK, axis=1)
-    return sc * (h + l_ / LO_SHIFT)

@@ -198,63 +198,3 @@ def test_act_split_exact_on_e4m3_grid():
     hi, lo, s = lora.act_split_e4m3(x)
     assert s[0] == 1.0
     assert np.array_equal(codecs.e4m3_decode(hi)[0], x[0]) and not np.any(lo & 0x7F)
-
-
-# ----------------------------------------------------------------------------- FP8 activations, block scales
-
-def test_act_split_blocks_error_bound_and_zero_blocks():
-    """Per element |x - 2^e (hi + lo/16)| <= 2^-8 |x| + 2^e 2^-13 with e the
-    element's block exponent; a zero block has e = 0 and zero codes."""
-    g = np.random.default_rng(31)
-    x = codecs.bf16_round((g.standard_normal((48, 256)) * np.exp(g.uniform(-8, 8, (48, 8))).repeat(32, 1))
-                          .astype(np.float32))
-    x[3, 32:64] = 0
-    x[5, 7] = 1e-30
-    hi, lo, e = lora.act_split_e4m3_blocks(x)
-    assert e[3, 1] == 0 and not hi[3, 32:64].any() and not lo[3, 32:64].any()
-    xr = lora.act_join_e4m3_blocks(hi, lo, e)
-    sc = np.repeat(np.ldexp(1.0, e.astype(np.int64)), 32, axis=1)
-    assert np.all(np.abs(xr - x) <= 2.0 ** -8 * np.abs(x) + sc * 2.0 ** -13)
-
-
-def test_act_split_blocks_exponent_is_minimal_and_clamped():
-    """e = max(smallest integer with 448 2^e >= block max, -123), found by
-    scanning the integers directly, on blocks spanning the fp32 range."""
-    g = np.random.default_rng(32)
-    x = (g.standard_normal((16, 128)) * np.exp(g.uniform(-85, 85, (16, 4))).repeat(32, 1)).astype(np.float32)
-    x[0, :32] = 448.0
-    x[0, 32:64] = 448.0 * 1.0000001
-    x[1, :32] = 1e-37                                   # below 448 2^-124: the clamp acts
-    _, _, e = lora.act_split_e4m3_blocks(x)
-    for i in range(x.shape[0]):
-        for b in range(4):
-            a = float(np.max(np.abs(x[i, 32 * b:32 * b + 32])))
-            want = max(next(k for k in range(-200, 200) if 448.0 * 2.0 ** k >= a), -123)
-            assert e[i, b] == want, (i, b, e[i, b], want)
-    assert e[0, 0] == 0 and e[0, 1] == 1 and e[1, 0] == -123
-
-
-def test_act_split_blocks_equals_row_split_when_every_block_holds_the_row_max():
-    """When each 32-block contains the row's largest magnitude, every block
-    exponent is the row exponent and the codes are those of the (separately
-    pinned) per-row split."""
-    g = np.random.default_rng(33)
-    x = codecs.bf16_round(g.standard_normal((8, 192)).astype(np.float32))
-    x[:, ::32] = np.float32(7.5)
-    hi, lo, e = lora.act_split_e4m3_blocks(x)
-    rh, rl, rs = lora.act_split_e4m3(x)
-    assert np.array_equal(hi, rh) and np.array_equal(lo, rl)
-    assert np.all(np.ldexp(1.0, e.astype(np.int64)) == rs[:, None])
-
-
-def test_act_split_blocks_exact_on_e4m3_grid():
-    """Blocks of E4M3 codes that include 448 (e = 0) reproduce with lo = 0."""
-    c = np.arange(0, 0x7F, dtype=np.uint8)
-    vals = codecs.e4m3_decode(c)
-    x = np.concatenate([vals, -vals, np.full(2, 448.0, np.float32)]).astype(np.float32)
-    x = np.concatenate([x, np.zeros((-x.size) % 32, np.float32)])
-    x = x.reshape(-1, 32)
-    x[:, 0] = 448.0
-    hi, lo, e = lora.act_split_e4m3_blocks(x.reshape(1, -1))
-    assert not e.any()
-    assert np.array_equal(codecs.e4m3_decode(hi)[0], x.reshape(-1)) and not np.any(lo & 0x7F)
