@@ -43,6 +43,24 @@ Surogate pages' NVFP4 (E2M1) recipes and MXFP4 checkpoints):
   nearest even, saturating to +-6; value E2M1(q) * X, exact in fp32 and bf16.
   A zero block stores e = 0 and codes 0.  e = 255 (NaN in E8M0) is never
   written and decodes to NaN.
+* NVFP4 (the FP4 format of the Surogate pages' Blackwell recipe, "NVFP4
+  (E2M1)" in the review page's highlights; the pages name it without
+  defining it, and the reading taken is NVIDIA's published structure): E2M1
+  element codes in blocks of 16, one E4M3 scale byte per block and one fp32
+  scale per tensor.  Decisions:
+    g   = fl32(amax / 2688)            the tensor scale (2688 = 6 * 448, the
+                                       largest E2M1 magnitude times the
+                                       largest E4M3 one)
+    sb  = E4M3(fl32(fl32(amax_b / 6) / g))   per block, nearest even,
+                                       saturating at 448; 0 when g = 0
+    X_b = fl32(E4M3(sb) * g)           the block's decode scale
+    q   = the E2M1 value nearest to the exact quotient w / X_b, ties to the
+          even mantissa, saturating at +-6, sign bit from w; 0 when X_b = 0
+  and the value is fl32(E2M1(q) * X_b).  Codes use the split-nibble groups of
+  32 of Q4_0 and NF4, so a group's low nibbles are one block of 16 and its
+  high nibbles the next.  The stored scale image is 16 header bytes (g's
+  fp32 bits little-endian, then 12 zero bytes) followed by the E4M3 bytes
+  u8 [N, K/16].  A zero tensor stores g = 0, zero scales and zero codes.
 """
 
 import statistics
@@ -51,8 +69,8 @@ import numpy as np
 
 from . import codecs
 
-FMT_Q4_0, FMT_NF4, FMT_FP8, FMT_MXFP4, FMT_Q8_0 = 1, 2, 3, 4, 5
-BLOCK = {FMT_Q4_0: 32, FMT_NF4: 64, FMT_MXFP4: 32, FMT_Q8_0: 32}
+FMT_Q4_0, FMT_NF4, FMT_FP8, FMT_MXFP4, FMT_Q8_0, FMT_NVFP4 = 1, 2, 3, 4, 5, 6
+BLOCK = {FMT_Q4_0: 32, FMT_NF4: 64, FMT_MXFP4: 32, FMT_Q8_0: 32, FMT_NVFP4: 16}
 
 
 # ----------------------------------------------------------------------------- NF4 book
@@ -288,6 +306,88 @@ def dequant_mxfp4(codes, e8):
     return w.reshape(n, k).astype(np.float32)
 
 
+# ----------------------------------------------------------------------------- NVFP4
+
+NVFP4_HEADER = 16          # bytes before the block scales in the stored image
+
+
+def nvfp4_tensor_scale(amax):
+    """g = fl32(amax / 2688) (IEEE fp32 division)."""
+    return np.float32(np.float32(amax) / np.float32(2688.0))
+
+
+def nvfp4_block_scale_codes(block_amax, g):
+    """E4M3 scale byte of each block: E4M3(fl32(fl32(amax_b / 6) / g)); 0 if g = 0."""
+    a = np.asarray(block_amax, dtype=np.float32)
+    g = np.float32(g)
+    if g == 0:
+        return np.zeros(a.shape, np.uint8)
+    t = ((a / np.float32(6.0)).astype(np.float32) / g).astype(np.float32)
+    return codecs.e4m3_encode(t)
+
+
+def nvfp4_decode_scales(sb, g):
+    """X_b = fl32(E4M3(sb) * g) for every scale byte."""
+    return (codecs.e4m3_decode(sb) * np.float32(g)).astype(np.float32)
+
+
+def pack_nvfp4_parts(w):
+    """fp32 W [N, K] -> (codes u8 [N, K/2] split-nibble, g fp32, E4M3 scale bytes u8 [N, K/16])."""
+    w = _check_w(w)
+    n, k = w.shape
+    if k % 32:
+        raise ValueError("K must be a multiple of 32")
+    g = nvfp4_tensor_scale(np.max(np.abs(w)) if w.size else 0.0)
+    blk = w.reshape(n, k // 16, 16)
+    sb = nvfp4_block_scale_codes(np.max(np.abs(blk), axis=2), g)
+    x = nvfp4_decode_scales(sb, g).astype(np.float64)
+    # the fp64 quotient of two fp32 numbers decides the E2M1 rounding as the
+    # exact quotient would: a midpoint of the E2M1 grid has at most 3
+    # significant bits, so w - m X, when not zero, is at least about 2^-27 of
+    # |w| and the fp64 rounding (2^-53 relative) cannot carry a quotient onto
+    # or across a midpoint
+    safe = np.where(x == 0, 1.0, x)
+    q = codecs.e2m1_encode(blk.astype(np.float64) / safe[:, :, None])
+    q = np.where((x == 0)[:, :, None], 0, q).astype(np.uint8)
+    return nibbles_to_bytes(q.reshape(n, k)), g, sb
+
+
+def nvfp4_scale_image(g, sb):
+    """The stored scale array: g's fp32 bytes, 12 zero bytes, then the E4M3 bytes row by row."""
+    head = np.zeros(NVFP4_HEADER, np.uint8)
+    head[:4] = np.frombuffer(np.float32(g).tobytes(), np.uint8)
+    return np.concatenate([head, np.asarray(sb, np.uint8).ravel()])
+
+
+def nvfp4_split_image(image, n, k):
+    """Inverse of nvfp4_scale_image: (g fp32, E4M3 bytes u8 [n, k/16])."""
+    image = np.asarray(image, np.uint8).ravel()
+    g = np.frombuffer(image[:4].tobytes(), np.float32)[0]
+    return g, image[NVFP4_HEADER:NVFP4_HEADER + n * (k // 16)].reshape(n, k // 16)
+
+
+def pack_nvfp4(w):
+    """fp32 W [N, K] -> (codes u8 [N, K/2], the scale image u8 [16 + N K / 16])."""
+    codes, g, sb = pack_nvfp4_parts(w)
+    return codes, nvfp4_scale_image(g, sb)
+
+
+def dequant_nvfp4_parts(codes, g, sb):
+    """(codes, g, E4M3 scale bytes) -> fp32 W [N, K]: fl32(E2M1(q) * fl32(E4M3(sb) * g))."""
+    v = codecs.e2m1_decode(bytes_to_nibbles(codes))
+    n, k = v.shape
+    x = nvfp4_decode_scales(sb, g)
+    w = (v.reshape(n, k // 16, 16) * x[:, :, None]).astype(np.float32)
+    return w.reshape(n, k)
+
+
+def dequant_nvfp4(codes, image):
+    codes = np.asarray(codes, np.uint8)
+    n, k = codes.shape[0], codes.shape[1] * 2
+    g, sb = nvfp4_split_image(image, n, k)
+    return dequant_nvfp4_parts(codes, g, sb)
+
+
 # ----------------------------------------------------------------------------- dispatch
 
 def pack(fmt, w):
@@ -301,6 +401,8 @@ def pack(fmt, w):
         return pack_mxfp4(w)
     if fmt == FMT_Q8_0:
         return pack_q8_0(w)
+    if fmt == FMT_NVFP4:
+        return pack_nvfp4(w)
     raise ValueError(f"unknown format {fmt}")
 
 
@@ -315,6 +417,8 @@ def dequant(fmt, codes, scales):
         return dequant_mxfp4(codes, scales)
     if fmt == FMT_Q8_0:
         return dequant_q8_0(codes, scales)
+    if fmt == FMT_NVFP4:
+        return dequant_nvfp4(codes, scales)
     raise ValueError(f"unknown format {fmt}")
 
 
