@@ -40,8 +40,8 @@ METRIC = "QLoRA-linear fwd+bwd tokens/s per layer; % bf16 MFMA peak, % HBM BW"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-FMT_NAME = {1: "q4_0", 2: "nf4", 3: "fp8_e4m3", 4: "mxfp4", 5: "q8_0"}
-BPW = {1: 18 / 32, 2: 0.5 + 4 / 64, 3: 1.0, 4: 17 / 32, 5: 34 / 32}
+FMT_NAME = {1: "q4_0", 2: "nf4", 3: "fp8_e4m3", 4: "mxfp4", 5: "q8_0", 6: "nvfp4"}
+BPW = {1: 18 / 32, 2: 0.5 + 4 / 64, 3: 1.0, 4: 17 / 32, 5: 34 / 32, 6: 0.5 + 1 / 16}
 ROTATE_BYTES = 512e6           # packed weight copies rotated per config (the MALL is 256 MB)
 MAX_CFG_STEPS = 20000          # sub-record steps: enough to pass over every rotated copy
 

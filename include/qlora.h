@@ -104,12 +104,29 @@ extern "C" {
  *                  127) (ties to even) stored as a two's complement byte, one
  *                  per element (u8 [N, K]); value q * d; a zero block stores
  *                  d = 0 and codes 0.
+ * QL_FMT_NVFP4     NVFP4 (the FP4 format of the Surogate pages' Blackwell
+ *                  recipe, named there as "NVFP4 (E2M1)" and not defined;
+ *                  NVIDIA's published structure): E2M1 codes in blocks of 16
+ *                  along K, one E4M3 scale byte per block and one fp32
+ *                  scale per tensor.  g = fl32(amax / 2688) (2688 = 6 * 448);
+ *                  block scale byte sb = E4M3(fl32(fl32(amax_b / 6) / g)),
+ *                  nearest even, saturating at 448 (0 when g = 0); block
+ *                  decode scale X = fl32(E4M3(sb) * g); element code = the
+ *                  E2M1 value nearest to the exact quotient w / X (ties to
+ *                  the even mantissa, saturating to +-6, sign bit from w;
+ *                  0 when X = 0); value fl32(E2M1(q) * X).  Codes u8
+ *                  [N, K/2] in the split-nibble groups of 32 of Q4_0 and
+ *                  NF4 (a group's low nibbles are one block of 16, its high
+ *                  nibbles the next).  scales: 16 + N K / 16 bytes -- g as
+ *                  fp32 at byte 0, zero bytes 4..15, then the E4M3 bytes
+ *                  u8 [N, K/16] from byte 16.  K must be a multiple of 32.
  */
 #define QL_FMT_Q4_0 1
 #define QL_FMT_NF4 2
 #define QL_FMT_FP8_E4M3 3
 #define QL_FMT_MXFP4 4
 #define QL_FMT_Q8_0 5
+#define QL_FMT_NVFP4 6
 
 /* workspace query operations */
 #define QL_OP_PACK 0
@@ -125,7 +142,9 @@ typedef struct ql_qweight {
   const uint8_t* codes;  /* Q4_0 / NF4 / MXFP4: u8 [N, K/2]; FP8 / Q8_0:
                             u8 [N, K]                                        */
   const void* scales;    /* Q4_0 / Q8_0: fp16 [N, K/32]; NF4: fp32 [N, K/64];
-                            FP8: fp32 [1]; MXFP4: u8 (E8M0) [N, K/32]        */
+                            FP8: fp32 [1]; MXFP4: u8 (E8M0) [N, K/32];
+                            NVFP4: fp32 g, 12 zero bytes, u8 (E4M3)
+                            [N, K/16]                                        */
 } ql_qweight;
 
 /* ---------------------------------------------------------------- misc */

@@ -17,9 +17,9 @@ LIB_PATH = os.path.join(HERE, "libqlora.so")
 QL_OK = 0
 QL_EINVAL, QL_EUNSUPPORTED, QL_EWORKSPACE, QL_EHIP, QL_ENONFINITE, QL_ESTATE, QL_EOVERFLOW = (
     -1, -2, -3, -4, -5, -6, -7)
-FMT_Q4_0, FMT_NF4, FMT_FP8, FMT_MXFP4, FMT_Q8_0 = 1, 2, 3, 4, 5
+FMT_Q4_0, FMT_NF4, FMT_FP8, FMT_MXFP4, FMT_Q8_0, FMT_NVFP4 = 1, 2, 3, 4, 5, 6
 OP_PACK, OP_FWD, OP_BWD = 0, 1, 2
-BLOCK = {FMT_Q4_0: 32, FMT_NF4: 64, FMT_FP8: 32, FMT_MXFP4: 32, FMT_Q8_0: 32}
+BLOCK = {FMT_Q4_0: 32, FMT_NF4: 64, FMT_FP8: 32, FMT_MXFP4: 32, FMT_Q8_0: 32, FMT_NVFP4: 32}
 
 EXPORTS = (
     "ql_last_error", "ql_version", "ql_nf4_levels", "qlora_workspace_bytes", "quant_pack",
@@ -225,6 +225,10 @@ class QWeight:
         elif fmt == FMT_Q8_0:
             codes = torch.empty((n, k), dtype=torch.uint8, device=device)
             scales = torch.empty((n, k // 32), dtype=torch.int16, device=device)
+        elif fmt == FMT_NVFP4:
+            # the tensor scale and 12 zero bytes, then one E4M3 byte per 16 elements
+            codes = torch.empty((n, k // 2), dtype=torch.uint8, device=device)
+            scales = torch.empty(16 + n * (k // 16), dtype=torch.uint8, device=device)
         else:
             raise ValueError(f"unknown format {fmt}")
         return QWeight(fmt, n, k, codes, scales)

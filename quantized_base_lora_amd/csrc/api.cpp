@@ -43,7 +43,8 @@ int check_sticky() {
 }
 
 int check_shape(int32_t fmt, int64_t n, int64_t k) {
-  if (fmt != QL_FMT_Q4_0 && fmt != QL_FMT_NF4 && fmt != QL_FMT_FP8_E4M3 && fmt != QL_FMT_MXFP4 && fmt != QL_FMT_Q8_0)
+  if (fmt != QL_FMT_Q4_0 && fmt != QL_FMT_NF4 && fmt != QL_FMT_FP8_E4M3 && fmt != QL_FMT_MXFP4 && fmt != QL_FMT_Q8_0 &&
+      fmt != QL_FMT_NVFP4)
     return set_error(QL_EUNSUPPORTED, "unknown format %d", fmt);
   if (n <= 0 || k <= 0) return set_error(QL_EINVAL, "n_out and k_in must be positive");
   if (k % block_of(fmt)) return set_error(QL_EINVAL, "k_in=%lld is not a multiple of %d", (long long)k, block_of(fmt));
@@ -431,6 +432,8 @@ int quant_pack(int32_t format, const float* w, int64_t n_out, int64_t k_in, uint
   hipError_t e;
   if (format == QL_FMT_FP8_E4M3) {
     e = launch_pack_fp8(w, n_out, k_in, codes, reinterpret_cast<float*>(scales), st, s);
+  } else if (format == QL_FMT_NVFP4) {
+    e = launch_pack_nvfp4(w, n_out, k_in, codes, scales, st, s);
   } else {
     e = launch_zero_u32(st, 2, s);
     if (e == hipSuccess) e = launch_pack_blocks(format, w, n_out, k_in, codes, scales, st + 1, s);

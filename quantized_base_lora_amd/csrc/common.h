@@ -58,6 +58,8 @@ hipError_t launch_pack_blocks(int fmt, const float* w, int64_t n, int64_t k,
                               hipStream_t s);
 hipError_t launch_pack_fp8(const float* w, int64_t n, int64_t k, uint8_t* codes,
                            float* scale, uint32_t* ws, hipStream_t s);
+hipError_t launch_pack_nvfp4(const float* w, int64_t n, int64_t k, uint8_t* codes, void* scales,
+                             uint32_t* ws, hipStream_t s);
 hipError_t launch_dequant(const ql_qweight& w, float* out_f32, uint16_t* out_bf16,
                           hipStream_t s);
 hipError_t launch_act_quant(const uint16_t* x, int64_t m, int64_t k, uint8_t* hi,

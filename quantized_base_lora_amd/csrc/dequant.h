@@ -23,8 +23,9 @@ struct Book { float c[16]; };
 // instruction right after a load has to wait for it.
 struct WGroup {
   uint4 c0, c1;      // 4-bit: c0 = 16 bytes; fp8: c0, c1 = 32 bytes
-  uint32_t sraw;     // Q4_0, Q8_0 / MXFP4: the dword holding the fp16 / E8M0 scale; NF4: fp32 bits; FP8: unused
-  uint32_t ssh;      // Q4_0: bit offset of the fp16 scale in sraw (0 or 16); MXFP4: 0, 8, 16 or 24
+  uint32_t sraw;     // Q4_0, Q8_0 / MXFP4 / NVFP4: the dword holding the fp16 / E8M0 / two E4M3 scales;
+                     // NF4: fp32 bits; FP8: unused
+  uint32_t ssh;      // Q4_0, Q8_0, NVFP4: bit offset of the entry in sraw (0 or 16); MXFP4: 0, 8, 16 or 24
 };
 
 
@@ -49,29 +50,74 @@ __device__ __forceinline__ void nf4_lookup4(uint32_t q4, const uint32_t* tl, con
   out23 = __builtin_amdgcn_perm(h, l, 0x07030602u);
 }
 
-// Scale words per row of W and bytes per scale, for the 4-bit formats.
+// Scale entries per row of W and bytes per entry (NVFP4: one entry is the
+// two E4M3 bytes of a 32-element group), and the byte offset of the per-row
+// scales in the scale array (NVFP4 keeps its tensor scale in front).
 template <int FMT> constexpr int64_t scales_per_row(int64_t k) { return FMT == QL_FMT_NF4 ? k / 64 : k / 32; }
 template <int FMT> constexpr int64_t scale_bytes() {
-  return (FMT == QL_FMT_Q4_0 || FMT == QL_FMT_Q8_0) ? 2 : (FMT == QL_FMT_MXFP4 ? 1 : 4);
+  return (FMT == QL_FMT_Q4_0 || FMT == QL_FMT_Q8_0 || FMT == QL_FMT_NVFP4) ? 2 : (FMT == QL_FMT_MXFP4 ? 1 : 4);
 }
+template <int FMT> constexpr int64_t scale_offset() { return FMT == QL_FMT_NVFP4 ? 16 : 0; }
 // formats with one code byte per element (a 32-element group is 32 bytes)
 template <int FMT> constexpr bool byte_codes() { return FMT == QL_FMT_FP8_E4M3 || FMT == QL_FMT_Q8_0; }
 // formats with an fp16 scale per 32-element group
 template <int FMT> constexpr bool fp16_scales() { return FMT == QL_FMT_Q4_0 || FMT == QL_FMT_Q8_0; }
+// formats whose scale entry per 32-element group is 2 bytes (fetched as the
+// aligned dword that holds it, plus a shift)
+template <int FMT> constexpr bool two_byte_scales() { return fp16_scales<FMT>() || FMT == QL_FMT_NVFP4; }
+// formats with one fp32 scale for the whole tensor at the start of the scale array
+template <int FMT> constexpr bool tensor_scale() { return FMT == QL_FMT_FP8_E4M3 || FMT == QL_FMT_NVFP4; }
+
+// The dequantization scale(s) of a group from its scale entry `raw` (already
+// shifted down) and the tensor scale.  NVFP4 has two: s0 for elements 0..15
+// (the low nibbles), s1 for 16..31, each fl32(E4M3(byte) * g); the E4M3
+// decode is the hardware conversion (OCP E4M3FN on gfx950, exact).
+template <int FMT>
+__device__ __forceinline__ void group_scales(uint32_t raw, float tscale, float& s0, float& s1) {
+  s1 = 0.0f;
+  if constexpr (FMT == QL_FMT_FP8_E4M3) {
+    s0 = tscale;
+  } else if constexpr (FMT == QL_FMT_NVFP4) {
+    s0 = __builtin_amdgcn_cvt_f32_fp8((int)raw, 0) * tscale;
+    s1 = __builtin_amdgcn_cvt_f32_fp8((int)raw, 1) * tscale;
+  } else if constexpr (fp16_scales<FMT>()) {
+    s0 = decode_scale_q40(raw);
+  } else if constexpr (FMT == QL_FMT_MXFP4) {
+    s0 = e8m0_as_scale(raw);
+  } else {
+    s0 = __uint_as_float(raw);
+  }
+}
 
 // Dequantizer of one 32-element group, split so its work can be spread over
 // the MFMAs of a contraction step: prepare() once per group (scale decode,
-// NF4 table), then piece(i) yields elements 8i .. 8i+7 as 4 dwords of bf16
-// pairs.  `scale` is already zero for a group outside W; for MXFP4 (whose
+// NF4 / NVFP4 tables), then piece(i) yields elements 8i .. 8i+7 as 4 dwords
+// of bf16 pairs.  NVFP4 is decoded like NF4 with the E2M1 values as the code
+// book and one table per block of 16 (pieces 0-1 and 2-3).  `scale` is already zero for a group outside W; for MXFP4 (whose
 // scale cannot express zero) such a group arrives with its codes cleared.
 // MXFP4 codes are pair-packed, so elements 8i .. 8i+7 are the 4 bytes of code
 // word i, each turned into a bf16 pair by the hardware conversion.
 template <int FMT> struct Deq {
   uint32_t wd[8];
-  uint32_t tl[4], th[4];   // NF4: byte planes of the 16-entry bf16 table
+  uint32_t tl[4], th[4];   // NF4: byte planes of the 16-entry bf16 table (NVFP4: elements 0..15)
+  uint32_t tl2[4], th2[4]; // NVFP4: the table of elements 16..31
   float d, nd8;            // Q4_0: d and -8 d; Q8_0: d and -128 d; FP8: the tensor scale in d
 
-  __device__ __forceinline__ void prepare(const WGroup& g, float scale, const Book& book, bool in = true) {
+  // per-thread table of bf16_RNE(fl32(c[q] * a)), split into byte planes
+  __device__ __forceinline__ static void build_table(const Book& book, float a, uint32_t* lo, uint32_t* hi) {
+    uint32_t pr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pr[i] = pack_bf16x2(book.c[2 * i] * a, book.c[2 * i + 1] * a);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      lo[w] = __builtin_amdgcn_perm(pr[2 * w + 1], pr[2 * w], 0x06040200u);
+      hi[w] = __builtin_amdgcn_perm(pr[2 * w + 1], pr[2 * w], 0x07050301u);
+    }
+  }
+
+  // scale2: NVFP4's scale of elements 16..31 (scale is that of 0..15)
+  __device__ __forceinline__ void prepare(const WGroup& g, float scale, const Book& book, bool in = true,
+                                          float scale2 = 0.0f) {
     wd[0] = g.c0.x; wd[1] = g.c0.y; wd[2] = g.c0.z; wd[3] = g.c0.w;
     wd[4] = g.c1.x; wd[5] = g.c1.y; wd[6] = g.c1.z; wd[7] = g.c1.w;
     if constexpr (FMT == QL_FMT_MXFP4) {
@@ -81,17 +127,8 @@ template <int FMT> struct Deq {
     }
     d = scale;
     nd8 = (FMT == QL_FMT_Q8_0 ? -128.0f : -8.0f) * scale;   // (q - 8) d = fma(q, d, -8d), exact
-    if constexpr (FMT == QL_FMT_NF4) {
-      // per-thread table of bf16_RNE(fl32(c[q] * a)), split into byte planes
-      uint32_t pr[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pr[i] = pack_bf16x2(book.c[2 * i] * scale, book.c[2 * i + 1] * scale);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        tl[w] = __builtin_amdgcn_perm(pr[2 * w + 1], pr[2 * w], 0x06040200u);
-        th[w] = __builtin_amdgcn_perm(pr[2 * w + 1], pr[2 * w], 0x07050301u);
-      }
-    }
+    if constexpr (FMT == QL_FMT_NF4 || FMT == QL_FMT_NVFP4) build_table(book, scale, tl, th);
+    if constexpr (FMT == QL_FMT_NVFP4) build_table(book, scale2, tl2, th2);
   }
 
   __device__ __forceinline__ uint4 piece(int i) const {
@@ -133,6 +170,9 @@ template <int FMT> struct Deq {
           for (int b = 0; b < 4; ++b) e[b] = fmaf((float)((q4 >> (8 * b)) & 0xFF), d, nd8);
           o[2 * h] = pack_bf16x2(e[0], e[1]);
           o[2 * h + 1] = pack_bf16x2(e[2], e[3]);
+        } else if constexpr (FMT == QL_FMT_NVFP4) {
+          if (i < 2) nf4_lookup4(q4, tl, th, o[2 * h], o[2 * h + 1]);
+          else nf4_lookup4(q4, tl2, th2, o[2 * h], o[2 * h + 1]);
         } else {
           nf4_lookup4(q4, tl, th, o[2 * h], o[2 * h + 1]);
         }

@@ -149,11 +149,11 @@ void qgemm_kernel(GemmArgs ga) {
   const int64_t srow = scales_per_row<FMT>(p.K);   // scale words per row
   const int64_t ssz = scale_bytes<FMT>();
   const __amdgpu_buffer_rsrc_t rscale =
-      rsrc((const char*)p.scales + wrow0 * srow * ssz, (p.N - wrow0) * srow * ssz);
+      rsrc((const char*)p.scales + scale_offset<FMT>() + wrow0 * srow * ssz, (p.N - wrow0) * srow * ssz);
   const __amdgpu_buffer_rsrc_t rdown = rsrc(p.down, (int64_t)R * p.C * 2);
 
   float tscale = 0.0f;
-  if constexpr (FP8) tscale = reinterpret_cast<const float*>(p.scales)[0];
+  if constexpr (tensor_scale<FMT>()) tscale = reinterpret_cast<const float*>(p.scales)[0];
 
   // ---- per-thread load coordinates
   const int arow = tid >> 3, acol = (tid & 7) * 8;   // act: rows arow + ARS i, 8 columns
@@ -205,7 +205,7 @@ void qgemm_kernel(GemmArgs ga) {
     if constexpr (BYTES) wreg[j].c1 = bload16(rcode, live ? coff + 16 : OOB);
     if constexpr (!FP8) {
       const int64_t kabs = TRANS ? (o0 >> 5) + wg[j] : kgrp;   // group index along K
-      if constexpr (fp16_scales<FMT>()) {
+      if constexpr (two_byte_scales<FMT>()) {
         const int64_t idx = wrow * srow + kabs;
         wreg[j].sraw = bload4(rscale, live ? (uint32_t)((idx * 2) & ~3LL) : OOB);
         wreg[j].ssh = (uint32_t)(idx & 1) * 16;
@@ -232,12 +232,9 @@ void qgemm_kernel(GemmArgs ga) {
     *reinterpret_cast<uint4*>(st + (arow + ARS * i) * SA + acol) = areg[i];
   };
   auto prepare_w = [&](int j) {
-    float scale;
-    if constexpr (FP8) scale = tscale;
-    else if constexpr (fp16_scales<FMT>()) scale = decode_scale_q40(wreg[j].sraw >> wreg[j].ssh);
-    else if constexpr (FMT == QL_FMT_MXFP4) scale = e8m0_as_scale(wreg[j].sraw >> wreg[j].ssh);
-    else scale = __uint_as_float(wreg[j].sraw);
-    deq.prepare(wreg[j], wg_in[j] ? scale : 0.0f, p.book, wg_in[j]);
+    float s0, s1;
+    group_scales<FMT>(wreg[j].sraw >> wreg[j].ssh, tscale, s0, s1);
+    deq.prepare(wreg[j], wg_in[j] ? s0 : 0.0f, p.book, wg_in[j], wg_in[j] ? s1 : 0.0f);
   };
   auto store_w = [&](uint16_t* st, int j, int i) {   // elements 8i .. 8i+7 of W group j
     if (!wtask) return;
@@ -638,6 +635,7 @@ hipError_t launch_tiles(int fmt, const GemmArgs& g, bool trans, int r, hipStream
     case QL_FMT_NF4: return launch_f<QL_FMT_NF4>(g, trans, r, s);
     case QL_FMT_MXFP4: return launch_f<QL_FMT_MXFP4>(g, trans, r, s);
     case QL_FMT_Q8_0: return launch_f<QL_FMT_Q8_0>(g, trans, r, s);
+    case QL_FMT_NVFP4: return launch_f<QL_FMT_NVFP4>(g, trans, r, s);
     default: return launch_f<QL_FMT_FP8_E4M3>(g, trans, r, s);
   }
 }
@@ -682,8 +680,17 @@ static void make_params(const GemmCall& c, Params& p, int& splits) {
   p.C = c.trans ? p.N : p.K;
   p.O = c.trans ? p.K : p.N;
   p.s = c.s;
-  const Nf4Table& t = nf4_table();
-  for (int i = 0; i < 16; ++i) p.book.c[i] = t.level[i];
+  if (c.w->format == QL_FMT_NVFP4) {
+    // E2M1 values in code order: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6, then their negatives
+    static const float e2m1[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+    for (int i = 0; i < 8; ++i) {
+      p.book.c[i] = e2m1[i];
+      p.book.c[8 + i] = -e2m1[i];
+    }
+  } else {
+    const Nf4Table& t = nf4_table();
+    for (int i = 0; i < 16; ++i) p.book.c[i] = t.level[i];
+  }
   const SplitPlan pl = split_plan(c.trans, c.m, p.N, p.K, c.r);
   splits = pl.splits;
   if (pl.splits > 0) {

@@ -7,9 +7,11 @@
 // blocks of 32 E2M1 codes with an E8M0 power-of-two scale (OCP
 // Microscaling, the FP4 base of the Surogate pages' FP4 recipes); Q8_0
 // blocks of 32 int8 codes with an fp16 scale absmax/127 (the 8-bit member
-// of the legacy GGUF family).  Every
+// of the legacy GGUF family); NVFP4 blocks of 16 E2M1 codes with an E4M3
+// scale and an fp32 tensor scale (the Surogate pages' NVFP4 (E2M1)).  Every
 // quantization decision is taken in IEEE fp32 with correctly rounded
-// division and ties-to-even rounding, so codes are reproducible bit for bit.
+// division and ties-to-even rounding (NVFP4's element codes by exact fp64
+// comparisons), so codes are reproducible bit for bit.
 //
 // Codecs are written out here from the format definitions (integer bit
 // manipulation): the hardware fp8 conversion does not saturate, and the fp16
@@ -212,6 +214,72 @@ __global__ __launch_bounds__(kThreads) void fill_u32_kernel(uint32_t* p, int64_t
   if (i < n) p[i] = value;
 }
 
+// ------------------------------------------------------------------ NVFP4 pack
+// E2M1 code of w against the block decode scale x > 0: the value nearest to
+// the exact quotient w / x, ties to the even mantissa, saturating at 6.  Each
+// midpoint m x (m = 0.25, 0.75, ..., 5: at most 3 significant bits) is formed
+// exactly in fp64 (x has 24), so the comparisons decide as exact arithmetic.
+__device__ __forceinline__ uint32_t e2m1_code_exact(float w, float x) {
+  const double a = fabs((double)w), d = (double)x;
+  const uint32_t c = (a > 0.25 * d) + (a >= 0.75 * d) + (a > 1.25 * d) + (a >= 1.75 * d) + (a > 2.5 * d) +
+                     (a >= 3.5 * d) + (a > 5.0 * d);
+  return c | ((__float_as_uint(w) >> 31) << 3);
+}
+
+// One thread per 32-element group (two blocks of 16).  ws[0] holds the bits
+// of the tensor's largest magnitude (absmax_kernel).  g = fl32(amax / 2688);
+// block scale byte E4M3(fl32(fl32(amax_b / 6) / g)) (0 when g = 0); block
+// decode scale X = fl32(E4M3(sb) g); codes against X (0 when X = 0), stored
+// in split-nibble groups; the scale array is g, 12 zero bytes, then two E4M3
+// bytes per group.
+__global__ __launch_bounds__(kThreads) void pack_nvfp4_kernel(const float* __restrict__ w, int64_t groups,
+                                                              const uint32_t* __restrict__ ws,
+                                                              uint8_t* __restrict__ codes,
+                                                              uint8_t* __restrict__ scales,
+                                                              uint32_t* __restrict__ status) {
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const float g = fdiv_rn(__uint_as_float(ws[0]), 2688.0f);
+  if (gid == 0) {
+    uint32_t* head = reinterpret_cast<uint32_t*>(scales);
+    head[0] = __float_as_uint(g);
+    head[1] = head[2] = head[3] = 0u;
+  }
+  if (gid >= groups) return;
+  float v[32];
+  const float4* src = reinterpret_cast<const float4*>(w + gid * 32);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float4 t = src[i];
+    v[4 * i + 0] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+  }
+  bool bad = false;
+  uint32_t q[32];
+  uint32_t sb[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      bad |= !isfinite(v[16 * b + i]);
+      amax = fmaxf(amax, fabsf(v[16 * b + i]));
+    }
+    sb[b] = g == 0.0f ? 0u : f32_to_e4m3(fdiv_rn(fdiv_rn(amax, 6.0f), g));
+    const float x = e4m3_to_f32(sb[b]) * g;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q[16 * b + i] = x == 0.0f ? 0u : e2m1_code_exact(v[16 * b + i], x);
+  }
+  uint32_t word[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    word[i] = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) word[i] |= (q[4 * i + b] | (q[4 * i + b + 16] << 4)) << (8 * b);
+  }
+  *reinterpret_cast<uint4*>(codes + gid * 16) = make_uint4(word[0], word[1], word[2], word[3]);
+  reinterpret_cast<uint16_t*>(scales + 16)[gid] = (uint16_t)(sb[0] | (sb[1] << 8));
+  if (bad) atomicOr(status, 1u);
+}
+
 // ws[0] = bits of max|w| (non-negative floats order like their bits), ws[1] |= 1 on non-finite.
 __global__ __launch_bounds__(kThreads) void absmax_kernel(const float* __restrict__ w, int64_t n4,
                                                           uint32_t* __restrict__ ws) {
@@ -289,6 +357,21 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
       uint32_t wd[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[16 * h + i] = (float)(int8_t)((wd[i / 4] >> (8 * (i % 4))) & 0xFF) * d;
+    }
+  } else if (FMT == QL_FMT_NVFP4) {
+    // fl32(E2M1(q) * X), X = fl32(E4M3(sb) * g); elements 0..15 low nibbles, 16..31 high
+    uint4 t = *reinterpret_cast<const uint4*>(codes + gid * 16);
+    uint32_t wd[4] = {t.x, t.y, t.z, t.w};
+    const uint8_t* sc = reinterpret_cast<const uint8_t*>(scales);
+    const float g = reinterpret_cast<const float*>(scales)[0];
+    const float x[2] = {e4m3_to_f32(sc[16 + 2 * gid]) * g, e4m3_to_f32(sc[16 + 2 * gid + 1]) * g};
+    const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      int j = e & 15, hi = e >> 4;
+      uint32_t c = (wd[j / 4] >> (8 * (j % 4) + 4 * hi)) & 0xF;
+      const float val = (c & 8) ? -mag[c & 7] : mag[c & 7];
+      v[e] = val * x[hi];
     }
   } else if (FMT == QL_FMT_MXFP4) {
     // the conversion the GEMMs use; its bf16 results are exact, so fp32 is the same value
@@ -517,6 +600,21 @@ hipError_t launch_pack_fp8(const float* w, int64_t n, int64_t k, uint8_t* codes,
   return hipGetLastError();
 }
 
+hipError_t launch_pack_nvfp4(const float* w, int64_t n, int64_t k, uint8_t* codes, void* scales,
+                             uint32_t* ws, hipStream_t s) {
+  int64_t total = n * k;   // multiple of 32 (validated)
+  hipError_t e = launch_zero_u32(ws, 2, s);
+  if (e != hipSuccess) return e;
+  int64_t n4 = total / 4;
+  unsigned blocks = (unsigned)std::min<int64_t>(grid_for(n4), 4096);
+  hipLaunchKernelGGL(absmax_kernel, dim3(blocks), dim3(kThreads), 0, s, w, n4, ws);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t groups = total / 32;
+  hipLaunchKernelGGL(pack_nvfp4_kernel, dim3(grid_for(groups)), dim3(kThreads), 0, s, w, groups, ws, codes,
+                     reinterpret_cast<uint8_t*>(scales), ws + 1);
+  return hipGetLastError();
+}
+
 hipError_t launch_dequant(const ql_qweight& w, float* out_f32, uint16_t* out_bf16, hipStream_t s) {
   int64_t groups = w.n_out * (w.k_in / 32);
   Levels lv{};
@@ -537,6 +635,10 @@ hipError_t launch_dequant(const ql_qweight& w, float* out_f32, uint16_t* out_bf1
       break;
     case QL_FMT_Q8_0:
       hipLaunchKernelGGL(dequant_kernel<QL_FMT_Q8_0>, dim3(grid_for(groups)), dim3(kThreads), 0, s,
+                         w.codes, w.scales, groups, w.k_in, out_f32, out_bf16, lv);
+      break;
+    case QL_FMT_NVFP4:
+      hipLaunchKernelGGL(dequant_kernel<QL_FMT_NVFP4>, dim3(grid_for(groups)), dim3(kThreads), 0, s,
                          w.codes, w.scales, groups, w.k_in, out_f32, out_bf16, lv);
       break;
     default:

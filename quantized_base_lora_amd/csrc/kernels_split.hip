@@ -87,10 +87,10 @@ void qsplit_kernel(SplitArgs ga) {
   const int64_t srow = scales_per_row<FMT>(p.K);
   const int64_t ssz = scale_bytes<FMT>();
   const __amdgpu_buffer_rsrc_t rscale =
-      rsrc((const char*)p.scales + wrow0 * srow * ssz, (p.N - wrow0) * srow * ssz);
+      rsrc((const char*)p.scales + scale_offset<FMT>() + wrow0 * srow * ssz, (p.N - wrow0) * srow * ssz);
   const __amdgpu_buffer_rsrc_t rdown = rsrc(p.down, (int64_t)R * p.C * 2);
   float tscale = 0.0f;
-  if constexpr (FP8) tscale = reinterpret_cast<const float*>(p.scales)[0];
+  if constexpr (tensor_scale<FMT>()) tscale = reinterpret_cast<const float*>(p.scales)[0];
 
   const int arow = tid >> 3, acol = (tid & 7) * 8;   // act rows arow (and arow + 32 when MBK = 2)
   const int wr = tid / GPR, wg = tid % GPR;          // one W group per thread per step
@@ -130,7 +130,7 @@ void qsplit_kernel(SplitArgs ga) {
         sl.w.c0 = bload16(rcode, gl ? (uint32_t)(wrow * crow + c0 / 2 + 16 * hsel) : OOB);
         sl.w.c1 = make_uint4(0, 0, 0, 0);
         const int64_t idx = wrow * srow + (c0 >> 5) + hsel;   // the group's scale index (NF4: per 64, below)
-        if constexpr (FMT == QL_FMT_Q4_0) sl.w.sraw = bload2(rscale, gl ? (uint32_t)(idx * 2) : OOB);
+        if constexpr (FMT == QL_FMT_Q4_0 || FMT == QL_FMT_NVFP4) sl.w.sraw = bload2(rscale, gl ? (uint32_t)(idx * 2) : OOB);
         else if constexpr (FMT == QL_FMT_MXFP4) sl.w.sraw = bload1(rscale, gl ? (uint32_t)idx : OOB);
         else sl.w.sraw = bload4(rscale, gl ? (uint32_t)((wrow * srow + (c0 >> 6)) * 4) : OOB);
       }
@@ -147,7 +147,7 @@ void qsplit_kernel(SplitArgs ga) {
       sl.w.sraw = 0;
     } else {
       const int64_t kabs = TRANS ? (o0 >> 5) + wg : kgrp;
-      if constexpr (fp16_scales<FMT>()) {
+      if constexpr (two_byte_scales<FMT>()) {
         const int64_t idx = wrow * srow + kabs;
         sl.w.sraw = bload4(rscale, wlive ? (uint32_t)((idx * 2) & ~3LL) : OOB);
         sl.w.ssh = (uint32_t)(idx & 1) * 16;
@@ -169,13 +169,10 @@ void qsplit_kernel(SplitArgs ga) {
   auto dequant_direct = [&](const Slot& sl, uint4* wb) {
     const int64_t c0 = (int64_t)sl.kt * TK;
     const bool gl = sl.kt < kend && c0 + 32 * hsel < p.C;
-    float sc;
-    if constexpr (FP8) sc = tscale;
-    else if constexpr (fp16_scales<FMT>()) sc = decode_scale_q40(sl.w.sraw);
-    else if constexpr (FMT == QL_FMT_MXFP4) sc = e8m0_as_scale(sl.w.sraw);
-    else sc = __uint_as_float(sl.w.sraw);
+    float s0, s1;
+    group_scales<FMT>(sl.w.sraw, tscale, s0, s1);
     Deq<FMT> dq;
-    dq.prepare(sl.w, gl ? sc : 0.0f, p.book, gl);
+    dq.prepare(sl.w, gl ? s0 : 0.0f, p.book, gl, gl ? s1 : 0.0f);
 #pragma unroll
     for (int i = 0; i < 4; ++i) wb[i] = dq.piece(i);
   };
@@ -187,13 +184,10 @@ void qsplit_kernel(SplitArgs ga) {
       dequant_direct(sl, wb);
       return;
     }
-    float scale;
-    if constexpr (FP8) scale = tscale;
-    else if constexpr (fp16_scales<FMT>()) scale = decode_scale_q40(sl.w.sraw >> sl.w.ssh);
-    else if constexpr (FMT == QL_FMT_MXFP4) scale = e8m0_as_scale(sl.w.sraw >> sl.w.ssh);
-    else scale = __uint_as_float(sl.w.sraw);
+    float s0, s1;
+    group_scales<FMT>(sl.w.sraw >> sl.w.ssh, tscale, s0, s1);
     Deq<FMT> dq;
-    dq.prepare(sl.w, wg_in ? scale : 0.0f, p.book, wg_in);
+    dq.prepare(sl.w, wg_in ? s0 : 0.0f, p.book, wg_in, wg_in ? s1 : 0.0f);
     uint16_t* dst = st + A_EL + (TRANS ? wr * SBT : wr * SA) + wg * 32;
 #pragma unroll
     for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(dst + 8 * i) = dq.piece(i);
@@ -371,8 +365,11 @@ void qsplit16_kernel(SplitArgs ga) {
   const __amdgpu_buffer_rsrc_t rcode = rsrc(p.codes + o0 * crow, (p.N - o0) * crow);
   const int64_t srow = scales_per_row<FMT>(p.K);
   const int64_t ssz = scale_bytes<FMT>();
-  const __amdgpu_buffer_rsrc_t rscale = rsrc((const char*)p.scales + o0 * srow * ssz, (p.N - o0) * srow * ssz);
+  const __amdgpu_buffer_rsrc_t rscale =
+      rsrc((const char*)p.scales + scale_offset<FMT>() + o0 * srow * ssz, (p.N - o0) * srow * ssz);
   const __amdgpu_buffer_rsrc_t rdown = rsrc(p.down, (int64_t)R * p.C * 2);
+  float tscale = 0.0f;
+  if constexpr (tensor_scale<FMT>()) tscale = reinterpret_cast<const float*>(p.scales)[0];
 
   const int arow = tid >> 4, acol = (tid & 15) * 8;  // activation: one 16-byte piece per thread
   const int q = lane >> 4;                           // this lane's group of the step
@@ -396,7 +393,7 @@ void qsplit16_kernel(SplitArgs ga) {
       sl.w[b].c0 = bload16(rcode, gl ? (uint32_t)(wrow * crow + c0 / 2 + 16 * q) : OOB);
       sl.w[b].c1 = make_uint4(0, 0, 0, 0);
       const int64_t idx = wrow * srow + (c0 >> 5) + q;
-      if constexpr (fp16_scales<FMT>()) sl.w[b].sraw = bload2(rscale, gl ? (uint32_t)(idx * 2) : OOB);
+      if constexpr (two_byte_scales<FMT>()) sl.w[b].sraw = bload2(rscale, gl ? (uint32_t)(idx * 2) : OOB);
       else if constexpr (FMT == QL_FMT_MXFP4) sl.w[b].sraw = bload1(rscale, gl ? (uint32_t)idx : OOB);
       else sl.w[b].sraw = bload4(rscale, gl ? (uint32_t)((wrow * srow + ((c0 + 32 * q) >> 6)) * 4) : OOB);
       sl.w[b].ssh = 0;
@@ -421,12 +418,10 @@ void qsplit16_kernel(SplitArgs ga) {
     const bool gl = sl.kt < kend && (int64_t)sl.kt * TK2 + 32 * q < p.C;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      float sc;
-      if constexpr (fp16_scales<FMT>()) sc = decode_scale_q40(sl.w[b].sraw);
-      else if constexpr (FMT == QL_FMT_MXFP4) sc = e8m0_as_scale(sl.w[b].sraw);
-      else sc = __uint_as_float(sl.w[b].sraw);
+      float s0, s1;
+      group_scales<FMT>(sl.w[b].sraw, tscale, s0, s1);
       Deq<FMT> dq;
-      dq.prepare(sl.w[b], gl ? sc : 0.0f, p.book, gl);
+      dq.prepare(sl.w[b], gl ? s0 : 0.0f, p.book, gl, gl ? s1 : 0.0f);
 #pragma unroll
       for (int i = 0; i < 4; ++i) wb[b][i] = dq.piece(i);
     }
@@ -958,6 +953,7 @@ hipError_t launch_split_path(int fmt, bool trans, int r, const SplitGroup& g, co
     case QL_FMT_NF4: return trans ? launch_r<QL_FMT_NF4, true>(g, r, gf, s) : launch_r<QL_FMT_NF4, false>(g, r, gf, s);
     case QL_FMT_MXFP4: return trans ? launch_r<QL_FMT_MXFP4, true>(g, r, gf, s) : launch_r<QL_FMT_MXFP4, false>(g, r, gf, s);
     case QL_FMT_Q8_0: return trans ? launch_r<QL_FMT_Q8_0, true>(g, r, gf, s) : launch_r<QL_FMT_Q8_0, false>(g, r, gf, s);
+    case QL_FMT_NVFP4: return trans ? launch_r<QL_FMT_NVFP4, true>(g, r, gf, s) : launch_r<QL_FMT_NVFP4, false>(g, r, gf, s);
     default: return trans ? launch_r<QL_FMT_FP8_E4M3, true>(g, r, gf, s) : launch_r<QL_FMT_FP8_E4M3, false>(g, r, gf, s);
   }
 }

@@ -30,6 +30,8 @@ def _sizes(fmt, n, k):
         return n * k // 2, n * (k // 32)
     if fmt == B.FMT_Q8_0:
         return n * k, n * (k // 32) * 2
+    if fmt == B.FMT_NVFP4:
+        return n * k // 2, 16 + n * (k // 16)
     return n * k // 2, n * (k // 64) * 4
 
 

@@ -21,7 +21,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-FMT_Q4_0, FMT_NF4, FMT_FP8, FMT_MXFP4, FMT_Q8_0 = 1, 2, 3, 4, 5
+FMT_Q4_0, FMT_NF4, FMT_FP8, FMT_MXFP4, FMT_Q8_0, FMT_NVFP4 = 1, 2, 3, 4, 5, 6
 TID_W, TID_A, TID_B, TID_X, TID_DY = 0, 1, 2, 3, 4
 
 
@@ -82,6 +82,9 @@ WORKLOADS = {
     "llama3.1_8b_q8_0": Workload(6, "llama3.1_8b_q8_0", FMT_Q8_0, LLAMA31_8B, 4096, 16, 16.0,
                                  "Llama-3.1-8B decoder layer, Q8_0-style base (int8, fp16 per 32)",
                                  extra_m=(16, 64)),
+    "llama3.1_8b_nvfp4": Workload(7, "llama3.1_8b_nvfp4", FMT_NVFP4, LLAMA31_8B, 4096, 16, 16.0,
+                                  "Llama-3.1-8B decoder layer, NVFP4 base (E2M1, E4M3 per 16, fp32 per tensor)",
+                                  extra_m=(16, 64)),
 }
 
 

@@ -41,7 +41,7 @@ def scales_bytes(fmt, s):
         return np.ascontiguousarray(s, dtype=np.uint16).view(np.uint8).ravel()
     if fmt == ofmt.FMT_NF4:
         return np.ascontiguousarray(s, dtype=np.float32).view(np.uint8).ravel()
-    if fmt == ofmt.FMT_MXFP4:
+    if fmt in (ofmt.FMT_MXFP4, ofmt.FMT_NVFP4):
         return np.ascontiguousarray(s, dtype=np.uint8).ravel()
     return np.array([s], dtype=np.float32).view(np.uint8)
 

@@ -28,6 +28,7 @@ CONFIGS = [
     ("qwen3_8b_fp8", 8192),
     ("llama3.1_8b_mxfp4", 4096), ("llama3.1_8b_mxfp4", 64), ("llama3.1_8b_mxfp4", 16),
     ("llama3.1_8b_q8_0", 4096), ("llama3.1_8b_q8_0", 64), ("llama3.1_8b_q8_0", 16),
+    ("llama3.1_8b_nvfp4", 4096), ("llama3.1_8b_nvfp4", 64), ("llama3.1_8b_nvfp4", 16),
 ]
 
 _oracle_cache = {}

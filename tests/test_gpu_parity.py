@@ -17,8 +17,8 @@ from quantized_base_lora_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-FMTS = [ofmt.FMT_Q4_0, ofmt.FMT_NF4, ofmt.FMT_FP8, ofmt.FMT_MXFP4, ofmt.FMT_Q8_0]
-FNAME = {1: "q4_0", 2: "nf4", 3: "fp8", 4: "mxfp4", 5: "q8_0"}
+FMTS = [ofmt.FMT_Q4_0, ofmt.FMT_NF4, ofmt.FMT_FP8, ofmt.FMT_MXFP4, ofmt.FMT_Q8_0, ofmt.FMT_NVFP4]
+FNAME = {1: "q4_0", 2: "nf4", 3: "fp8", 4: "mxfp4", 5: "q8_0", 6: "nvfp4"}
 
 
 def say(*a):
@@ -69,6 +69,26 @@ def special_weight(fmt, n, k, seed):
         w[2, 0] = np.float32(127 * 2.0 ** -7)
         # a scale that rounds down to the smallest fp16 subnormal: the clamp acts
         w[3, :32] = np.float32(8.5e-8 * 127) * np.linspace(-1, 1, 32, dtype=np.float32)
+    elif fmt == ofmt.FMT_NVFP4:
+        # the tensor maximum 2688 * 2^-12 makes g = 2^-12; a block whose
+        # largest element 6 * 8 g gives scale byte 8.0 (0x50) and X = 2^-9,
+        # holding every E2M1 midpoint in both signs, saturation, negative zero
+        # and a negative value that rounds to zero; a block whose scale is an
+        # E4M3 tie (42 -> 40); a block whose scale rounds to zero
+        g = np.float32(2.0 ** -12)
+        w[5, 0] = np.float32(2688) * g
+        x = np.float32(8.0) * g
+        t = np.float32([6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+        w[2, :32] = 0
+        w[2, :8] = t * x
+        w[2, 8:15] = -t[1:] * x
+        w[2, 15] = -0.0
+        w[2, 16:24] = -t * x
+        w[2, 24] = np.float32(-0.2) * x
+        w[2, 25] = np.float32(6.3) * x      # scale quotient 8.4 rounds down to 8: saturates at 6 X
+        w[3, :32] = 0
+        w[3, :16] = np.float32(42 * 6) * g * np.linspace(-1, 1, 16, dtype=np.float32)
+        w[3, 16] = np.float32(2.0 ** -12) * g
     w[4, :blk] = np.float32(0.01)
     return w
 
@@ -174,6 +194,23 @@ def test_dequant_all_codes_and_scales(lib):
     assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
     gb = H.bf16_tensor_bits(b).reshape(n, 32)
     assert np.array_equal(gb[:255], codecs.bf16_encode(ref[:255]))
+    # NVFP4: all 16 codes against every E4M3 scale byte (0x7F and 0xFF are NaN), a few tensor scales
+    n = 256
+    sb = np.stack([np.arange(256, dtype=np.uint8), np.arange(256, dtype=np.uint8)[::-1]], axis=1)
+    q = np.tile(np.arange(16, dtype=np.uint8), (n, 2))
+    codes = ofmt.nibbles_to_bytes(q)
+    for gt in np.float32([1.0, 0.1, 3.7e-5]):
+        image = ofmt.nvfp4_scale_image(gt, sb)
+        qw = B.QWeight(B.FMT_NVFP4, n, 32, torch.from_numpy(codes).cuda(), torch.from_numpy(image).cuda())
+        f, b = B.dequant(qw)
+        ref = ofmt.dequant_nvfp4(codes, image)
+        got = f.cpu().numpy()
+        nan = np.isnan(ref)
+        assert nan.sum() == 64 and np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+        gb = H.bf16_tensor_bits(b)
+        rb = codecs.bf16_encode(ref)
+        assert np.array_equal(gb[~nan], rb[~nan])
     # FP8: all 256 codes (two of them NaN) times a few scales
     for s in np.float32([1.0, 0.02 / 448, 7.77e-3]):
         codes = np.tile(np.arange(256, dtype=np.uint8), (32, 1))
@@ -257,6 +294,13 @@ CASES = [
     ("q80_tiles_r8", ofmt.FMT_Q8_0, 520, 1024, 416, 8, 16.0),
     ("small_q80_m64_r32", ofmt.FMT_Q8_0, 64, 1056, 224, 32, 64.0),
     ("small_q80_m20", ofmt.FMT_Q8_0, 20, 2048, 320, 16, 32.0),
+    # NVFP4 base (E2M1 codes, E4M3 scale per 16, fp32 tensor scale): tiles with
+    # ragged edges, the split path with 64, 33 and 17 tokens
+    ("nvfp4_ragged_mn", ofmt.FMT_NVFP4, 300, 320, 160, 16, 32.0),
+    ("nvfp4_tiles_r32", ofmt.FMT_NVFP4, 520, 1024, 416, 32, 64.0),
+    ("small_nvfp4_m64_r8", ofmt.FMT_NVFP4, 64, 512, 384, 8, 16.0),
+    ("small_nvfp4_m33", ofmt.FMT_NVFP4, 33, 1056, 224, 16, 32.0),
+    ("small_nvfp4_m17_r32", ofmt.FMT_NVFP4, 17, 2048, 320, 32, 64.0),
     # 128x128 tiles, 10 row blocks x 16 column tiles = 160 tiles: the per-XCD
     # tile runs are active (tiles % 8 == 0) and the row blocks fall into
     # groups of 4 + 4 + 2; forward in the first case, dX in the second

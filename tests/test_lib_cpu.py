@@ -101,6 +101,8 @@ def test_pack_argument_errors(lib):
     assert lib.quant_pack(9, P, 64, 128, P, P, P, 256, None) == binding.QL_EUNSUPPORTED
     assert lib.quant_pack(binding.FMT_NF4, P, 64, 96, P, P, P, 256, None) == binding.QL_EINVAL
     assert "multiple of 64" in _err(lib)
+    assert lib.quant_pack(binding.FMT_NVFP4, P, 64, 48, P, P, P, 256, None) == binding.QL_EINVAL
+    assert "multiple of 32" in _err(lib)
     assert lib.quant_pack(binding.FMT_Q4_0, P, 48, 64, P, P, P, 256, None) == binding.QL_EINVAL
     assert lib.quant_pack(binding.FMT_Q4_0, None, 64, 64, P, P, P, 256, None) == binding.QL_EINVAL
     assert lib.quant_pack(binding.FMT_Q4_0, ctypes.c_void_p(0x10004), 64, 64, P, P, P, 256, None) == binding.QL_EINVAL
