@@ -20,7 +20,8 @@ namespace {
 // across workgroups; fp32 partial sums out.  One launch serves a group of
 // independent problems: each workgroup finds its problem, column tile and
 // split in a table in the kernel arguments.  (The forward with at most 16
-// tokens and a 4-bit base runs qsplit16_kernel below instead.)
+// tokens and a 4-bit base runs qstream16_kernel or qsplit16_kernel below
+// instead.)
 //
 // Forward (y = x.W^T): no W element is used by more than one wave, so W is
 // not staged through LDS.  Each lane loads the codes of its own MFMA
@@ -529,6 +530,197 @@ void qsplit16_kernel(SplitArgs ga) {
   }
 }
 
+// Forward with at most 16 tokens, streaming form.  The same tile, lane
+// mapping and partial layout as qsplit16_kernel, but no workgroup barrier
+// inside the contraction: the workgroup's whole activation slice (16 tokens
+// x at most S16_STEPS steps of 128) is loaded into LDS once, behind the
+// first W loads, and each wave then streams its 32 W rows through a ring of
+// D register stages, dequantizing straight into MFMA operands, at its own
+// pace.  The rank-r projection U of column tile 0 is spread over its four
+// waves (wave w takes the 32-element slice w of every step, loading its
+// adapter fragments in the same ring), and the four partial sums are added
+// through LDS at the end.
+constexpr int S16_STEPS = 8;
+constexpr int XS16 = S16_STEPS * TK2 + 8;          // LDS row stride of the activation slice (bf16)
+
+template <int FMT, int R>
+__global__ __launch_bounds__(256) void qstream16_kernel(SplitArgs ga) {
+  constexpr int TN = 128, D = 4;
+  constexpr int RB = (R + 15) / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[16 * XS16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bid = (int)blockIdx.x;
+  int pi = 0;
+  while (pi + 1 < ga.n && bid >= ga.unit0[pi + 1]) ++pi;
+  const Params& p = ga.p[pi];
+  const int u0 = ga.unit0[pi], nunits = ga.unit0[pi + 1] - u0, nt = ga.ntiles[pi];
+  int unit = bid - u0;
+  if ((nunits & 7) == 0 && (u0 & 7) == 0) unit = (unit & 7) * (nunits >> 3) + (unit >> 3);
+  const int ntile = unit % nt, split = unit / nt;
+  const int64_t o0 = (int64_t)ntile * TN;
+  const int KT = (int)((p.C + TK2 - 1) / TK2);
+  const int kbeg = split * p.sps;
+  const int kend = min(KT, kbeg + p.sps);
+  const int NKT = kend - kbeg;                       // 1 .. S16_STEPS (checked by the launcher)
+
+  const __amdgpu_buffer_rsrc_t ract = rsrc(p.act, p.M * p.C * 2);
+  const int64_t crow = p.K / 2;                     // 4-bit codes
+  const __amdgpu_buffer_rsrc_t rcode = rsrc(p.codes + o0 * crow, (p.N - o0) * crow);
+  const int64_t srow = scales_per_row<FMT>(p.K);
+  const int64_t ssz = scale_bytes<FMT>();
+  const __amdgpu_buffer_rsrc_t rscale =
+      rsrc((const char*)p.scales + scale_offset<FMT>() + o0 * srow * ssz, (p.N - o0) * srow * ssz);
+  const __amdgpu_buffer_rsrc_t rdown = rsrc(p.down, (int64_t)R * p.C * 2);
+  float tscale = 0.0f;
+  if constexpr (tensor_scale<FMT>()) tscale = reinterpret_cast<const float*>(p.scales)[0];
+
+  const int q = lane >> 4;                           // this lane's group of a step
+  const bool rank_tile = ntile == 0;
+
+  // ---- activation slice: every load issued before any W load, so waiting
+  // for it leaves the W loads in flight.  Thread t loads row t / 16, pieces
+  // t % 16 + 16 s (s < S16_STEPS; pieces outside the slice read zero).
+  {
+    const int xr = tid >> 4, xp = (tid & 15) * 8;
+    uint4 xv[S16_STEPS];
+#pragma unroll
+    for (int st = 0; st < S16_STEPS; ++st) {
+      const int64_t col = (int64_t)(kbeg + st) * TK2 + xp;
+      const bool ok = st < NKT && xr < p.M && col < p.C;
+      xv[st] = bload16(ract, ok ? (uint32_t)((xr * p.C + col) * 2) : OOB);
+    }
+#pragma unroll
+    for (int st = 0; st < S16_STEPS; ++st)
+      *reinterpret_cast<uint4*>(xs + xr * XS16 + st * TK2 + xp) = xv[st];
+  }
+
+  struct Slot {
+    uint4 c[2];                                      // codes of the lane's group in W row blocks 0 and 1
+    uint32_t s[2];                                   // their scale entries
+    uint4 ad[RB];                                    // rank tile: adapter fragments of slice `wave` of the step
+  };
+  Slot ring[D];
+  auto issue = [&](Slot& sl, int kt) {
+    const bool sv = kt < kend;
+    const int64_t c0 = (int64_t)kt * TK2;
+    const bool gl = sv && c0 + 32 * q < p.C;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t wrow = 32 * wave + 16 * b + (lane & 15);   // W row, relative to the tile
+      sl.c[b] = bload16(rcode, gl ? (uint32_t)(wrow * crow + c0 / 2 + 16 * q) : OOB);
+      const int64_t idx = wrow * srow + (c0 >> 5) + q;
+      if constexpr (two_byte_scales<FMT>()) sl.s[b] = bload2(rscale, gl ? (uint32_t)(idx * 2) : OOB);
+      else if constexpr (FMT == QL_FMT_MXFP4) sl.s[b] = bload1(rscale, gl ? (uint32_t)idx : OOB);
+      else sl.s[b] = bload4(rscale, gl ? (uint32_t)((wrow * srow + ((c0 + 32 * q) >> 6)) * 4) : OOB);
+    }
+    const int64_t kk = c0 + 32 * wave + 8 * q;
+#pragma unroll
+    for (int jb = 0; jb < RB; ++jb) {
+      const int j = 16 * jb + (lane & 15);
+      const bool live = rank_tile && sv && j < R && kk < p.C;
+      sl.ad[jb] = bload16(rdown, live ? (uint32_t)((j * p.C + kk) * 2) : OOB);
+    }
+  };
+
+  f32x4 acc[2], uacc[RB];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int jb = 0; jb < RB; ++jb) uacc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // step t of the slice (absolute step kbeg + t) from its ring slot; refill
+  // the slot with step t + D when `refill`
+  auto step = [&](Slot& sl, int t, bool refill) {
+    const bool gl = kbeg + t < kend && (int64_t)(kbeg + t) * TK2 + 32 * q < p.C;
+    uint4 wb[2][4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      WGroup g;
+      g.c0 = sl.c[b];
+      g.c1 = make_uint4(0, 0, 0, 0);
+      g.sraw = sl.s[b];
+      g.ssh = 0;
+      float s0, s1;
+      group_scales<FMT>(sl.s[b], tscale, s0, s1);
+      Deq<FMT> dq;
+      dq.prepare(g, gl ? s0 : 0.0f, p.book, gl, gl ? s1 : 0.0f);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wb[b][i] = dq.piece(i);
+    }
+    const uint16_t* xrow = xs + (lane & 15) * XS16 + t * TK2;
+    if (rank_tile) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(xrow + 32 * wave + 8 * q);
+#pragma unroll
+      for (int jb = 0; jb < RB; ++jb)
+        uacc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, sl.ad[jb]), uacc[jb], 0, 0, 0);
+    }
+    if (refill) issue(sl, kbeg + t + D);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(xrow + 32 * q + 8 * s4);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wb[b][s4]), af, acc[b], 0, 0, 0);
+    }
+  };
+
+#pragma unroll
+  for (int u = 0; u < D; ++u) issue(ring[u], kbeg + u);
+  lds_barrier();                                     // the activation slice is in LDS
+
+  // whole chunks of D steps run branch-free (static slot indices), so the
+  // wait for each slot counts only the loads issued after it; the last
+  // chunk issues nothing
+  int it = 0;
+  for (; it + D < NKT; it += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) step(ring[u], it + u, true);
+  }
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+    if (it + u < NKT) step(ring[u], it + u, false);
+
+  mfma_result_guard();
+  float* pp = p.part + (int64_t)split * p.M * p.O;
+  const int64_t m = lane & 15;
+  if (m < p.M) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t col = o0 + 32 * wave + 16 * b + 4 * q;
+      if (col < p.O) *reinterpret_cast<float4*>(pp + m * p.O + col) = make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+    }
+  }
+  if (rank_tile) {
+    // waves 1-3 hand their U partials to wave 0 through LDS (the slice is no longer read)
+    f32x4* red = reinterpret_cast<f32x4*>(xs);
+    lds_barrier();
+    if (wave > 0) {
+#pragma unroll
+      for (int jb = 0; jb < RB; ++jb) red[((wave - 1) * RB + jb) * 64 + lane] = uacc[jb];
+    }
+    lds_barrier();
+    if (wave == 0) {
+      float* up = p.upart + (int64_t)split * p.M * R;
+#pragma unroll
+      for (int jb = 0; jb < RB; ++jb) {
+        f32x4 t = uacc[jb];
+#pragma unroll
+        for (int w = 0; w < 3; ++w) {
+          const f32x4 o = red[(w * RB + jb) * 64 + lane];
+          t = f32x4{t[0] + o[0], t[1] + o[1], t[2] + o[2], t[3] + o[3]};
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = 4 * q + e;
+          const int j = 16 * jb + (lane & 15);
+          if (j < R && row < p.M) up[row * R + j] = t[e];
+        }
+      }
+    }
+  }
+}
+
 // steps of 128 per split for the 16-token kernel, from the 64-step plan (never
 // more splits than the plan's, so its workspace suffices); 0 if unsuited
 inline int split16_plan(const Params& p, int splits, int& sps2) {
@@ -566,7 +758,15 @@ hipError_t launch_split16(SplitGroup& g, hipStream_t s) {
     units += a.ntiles[i] * s2;
   }
   a.unit0[g.n] = units;
-  hipLaunchKernelGGL((qsplit16_kernel<FMT, R>), dim3((unsigned)units), dim3(256), smem, s, a);
+  // the streaming kernel holds the whole activation slice in LDS: at most
+  // S16_STEPS steps per workgroup (measured 10 % faster per launch than the
+  // staged kernel, which serves longer slices)
+  bool stream = true;
+  for (int i = 0; i < g.n; ++i) stream = stream && a.p[i].sps <= S16_STEPS;
+  if (stream)
+    hipLaunchKernelGGL((qstream16_kernel<FMT, R>), dim3((unsigned)units), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((qsplit16_kernel<FMT, R>), dim3((unsigned)units), dim3(256), smem, s, a);
   return hipGetLastError();
 }
 

@@ -294,6 +294,9 @@ CASES = [
     ("q80_tiles_r8", ofmt.FMT_Q8_0, 520, 1024, 416, 8, 16.0),
     ("small_q80_m64_r32", ofmt.FMT_Q8_0, 64, 1056, 224, 32, 64.0),
     ("small_q80_m20", ofmt.FMT_Q8_0, 20, 2048, 320, 16, 32.0),
+    # 8 tokens, a contraction slice of 12 steps of 128 per workgroup: longer
+    # than the streaming kernel's LDS slice, so the staged 16-token kernel runs
+    ("small_nf4_m8_long_slice", ofmt.FMT_NF4, 8, 6144, 13312, 16, 32.0),
     # NVFP4 base (E2M1 codes, E4M3 scale per 16, fp32 tensor scale): tiles with
     # ragged edges, the split path with 64, 33 and 17 tokens
     ("nvfp4_ragged_mn", ofmt.FMT_NVFP4, 300, 320, 160, 16, 32.0),
