@@ -75,6 +75,9 @@ def parse():
     ap.add_argument("--hbm-ceiling", action="store_true",
                     help="only measure plain streaming kernels (device copy, read-only reduction) over 4 GiB "
                          "and exit: the HBM ceiling the kernels are compared with")
+    ap.add_argument("--counters-json", default=None, metavar="DIR",
+                    help="build profiles/fwd_counters.json from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs in DIR "
+                         "(fetch_<workload>_m<tokens>, write_..., fetch_copy, write_copy) and exit; needs no GPU")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device (a plain copy kernel of known size, "
                          "to calibrate HBM byte counters) and exit")
@@ -127,6 +130,95 @@ def traffic_from_profile(key):
         return None
     e = d.get("configs", {}).get(key)
     return None if e is None else e.get("hbm_bytes_per_launch")
+
+
+def fwd_launches_per_step(wl, m):
+    """Forward launches of one layer step, as layer.LayerStep issues them: one
+    per group of calls (q|k|v, o, gate|up, down; one per call when the layer's
+    projections do not form those groups), one per call for the FP8 base above
+    64 tokens."""
+    from quantized_base_lora_amd.layer import GROUPS
+    names = [p.name for p in wl.projs]
+    groups = [g for g in ([n for n in grp if n in names] for grp in GROUPS) if g]
+    if sum(len(g) for g in groups) != len(names):
+        groups = [[n] for n in names]
+    return len(names) if wl.fmt == 3 and m > 64 else len(groups)
+
+
+MAIN_FWD_KERNELS = ("qgemm_kernel", "qgemm8_kernel", "qstream16_kernel", "qsplit16_kernel", "qsplit_kernel")
+SETUP_KERNELS = ("pack4_kernel", "pack_nvfp4_kernel", "absmax_kernel", "quant_fp8_kernel", "fill_u32_kernel")
+
+
+def _kernel_base(name):
+    n = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return n.split("(")[0].split("<")[0].split("::")[-1]
+
+
+def _counter_rows(path, counter):
+    """(kernel base name, value) per dispatch of one counter in a rocprofv3 CSV."""
+    import csv
+    out = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    out.sort()
+    return [(n, v) for _, n, v in out]
+
+
+def counters_json(art):
+    """HBM bytes per forward launch of every layer config, from rocprofv3
+    counter runs of `bench.py --workload W --m M --phase fwd` (only forward
+    launches run after the bases are packed): every library kernel but the
+    packing ones is summed, FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
+    scaled by what the same counters read for a plain 1 GiB device copy, and
+    divided by the number of forward launches (dispatches of the GEMM kernel:
+    one per group of calls, one per call for the FP8 base above 64 tokens;
+    the reduction, activation-split and projection kernels belong to their
+    launch)."""
+    def path(tag):
+        return os.path.join(art, f"{tag}_counter_collection.csv")
+    copy = 1 << 30
+    fk = max(v for n, v in _counter_rows(path("fetch_copy"), "FETCH_SIZE") if "copyBuffer" in n)
+    wk = max(v for n, v in _counter_rows(path("write_copy"), "WRITE_SIZE") if "copyBuffer" in n)
+    ff, wf = copy / (fk * 1024), copy / (wk * 1024)
+    from quantized_base_lora_amd import synth
+    entries, cmds = {}, []
+    for name, m in LAYER_CONFIGS:
+        tag = f"{name}_m{m}"
+        if not os.path.exists(path(f"fetch_{tag}")):
+            continue
+        wl = synth.WORKLOADS[name]
+        per = {}
+        for cname, tagp in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+            rows = [(n, v) for n, v in _counter_rows(path(f"{tagp}_{tag}"), cname)
+                    if "ql::" in n and _kernel_base(n) not in SETUP_KERNELS]
+            launches = sum(1 for n, _ in rows if _kernel_base(n) in MAIN_FWD_KERNELS)
+            per[cname] = (sum(v for _, v in rows), launches, sorted({_kernel_base(n) for n, _ in rows}))
+        (fs, nl, kern), (ws, nl2, _) = per["FETCH_SIZE"], per["WRITE_SIZE"]
+        assert nl == nl2 and nl > 0, (tag, nl, nl2)
+        hbm = (fs * 1024 * ff + ws * 1024 * wf) / nl
+        alg = sum(fwd_kernel_bytes(wl, p, m) for p in wl.projs) / fwd_launches_per_step(wl, m)
+        entries[f"{name}@{m}"] = {"hbm_bytes_per_launch": hbm, "algorithmic_bytes_per_launch": alg,
+                                  "hbm_over_algorithmic": hbm / alg, "launches_counted": nl,
+                                  "FETCH_SIZE_KiB_per_launch": fs / nl, "WRITE_SIZE_KiB_per_launch": ws / nl,
+                                  "kernels": kern}
+        for tagp, cname in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+            cmds.append(f"rocprofv3 --pmc {cname} --output-format csv -d {art} -o {tagp}_{tag} -- python3 bench.py "
+                        f"--workload {name} --m {m} --phase fwd --steps 2 --warmup 1 --no-cpu-baseline")
+    for tagp, cname in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        cmds.append(f"rocprofv3 --pmc {cname} --output-format csv -d {art} -o {tagp}_copy -- python3 bench.py "
+                    f"--calibrate-copy 1024")
+    out = {"what": "HBM bytes per forward launch (a launch: one group of calls, with its reduction; the FP8 base "
+                   "above 64 tokens: one call with its activation split and projection)",
+           "kernel_source_sha": source_hash(), "commands": cmds,
+           "calibration": {"copy_bytes": copy, "FETCH_SIZE_KiB": fk, "WRITE_SIZE_KiB": wk,
+                           "fetch_factor": ff, "write_factor": wf},
+           "configs": entries}
+    dst = os.path.join(ROOT, "profiles", "fwd_counters.json")
+    with open(dst, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps({"written": dst, "configs": sorted(entries)}), flush=True)
 
 
 def copies_for(packed_bytes, override=0):
@@ -519,6 +611,8 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
+    if args.counters_json:
+        return counters_json(args.counters_json)
     import torch
 
     if args.calibrate_copy:
