@@ -227,7 +227,7 @@ def copies_for(packed_bytes, override=0):
 
 def roofline_kind(wl, m):
     if m <= 64:
-        return {"kernel": "qsplit16_kernel / qsplit_kernel + split_reduce_kernel (forward: split-contraction "
+        return {"kernel": "qstream16_kernel (16 tokens, 4-bit) / qsplit_kernel + split_reduce_kernel (forward: split-contraction "
                           "dequant GEMM, fixed-order reduction with the fused LoRA term)",
                 "bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     if wl.fmt == 3:
