@@ -542,12 +542,17 @@ void qsplit16_kernel(SplitArgs ga) {
 // through LDS at the end.
 constexpr int S16_STEPS = 8;
 constexpr int XS16 = S16_STEPS * TK2 + 8;          // LDS row stride of the activation slice (bf16)
+constexpr int SW16 = 80;                           // LDS row stride of the scale window (bytes, >= 64)
+// scale bytes per row and step of 128 (MXFP4: 4 one-byte entries; the others 8 bytes)
+template <int FMT> constexpr int scale_step_bytes() { return FMT == QL_FMT_MXFP4 ? 4 : 8; }
 
 template <int FMT, int R>
 __global__ __launch_bounds__(256) void qstream16_kernel(SplitArgs ga) {
   constexpr int TN = 128, D = 4;
   constexpr int RB = (R + 15) / 16;
   __shared__ __attribute__((aligned(16))) uint16_t xs[16 * XS16];
+  __shared__ __attribute__((aligned(16))) uint8_t sw[128 * SW16];   // the tile's scale window
+  constexpr int SBS = scale_step_bytes<FMT>();
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bid = (int)blockIdx.x;
@@ -590,14 +595,30 @@ __global__ __launch_bounds__(256) void qstream16_kernel(SplitArgs ga) {
       const bool ok = st < NKT && xr < p.M && col < p.C;
       xv[st] = bload16(ract, ok ? (uint32_t)((xr * p.C + col) * 2) : OOB);
     }
+    // the scale entries of the tile's 128 rows over the slice (at most 64
+    // contiguous bytes a row), loaded once in dwords (16 lanes a row, so a
+    // load covers 4 rows x 64 bytes; no load reaches past the window) and
+    // read from LDS by each step: per-step scale loads touch 16 rows with 2-8
+    // bytes each and cost 7-15 % of the launch
+    uint32_t sv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int pc = tid + 256 * i, row = pc >> 4, dw = pc & 15;
+      const bool ok = 4 * dw < SBS * NKT;
+      sv[i] = bload4(rscale, ok ? (uint32_t)(row * srow * ssz + (int64_t)kbeg * SBS + 4 * dw) : OOB);
+    }
 #pragma unroll
     for (int st = 0; st < S16_STEPS; ++st)
       *reinterpret_cast<uint4*>(xs + xr * XS16 + st * TK2 + xp) = xv[st];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int pc = tid + 256 * i;
+      *reinterpret_cast<uint32_t*>(sw + (pc >> 4) * SW16 + 4 * (pc & 15)) = sv[i];
+    }
   }
 
   struct Slot {
     uint4 c[2];                                      // codes of the lane's group in W row blocks 0 and 1
-    uint32_t s[2];                                   // their scale entries
     uint4 ad[RB];                                    // rank tile: adapter fragments of slice `wave` of the step
   };
   Slot ring[D];
@@ -609,10 +630,6 @@ __global__ __launch_bounds__(256) void qstream16_kernel(SplitArgs ga) {
     for (int b = 0; b < 2; ++b) {
       const int64_t wrow = 32 * wave + 16 * b + (lane & 15);   // W row, relative to the tile
       sl.c[b] = bload16(rcode, gl ? (uint32_t)(wrow * crow + c0 / 2 + 16 * q) : OOB);
-      const int64_t idx = wrow * srow + (c0 >> 5) + q;
-      if constexpr (two_byte_scales<FMT>()) sl.s[b] = bload2(rscale, gl ? (uint32_t)(idx * 2) : OOB);
-      else if constexpr (FMT == QL_FMT_MXFP4) sl.s[b] = bload1(rscale, gl ? (uint32_t)idx : OOB);
-      else sl.s[b] = bload4(rscale, gl ? (uint32_t)((wrow * srow + ((c0 + 32 * q) >> 6)) * 4) : OOB);
     }
     const int64_t kk = c0 + 32 * wave + 8 * q;
 #pragma unroll
@@ -636,13 +653,19 @@ __global__ __launch_bounds__(256) void qstream16_kernel(SplitArgs ga) {
     uint4 wb[2][4];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
+      // this group's scale entry from the window: group 4 t + q of the slice
+      const uint8_t* srw = sw + (32 * wave + 16 * b + (lane & 15)) * SW16;
+      uint32_t raw;
+      if constexpr (two_byte_scales<FMT>()) raw = *reinterpret_cast<const uint16_t*>(srw + 2 * (4 * t + q));
+      else if constexpr (FMT == QL_FMT_MXFP4) raw = srw[4 * t + q];
+      else raw = *reinterpret_cast<const uint32_t*>(srw + 4 * (2 * t + (q >> 1)));   // NF4: one fp32 per 64
       WGroup g;
       g.c0 = sl.c[b];
       g.c1 = make_uint4(0, 0, 0, 0);
-      g.sraw = sl.s[b];
+      g.sraw = raw;
       g.ssh = 0;
       float s0, s1;
-      group_scales<FMT>(sl.s[b], tscale, s0, s1);
+      group_scales<FMT>(raw, tscale, s0, s1);
       Deq<FMT> dq;
       dq.prepare(g, gl ? s0 : 0.0f, p.book, gl, gl ? s1 : 0.0f);
 #pragma unroll
@@ -762,7 +785,8 @@ hipError_t launch_split16(SplitGroup& g, hipStream_t s) {
   // S16_STEPS steps per workgroup (measured 10 % faster per launch than the
   // staged kernel, which serves longer slices)
   bool stream = true;
-  for (int i = 0; i < g.n; ++i) stream = stream && a.p[i].sps <= S16_STEPS;
+  for (int i = 0; i < g.n; ++i)   // the scale window's rows start 4-byte aligned
+    stream = stream && a.p[i].sps <= S16_STEPS && (a.p[i].K * scale_bytes<FMT>() / (FMT == QL_FMT_NF4 ? 64 : 32)) % 4 == 0;
   if (stream)
     hipLaunchKernelGGL((qstream16_kernel<FMT, R>), dim3((unsigned)units), dim3(256), 0, s, a);
   else

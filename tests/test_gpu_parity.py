@@ -463,13 +463,19 @@ def test_deterministic_and_base_untouched(lib, case):
 
 
 # at most 16 tokens the forward runs on 16x16x32 MFMAs over steps of 128:
-# every format, ragged K (a step with live and dead groups), ragged N, one token
+# every format, ragged K (a step with live and dead groups), ragged N, one
+# token; scale rows that do not start 4-byte aligned (Q4_0 at K = 1056, MXFP4
+# at K = 4128) take the staged kernel, the others the streaming one
 SMALL16 = [
     ("s16_nf4_k1088", ofmt.FMT_NF4, 16, 1088, 224, 16, 32.0),
     ("s16_q40_m5_k1056", ofmt.FMT_Q4_0, 5, 1056, 160, 32, 64.0),
     ("s16_fp8_m16", ofmt.FMT_FP8, 16, 768, 352, 8, 16.0),
     ("s16_mxfp4_m9_k4128", ofmt.FMT_MXFP4, 9, 4128, 96, 16, 32.0),
     ("s16_q80_m1", ofmt.FMT_Q8_0, 1, 2080, 416, 32, 64.0),
+    # the streaming kernel (scale rows 4-byte aligned) with every 4-bit format
+    ("s16_q40_m16_k1088", ofmt.FMT_Q4_0, 16, 1088, 288, 16, 32.0),
+    ("s16_mxfp4_m7_k1152", ofmt.FMT_MXFP4, 7, 1152, 224, 8, 16.0),
+    ("s16_nvfp4_m12_k1088", ofmt.FMT_NVFP4, 12, 1088, 160, 32, 64.0),
 ]
 
 
