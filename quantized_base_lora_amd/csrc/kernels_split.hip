@@ -43,9 +43,18 @@ struct SplitArgs {
   int32_t n;
 };
 
-template <int FMT, bool TRANS, int R, int MBK>
+// Scale window (SW, forward only): the tile's scale entries over the
+// workgroup's slice (at most 64 contiguous bytes a row) are loaded once into
+// LDS with coalesced dword loads, after the stages, and each step reads its
+// scale there instead of issuing a load that touches 32 rows with 1-4 bytes
+// each.
+constexpr int SWB = 80;                            // LDS row stride of the scale window (bytes)
+template <int FMT> constexpr int scale_step64_bytes() { return FMT == QL_FMT_MXFP4 ? 2 : 4; }
+
+template <int FMT, bool TRANS, int R, int MBK, bool SW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void qsplit_kernel(SplitArgs ga) {
+  static_assert(!SW || (!TRANS && FMT != QL_FMT_FP8_E4M3), "scale window: forward, scaled formats");
   constexpr int TM = 32 * MBK, TN = 128, NT = 256, D = 4;
   static_assert(D % 2 == 0, "buffer parity of a step is its position in the chunk");
   constexpr int SBT = TN + 32;
@@ -58,8 +67,10 @@ void qsplit_kernel(SplitArgs ga) {
   constexpr bool FP8 = FMT == QL_FMT_FP8_E4M3;
   constexpr bool BYTES = byte_codes<FMT>();
   constexpr bool DIRECT = !TRANS;                    // forward: W straight into operand registers
+  constexpr size_t STAGES_BYTES = 2 * (size_t)(TM * SA + split_b_elems<TRANS>() + (TRANS ? BL_ELEMS : AD_ELEMS)) * 2;
   static_assert(!DIRECT || TN == 4 * 32, "one 32-row W block per wave");
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  uint8_t* swin = reinterpret_cast<uint8_t*>(smem) + STAGES_BYTES;   // scale window (SW)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // units (column tile, split) are handed to the 8 XCDs (round robin over the
@@ -126,12 +137,13 @@ void qsplit_kernel(SplitArgs ga) {
         sl.w.c0 = bload16(rcode, gl ? base : OOB);
         sl.w.c1 = bload16(rcode, gl ? base + 16 : OOB);
         const int64_t idx = wrow * srow + (c0 >> 5) + hsel;
-        sl.w.sraw = FP8 ? 0u : bload2(rscale, gl ? (uint32_t)(idx * 2) : OOB);
+        sl.w.sraw = (FP8 || SW) ? 0u : bload2(rscale, gl ? (uint32_t)(idx * 2) : OOB);
       } else {
         sl.w.c0 = bload16(rcode, gl ? (uint32_t)(wrow * crow + c0 / 2 + 16 * hsel) : OOB);
         sl.w.c1 = make_uint4(0, 0, 0, 0);
         const int64_t idx = wrow * srow + (c0 >> 5) + hsel;   // the group's scale index (NF4: per 64, below)
-        if constexpr (FMT == QL_FMT_Q4_0 || FMT == QL_FMT_NVFP4) sl.w.sraw = bload2(rscale, gl ? (uint32_t)(idx * 2) : OOB);
+        if constexpr (SW) sl.w.sraw = 0;
+        else if constexpr (FMT == QL_FMT_Q4_0 || FMT == QL_FMT_NVFP4) sl.w.sraw = bload2(rscale, gl ? (uint32_t)(idx * 2) : OOB);
         else if constexpr (FMT == QL_FMT_MXFP4) sl.w.sraw = bload1(rscale, gl ? (uint32_t)idx : OOB);
         else sl.w.sraw = bload4(rscale, gl ? (uint32_t)((wrow * srow + (c0 >> 6)) * 4) : OOB);
       }
@@ -170,8 +182,17 @@ void qsplit_kernel(SplitArgs ga) {
   auto dequant_direct = [&](const Slot& sl, uint4* wb) {
     const int64_t c0 = (int64_t)sl.kt * TK;
     const bool gl = sl.kt < kend && c0 + 32 * hsel < p.C;
+    uint32_t raw = sl.w.sraw;
+    if constexpr (SW) {
+      // step t of the slice: groups 2 t + hsel (NF4: one entry per step)
+      const uint8_t* srw = swin + (32 * wave + (lane & 31)) * SWB;
+      const int t = sl.kt - kbeg;
+      if constexpr (two_byte_scales<FMT>()) raw = *reinterpret_cast<const uint16_t*>(srw + 2 * (2 * t + hsel));
+      else if constexpr (FMT == QL_FMT_MXFP4) raw = srw[2 * t + hsel];
+      else raw = *reinterpret_cast<const uint32_t*>(srw + 4 * t);
+    }
     float s0, s1;
-    group_scales<FMT>(sl.w.sraw, tscale, s0, s1);
+    group_scales<FMT>(raw, tscale, s0, s1);
     Deq<FMT> dq;
     dq.prepare(sl.w, gl ? s0 : 0.0f, p.book, gl, gl ? s1 : 0.0f);
 #pragma unroll
@@ -262,9 +283,27 @@ void qsplit_kernel(SplitArgs ga) {
     smem[A_EL + B_EL + i] = 0;
     smem[STAGE + A_EL + B_EL + i] = 0;
   }
+  // scale window (before the stages, so that waiting for it leaves their loads in flight)
+  uint32_t swv[SW ? 8 : 1];
+  if constexpr (SW) {
+    constexpr int SBS = scale_step64_bytes<FMT>();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int pc = tid + 256 * i, row = pc >> 4, dw = pc & 15;
+      const bool ok = 4 * dw < SBS * NKT;
+      swv[i] = bload4(rscale, ok ? (uint32_t)(row * srow * ssz + (int64_t)kbeg * SBS + 4 * dw) : OOB);
+    }
+  }
   // prologue: D stages in flight, the first stored and its slot refilled
 #pragma unroll
   for (int u = 0; u < D; ++u) issue(ring[u], kbeg + u);
+  if constexpr (SW) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int pc = tid + 256 * i;
+      *reinterpret_cast<uint32_t*>(swin + (pc >> 4) * SWB + 4 * (pc & 15)) = swv[i];
+    }
+  }
   lds_barrier();
   store(ring[0], smem, wbuf[0]);
   issue(ring[0], kbeg + D);
@@ -794,15 +833,15 @@ hipError_t launch_split16(SplitGroup& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int FMT, bool TRANS, int R, int MBK>
+template <int FMT, bool TRANS, int R, int MBK, bool SW>
 hipError_t launch_split_m(const SplitGroup& g, hipStream_t s) {
   constexpr int B_EL = split_b_elems<TRANS>();
   constexpr int D_EL = TRANS ? BL_ELEMS : AD_ELEMS;
-  constexpr size_t smem = 2 * (size_t)(32 * MBK * SA + B_EL + D_EL) * sizeof(uint16_t);
+  constexpr size_t smem = 2 * (size_t)(32 * MBK * SA + B_EL + D_EL) * sizeof(uint16_t) + (SW ? 128 * SWB : 0);
   static_assert(smem <= 80 * 1024, "two workgroups per CU");
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)qsplit_kernel<FMT, TRANS, R, MBK>,
+    hipError_t e = hipFuncSetAttribute((const void*)qsplit_kernel<FMT, TRANS, R, MBK, SW>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -817,7 +856,7 @@ hipError_t launch_split_m(const SplitGroup& g, hipStream_t s) {
     units += a.ntiles[i] * g.splits[i];
   }
   a.unit0[g.n] = units;
-  hipLaunchKernelGGL((qsplit_kernel<FMT, TRANS, R, MBK>), dim3((unsigned)units), dim3(256), smem, s, a);
+  hipLaunchKernelGGL((qsplit_kernel<FMT, TRANS, R, MBK, SW>), dim3((unsigned)units), dim3(256), smem, s, a);
   return hipGetLastError();
 }
 
@@ -834,7 +873,16 @@ hipError_t launch_split(SplitGroup& g, hipStream_t s) {
     }
     if (fits) return launch_split16<FMT, R>(g, s);
   }
-  return g.p[0].M <= 32 ? launch_split_m<FMT, TRANS, R, 1>(g, s) : launch_split_m<FMT, TRANS, R, 2>(g, s);
+  if constexpr (!TRANS && FMT != QL_FMT_FP8_E4M3) {
+    // the scale window holds at most 64 bytes a row, and its rows must start 4-byte aligned
+    bool sw = true;
+    for (int i = 0; i < g.n; ++i)
+      sw = sw && scale_step64_bytes<FMT>() * g.p[i].sps <= 64 &&
+           (g.p[i].K * scale_bytes<FMT>() / (FMT == QL_FMT_NF4 ? 64 : 32)) % 4 == 0;
+    if (sw)
+      return g.p[0].M <= 32 ? launch_split_m<FMT, TRANS, R, 1, true>(g, s) : launch_split_m<FMT, TRANS, R, 2, true>(g, s);
+  }
+  return g.p[0].M <= 32 ? launch_split_m<FMT, TRANS, R, 1, false>(g, s) : launch_split_m<FMT, TRANS, R, 2, false>(g, s);
 }
 
 // Split-contraction reduction and epilogue: per output element the partials
