@@ -202,8 +202,8 @@ struct Params {
 
 // ---- the small-M split path (kernels_split.hip)
 // At most SMALL_M tokens: 64-row tiles, STN columns wide, the contraction split
-// across workgroups so that up to 512 of them (two per CU, one round) stream
-// W with at least 4 steps each, then a fixed-order reduction kernel.
+// across workgroups so that up to 256 of them (512 for the 16-token forward)
+// stream W with at least 4 steps each, then a fixed-order reduction kernel.
 constexpr int64_t SMALL_M = 64;
 constexpr int STN = 128;
 constexpr int MAX_SPLITS = 16;
