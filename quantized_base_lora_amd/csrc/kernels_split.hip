@@ -210,9 +210,12 @@ void qsplit_kernel(SplitArgs ga) {
     group_scales<FMT>(sl.w.sraw >> sl.w.ssh, tscale, s0, s1);
     Deq<FMT> dq;
     dq.prepare(sl.w, wg_in ? s0 : 0.0f, p.book, wg_in, wg_in ? s1 : 0.0f);
+    // dX W tile: 16-byte piece i of group wg stored at piece i ^ (wg & 3), so a
+    // wave's stores (16 rows x 4 groups, rows 320 B apart) spread over all
+    // banks instead of four-way conflicts (measured 56 % of LDS-active cycles)
     uint16_t* dst = st + A_EL + (TRANS ? wr * SBT : wr * SA) + wg * 32;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(dst + 8 * i) = dq.piece(i);
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(dst + 8 * (i ^ (wg & 3))) = dq.piece(i);
   };
   // every slot starts defined (the prologue may leave some unused)
 #pragma unroll
@@ -253,7 +256,8 @@ void qsplit_kernel(SplitArgs ga) {
         const int b = lane >> 4, sl = lane & 15;
         const int col = 32 * wave + 16 * (b & 1) + 4 * (sl & 3);
         const int row = ks * 16 + 8 * (b >> 1) + (sl >> 2);
-        bf = tr16x8(Bs + row * SBT + col, Bs + (row + 4) * SBT + col);
+        const int pcol = col ^ (((col >> 5) & 3) << 3);   // the stores' piece swizzle (bits 3-4 of col)
+        bf = tr16x8(Bs + row * SBT + pcol, Bs + (row + 4) * SBT + pcol);
       }
 #pragma unroll
       for (int i = 0; i < MBK; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af[i], acc[i], 0, 0, 0);
