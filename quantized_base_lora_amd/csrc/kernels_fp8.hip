@@ -78,8 +78,14 @@ void qgemm8_kernel(P8 p) {
   const int tiles = nt * mt;
   int t = blockIdx.x;
   if ((tiles & 7) == 0) t = (t & 7) * (tiles >> 3) + (t >> 3);
-  const int64_t o0 = (int64_t)(t % nt) * TN;
-  const int64_t m0 = (int64_t)(t / nt) * TM;
+  // tiles in groups of GM row blocks, column by column within a group, so the
+  // workgroups an XCD runs at once share W panels as well as activation panels
+  constexpr int GM = 2;
+  const int grp = t / (GM * nt), fm = grp * GM;
+  const int gm = mt - fm < GM ? mt - fm : GM;
+  const int tg = t - grp * GM * nt;
+  const int64_t o0 = (int64_t)(tg / gm) * TN;
+  const int64_t m0 = (int64_t)(fm + tg % gm) * TM;
   const int KT = (int)((p.C + TK - 1) / TK);
 
   const __amdgpu_buffer_rsrc_t rhi = rsrc(p.hi + m0 * p.C, (p.M - m0) * p.C);
@@ -189,6 +195,7 @@ void qgemm8_kernel(P8 p) {
   for (int kt = 0; kt + 1 < KT; ++kt) {
     store(sm8 + ((kt + 1) & 1) * S::STAGE);
     load(kt + 2 < KT ? kt + 2 : KT - 1);
+    __builtin_amdgcn_sched_barrier(0);
     compute(sm8 + (kt & 1) * S::STAGE);
     lds_barrier();
   }
