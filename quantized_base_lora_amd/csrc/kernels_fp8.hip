@@ -37,7 +37,7 @@ template <int TN, bool TRANS> struct Shape8 {
   static constexpr int WAVES_M = 8 / WAVES_N;
   static constexpr int WM = TM / WAVES_M, WN = TN / WAVES_N;
   static constexpr int MB = WM / 32, NB = WN / 32;
-  static constexpr int SBT = TN + 16;              // dX W tile [TK][TN]: row stride in bytes
+  static constexpr int SBT = TN + 32;              // dX W tile [TK][TN]: row stride in bytes (transposing reads conflict-free)
   static constexpr int A_BYTES = TM * SB;          // one activation plane
   static constexpr int W_BYTES = TRANS ? TK * SBT : TN * SB;
   static constexpr int STAGE = 2 * A_BYTES + W_BYTES;
