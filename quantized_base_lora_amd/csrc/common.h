@@ -94,10 +94,12 @@ struct GemmCall {
   const GradFuse* grads;   // dX only, with split_path_fuses_grads(m): also write dA, dB (else null)
 };
 hipError_t launch_qgemm(const GemmCall& c, hipStream_t s);
-// independent calls of one format, direction, token count and rank on the
-// small-M split path: one split launch and one reduction launch for all of
-// them (bitwise the results of separate calls); other call sets are launched
-// one by one
+// independent calls of one format, direction, token count and rank: on the
+// small-M split path one split launch and one reduction launch for all of
+// them, on the bf16 tile path one launch, for the FP8 base above SMALL_M one
+// fp8 GEMM launch (with one activation split per distinct activation); all
+// bitwise the results of separate calls.  Other call sets are launched one
+// by one
 bool qgemm_groupable(const GemmCall* calls, int n);
 hipError_t launch_qgemm_group(const GemmCall* calls, int n, hipStream_t s);
 // scratch the GEMM needs: split-contraction partials when m is small; for the
@@ -119,7 +121,8 @@ struct Gemm8Call {
   float s;
   uint16_t* out;           // [M, O] bf16
 };
-hipError_t launch_qgemm8(const Gemm8Call& c, hipStream_t s);
+// one launch for n (1 .. QL_GROUP_MAX) independent calls of one direction and rank
+hipError_t launch_qgemm8(const Gemm8Call* c, int n, hipStream_t s);
 // out [m, r] fp32 = act [m, c] . D, D = A^T (a_layout, A [r, c]) or B ([c, r])
 hipError_t launch_rproj(const uint16_t* act, int64_t m, int64_t c, const uint16_t* d, bool a_layout, int32_t r,
                         float* out, hipStream_t s);

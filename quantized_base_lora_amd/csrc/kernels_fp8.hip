@@ -20,6 +20,8 @@
 // took the forward GEMM from 62 % to 80 % MFMA busy; at that load the chip's
 // power limit lowers the clock (≈ 1.95 -> 1.65 GHz in the counter runs), so
 // wall time fell by less than the cycles.
+#include <algorithm>
+
 #include "common.h"
 #include "device.h"
 
@@ -69,20 +71,35 @@ __device__ __forceinline__ v2i tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)p);
 }
 
+// problems of one launch: workgroups [tile0[g], tile0[g + 1]) own the tiles
+// of problem g (tile0[n] = grid size)
+struct Args8 {
+  P8 p[QL_GROUP_MAX];
+  int32_t tile0[QL_GROUP_MAX + 1];
+  int32_t n;
+};
+
 template <bool TRANS, int R, int TN>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void qgemm8_kernel(P8 p) {
+void qgemm8_kernel(Args8 ga) {
   using S = Shape8<TN, TRANS>;
   extern __shared__ __attribute__((aligned(16))) uint8_t sm8[];
   constexpr int MB = S::MB, NB = S::NB, WCH = S::WCH;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / S::WAVES_N, wn = wave % S::WAVES_N;
 
+  // problem and tile: each problem's tiles in contiguous runs per XCD
+  // (workgroups go round-robin over the 8 XCDs; a run of a multiple of 8
+  // workgroups starting at a multiple of 8 keeps that order)
+  const int bid = (int)blockIdx.x;
+  int pi = 0;
+  while (pi + 1 < ga.n && bid >= ga.tile0[pi + 1]) ++pi;
+  const P8& p = ga.p[pi];
+  const int t0 = ga.tile0[pi], tiles = ga.tile0[pi + 1] - t0;
   const int nt = (int)((p.O + TN - 1) / TN);
-  const int mt = (int)((p.M + TM - 1) / TM);
-  const int tiles = nt * mt;
-  int t = blockIdx.x;
-  if ((tiles & 7) == 0) t = (t & 7) * (tiles >> 3) + (t >> 3);
+  const int mt = tiles / nt;
+  int t = bid - t0;
+  if ((tiles & 7) == 0 && (t0 & 7) == 0) t = (t & 7) * (tiles >> 3) + (t >> 3);
   // tiles in groups of GM row blocks, column by column within a group, so the
   // workgroups an XCD runs at once share W panels as well as activation panels
   constexpr int GM = 2;
@@ -126,26 +143,34 @@ void qgemm8_kernel(P8 p) {
     wrow[i] = TRANS ? q / S::CPR : q >> 2;
     wcol[i] = TRANS ? (q % S::CPR) * 16 : (q & 3) * 16;
   }
+  // per-thread load offsets and limits, formed once: the loop then reads no
+  // field of the problem table (a field reloaded from it in the loop waits for
+  // this wave's LDS traffic as well, the two sharing one counter)
+  const int32_t C32 = (int32_t)p.C, K32 = (int32_t)p.K;
+  uint32_t aoff[4];
+  int32_t alim[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    aoff[i] = (uint32_t)(arow[i] * C32 + acol[i]);
+    alim[i] = C32 - acol[i];                     // column c0 + acol < C
+  }
+  uint32_t woff[WH];
+  int32_t wlim[WH];
+#pragma unroll
+  for (int i = 0; i < WH; ++i) {
+    woff[i] = (uint32_t)(wrow[i] * K32 + wcol[i]);
+    // forward: column c0 + wcol < K; dX: the piece's columns o0 + wcol lie inside K (all steps)
+    wlim[i] = TRANS ? (o0 + wcol[i] < p.K ? 0x7FFFFFFF : 0) : K32 - wcol[i];
+  }
+  uint32_t kstep = TRANS ? (uint32_t)(TK * K32) : (uint32_t)TK;   // W offset advance per step
+  asm volatile("" : "+s"(kstep));
   auto load = [&](int kt, uint4 (&da)[4], uint4 (&dw)[WH]) {
-    const int64_t c0 = (int64_t)kt * TK;
+    const int32_t c0 = kt * TK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = c0 + acol[i] < p.C;
-      da[i] = bload16(rpl, ok ? (uint32_t)(arow[i] * p.C + c0 + acol[i]) : OOB);
-    }
+    for (int i = 0; i < 4; ++i) da[i] = bload16(rpl, c0 < alim[i] ? aoff[i] + (uint32_t)c0 : OOB);
+    // W rows past N lie outside the resource (dX: rows c0 + wrow; forward: o0 + wrow)
 #pragma unroll
-    for (int i = 0; i < WH; ++i) {
-      uint32_t off;
-      bool ok;
-      if constexpr (TRANS) {          // W rows c0 + wrow (past N: outside the resource), columns o0 + wcol
-        off = (uint32_t)((c0 + wrow[i]) * p.K + wcol[i]);
-        ok = o0 + wcol[i] < p.K;
-      } else {                        // W rows o0 + wrow (past N: outside), columns c0 + wcol
-        off = (uint32_t)(wrow[i] * p.K + c0 + wcol[i]);
-        ok = c0 + wcol[i] < p.K;
-      }
-      dw[i] = bload16(rcode, ok ? off : OOB);
-    }
+    for (int i = 0; i < WH; ++i) dw[i] = bload16(rcode, c0 < wlim[i] ? woff[i] + (uint32_t)kt * kstep : OOB);
   };
   auto store = [&](uint8_t* st, const uint4 (&da)[4], const uint4 (&dw)[WH]) {
 #pragma unroll
@@ -359,7 +384,7 @@ void qgemm8_kernel(P8 p) {
 }
 
 template <bool TRANS, int R, int TN>
-hipError_t launch8_t(const P8& p, hipStream_t s) {
+hipError_t launch8_t(Args8& a, hipStream_t s) {
   using S = Shape8<TN, TRANS>;
   constexpr size_t smem = 2 * (size_t)S::STAGE;
   static_assert(smem <= 160 * 1024, "LDS budget");
@@ -371,16 +396,23 @@ hipError_t launch8_t(const P8& p, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int64_t tiles = ((p.O + TN - 1) / TN) * ((p.M + TM - 1) / TM);
-  hipLaunchKernelGGL((qgemm8_kernel<TRANS, R, TN>), dim3((unsigned)tiles), dim3(NT), smem, s, p);
+  int32_t tiles = 0;
+  for (int i = 0; i < a.n; ++i) {
+    a.tile0[i] = tiles;
+    tiles += (int32_t)(((a.p[i].O + TN - 1) / TN) * ((a.p[i].M + TM - 1) / TM));
+  }
+  a.tile0[a.n] = tiles;
+  hipLaunchKernelGGL((qgemm8_kernel<TRANS, R, TN>), dim3((unsigned)tiles), dim3(NT), smem, s, a);
   return hipGetLastError();
 }
 
+// 256-wide tiles when the launch has at least one workgroup per CU of them
 template <bool TRANS, int R>
-hipError_t launch8_w(const P8& p, hipStream_t s) {
-  const int64_t tiles256 = ((p.O + 255) / 256) * ((p.M + TM - 1) / TM);
-  if (tiles256 >= 256) return launch8_t<TRANS, R, 256>(p, s);
-  return launch8_t<TRANS, R, 128>(p, s);
+hipError_t launch8_w(Args8& a, hipStream_t s) {
+  int64_t tiles256 = 0;
+  for (int i = 0; i < a.n; ++i) tiles256 += ((a.p[i].O + 255) / 256) * ((a.p[i].M + TM - 1) / TM);
+  if (tiles256 >= 256) return launch8_t<TRANS, R, 256>(a, s);
+  return launch8_t<TRANS, R, 128>(a, s);
 }
 
 // ------------------------------------------------------------------ rank-r projection
@@ -528,26 +560,38 @@ hipError_t launch_rproj(const uint16_t* act, int64_t m, int64_t c, const uint16_
   return hipGetLastError();
 }
 
-hipError_t launch_qgemm8(const Gemm8Call& c, hipStream_t s) {
-  P8 p{};
-  p.hi = c.hi;
-  p.lo = c.lo;
-  p.rs = c.rs;
-  p.codes = c.w->codes;
-  p.wscale = reinterpret_cast<const float*>(c.w->scales);
-  p.u = c.u;
-  p.up = c.up;
-  p.out = c.out;
-  p.M = c.m;
-  p.N = c.w->n_out;
-  p.K = c.w->k_in;
-  p.C = c.trans ? p.N : p.K;
-  p.O = c.trans ? p.K : p.N;
-  p.s = c.s;
-  switch (c.r) {
-    case 8: return c.trans ? launch8_w<true, 8>(p, s) : launch8_w<false, 8>(p, s);
-    case 16: return c.trans ? launch8_w<true, 16>(p, s) : launch8_w<false, 16>(p, s);
-    default: return c.trans ? launch8_w<true, 32>(p, s) : launch8_w<false, 32>(p, s);
+hipError_t launch_qgemm8(const Gemm8Call* c, int n, hipStream_t s) {
+  if (n < 1 || n > QL_GROUP_MAX) return hipErrorInvalidValue;
+  // longest contraction first (stable), so its tiles start first
+  int order[QL_GROUP_MAX];
+  for (int i = 0; i < n; ++i) order[i] = i;
+  auto clen = [&](int i) { return c[i].trans ? c[i].w->n_out : c[i].w->k_in; };
+  std::stable_sort(order, order + n, [&](int x, int y) { return clen(x) > clen(y); });
+  Args8 a{};
+  a.n = n;
+  for (int i = 0; i < n; ++i) {
+    const Gemm8Call& ci = c[order[i]];
+    if (ci.trans != c[0].trans || ci.r != c[0].r) return hipErrorInvalidValue;
+    P8& p = a.p[i];
+    p.hi = ci.hi;
+    p.lo = ci.lo;
+    p.rs = ci.rs;
+    p.codes = ci.w->codes;
+    p.wscale = reinterpret_cast<const float*>(ci.w->scales);
+    p.u = ci.u;
+    p.up = ci.up;
+    p.out = ci.out;
+    p.M = ci.m;
+    p.N = ci.w->n_out;
+    p.K = ci.w->k_in;
+    p.C = ci.trans ? p.N : p.K;
+    p.O = ci.trans ? p.K : p.N;
+    p.s = ci.s;
+  }
+  switch (c[0].r) {
+    case 8: return c[0].trans ? launch8_w<true, 8>(a, s) : launch8_w<false, 8>(a, s);
+    case 16: return c[0].trans ? launch8_w<true, 16>(a, s) : launch8_w<false, 16>(a, s);
+    default: return c[0].trans ? launch8_w<true, 32>(a, s) : launch8_w<false, 32>(a, s);
   }
 }
 

@@ -700,32 +700,59 @@ static void make_params(const GemmCall& c, Params& p, int& splits) {
   }
 }
 
-hipError_t launch_qgemm(const GemmCall& c, hipStream_t s) {
-  if (use_fp8_mfma(c.w->format, c.m)) {
-    // a1 split of the activation, the rank-r projection (U or V, written to save), fp8 GEMM
-    const int64_t N = c.w->n_out, K = c.w->k_in, C = c.trans ? N : K;
-    const Fp8Plan fp = fp8_plan(c.trans, c.m, N, K);
-    uint8_t* base = reinterpret_cast<uint8_t*>(c.ws);
-    uint8_t* hi = base;
-    uint8_t* lo = base + fp.lo_off;
-    float* rs = reinterpret_cast<float*>(base + fp.rs_off);
-    hipError_t e = launch_act_quant(c.act, c.m, C, hi, lo, rs, s);
-    if (e == hipSuccess) e = launch_rproj(c.act, c.m, C, c.down, !c.trans, c.r, c.save, s);
-    if (e != hipSuccess) return e;
-    Gemm8Call g{};
-    g.w = c.w;
-    g.trans = c.trans;
-    g.hi = hi;
-    g.lo = lo;
-    g.rs = rs;
-    g.m = c.m;
-    g.u = c.save;
-    g.up = c.up;
-    g.r = c.r;
-    g.s = c.s;
-    g.out = c.out;
-    return launch_qgemm8(g, s);
+// FP8 base above SMALL_M: per call the a1 split of the activation (done once
+// for calls that share their activation), the rank-r projection (U or V,
+// written to save), then one fp8 GEMM launch for all the calls
+static bool fp8_group(const GemmCall* calls, int n) {
+  if (n < 1 || n > MAX_GROUP) return false;
+  for (int i = 0; i < n; ++i) {
+    const GemmCall& c = calls[i];
+    if (!use_fp8_mfma(c.w->format, c.m) || c.grads || c.trans != calls[0].trans || c.m != calls[0].m ||
+        c.r != calls[0].r)
+      return false;
   }
+  return true;
+}
+
+static hipError_t launch_fp8_calls(const GemmCall* calls, int n, hipStream_t s) {
+  Gemm8Call g[MAX_GROUP];
+  for (int i = 0; i < n; ++i) {
+    const GemmCall& c = calls[i];
+    const int64_t N = c.w->n_out, K = c.w->k_in, C = c.trans ? N : K;
+    int j = 0;
+    while (j < i && !(calls[j].act == c.act && (calls[j].trans ? calls[j].w->n_out : calls[j].w->k_in) == C)) ++j;
+    if (j < i) {                                     // same activation: its split is already there
+      g[i].hi = g[j].hi;
+      g[i].lo = g[j].lo;
+      g[i].rs = g[j].rs;
+    } else {
+      const Fp8Plan fp = fp8_plan(c.trans, c.m, N, K);
+      uint8_t* base = reinterpret_cast<uint8_t*>(c.ws);
+      uint8_t* hi = base;
+      uint8_t* lo = base + fp.lo_off;
+      float* rs = reinterpret_cast<float*>(base + fp.rs_off);
+      hipError_t e = launch_act_quant(c.act, c.m, C, hi, lo, rs, s);
+      if (e != hipSuccess) return e;
+      g[i].hi = hi;
+      g[i].lo = lo;
+      g[i].rs = rs;
+    }
+    hipError_t e = launch_rproj(c.act, c.m, C, c.down, !c.trans, c.r, c.save, s);
+    if (e != hipSuccess) return e;
+    g[i].w = c.w;
+    g[i].trans = c.trans;
+    g[i].m = c.m;
+    g[i].u = c.save;
+    g[i].up = c.up;
+    g[i].r = c.r;
+    g[i].s = c.s;
+    g[i].out = c.out;
+  }
+  return launch_qgemm8(g, n, s);
+}
+
+hipError_t launch_qgemm(const GemmCall& c, hipStream_t s) {
+  if (use_fp8_mfma(c.w->format, c.m)) return launch_fp8_calls(&c, 1, s);
   Params p;
   int splits = 0;
   make_params(c, p, splits);
@@ -746,7 +773,7 @@ hipError_t launch_qgemm(const GemmCall& c, hipStream_t s) {
 
 // one launch (pair) for the group: one format, direction, token count and
 // rank, and one path for all (the small-M split path, or the bf16 tile kernel;
-// the FP8 base's fp8 path above SMALL_M runs call by call)
+// the FP8 base's fp8 path above SMALL_M is grouped by launch_fp8_calls)
 bool qgemm_groupable(const GemmCall* calls, int n) {
   if (n < 2 || n > MAX_GROUP) return false;
   const GemmCall& c0 = calls[0];
@@ -763,6 +790,7 @@ bool qgemm_groupable(const GemmCall* calls, int n) {
 }
 
 hipError_t launch_qgemm_group(const GemmCall* calls, int n, hipStream_t s) {
+  if (n > 1 && fp8_group(calls, n)) return launch_fp8_calls(calls, n, s);
   if (!qgemm_groupable(calls, n)) {
     for (int i = 0; i < n; ++i) {
       hipError_t e = launch_qgemm(calls[i], s);

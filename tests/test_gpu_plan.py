@@ -72,7 +72,7 @@ GROUPS = [
     # group): ragged row and column tiles, contractions of different lengths in both
     # directions (the table is reordered, longest first), a q|k|v-shaped group whose
     # tile counts are multiples of 8 (per-problem XCD remap), and the FP8 base above
-    # 64 tokens (call by call)
+    # 64 tokens (one fp8 GEMM launch, reordered longest contraction first)
     (ofmt.FMT_NF4, 16, 16, [(512, 384), (512, 128), (512, 128)]),
     (ofmt.FMT_MXFP4, 64, 8, [(1024, 256), (256, 1024)]),
     (ofmt.FMT_Q4_0, 33, 32, [(96, 224), (1056, 64), (256, 96)]),
@@ -83,6 +83,7 @@ GROUPS = [
     (ofmt.FMT_Q4_0, 129, 16, [(64, 64), (320, 1088), (64, 256), (128, 32)]),
     (ofmt.FMT_NF4, 2048, 16, [(1024, 2048), (1024, 1024), (1024, 1024)]),
     (ofmt.FMT_FP8, 96, 16, [(256, 160), (512, 96)]),
+    (ofmt.FMT_FP8, 600, 32, [(256, 512), (512, 256), (768, 128)]),
 ]
 
 
@@ -130,6 +131,43 @@ def test_group_matches_single_calls(lib, grp):
         pl.run()
         check(f"plan run {run}")
     pl.close()
+
+
+@pytest.mark.parametrize("m", [300, 1030])
+def test_fp8_group_shared_activation(lib, m):
+    """q|k|v-shaped FP8 group above 64 tokens whose calls share one input x (its
+    two-term split is made once for the group): y, U, dX, dA and dB bitwise those
+    of single calls."""
+    from quantized_base_lora_amd import binding as B
+    fmt, r, alpha, k = ofmt.FMT_FP8, 16, 32.0, 512
+    ns = [512, 128, 128]
+    print(f"fp8 shared-activation group m={m}", flush=True)
+    x = H.bits_to_bf16_tensor(H.make_case(m, k, 32, r, seed=120)["x"])
+    items = []
+    for i, n in enumerate(ns):
+        c = H.make_case(m, k, n, r, seed=121 + i)
+        qw = B.quant_pack(fmt, torch.from_numpy(c["W"]).cuda())
+        t = {key: H.bits_to_bf16_tensor(c[key]) for key in ("dY", "A", "B")}
+        items.append((qw, t, n))
+    ref, fi, bi = [], [], []
+    for qw, t, n in items:
+        y, u = B.linear_fwd(qw, x, t["A"], t["B"], alpha)
+        dx, da, db = B.linear_bwd(qw, x, t["dY"], u, t["A"], t["B"], alpha)
+        ref.append(dict(y=y, u=u, dx=dx, da=da, db=db))
+        o = {key: torch.empty_like(v) for key, v in ref[-1].items()}
+        wsf = torch.empty(max(256, B.workspace_bytes(B.OP_FWD, fmt, n, k, m, r)), dtype=torch.uint8, device="cuda")
+        wsb = torch.empty(max(256, B.workspace_bytes(B.OP_BWD, fmt, n, k, m, r)), dtype=torch.uint8, device="cuda")
+        fi.append((qw, x, t["A"], t["B"], alpha, o["y"], o["u"], wsf))
+        bi.append((qw, x, t["dY"], o["u"], t["A"], t["B"], alpha, o["dx"], o["da"], o["db"], wsb, False))
+    torch.cuda.synchronize()
+    B.linear_fwd_group(fi)
+    B.linear_bwd_group(bi)
+    torch.cuda.synchronize()
+    for j, rf in enumerate(ref):
+        got = {"y": fi[j][5], "u": fi[j][6], "dx": bi[j][7], "da": bi[j][8], "db": bi[j][9]}
+        for key, v in rf.items():
+            iv = torch.int16 if v.dtype == torch.bfloat16 else torch.int32
+            assert torch.equal(got[key].view(iv), v.view(iv)), (m, j, key)
 
 
 def test_group_edge_cases(lib):
