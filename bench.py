@@ -133,16 +133,15 @@ def traffic_from_profile(key):
 
 
 def fwd_launches_per_step(wl, m):
-    """Forward launches of one layer step, as layer.LayerStep issues them: one
-    per group of calls (q|k|v, o, gate|up, down; one per call when the layer's
-    projections do not form those groups), one per call for the FP8 base above
-    64 tokens."""
+    """Forward GEMM launches of one layer step, as layer.LayerStep issues
+    them: one per group of calls (q|k|v, o, gate|up, down; one per call when
+    the layer's projections do not form those groups)."""
     from quantized_base_lora_amd.layer import GROUPS
     names = [p.name for p in wl.projs]
     groups = [g for g in ([n for n in grp if n in names] for grp in GROUPS) if g]
     if sum(len(g) for g in groups) != len(names):
         groups = [[n] for n in names]
-    return len(names) if wl.fmt == 3 and m > 64 else len(groups)
+    return len(groups)
 
 
 MAIN_FWD_KERNELS = ("qgemm_kernel", "qgemm8_kernel", "qstream16_kernel", "qsplit16_kernel", "qsplit_kernel")
@@ -172,10 +171,9 @@ def counters_json(art):
     launches run after the bases are packed): every library kernel but the
     packing ones is summed, FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
     scaled by what the same counters read for a plain 1 GiB device copy, and
-    divided by the number of forward launches (dispatches of the GEMM kernel:
-    one per group of calls, one per call for the FP8 base above 64 tokens;
-    the reduction, activation-split and projection kernels belong to their
-    launch)."""
+    divided by the number of forward launches (dispatches of the GEMM kernel,
+    one per group of calls; the reduction, activation-split and projection
+    kernels belong to their launch)."""
     def path(tag):
         return os.path.join(art, f"{tag}_counter_collection.csv")
     copy = 1 << 30
@@ -209,8 +207,8 @@ def counters_json(art):
     for tagp, cname in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
         cmds.append(f"rocprofv3 --pmc {cname} --output-format csv -d {art} -o {tagp}_copy -- python3 bench.py "
                     f"--calibrate-copy 1024")
-    out = {"what": "HBM bytes per forward launch (a launch: one group of calls, with its reduction; the FP8 base "
-                   "above 64 tokens: one call with its activation split and projection)",
+    out = {"what": "HBM bytes per forward launch (a launch: one group of calls, with its reduction, or for the FP8 "
+                   "base above 64 tokens with its activation splits and projections)",
            "kernel_source_sha": source_hash(), "commands": cmds,
            "calibration": {"copy_bytes": copy, "FETCH_SIZE_KiB": fk, "WRITE_SIZE_KiB": wk,
                            "fetch_factor": ff, "write_factor": wf},

@@ -108,10 +108,9 @@ class LayerStep:
         self.plans()[i % self.copies].run(stream)
 
     def fwd_launches_per_step(self):
-        """Launches (or launch pairs) of one step's forward: one per group,
-        except the FP8 base above 64 tokens, whose calls run one by one."""
-        if self.wl.fmt == B.FMT_FP8 and self.m > 64:
-            return len(self.projs)
+        """GEMM launches of one step's forward: one per group of calls (with
+        its reduction launch on the small-M path, or for the FP8 base above 64
+        tokens after the group's activation splits and projections)."""
         return len(self.groups)
 
     def close(self):
