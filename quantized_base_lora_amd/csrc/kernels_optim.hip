@@ -97,15 +97,28 @@ struct Adamw8KernelArgs {
   float decay, b1, omb1, b2, omb2, step_size, inv_bc2_sqrt, eps, gs;
 };
 
-// number of thresholds of `t` strictly below x (binary search; NaN -> 0)
-__device__ __forceinline__ uint32_t dyn8_rank(const Dyn8Table& t, float x) {
-  int lo = 0, hi = t.count - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (t.thresh[mid] < x) lo = mid + 1;
-    else hi = mid;
-  }
-  return (uint32_t)lo;
+// number of the ascending thresholds thr[0 .. 2^bits - 2] strictly below x
+// (0 and NaN -> 0): an estimate from the level formula (decade z from log10,
+// then the nearest of the decade's 2^f levels), moved down while the
+// threshold below it is not below x and up while the one above it is, so
+// the result is the rank by definition whatever the estimate (usually one
+// or two comparisons instead of a binary search's eight dependent lookups)
+__device__ __forceinline__ uint32_t dyn8_rank(const float* thr, int bits, float x) {
+  if (!(x > 0.0f)) return 0u;
+  const int last = (1 << bits) - 1;
+  int z = (int)(-__log10f(x));
+  z = z < 0 ? 0 : (z > bits - 1 ? bits - 1 : z);
+  const int f = bits - 1 - z;
+  float y = x;
+#pragma unroll
+  for (int i = 0; i < 7; ++i)
+    if (i < z) y *= 10.0f;
+  int q = (int)rintf((y - 0.1f) * ((float)(1 << f) / 0.9f)) - 1;
+  q = q < 0 ? 0 : (q > (1 << f) - 1 ? (1 << f) - 1 : q);
+  int c = (1 << f) + q;
+  while (c > 0 && !(thr[c - 1] < x)) --c;
+  while (c < last && thr[c] < x) ++c;
+  return (uint32_t)c;
 }
 
 __device__ __forceinline__ float block_max(float v, float* red) {
@@ -122,6 +135,17 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 
 __global__ __launch_bounds__(kThreads8) void adamw8_kernel(Adamw8KernelArgs a) {
   __shared__ float red_m[kThreads8 / 64], red_v[kThreads8 / 64];
+  // the level and threshold tables in LDS (lane-divergent lookups)
+  __shared__ float lvl_s[128], lvl_u[256], thr_s[127], thr_u[255];
+  static_assert(kThreads8 == 256, "one table entry per thread");
+  {
+    const int t = threadIdx.x;
+    lvl_u[t] = kDynU.level[t];
+    if (t < 255) thr_u[t] = kDynU.thresh[t];
+    if (t < 128) lvl_s[t] = kDynS.level[t];
+    if (t < 127) thr_s[t] = kDynS.thresh[t];
+  }
+  __syncthreads();
   const int64_t b = blockIdx.x;
   int ti = 0;
   while (ti + 1 < a.nt && b >= a.blk0[ti + 1]) ++ti;   // uniform over the block
@@ -147,9 +171,9 @@ __global__ __launch_bounds__(kThreads8) void adamw8_kernel(Adamw8KernelArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t cm = (mc[i >> 2] >> (8 * (i & 3))) & 0xFF, cv = (vc[i >> 2] >> (8 * (i & 3))) & 0xFF;
-    const float mag = mul_rn(kDynS.level[cm & 0x7F], am);
+    const float mag = mul_rn(lvl_s[cm & 0x7F], am);
     const float mo = (cm & 0x80) ? -mag : mag;
-    const float vo = mul_rn(kDynU.level[cv], av);
+    const float vo = mul_rn(lvl_u[cv], av);
     const float gi = mul_rn(g[i], a.gs);
     const float th = mul_rn(p[i], a.decay);
     m[i] = add_rn(mul_rn(a.b1, mo), mul_rn(a.omb1, gi));
@@ -171,10 +195,10 @@ __global__ __launch_bounds__(kThreads8) void adamw8_kernel(Adamw8KernelArgs a) {
     uint32_t km = 0, kv = 0;
     if (am2 > 0.0f) {
       const float r = __fdiv_rn(m[i], am2);
-      km = dyn8_rank(kDynS, fabsf(r));
+      km = dyn8_rank(thr_s, 7, fabsf(r));
       if (r < 0.0f && km > 0) km |= 0x80;
     }
-    if (av2 > 0.0f) kv = dyn8_rank(kDynU, fabsf(__fdiv_rn(v[i], av2)));
+    if (av2 > 0.0f) kv = dyn8_rank(thr_u, 8, fabsf(__fdiv_rn(v[i], av2)));
     om[i >> 2] |= km << (8 * (i & 3));
     ov[i >> 2] |= kv << (8 * (i & 3));
   }
