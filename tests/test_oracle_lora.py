@@ -198,3 +198,30 @@ def test_act_split_exact_on_e4m3_grid():
     hi, lo, s = lora.act_split_e4m3(x)
     assert s[0] == 1.0
     assert np.array_equal(codecs.e4m3_decode(hi)[0], x[0]) and not np.any(lo & 0x7F)
+
+
+def test_act_split_second_term_is_needed():
+    """Why the FP8 base's GEMM runs two fp8 products per output: with the high
+    term alone (one E4M3 rounding of the activation) the forward against the
+    FP8 weight reaches the 3e-2 bound at the headline widths (this seeded case,
+    64 tokens, K = 4096, N = 256: 3.3e-2; other seeds and widths 2.5e-2 to
+    3.0e-2), while the two-term split reproduces bf16 activations exactly
+    over a row's upper range (the residual of rounding an 8-bit significand
+    to 4 bits is a multiple of the input's ulp of at most 4 significant
+    bits), so its product is the dequantized reference up to fp64 rounding."""
+    from oracle import formats as ofmt
+    g = np.random.default_rng(23)
+    x = codecs.bf16_round(g.standard_normal((64, 4096)).astype(np.float32))
+    w = (g.standard_normal((256, 4096)) * 0.02).astype(np.float32)
+    codes, scales = ofmt.pack(ofmt.FMT_FP8, w)
+    wd = ofmt.dequant(ofmt.FMT_FP8, codes, scales).astype(np.float64)
+    ref = x.astype(np.float64) @ wd.T
+    hi, lo, s = lora.act_split_e4m3(x)
+    one = lora.act_join_e4m3(hi, np.zeros_like(lo), s) @ wd.T
+    two = lora.act_join_e4m3(hi, lo, s) @ wd.T
+    assert lora.rel_err(one, ref) > 1.5e-2
+    assert lora.rel_err(two, ref) < 1e-6
+    # exact over the upper range: elements within 2^-5 of the row maximum
+    xr = lora.act_join_e4m3(hi, lo, s)
+    big = np.abs(x) >= np.max(np.abs(x), axis=1, keepdims=True) * 2.0 ** -5
+    assert np.array_equal(xr[big], x.astype(np.float64)[big])
