@@ -43,7 +43,6 @@ template <int TN, bool TRANS> struct Shape8 {
   static constexpr int A_BYTES = TM * SB;          // one activation plane
   static constexpr int W_BYTES = TRANS ? TK * SBT : TN * SB;
   static constexpr int STAGE = 2 * A_BYTES + W_BYTES;
-  static constexpr int WCH = TN * TK / 16 / NT;    // 16-byte W pieces per thread: 2 or 1
   static constexpr int CPR = TN / 16;              // dX: pieces per W-tile row
 };
 
@@ -84,7 +83,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void qgemm8_kernel(Args8 ga) {
   using S = Shape8<TN, TRANS>;
   extern __shared__ __attribute__((aligned(16))) uint8_t sm8[];
-  constexpr int MB = S::MB, NB = S::NB, WCH = S::WCH;
+  constexpr int MB = S::MB, NB = S::NB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / S::WAVES_N, wn = wave % S::WAVES_N;
 
