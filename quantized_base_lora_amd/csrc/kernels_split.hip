@@ -90,6 +90,10 @@ void qsplit_kernel(SplitArgs ga) {
   const int kbeg = split * p.sps;
   const int kend = min(KT, kbeg + p.sps);
   const int NKT = kend - kbeg;
+  // scale window: the slice's first scale byte in its row, and its offset in
+  // the dword that holds it (MXFP4, two bytes a step: 0 or 2)
+  const int64_t sb0 = (int64_t)kbeg * scale_step64_bytes<FMT>();
+  const int sdel = (int)(sb0 & 3);
 
   const __amdgpu_buffer_rsrc_t ract = rsrc(p.act, p.M * p.C * 2);
   const int64_t crow = BYTES ? p.K : p.K / 2;
@@ -184,8 +188,9 @@ void qsplit_kernel(SplitArgs ga) {
     const bool gl = sl.kt < kend && c0 + 32 * hsel < p.C;
     uint32_t raw = sl.w.sraw;
     if constexpr (SW) {
-      // step t of the slice: groups 2 t + hsel (NF4: one entry per step)
-      const uint8_t* srw = swin + (32 * wave + (lane & 31)) * SWB;
+      // step t of the slice: groups 2 t + hsel (NF4: one entry per step),
+      // sdel bytes into the window row
+      const uint8_t* srw = swin + (32 * wave + (lane & 31)) * SWB + sdel;
       const int t = sl.kt - kbeg;
       if constexpr (two_byte_scales<FMT>()) raw = *reinterpret_cast<const uint16_t*>(srw + 2 * (2 * t + hsel));
       else if constexpr (FMT == QL_FMT_MXFP4) raw = srw[2 * t + hsel];
@@ -287,15 +292,15 @@ void qsplit_kernel(SplitArgs ga) {
     smem[A_EL + B_EL + i] = 0;
     smem[STAGE + A_EL + B_EL + i] = 0;
   }
-  // scale window (before the stages, so that waiting for it leaves their loads in flight)
+  // scale window (before the stages, so that waiting for it leaves their loads in flight):
+  // each row's dwords from the one holding the slice's first scale byte
   uint32_t swv[SW ? 8 : 1];
   if constexpr (SW) {
-    constexpr int SBS = scale_step64_bytes<FMT>();
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int pc = tid + 256 * i, row = pc >> 4, dw = pc & 15;
-      const bool ok = 4 * dw < SBS * NKT;
-      swv[i] = bload4(rscale, ok ? (uint32_t)(row * srow * ssz + (int64_t)kbeg * SBS + 4 * dw) : OOB);
+      const bool ok = 4 * dw < sdel + scale_step64_bytes<FMT>() * NKT;
+      swv[i] = bload4(rscale, ok ? (uint32_t)(row * srow * ssz + sb0 - sdel + 4 * dw) : OOB);
     }
   }
   // prologue: D stages in flight, the first stored and its slot refilled
@@ -878,11 +883,15 @@ hipError_t launch_split(SplitGroup& g, hipStream_t s) {
     if (fits) return launch_split16<FMT, R>(g, s);
   }
   if constexpr (!TRANS && FMT != QL_FMT_FP8_E4M3) {
-    // the scale window holds at most 64 bytes a row, and its rows must start 4-byte aligned
+    // the scale window holds at most 64 bytes a row, read in aligned dwords
+    // from the one holding a slice's first scale byte (an MXFP4 slice of an
+    // odd number of steps starts 2 bytes into it in every other split, so 2
+    // more bytes); the rows must start 4-byte aligned
     bool sw = true;
-    for (int i = 0; i < g.n; ++i)
-      sw = sw && scale_step64_bytes<FMT>() * g.p[i].sps <= 64 &&
-           (g.p[i].K * scale_bytes<FMT>() / (FMT == QL_FMT_NF4 ? 64 : 32)) % 4 == 0;
+    for (int i = 0; i < g.n; ++i) {
+      const int sb = scale_step64_bytes<FMT>() * g.p[i].sps;
+      sw = sw && sb + (sb % 4 ? 2 : 0) <= 64 && (g.p[i].K * scale_bytes<FMT>() / (FMT == QL_FMT_NF4 ? 64 : 32)) % 4 == 0;
+    }
     if (sw)
       return g.p[0].M <= 32 ? launch_split_m<FMT, TRANS, R, 1, true>(g, s) : launch_split_m<FMT, TRANS, R, 2, true>(g, s);
   }

@@ -289,6 +289,11 @@ CASES = [
     ("small_mxfp4_m64_r8", ofmt.FMT_MXFP4, 64, 512, 384, 8, 16.0),
     ("small_mxfp4_m33", ofmt.FMT_MXFP4, 33, 1056, 224, 16, 32.0),
     ("small_mxfp4_m17_r32", ofmt.FMT_MXFP4, 17, 2048, 320, 32, 64.0),
+    # MXFP4, 4 splits of 5 steps (K = 1152): slices whose scale bytes start at
+    # odd 2-byte offsets, so the scale window is not used (it read the last
+    # W row's last scales as zero: found by the shape sweep)
+    ("small_mxfp4_m17_odd_slices", ofmt.FMT_MXFP4, 17, 1152, 160, 8, 16.0),
+    ("small_mxfp4_m40_odd_slices", ofmt.FMT_MXFP4, 40, 1152, 32, 16, 32.0),
     # Q8_0 base (int8 codes, fp16 scale per 32): tiles with ragged edges, split path
     ("q80_ragged_mnk", ofmt.FMT_Q8_0, 300, 352, 160, 16, 32.0),
     ("q80_tiles_r8", ofmt.FMT_Q8_0, 520, 1024, 416, 8, 16.0),
