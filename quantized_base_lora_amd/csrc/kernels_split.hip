@@ -803,8 +803,18 @@ inline int split16_plan(const Params& p, int splits, int& sps2) {
   return s2 <= splits ? s2 : 0;
 }
 
+// the streaming 16-token kernel holds the whole activation slice in LDS (at
+// most S16_STEPS steps per workgroup; measured 10 % faster per launch than the
+// staged kernel, which serves longer slices), and its scale window's rows
+// must start 4-byte aligned
+template <int FMT> bool stream16_ok(const Params& p, int sps2) {
+  return sps2 <= S16_STEPS && (p.K * scale_bytes<FMT>() / (FMT == QL_FMT_NF4 ? 64 : 32)) % 4 == 0;
+}
+
+// problems idx[0 .. n) of g on the streaming (stream) or the staged 16-token
+// kernel, in steps of 128; each problem's split count set to its 128-step plan
 template <int FMT, int R>
-hipError_t launch_split16(SplitGroup& g, hipStream_t s) {
+hipError_t launch_split16(SplitGroup& g, const int* idx, int n, bool stream, hipStream_t s) {
   static_assert(!byte_codes<FMT>(), "4-bit formats only");
   constexpr size_t smem = 2 * (size_t)(16 * SA2 + 32 * SA2) * sizeof(uint16_t);
   static bool attr_set = false;
@@ -815,26 +825,21 @@ hipError_t launch_split16(SplitGroup& g, hipStream_t s) {
     attr_set = true;
   }
   SplitArgs a{};
-  a.n = g.n;
+  a.n = n;
   int32_t units = 0;
-  for (int i = 0; i < g.n; ++i) {
+  for (int j = 0; j < n; ++j) {
+    const int i = idx[j];
     int sps2 = 0;
     const int s2 = split16_plan(g.p[i], g.splits[i], sps2);
     if (s2 == 0) return hipErrorInvalidValue;
-    a.p[i] = g.p[i];
-    a.p[i].sps = sps2;
+    a.p[j] = g.p[i];
+    a.p[j].sps = sps2;
     g.splits[i] = s2;                                // the reduction adds this many partials
-    a.ntiles[i] = (int32_t)((g.p[i].O + 127) / 128);
-    a.unit0[i] = units;
-    units += a.ntiles[i] * s2;
+    a.ntiles[j] = (int32_t)((g.p[i].O + 127) / 128);
+    a.unit0[j] = units;
+    units += a.ntiles[j] * s2;
   }
-  a.unit0[g.n] = units;
-  // the streaming kernel holds the whole activation slice in LDS: at most
-  // S16_STEPS steps per workgroup (measured 10 % faster per launch than the
-  // staged kernel, which serves longer slices)
-  bool stream = true;
-  for (int i = 0; i < g.n; ++i)   // the scale window's rows start 4-byte aligned
-    stream = stream && a.p[i].sps <= S16_STEPS && (a.p[i].K * scale_bytes<FMT>() / (FMT == QL_FMT_NF4 ? 64 : 32)) % 4 == 0;
+  a.unit0[n] = units;
   if (stream)
     hipLaunchKernelGGL((qstream16_kernel<FMT, R>), dim3((unsigned)units), dim3(256), 0, s, a);
   else
@@ -869,19 +874,11 @@ hipError_t launch_split_m(const SplitGroup& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-// 32-row tiles when every token fits in one 32x32 MFMA block
+// the general split kernel: 32-row tiles when every token fits in one 32x32
+// MFMA block; the scale-window variant when every problem allows it (it
+// reads the same scales, so results do not depend on the choice)
 template <int FMT, bool TRANS, int R>
-hipError_t launch_split(SplitGroup& g, hipStream_t s) {
-  // the 16-token kernel holds a ring of four steps of two groups per lane:
-  // 4-bit codes fit the registers, one-byte codes (FP8, Q8_0) would spill
-  if constexpr (!TRANS && !byte_codes<FMT>()) {
-    bool fits = g.p[0].M <= 16;
-    for (int i = 0; i < g.n && fits; ++i) {
-      int sps2;
-      fits = split16_plan(g.p[i], g.splits[i], sps2) > 0;
-    }
-    if (fits) return launch_split16<FMT, R>(g, s);
-  }
+hipError_t launch_split_general(const SplitGroup& g, hipStream_t s) {
   if constexpr (!TRANS && FMT != QL_FMT_FP8_E4M3) {
     // the scale window holds at most 64 bytes a row, read in aligned dwords
     // from the one holding a slice's first scale byte (an MXFP4 slice of an
@@ -896,6 +893,40 @@ hipError_t launch_split(SplitGroup& g, hipStream_t s) {
       return g.p[0].M <= 32 ? launch_split_m<FMT, TRANS, R, 1, true>(g, s) : launch_split_m<FMT, TRANS, R, 2, true>(g, s);
   }
   return g.p[0].M <= 32 ? launch_split_m<FMT, TRANS, R, 1, false>(g, s) : launch_split_m<FMT, TRANS, R, 2, false>(g, s);
+}
+
+template <int FMT, bool TRANS, int R>
+hipError_t launch_split(SplitGroup& g, hipStream_t s) {
+  // the 16-token kernels hold a ring of four steps of two groups per lane:
+  // 4-bit codes fit the registers, one-byte codes (FP8, Q8_0) would spill.
+  // Each problem of a group runs the kernel a call of its own would run (the
+  // streaming or the staged 16-token kernel, or the general split kernel:
+  // their summation orders differ), one launch per kernel, so the group's
+  // results stay bitwise those of single calls.
+  if constexpr (!TRANS && !byte_codes<FMT>()) {
+    if (g.p[0].M <= 16) {
+      int ist[MAX_GROUP], isg[MAX_GROUP], ipl[MAX_GROUP], nst = 0, nsg = 0, npl = 0;
+      for (int i = 0; i < g.n; ++i) {
+        int sps2 = 0;
+        const int s2 = split16_plan(g.p[i], g.splits[i], sps2);
+        if (s2 == 0) ipl[npl++] = i;
+        else if (stream16_ok<FMT>(g.p[i], sps2)) ist[nst++] = i;
+        else isg[nsg++] = i;
+      }
+      hipError_t e = hipSuccess;
+      if (nst) e = launch_split16<FMT, R>(g, ist, nst, true, s);
+      if (e == hipSuccess && nsg) e = launch_split16<FMT, R>(g, isg, nsg, false, s);
+      if (e != hipSuccess || npl == 0) return e;
+      SplitGroup gp{};
+      gp.n = npl;
+      for (int j = 0; j < npl; ++j) {
+        gp.p[j] = g.p[ipl[j]];
+        gp.splits[j] = g.splits[ipl[j]];
+      }
+      return launch_split_general<FMT, TRANS, R>(gp, s);
+    }
+  }
+  return launch_split_general<FMT, TRANS, R>(g, s);
 }
 
 // Split-contraction reduction and epilogue: per output element the partials

@@ -74,6 +74,10 @@ GROUPS = [
     # tile counts are multiples of 8 (per-problem XCD remap), and the FP8 base above
     # 64 tokens (one fp8 GEMM launch, reordered longest contraction first)
     (ofmt.FMT_NF4, 16, 16, [(512, 384), (512, 128), (512, 128)]),
+    # 16 tokens, one problem for the streaming kernel and one whose scale rows
+    # (11 fp16 entries) rule it out: each runs the kernel of its own call
+    (ofmt.FMT_Q4_0, 16, 8, [(352, 224), (768, 512)]),
+    (ofmt.FMT_MXFP4, 3, 16, [(96, 160), (896, 864)]),
     (ofmt.FMT_MXFP4, 64, 8, [(1024, 256), (256, 1024)]),
     (ofmt.FMT_Q4_0, 33, 32, [(96, 224), (1056, 64), (256, 96)]),
     (ofmt.FMT_FP8, 24, 16, [(256, 160), (512, 96)]),

@@ -26,8 +26,12 @@ def shapes(fmt, count=24):
     out = []
     for i in range(count):
         m = int(MS[(i * 7 + fmt) % len(MS)])
-        # mostly short contractions; every fourth up to 4096 (long split slices)
+        # mostly short contractions; every fourth up to 4096 (long split slices);
+        # formats with 32-element blocks also take odd multiples of 32 (a half
+        # contraction step at the end)
         k = 64 * int(g.integers(1, 65 if i % 4 == 3 else 25))
+        if fmt != ofmt.FMT_NF4 and i % 3 == 1:
+            k -= 32
         n = 32 * int(g.integers(1, 33))
         r = int(g.choice([8, 16, 32]))
         out.append((fmt, m, k, n, r, int(g.integers(0, 1 << 30))))
@@ -65,7 +69,8 @@ def groups(fmt, count=2):
     for i in range(count):
         m = int(MS[(i * 5 + 3 * fmt) % len(MS)])
         r = int(g.choice([8, 16, 32]))
-        probs = [(64 * int(g.integers(1, 25)), 32 * int(g.integers(1, 33))) for _ in range(int(g.integers(2, 4)))]
+        kb = 64 if fmt == ofmt.FMT_NF4 else 32
+        probs = [(kb * int(g.integers(1, 49)), 32 * int(g.integers(1, 33))) for _ in range(int(g.integers(2, 4)))]
         out.append((fmt, m, r, probs, int(g.integers(0, 1 << 30))))
     return out
 
