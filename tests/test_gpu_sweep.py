@@ -114,3 +114,40 @@ def test_sweep_groups(lib, grp):
             g_ = got[key].float().cpu().numpy() if got[key].dtype == torch.bfloat16 else got[key].cpu().numpy()
             e = H.rel(g_, ref[rk])
             assert e <= H.FWD_TOL, (j, key, e)
+
+
+@pytest.mark.parametrize("case", CASES[::3], ids=[f"fmt{c[0]}-m{c[1]}-k{c[2]}-n{c[3]}-r{c[4]}" for c in CASES[::3]])
+def test_sweep_backward_variants(lib, case):
+    """The backward's other forms on the sweep's shapes: without dX (dA, dB
+    within 1e-2 of the oracle), accumulating into given dA / dB (bitwise the
+    given values plus the fresh gradients), and the allocation-free call
+    (bitwise the workspace call's outputs)."""
+    from quantized_base_lora_amd import binding as B
+    fmt, m, k, n, r, seed = case
+    print(f"sweep backward variants fmt={fmt} m={m} k={k} n={n} r={r}", flush=True)
+    alpha = 2.0 * r
+    c = H.make_case(m, k, n, r, seed=seed)
+    qw = B.quant_pack(fmt, torch.from_numpy(c["W"]).cuda())
+    t = {key: H.bits_to_bf16_tensor(c[key]) for key in ("x", "dY", "A", "B")}
+    _, u = B.linear_fwd(qw, t["x"], t["A"], t["B"], alpha)
+    dx, da, db = B.linear_bwd(qw, t["x"], t["dY"], u, t["A"], t["B"], alpha)
+    _, da_n, db_n = B.linear_bwd(qw, t["x"], t["dY"], u, t["A"], t["B"], alpha, need_dx=False)
+    g = np.random.default_rng(seed)
+    da0 = torch.from_numpy(g.standard_normal((r, k)).astype(np.float32)).cuda()
+    db0 = torch.from_numpy(g.standard_normal((n, r)).astype(np.float32)).cuda()
+    _, da_a, db_a = B.linear_bwd(qw, t["x"], t["dY"], u, t["A"], t["B"], alpha, accumulate=True,
+                                 da=da0.clone(), db=db0.clone())
+    torch.cuda.synchronize()
+    _, _, wd = H.oracle_packed(fmt, c["W"])
+    ref = H.oracle_layer(c, wd, alpha)
+    assert H.rel(da_n.cpu().numpy(), ref["dA"]) <= H.FWD_TOL
+    assert H.rel(db_n.cpu().numpy(), ref["dB"]) <= H.FWD_TOL
+    assert torch.equal(da_a, da0 + da) and torch.equal(db_a, db0 + db)
+    if B.workspace_bytes(B.OP_BWD, fmt, n, k, m, r) <= B.NOALLOC_SCRATCH_BYTES:
+        dx2 = torch.empty_like(dx)
+        da2 = torch.empty_like(da)
+        db2 = torch.empty_like(db)
+        B.linear_bwd_noalloc(qw, t["x"], t["dY"], u, t["A"], t["B"], alpha, dx2, da2, db2)
+        torch.cuda.synchronize()
+        assert torch.equal(dx2.view(torch.int16), dx.view(torch.int16))
+        assert torch.equal(da2, da) and torch.equal(db2, db)
