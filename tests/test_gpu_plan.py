@@ -399,3 +399,117 @@ def test_bench_launch_configuration_matches_single_calls(lib, wname, m):
                 iv = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
                 assert torch.equal(a.view(iv), b.view(iv)), (run, e["p"].name, key)
     pl.close()
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_plan_random_sequences(lib, seed):
+    """Random launch plans of forward, backward and grouped backward steps and
+    events over a pool of calls at three of 24, 96, 600 and 1100 tokens (the fused,
+    single-partition and several-partition gradient paths), with workspaces
+    borrowed from other calls and backward steps accumulating into earlier
+    outputs: every output bitwise that of the same calls made one by one, on
+    two runs of the plan."""
+    from quantized_base_lora_amd import binding as B
+    g = np.random.default_rng(4200 + seed)
+    fmt = [ofmt.FMT_NF4, ofmt.FMT_MXFP4, ofmt.FMT_Q4_0, ofmt.FMT_NVFP4, ofmt.FMT_Q8_0, ofmt.FMT_FP8][seed % 6]
+    r, alpha = int(g.choice([8, 16, 32])), 16.0
+    pool = []
+    for m in [int(x) for x in g.choice([24, 96, 600, 1100], size=3, replace=False)]:
+        for _ in range(3):                                # three calls per token count (groups share it)
+            pool.append((m, 64 * int(g.integers(1, 6)), 32 * int(g.integers(1, 9))))
+    print(f"random plan seed={seed} fmt={fmt} r={r} pool={pool}", flush=True)
+    wsb = max(256, max(max(B.workspace_bytes(B.OP_BWD, fmt, n, k, m, r), B.workspace_bytes(B.OP_FWD, fmt, n, k, m, r))
+                       for m, k, n in pool))
+    calls = []
+    for i, (m, k, n) in enumerate(pool):
+        c = H.make_case(m, k, n, r, seed=4300 + 10 * seed + i)
+        qw = B.quant_pack(fmt, torch.from_numpy(c["W"]).cuda())
+        t = {key: H.bits_to_bf16_tensor(c[key]) for key in ("x", "dY", "A", "B")}
+        _, u = B.linear_fwd(qw, t["x"], t["A"], t["B"], alpha)
+        calls.append({"qw": qw, "t": t, "u": u, "m": m, "k": k, "n": n,
+                      "ws": torch.empty(wsb, dtype=torch.uint8, device="cuda")})
+    torch.cuda.synchronize()
+    # steps: ("fwd"|"bwd", [(call, slot, workspace owner, accumulate)]) or ("event", [])
+    seq, slot_of = [], {}
+    for _ in range(12):
+        kind = g.choice(["fwd", "bwd", "bwd", "group", "group", "event"])
+        if kind == "event":
+            seq.append(("event", []))
+            continue
+        if kind == "group":
+            m0 = int(g.integers(0, 3))                   # one token count for the group
+            cis = [3 * m0 + int(x) for x in g.choice(3, size=int(g.integers(2, 4)), replace=False)]
+            items = [(ci, f"b{ci}", ci, False) for ci in cis]   # own slots and workspaces: independent
+            seq.append(("group", items))
+            continue
+        ci = int(g.integers(0, len(calls)))
+        wsi = int(g.integers(0, len(calls))) if g.random() < 0.4 else ci
+        if kind == "fwd":
+            seq.append(("fwd", [(ci, f"f{ci}", wsi, False)]))
+        else:
+            acc = bool(f"b{ci}" in slot_of and g.random() < 0.5)
+            seq.append(("bwd", [(ci, f"b{ci}", wsi, acc)]))
+        for it in seq[-1][1]:
+            slot_of[it[1]] = it[0]
+    for kind, its in seq:
+        for ci, slot, _, _ in its:
+            slot_of[slot] = ci
+
+    def new_out(slot):
+        c = calls[slot_of[slot]]
+        if slot[0] == "f":
+            return {"y": torch.empty((c["m"], c["n"]), dtype=torch.bfloat16, device="cuda"),
+                    "u": torch.empty((c["m"], r), dtype=torch.float32, device="cuda")}
+        return {"dx": torch.empty((c["m"], c["k"]), dtype=torch.bfloat16, device="cuda"),
+                "da": torch.zeros((r, c["k"]), dtype=torch.float32, device="cuda"),
+                "db": torch.zeros((c["n"], r), dtype=torch.float32, device="cuda")}
+
+    def bitem(ci, o, wsi, acc):
+        c = calls[ci]
+        t = c["t"]
+        return (c["qw"], t["x"], t["dY"], c["u"], t["A"], t["B"], alpha, o["dx"], o["da"], o["db"],
+                calls[wsi]["ws"], acc)
+
+    ref = {s: new_out(s) for s in slot_of}
+    for kind, its in seq:
+        for ci, slot, wsi, acc in its:
+            c = calls[ci]
+            o = ref[slot]
+            if kind == "fwd":
+                B.linear_fwd(c["qw"], c["t"]["x"], c["t"]["A"], c["t"]["B"], alpha, y=o["y"], u=o["u"],
+                             ws=calls[wsi]["ws"])
+            elif kind in ("bwd", "group"):
+                B.linear_bwd(c["qw"], c["t"]["x"], c["t"]["dY"], c["u"], c["t"]["A"], c["t"]["B"], alpha,
+                             accumulate=acc, dx=o["dx"], da=o["da"], db=o["db"], ws=calls[wsi]["ws"])
+    torch.cuda.synchronize()
+    got = {s: new_out(s) for s in slot_of}
+    pl = B.Plan()
+    stream = torch.cuda.current_stream()
+    ev = torch.cuda.Event()
+    for kind, its in seq:
+        if kind == "event":
+            pl.add_event(ev, stream)
+        elif kind == "fwd":
+            ci, slot, wsi, _ = its[0]
+            c = calls[ci]
+            pl.add_fwd(c["qw"], c["t"]["x"], c["t"]["A"], c["t"]["B"], alpha, got[slot]["y"], got[slot]["u"],
+                       calls[wsi]["ws"])
+        elif kind == "bwd":
+            ci, slot, wsi, acc = its[0]
+            pl.add_bwd(*bitem(ci, got[slot], wsi, acc))
+        else:
+            pl.add_bwd_group([bitem(ci, got[slot], wsi, acc) for ci, slot, wsi, acc in its])
+    for run in range(2):
+        for s, o in got.items():
+            for key, v in o.items():
+                if key in ("da", "db"):
+                    v.zero_()                              # the starting values of accumulating steps
+                else:
+                    v.fill_(float("nan"))
+        pl.run()
+        torch.cuda.synchronize()
+        for s, o in got.items():
+            for key, v in o.items():
+                iv = torch.int16 if v.dtype == torch.bfloat16 else torch.int32
+                assert torch.equal(v.view(iv), ref[s][key].view(iv)), (run, s, key)
+    pl.close()
