@@ -22,6 +22,30 @@ CASES = [
 ]
 
 
+def random_cases(count=10):
+    """Seeded stacks: 2-4 adapters whose ranks sum to 8, 16 or 32, alphas with
+    non-power-of-two ratios, every format, token counts on every path."""
+    g = np.random.default_rng(77)
+    fmts = [ofmt.FMT_Q4_0, ofmt.FMT_NF4, ofmt.FMT_FP8, ofmt.FMT_MXFP4, ofmt.FMT_Q8_0, ofmt.FMT_NVFP4]
+    out = []
+    for i in range(count):
+        fmt = fmts[i % len(fmts)]
+        R = int(g.choice([8, 16, 32]))
+        parts = int(g.integers(2, 5))
+        cuts = sorted(int(x) for x in g.choice(np.arange(1, R), size=parts - 1, replace=False))
+        ranks = [b - a for a, b in zip([0] + cuts, cuts + [R])]
+        # alphas cross the C ABI as fp32: draw them as fp32 values
+        spec = [(r, float(np.float32(np.round(g.uniform(0.5, 4.0) * r, 2)))) for r in ranks]
+        m = int(g.choice([5, 16, 40, 96, 300]))
+        k = (64 if fmt == ofmt.FMT_NF4 else 32) * int(g.integers(2, 17))
+        n = 32 * int(g.integers(1, 13))
+        out.append((f"random{i}_fmt{fmt}_m{m}_R{R}_{parts}", fmt, m, k, n, spec))
+    return out
+
+
+CASES += random_cases()
+
+
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_stacked_parity(lib, case):
     from quantized_base_lora_amd import binding as B
