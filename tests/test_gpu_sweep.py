@@ -43,25 +43,7 @@ CASES = [c for f in FMTS for c in shapes(f)]
 
 @pytest.mark.parametrize("case", CASES, ids=[f"fmt{c[0]}-m{c[1]}-k{c[2]}-n{c[3]}-r{c[4]}" for c in CASES])
 def test_sweep_parity(lib, case):
-    from quantized_base_lora_amd import binding as B
-    fmt, m, k, n, r, seed = case
-    print(f"sweep fmt={fmt} m={m} k={k} n={n} r={r} seed={seed}", flush=True)
-    sys.stdout.flush()
-    alpha = 2.0 * r
-    c = H.make_case(m, k, n, r, seed=seed)
-    qw = B.quant_pack(fmt, torch.from_numpy(c["W"]).cuda())
-    t = {key: H.bits_to_bf16_tensor(c[key]) for key in ("x", "dY", "A", "B")}
-    y, u = B.linear_fwd(qw, t["x"], t["A"], t["B"], alpha)
-    dx, da, db = B.linear_bwd(qw, t["x"], t["dY"], u, t["A"], t["B"], alpha)
-    torch.cuda.synchronize()
-    _, _, wd = H.oracle_packed(fmt, c["W"])
-    ref = H.oracle_layer(c, wd, alpha)
-    got = {"y": y.float().cpu().numpy(), "U": u.cpu().numpy(), "dX": dx.float().cpu().numpy(),
-           "dA": da.cpu().numpy(), "dB": db.cpu().numpy()}
-    for key, v in got.items():
-        e = H.rel(v, ref[key])
-        assert e <= H.FWD_TOL, (key, e)
-
+    _parity(case)
 
 def groups(fmt, count=2):
     g = np.random.default_rng(2000 + fmt)
@@ -151,3 +133,47 @@ def test_sweep_backward_variants(lib, case):
         torch.cuda.synchronize()
         assert torch.equal(dx2.view(torch.int16), dx.view(torch.int16))
         assert torch.equal(da2, da) and torch.equal(db2, db)
+
+
+def large_shapes(count=12):
+    g = np.random.default_rng(3000)
+    out = []
+    for i in range(count):
+        fmt = FMTS[i % len(FMTS)]
+        m = int(g.integers(600, 3100))
+        kb = 64 if fmt == ofmt.FMT_NF4 else 32
+        k = kb * int(g.integers(2, 2048 // kb + 1))
+        n = 32 * int(g.integers(2, 41))
+        out.append((fmt, m, k, n, int(g.choice([8, 16, 32])), int(g.integers(0, 1 << 30))))
+    return out
+
+
+LARGE = large_shapes()
+
+
+@pytest.mark.parametrize("case", LARGE, ids=[f"fmt{c[0]}-m{c[1]}-k{c[2]}-n{c[3]}-r{c[4]}" for c in LARGE])
+def test_sweep_large_m(lib, case):
+    """600-3100 tokens: several waves of row tiles, two to seven gradient
+    partitions, ragged last tiles in every dimension; all five outputs
+    against the oracle on every row."""
+    _parity(case)
+
+
+def _parity(case):
+    from quantized_base_lora_amd import binding as B
+    fmt, m, k, n, r, seed = case
+    print(f"sweep fmt={fmt} m={m} k={k} n={n} r={r} seed={seed}", flush=True)
+    alpha = 2.0 * r
+    c = H.make_case(m, k, n, r, seed=seed)
+    qw = B.quant_pack(fmt, torch.from_numpy(c["W"]).cuda())
+    t = {key: H.bits_to_bf16_tensor(c[key]) for key in ("x", "dY", "A", "B")}
+    y, u = B.linear_fwd(qw, t["x"], t["A"], t["B"], alpha)
+    dx, da, db = B.linear_bwd(qw, t["x"], t["dY"], u, t["A"], t["B"], alpha)
+    torch.cuda.synchronize()
+    _, _, wd = H.oracle_packed(fmt, c["W"])
+    ref = H.oracle_layer(c, wd, alpha)
+    got = {"y": y.float().cpu().numpy(), "U": u.cpu().numpy(), "dX": dx.float().cpu().numpy(),
+           "dA": da.cpu().numpy(), "dB": db.cpu().numpy()}
+    for key, v in got.items():
+        e = H.rel(v, ref[key])
+        assert e <= H.FWD_TOL, (key, e)
