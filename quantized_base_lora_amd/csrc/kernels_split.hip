@@ -1251,6 +1251,11 @@ SplitPlan split_plan(bool trans, int64_t m, int64_t n, int64_t k, int r) {
   const int64_t cap = (!trans && m <= 16) ? 512 : 256;
   int64_t sp = std::min<int64_t>({std::max<int64_t>(1, KT / 4), cap / tn, (int64_t)MAX_SPLITS});
   if (sp < 1) sp = 1;
+  // a wide dX output (more than 128 column tiles at two splits: fewer units
+  // than CUs) takes up to 512 units, so every CU gets work (Llama-3.1-8B's
+  // down projection at 16-64 tokens: 224 -> 448 units, the step 2-3 % shorter)
+  if (trans && tn * sp < 256)
+    sp = std::max<int64_t>(sp, std::min<int64_t>({std::max<int64_t>(1, KT / 4), 512 / tn, (int64_t)MAX_SPLITS}));
   pl.sps = (int)((KT + sp - 1) / sp);
   pl.splits = (int)((KT + pl.sps - 1) / pl.sps);
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
