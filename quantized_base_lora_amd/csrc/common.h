@@ -181,6 +181,6 @@ hipError_t launch_grads_group(const GradLaunch* g, int n, hipStream_t s, GradRed
 // launches the set's reductions as one launch (nothing if it is empty) and empties it
 hipError_t launch_grad_reduce(GradReduceSet& d, hipStream_t s);
 int32_t grad_parts(int64_t m);
-int64_t grad_tiles(int64_t pdim);
+int64_t grad_tiles(int64_t pdim, int32_t r);
 
 }  // namespace ql

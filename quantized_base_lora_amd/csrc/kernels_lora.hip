@@ -5,9 +5,10 @@
 // Both have the form out[p][j] = s . sum_m X[m][p] . Q[m][j] with X a bf16
 // activation ([M, K] or [M, N]) and Q an fp32 rank-r projection ([M, r]);
 // one launch serves both, for up to QL_GROUP_MAX calls at once (a problem
-// table in the kernel arguments).  A workgroup owns 64 columns p and one
-// of P fixed partitions of M; it streams its rows through LDS in steps of
-// 64 (loads running three steps ahead) and accumulates on 16x16x32 bf16
+// table in the kernel arguments).  A workgroup owns 64 columns p (128 at
+// rank 32) and one of P fixed partitions of M; it streams its rows through
+// LDS in steps of 64 (loads running ahead in a ring of register sets) and
+// accumulates on 16x16x32 bf16
 // MFMAs, with X reaching the A operand through LDS transpose reads and Q
 // split into a high and a low bf16 term (about 16 bits kept).  Each
 // workgroup writes its partial sums; a second launch adds the P partials in
@@ -23,11 +24,14 @@ namespace ql {
 namespace {
 
 constexpr int NT = 256;
-constexpr int TP = 64;          // p columns per workgroup (16 per wave)
 constexpr int TMC = 64;         // m rows per step
-constexpr int SX = TP + 32;     // X tile stride (bf16): 192 B rows
 constexpr int SQ = 32 + 16;     // Q tile stride (bf16), up to 32 columns
 constexpr int CHUNK = 512;      // rows per partition
+// p columns per workgroup: 16 per wave up to rank 16; 32 per wave (two MFMA
+// column blocks sharing each Q fragment) at rank 32, which halves the Q loads,
+// splits and LDS reads per X byte
+template <int R> constexpr int grad_cpw() { return R == 32 ? 2 : 1; }
+template <int R> constexpr int grad_tp() { return 64 * grad_cpw<R>(); }
 
 struct GradProb {
   const uint16_t* x;
@@ -55,14 +59,17 @@ struct GradArgs {
 };
 
 // four workgroups per CU (register budget of four waves per SIMD) for ranks up
-// to 16; rank 32 needs more registers
-template <int R> constexpr int grad_waves() { return R <= 16 ? 4 : 2; }
+// to 16; rank 32 needs more registers (three)
+template <int R> constexpr int grad_waves() { return R <= 16 ? 4 : 3; }
 
 template <int R>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(grad_waves<R>(), grad_waves<R>())))
 void grad_kernel(GradArgs a) {
   constexpr int RB = (R + 15) / 16;
   constexpr int QPT = R / 4;                         // Q floats per thread per step
+  constexpr int CPW = grad_cpw<R>(), TP = grad_tp<R>();
+  constexpr int SX = TP + 32;                        // X tile stride (bf16)
+  constexpr int XPT = TP / 32;                       // X pieces (8 columns) per thread per step
   __shared__ __attribute__((aligned(16))) uint16_t Xs[TMC * SX];
   __shared__ __attribute__((aligned(16))) uint16_t Qh[TMC * SQ];
   __shared__ __attribute__((aligned(16))) uint16_t Ql[TMC * SQ];
@@ -80,27 +87,33 @@ void grad_kernel(GradArgs a) {
 
   for (int i = tid; i < TMC * SQ; i += NT) { Qh[i] = 0; Ql[i] = 0; }
 
-  f32x4 acc[RB];
+  f32x4 acc[CPW][RB];
 #pragma unroll
-  for (int jb = 0; jb < RB; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int cb = 0; cb < CPW; ++cb)
+#pragma unroll
+    for (int jb = 0; jb < RB; ++jb) acc[cb][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int xr = tid >> 3, xc = (tid & 7) * 8;       // X: rows xr, xr + 32; 8 columns
+  // X: rows xr + (256 / (TP / 8)) i, 8 columns at xc
+  constexpr int XROWS = NT / (TP / 8);
+  const int xr = tid / (TP / 8), xc = (tid % (TP / 8)) * 8;
   const int qr = tid >> 2, qc = (tid & 3) * QPT;
 
   // loads run DEPTH - 1 steps ahead of the LDS stores (a ring of register sets).
   // Reads past the partition or past the last column go to an out-of-range
   // buffer offset and return zero, so no loaded value is inspected at issue.
-  constexpr int DEPTH = grad_waves<R>() == 4 ? 3 : 4;   // ring depth that fits the register budget
+  // ring depth that fits the register budget (the rank-32 tile's X pieces
+  // are twice as many)
+  constexpr int DEPTH = R == 32 ? 2 : 3;
   const __amdgpu_buffer_rsrc_t rx = rsrc(pr.x + mq0 * pr.pdim, (mq1 - mq0) * pr.pdim * 2);
   const __amdgpu_buffer_rsrc_t rq = rsrc(pr.q + mq0 * R, (mq1 - mq0) * R * 4);
   const int NS = (int)((mq1 - mq0 + TMC - 1) / TMC);
-  uint4 xv[DEPTH][2];
+  uint4 xv[DEPTH][XPT];
   uint32_t qv[DEPTH][QPT];
   auto load = [&](int slot, int step) {
     const int64_t r0 = (int64_t)step * TMC;            // first row of the step, partition-relative
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t row = r0 + xr + 32 * i, col = p0 + xc;
+    for (int i = 0; i < XPT; ++i) {
+      const int64_t row = r0 + xr + XROWS * i, col = p0 + xc;
       xv[slot][i] = bload16(rx, col < pr.pdim ? (uint32_t)((row * pr.pdim + col) * 2) : OOB);
     }
     const uint32_t qoff = (uint32_t)(((r0 + qr) * R + qc) * 4);
@@ -119,7 +132,7 @@ void grad_kernel(GradArgs a) {
   auto step = [&](int u) {
     lds_barrier();                                    // previous step's readers are done
 #pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(Xs + (xr + 32 * i) * SX + xc) = xv[u][i];
+    for (int i = 0; i < XPT; ++i) *reinterpret_cast<uint4*>(Xs + (xr + XROWS * i) * SX + xc) = xv[u][i];
     // this thread's QPT consecutive Q values as hi / lo bf16 pairs, packed into
     // 32-bit words and stored 8 bytes at a time (4 for rank 8)
     uint32_t hw[QPT / 2], lw[QPT / 2];
@@ -145,15 +158,22 @@ void grad_kernel(GradArgs a) {
     for (int kp = 0; kp < 2; ++kp) {
       const int b = lane >> 4, sl = lane & 15;
       const int rbase = 32 * kp + 8 * b + (sl >> 2);
-      const int xcol = 16 * wave + 4 * (sl & 3);
-      const bf16x8 af = tr16x8(Xs + rbase * SX + xcol, Xs + (rbase + 4) * SX + xcol);
+      bf16x8 af[CPW];
+#pragma unroll
+      for (int cb = 0; cb < CPW; ++cb) {
+        const int xcol = 16 * (CPW * wave + cb) + 4 * (sl & 3);
+        af[cb] = tr16x8(Xs + rbase * SX + xcol, Xs + (rbase + 4) * SX + xcol);
+      }
 #pragma unroll
       for (int jb = 0; jb < RB; ++jb) {
         const int col = 16 * jb + 4 * (sl & 3);
         const bf16x8 th = tr16x8(Qh + rbase * SQ + col, Qh + (rbase + 4) * SQ + col);
         const bf16x8 tl = tr16x8(Ql + rbase * SQ + col, Ql + (rbase + 4) * SQ + col);
-        acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, th, acc[jb], 0, 0, 0);
-        acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, tl, acc[jb], 0, 0, 0);
+#pragma unroll
+        for (int cb = 0; cb < CPW; ++cb) {
+          acc[cb][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[cb], th, acc[cb][jb], 0, 0, 0);
+          acc[cb][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[cb], tl, acc[cb][jb], 0, 0, 0);
+        }
       }
     }
   };
@@ -183,21 +203,23 @@ void grad_kernel(GradArgs a) {
   const bool final_out = a.nparts == 1;
   float* dst = pr.part + (int64_t)part * pr.pdim * R;
 #pragma unroll
-  for (int jb = 0; jb < RB; ++jb)
+  for (int cb = 0; cb < CPW; ++cb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t prow = p0 + 16 * wave + 4 * (lane >> 4) + e;
-      const int j = 16 * jb + (lane & 15);
-      if (prow < pr.pdim && j < R) {
-        if (final_out) {
-          const int64_t o = pr.transpose_out ? (int64_t)j * pr.pdim + prow : prow * R + j;
-          const float v = pr.s * acc[jb][e];
-          pr.out[o] = pr.accumulate ? pr.out[o] + v : v;
-        } else {
-          dst[prow * R + j] = acc[jb][e];
+    for (int jb = 0; jb < RB; ++jb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t prow = p0 + 16 * (CPW * wave + cb) + 4 * (lane >> 4) + e;
+        const int j = 16 * jb + (lane & 15);
+        if (prow < pr.pdim && j < R) {
+          if (final_out) {
+            const int64_t o = pr.transpose_out ? (int64_t)j * pr.pdim + prow : prow * R + j;
+            const float v = pr.s * acc[cb][jb][e];
+            pr.out[o] = pr.accumulate ? pr.out[o] + v : v;
+          } else {
+            dst[prow * R + j] = acc[cb][jb][e];
+          }
         }
       }
-    }
 }
 
 // out[p][j] (or out[j][p]) = s * sum_q part[q][p][j], q in partition order; one
@@ -266,7 +288,10 @@ int32_t grad_parts(int64_t m) {
   return (int32_t)p;
 }
 
-int64_t grad_tiles(int64_t pdim) { return (pdim + TP - 1) / TP; }
+int64_t grad_tiles(int64_t pdim, int32_t r) {
+  const int64_t tp = r == 32 ? grad_tp<32>() : grad_tp<16>();
+  return (pdim + tp - 1) / tp;
+}
 
 hipError_t launch_down_proj(const uint16_t* x, int64_t m, int64_t c, const uint16_t* b, int32_t r,
                             float* out, hipStream_t s) {
@@ -317,7 +342,7 @@ hipError_t launch_grads_group(const GradLaunch* g, int n, hipStream_t s, GradRed
   for (int i = 0; i < a.nprob; ++i) {
     GradProb& pr = a.prob[i];
     pr.blk0 = blocks;
-    blocks += (int32_t)grad_tiles(pr.pdim) * a.nparts;
+    blocks += (int32_t)grad_tiles(pr.pdim, a.r) * a.nparts;
     pr.rblk0 = rblocks;
     rblocks += (int32_t)((pr.pdim * a.r + NT - 1) / NT);
   }
