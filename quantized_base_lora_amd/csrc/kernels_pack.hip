@@ -20,6 +20,7 @@
 
 #include "common.h"
 #include "device.h"
+#include "actsplit.h"
 
 namespace ql {
 namespace {
@@ -418,20 +419,8 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
 }
 
 // ------------------------------------------------------------------ a1: activation split
-// One workgroup per row: s = max|x| / 448, t = x / s, hi = E4M3(t),
-// lo = E4M3((t - hi) * 16).
-// a1: per-token two-term E4M3 split.  Row scale s = 2^e, e the smallest
-// integer with 448 * 2^e >= max|x|; t = x * 2^-e is exact (|t| <= 448), and so
-// are t - hi and the factor 16, leaving the two E4M3 roundings (the hardware
-// conversion, nearest even; it is never asked to saturate: |t| <= 448 and
-// |16 (t - hi)| <= 256).  One workgroup per row; the second pass re-reads
-// the row from cache.
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
-  return (uint32_t)v;
-}
-
+// The two-term E4M3 split of actsplit.h, one workgroup per row; the second
+// pass re-reads the row from cache.
 __global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t* __restrict__ x, int64_t k,
                                                              uint8_t* __restrict__ hi,
                                                              uint8_t* __restrict__ lo,
@@ -441,50 +430,24 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t* __r
   const uint16_t* xr = x + row * k;
   float amax = 0.0f;
   for (int64_t c = (int64_t)threadIdx.x * 8; c < k; c += kThreads * 8) {
-    uint4 t = *reinterpret_cast<const uint4*>(xr + c);
-    uint32_t wd[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      amax = fmaxf(amax, fabsf(__uint_as_float(wd[i] << 16)));
-      amax = fmaxf(amax, fabsf(__uint_as_float(wd[i] & 0xFFFF0000u)));
-    }
+    const uint4 t = *reinterpret_cast<const uint4*>(xr + c);
+    const uint32_t wd[4] = {t.x, t.y, t.z, t.w};
+    amax = absmax8(amax, wd);
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  int e = 0;
-  if (amax > 0.0f) {
-    const int E = ilogbf(amax);                        // amax = m 2^E, m in [1, 2)
-    e = ldexpf(amax, -E) <= 1.75f ? E - 8 : E - 7;     // 448 2^(E-8) = 1.75 2^E
-  }
+  const int e = amax > 0.0f ? split_exponent(amax) : 0;
   if (threadIdx.x == 0) scale[row] = amax > 0.0f ? ldexpf(1.0f, e) : 0.0f;
   for (int64_t c = (int64_t)threadIdx.x * 8; c < k; c += kThreads * 8) {
-    uint4 t = *reinterpret_cast<const uint4*>(xr + c);
-    uint32_t wd[4] = {t.x, t.y, t.z, t.w};
-    float v[8], r[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = ldexpf(__uint_as_float(wd[i] << 16), -e);
-      v[2 * i + 1] = ldexpf(__uint_as_float(wd[i] & 0xFFFF0000u), -e);
-    }
-    uint32_t h[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      h[q] = e4m3x4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-      typedef float f2v __attribute__((ext_vector_type(2)));
-      const f2v d0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h[q], false);
-      const f2v d1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h[q], true);
-      r[4 * q] = (v[4 * q] - d0.x) * 16.0f;
-      r[4 * q + 1] = (v[4 * q + 1] - d0.y) * 16.0f;
-      r[4 * q + 2] = (v[4 * q + 2] - d1.x) * 16.0f;
-      r[4 * q + 3] = (v[4 * q + 3] - d1.y) * 16.0f;
-    }
-    const uint32_t l0 = e4m3x4(r[0], r[1], r[2], r[3]), l1 = e4m3x4(r[4], r[5], r[6], r[7]);
-    if (amax == 0.0f) h[0] = h[1] = 0u;
-    *reinterpret_cast<uint2*>(hi + row * k + c) = make_uint2(h[0], h[1]);
-    *reinterpret_cast<uint2*>(lo + row * k + c) = make_uint2(amax == 0.0f ? 0u : l0, amax == 0.0f ? 0u : l1);
+    const uint4 t = *reinterpret_cast<const uint4*>(xr + c);
+    const uint32_t wd[4] = {t.x, t.y, t.z, t.w};
+    uint2 h8, l8;
+    split8(wd, e, amax == 0.0f, h8, l8);
+    *reinterpret_cast<uint2*>(hi + row * k + c) = h8;
+    *reinterpret_cast<uint2*>(lo + row * k + c) = l8;
   }
 }
 
@@ -492,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t* __r
 // held in registers: each lane loads CH 16-byte chunks (columns
 // 8 (lane + 64 c) ..; chunks past K read zero), the row maximum is a wave
 // reduction, and the quantization runs from the registers, so x is read from
-// memory once.  Per element the arithmetic is that of act_quant_kernel.
+// memory once.
 template <int CH>
 __global__ __launch_bounds__(256) void act_quant_wave_kernel(const uint16_t* __restrict__ x, int64_t m, int64_t k,
                                                              uint8_t* __restrict__ hi, uint8_t* __restrict__ lo,
@@ -508,47 +471,21 @@ __global__ __launch_bounds__(256) void act_quant_wave_kernel(const uint16_t* __r
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const uint32_t wd[4] = {t[c].x, t[c].y, t[c].z, t[c].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      amax = fmaxf(amax, fabsf(__uint_as_float(wd[i] << 16)));
-      amax = fmaxf(amax, fabsf(__uint_as_float(wd[i] & 0xFFFF0000u)));
-    }
+    amax = absmax8(amax, wd);
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  int e = 0;
-  if (amax > 0.0f) {
-    const int E = ilogbf(amax);                        // amax = m 2^E, m in [1, 2)
-    e = ldexpf(amax, -E) <= 1.75f ? E - 8 : E - 7;     // 448 2^(E-8) = 1.75 2^E
-  }
+  const int e = amax > 0.0f ? split_exponent(amax) : 0;
   if (lane == 0) scale[row] = amax > 0.0f ? ldexpf(1.0f, e) : 0.0f;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int64_t col = 8 * (lane + 64 * (int64_t)c);
     if (col >= k) continue;
     const uint32_t wd[4] = {t[c].x, t[c].y, t[c].z, t[c].w};
-    float v[8], r[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = ldexpf(__uint_as_float(wd[i] << 16), -e);
-      v[2 * i + 1] = ldexpf(__uint_as_float(wd[i] & 0xFFFF0000u), -e);
-    }
-    uint32_t h[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      h[q] = e4m3x4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-      typedef float f2v __attribute__((ext_vector_type(2)));
-      const f2v d0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h[q], false);
-      const f2v d1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h[q], true);
-      r[4 * q] = (v[4 * q] - d0.x) * 16.0f;
-      r[4 * q + 1] = (v[4 * q + 1] - d0.y) * 16.0f;
-      r[4 * q + 2] = (v[4 * q + 2] - d1.x) * 16.0f;
-      r[4 * q + 3] = (v[4 * q + 3] - d1.y) * 16.0f;
-    }
-    const uint32_t l0 = e4m3x4(r[0], r[1], r[2], r[3]), l1 = e4m3x4(r[4], r[5], r[6], r[7]);
-    if (amax == 0.0f) h[0] = h[1] = 0u;
-    *reinterpret_cast<uint2*>(hi + row * k + col) = make_uint2(h[0], h[1]);
-    *reinterpret_cast<uint2*>(lo + row * k + col) = make_uint2(amax == 0.0f ? 0u : l0, amax == 0.0f ? 0u : l1);
+    uint2 h8, l8;
+    split8(wd, e, amax == 0.0f, h8, l8);
+    *reinterpret_cast<uint2*>(hi + row * k + col) = h8;
+    *reinterpret_cast<uint2*>(lo + row * k + col) = l8;
   }
 }
 
