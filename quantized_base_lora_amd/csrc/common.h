@@ -64,6 +64,16 @@ hipError_t launch_dequant(const ql_qweight& w, float* out_f32, uint16_t* out_bf1
                           hipStream_t s);
 hipError_t launch_act_quant(const uint16_t* x, int64_t m, int64_t k, uint8_t* hi,
                             uint8_t* lo, float* scale, hipStream_t s);
+// the split of n (1 .. QL_GROUP_MAX) activations of m rows each: one launch
+// per split kernel used
+struct ActSplit {
+  const uint16_t* x;
+  uint8_t* hi;
+  uint8_t* lo;
+  float* scale;
+  int64_t k;
+};
+hipError_t launch_act_quant_group(const ActSplit* sp, int n, int64_t m, hipStream_t s);
 hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t s);
 
@@ -126,6 +136,14 @@ hipError_t launch_qgemm8(const Gemm8Call* c, int n, hipStream_t s);
 // out [m, r] fp32 = act [m, c] . D, D = A^T (a_layout, A [r, c]) or B ([c, r])
 hipError_t launch_rproj(const uint16_t* act, int64_t m, int64_t c, const uint16_t* d, bool a_layout, int32_t r,
                         float* out, hipStream_t s);
+// n (1 .. QL_GROUP_MAX) projections of m rows each, one layout and rank: one launch
+struct Rproj {
+  const uint16_t* act;
+  const uint16_t* d;
+  float* out;
+  int64_t c;
+};
+hipError_t launch_rproj_group(const Rproj* pr, int n, int64_t m, bool a_layout, int32_t r, hipStream_t s);
 
 // stacked adapters -> one concatenated adapter (kernels_stack.hip); arguments already validated
 hipError_t launch_stack(const ql_adapter* ad, int32_t n, int64_t n_out, int64_t k_in, uint16_t* a_cat,

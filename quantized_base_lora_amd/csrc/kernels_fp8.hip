@@ -430,9 +430,31 @@ hipError_t launch8_w(Args8& a, hipStream_t s) {
 // with transposing reads.
 constexpr int RP_NW = 8;        // waves per rank-r projection workgroup
 
+// up to QL_GROUP_MAX projections of one token count, rank and layout in one
+// launch; each workgroup finds its problem in a table in the kernel arguments
+struct RprojJob {
+  const uint16_t* act;
+  const uint16_t* d;
+  float* out;
+  int64_t C;
+  int32_t blk0;          // first workgroup of this problem
+};
+struct RprojJobs {
+  RprojJob j[QL_GROUP_MAX];
+  int32_t n;
+  int64_t M;
+};
+
 template <int R, bool ALAYOUT>
-__global__ __launch_bounds__(64 * RP_NW) void rproj_kernel(const uint16_t* __restrict__ act, int64_t M, int64_t C,
-                                                           const uint16_t* __restrict__ d, float* __restrict__ out) {
+__global__ __launch_bounds__(64 * RP_NW) void rproj_kernel(RprojJobs jobs) {
+  const int bid = (int)blockIdx.x;
+  int ji = 0;
+  while (ji + 1 < jobs.n && bid >= jobs.j[ji + 1].blk0) ++ji;
+  const uint16_t* __restrict__ act = jobs.j[ji].act;
+  const uint16_t* __restrict__ d = jobs.j[ji].d;
+  float* __restrict__ out = jobs.j[ji].out;
+  const int64_t M = jobs.M, C = jobs.j[ji].C;
+  const int blk = bid - jobs.j[ji].blk0;
   constexpr int SLD = 48, SX = 72, D = 3, NW = RP_NW, NT = 64 * NW;
   constexpr int DP = ALAYOUT ? 4 : R / 8;            // adapter pieces per lane and chunk
   __shared__ __attribute__((aligned(16))) uint16_t xt[NW][32 * SX];                       // activation chunk
@@ -440,7 +462,7 @@ __global__ __launch_bounds__(64 * RP_NW) void rproj_kernel(const uint16_t* __res
   __shared__ float red[NW][32][33];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the chunk loop is not divergent
-  const int64_t m0 = (int64_t)blockIdx.x * 32;
+  const int64_t m0 = (int64_t)blk * 32;
   const __amdgpu_buffer_rsrc_t ract = rsrc(act + m0 * C, (M - m0) * C * 2);
   const __amdgpu_buffer_rsrc_t rd = rsrc(d, (int64_t)R * C * 2);
   if constexpr (!ALAYOUT)
@@ -543,13 +565,18 @@ __global__ __launch_bounds__(64 * RP_NW) void rproj_kernel(const uint16_t* __res
 
 }  // namespace
 
-hipError_t launch_rproj(const uint16_t* act, int64_t m, int64_t c, const uint16_t* d, bool a_layout, int32_t r,
-                        float* out, hipStream_t s) {
-  if (m == 0) return hipSuccess;
-  const dim3 grid((unsigned)((m + 31) / 32));
-#define QL_RPROJ(RR)                                                                                  \
-  if (a_layout) hipLaunchKernelGGL((rproj_kernel<RR, true>), grid, dim3(64 * RP_NW), 0, s, act, m, c, d, out); \
-  else hipLaunchKernelGGL((rproj_kernel<RR, false>), grid, dim3(64 * RP_NW), 0, s, act, m, c, d, out);
+hipError_t launch_rproj_group(const Rproj* pr, int n, int64_t m, bool a_layout, int32_t r, hipStream_t s) {
+  if (m == 0 || n == 0) return hipSuccess;
+  if (n > QL_GROUP_MAX) return hipErrorInvalidValue;
+  RprojJobs a{};
+  a.n = n;
+  a.M = m;
+  const int32_t per = (int32_t)((m + 31) / 32);
+  for (int i = 0; i < n; ++i) a.j[i] = RprojJob{pr[i].act, pr[i].d, pr[i].out, pr[i].c, per * i};
+  const dim3 grid((unsigned)(per * n));
+#define QL_RPROJ(RR)                                                                                 \
+  if (a_layout) hipLaunchKernelGGL((rproj_kernel<RR, true>), grid, dim3(64 * RP_NW), 0, s, a);      \
+  else hipLaunchKernelGGL((rproj_kernel<RR, false>), grid, dim3(64 * RP_NW), 0, s, a);
   switch (r) {
     case 8: QL_RPROJ(8) break;
     case 16: QL_RPROJ(16) break;
@@ -557,6 +584,12 @@ hipError_t launch_rproj(const uint16_t* act, int64_t m, int64_t c, const uint16_
   }
 #undef QL_RPROJ
   return hipGetLastError();
+}
+
+hipError_t launch_rproj(const uint16_t* act, int64_t m, int64_t c, const uint16_t* d, bool a_layout, int32_t r,
+                        float* out, hipStream_t s) {
+  const Rproj pr{act, d, out, c};
+  return launch_rproj_group(&pr, 1, m, a_layout, r, s);
 }
 
 hipError_t launch_qgemm8(const Gemm8Call* c, int n, hipStream_t s) {

@@ -715,7 +715,13 @@ static bool fp8_group(const GemmCall* calls, int n) {
 }
 
 static hipError_t launch_fp8_calls(const GemmCall* calls, int n, hipStream_t s) {
+  // the activation splits of the group's distinct activations, then the
+  // calls' projections, each in one launch (the computations are
+  // independent, so the order does not change results), then the GEMMs
   Gemm8Call g[MAX_GROUP];
+  ActSplit sp[MAX_GROUP];
+  Rproj pr[MAX_GROUP];
+  int nsp = 0;
   for (int i = 0; i < n; ++i) {
     const GemmCall& c = calls[i];
     const int64_t N = c.w->n_out, K = c.w->k_in, C = c.trans ? N : K;
@@ -731,14 +737,12 @@ static hipError_t launch_fp8_calls(const GemmCall* calls, int n, hipStream_t s) 
       uint8_t* hi = base;
       uint8_t* lo = base + fp.lo_off;
       float* rs = reinterpret_cast<float*>(base + fp.rs_off);
-      hipError_t e = launch_act_quant(c.act, c.m, C, hi, lo, rs, s);
-      if (e != hipSuccess) return e;
       g[i].hi = hi;
       g[i].lo = lo;
       g[i].rs = rs;
+      sp[nsp++] = ActSplit{c.act, hi, lo, rs, C};
     }
-    hipError_t e = launch_rproj(c.act, c.m, C, c.down, !c.trans, c.r, c.save, s);
-    if (e != hipSuccess) return e;
+    pr[i] = Rproj{c.act, c.down, c.save, C};
     g[i].w = c.w;
     g[i].trans = c.trans;
     g[i].m = c.m;
@@ -748,6 +752,10 @@ static hipError_t launch_fp8_calls(const GemmCall* calls, int n, hipStream_t s) 
     g[i].s = c.s;
     g[i].out = c.out;
   }
+  hipError_t e = launch_act_quant_group(sp, nsp, calls[0].m, s);
+  if (e != hipSuccess) return e;
+  e = launch_rproj_group(pr, n, calls[0].m, !calls[0].trans, calls[0].r, s);
+  if (e != hipSuccess) return e;
   return launch_qgemm8(g, n, s);
 }
 

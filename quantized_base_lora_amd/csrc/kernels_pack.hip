@@ -419,15 +419,33 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
 }
 
 // ------------------------------------------------------------------ a1: activation split
-// The two-term E4M3 split of actsplit.h, one workgroup per row; the second
-// pass re-reads the row from cache.
-__global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t* __restrict__ x, int64_t k,
-                                                             uint8_t* __restrict__ hi,
-                                                             uint8_t* __restrict__ lo,
-                                                             float* __restrict__ scale) {
+// The two-term E4M3 split of actsplit.h for up to QL_GROUP_MAX activations
+// of one token count in one launch; each workgroup finds its activation in a
+// table in the kernel arguments.
+struct SplitJob {
+  const uint16_t* x;
+  uint8_t* hi;
+  uint8_t* lo;
+  float* scale;
+  int64_t k;
+  int32_t blk0;          // first workgroup of this activation
+};
+struct SplitJobs {
+  SplitJob j[QL_GROUP_MAX];
+  int32_t n;
+  int64_t m;
+};
+
+// One workgroup per row; the second pass re-reads the row from cache.
+__global__ __launch_bounds__(kThreads) void act_quant_kernel(SplitJobs a) {
   __shared__ float red[kThreads / 64];
-  const int64_t row = blockIdx.x;
-  const uint16_t* xr = x + row * k;
+  const int bid = (int)blockIdx.x;
+  int ji = 0;
+  while (ji + 1 < a.n && bid >= a.j[ji + 1].blk0) ++ji;
+  const SplitJob& J = a.j[ji];
+  const int64_t k = J.k;
+  const int64_t row = bid - J.blk0;
+  const uint16_t* xr = J.x + row * k;
   float amax = 0.0f;
   for (int64_t c = (int64_t)threadIdx.x * 8; c < k; c += kThreads * 8) {
     const uint4 t = *reinterpret_cast<const uint4*>(xr + c);
@@ -440,14 +458,14 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t* __r
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const int e = amax > 0.0f ? split_exponent(amax) : 0;
-  if (threadIdx.x == 0) scale[row] = amax > 0.0f ? ldexpf(1.0f, e) : 0.0f;
+  if (threadIdx.x == 0) J.scale[row] = amax > 0.0f ? ldexpf(1.0f, e) : 0.0f;
   for (int64_t c = (int64_t)threadIdx.x * 8; c < k; c += kThreads * 8) {
     const uint4 t = *reinterpret_cast<const uint4*>(xr + c);
     const uint32_t wd[4] = {t.x, t.y, t.z, t.w};
     uint2 h8, l8;
     split8(wd, e, amax == 0.0f, h8, l8);
-    *reinterpret_cast<uint2*>(hi + row * k + c) = h8;
-    *reinterpret_cast<uint2*>(lo + row * k + c) = l8;
+    *reinterpret_cast<uint2*>(J.hi + row * k + c) = h8;
+    *reinterpret_cast<uint2*>(J.lo + row * k + c) = l8;
   }
 }
 
@@ -457,13 +475,16 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t* __r
 // reduction, and the quantization runs from the registers, so x is read from
 // memory once.
 template <int CH>
-__global__ __launch_bounds__(256) void act_quant_wave_kernel(const uint16_t* __restrict__ x, int64_t m, int64_t k,
-                                                             uint8_t* __restrict__ hi, uint8_t* __restrict__ lo,
-                                                             float* __restrict__ scale) {
+__global__ __launch_bounds__(256) void act_quant_wave_kernel(SplitJobs a) {
+  const int bid = (int)blockIdx.x;
+  int ji = 0;
+  while (ji + 1 < a.n && bid >= a.j[ji + 1].blk0) ++ji;
+  const SplitJob& J = a.j[ji];
+  const int64_t k = J.k;
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= m) return;                                // whole wave
-  const __amdgpu_buffer_rsrc_t rx = rsrc(x + row * k, k * 2);
+  const int64_t row = (int64_t)(bid - J.blk0) * 4 + (threadIdx.x >> 6);
+  if (row >= a.m) return;                              // whole wave
+  const __amdgpu_buffer_rsrc_t rx = rsrc(J.x + row * k, k * 2);
   uint4 t[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) t[c] = bload16(rx, (uint32_t)((8 * (lane + 64 * c)) * 2));
@@ -476,7 +497,7 @@ __global__ __launch_bounds__(256) void act_quant_wave_kernel(const uint16_t* __r
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   const int e = amax > 0.0f ? split_exponent(amax) : 0;
-  if (lane == 0) scale[row] = amax > 0.0f ? ldexpf(1.0f, e) : 0.0f;
+  if (lane == 0) J.scale[row] = amax > 0.0f ? ldexpf(1.0f, e) : 0.0f;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int64_t col = 8 * (lane + 64 * (int64_t)c);
@@ -484,8 +505,8 @@ __global__ __launch_bounds__(256) void act_quant_wave_kernel(const uint16_t* __r
     const uint32_t wd[4] = {t[c].x, t[c].y, t[c].z, t[c].w};
     uint2 h8, l8;
     split8(wd, e, amax == 0.0f, h8, l8);
-    *reinterpret_cast<uint2*>(hi + row * k + col) = h8;
-    *reinterpret_cast<uint2*>(lo + row * k + col) = l8;
+    *reinterpret_cast<uint2*>(J.hi + row * k + col) = h8;
+    *reinterpret_cast<uint2*>(J.lo + row * k + col) = l8;
   }
 }
 
@@ -585,17 +606,37 @@ hipError_t launch_dequant(const ql_qweight& w, float* out_f32, uint16_t* out_bf1
   return hipGetLastError();
 }
 
-hipError_t launch_act_quant(const uint16_t* x, int64_t m, int64_t k, uint8_t* hi, uint8_t* lo,
-                            float* scale, hipStream_t s) {
-  if (m == 0) return hipSuccess;
+hipError_t launch_act_quant_group(const ActSplit* sp, int n, int64_t m, hipStream_t s) {
+  if (m == 0 || n == 0) return hipSuccess;
+  if (n > QL_GROUP_MAX) return hipErrorInvalidValue;
   // rows of at most 4096 elements: one wave per row, x read once (measured
   // 20 % faster); longer rows would need so many registers per lane that one
-  // wave per SIMD remains, and the two-pass workgroup kernel is faster there
-  if (k <= 4096)
-    hipLaunchKernelGGL(act_quant_wave_kernel<8>, dim3((unsigned)((m + 3) / 4)), dim3(256), 0, s, x, m, k, hi, lo, scale);
-  else
-    hipLaunchKernelGGL(act_quant_kernel, dim3((unsigned)m), dim3(kThreads), 0, s, x, k, hi, lo, scale);
-  return hipGetLastError();
+  // wave per SIMD remains, and the two-pass workgroup kernel is faster there.
+  // One launch per kernel for the activations it takes.
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool wave = pass == 0;
+    SplitJobs a{};
+    a.m = m;
+    int32_t blocks = 0;
+    for (int i = 0; i < n; ++i) {
+      if ((sp[i].k <= 4096) != wave) continue;
+      a.j[a.n] = SplitJob{sp[i].x, sp[i].hi, sp[i].lo, sp[i].scale, sp[i].k, blocks};
+      ++a.n;
+      blocks += wave ? (int32_t)((m + 3) / 4) : (int32_t)m;
+    }
+    if (a.n == 0) continue;
+    if (wave) hipLaunchKernelGGL(act_quant_wave_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(act_quant_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_act_quant(const uint16_t* x, int64_t m, int64_t k, uint8_t* hi, uint8_t* lo,
+                            float* scale, hipStream_t s) {
+  const ActSplit sp{x, hi, lo, scale, k};
+  return launch_act_quant_group(&sp, 1, m, s);
 }
 
 }  // namespace ql
