@@ -699,6 +699,34 @@ __global__ __launch_bounds__(256) void qstream16_kernel(SplitArgs ga) {
   auto step = [&](Slot& sl, int t, bool refill) {
     const bool gl = kbeg + t < kend && (int64_t)(kbeg + t) * TK2 + 32 * q < p.C;
     uint4 wb[2][4];
+    if constexpr (FMT == QL_FMT_NF4) {
+      // The lanes of rows q and q ^ 1 (16 lanes each) hold the two 32-element
+      // groups of one NF4 block (64 elements, one absmax) for the same two W
+      // rows, so they need the same two lookup tables: each lane builds the
+      // table of row block q & 1, and one row swap per table word hands every
+      // lane of the pair both (the values are those it would have built).
+      const int bq = q & 1;
+      const uint8_t* srw = sw + (32 * wave + 16 * bq + (lane & 15)) * SW16;
+      const float a = __uint_as_float(*reinterpret_cast<const uint32_t*>(srw + 4 * (2 * t + (q >> 1))));
+      uint32_t tl[4], th[4], tb[2][2][4];
+      Deq<FMT>::build_table(p.book, gl ? a : 0.0f, tl, th);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const auto sl_ = __builtin_amdgcn_permlane16_swap(tl[w], tl[w], false, false);
+        const auto sh_ = __builtin_amdgcn_permlane16_swap(th[w], th[w], false, false);
+        tb[0][0][w] = sl_[0]; tb[1][0][w] = sl_[1];   // even row of the pair: row block 0; odd: 1
+        tb[0][1][w] = sh_[0]; tb[1][1][w] = sh_[1];
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        Deq<FMT> dq;
+        dq.wd[0] = sl.c[b].x; dq.wd[1] = sl.c[b].y; dq.wd[2] = sl.c[b].z; dq.wd[3] = sl.c[b].w;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) { dq.tl[w] = tb[b][0][w]; dq.th[w] = tb[b][1][w]; }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wb[b][i] = dq.piece(i);
+      }
+    } else {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       // this group's scale entry from the window: group 4 t + q of the slice
@@ -718,6 +746,7 @@ __global__ __launch_bounds__(256) void qstream16_kernel(SplitArgs ga) {
       dq.prepare(g, gl ? s0 : 0.0f, p.book, gl, gl ? s1 : 0.0f);
 #pragma unroll
       for (int i = 0; i < 4; ++i) wb[b][i] = dq.piece(i);
+    }
     }
     const uint16_t* xrow = xs + (lane & 15) * XS16 + t * TK2;
     if (rank_tile) {
