@@ -561,16 +561,30 @@ def optimizer_bench(args, wl):
 # ----------------------------------------------------------------------------- HBM ceiling
 
 def hbm_ceiling(args):
-    """Plain streaming kernels on 4 GiB (16x the MALL): a device-to-device
-    copy (read + write) and a read-only reduction (torch's sum), each timed
-    with HIP events over several repetitions; bytes moved / time."""
+    """Plain streaming kernels on 4 GiB (16x the MALL): the library's
+    streaming read (ql_stream_read, one pass, every word read once), a
+    device-to-device copy (read + write) and a read-only reduction (torch's
+    sum), each timed with HIP events over several repetitions; bytes moved /
+    time.  The streaming read's XOR of all words is checked against the
+    host's on a 64 MB prefix first."""
     import torch
+
+    from quantized_base_lora_amd import binding as B
     n = 4 << 30
     a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    a[:: 4097] = 3.0                                   # a pattern whose XOR is not zero
     b = torch.empty_like(a)
+    sink = torch.empty(B.STREAM_READ_THREADS, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
+    chk = a[: 1 << 24]                                 # 64 MB: every word read once, checked on the host
+    B.stream_read(chk, sink, stream)
+    got = int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)))
+    want = int(np.bitwise_xor.reduce(chk.cpu().numpy().view(np.uint32)))
+    if got != want:
+        raise SystemExit(f"stream read check failed: XOR {got:#x} != {want:#x}")
     out = {}
-    for name, fn, nbytes in (("copy", lambda: b.copy_(a), 2 * n), ("read_sum", lambda: a.sum(), n)):
+    for name, fn, nbytes in (("read_kernel", lambda: B.stream_read(a, sink, stream), n),
+                             ("copy", lambda: b.copy_(a), 2 * n), ("read_sum", lambda: a.sum(), n)):
         for _ in range(2):
             fn()
         torch.cuda.synchronize()

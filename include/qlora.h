@@ -520,6 +520,18 @@ int ql_pool_debug(ql_pool* pool, int32_t delay_us, int32_t poison,
  * touched).  QL_EHIP if waiting for a copy failed; the pool is freed anyway. */
 int ql_pool_destroy(ql_pool* pool);
 
+/* ---------------------------------------------------------------- measurement
+ * The HBM ceiling the kernels are measured against: one pass of a plain
+ * streaming read over buf (dev, 16-byte aligned, bytes a positive multiple of
+ * 16), every 16-byte word read once by a grid of QL_STREAM_READ_THREADS
+ * threads (256 workgroups of 256, eight loads in flight per thread, strided
+ * by the grid), each thread's words folded by XOR into sink[thread] (dev
+ * uint32 [QL_STREAM_READ_THREADS]), so the XOR of all of sink is the XOR of
+ * every 32-bit word of buf.  Asynchronous on stream.  QL_EINVAL for a null
+ * or misaligned pointer or a bad size. */
+#define QL_STREAM_READ_THREADS 65536
+int ql_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,9 +29,10 @@ EXPORTS = (
     "ql_plan_create", "ql_plan_add_fwd", "ql_plan_add_bwd", "ql_plan_add_event", "ql_plan_size",
     "ql_plan_run", "ql_plan_destroy", "qlora_linear_fwd_group", "qlora_linear_bwd_group",
     "ql_plan_add_fwd_group", "ql_plan_add_bwd_group", "ql_stack_adapters", "qlora_linear_bwd_noalloc",
-    "ql_adamw8_step", "ql_dyn8_levels",
+    "ql_adamw8_step", "ql_dyn8_levels", "ql_stream_read",
 )
 ADAMW8_BLOCK = 2048
+STREAM_READ_THREADS = 65536
 NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 STACK_MAX = 8
 GROUP_MAX = 8
@@ -135,6 +136,7 @@ def load(path=LIB_PATH):
         "ql_adamw8_step": (ctypes.c_int, [ctypes.POINTER(Adamw8TensorC), I32,
                                           ctypes.POINTER(AdamwHparamsC), P]),
         "ql_dyn8_levels": (ctypes.c_int, [I32, P]),
+        "ql_stream_read": (ctypes.c_int, [P, I64, P, P]),
         "ql_stack_adapters": (ctypes.c_int, [ctypes.POINTER(AdapterC), I32, I64, I64, P, P,
                                              ctypes.POINTER(ctypes.c_float), P]),
     }
@@ -277,6 +279,17 @@ def act_quant_e4m3(x, stream=None):
         s = torch.empty(m, dtype=torch.float32, device=x.device)
     _check(load().ql_act_quant_e4m3(_ptr(x), m, k, _ptr(hi), _ptr(lo), _ptr(s), _stream(stream)))
     return hi, lo, s
+
+
+def stream_read(buf, sink, stream=None):
+    """One streaming read of the device tensor buf (the HBM ceiling kernel);
+    sink: int32 device tensor of STREAM_READ_THREADS entries, whose XOR is the
+    XOR of every 32-bit word of buf."""
+    if not buf.is_cuda or not sink.is_cuda or sink.dtype != torch.int32 or sink.numel() != STREAM_READ_THREADS:
+        raise ValueError("buf and sink must be device tensors, sink int32 of STREAM_READ_THREADS entries")
+    if not buf.is_contiguous() or not sink.is_contiguous():
+        raise ValueError("buf and sink must be contiguous")
+    _check(load().ql_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
 
 
 # ----------------------------------------------------------------------------- layer

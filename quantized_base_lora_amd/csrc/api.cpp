@@ -460,6 +460,17 @@ int qlora_dequant(const ql_qweight* w, float* out_f32, uint16_t* out_bf16, void*
   return QL_OK;
 }
 
+int ql_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return set_error(QL_EINVAL, "null pointer");
+  if (bytes <= 0 || bytes % 16) return set_error(QL_EINVAL, "bytes=%lld: need a positive multiple of 16", (long long)bytes);
+  if (!aligned16(buf) || ((uintptr_t)sink & 3u)) return set_error(QL_EINVAL, "misaligned pointer");
+  int rc = check_sticky();
+  if (rc) return rc;
+  hipError_t e = launch_stream_read(buf, bytes, sink, as_stream(stream));
+  if (e != hipSuccess) return hip_error(e, "stream read launch");
+  return QL_OK;
+}
+
 int ql_act_quant_e4m3(const uint16_t* x, int64_t m, int64_t k, uint8_t* hi, uint8_t* lo,
                       float* scale, void* stream) {
   if (m < 0 || k <= 0 || k % 16) return set_error(QL_EINVAL, "need m >= 0 and k a positive multiple of 16");

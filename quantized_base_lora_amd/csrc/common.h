@@ -75,6 +75,8 @@ struct ActSplit {
 };
 hipError_t launch_act_quant_group(const ActSplit* sp, int n, int64_t m, hipStream_t s);
 hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s);
+// one streaming read of bytes (a multiple of 16) at buf; sink [QL_STREAM_READ_THREADS]
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t s);
 
 // fused base GEMM + LoRA (kernels_gemm.hip)

@@ -128,6 +128,18 @@ def test_layer_argument_errors(lib):
     assert lib.ql_act_quant_e4m3(P, 4, 24, P, P, P, None) == binding.QL_EINVAL
 
 
+def test_stream_read_argument_errors(lib):
+    """The measurement read refuses null or misaligned pointers and sizes that
+    are not a positive multiple of 16, before any launch."""
+    P = FAKE
+    assert lib.ql_stream_read(None, 1024, P, None) == binding.QL_EINVAL
+    assert lib.ql_stream_read(P, 1024, None, None) == binding.QL_EINVAL
+    assert lib.ql_stream_read(P, 0, P, None) == binding.QL_EINVAL
+    assert lib.ql_stream_read(P, 1000, P, None) == binding.QL_EINVAL
+    assert lib.ql_stream_read(ctypes.c_void_p(P.value + 8), 1024, P, None) == binding.QL_EINVAL
+    assert lib.ql_stream_read(P, 1024, ctypes.c_void_p(P.value + 2), None) == binding.QL_EINVAL
+
+
 def test_size_limits_refused(lib):
     """Shapes whose 32-bit buffer offsets would overflow are refused before
     any launch: more than QL_MAX_FEATURES per side, or codes of 2 GiB or more
