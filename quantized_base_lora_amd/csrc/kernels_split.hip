@@ -962,7 +962,10 @@ hipError_t launch_split(SplitGroup& g, hipStream_t s) {
 // are summed in split order (deterministic), the LoRA term s . U . up^T is
 // added in fp32 (U = sum of its partials), and the sum is rounded once to
 // bf16.  Column-slab 0 also writes U (forward) or V (dX).  One thread per 4
-// consecutive outputs of one row.
+// consecutive outputs of MR rows: it loads their up-matrix entries once and
+// the partials of all MR rows at once (SPL per row, SPL at least the split
+// count; MR SPL = 16 keeps the loads in flight within the same registers), so
+// with few splits the up matrix is read once per MR rows instead of per row.
 struct ReduceItem {
   const float* part;
   const float* upart;
@@ -979,9 +982,10 @@ struct ReduceArgs {
   int32_t trans;
 };
 
-template <int R>
+template <int R, int SPL>
 __global__ __launch_bounds__(128) void split_reduce_kernel(ReduceArgs ra) {
-  __shared__ float us[R];
+  constexpr int MR = MAX_SPLITS / SPL;
+  __shared__ float us[MR][R];
   const int bid = (int)blockIdx.x;
   int ii = 0;
   while (ii + 1 < ra.n && bid >= ra.it[ii + 1].blk0) ++ii;
@@ -992,25 +996,27 @@ __global__ __launch_bounds__(128) void split_reduce_kernel(ReduceArgs ra) {
   uint16_t* __restrict__ out = I.out;
   float* __restrict__ save = I.save;
   const int64_t M = I.M, O = I.O;
-  const int splits = I.splits;
   const float s = I.s;
   const bool trans = ra.trans != 0;
   const int local = bid - I.blk0;
   const int bx = local % I.xblocks;
-  const int64_t m = local / I.xblocks;
+  const int64_t m0 = (int64_t)(local / I.xblocks) * MR;
   const int tid = threadIdx.x;
   // splits past the last read as zero through the resource bounds
-  const __amdgpu_buffer_rsrc_t rp = rsrc(part, (int64_t)splits * M * O * 4);
-  const __amdgpu_buffer_rsrc_t ru = rsrc(upart, (int64_t)splits * M * R * 4);
-  if (tid < R) {
-    uint32_t v[MAX_SPLITS];
+  const __amdgpu_buffer_rsrc_t rp = rsrc(part, (int64_t)I.splits * M * O * 4);
+  const __amdgpu_buffer_rsrc_t ru = rsrc(upart, (int64_t)I.splits * M * R * 4);
+  for (int t = tid; t < MR * R; t += 128) {
+    const int r = t / R, j = t % R;
+    const int64_t m = m0 + r;
+    uint32_t v[SPL];
 #pragma unroll
-    for (int sp = 0; sp < MAX_SPLITS; ++sp) v[sp] = bload4(ru, (uint32_t)((((int64_t)sp * M + m) * R + tid) * 4));
+    for (int sp = 0; sp < SPL; ++sp)
+      v[sp] = bload4(ru, m < M ? (uint32_t)((((int64_t)sp * M + m) * R + j) * 4) : OOB);
     float u = 0.0f;
 #pragma unroll
-    for (int sp = 0; sp < MAX_SPLITS; ++sp) u += __uint_as_float(v[sp]);
-    if (save && bx == 0) save[m * R + tid] = u;
-    us[tid] = s * u;
+    for (int sp = 0; sp < SPL; ++sp) u += __uint_as_float(v[sp]);
+    if (save && bx == 0 && m < M) save[m * R + j] = u;
+    us[r][j] = s * u;
   }
   const int64_t o = (int64_t)bx * 512 + tid * 4;
   const bool live = o < O;
@@ -1037,30 +1043,38 @@ __global__ __launch_bounds__(128) void split_reduce_kernel(ReduceArgs ra) {
       }
     }
   }
-  // all partial loads in flight at once, then summed in split order
-  uint4 pv[MAX_SPLITS];
+  // all partial loads of the MR rows in flight at once, then summed in split order
+  uint4 pv[MR][SPL];
 #pragma unroll
-  for (int sp = 0; sp < MAX_SPLITS; ++sp)
-    pv[sp] = bload16(rp, live ? (uint32_t)((((int64_t)sp * M + m) * O + o) * 4) : OOB);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int r = 0; r < MR; ++r)
 #pragma unroll
-  for (int sp = 0; sp < MAX_SPLITS; ++sp) {
-    acc.x += __uint_as_float(pv[sp].x); acc.y += __uint_as_float(pv[sp].y);
-    acc.z += __uint_as_float(pv[sp].z); acc.w += __uint_as_float(pv[sp].w);
-  }
+    for (int sp = 0; sp < SPL; ++sp)
+      pv[r][sp] = bload16(rp, (live && m0 + r < M) ? (uint32_t)((((int64_t)sp * M + m0 + r) * O + o) * 4) : OOB);
   __syncthreads();
   if (!live) return;
-  float l[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int r = 0; r < MR; ++r) {
+    const int64_t m = m0 + r;
+    if (m < M) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int q = 0; q < R / 2; ++q) {
-      l[c] += us[2 * q] * __uint_as_float(w[c][q] << 16);
-      l[c] += us[2 * q + 1] * __uint_as_float(w[c][q] & 0xFFFF0000u);
+      for (int sp = 0; sp < SPL; ++sp) {
+        acc.x += __uint_as_float(pv[r][sp].x); acc.y += __uint_as_float(pv[r][sp].y);
+        acc.z += __uint_as_float(pv[r][sp].z); acc.w += __uint_as_float(pv[r][sp].w);
+      }
+      float l[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int q = 0; q < R / 2; ++q) {
+          l[c] += us[r][2 * q] * __uint_as_float(w[c][q] << 16);
+          l[c] += us[r][2 * q + 1] * __uint_as_float(w[c][q] & 0xFFFF0000u);
+        }
+      const uint32_t lo = pack_bf16x2(acc.x + l[0], acc.y + l[1]);
+      const uint32_t hi = pack_bf16x2(acc.z + l[2], acc.w + l[3]);
+      *reinterpret_cast<uint2*>(out + m * O + o) = make_uint2(lo, hi);
     }
-  const uint32_t lo = pack_bf16x2(acc.x + l[0], acc.y + l[1]);
-  const uint32_t hi = pack_bf16x2(acc.z + l[2], acc.w + l[3]);
-  *reinterpret_cast<uint2*>(out + m * O + o) = make_uint2(lo, hi);
+  }
 }
 
 // dX reduction with the adapter gradients, at most 32 tokens (all of them in
@@ -1233,6 +1247,10 @@ hipError_t launch_path(const SplitGroup& g0, const GradFuse* gf, hipStream_t s) 
   ReduceArgs ra{};
   ra.n = g.n;
   ra.trans = TRANS ? 1 : 0;
+  int32_t maxsp = 1;
+  for (int i = 0; i < g.n; ++i) maxsp = std::max(maxsp, (int32_t)g.splits[i]);
+  const int spl = maxsp <= 2 ? 2 : maxsp <= 4 ? 4 : maxsp <= 8 ? 8 : MAX_SPLITS;
+  const int mr = MAX_SPLITS / spl;                   // rows per workgroup
   int32_t blocks = 0;
   for (int i = 0; i < g.n; ++i) {
     const Params& p = g.p[i];
@@ -1248,9 +1266,14 @@ hipError_t launch_path(const SplitGroup& g0, const GradFuse* gf, hipStream_t s) 
     I.splits = g.splits[i];
     I.xblocks = (int32_t)((p.O + 511) / 512);
     I.blk0 = blocks;
-    blocks += I.xblocks * (int32_t)p.M;
+    blocks += I.xblocks * (int32_t)((p.M + mr - 1) / mr);
   }
-  hipLaunchKernelGGL(split_reduce_kernel<R>, dim3((unsigned)blocks), dim3(128), 0, s, ra);
+  switch (spl) {
+    case 2: hipLaunchKernelGGL((split_reduce_kernel<R, 2>), dim3((unsigned)blocks), dim3(128), 0, s, ra); break;
+    case 4: hipLaunchKernelGGL((split_reduce_kernel<R, 4>), dim3((unsigned)blocks), dim3(128), 0, s, ra); break;
+    case 8: hipLaunchKernelGGL((split_reduce_kernel<R, 8>), dim3((unsigned)blocks), dim3(128), 0, s, ra); break;
+    default: hipLaunchKernelGGL((split_reduce_kernel<R, MAX_SPLITS>), dim3((unsigned)blocks), dim3(128), 0, s, ra); break;
+  }
   return hipGetLastError();
 }
 
