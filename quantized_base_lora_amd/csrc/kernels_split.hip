@@ -44,11 +44,14 @@ struct SplitArgs {
 };
 
 // Scale window (SW, forward only): the tile's scale entries over the
-// workgroup's slice (at most 64 contiguous bytes a row) are loaded once into
+// workgroup's slice (at most 128 contiguous bytes a row) are loaded once into
 // LDS with coalesced dword loads, after the stages, and each step reads its
 // scale there instead of issuing a load that touches 32 rows with 1-4 bytes
 // each.
-constexpr int SWB = 80;                            // LDS row stride of the scale window (bytes)
+constexpr int SWB = 144;                           // LDS row stride of the scale window (bytes)
+// dwords a window row: 128 bytes (32 steps of a 4-byte scale step); MXFP4's
+// one-byte scales need at most 64
+template <int FMT> constexpr int sw_dw() { return FMT == QL_FMT_MXFP4 ? 16 : 32; }
 template <int FMT> constexpr int scale_step64_bytes() { return FMT == QL_FMT_MXFP4 ? 2 : 4; }
 
 template <int FMT, bool TRANS, int R, int MBK, bool SW>
@@ -294,11 +297,12 @@ void qsplit_kernel(SplitArgs ga) {
   }
   // scale window (before the stages, so that waiting for it leaves their loads in flight):
   // each row's dwords from the one holding the slice's first scale byte
-  uint32_t swv[SW ? 8 : 1];
+  constexpr int SW_DW = sw_dw<FMT>();
+  uint32_t swv[SW ? 128 * SW_DW / 256 : 1];
   if constexpr (SW) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int pc = tid + 256 * i, row = pc >> 4, dw = pc & 15;
+    for (int i = 0; i < 128 * SW_DW / 256; ++i) {
+      const int pc = tid + 256 * i, row = pc / SW_DW, dw = pc % SW_DW;
       const bool ok = 4 * dw < sdel + scale_step64_bytes<FMT>() * NKT;
       swv[i] = bload4(rscale, ok ? (uint32_t)(row * srow * ssz + sb0 - sdel + 4 * dw) : OOB);
     }
@@ -308,9 +312,9 @@ void qsplit_kernel(SplitArgs ga) {
   for (int u = 0; u < D; ++u) issue(ring[u], kbeg + u);
   if constexpr (SW) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 128 * SW_DW / 256; ++i) {
       const int pc = tid + 256 * i;
-      *reinterpret_cast<uint32_t*>(swin + (pc >> 4) * SWB + 4 * (pc & 15)) = swv[i];
+      *reinterpret_cast<uint32_t*>(swin + (pc / SW_DW) * SWB + 4 * (pc % SW_DW)) = swv[i];
     }
   }
   lds_barrier();
@@ -909,14 +913,14 @@ hipError_t launch_split_m(const SplitGroup& g, hipStream_t s) {
 template <int FMT, bool TRANS, int R>
 hipError_t launch_split_general(const SplitGroup& g, hipStream_t s) {
   if constexpr (!TRANS && FMT != QL_FMT_FP8_E4M3) {
-    // the scale window holds at most 64 bytes a row, read in aligned dwords
+    // the scale window holds 4 sw_dw bytes a row, read in aligned dwords
     // from the one holding a slice's first scale byte (an MXFP4 slice of an
     // odd number of steps starts 2 bytes into it in every other split, so 2
     // more bytes); the rows must start 4-byte aligned
     bool sw = true;
     for (int i = 0; i < g.n; ++i) {
       const int sb = scale_step64_bytes<FMT>() * g.p[i].sps;
-      sw = sw && sb + (sb % 4 ? 2 : 0) <= 64 && (g.p[i].K * scale_bytes<FMT>() / (FMT == QL_FMT_NF4 ? 64 : 32)) % 4 == 0;
+      sw = sw && sb + (sb % 4 ? 2 : 0) <= 4 * sw_dw<FMT>() && (g.p[i].K * scale_bytes<FMT>() / (FMT == QL_FMT_NF4 ? 64 : 32)) % 4 == 0;
     }
     if (sw)
       return g.p[0].M <= 32 ? launch_split_m<FMT, TRANS, R, 1, true>(g, s) : launch_split_m<FMT, TRANS, R, 2, true>(g, s);
