@@ -232,20 +232,42 @@ GradLaunch grad_launch(const BwdArgs& a, const BwdParts& b) {
   return g;
 }
 
-hipError_t bwd_grads(const BwdArgs& a, const BwdParts& b, hipStream_t s, GradReduceSet* defer) {
-  if (b.fuse) return hipSuccess;
-  const GradLaunch g = grad_launch(a, b);
-  return launch_grads_group(&g, 1, s, defer);
+// the adapter gradients of n calls: launched now, or (kdefer, launch plans)
+// added to the held-back set, which is launched first if they do not fit it.
+// Held back only on the small-token path, where a launch costs more than its
+// work (the 64-token Llama-3.1-8B step 5 % shorter); with many tokens each
+// launch right after its dX GEMM finds dY still in the last-level cache
+// (held back to the end of the step, the Qwen3-0.6B layer at 8192 tokens
+// ran 1.7 % slower).
+hipError_t grads_now_or_held(const GradLaunch* g, int n, hipStream_t s, GradReduceSet* defer,
+                             GradKernelSet* kdefer) {
+  if (!kdefer || !split_path_tokens(g[0].m)) return launch_grads_group(g, n, s, defer);
+  for (int i = 0; i < n; ++i) {
+    if (!kdefer->fits(g[i])) {
+      hipError_t e = launch_grad_kernels(*kdefer, s, defer);
+      if (e != hipSuccess) return e;
+    }
+    kdefer->g[kdefer->n++] = g[i];
+  }
+  return hipSuccess;
 }
 
-// defer: hold the gradient reduction back in that set (launch plans)
-int enqueue_bwd(const BwdArgs& a, hipStream_t s, GradReduceSet* defer = nullptr) {
+hipError_t bwd_grads(const BwdArgs& a, const BwdParts& b, hipStream_t s, GradReduceSet* defer,
+                     GradKernelSet* kdefer) {
+  if (b.fuse) return hipSuccess;
+  const GradLaunch g = grad_launch(a, b);
+  return grads_now_or_held(&g, 1, s, defer, kdefer);
+}
+
+// defer: hold the gradient reduction back in that set; kdefer: hold the
+// gradient launch itself back (launch plans)
+int enqueue_bwd(const BwdArgs& a, hipStream_t s, GradReduceSet* defer = nullptr, GradKernelSet* kdefer = nullptr) {
   BwdParts b;
   bwd_parts(a, b);
   hipError_t e = hipSuccess;
   if (a.m > 0 && a.dx) e = launch_qgemm(b.gemm, s);
   else if (a.m > 0) e = launch_down_proj(a.dy, a.m, a.w.n_out, a.b, a.r, b.v, s);
-  if (e == hipSuccess) e = bwd_grads(a, b, s, defer);
+  if (e == hipSuccess) e = bwd_grads(a, b, s, defer, kdefer);
   if (e != hipSuccess) return hip_error(e, "backward launch");
   return QL_OK;
 }
@@ -317,12 +339,13 @@ int enqueue_fwd_group(const FwdArgs* a, int n, hipStream_t s) {
   return QL_OK;
 }
 
-int enqueue_bwd_group(const BwdArgs* a, int n, hipStream_t s, GradReduceSet* defer = nullptr) {
+int enqueue_bwd_group(const BwdArgs* a, int n, hipStream_t s, GradReduceSet* defer = nullptr,
+                      GradKernelSet* kdefer = nullptr) {
   bool all_dx = true;
   for (int i = 0; i < n; ++i) all_dx = all_dx && a[i].dx;
   if (n <= 1 || a[0].m == 0 || !all_dx) {
     for (int i = 0; i < n; ++i) {
-      int rc = enqueue_bwd(a[i], s, defer);
+      int rc = enqueue_bwd(a[i], s, defer, kdefer);
       if (rc) return rc;
     }
     return QL_OK;
@@ -337,7 +360,7 @@ int enqueue_bwd_group(const BwdArgs* a, int n, hipStream_t s, GradReduceSet* def
   if (e == hipSuccess && !b[0].fuse) {   // one token count: all fused or none
     GradLaunch g[QL_GROUP_MAX];
     for (int i = 0; i < n; ++i) g[i] = grad_launch(a[i], b[i]);
-    e = launch_grads_group(g, n, s, defer);
+    e = grads_now_or_held(g, n, s, defer, kdefer);
   }
   if (e != hipSuccess) return hip_error(e, "grouped backward launch");
   return QL_OK;
@@ -696,14 +719,48 @@ int ql_plan_run(ql_plan* plan, void* stream) {
   int rc = check_sticky();
   if (rc) return rc;
   hipStream_t s = as_stream(stream);
-  // The adapter-gradient reductions of backward steps are held back and run
-  // as one launch: before the first later step that touches a buffer they
-  // write (dA, dB) or writes a buffer they read (the partials in a backward
-  // workspace), before an event, and at the end of the plan.  The reductions
-  // are the same kernels on the same partials, so results are bitwise those
-  // of the calls made one by one.
+  // The adapter-gradient launches of backward steps, and their reductions,
+  // are held back and run as one launch each: before the first later step
+  // that touches a buffer they write (dA, dB, partials in a backward
+  // workspace) or writes a buffer they read (x, dY, U, and V in a backward
+  // workspace), before an event, and at the end of the plan.  They are the
+  // same kernels on the same data (a problem's result does not depend on the
+  // others in a launch), so results are bitwise those of the calls made one
+  // by one.
   GradReduceSet pend;
+  GradKernelSet kpend;
   for (const PlanStep& st : plan->steps) {
+    bool kflush = st.kind == PlanStep::EVENT;
+    if (!kflush && kpend.n > 0) {
+      std::vector<Span> all, out;
+      auto add = [&](const Span* ai, int na, const Span* ao, int no) {
+        all.insert(all.end(), ai, ai + na);
+        out.insert(out.end(), ao, ao + no);
+      };
+      Span ai[10], ao[6];
+      int na, no;
+      if (st.kind == PlanStep::FWD) { fwd_spans(st.fwd, ai, na, ao, no); add(ai, na, ao, no); }
+      if (st.kind == PlanStep::BWD) { bwd_spans(st.bwd, ai, na, ao, no); add(ai, na, ao, no); }
+      for (const FwdArgs& f : st.fwds) { fwd_spans(f, ai, na, ao, no); add(ai, na, ao, no); }
+      for (const BwdArgs& b : st.bwds) { bwd_spans(b, ai, na, ao, no); add(ai, na, ao, no); }
+      for (int i = 0; i < kpend.n && !kflush; ++i) {
+        const GradLaunch& g = kpend.g[i];
+        const size_t r4 = (size_t)g.r * 4;
+        const Span reads[4] = {{g.x, (size_t)(g.m * g.k * 2)}, {g.dy, (size_t)(g.m * g.n * 2)},
+                               {g.v, (size_t)g.m * r4}, {g.u, (size_t)g.m * r4}};
+        const Span writes[4] = {{g.d_a, (size_t)g.k * r4}, {g.d_b, (size_t)g.n * r4},
+                                {g.part_a, g.nparts > 1 ? (size_t)g.nparts * g.k * r4 : 0},
+                                {g.part_b, g.nparts > 1 ? (size_t)g.nparts * g.n * r4 : 0}};
+        for (const Span& x : out)
+          for (const Span& y : reads) kflush = kflush || overlaps(x.p, x.n, y.p, y.n);
+        for (const Span& x : all)
+          for (const Span& y : writes) kflush = kflush || overlaps(x.p, x.n, y.p, y.n);
+      }
+    }
+    if (kflush && kpend.n > 0) {
+      hipError_t e = launch_grad_kernels(kpend, s, &pend);
+      if (e != hipSuccess) return hip_error(e, "plan gradient launch");
+    }
     bool flush = st.kind == PlanStep::EVENT;
     if (!flush && pend.n > 0) {
       std::vector<Span> all, out;
@@ -738,9 +795,9 @@ int ql_plan_run(ql_plan* plan, void* stream) {
     }
     switch (st.kind) {
       case PlanStep::FWD: rc = enqueue_fwd(st.fwd, s); break;
-      case PlanStep::BWD: rc = enqueue_bwd(st.bwd, s, &pend); break;
+      case PlanStep::BWD: rc = enqueue_bwd(st.bwd, s, &pend, &kpend); break;
       case PlanStep::FWD_GROUP: rc = enqueue_fwd_group(st.fwds.data(), (int)st.fwds.size(), s); break;
-      case PlanStep::BWD_GROUP: rc = enqueue_bwd_group(st.bwds.data(), (int)st.bwds.size(), s, &pend); break;
+      case PlanStep::BWD_GROUP: rc = enqueue_bwd_group(st.bwds.data(), (int)st.bwds.size(), s, &pend, &kpend); break;
       default: {
         hipError_t e = hipEventRecord(st.event, s);
         rc = e == hipSuccess ? QL_OK : hip_error(e, "plan event record");
@@ -748,7 +805,9 @@ int ql_plan_run(ql_plan* plan, void* stream) {
     }
     if (rc) return rc;
   }
-  hipError_t e = launch_grad_reduce(pend, s);
+  hipError_t e = launch_grad_kernels(kpend, s, &pend);
+  if (e != hipSuccess) return hip_error(e, "plan gradient launch");
+  e = launch_grad_reduce(pend, s);
   return e == hipSuccess ? QL_OK : hip_error(e, "plan gradient reduction");
 }
 

@@ -90,6 +90,8 @@ struct GradFuse {
   int32_t accumulate;
 };
 bool split_path_fuses_grads(int64_t m);
+// the small-token (split-contraction) path serves this many tokens
+bool split_path_tokens(int64_t m);
 
 struct GemmCall {
   const ql_qweight* w;
@@ -200,6 +202,19 @@ struct GradReduceSet {
 hipError_t launch_grads_group(const GradLaunch* g, int n, hipStream_t s, GradReduceSet* defer = nullptr);
 // launches the set's reductions as one launch (nothing if it is empty) and empties it
 hipError_t launch_grad_reduce(GradReduceSet& d, hipStream_t s);
+// Adapter-gradient launches held back by a launch plan, so that those of
+// consecutive backward steps run as one grad_kernel launch; the calls of a
+// set share the token count (> 0), rank and partition plan.
+struct GradKernelSet {
+  GradLaunch g[QL_GROUP_MAX];
+  int32_t n = 0;
+  bool fits(const GradLaunch& x) const {
+    return n == 0 || (n < QL_GROUP_MAX && x.m == g[0].m && x.r == g[0].r && x.nparts == g[0].nparts);
+  }
+};
+// launches the set's calls as one group (reductions into `defer` as
+// launch_grads_group does) and empties it
+hipError_t launch_grad_kernels(GradKernelSet& k, hipStream_t s, GradReduceSet* defer);
 int32_t grad_parts(int64_t m);
 int64_t grad_tiles(int64_t pdim, int32_t r);
 

@@ -378,4 +378,11 @@ hipError_t launch_grads_group(const GradLaunch* g, int n, hipStream_t s, GradRed
 
 hipError_t launch_grads(const GradLaunch& g, hipStream_t s) { return launch_grads_group(&g, 1, s); }
 
+hipError_t launch_grad_kernels(GradKernelSet& k, hipStream_t s, GradReduceSet* defer) {
+  if (k.n == 0) return hipSuccess;
+  const int n = k.n;
+  k.n = 0;
+  return launch_grads_group(k.g, n, s, defer);
+}
+
 }  // namespace ql

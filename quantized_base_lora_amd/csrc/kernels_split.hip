@@ -1325,6 +1325,8 @@ SplitPlan split_plan(bool trans, int64_t m, int64_t n, int64_t k, int r) {
 // per-token loops of the fused kernel cost more than the launch it saves
 bool split_path_fuses_grads(int64_t m) { return m > 0 && m <= 32; }
 
+bool split_path_tokens(int64_t m) { return m > 0 && m <= SMALL_M; }
+
 hipError_t launch_split_path(int fmt, bool trans, int r, const SplitGroup& g, const GradFuse* gf, hipStream_t s) {
   if (g.n < 1 || g.n > MAX_GROUP) return hipErrorInvalidValue;
   if (gf && (!trans || !split_path_fuses_grads(g.p[0].M))) return hipErrorInvalidValue;
