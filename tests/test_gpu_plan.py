@@ -232,18 +232,31 @@ def test_group_edge_cases(lib):
                 assert torch.equal(a.view(iv), b.view(iv)), (m, j, key)
 
 
-def test_plan_held_back_reductions(lib):
-    """A plan holds the adapter-gradient reductions of its backward steps back
-    and runs them as one launch.  Each rule that launches them early is hit
-    here: a later step accumulating into the same dA / dB, later forward and
-    backward steps reusing a held step's workspace, an event, another partition count, a set
-    that is full (16 reductions) and the end of the plan.  Every output must
-    equal, bit for bit, the same calls made one by one."""
+HELD_SPECS = {
+    # 1100 tokens: three partitions of M; 600: two (the reductions are held back)
+    "reductions": [(1100, 256, 192), (1100, 128, 320), (1100, 320, 64), (1100, 192, 128), (1100, 64, 256),
+                   (1100, 256, 64), (1100, 128, 128), (1100, 64, 192), (1100, 192, 96), (600, 128, 192)],
+    # 48 tokens: the small-token path, whose gradient launches are held back
+    # themselves (one partition); the last call has 40 tokens, another plan
+    "gradient_launches": [(48, 256, 192), (48, 128, 320), (48, 320, 64), (48, 192, 128), (48, 64, 256),
+                          (48, 256, 64), (48, 128, 128), (48, 64, 192), (48, 192, 96), (40, 128, 192)],
+}
+
+
+@pytest.mark.parametrize("held", list(HELD_SPECS))
+def test_plan_held_back_reductions(lib, held):
+    """A plan holds the adapter-gradient work of its backward steps back and
+    runs it as one launch: the reductions of partial sums (more than 512
+    tokens), and on the small-token path (33-64 tokens) the gradient launches
+    themselves.  Each rule that launches them early is hit here: a later step
+    accumulating into the same dA / dB, later forward and backward steps
+    reusing a held step's workspace, an event, another partition count or
+    token count, a set that is full (16 reductions, or 8 calls) and the end of
+    the plan.  Every output must equal, bit for bit, the same calls made one
+    by one."""
     from quantized_base_lora_amd import binding as B
     fmt, r, alpha = ofmt.FMT_NF4, 16, 16.0
-    # 1100 tokens: three partitions of M; 600: two
-    specs = [(1100, 256, 192), (1100, 128, 320), (1100, 320, 64), (1100, 192, 128), (1100, 64, 256),
-             (1100, 256, 64), (1100, 128, 128), (1100, 64, 192), (1100, 192, 96), (600, 128, 192)]
+    specs = HELD_SPECS[held]
     calls = []
     wsb = max(256, max(B.workspace_bytes(B.OP_BWD, fmt, n, k, m, r) for m, k, n in specs))
     for i, (m, k, n) in enumerate(specs):
@@ -404,8 +417,8 @@ def test_bench_launch_configuration_matches_single_calls(lib, wname, m):
 @pytest.mark.parametrize("seed", range(12))
 def test_plan_random_sequences(lib, seed):
     """Random launch plans of forward, backward and grouped backward steps and
-    events over a pool of calls at three of 24, 96, 600 and 1100 tokens (the fused,
-    single-partition and several-partition gradient paths), with workspaces
+    events over a pool of calls at three of 24, 48, 96, 600 and 1100 tokens (the fused,
+    held-back, single-partition and several-partition gradient paths), with workspaces
     borrowed from other calls and backward steps accumulating into earlier
     outputs: every output bitwise that of the same calls made one by one, on
     two runs of the plan."""
@@ -414,7 +427,7 @@ def test_plan_random_sequences(lib, seed):
     fmt = [ofmt.FMT_NF4, ofmt.FMT_MXFP4, ofmt.FMT_Q4_0, ofmt.FMT_NVFP4, ofmt.FMT_Q8_0, ofmt.FMT_FP8][seed % 6]
     r, alpha = int(g.choice([8, 16, 32])), 16.0
     pool = []
-    for m in [int(x) for x in g.choice([24, 96, 600, 1100], size=3, replace=False)]:
+    for m in [int(x) for x in g.choice([24, 48, 96, 600, 1100], size=3, replace=False)]:
         for _ in range(3):                                # three calls per token count (groups share it)
             pool.append((m, 64 * int(g.integers(1, 6)), 32 * int(g.integers(1, 9))))
     print(f"random plan seed={seed} fmt={fmt} r={r} pool={pool}", flush=True)
