@@ -594,15 +594,25 @@ void qsplit16_kernel(SplitArgs ga) {
 // through LDS at the end.
 constexpr int S16_STEPS = 8;
 constexpr int XS16 = S16_STEPS * TK2 + 8;          // LDS row stride of the activation slice (bf16)
-constexpr int SW16 = 80;                           // LDS row stride of the scale window (bytes, >= 64)
+// the scale window: dwords a row (the slice's S16_STEPS steps of scale bytes)
+// and the LDS row stride (a pad of 4 or 16 bytes spreads the rows over the
+// banks); MXFP4's one-byte scales need half, which leaves room for four
+// workgroups a CU
+template <int FMT> constexpr int s16_dw() { return (FMT == QL_FMT_MXFP4 ? 4 : 8) * S16_STEPS / 4; }
+template <int FMT> constexpr int s16_stride() { return 4 * s16_dw<FMT>() + (FMT == QL_FMT_MXFP4 ? 4 : 16); }
+// waves a SIMD: four for MXFP4 up to rank 16 (its decode needs fewer
+// registers; rank 32 would spill), three otherwise
+template <int FMT, int R> constexpr int s16_waves() { return FMT == QL_FMT_MXFP4 && R <= 16 ? 4 : 3; }
 // scale bytes per row and step of 128 (MXFP4: 4 one-byte entries; the others 8 bytes)
 template <int FMT> constexpr int scale_step_bytes() { return FMT == QL_FMT_MXFP4 ? 4 : 8; }
 
 template <int FMT, int R>
-__global__ __launch_bounds__(256) void qstream16_kernel(SplitArgs ga) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(s16_waves<FMT, R>(), s16_waves<FMT, R>())))
+void qstream16_kernel(SplitArgs ga) {
   constexpr int TN = 128, D = 4;
   constexpr int RB = (R + 15) / 16;
   __shared__ __attribute__((aligned(16))) uint16_t xs[16 * XS16];
+  constexpr int SW16 = s16_stride<FMT>(), SWD = s16_dw<FMT>();
   __shared__ __attribute__((aligned(16))) uint8_t sw[128 * SW16];   // the tile's scale window
   constexpr int SBS = scale_step_bytes<FMT>();
 
@@ -648,14 +658,14 @@ __global__ __launch_bounds__(256) void qstream16_kernel(SplitArgs ga) {
       xv[st] = bload16(ract, ok ? (uint32_t)((xr * p.C + col) * 2) : OOB);
     }
     // the scale entries of the tile's 128 rows over the slice (at most 64
-    // contiguous bytes a row), loaded once in dwords (16 lanes a row, so a
-    // load covers 4 rows x 64 bytes; no load reaches past the window) and
+    // contiguous bytes a row, 32 for MXFP4), loaded once in dwords (a
+    // lane per dword of a row; no load reaches past the window) and
     // read from LDS by each step: per-step scale loads touch 16 rows with 2-8
     // bytes each and cost 7-15 % of the launch
-    uint32_t sv[8];
+    uint32_t sv[128 * SWD / 256];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int pc = tid + 256 * i, row = pc >> 4, dw = pc & 15;
+    for (int i = 0; i < 128 * SWD / 256; ++i) {
+      const int pc = tid + 256 * i, row = pc / SWD, dw = pc % SWD;
       const bool ok = 4 * dw < SBS * NKT;
       sv[i] = bload4(rscale, ok ? (uint32_t)(row * srow * ssz + (int64_t)kbeg * SBS + 4 * dw) : OOB);
     }
@@ -663,9 +673,9 @@ __global__ __launch_bounds__(256) void qstream16_kernel(SplitArgs ga) {
     for (int st = 0; st < S16_STEPS; ++st)
       *reinterpret_cast<uint4*>(xs + xr * XS16 + st * TK2 + xp) = xv[st];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 128 * SWD / 256; ++i) {
       const int pc = tid + 256 * i;
-      *reinterpret_cast<uint32_t*>(sw + (pc >> 4) * SW16 + 4 * (pc & 15)) = sv[i];
+      *reinterpret_cast<uint32_t*>(sw + (pc / SWD) * SW16 + 4 * (pc % SWD)) = sv[i];
     }
   }
 
