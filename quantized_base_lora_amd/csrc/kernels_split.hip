@@ -1302,7 +1302,7 @@ hipError_t launch_r(const SplitGroup& g, int r, const GradFuse* gf, hipStream_t 
 
 }  // namespace
 
-static_assert(MAX_SPLITS == 16, "split_reduce_kernel unrolls over 16 splits");
+static_assert(MAX_SPLITS == 16, "split_reduce_kernel: rows x splits per thread add up to 16");
 
 SplitPlan split_plan(bool trans, int64_t m, int64_t n, int64_t k, int r) {
   SplitPlan pl;
