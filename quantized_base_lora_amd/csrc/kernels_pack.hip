@@ -469,25 +469,31 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(SplitJobs a) {
   }
 }
 
-// The same split with one wave per row (four rows per workgroup) and the row
-// held in registers: each lane loads CH 16-byte chunks (columns
-// 8 (lane + 64 c) ..; chunks past K read zero), the row maximum is a wave
-// reduction, and the quantization runs from the registers, so x is read from
-// memory once.
-template <int CH>
-__global__ __launch_bounds__(256) void act_quant_wave_kernel(SplitJobs a) {
+// The same split with one workgroup of NT threads per row and the row held
+// in registers, so x is read from memory once: with an even chunk count CH,
+// thread t takes the 16-element pieces at columns 16 (t + NT i), i < CH / 2
+// (16-byte stores of each plane), with CH = 1 the 8 elements at 8 t; pieces
+// past K read zero and are not stored (K is a multiple of 16).  The row
+// maximum is a workgroup reduction.  With one short workgroup per row the
+// launch holds several rounds of workgroups per CU, so the loads of later
+// rows overlap the stores of earlier ones.
+template <int CH, int NT>
+__global__ __launch_bounds__(NT) void act_quant_row_kernel(SplitJobs a) {
+  static_assert(CH == 1 || CH % 2 == 0, "chunk count");
+  constexpr int W = CH == 1 ? 8 : 16;                  // elements per piece
+  __shared__ float red[NT / 64];
   const int bid = (int)blockIdx.x;
   int ji = 0;
   while (ji + 1 < a.n && bid >= a.j[ji + 1].blk0) ++ji;
   const SplitJob& J = a.j[ji];
   const int64_t k = J.k;
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)(bid - J.blk0) * 4 + (threadIdx.x >> 6);
-  if (row >= a.m) return;                              // whole wave
+  const int64_t row = bid - J.blk0;
+  const int tid = threadIdx.x;
   const __amdgpu_buffer_rsrc_t rx = rsrc(J.x + row * k, k * 2);
   uint4 t[CH];
 #pragma unroll
-  for (int c = 0; c < CH; ++c) t[c] = bload16(rx, (uint32_t)((8 * (lane + 64 * c)) * 2));
+  for (int c = 0; c < CH; ++c)
+    t[c] = bload16(rx, (uint32_t)((W * (tid + NT * (c * 8 / W)) + 8 * (c % (W / 8))) * 2));
   float amax = 0.0f;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
@@ -496,17 +502,31 @@ __global__ __launch_bounds__(256) void act_quant_wave_kernel(SplitJobs a) {
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  const int e = amax > 0.0f ? split_exponent(amax) : 0;
-  if (lane == 0) J.scale[row] = amax > 0.0f ? ldexpf(1.0f, e) : 0.0f;
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = red[0];
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int64_t col = 8 * (lane + 64 * (int64_t)c);
+  for (int w = 1; w < NT / 64; ++w) amax = fmaxf(amax, red[w]);
+  const int e = amax > 0.0f ? split_exponent(amax) : 0;
+  if (tid == 0) J.scale[row] = amax > 0.0f ? ldexpf(1.0f, e) : 0.0f;
+#pragma unroll
+  for (int i = 0; i < CH * 8 / W; ++i) {
+    const int64_t col = W * (tid + NT * (int64_t)i);
     if (col >= k) continue;
-    const uint32_t wd[4] = {t[c].x, t[c].y, t[c].z, t[c].w};
-    uint2 h8, l8;
-    split8(wd, e, amax == 0.0f, h8, l8);
-    *reinterpret_cast<uint2*>(J.hi + row * k + col) = h8;
-    *reinterpret_cast<uint2*>(J.lo + row * k + col) = l8;
+    uint2 h8[W / 8], l8[W / 8];
+#pragma unroll
+    for (int h = 0; h < W / 8; ++h) {
+      const uint4& q = t[i * (W / 8) + h];
+      const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+      split8(wd, e, amax == 0.0f, h8[h], l8[h]);
+    }
+    if constexpr (W == 16) {
+      *reinterpret_cast<uint4*>(J.hi + row * k + col) = make_uint4(h8[0].x, h8[0].y, h8[1].x, h8[1].y);
+      *reinterpret_cast<uint4*>(J.lo + row * k + col) = make_uint4(l8[0].x, l8[0].y, l8[1].x, l8[1].y);
+    } else {
+      *reinterpret_cast<uint2*>(J.hi + row * k + col) = h8[0];
+      *reinterpret_cast<uint2*>(J.lo + row * k + col) = l8[0];
+    }
   }
 }
 
@@ -609,24 +629,35 @@ hipError_t launch_dequant(const ql_qweight& w, float* out_f32, uint16_t* out_bf1
 hipError_t launch_act_quant_group(const ActSplit* sp, int n, int64_t m, hipStream_t s) {
   if (m == 0 || n == 0) return hipSuccess;
   if (n > QL_GROUP_MAX) return hipErrorInvalidValue;
-  // rows of at most 4096 elements: one wave per row, x read once (measured
-  // 20 % faster); longer rows would need so many registers per lane that one
-  // wave per SIMD remains, and the two-pass workgroup kernel is faster there.
-  // One launch per kernel for the activations it takes.
-  for (int pass = 0; pass < 2; ++pass) {
-    const bool wave = pass == 0;
+  // rows of at most 16384 elements: one workgroup per row with the row in
+  // registers, x read once (128 threads with 1, 2, 4 or 8 chunks of 1024
+  // elements up to 8192, above that 256 threads with 6 or 8 chunks of 2048);
+  // longer rows take the two-pass kernel.  One launch per kernel instance
+  // for the activations it takes.
+  auto kind_for = [](int64_t k) {
+    return k <= 1024 ? 0 : k <= 2048 ? 1 : k <= 4096 ? 2 : k <= 8192 ? 3 : k <= 12288 ? 4 : k <= 16384 ? 5 : 6;
+  };
+  for (int kind = 0; kind < 7; ++kind) {
     SplitJobs a{};
     a.m = m;
     int32_t blocks = 0;
     for (int i = 0; i < n; ++i) {
-      if ((sp[i].k <= 4096) != wave) continue;
+      if (kind_for(sp[i].k) != kind) continue;
       a.j[a.n] = SplitJob{sp[i].x, sp[i].hi, sp[i].lo, sp[i].scale, sp[i].k, blocks};
       ++a.n;
-      blocks += wave ? (int32_t)((m + 3) / 4) : (int32_t)m;
+      blocks += (int32_t)m;
     }
     if (a.n == 0) continue;
-    if (wave) hipLaunchKernelGGL(act_quant_wave_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(act_quant_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    const dim3 grid((unsigned)blocks);
+    switch (kind) {
+      case 0: hipLaunchKernelGGL((act_quant_row_kernel<1, 128>), grid, dim3(128), 0, s, a); break;
+      case 1: hipLaunchKernelGGL((act_quant_row_kernel<2, 128>), grid, dim3(128), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((act_quant_row_kernel<4, 128>), grid, dim3(128), 0, s, a); break;
+      case 3: hipLaunchKernelGGL((act_quant_row_kernel<8, 128>), grid, dim3(128), 0, s, a); break;
+      case 4: hipLaunchKernelGGL((act_quant_row_kernel<6, 256>), grid, dim3(256), 0, s, a); break;
+      case 5: hipLaunchKernelGGL((act_quant_row_kernel<8, 256>), grid, dim3(256), 0, s, a); break;
+      default: hipLaunchKernelGGL(act_quant_kernel, grid, dim3(kThreads), 0, s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -224,8 +224,11 @@ def test_dequant_all_codes_and_scales(lib):
         assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
 
 
-# one wave per row (rows up to 4096 wide, any row count) and the workgroup-per-row kernel
-@pytest.mark.parametrize("shape", [(40, 320), (37, 4096), (6, 4608)])
+# the register-resident workgroup-per-row kernel in each of its shapes (rows
+# of at most 1024, 2048, 4096, 8192, 12288 and 16384 elements, ragged ones
+# included) and the two-pass kernel for longer rows
+@pytest.mark.parametrize("shape", [(40, 320), (10, 1040), (37, 4096), (9, 2064), (6, 4608), (7, 12288),
+                                   (6, 12304), (6, 16384), (6, 16400)])
 def test_act_split_bitexact(lib, shape):
     from quantized_base_lora_amd import binding as B
     g = np.random.default_rng(5)
