@@ -431,30 +431,36 @@ hipError_t launch8_w(Args8& a, hipStream_t s) {
 constexpr int RP_NW = 8;        // waves per rank-r projection workgroup
 
 // up to QL_GROUP_MAX projections of one token count, rank and layout in one
-// launch; each workgroup finds its problem in a table in the kernel arguments
+// launch; each workgroup finds its problem in a table in the kernel
+// arguments.  Workgroup b runs row block 8 (s / n) + b % 8 of problem s % n,
+// s = b / 8: workgroups are dealt to the eight XCDs in turn, so the n
+// problems' workgroups for one row block run side by side on one XCD, and
+// problems that project the same activation (q|k|v, gate|up) read it from
+// that XCD's L2 instead of once each from memory.
 struct RprojJob {
   const uint16_t* act;
   const uint16_t* d;
   float* out;
   int64_t C;
-  int32_t blk0;          // first workgroup of this problem
 };
 struct RprojJobs {
   RprojJob j[QL_GROUP_MAX];
   int32_t n;
+  int32_t per;           // row blocks of 32 per problem
   int64_t M;
 };
 
 template <int R, bool ALAYOUT>
 __global__ __launch_bounds__(64 * RP_NW) void rproj_kernel(RprojJobs jobs) {
   const int bid = (int)blockIdx.x;
-  int ji = 0;
-  while (ji + 1 < jobs.n && bid >= jobs.j[ji + 1].blk0) ++ji;
+  const int slot = bid >> 3;
+  const int ji = slot % jobs.n;
+  const int blk = (slot / jobs.n) * 8 + (bid & 7);
+  if (blk >= jobs.per) return;                       // whole workgroup, before any barrier
   const uint16_t* __restrict__ act = jobs.j[ji].act;
   const uint16_t* __restrict__ d = jobs.j[ji].d;
   float* __restrict__ out = jobs.j[ji].out;
   const int64_t M = jobs.M, C = jobs.j[ji].C;
-  const int blk = bid - jobs.j[ji].blk0;
   constexpr int SLD = 48, SX = 72, D = 3, NW = RP_NW, NT = 64 * NW;
   constexpr int DP = ALAYOUT ? 4 : R / 8;            // adapter pieces per lane and chunk
   __shared__ __attribute__((aligned(16))) uint16_t xt[NW][32 * SX];                       // activation chunk
@@ -571,9 +577,9 @@ hipError_t launch_rproj_group(const Rproj* pr, int n, int64_t m, bool a_layout, 
   RprojJobs a{};
   a.n = n;
   a.M = m;
-  const int32_t per = (int32_t)((m + 31) / 32);
-  for (int i = 0; i < n; ++i) a.j[i] = RprojJob{pr[i].act, pr[i].d, pr[i].out, pr[i].c, per * i};
-  const dim3 grid((unsigned)(per * n));
+  a.per = (int32_t)((m + 31) / 32);
+  for (int i = 0; i < n; ++i) a.j[i] = RprojJob{pr[i].act, pr[i].d, pr[i].out, pr[i].c};
+  const dim3 grid((unsigned)((a.per + 7) / 8 * 8 * n));
 #define QL_RPROJ(RR)                                                                                 \
   if (a_layout) hipLaunchKernelGGL((rproj_kernel<RR, true>), grid, dim3(64 * RP_NW), 0, s, a);      \
   else hipLaunchKernelGGL((rproj_kernel<RR, false>), grid, dim3(64 * RP_NW), 0, s, a);
