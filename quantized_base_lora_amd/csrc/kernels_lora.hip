@@ -42,9 +42,17 @@ struct GradProb {
   int32_t transpose_out;
   float s;
   int32_t accumulate;
-  int32_t blk0;          // first workgroup of this problem (its tiles x partitions)
+  int32_t blk0;          // first workgroup of this problem's run (below)
   int32_t rblk0;         // first workgroup of this problem in the reduction launch
+  int32_t nblk;          // workgroups of this problem: tiles x partitions
+  int32_t nrun, ridx;    // size of its run, its index in the run
 };
+// Problems that read the same input with the same width (dA of calls with one
+// activation: q|k|v, gate|up) form a run.  Workgroup b of a run of n takes
+// workgroup 8 (s / n) + b % 8 of its problem s % n, s = b / 8: workgroups are
+// dealt to the eight XCDs in turn, so the run's workgroups for one tile and
+// partition run side by side on one XCD and read the input from its L2
+// instead of once each from memory.
 
 // dA and dB of up to QL_GROUP_MAX calls with one token count and rank: the
 // problems of a launch share m, the partition plan and r.
@@ -76,9 +84,15 @@ void grad_kernel(GradArgs a) {
 
   const int bid = (int)blockIdx.x;
   int pi = 0;                                        // this workgroup's problem (uniform)
-  while (pi + 1 < a.nprob && bid >= a.prob[pi + 1].blk0) ++pi;
+  while (pi + 1 < a.nprob && bid >= a.prob[pi + 1].blk0) ++pi;   // the last problem of its run
+  int local = bid - a.prob[pi].blk0;
+  if (a.prob[pi].nrun > 1) {
+    const int nrun = a.prob[pi].nrun, slot = local >> 3;
+    pi += slot % nrun - a.prob[pi].ridx;
+    local = (slot / nrun) * 8 + (local & 7);
+    if (local >= a.prob[pi].nblk) return;             // whole workgroup, before any barrier
+  }
   const GradProb& pr = a.prob[pi];
-  const int local = bid - pr.blk0;
   const int part = local % a.nparts;                 // partition of M
   const int64_t p0 = (int64_t)(local / a.nparts) * TP;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -314,7 +328,7 @@ hipError_t launch_grad_reduce(GradReduceSet& d, hipStream_t s) {
   for (int i = 0; i < d.n; ++i) {
     const GradReduceSet::Item& it = d.item[i];
     a.prob[i] = GradProb{nullptr, nullptr, it.out, const_cast<float*>(it.part), it.pdim, it.transpose_out,
-                         it.s, it.accumulate, 0, rblocks};
+                         it.s, it.accumulate, 0, rblocks, 0, 1, 0};
     rblocks += (int32_t)((it.pdim * d.r + NT - 1) / NT);
   }
   d.n = 0;
@@ -332,19 +346,37 @@ hipError_t launch_grads_group(const GradLaunch* g, int n, hipStream_t s, GradRed
   int64_t chunk = (g[0].m + g[0].nparts - 1) / g[0].nparts;
   a.chunk = (chunk + TMC - 1) / TMC * TMC;
   int32_t blocks = 0, rblocks = 0;
+  GradProb src[MAX_PROB];
   for (int i = 0; i < n; ++i) {
     if (g[i].m != a.m || g[i].r != a.r || g[i].nparts != a.nparts) return hipErrorInvalidValue;
     const float sc = g[i].s;
     const int32_t acc = g[i].accumulate;
-    a.prob[2 * i] = GradProb{g[i].x, g[i].v, g[i].d_a, g[i].part_a, g[i].k, 1, sc, acc, 0, 0};
-    a.prob[2 * i + 1] = GradProb{g[i].dy, g[i].u, g[i].d_b, g[i].part_b, g[i].n, 0, sc, acc, 0, 0};
+    src[2 * i] = GradProb{g[i].x, g[i].v, g[i].d_a, g[i].part_a, g[i].k, 1, sc, acc, 0, 0, 0, 1, 0};
+    src[2 * i + 1] = GradProb{g[i].dy, g[i].u, g[i].d_b, g[i].part_b, g[i].n, 0, sc, acc, 0, 0, 0, 1, 0};
   }
+  // runs of problems with one input and width, in order of first appearance
+  bool taken[MAX_PROB] = {};
+  int np = 0;
   for (int i = 0; i < a.nprob; ++i) {
-    GradProb& pr = a.prob[i];
-    pr.blk0 = blocks;
-    blocks += (int32_t)grad_tiles(pr.pdim, a.r) * a.nparts;
-    pr.rblk0 = rblocks;
-    rblocks += (int32_t)((pr.pdim * a.r + NT - 1) / NT);
+    if (taken[i]) continue;
+    const int first = np;
+    for (int j = i; j < a.nprob; ++j)
+      if (!taken[j] && src[j].x == src[i].x && src[j].pdim == src[i].pdim) {
+        taken[j] = true;
+        a.prob[np++] = src[j];
+      }
+    const int nrun = np - first;
+    const int32_t w = (int32_t)grad_tiles(src[i].pdim, a.r) * a.nparts;
+    for (int j = first; j < np; ++j) {
+      GradProb& pr = a.prob[j];
+      pr.blk0 = blocks;
+      pr.nblk = w;
+      pr.nrun = nrun;
+      pr.ridx = j - first;
+      pr.rblk0 = rblocks;
+      rblocks += (int32_t)((pr.pdim * a.r + NT - 1) / NT);
+    }
+    blocks += nrun == 1 ? w : (w + 7) / 8 * 8 * nrun;
   }
   const bool held = defer && a.m > 0 && a.nparts > 1;
   if (held && defer->n > 0 &&

@@ -137,15 +137,20 @@ def test_group_matches_single_calls(lib, grp):
     pl.close()
 
 
-@pytest.mark.parametrize("m", [300, 1030])
-def test_fp8_group_shared_activation(lib, m):
-    """q|k|v-shaped FP8 group above 64 tokens whose calls share one input x (its
-    two-term split is made once for the group): y, U, dX, dA and dB bitwise those
-    of single calls."""
+# FP8: the two-term split made once for the group, the projections' and the
+# dA launches' workgroups of one row block or tile side by side (ragged row
+# blocks at 300 tokens); NF4 on the bf16 tiles, the dA runs with tile x
+# partition counts that are not multiples of 8 (k = 320: 5 tiles at rank 16,
+# 3 at rank 32)
+@pytest.mark.parametrize("fmt,r,k,m", [(ofmt.FMT_FP8, 16, 512, 300), (ofmt.FMT_FP8, 16, 512, 1030),
+                                       (ofmt.FMT_NF4, 32, 320, 600), (ofmt.FMT_NF4, 16, 320, 1100)])
+def test_group_shared_activation(lib, fmt, r, k, m):
+    """q|k|v-shaped group above 64 tokens whose calls share one input x: y, U,
+    dX, dA and dB bitwise those of single calls."""
     from quantized_base_lora_amd import binding as B
-    fmt, r, alpha, k = ofmt.FMT_FP8, 16, 32.0, 512
+    alpha = 32.0
     ns = [512, 128, 128]
-    print(f"fp8 shared-activation group m={m}", flush=True)
+    print(f"shared-activation group fmt={fmt} r={r} k={k} m={m}", flush=True)
     x = H.bits_to_bf16_tensor(H.make_case(m, k, 32, r, seed=120)["x"])
     items = []
     for i, n in enumerate(ns):
